@@ -1,0 +1,55 @@
+// Internal declarations shared by the host layer and the kernels of libgdr.
+// Nothing here is part of the public ABI (include/gdr.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr.h"
+
+namespace gdr {
+
+// Everything a kernel launch needs, resolved and validated on the host.
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *beta, *log_alpha;
+  const void *erase, *write, *write_key;
+  const float *pc_h_in;
+  float *pc_h_out;
+  const float *state_in;
+  void *out;
+  float *state_out;
+  int B, T, H, Dk, Dv, C;
+  int gain, decay, wkey, N;   // N < 0: exact T; else band i - j <= N
+  float scale, rho, log_rho, eps, h0;
+  long long t0;
+};
+
+// Host launchers (return hipSuccess or the launch error).
+hipError_t launch_chunk_generic(const ChunkArgs &a, int io_dtype, hipStream_t s);
+hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
+bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in,
+                         const void *out, const float *state_out);
+hipError_t launch_step(const ChunkArgs &a, int io_dtype, hipStream_t s);
+
+// ---------------------------------------------------------------------------------
+// Device helpers: storage conversions.  bf16 is stored as uint16_t bit patterns.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float ld_f(const float *p, long long i) { return p[i]; }
+__device__ __forceinline__ float ld_f(const uint16_t *p, long long i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ void st_f(float *p, long long i, float x) { p[i] = x; }
+__device__ __forceinline__ void st_f(uint16_t *p, long long i, float x) { p[i] = f32_to_bf16_bits(x); }
+
+}  // namespace gdr

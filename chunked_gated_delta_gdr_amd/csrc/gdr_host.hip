@@ -1,0 +1,238 @@
+// Host layer of libgdr: argument validation, kernel choice, launch, error reporting.
+//
+// Validation is a pure host function (no HIP call), so malformed calls are rejected
+// before anything is enqueued and can be tested without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status_t fail(gdr_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gdr_status_t ok() {
+  g_last_error.clear();
+  return GDR_OK;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char *e = std::getenv("GDR_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+struct Range {
+  const char *name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range &a, const Range &b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const char *name, const void *p, long double bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p == nullptr ? lo : lo + static_cast<uintptr_t>(bytes)};
+}
+
+// Largest element count of any one tensor the library accepts (2^40 elements).
+constexpr long double kMaxElems = 1099511627776.0L;
+
+}  // namespace
+
+extern "C" {
+
+const char *gdr_status_str(gdr_status_t s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_EINVAL: return "GDR_EINVAL: invalid argument";
+    case GDR_ENOTSUP: return "GDR_ENOTSUP: not supported";
+    case GDR_EHIP: return "GDR_EHIP: HIP runtime error";
+  }
+  return "GDR_UNKNOWN_STATUS";
+}
+
+const char *gdr_last_error(void) { return g_last_error.c_str(); }
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                          const void *out, const float *state_out, int for_step) {
+  if (d == nullptr || in == nullptr) return fail(GDR_EINVAL, "desc and inputs must be non-NULL");
+  if (d->struct_size != sizeof(gdr_desc_t))
+    return fail(GDR_EINVAL, "desc->struct_size = %u, expected %zu (ABI mismatch)", d->struct_size,
+                sizeof(gdr_desc_t));
+  if (d->B < 1 || d->H < 1) return fail(GDR_EINVAL, "B = %d and H = %d must be >= 1", d->B, d->H);
+  if (d->B > 65535 || d->H > 65535) return fail(GDR_ENOTSUP, "B = %d, H = %d (max 65535 each)", d->B, d->H);
+  if (for_step ? d->T != 1 : d->T < 0)
+    return fail(GDR_EINVAL, for_step ? "T = %d; gdr_recurrent_step takes exactly one token"
+                                     : "T = %d must be >= 0", d->T);
+  if (d->Dk < 1 || d->Dv < 1) return fail(GDR_EINVAL, "Dk = %d and Dv = %d must be >= 1", d->Dk, d->Dv);
+  if (d->Dk > 128 || d->Dv > 512)
+    return fail(GDR_ENOTSUP, "Dk = %d (max 128), Dv = %d (max 512)", d->Dk, d->Dv);
+  if (!for_step && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+    return fail(d->chunk < 1 ? GDR_EINVAL : GDR_ENOTSUP, "chunk = %d; supported: 16, 32, 64", d->chunk);
+  if (d->io_dtype != GDR_F32 && d->io_dtype != GDR_BF16)
+    return fail(GDR_EINVAL, "io_dtype = %d", d->io_dtype);
+  if (d->gain != GDR_GAIN_SCALAR && d->gain != GDR_GAIN_CHANNEL) return fail(GDR_EINVAL, "gain = %d", d->gain);
+  if (d->decay != GDR_DECAY_NONE && d->decay != GDR_DECAY_SCALAR) return fail(GDR_EINVAL, "decay = %d", d->decay);
+  if (d->wkey != GDR_WKEY_SAME && d->wkey != GDR_WKEY_DIAG_PRECOND && d->wkey != GDR_WKEY_EXPLICIT)
+    return fail(GDR_EINVAL, "wkey = %d", d->wkey);
+  if (d->impl != GDR_IMPL_AUTO && d->impl != GDR_IMPL_GENERIC && d->impl != GDR_IMPL_MFMA)
+    return fail(GDR_EINVAL, "impl = %d", d->impl);
+  if (!std::isfinite(d->scale)) return fail(GDR_EINVAL, "scale must be finite");
+
+  const long double B = d->B, T = d->T, H = d->H, Dk = d->Dk, Dv = d->Dv;
+  if (B * T * H * (Dk > Dv ? Dk : Dv) > kMaxElems || B * H * Dv * Dk > kMaxElems)
+    return fail(GDR_ENOTSUP, "problem too large (more than 2^40 elements in one tensor)");
+  const long double esz = d->io_dtype == GDR_BF16 ? 2.0L : 4.0L;
+  const bool need = d->T > 0;  // tensors indexed by token are only read when T > 0
+
+  // required / forbidden pointers
+  if (need && (in->q == nullptr || in->k == nullptr || in->v == nullptr))
+    return fail(GDR_EINVAL, "q, k and v are required");
+  if (d->gain == GDR_GAIN_SCALAR) {
+    if (need && in->beta == nullptr) return fail(GDR_EINVAL, "gain SCALAR needs beta");
+    if (in->erase != nullptr || in->write != nullptr)
+      return fail(GDR_EINVAL, "erase/write gates given with gain SCALAR");
+  } else {
+    if (need && (in->erase == nullptr || in->write == nullptr))
+      return fail(GDR_EINVAL, "gain CHANNEL needs erase and write");
+    if (in->beta != nullptr) return fail(GDR_EINVAL, "beta given with gain CHANNEL");
+  }
+  if (d->decay == GDR_DECAY_SCALAR) {
+    if (need && in->log_alpha == nullptr) return fail(GDR_EINVAL, "decay SCALAR needs log_alpha");
+  } else if (in->log_alpha != nullptr) {
+    return fail(GDR_EINVAL, "log_alpha given with decay NONE");
+  }
+  if (d->wkey == GDR_WKEY_EXPLICIT) {
+    if (need && in->write_key == nullptr) return fail(GDR_EINVAL, "wkey EXPLICIT needs write_key");
+  } else if (in->write_key != nullptr) {
+    return fail(GDR_EINVAL, "write_key given without wkey EXPLICIT");
+  }
+  if (d->wkey == GDR_WKEY_DIAG_PRECOND) {
+    if (!(d->pc_rho > 0.f && d->pc_rho < 1.f)) return fail(GDR_EINVAL, "pc_rho must be in (0, 1)");
+    if (!(d->pc_eps > 0.f) || !std::isfinite(d->pc_eps)) return fail(GDR_EINVAL, "pc_eps must be > 0");
+    if (!(d->pc_h0 >= 0.f) || !std::isfinite(d->pc_h0)) return fail(GDR_EINVAL, "pc_h0 must be >= 0");
+    if (d->pc_t0 < 0) return fail(GDR_EINVAL, "pc_t0 must be >= 0");
+  } else if (in->pc_h_in != nullptr || in->pc_h_out != nullptr) {
+    return fail(GDR_EINVAL, "pc_h_in/pc_h_out given without wkey DIAG_PRECOND");
+  }
+  if ((need || for_step) && out == nullptr) return fail(GDR_EINVAL, "out is required");
+  if (for_step && state_out == nullptr) return fail(GDR_EINVAL, "state is required");
+
+  // alignment to the element size
+  const uintptr_t ea = d->io_dtype == GDR_BF16 ? 1u : 3u;
+  const void *io_ptrs[] = {in->q, in->k, in->v, in->erase, in->write, in->write_key, out};
+  for (const void *p : io_ptrs)
+    if ((reinterpret_cast<uintptr_t>(p) & ea) != 0) return fail(GDR_EINVAL, "misaligned io pointer");
+  const void *f_ptrs[] = {in->beta, in->log_alpha, in->pc_h_in, in->pc_h_out, state_in, state_out};
+  for (const void *p : f_ptrs)
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return fail(GDR_EINVAL, "misaligned fp32 pointer");
+
+  // overlap rules
+  const long double ntok = B * T * H;
+  const Range r_out = rng("out", out, ntok * Dv * esz);
+  const Range inputs[] = {
+      rng("q", in->q, ntok * Dk * esz), rng("k", in->k, ntok * Dk * esz),
+      rng("v", in->v, ntok * Dv * esz), rng("beta", in->beta, ntok * 4),
+      rng("log_alpha", in->log_alpha, ntok * 4), rng("erase", in->erase, ntok * Dk * esz),
+      rng("write", in->write, ntok * Dv * esz), rng("write_key", in->write_key, ntok * Dk * esz),
+      rng("pc_h_in", in->pc_h_in, B * H * Dk * 4)};
+  const Range r_sin = rng("state_in", for_step ? nullptr : state_in, B * H * Dv * Dk * 4);
+  const Range r_sout = rng(for_step ? "state" : "state_out", state_out, B * H * Dv * Dk * 4);
+  const Range r_hout = rng("pc_h_out", in->pc_h_out, B * H * Dk * 4);
+  for (const Range &r : inputs) {
+    if (overlap(r_out, r)) return fail(GDR_EINVAL, "out overlaps %s", r.name);
+    if (overlap(r_sout, r)) return fail(GDR_EINVAL, "%s overlaps %s", r_sout.name, r.name);
+    if (overlap(r_hout, r) && !(for_step && r.lo == r_hout.lo && r.hi == r_hout.hi &&
+                                 r.lo == reinterpret_cast<uintptr_t>(in->pc_h_in)))
+      return fail(GDR_EINVAL, "pc_h_out overlaps %s", r.name);
+  }
+  if (overlap(r_out, r_sout)) return fail(GDR_EINVAL, "out overlaps %s", r_sout.name);
+  if (overlap(r_out, r_sin)) return fail(GDR_EINVAL, "out overlaps state_in");
+  if (overlap(r_out, r_hout)) return fail(GDR_EINVAL, "out overlaps pc_h_out");
+  if (overlap(r_hout, r_sout) || overlap(r_hout, r_sin))
+    return fail(GDR_EINVAL, "pc_h_out overlaps the state");
+  if (overlap(r_sin, r_sout) && !(r_sin.lo == r_sout.lo))
+    return fail(GDR_EINVAL, "state_out partially overlaps state_in");
+  return ok();
+}
+
+int gdr_chunk_fwd_impl(const gdr_desc_t *d) {
+  if (d == nullptr || d->struct_size != sizeof(gdr_desc_t)) return -1;
+  gdr_inputs_t none{};
+  const bool mfma = gdr::chunk_mfma_supports(*d, none, nullptr, nullptr, nullptr);
+  if (d->impl == GDR_IMPL_GENERIC) return GDR_IMPL_GENERIC;
+  if (d->impl == GDR_IMPL_MFMA) return mfma ? GDR_IMPL_MFMA : -1;
+  return mfma ? GDR_IMPL_MFMA : GDR_IMPL_GENERIC;
+}
+
+static gdr::ChunkArgs make_args(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                                void *out, float *state_out) {
+  gdr::ChunkArgs a{};
+  a.q = in->q; a.k = in->k; a.v = in->v;
+  a.beta = in->beta; a.log_alpha = in->log_alpha;
+  a.erase = in->erase; a.write = in->write; a.write_key = in->write_key;
+  a.pc_h_in = in->pc_h_in; a.pc_h_out = in->pc_h_out;
+  a.state_in = state_in; a.out = out; a.state_out = state_out;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv; a.C = d->chunk;
+  a.gain = d->gain; a.decay = d->decay; a.wkey = d->wkey;
+  a.N = d->neumann_order < 0 ? -1 : d->neumann_order;
+  a.scale = d->scale;
+  a.rho = d->pc_rho; a.log_rho = d->wkey == GDR_WKEY_DIAG_PRECOND ? std::log(d->pc_rho) : 0.f;
+  a.eps = d->pc_eps; a.h0 = d->pc_h0; a.t0 = d->pc_t0;
+  return a;
+}
+
+gdr_status_t gdr_chunk_fwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                           void *out, float *state_out, void *stream) {
+  gdr_status_t st = gdr_validate(d, in, state_in, out, state_out, 0);
+  if (st != GDR_OK) return st;
+  const bool mfma_ok = gdr::chunk_mfma_supports(*d, *in, state_in, out, state_out);
+  if (d->impl == GDR_IMPL_MFMA && !mfma_ok)
+    return fail(GDR_ENOTSUP, "the MFMA kernel does not cover this descriptor "
+                             "(needs bf16, Dk = Dv = 128, chunk 64, 16-byte aligned tensors)");
+  const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
+  const gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[gdr] chunk_fwd %s B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d N=%d\n",
+                 use_mfma ? "mfma" : "generic", d->B, d->T, d->H, d->Dk, d->Dv, d->chunk,
+                 d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay, d->wkey, a.N);
+  const hipError_t e = use_mfma ? gdr::launch_chunk_mfma(a, s) : gdr::launch_chunk_generic(a, d->io_dtype, s);
+  if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdr_status_t gdr_recurrent_step(const gdr_desc_t *d, const gdr_inputs_t *in, float *state, void *out,
+                                void *stream) {
+  gdr_status_t st = gdr_validate(d, in, nullptr, out, state, 1);
+  if (st != GDR_OK) return st;
+  const gdr::ChunkArgs a = make_args(d, in, state, out, state);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[gdr] recurrent_step B=%d H=%d Dk=%d Dv=%d io=%s\n", d->B, d->H, d->Dk, d->Dv,
+                 d->io_dtype == GDR_BF16 ? "bf16" : "f32");
+  const hipError_t e = gdr::launch_step(a, d->io_dtype, s);
+  if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+/*
+ * gdr.h -- C ABI of the chunked gated delta-rule library for AMD MI355X (gfx950).
+ *
+ * The library computes, for every (batch b, head h) stream, the linear recurrence
+ *
+ *     S_t = alpha_t S_{t-1} (I - e_t r_t^T) + v'_t r_t^T,      o_t = S_t (scale q_t)
+ *
+ * with state S (Dv x Dk), erase (read) key e_t, write key r_t, written value v'_t and
+ * scalar decay alpha_t = exp(log_alpha_t).  The variants are chosen by the descriptor:
+ *
+ *   gain   SCALAR   e = beta k,           v' = beta v        (delta rule / gated delta rule)
+ *          CHANNEL  e = erase (.) k,      v' = write (.) v   (erase gate on the key axis,
+ *                                                              write gate on the value axis)
+ *   decay  NONE     alpha = 1;  SCALAR  alpha_t = exp(log_alpha_t), log_alpha <= 0
+ *   wkey   SAME     r = k;  EXPLICIT  r = write_key;
+ *          DIAG_PRECOND  r = k (.) p_t with p_t = 1 / (hhat_t + eps),
+ *                        h_t = rho h_{t-1} + k_t (.) k_t, hhat_t = h_t / (1 - rho^t),
+ *                        t the 1-based global token index (pc_t0 + position + 1).
+ *
+ * Sources (page titles): the delta rule as an online SGD step on a least-squares loss,
+ * and the decay / gain / preconditioner axes -- "Preconditioned DeltaNet: Curvature-aware
+ * Sequence Modeling for Linear Recurrences", technical summary sections 1, 2a (apply-to-key
+ * write key), 2b (diagonal second-moment preconditioner), 2c (DGPS axes); channel-wise
+ * erase and write gates -- "NVIDIA Apresenta Gated DeltaNet-2", section "Como DeltaNet-2
+ * Redesenhou a Arquitetura"; chunk-wise evaluation with T = (I - A)^-1 for a strictly
+ * lower-triangular A, and the truncated Neumann series with a diagonal band mask --
+ * "Quando o 'Bom o Suficiente' e Otimo: Aproximacao de Inversao de Matriz Baseada Apenas
+ * em Multiplicacao para Gated DeltaNet Quantizado", "Declaracao do Problema" and
+ * "Metodologia" 1-2.
+ *
+ * Conventions shared by every entry point:
+ *  - Layout: q, k, write_key, erase are [B, T, H, Dk]; v, write, out are [B, T, H, Dv];
+ *    beta, log_alpha are [B, T, H]; all contiguous, row-major, last index fastest.  The
+ *    state is [B, H, Dv, Dk] fp32 (value rows contiguous); the preconditioner accumulator
+ *    is [B, H, Dk] fp32.
+ *  - Element types: q, k, v, erase, write, write_key and out use io_dtype (fp32 or bf16);
+ *    beta, log_alpha, state and pc_h are always fp32.
+ *  - Memory: every pointer is a device pointer owned by the caller.  The library never
+ *    allocates, frees or keeps a pointer after the call returns, and needs no workspace.
+ *  - Execution: the work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the null stream) and the call returns without synchronising.
+ *  - Errors: arguments are validated on the host before anything is enqueued.  On
+ *    GDR_EINVAL or GDR_ENOTSUP nothing is launched and nothing is written.  A launch
+ *    failure returns GDR_EHIP.  gdr_last_error() gives a thread-local description of the
+ *    last non-OK return.  Faults inside a kernel surface at the caller's next
+ *    synchronisation, as usual in HIP.
+ *  - Determinism: no atomics; results are bitwise reproducible run to run.
+ *  - Threads: the library is stateless and reentrant.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_EINVAL = 1,   /* malformed descriptor, missing or overlapping pointer */
+  GDR_ENOTSUP = 2,  /* well-formed but outside what the library implements   */
+  GDR_EHIP = 3      /* a HIP runtime call failed                             */
+} gdr_status_t;
+
+enum { GDR_F32 = 0, GDR_BF16 = 1 };                                     /* io_dtype */
+enum { GDR_GAIN_SCALAR = 0, GDR_GAIN_CHANNEL = 1 };                     /* gain     */
+enum { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1 };                      /* decay    */
+enum { GDR_WKEY_SAME = 0, GDR_WKEY_DIAG_PRECOND = 1, GDR_WKEY_EXPLICIT = 2 }; /* wkey */
+enum { GDR_IMPL_AUTO = 0, GDR_IMPL_GENERIC = 1, GDR_IMPL_MFMA = 2 };    /* impl     */
+
+typedef struct gdr_desc {
+  uint32_t struct_size;   /* must equal sizeof(gdr_desc_t) (ABI guard)                    */
+  int32_t B, T, H;        /* batch, tokens in this call (1 for gdr_recurrent_step), heads */
+  int32_t Dk, Dv;         /* key and value head dims: 1 <= Dk <= 128, 1 <= Dv <= 512      */
+  int32_t chunk;          /* chunk size C in tokens: 16, 32 or 64 (ignored by the step)   */
+  int32_t io_dtype;       /* GDR_F32 | GDR_BF16                                            */
+  int32_t gain;           /* GDR_GAIN_*                                                    */
+  int32_t decay;          /* GDR_DECAY_*                                                   */
+  int32_t wkey;           /* GDR_WKEY_*                                                    */
+  int32_t neumann_order;  /* < 0: exact T = (I - A)^-1 by forward substitution;
+                             N >= 0: T restricted to the band i - j <= N (the masked
+                             truncated Neumann series sum_{n<=N} A^n, which equals the band
+                             of the exact inverse); N >= C - 1 reproduces the exact path
+                             bit for bit in fp32                                           */
+  int32_t impl;           /* GDR_IMPL_AUTO picks the fastest kernel for the shape;
+                             GENERIC forces the fp32 VALU kernel; MFMA forces the bf16
+                             matrix-core kernel (GDR_ENOTSUP if the shape is outside it)   */
+  float scale;            /* query scale (finite)                                          */
+  float pc_rho;           /* preconditioner decay rho, 0 < rho < 1 (wkey DIAG_PRECOND)     */
+  float pc_eps;           /* preconditioner epsilon, > 0                                   */
+  float pc_h0;            /* initial accumulator value when pc_h_in is NULL, >= 0          */
+  int64_t pc_t0;          /* tokens already absorbed into pc_h_in (>= 0)                   */
+} gdr_desc_t;
+
+typedef struct gdr_inputs {
+  const void *q, *k, *v;    /* io_dtype; required                                         */
+  const float *beta;        /* [B,T,H] fp32; required iff gain == SCALAR                   */
+  const float *log_alpha;   /* [B,T,H] fp32 (<= 0); required iff decay == SCALAR           */
+  const void *erase;        /* [B,T,H,Dk] io_dtype; required iff gain == CHANNEL           */
+  const void *write;        /* [B,T,H,Dv] io_dtype; required iff gain == CHANNEL           */
+  const void *write_key;    /* [B,T,H,Dk] io_dtype; required iff wkey == EXPLICIT          */
+  const float *pc_h_in;     /* [B,H,Dk] fp32 or NULL (=> every entry pc_h0); DIAG_PRECOND  */
+  float *pc_h_out;          /* [B,H,Dk] fp32 or NULL (=> not returned); DIAG_PRECOND.  For
+                               gdr_chunk_fwd it must not overlap pc_h_in; for
+                               gdr_recurrent_step it may equal pc_h_in (in-place update)   */
+} gdr_inputs_t;
+
+/*
+ * gdr_chunk_fwd -- chunk-parallel forward pass over T tokens.
+ *
+ * Per chunk of C tokens, with g the in-chunk inclusive cumulative sum of log_alpha and
+ * Gamma_ij = exp(g_i - g_j) (j <= i):
+ *     A = -tril_{-1}((E R^T) (.) Gamma),  T = (I - A)^-1  (exact, or its band i - j <= N)
+ *     W = T (e^g (.) E),  U = T V',  D = U - W S^T
+ *     O = (e^g (.) Q) S^T + (tril(Q R^T) (.) Gamma) D,   S <- e^{g_C} S + D^T (e^{g_C - g} (.) R)
+ * (chunk-wise form and T of the MatMul-only inversion summary, "Declaracao do Problema").
+ *
+ *   state_in   [B,H,Dv,Dk] fp32 initial state, or NULL for zeros.
+ *   out        [B,T,H,Dv] io_dtype; must not overlap any input.  May be NULL only if T == 0.
+ *   state_out  [B,H,Dv,Dk] fp32 final state, or NULL (not written).  May be the same
+ *              pointer as state_in (in-place); any other overlap is rejected.
+ *   stream     hipStream_t as void*.
+ * T == 0 is valid: state_out receives state_in (or zeros) and pc_h_out receives pc_h_in.
+ */
+gdr_status_t gdr_chunk_fwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
+                           const float *state_in, void *out, float *state_out,
+                           void *stream);
+
+/*
+ * gdr_recurrent_step -- one token for every stream, updating the state in place:
+ *     S <- alpha S;  d = v' - S e;  S <- S + d r^T;  o = S (scale q)
+ * (one online SGD step of the delta rule, Preconditioned DeltaNet summary section 1; the
+ * fixed-size state replaces a growing key-value cache, Gated DeltaNet-2 news item).
+ *
+ *   desc->T must be 1; inputs are laid out [B,1,H,D] (= [B,H,D]) and [B,1,H].
+ *   state      [B,H,Dv,Dk] fp32, read and overwritten.
+ *   out        [B,H,Dv] io_dtype; must not overlap any input or the state.
+ *   For DIAG_PRECOND the token's global index is pc_t0 + 1 and pc_h_out may equal pc_h_in.
+ */
+gdr_status_t gdr_recurrent_step(const gdr_desc_t *desc, const gdr_inputs_t *in,
+                                float *state, void *out, void *stream);
+
+/*
+ * gdr_validate -- the host-side argument check used by both entry points, exposed on its
+ * own.  Makes no HIP call.  `for_step` = 1 checks gdr_recurrent_step's contract (then
+ * state_out names the in-place state and state_in is ignored), 0 checks gdr_chunk_fwd's.
+ */
+gdr_status_t gdr_validate(const gdr_desc_t *desc, const gdr_inputs_t *in,
+                          const float *state_in, const void *out, const float *state_out,
+                          int for_step);
+
+/* Which kernel gdr_chunk_fwd would launch for this descriptor: GDR_IMPL_GENERIC or
+ * GDR_IMPL_MFMA, or a negative value if the descriptor is rejected.  No HIP call. */
+int gdr_chunk_fwd_impl(const gdr_desc_t *desc);
+
+const char *gdr_status_str(gdr_status_t status);  /* static string, never NULL          */
+const char *gdr_last_error(void);                 /* thread-local; "" after GDR_OK       */
+int gdr_abi_version(void);                        /* GDR_ABI_VERSION                     */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

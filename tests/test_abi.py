@@ -1,0 +1,177 @@
+"""The C ABI without a GPU: the library loads, exports what include/gdr.h declares, and
+rejects malformed calls on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_gated_delta_gdr_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+BASE = 1 << 32          # fake, well-aligned, disjoint "device addresses" (never dereferenced)
+MB = 1 << 26
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gdr_chunk_fwd", "gdr_recurrent_step", "gdr_validate", "gdr_status_str",
+            "gdr_last_error", "gdr_abi_version", "gdr_chunk_fwd_impl"} <= set(names)
+    L = G.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert G.gdr_abi_version() == 1
+    for s in (G.GDR_OK, G.GDR_EINVAL, G.GDR_ENOTSUP, G.GDR_EHIP):
+        assert G.gdr_status_str(s).startswith("GDR_")
+    assert "UNKNOWN" in G.gdr_status_str(42)
+
+
+def test_struct_layout_matches_header():
+    # int32 fields and an int64 at the end: 4 + 12*4 + 4*4 + 8 = 76 -> padded to 80
+    assert ctypes.sizeof(G.gdr_desc_t) == 80
+    assert ctypes.sizeof(G.gdr_inputs_t) == 10 * 8
+
+
+def desc(**kw):
+    d = dict(B=2, T=100, H=3, Dk=64, Dv=32, chunk=64, io_dtype=G.GDR_BF16)
+    d.update(kw)
+    return G.make_desc(**d)
+
+
+def ptrs(n=10):
+    return [BASE + i * MB for i in range(n)]
+
+
+def inputs(**kw):
+    p = ptrs()
+    d = dict(q=p[0], k=p[1], v=p[2], beta=p[3])
+    d.update(kw)
+    return G.gdr_inputs_t(**d)
+
+
+OUT, SIN, SOUT = BASE + 20 * MB, BASE + 21 * MB, BASE + 22 * MB
+
+
+def check(expect, d=None, ins=None, state_in=None, out=OUT, state_out=SOUT, for_step=False):
+    d = d or desc()
+    ins = ins or inputs()
+    st = G.gdr_validate(d, ins, state_in, out, state_out, for_step)
+    assert st == expect, (st, G.gdr_last_error())
+    if expect != G.GDR_OK:
+        assert G.gdr_last_error() != ""
+    return st
+
+
+def test_valid_call_validates():
+    check(G.GDR_OK)
+    check(G.GDR_OK, state_in=SIN)
+    check(G.GDR_OK, state_in=SOUT)                 # in-place state
+    check(G.GDR_OK, state_out=None)
+    check(G.GDR_OK, d=desc(T=0), ins=inputs(q=None, k=None, v=None, beta=None), out=None)
+    assert G.gdr_last_error() == ""
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 12, G.GDR_EINVAL),
+    ("B", 0, G.GDR_EINVAL), ("H", 0, G.GDR_EINVAL), ("T", -1, G.GDR_EINVAL),
+    ("Dk", 0, G.GDR_EINVAL), ("Dv", 0, G.GDR_EINVAL),
+    ("Dk", 256, G.GDR_ENOTSUP), ("Dv", 1024, G.GDR_ENOTSUP),
+    ("chunk", 0, G.GDR_EINVAL), ("chunk", 128, G.GDR_ENOTSUP), ("chunk", 48, G.GDR_ENOTSUP),
+    ("io_dtype", 7, G.GDR_EINVAL), ("gain", 5, G.GDR_EINVAL), ("decay", 3, G.GDR_EINVAL),
+    ("wkey", 9, G.GDR_EINVAL), ("impl", 4, G.GDR_EINVAL),
+    ("scale", float("nan"), G.GDR_EINVAL), ("scale", float("inf"), G.GDR_EINVAL),
+])
+def test_bad_descriptor(field, value, status):
+    d = desc()
+    setattr(d, field, value)
+    check(status, d=d)
+
+
+def test_huge_problem_rejected():
+    check(G.GDR_ENOTSUP, d=desc(B=1 << 20, T=1 << 20, H=1 << 10))
+
+
+def test_pointer_consistency_with_variant():
+    p = ptrs()
+    check(G.GDR_EINVAL, ins=inputs(beta=None))                                   # gain scalar, no beta
+    check(G.GDR_EINVAL, ins=inputs(q=None))
+    check(G.GDR_EINVAL, ins=inputs(erase=p[5], write=p[6]))                     # gates with scalar gain
+    check(G.GDR_EINVAL, d=desc(gain=G.GDR_GAIN_CHANNEL), ins=inputs(erase=p[5], write=p[6]))  # beta too
+    check(G.GDR_OK, d=desc(gain=G.GDR_GAIN_CHANNEL), ins=inputs(beta=None, erase=p[5], write=p[6]))
+    check(G.GDR_EINVAL, d=desc(gain=G.GDR_GAIN_CHANNEL), ins=inputs(beta=None, erase=p[5]))
+    check(G.GDR_EINVAL, d=desc(decay=G.GDR_DECAY_SCALAR))                       # no log_alpha
+    check(G.GDR_OK, d=desc(decay=G.GDR_DECAY_SCALAR), ins=inputs(log_alpha=p[4]))
+    check(G.GDR_EINVAL, ins=inputs(log_alpha=p[4]))                             # log_alpha, no decay
+    check(G.GDR_EINVAL, d=desc(wkey=G.GDR_WKEY_EXPLICIT))
+    check(G.GDR_OK, d=desc(wkey=G.GDR_WKEY_EXPLICIT), ins=inputs(write_key=p[7]))
+    check(G.GDR_EINVAL, ins=inputs(write_key=p[7]))
+    check(G.GDR_EINVAL, ins=inputs(pc_h_in=p[8]))                               # pc_h without precond
+    check(G.GDR_OK, d=desc(wkey=G.GDR_WKEY_DIAG_PRECOND), ins=inputs(pc_h_in=p[8], pc_h_out=p[9]))
+    check(G.GDR_EINVAL, out=None)
+
+
+@pytest.mark.parametrize("field,value", [("pc_rho", 1.0), ("pc_rho", 0.0), ("pc_eps", 0.0),
+                                         ("pc_h0", -1.0), ("pc_t0", -3)])
+def test_bad_precond_constants(field, value):
+    d = desc(wkey=G.GDR_WKEY_DIAG_PRECOND)
+    setattr(d, field, value)
+    check(G.GDR_EINVAL, d=d)
+
+
+def test_overlaps_rejected():
+    p = ptrs()
+    check(G.GDR_EINVAL, out=p[0])                                  # out == q
+    check(G.GDR_EINVAL, out=p[2] + 64)                             # out inside v
+    check(G.GDR_EINVAL, state_out=p[1])                            # state over k
+    check(G.GDR_EINVAL, state_in=SOUT + 1024)                      # partial state overlap
+    check(G.GDR_EINVAL, state_out=OUT)                             # state over out
+    d = desc(wkey=G.GDR_WKEY_DIAG_PRECOND)
+    check(G.GDR_EINVAL, d=d, ins=inputs(pc_h_in=p[8], pc_h_out=p[8]))   # chunk_fwd: no in-place h
+    # the step allows the in-place accumulator
+    ds = desc(T=1, wkey=G.GDR_WKEY_DIAG_PRECOND)
+    check(G.GDR_OK, d=ds, ins=inputs(pc_h_in=p[8], pc_h_out=p[8]), for_step=True)
+
+
+def test_misaligned_rejected():
+    p = ptrs()
+    check(G.GDR_EINVAL, ins=inputs(q=p[0] + 1))
+    check(G.GDR_EINVAL, ins=inputs(beta=p[3] + 2))
+    check(G.GDR_OK, d=desc(io_dtype=G.GDR_BF16), ins=inputs(q=p[0] + 2))
+    check(G.GDR_EINVAL, d=desc(io_dtype=G.GDR_F32), ins=inputs(q=p[0] + 2))
+    check(G.GDR_EINVAL, state_out=SOUT + 2)
+
+
+def test_step_contract():
+    check(G.GDR_OK, d=desc(T=1), for_step=True)
+    check(G.GDR_EINVAL, d=desc(T=2), for_step=True)
+    check(G.GDR_EINVAL, d=desc(T=1), state_out=None, for_step=True)
+    check(G.GDR_EINVAL, d=desc(T=1), out=None, for_step=True)
+
+
+def test_entry_points_reject_before_launch():
+    """With an invalid descriptor the entry points return before any HIP call, so they can
+    be called on a host without a GPU."""
+    L = G.lib()
+    d = desc(B=0)
+    ins = inputs()
+    assert L.gdr_chunk_fwd(ctypes.byref(d), ctypes.byref(ins), None, OUT, SOUT, None) == G.GDR_EINVAL
+    assert "B = 0" in G.gdr_last_error()
+    d = desc(T=1, Dk=300)
+    assert L.gdr_recurrent_step(ctypes.byref(d), ctypes.byref(ins), SOUT, OUT, None) == G.GDR_ENOTSUP
+    assert L.gdr_chunk_fwd(None, None, None, None, None, None) == G.GDR_EINVAL
+
+
+def test_impl_choice():
+    assert G.gdr_chunk_fwd_impl(desc(impl=G.GDR_IMPL_GENERIC)) == G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(desc(io_dtype=G.GDR_F32)) == G.GDR_IMPL_GENERIC

@@ -1,0 +1,336 @@
+"""GPU parity of gdr_chunk_fwd and gdr_recurrent_step against the fp64 CPU oracle.
+
+Every test prints the case it runs (workload, shape, seed, entry point) before touching
+the GPU.  Bounds: rel-L2 <= 1e-4 for the fp32 path, <= 2e-2 for the bf16 path.
+"""
+import numpy as np
+import pytest
+
+import gdr_synth as gs
+import oracle as O
+from _gpu_util import TOL_BF16, TOL_F32, dev, host, precond_opts, run_chunk, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def tol(s):
+    return TOL_F32 if s.dtype == "f32" else TOL_BF16
+
+
+def small(variant, dtype="f32", **kw):
+    base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "pdn": "pdn", "explicit": "gdn",
+            "gdn2_decay": "gdn2", "pdn_decay": "pdn"}[variant]
+    over = dict(B=2, H=3, T=150, Dk=64, Dv=48, dtype=dtype, seed=11)
+    over.update(kw)
+    if variant == "explicit":
+        over["wkey"] = "explicit"
+    if variant.endswith("_decay"):
+        over["decay"] = "scalar"
+    return gs.spec(base, **over)
+
+
+# ---------------------------------------------------------------------------------
+# The fp32 path
+# ---------------------------------------------------------------------------------
+
+def test_plain_fp32_workload():
+    """Plain delta rule, B1 H1 T256 d64 fp32, C64: exact T within 1e-4 of the oracle."""
+    s = gs.spec("plain")
+    announce(f"plain f32 {s}")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.recurrent(x)
+    o, S, _ = run_chunk(s, x)
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(S), S_ref) <= TOL_F32
+
+
+def test_full_neumann_is_bitwise_exact_fp32():
+    """N >= C - 1 runs the same computation as the exact path: bit-identical in fp32."""
+    import torch
+    s = gs.spec("plain")
+    announce("plain f32 neumann N=63,100 vs exact, bitwise")
+    x = gs.make_inputs(s)
+    o, S, _ = run_chunk(s, x)
+    for N in (63, 100):
+        oN, SN, _ = run_chunk(s, x, neumann_order=N)
+        assert torch.equal(oN, o) and torch.equal(SN, S), N
+    o3, _, _ = run_chunk(s, x, neumann_order=3)
+    assert not torch.equal(o3, o)
+
+
+@pytest.mark.parametrize("N", [0, 1, 3, 7])
+def test_band_fp32_matches_literal_neumann(N):
+    """Band-N T on the GPU vs the oracle's literal sum_{n<=N} A^n with the diagonal mask."""
+    s = gs.spec("plain")
+    announce(f"plain f32 band N={N}")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=("neumann", N))
+    o, S, _ = run_chunk(s, x, neumann_order=N)
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(S), S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay"])
+@pytest.mark.parametrize("chunk,Dk,Dv,T", [(64, 64, 48, 150), (16, 32, 16, 37), (32, 128, 128, 200),
+                                           (64, 128, 20, 64)])
+def test_variants_fp32(variant, chunk, Dk, Dv, T):
+    """Every variant, ragged tails, non-zero state, query scale: fp32 within 1e-4."""
+    s = small(variant, "f32", Dk=Dk, Dv=Dv, T=T, chunk=chunk)
+    announce(f"{variant} f32 C={chunk} Dk={Dk} Dv={Dv} T={T}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(5)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    pc = precond_opts(s)
+    h_in = None
+    if pc is not None:
+        h_in = (1.0 + rng.random((s.B, s.H, s.Dk))).astype(np.float32)
+        pc = dict(pc, h_init=h_in.astype(np.float64), t0=9)
+    o_ref, S_ref, h_ref = O.recurrent(x, state0=S0.astype(np.float64), precond=pc, scale=0.8)
+    o, S, h = run_chunk(s, x, state_in=S0, pc_h_in=h_in, pc_t0=9 if pc else 0, scale=0.8)
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(S), S_ref) <= TOL_F32
+    if pc is not None:
+        assert O.rel_l2(host(h), h_ref) <= 1e-6
+
+
+def test_exact_preconditioner_ridge_regression_fp32():
+    """Explicit write key G_t^-1 k_t, beta = 1: outputs are the ridge-regression predictions."""
+    T, Dk, Dv, lam = 96, 16, 16, 0.5
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((T, Dk)); k = rng.standard_normal((T, Dk)); v = rng.standard_normal((T, Dv))
+    G = lam * np.eye(Dk); M = np.zeros((Dv, Dk)); wk = np.empty((T, Dk)); ref = np.empty((T, Dv))
+    for t in range(T):
+        G = G + np.outer(k[t], k[t]); wk[t] = np.linalg.solve(G, k[t])
+        M = M + np.outer(v[t], k[t]); ref[t] = np.linalg.solve(G.T, M.T).T @ q[t]
+    f = lambda a: a.astype(np.float32)[None, :, None]
+    x = {"q": f(q), "k": f(k), "v": f(v), "beta": np.ones((1, T, 1), np.float32), "write_key": f(wk)}
+    s = gs.spec("gdn", B=1, H=1, T=T, Dk=Dk, Dv=Dv, dtype="f32", decay="none", wkey="explicit")
+    announce("ridge regression f32")
+    o, _, _ = run_chunk(s, x, chunk=32)
+    assert O.rel_l2(host(o)[0, :, 0], ref) <= 1e-3   # fp32 inputs of an ill-conditioned solve
+
+
+# ---------------------------------------------------------------------------------
+# Edge cases, state I/O, determinism, isolation
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65])
+def test_lengths_edge_cases(T):
+    import torch
+    s = small("gdn", "f32", T=max(T, 1), B=1, H=2)
+    announce(f"gdn f32 T={T}")
+    x = gs.make_inputs(s)
+    x = {k_: v_[:, :T] for k_, v_ in x.items()}
+    rng = np.random.default_rng(1)
+    S0 = rng.standard_normal((s.B, s.H, s.Dv, s.Dk)).astype(np.float32)
+    s = s.replace(T=T)
+    o, S, _ = run_chunk(s, x, state_in=S0)
+    if T == 0:
+        assert o.numel() == 0
+        assert torch.equal(S.cpu(), torch.from_numpy(S0))
+        return
+    o_ref, S_ref, _ = O.recurrent(x, state0=S0.astype(np.float64))
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(S), S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype,impl", [("f32", "generic"), ("bf16", "auto")])
+def test_split_sequence_resume(dtype, impl):
+    """Running T tokens at once == running a prefix, then the rest from its state (and
+    preconditioner accumulator): bitwise when the cut is on a chunk boundary."""
+    import torch
+    s = small("pdn_decay", dtype, T=256, Dk=128, Dv=128, B=1, H=2)
+    announce(f"split resume pdn_decay {dtype} {impl}")
+    x = gs.make_inputs(s)
+    o, S, h = run_chunk(s, x, impl=impl)
+    cut = 128
+    xa = {k_: v_[:, :cut] for k_, v_ in x.items()}
+    xb = {k_: v_[:, cut:] for k_, v_ in x.items()}
+    oa, Sa, ha = run_chunk(s.replace(T=cut), xa, impl=impl)
+    ob, Sb, hb = run_chunk(s.replace(T=256 - cut), xb, state_in=host(Sa).astype(np.float32),
+                           pc_h_in=host(ha).astype(np.float32), pc_t0=cut, impl=impl)
+    assert torch.equal(torch.cat([oa, ob], dim=1), o)
+    assert torch.equal(Sb, S) and torch.equal(hb, h)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic(dtype):
+    import torch
+    s = small("gdn", dtype, Dk=128, Dv=128, T=300)
+    announce(f"determinism gdn {dtype}")
+    x = gs.make_inputs(s)
+    o1, S1, _ = run_chunk(s, x)
+    o2, S2, _ = run_chunk(s, x)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_stays_in_its_head(dtype):
+    s = small("gdn", dtype, Dk=128, Dv=128, T=130, B=2, H=3)
+    announce(f"head isolation gdn {dtype}")
+    x = gs.make_inputs(s)
+    x["v"] = x["v"].copy()
+    x["v"][1, 70, 2, 5] = np.nan
+    o, S, _ = run_chunk(s, x)
+    o, S = host(o), host(S)
+    bad = np.zeros((s.B, s.H), bool)
+    bad[1, 2] = True
+    for b in range(s.B):
+        for h in range(s.H):
+            if bad[b, h]:
+                assert np.isnan(o[b, 70:, h]).any()
+                assert np.isfinite(o[b, :64, h]).all()    # chunks before the NaN are clean
+            else:
+                assert np.isfinite(o[b, :, h]).all() and np.isfinite(S[b, h]).all()
+
+
+# ---------------------------------------------------------------------------------
+# The bf16 path
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "pdn", "explicit", "plain"])
+@pytest.mark.parametrize("impl", ["generic", "auto"])
+def test_variants_bf16_small(variant, impl):
+    s = small(variant, "bf16", Dk=128, Dv=128, T=200, B=2, H=2)
+    announce(f"{variant} bf16 {impl} T=200")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(2)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    o_ref, S_ref, _ = O.recurrent(x, state0=S0.astype(np.float64), precond=precond_opts(s))
+    o, S, _ = run_chunk(s, x, state_in=S0, impl=impl)
+    assert O.rel_l2(host(o), o_ref) <= TOL_BF16
+    assert O.rel_l2(host(S), S_ref) <= TOL_BF16
+
+
+def _sampled(s, x, o, S, streams, precond=None, t_mode=None):
+    """Oracle on a few (b, h) streams only; compare those streams."""
+    if t_mode is None:
+        o_ref, S_ref, _ = O.recurrent(x, precond=precond, streams=streams)
+    else:
+        o_ref, S_ref, _ = O.chunked(x, chunk=s.chunk, t_mode=t_mode, precond=precond, streams=streams)
+    o, S = host(o), host(S)
+    errs = []
+    for (b, h) in streams:
+        errs.append((O.rel_l2(o[b, :, h], o_ref[b, :, h]), O.rel_l2(S[b, h], S_ref[b, h])))
+    return errs
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["gdn", "gdn2", "pdn"])
+def test_full_size_workloads_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration; the oracle checks a
+    sample of streams end to end."""
+    s = gs.spec(name)
+    announce(f"full size {name} {s}")
+    x = gs.make_inputs(s)
+    o, S, _ = run_chunk(s, x)
+    streams = [(0, 0), (s.B - 1, s.H - 1), (s.B // 2, 7)]
+    for eo, eS in _sampled(s, x, o, S, streams, precond=precond_opts(s)):
+        print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+@pytest.mark.timeout(300)
+def test_precond_band3_vs_exact():
+    """Preconditioned workload with exact T and with band N = 3: each vs its oracle, and
+    the error between the two reported."""
+    s = gs.spec("pdn")
+    announce(f"pdn exact vs band3 {s}")
+    x = gs.make_inputs(s)
+    oe, Se, _ = run_chunk(s, x)
+    ob, Sb, _ = run_chunk(s, x, neumann_order=3)
+    streams = [(0, 0), (3, 15)]
+    for eo, eS in _sampled(s, x, ob, Sb, streams, precond=precond_opts(s), t_mode=("neumann", 3)):
+        print(f"  band3 vs oracle band3: out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+    gpu_gap = O.rel_l2(host(ob), host(oe))
+    print(f"  rel-L2(exact, band3) on the GPU, whole output: {gpu_gap:.3e}", flush=True)
+    assert gpu_gap > 1e-2   # the band approximation is far from exact on this data
+
+
+@pytest.mark.timeout(600)
+def test_long_prefill_sampled():
+    s = gs.spec("long")
+    announce(f"long prefill {s}")
+    x = gs.make_inputs(s)
+    o, S, _ = run_chunk(s, x)
+    for eo, eS in _sampled(s, x, o, S, [(0, 0), (0, 31)]):
+        print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------------
+# Decode step
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant,dtype,Dk", [("gdn", "bf16", 128), ("gdn", "f32", 64), ("gdn2", "bf16", 128),
+                                              ("pdn", "bf16", 128), ("explicit", "f32", 40),
+                                              ("gdn", "f32", 100)])
+def test_steps_equal_chunk_fwd_and_oracle(variant, dtype, Dk):
+    """n x gdr_recurrent_step == oracle recurrence == gdr_chunk_fwd over the same tokens."""
+    import torch
+    import chunked_gated_delta_gdr_amd as G
+    s = small(variant, dtype, T=20, Dk=Dk, Dv=Dk, B=3, H=2)
+    announce(f"steps {variant} {dtype} Dk={Dk}")
+    x = gs.make_inputs(s)
+    pc = precond_opts(s)
+    o_ref, S_ref, h_ref = O.recurrent(x, precond=pc)
+    o_c, S_c, _ = run_chunk(s, x, chunk=16)
+    io = torch_dtype(dtype)
+    state = torch.zeros((s.B, s.H, s.Dv, s.Dk), dtype=torch.float32, device="cuda")
+    h = torch.full((s.B, s.H, s.Dk), s.pc_h0, dtype=torch.float32, device="cuda") if pc else None
+    outs = []
+    for t in range(s.T):
+        xt = {k_: v_[:, t] for k_, v_ in x.items()}
+        o_t, _ = G.gdr_recurrent_step(
+            dev(xt["q"], io), dev(xt["k"], io), dev(xt["v"], io), state,
+            beta=dev(xt.get("beta"), torch.float32), log_alpha=dev(xt.get("log_alpha"), torch.float32),
+            erase=dev(xt.get("erase"), io), write=dev(xt.get("write"), io),
+            write_key=dev(xt.get("write_key"), io), precond=pc is not None, pc_h_in=h, pc_h_out=h,
+            pc_t0=t)
+        outs.append(o_t)
+    torch.cuda.synchronize()
+    o_s = torch.stack(outs, dim=1)
+    t_ = tol(s)
+    assert O.rel_l2(host(o_s), o_ref) <= t_
+    assert O.rel_l2(host(state), S_ref) <= t_
+    assert O.rel_l2(host(o_s), host(o_c)) <= t_
+    if pc:
+        assert O.rel_l2(host(h), h_ref) <= 1e-6
+
+
+@pytest.mark.timeout(600)
+def test_long_decode_batch64():
+    """Long-context workload: prefill B1 H32 T32768, replicate its final state to batch 64,
+    run 1024 decode steps with inputs pre-staged on the device; the oracle checks batch
+    rows 0 and 63 (all heads) over every step, decode-only from the GPU's state."""
+    import torch
+    import chunked_gated_delta_gdr_amd as G
+    s = gs.spec("long")
+    announce(f"long decode {s.decode_batch}x{s.decode_steps}")
+    x = gs.make_inputs(s)
+    _, S, _ = run_chunk(s, x)
+    del x
+    Bd, steps = s.decode_batch, s.decode_steps
+    state = S.expand(Bd, -1, -1, -1).contiguous()
+    S0 = host(state[[0, Bd - 1]])
+    bf = torch.bfloat16
+    ins = [gs.make_decode_inputs(s, t) for t in range(steps)]
+    dq = [(dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf), dev(d["beta"], torch.float32),
+           dev(d["log_alpha"], torch.float32)) for d in ins]
+    outs = torch.empty((steps, Bd, s.H, s.Dv), dtype=bf, device="cuda")
+    for t in range(steps):
+        q, k, v, be, la = dq[t]
+        G.gdr_recurrent_step(q, k, v, state, beta=be, log_alpha=la, out=outs[t])
+    torch.cuda.synchronize()
+    rows = [0, Bd - 1]
+    xo = {key: np.stack([d[key][rows] for d in ins], axis=1) for key in ("q", "k", "v", "beta", "log_alpha")}
+    o_ref, S_ref, _ = O.recurrent(xo, state0=S0)
+    e_o = O.rel_l2(host(outs[:, rows].transpose(0, 1)), o_ref)
+    e_S = O.rel_l2(host(state[rows]), S_ref)
+    print(f"  decode rel-L2 out {e_o:.3e} state {e_S:.3e}", flush=True)
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
