@@ -42,12 +42,16 @@ __device__ __forceinline__ float ld_f(const uint16_t *p, long long i) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// two values packed low | high << 16
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ void st_f(float *p, long long i, float x) { p[i] = x; }
 __device__ __forceinline__ void st_f(uint16_t *p, long long i, float x) { p[i] = f32_to_bf16_bits(x); }

@@ -175,3 +175,7 @@ def test_entry_points_reject_before_launch():
 def test_impl_choice():
     assert G.gdr_chunk_fwd_impl(desc(impl=G.GDR_IMPL_GENERIC)) == G.GDR_IMPL_GENERIC
     assert G.gdr_chunk_fwd_impl(desc(io_dtype=G.GDR_F32)) == G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128)) == G.GDR_IMPL_MFMA
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=32)) == G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, impl=G.GDR_IMPL_GENERIC)) == G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(desc(Dk=64, impl=G.GDR_IMPL_MFMA)) == -1

@@ -334,3 +334,83 @@ def test_long_decode_batch64():
     e_S = O.rel_l2(host(state[rows]), S_ref)
     print(f"  decode rel-L2 out {e_o:.3e} state {e_S:.3e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------------
+# The bf16 matrix-core kernel, forced (impl="mfma")
+# ---------------------------------------------------------------------------------
+
+MFMA_VARIANTS = ["gdn", "plain", "gdn2", "gdn2_decay", "pdn", "pdn_decay", "explicit"]
+
+
+@pytest.mark.parametrize("variant", MFMA_VARIANTS)
+@pytest.mark.parametrize("B,H,T", [(2, 2, 200), (4, 16, 130)])   # value tiles of 16 and 32 rows
+def test_mfma_variants(variant, B, H, T):
+    s = small(variant, "bf16", Dk=128, Dv=128, T=T, B=B, H=H)
+    announce(f"mfma {variant} B={B} H={H} T={T}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(3)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    pc = precond_opts(s)
+    h_in = None
+    if pc is not None:
+        h_in = (1.0 + rng.random((s.B, s.H, s.Dk))).astype(np.float32)
+        pc = dict(pc, h_init=h_in.astype(np.float64), t0=70)
+    streams = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    o_ref, S_ref, h_ref = O.recurrent(x, state0=S0.astype(np.float64), precond=pc, scale=0.9, streams=streams)
+    o, S, h = run_chunk(s, x, state_in=S0, pc_h_in=h_in, pc_t0=70 if pc else 0, scale=0.9, impl="mfma")
+    o, S = host(o), host(S)
+    for (b, hh) in streams:
+        eo = O.rel_l2(o[b, :, hh], o_ref[b, :, hh])
+        eS = O.rel_l2(S[b, hh], S_ref[b, hh])
+        print(f"  ({b},{hh}) rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+    if pc is not None:
+        hh = host(h)
+        for (b, k_) in streams:
+            assert O.rel_l2(hh[b, k_], h_ref[b, k_]) <= 1e-5
+
+
+@pytest.mark.parametrize("N", [0, 3, 15, 20, 63])
+def test_mfma_band(N):
+    """Band-limited T on the matrix-core kernel vs the oracle's literal masked Neumann sum."""
+    s = small("pdn", "bf16", Dk=128, Dv=128, T=192, B=2, H=2)
+    announce(f"mfma band N={N}")
+    x = gs.make_inputs(s)
+    pc = precond_opts(s)
+    mode = "exact" if N >= 63 else ("neumann", N)
+    o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=mode, precond=pc)
+    o, S, _ = run_chunk(s, x, neumann_order=N, impl="mfma")
+    eo, eS = O.rel_l2(host(o), o_ref), O.rel_l2(host(S), S_ref)
+    print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_mfma_matches_generic_kernel():
+    """The two kernels agree with each other (bf16 inputs; fp32 vs bf16-MFMA internals)."""
+    s = small("gdn", "bf16", Dk=128, Dv=128, T=333, B=2, H=4)
+    announce("mfma vs generic gdn")
+    x = gs.make_inputs(s)
+    o1, S1, _ = run_chunk(s, x, impl="mfma")
+    o2, S2, _ = run_chunk(s, x, impl="generic")
+    assert O.rel_l2(host(o1), host(o2)) <= TOL_BF16
+    assert O.rel_l2(host(S1), host(S2)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [0, 1, 64, 65, 127])
+def test_mfma_lengths(T):
+    import torch
+    s = small("gdn", "bf16", Dk=128, Dv=128, T=max(T, 1), B=1, H=2)
+    announce(f"mfma gdn T={T}")
+    x = gs.make_inputs(s)
+    x = {k_: v_[:, :T] for k_, v_ in x.items()}
+    rng = np.random.default_rng(4)
+    S0 = rng.standard_normal((s.B, s.H, s.Dv, s.Dk)).astype(np.float32)
+    s = s.replace(T=T)
+    o, S, _ = run_chunk(s, x, state_in=S0, impl="mfma")
+    if T == 0:
+        assert torch.equal(S.cpu(), torch.from_numpy(S0))
+        return
+    o_ref, S_ref, _ = O.recurrent(x, state0=S0.astype(np.float64))
+    assert O.rel_l2(host(o), o_ref) <= TOL_BF16
+    assert O.rel_l2(host(S), S_ref) <= TOL_BF16
