@@ -1,36 +1,45 @@
 // Fused chunk-parallel gated delta-rule forward on the gfx950 matrix cores (bf16 in,
 // fp32 accumulate, fp32 state), for Dk = Dv = 128 and chunks of 64 tokens.
 //
-// One workgroup (8 wave64s) owns one (batch, head, value tile of BV state rows) and
-// walks the sequence chunk by chunk.  The state tile S (BV x 128, fp32) lives in MFMA
-// accumulator registers for the whole sequence; a bf16 copy in LDS feeds the products
-// that read it.  Nothing but the inputs, the output and the final state touches HBM.
-//
 // Per chunk of 64 tokens (chunk-wise form of the MatMul-only inversion summary,
-// "Declaracao do Problema"; the WY correction U - W S^T is evaluated here as
-// T (V' - (e^g (.) E) S^T), the same product regrouped so that only one 64 x BV
-// right-hand side meets T):
-//   g       inclusive cumulative sum of log alpha (kept in log2 units for exp2)
-//   L       = tril_{-1}((E R^T) (.) Gamma)                        [MFMA, fp32 in LDS]
-//   T       = (I + L)^-1 = (I - A)^-1                             [see below]
-//   P       = tril(Q R^T) (.) Gamma                               [MFMA]
-//   X       = V' - (e^g (.) E) S^T                                [MFMA + epilogue]
-//   D       = T X                                                 [MFMA]
-//   O       = scale ((e^g (.) Q) S^T + P D)                       [MFMA]
-//   S       <- e^{g_C} S + (e^{g_C - g} (.) D)^T R                [MFMA into the accumulators]
-// T is built blockwise: the four 16 x 16 diagonal blocks by forward substitution on the
-// vector ALUs (one lane per column), then two merge levels on the matrix cores using
-// (I + L)^-1 = [[T_a, 0], [-T_b L_ba T_a, T_b]].  With a band limit N <= 15 (the
-// truncated Neumann series with its diagonal mask, same summary, Metodologia 1-2, whose
-// band equals the band of the exact inverse by Lemma 3.1) each lane forms its column's N
-// sub-diagonal entries by the band-limited substitution instead; a larger N masks the
-// exact inverse.
+// "Declaracao do Problema"; the WY correction U - W S^T is evaluated as T (V' - e^g E S^T),
+// the same product regrouped so only one 64 x 16 right-hand side per value block meets T):
+//   g   inclusive cumulative sum of log alpha (log2 units)      Gamma_ij = 2^(g_i - g_j), j <= i
+//   A   = -tril_{-1}((E R^T) (.) Gamma),  T = (I - A)^-1        (16 x 16 blocks, see below)
+//   P   = tril(Q R^T) (.) Gamma
+//   X   = V' - (e^g (.) E) S^T
+//   D   = T X
+//   O   = scale ((e^g (.) Q) S^T + P D)
+//   S  <- e^{g_C} S + (e^{g_C - g} (.) D)^T R
 //
-// MFMA operand layouts (v_mfma_f32_16x16x32_bf16): lane l supplies row (l % 16) of A
-// and column (l % 16) of B, each as 8 consecutive K values starting at 8 * (l / 16);
-// the 16 x 16 fp32 result sits in lane l as rows 4 * (l / 16) + r, column l % 16.
-// Products that contract over tokens therefore read operands stored token-contiguous
-// (R^T, X^T, D^T), which the loaders and epilogues write directly.
+// Work split inside one workgroup (8 wave64s; one workgroup per batch, head and value tile
+// of BV = 16 or 32 state rows):
+//  * value waves (BV / 16 of them) each own 16 state rows.  The transposed state S^T
+//    (128 x 16, fp32) lives in that wave's MFMA accumulators for the whole sequence, and
+//    every S-dependent product of a chunk is chained through registers: an accumulator
+//    tile converted to bf16 is directly the B operand of the next product.  Only these
+//    waves store to HBM.
+//  * helper waves prepare chunk c + 1 while the value waves run chunk c: they stage the
+//    next inputs into LDS from registers prefetched a chunk earlier (only helpers load
+//    from HBM), build T and P.  T is formed blockwise: each 16 x 16 diagonal block
+//    D = (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) (N strictly lower, so N^16 = 0)
+//    on the matrix cores, then T_10 = D_1 A_10 D_0 (same for T_32), then
+//    T_ba = T_b A_ba T_a for the lower-left 32 x 32 quadrant.
+//  * With a band limit N >= 0 (the truncated Neumann series with its diagonal mask, same
+//    summary, Metodologia 1-2) entries with i - j > N are dropped when T is written; by
+//    Lemma 3.1 the band of every product above depends only on the bands of its factors,
+//    so the stored band equals the band of the exact inverse.
+//  Two barriers per chunk (three with the diagonal preconditioner, whose write keys need a
+//  scan over the chunk before A and P can use them).
+//
+// MFMA operand conventions: v_mfma_f32_16x16x32_bf16 takes in lane l row (l % 16) of A and
+// column (l % 16) of B with 8 K-slots each; v_mfma_f32_16x16x16bf16_1k takes 4 K-slots
+// (K = 4 (l / 16) + i); the 16 x 16 fp32 result holds rows 4 (l / 16) + r, column l % 16.
+// An accumulator tile is therefore the B-operand layout of its K = 16 rows.  For K = 32
+// products fed from two accumulator tiles the K-slot order is "split": slots 0..3 are
+// rows 4 (l / 16) + r of the first tile, slots 4..7 those of the second, and the A
+// operand is gathered from LDS in the same order.  A product X Y whose factors are both
+// accumulators needs acc(X^T) and acc(Y); transposed copies are computed where needed.
 #include "common.h"
 
 namespace gdr {
@@ -40,74 +49,76 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int kC = 64;            // chunk
-constexpr int kD = 128;           // Dk = Dv
-constexpr int kNW = 8;            // waves per workgroup
-constexpr int kNT = kNW * 64;     // threads
-constexpr int kLdr = kD + 8;      // bf16 row stride of [64][128] tiles (272 B)
-constexpr int kLdc = kC + 8;      // bf16 row stride of [*][64] tiles (144 B)
-constexpr int kLda = kC + 4;      // fp32 row stride of L
+constexpr int kC = 64;          // chunk
+constexpr int kD = 128;         // Dk = Dv
+constexpr int kNW = 8;          // waves per workgroup
+constexpr int kNT = kNW * 64;   // threads
+constexpr int kLdc = kC + 8;    // padded bf16 row stride of [*][64] tiles (T, P, V'^T)
+constexpr int kLdl = 32 + 8;    // bf16 row stride of the 32 x 32 block A_ba
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum : int { kWkSame = 0, kWkPrecond = 1, kWkExplicit = 2 };
 
+// XOR-swizzled row-major bf16 layouts (16-byte granules), conflict-free for MFMA reads
+__device__ __forceinline__ int sw128(int row, int col) {
+  return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+}
+__device__ __forceinline__ int sw64(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
+}
+
 template <int BV, bool CHAN, int WK>
 struct __align__(16) Smem {
-  uint16_t q[kC][kLdr];
-  uint16_t k[kC][kLdr];
-  uint16_t r[WK != kWkSame ? kC : 1][kLdr];   // write key when it differs from k
-  uint16_t e[CHAN ? kC : 1][kLdr];            // erase key b (.) k (channel gain)
-  uint16_t rt[kD][kLdc];                      // R^T
-  uint16_t t[kC][kLdc];                       // T (bf16)
-  uint16_t p[kC][kLdc];                       // P (bf16)
-  uint16_t s[BV][kLdr];                       // state copy (bf16)
-  uint16_t xt[BV][kLdc];                      // X^T
-  uint16_t dt[BV][kLdc];                      // D^T
-  uint16_t dt2[BV][kLdc];                     // (e^{g_C - g} D)^T
-  float a[kC][kLda];                          // L (fp32)
-  float vp[kC][BV + 4];                       // V' tile (fp32)
-  float o1[kC][BV + 4];                       // e^g (Q S^T) (fp32)
-  float g2[kC], eg[kC], wd[kC], cy[kC], ic[kC], beta[kC];
+  uint16_t q[kC * kD];                                     // Q (one buffer)
+  uint16_t k[2][kC * kD];                                  // K
+  uint16_t e[CHAN ? 2 : 1][CHAN ? kC * kD : 8];            // erase key b (.) k
+  uint16_t r[WK != kWkSame ? 2 : 1][WK != kWkSame ? kC * kD : 8];   // write key if != k
+  uint16_t rt[2][kD * kC];                                 // R^T
+  uint16_t vpt[2][BV][kLdc];                               // V'^T; output staging later
+  uint16_t t[2][kC][kLdc];                                 // T
+  uint16_t p[kC][kLdc];                                    // P (one buffer)
+  uint16_t lba[32][kLdl];                                  // A_ba = -L_ba
+  float g2[2][kC], eg[2][kC], wd[2][kC], cy[2][kC], beta[2][kC], ic[2][kC];
 };
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-// element e (0..7) of 8 bf16 packed in a uint4, as a bit pattern / as fp32
+__device__ __forceinline__ uint16_t tobf(float x) { return f32_to_bf16_bits(x); }
 __device__ __forceinline__ uint32_t word(const uint4 &v, int e) {
   const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 __device__ __forceinline__ float elem(const uint4 &v, int e) { return bf(word(v, e)); }
-// 16-byte global load, or zeros when !ok (no select of addresses: the zero is a value)
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p, bool ok) {
   uint4 r = make_uint4(0u, 0u, 0u, 0u);
   if (ok) r = *reinterpret_cast<const uint4 *>(p);
   return r;
 }
-__device__ __forceinline__ uint16_t tobf(float x) { return f32_to_bf16_bits(x); }
 
+__device__ __forceinline__ short8v ld8(const uint16_t *p) { return *reinterpret_cast<const short8v *>(p); }
+__device__ __forceinline__ short4v ld4(const uint16_t *p) { return *reinterpret_cast<const short4v *>(p); }
+__device__ __forceinline__ short8v cat(short4v a, short4v b) {
+  return short8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 __device__ __forceinline__ float4v mfma32(short8v a, short8v b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// K = 16 product issued as the native gfx950 K = 32 instruction with K-slots 4..7 zero.
+// (The legacy v_mfma_f32_16x16x16_bf16 is avoided: its results were read back before
+// they were written -- first two result registers stale -- with the wait states the
+// compiler inserts for it on gfx950.)
 __device__ __forceinline__ float4v mfma16(short4v a, short4v b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  const short4v z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(a, z), cat(b, z), c, 0, 0, 0);
 }
-__device__ __forceinline__ short8v ld8(const uint16_t *p) {
-  return *reinterpret_cast<const short8v *>(p);
-}
-__device__ __forceinline__ short4v ld4(const uint16_t *p) {
-  return *reinterpret_cast<const short4v *>(p);
-}
-// 4 fp32 from LDS -> 4 bf16
-__device__ __forceinline__ short4v ld4f(const float *p) {
-  const float4 f = *reinterpret_cast<const float4 *>(p);
+__device__ __forceinline__ short4v tobf4(float4v v) {
   short4v r;
-  r[0] = static_cast<short>(tobf(f.x));
-  r[1] = static_cast<short>(tobf(f.y));
-  r[2] = static_cast<short>(tobf(f.z));
-  r[3] = static_cast<short>(tobf(f.w));
+  const uint32_t lo = f32x2_to_bf16x2_bits(v[0], v[1]), hi = f32x2_to_bf16x2_bits(v[2], v[3]);
+  r[0] = static_cast<short>(lo & 0xffff);
+  r[1] = static_cast<short>(lo >> 16);
+  r[2] = static_cast<short>(hi & 0xffff);
+  r[3] = static_cast<short>(hi >> 16);
   return r;
 }
-// 4 bf16 down a column (stride ld elements)
 __device__ __forceinline__ short4v ld4col(const uint16_t *p, int ld) {
   short4v r;
   r[0] = static_cast<short>(p[0]);
@@ -116,54 +127,92 @@ __device__ __forceinline__ short4v ld4col(const uint16_t *p, int ld) {
   r[3] = static_cast<short>(p[3 * ld]);
   return r;
 }
-__device__ __forceinline__ short4v tobf4(float4v v, float s = 1.f) {
-  short4v r;
-  r[0] = static_cast<short>(tobf(s * v[0]));
-  r[1] = static_cast<short>(tobf(s * v[1]));
-  r[2] = static_cast<short>(tobf(s * v[2]));
-  r[3] = static_cast<short>(tobf(s * v[3]));
-  return r;
+__device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4v zero4() { return float4v{0.f, 0.f, 0.f, 0.f}; }
+// keep the scheduler from hoisting the next tile's operand loads above this point
+// (bounds register pressure; the hardware still overlaps the independent work)
+#define GDR_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// operand gathers; `l4` = lane / 16
+// natural K order, 128-wide swizzled rows: 8 consecutive K from k0 + 8 l4
+__device__ __forceinline__ short8v opn128(const uint16_t *a, int row, int k0, int l4) {
+  return ld8(a + sw128(row, k0 + 8 * l4));
+}
+// split K order (see header): K = k0 + 4 l4 + i and k0 + 16 + 4 l4 + i
+__device__ __forceinline__ short8v ops128(const uint16_t *a, int row, int k0, int l4) {
+  return cat(ld4(a + sw128(row, k0 + 4 * l4)), ld4(a + sw128(row, k0 + 16 + 4 * l4)));
+}
+__device__ __forceinline__ short8v ops64(const uint16_t *a, int row, int k0, int l4) {
+  return cat(ld4(a + sw64(row, k0 + 4 * l4)), ld4(a + sw64(row, k0 + 16 + 4 * l4)));
+}
+__device__ __forceinline__ short8v opsp(const uint16_t *a, int ld, int row, int k0, int l4) {
+  return cat(ld4(a + row * ld + k0 + 4 * l4), ld4(a + row * ld + k0 + 16 + 4 * l4));
 }
 
-// acc += A[m0.., :K] * B[n0.., :K]^T over K = 32 * nk columns starting at k0; A and B are
-// row-major with K contiguous.
-__device__ __forceinline__ float4v tile_mma(float4v acc, const uint16_t *A, int lda, const uint16_t *Bm,
-                                           int ldb, int m0, int n0, int k0, int nk, int lane) {
-  const uint16_t *pa = A + (m0 + (lane & 15)) * lda + k0 + 8 * (lane >> 4);
-  const uint16_t *pb = Bm + (n0 + (lane & 15)) * ldb + k0 + 8 * (lane >> 4);
-#pragma unroll 4
-  for (int kk = 0; kk < nk; ++kk) acc = mfma32(ld8(pa + 32 * kk), ld8(pb + 32 * kk), acc);
-  return acc;
+// D = (I - N)^-1 for a strictly lower 16 x 16 N given as acc(N) and acc(N^T); returns
+// acc(D) and, when wanted, acc(D^T).  Doubling: N^16 = 0 so (I - N)^-1 = prod (I + N^(2^k)).
+__device__ __forceinline__ void diag_inverse(float4v nA, float4v ntA, float4v &d, float4v *dt, int lane) {
+  const short4v n = tobf4(nA), nt = tobf4(ntA);   // B-layout(N), B-layout(N^T)
+  const float4v z = zero4();
+  const short4v b2 = tobf4(mfma16(nt, n, z)), b2t = tobf4(mfma16(n, nt, z));
+  const short4v b4 = tobf4(mfma16(b2t, b2, z)), b4t = tobf4(mfma16(b2, b2t, z));
+  const short4v b8t = tobf4(mfma16(b4, b4t, z));
+  const int l16 = lane & 15, l4 = lane >> 4;
+  float4v id;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) id[r] = (4 * l4 + r == l16) ? 1.f : 0.f;
+  float4v R = nA + id;
+  R = mfma16(b2t, tobf4(R), R);
+  R = mfma16(b4t, tobf4(R), R);
+  R = mfma16(b8t, tobf4(R), R);
+  d = R;
+  if (dt != nullptr) {
+    const short4v b8 = tobf4(mfma16(b4t, b4, z));
+    float4v Rt = ntA + id;
+    Rt = mfma16(b2, tobf4(Rt), Rt);
+    Rt = mfma16(b4, tobf4(Rt), Rt);
+    Rt = mfma16(b8, tobf4(Rt), Rt);
+    *dt = Rt;
+  }
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK, bool BAND>
+template <int BV, bool CHAN, bool DECAY, int WK>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
-  constexpr int NVB = BV / 16;         // 16-row blocks of the value tile
-  constexpr int NVT = kD / BV;         // value tiles per head
-  constexpr int NST = NVB * 8;         // state tiles (16 x 16)
-  constexpr int SPW = NST / kNW;       // state tiles per wave
-  constexpr int NOT = 4 * NVB;         // output / X / D tiles
-  static_assert(NST % kNW == 0, "state tiles must divide among waves");
+  constexpr int NVW = BV / 16;             // value waves
+  constexpr int NVT = kD / BV;             // value tiles per head
+  constexpr int NH = (kNW - NVW) * 64;     // helper threads
+  constexpr int NVI = kC * BV / 8;         // V items (8 bf16 each)
+  // staging items: [k ... | r ... | v ...] staged in phase 1, [q ...] in phase 2
+  constexpr int NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
+  constexpr int N1 = NK + NR + NVI;
+  constexpr int S1 = (N1 + NH - 1) / NH;   // phase-1 slots per helper thread
+  constexpr int S2 = (1024 + NH - 1) / NH; // q slots
+  constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
   __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index as a provably wave-uniform (scalar) value: role dispatch below is then a
+  // scalar branch, and each role's loop (with its barriers) runs only in its own waves
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, l4 = lane >> 4;
+  const bool vwave = wave < NVW;
+  const int hw = wave - NVW;               // helper wave index
+  const int ht = tid - NVW * 64;           // helper thread index
 
-  // XCD-aware tile order: consecutive logical tiles (the value tiles of one head) land
-  // on the same XCD, whose L2 then serves the head's q/k reads to all of them.
+  // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
   const int G = static_cast<int>(gridDim.x);
   const int bid = static_cast<int>(blockIdx.x);
   const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int bh = logical / NVT;
-  const int vt = logical % NVT;
-  const int v0 = vt * BV;
+  const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
   const int H = a.H, T = a.T;
   const int b = bh / H, h = bh % H;
-  const long long tokstride = static_cast<long long>(H) * kD;   // elements between tokens
-  const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;  // (b, 0, h, 0)
-  const long long gate0 = static_cast<long long>(b) * T * H + h;         // (b, 0, h)
+  const long long tokstride = static_cast<long long>(H) * kD;
+  const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
+  const long long gate0 = static_cast<long long>(b) * T * H + h;
+  const int nchunks = (T + kC - 1) / kC;
+  const int N = a.N;
+  auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
 
   const uint16_t *gq = static_cast<const uint16_t *>(a.q);
   const uint16_t *gk = static_cast<const uint16_t *>(a.k);
@@ -173,108 +222,104 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
   uint16_t *gout = static_cast<uint16_t *>(a.out);
 
-  // ---- one-time LDS init: zero upper blocks of T and P; unit diagonal for band T ----
-  for (int idx = tid; idx < kC * kLdc; idx += kNT) {
-    const int i = idx / kLdc, j = idx % kLdc;
-    (&sm.t[0][0])[idx] = (BAND && i == j) ? tobf(1.f) : 0;
-    (&sm.p[0][0])[idx] = 0;
+  // ---------------- one-time init: zero T (upper blocks stay zero) ----------------
+  for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = 0;
+  for (int i = tid; i < kC * kLdc; i += kNT) (&sm.p[0][0])[i] = 0;
+
+  // ---------------- helper prefetch registers ----------------
+  uint4 pa[S1], pb[S1], pqv[S2];
+  float pbeta_v[S1];
+#pragma unroll
+  for (int s = 0; s < S1; ++s) {
+    pa[s] = pb[s] = make_uint4(0u, 0u, 0u, 0u);
+    pbeta_v[s] = 0.f;
   }
-
-  // ---- state tiles in accumulators ----
-  float4v sacc[SPW];
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int st = wave + u * kNW;
-    const int vb = st / 8, cb = st % 8;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int v = vb * 16 + 4 * l4 + r, c = cb * 16 + l16;
-      float x = 0.f;
-      if (a.state_in != nullptr) x = a.state_in[(static_cast<long long>(bh) * kD + v0 + v) * kD + c];
-      sacc[u][r] = x;
-      sm.s[v][c] = tobf(x);
-    }
-  }
+  for (int s = 0; s < S2; ++s) pqv[s] = make_uint4(0u, 0u, 0u, 0u);
+  float gla = 0.f, gbeta = 0.f;            // gate item (last helper wave)
+  const bool gate_wave = wave == kNW - 1;
 
-  // preconditioner accumulator: 4 lanes per channel (token segments of 16)
-  const int pc_c = tid >> 2, pc_seg = tid & 3;
-  float hcarry = 0.f;
-  if (WK == kWkPrecond) hcarry = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + pc_c] : a.h0;
-
-  // ---- register prefetch of one chunk ----
-  // q, k (and write key / erase gate): units of 8 bf16, 1024 per tensor, 2 per thread
-  // v (and write gate) tile: 64 x BV, units of 8 bf16, 8 * BV units
-  constexpr int VU = kC * BV / 8;
-  uint4 pq[2], pk[2], pr[2], pe[2], pv, pw;
-  float pbeta = 0.f, pla = 0.f, pvbeta = 0.f;
-  auto prefetch = [&](int c0, int n) {
+  auto load1 = [&](int c) {                // phase-1 items of chunk c
+    const int c0 = c * kC, n = min(kC, T - c0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int unit = tid + u * kNT;
-      const int t = unit >> 4, col = (unit & 15) * 8;
-      const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + col;
-      const bool ok = t < n;
-      pq[u] = ldg16(gq + off, ok);
-      pk[u] = ldg16(gk + off, ok);
-      if (WK == kWkExplicit) pr[u] = ldg16(gwk + off, ok);
-      if (CHAN) pe[u] = ldg16(ger + off, ok);
+    for (int s = 0; s < S1; ++s) {
+      const int it = ht + s * NH;
+      if (it < NK + NR) {
+        const int u = it < NK ? it : it - NK;
+        const int t = u >> 4, col = (u & 15) * 8;
+        const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + col;
+        const bool ok = t < n;
+        if (it < NK) {
+          pa[s] = ldg16(gk + off, ok);
+          if (CHAN) pb[s] = ldg16(ger + off, ok);
+        } else {
+          pa[s] = ldg16(gwk + off, ok);
+        }
+      } else if (it < N1) {
+        const int u = it - NK - NR;
+        const int t = u / (BV / 8), col = (u % (BV / 8)) * 8;
+        const bool ok = t < n;
+        const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + v0 + col;
+        pa[s] = ldg16(gv + off, ok);
+        if (CHAN) pb[s] = ldg16(gwr + off, ok);
+        else pbeta_v[s] = ok ? a.beta[gate0 + static_cast<long long>(c0 + t) * H] : 0.f;
+      }
     }
-    if (tid < VU) {
-      const int t = tid / (BV / 8), col = (tid % (BV / 8)) * 8;
-      const bool ok = t < n;
-      const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + v0 + col;
-      pv = ldg16(gv + off, ok);
-      if (CHAN) pw = ldg16(gwr + off, ok);
-      if (!CHAN) pvbeta = ok ? a.beta[gate0 + static_cast<long long>(c0 + t) * H] : 0.f;
-    }
-    if (tid < kC) {
-      const bool ok = tid < n;
-      const long long gi = gate0 + static_cast<long long>(c0 + tid) * H;
-      pbeta = (!CHAN && ok) ? a.beta[gi] : 0.f;
-      pla = (DECAY && ok) ? a.log_alpha[gi] : 0.f;
+    if (gate_wave) {
+      const bool ok = lane < n;
+      const long long gi = gate0 + static_cast<long long>(c0 + lane) * H;
+      gla = (DECAY && ok) ? a.log_alpha[gi] : 0.f;
+      gbeta = (!CHAN && ok) ? a.beta[gi] : 0.f;
     }
   };
-
-  const int nchunks = (T + kC - 1) / kC;
-  if (nchunks > 0) prefetch(0, min(kC, T));
-
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int c0 = ci * kC;
-    const int n = min(kC, T - c0);
-    __syncthreads();  // previous chunk done with every LDS buffer
-
-    // ================= Phase L: prefetched registers -> LDS; gates =================
+  auto load2 = [&](int c) {                // q items of chunk c
+    const int c0 = c * kC, n = min(kC, T - c0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int unit = tid + u * kNT;
-      const int t = unit >> 4, col = (unit & 15) * 8;
-      *reinterpret_cast<uint4 *>(&sm.q[t][col]) = pq[u];
-      *reinterpret_cast<uint4 *>(&sm.k[t][col]) = pk[u];
-      if (WK == kWkSame) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.rt[col + e][t] = static_cast<uint16_t>(word(pk[u], e));
-      } else if (WK == kWkExplicit) {
-        *reinterpret_cast<uint4 *>(&sm.r[t][col]) = pr[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.rt[col + e][t] = static_cast<uint16_t>(word(pr[u], e));
-      }
-      if (CHAN) {
-        uint4 ev;
-        ev.x = tobf(elem(pe[u], 0) * elem(pk[u], 0)) | (uint32_t(tobf(elem(pe[u], 1) * elem(pk[u], 1))) << 16);
-        ev.y = tobf(elem(pe[u], 2) * elem(pk[u], 2)) | (uint32_t(tobf(elem(pe[u], 3) * elem(pk[u], 3))) << 16);
-        ev.z = tobf(elem(pe[u], 4) * elem(pk[u], 4)) | (uint32_t(tobf(elem(pe[u], 5) * elem(pk[u], 5))) << 16);
-        ev.w = tobf(elem(pe[u], 6) * elem(pk[u], 6)) | (uint32_t(tobf(elem(pe[u], 7) * elem(pk[u], 7))) << 16);
-        *reinterpret_cast<uint4 *>(&sm.e[t][col]) = ev;
+    for (int s = 0; s < S2; ++s) {
+      const int u = ht + s * NH;
+      if (u < 1024) {
+        const int t = u >> 4, col = (u & 15) * 8;
+        pqv[s] = ldg16(gq + head0 + static_cast<long long>(c0 + t) * tokstride + col, t < n);
       }
     }
-    if (tid < VU) {
-      const int t = tid / (BV / 8), col = (tid % (BV / 8)) * 8;
+  };
+  auto stage1 = [&](int c, int buf) {      // registers -> LDS, phase-1 items, and gates
+    const int n = min(kC, T - c * kC);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.vp[t][col + e] = CHAN ? elem(pw, e) * elem(pv, e) : pvbeta * elem(pv, e);
+    for (int s = 0; s < S1; ++s) {
+      const int it = ht + s * NH;
+      if (it < NK + NR) {
+        const int u = it < NK ? it : it - NK;
+        const int t = u >> 4, col = (u & 15) * 8;
+        if (it < NK) {
+          *reinterpret_cast<uint4 *>(&sm.k[buf][sw128(t, col)]) = pa[s];
+          if (WK == kWkSame) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.rt[buf][sw64(col + e, t)] = static_cast<uint16_t>(word(pa[s], e));
+          }
+          if (CHAN) {
+            uint4 ev;
+            ev.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(pa[s], 0), elem(pb[s], 1) * elem(pa[s], 1));
+            ev.y = f32x2_to_bf16x2_bits(elem(pb[s], 2) * elem(pa[s], 2), elem(pb[s], 3) * elem(pa[s], 3));
+            ev.z = f32x2_to_bf16x2_bits(elem(pb[s], 4) * elem(pa[s], 4), elem(pb[s], 5) * elem(pa[s], 5));
+            ev.w = f32x2_to_bf16x2_bits(elem(pb[s], 6) * elem(pa[s], 6), elem(pb[s], 7) * elem(pa[s], 7));
+            *reinterpret_cast<uint4 *>(&sm.e[buf][sw128(t, col)]) = ev;
+          }
+        } else {
+          *reinterpret_cast<uint4 *>(&sm.r[buf][sw128(t, col)]) = pa[s];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm.rt[buf][sw64(col + e, t)] = static_cast<uint16_t>(word(pa[s], e));
+        }
+      } else if (it < N1) {
+        const int u = it - NK - NR;
+        const int t = u / (BV / 8), col = (u % (BV / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sm.vpt[buf][col + e][t] = tobf(CHAN ? elem(pb[s], e) * elem(pa[s], e) : pbeta_v[s] * elem(pa[s], e));
+      }
     }
-    if (wave == 0) {
-      // inclusive scan of log2(alpha) over the chunk (padded tokens add 0)
-      float g = pla * kLog2e;
+    if (gate_wave) {
+      float g = gla * kLog2e;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const float y = __shfl_up(g, d, 64);
@@ -282,302 +327,338 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       }
       const float glast = __shfl(g, n - 1, 64);
       const float egv = DECAY ? exp2f(g) : 1.f;
-      sm.g2[lane] = g;
-      sm.eg[lane] = egv;
-      sm.wd[lane] = DECAY ? exp2f(glast - g) : 1.f;
-      sm.cy[lane] = CHAN ? egv : pbeta * egv;
-      sm.beta[lane] = pbeta;
+      sm.g2[buf][lane] = g;
+      sm.eg[buf][lane] = egv;
+      sm.wd[buf][lane] = DECAY ? exp2f(glast - g) : 1.f;
+      sm.cy[buf][lane] = CHAN ? egv : gbeta * egv;
+      sm.beta[buf][lane] = gbeta;
       if (WK == kWkPrecond) {
-        const float tg = static_cast<float>(a.t0 + c0 + lane + 1);
-        sm.ic[lane] = 1.f / (-expm1f(tg * a.log_rho));   // 1 / (1 - rho^t)
+        const float tg = static_cast<float>(a.t0 + static_cast<long long>(c) * kC + lane + 1);
+        sm.ic[buf][lane] = 1.f / (-expm1f(tg * a.log_rho));   // 1 / (1 - rho^t)
       }
     }
-    // issue the next chunk's loads; they land while this chunk computes
-    if (ci + 1 < nchunks) prefetch(c0 + kC, min(kC, T - c0 - kC));
-    __syncthreads();
-
-    // ============ Phase U (preconditioner): u = k / (h / (1 - rho^t) + eps) ============
-    if (WK == kWkPrecond) {
-      // lanes (channel c, segment s) cover tokens 16 s .. 16 s + 15
-      const int c = pc_c, s0 = pc_seg * 16;
-      const int m = max(0, min(16, n - s0));   // valid tokens of this segment
-      float hl[16], kv[16];
-      float acc = 0.f;
+  };
+  auto stage2 = [&]() {                    // q registers -> LDS
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        kv[i] = bf(sm.k[s0 + i][c]);
-        if (i < m) acc = fmaf(a.rho, acc, kv[i] * kv[i]);
-        hl[i] = acc;
-      }
-      // carry into segment s: compose the affine maps h -> rho^m h + acc of earlier segments
-      float rm = 1.f;
-      for (int i = 0; i < m; ++i) rm *= a.rho;
-      const int base = lane & ~3;
-      float cin = hcarry, cend = hcarry;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float ms = __shfl(rm, base + s, 64);
-        const float as = __shfl(acc, base + s, 64);
-        if (s < pc_seg) cin = fmaf(ms, cin, as);
-        cend = fmaf(ms, cend, as);
-      }
-      float pw = a.rho;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float u = 0.f;
-        if (i < m) {
-          const float hv = fmaf(pw, cin, hl[i]);
-          u = kv[i] / fmaf(hv, sm.ic[s0 + i], a.eps);
-        }
-        pw *= a.rho;
-        const uint16_t ub = tobf(u);
-        sm.r[s0 + i][c] = ub;
-        sm.rt[c][s0 + i] = ub;
-      }
-      hcarry = cend;
-      __syncthreads();
+    for (int s = 0; s < S2; ++s) {
+      const int u = ht + s * NH;
+      if (u < 1024) *reinterpret_cast<uint4 *>(&sm.q[sw128(u >> 4, (u & 15) * 8)]) = pqv[s];
     }
+  };
 
-    const uint16_t *Ea = CHAN ? &sm.e[0][0] : &sm.k[0][0];                // erase key rows
-    const uint16_t *Rr = (WK == kWkSame) ? &sm.k[0][0] : &sm.r[0][0];    // write key rows
-
-    // ================= Phase A: L = tril_{-1}((E R^T) (.) Gamma) =================
-    for (int job = wave; job < 10; job += kNW) {
-      // lower-triangular tile index -> (ib, jb)
-      const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-      const int jb = job - ib * (ib + 1) / 2;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile_mma(acc, Ea, kLdr, Rr, kLdr, ib * 16, jb * 16, 0, 4, lane);
-      const int j = jb * 16 + l16;
+  // raw (E R^T) tile for rows ib, cols jb (trans: the transposed tile), scaled to A = -L
+  auto a_tile = [&](int buf, int ib, int jb, bool trans) -> float4v {
+    const uint16_t *E = CHAN ? sm.e[buf] : sm.k[buf];
+    const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
+    const uint16_t *A = trans ? R : E;
+    const uint16_t *B = trans ? E : R;
+    const int ra = (trans ? jb : ib) * 16 + l16, rb = (trans ? ib : jb) * 16 + l16;
+    float4v acc = zero4();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ib * 16 + 4 * l4 + r;
-        float x = acc[r];
-        if (!CHAN) x *= sm.beta[i];
-        if (DECAY) x *= exp2f(sm.g2[i] - sm.g2[j]);
-        sm.a[i][j] = (j < i) ? x : 0.f;
+    for (int s = 0; s < 4; ++s) acc = mfma32(opn128(A, ra, 32 * s, l4), opn128(B, rb, 32 * s, l4), acc);
+    // lane holds element (i, j) of L for i = row index of L, j = column index of L
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = trans ? ib * 16 + l16 : ib * 16 + 4 * l4 + r;
+      const int j = trans ? jb * 16 + 4 * l4 + r : jb * 16 + l16;
+      float x = acc[r];
+      if (SCALED_E) x *= sm.beta[buf][i];
+      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
+      acc[r] = (j < i) ? -x : 0.f;
+    }
+    return acc;
+  };
+
+  // Each role runs its own loop with the same barrier sequence, so the compiler allocates
+  // registers for one role's loop-carried state at a time.
+  if (vwave) {
+    // ---------------- value waves: S^T tiles in accumulators ----------------
+    // tile cb holds S^T[c = 16 cb + 4 l4 + r][v = 16 wave + l16]
+    float4v st[8];
+    const int vrow = v0 + 16 * wave + l16;   // this lane's state row
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      st[cb] = zero4();
+      if (a.state_in != nullptr) {
+        const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4);
+        st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
       }
     }
-    __syncthreads();
-
-    // ===== Phase B: diagonal blocks of T (wave 0)  ||  P, X, O1 (other waves) =====
-    if (wave == 0) {
-      if (!BAND) {
-        // lane = (block, column): forward substitution down the column of a 16x16 block
-        const int blk = l4, j = l16, o = blk * 16;
-        float tv[16];
+    for (int c = -1; c < nchunks; ++c) {
+      const int cur = c & 1;
+      const int c0 = c * kC;
+      const int n = min(kC, T - c0);
+      short4v x4[4];
+      float4v O1[4];
+      __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
+      if (c >= 0) {
+        // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - cy Y
+        short8v sb[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tv[i] = (i == j) ? 1.f : 0.f;
+        for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
+        const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) {
-          float acc = 0.f;
+        for (int tb = 0; tb < 4; ++tb) {
+          float4v y = zero4(), o = zero4();
 #pragma unroll
-          for (int m = 0; m < i; ++m) acc = fmaf(sm.a[o + i][o + m], tv[m], acc);
-          if (i > j) tv[i] = -acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool keep = (i - j) <= a.N || a.N < 0;
-          sm.t[o + i][o + j] = (i >= j && keep) ? tobf(tv[i]) : 0;
-        }
-      } else {
-        // band-limited substitution: lane j forms T_{j+d, j}, d = 1..N (N <= 15)
-        const int j = lane;
-        float tc[16];
-        tc[0] = 1.f;
-#pragma unroll
-        for (int d = 1; d < 16; ++d) {
-          float acc = 0.f;
-          if (d <= a.N && j + d < kC) {
-#pragma unroll
-            for (int m = 0; m < d; ++m) acc = fmaf(-sm.a[j + d][j + m], tc[m], acc);
-            sm.t[j + d][j] = tobf(acc);
+          for (int j = 0; j < 4; ++j) {
+            y = mfma32(ops128(E, tb * 16 + l16, 32 * j, l4), sb[j], y);
+            o = mfma32(ops128(sm.q, tb * 16 + l16, 32 * j, l4), sb[j], o);
           }
-          tc[d] = acc;
+          const int t0 = tb * 16 + 4 * l4;
+          const float4 cy = ld4f(&sm.cy[cur][t0]);
+          const float4 eg = ld4f(&sm.eg[cur][t0]);
+          const short4v vp = ld4(&sm.vpt[cur][16 * wave + l16][t0]);
+          x4[tb] = tobf4(float4v{bf(static_cast<uint16_t>(vp[0])) - cy.x * y[0],
+                                 bf(static_cast<uint16_t>(vp[1])) - cy.y * y[1],
+                                 bf(static_cast<uint16_t>(vp[2])) - cy.z * y[2],
+                                 bf(static_cast<uint16_t>(vp[3])) - cy.w * y[3]});
+          O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
+          GDR_FENCE();
         }
       }
-    } else {
-      constexpr int NJ = 10 + 2 * NOT;
-      for (int job = wave - 1; job < NJ; job += kNW - 1) {
-        if (job < 10) {
-          // P tile
-          const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-          const int jb = job - ib * (ib + 1) / 2;
-          float4v acc = {0.f, 0.f, 0.f, 0.f};
-          acc = tile_mma(acc, &sm.q[0][0], kLdr, Rr, kLdr, ib * 16, jb * 16, 0, 4, lane);
-          const int j = jb * 16 + l16;
+      __syncthreads();   // (2) T(c) and P(c) complete
+      if (c >= 0) {
+        const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
+        // D = T X
+        const uint16_t *Tm = &sm.t[cur][0][0];
+        float4v D[4];
+        D[0] = mfma16(ld4(Tm + l16 * kLdc + 4 * l4), x4[0], zero4());
+        D[1] = mfma32(opsp(Tm, kLdc, 16 + l16, 0, l4), x01, zero4());
+        D[2] = mfma32(opsp(Tm, kLdc, 32 + l16, 0, l4), x01, zero4());
+        D[2] = mfma16(ld4(Tm + (32 + l16) * kLdc + 32 + 4 * l4), x4[2], D[2]);
+        D[3] = mfma32(opsp(Tm, kLdc, 48 + l16, 0, l4), x01, zero4());
+        D[3] = mfma32(opsp(Tm, kLdc, 48 + l16, 32, l4), x23, D[3]);
+        GDR_FENCE();
+        // O2 = P D
+        short4v d4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = ib * 16 + 4 * l4 + r;
-            float x = acc[r];
-            if (DECAY) x *= exp2f(sm.g2[i] - sm.g2[j]);
-            sm.p[i][j] = (j <= i) ? tobf(x) : 0;
-          }
-        } else if (job < 10 + NOT) {
-          // X tile: X = V' - cy (.) (E S^T), stored transposed
-          const int o = job - 10, tb = o / NVB, vb = o % NVB;
-          float4v acc = {0.f, 0.f, 0.f, 0.f};
-          acc = tile_mma(acc, Ea, kLdr, &sm.s[0][0], kLdr, tb * 16, vb * 16, 0, 4, lane);
-          const int v = vb * 16 + l16;
-          short4v xv;
+        for (int j = 0; j < 4; ++j) d4[j] = tobf4(D[j]);
+        const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
+        const uint16_t *Pm = &sm.p[0][0];
+        float4v O2[4];
+        O2[0] = mfma16(ld4(Pm + l16 * kLdc + 4 * l4), d4[0], zero4());
+        O2[1] = mfma32(opsp(Pm, kLdc, 16 + l16, 0, l4), d01, zero4());
+        O2[2] = mfma32(opsp(Pm, kLdc, 32 + l16, 0, l4), d01, zero4());
+        O2[2] = mfma16(ld4(Pm + (32 + l16) * kLdc + 32 + 4 * l4), d4[2], O2[2]);
+        O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 0, l4), d01, zero4());
+        O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 32, l4), d23, O2[3]);
+        GDR_FENCE();
+        // state update S^T <- e^{g_C} S^T + R^T (wd (.) D)
+        short4v w4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tb * 16 + 4 * l4 + r;
-            xv[r] = static_cast<short>(tobf(sm.vp[t][v] - sm.cy[t] * acc[r]));
-          }
-          *reinterpret_cast<short4v *>(&sm.xt[v][tb * 16 + 4 * l4]) = xv;
-        } else {
-          // O1 tile: e^g (.) (Q S^T)
-          const int o = job - 10 - NOT, tb = o / NVB, vb = o % NVB;
-          float4v acc = {0.f, 0.f, 0.f, 0.f};
-          acc = tile_mma(acc, &sm.q[0][0], kLdr, &sm.s[0][0], kLdr, tb * 16, vb * 16, 0, 4, lane);
-          const int v = vb * 16 + l16;
+        for (int j = 0; j < 4; ++j) {
+          const float4 wdv = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
+          w4[j] = tobf4(float4v{wdv.x * D[j][0], wdv.y * D[j][1], wdv.z * D[j][2], wdv.w * D[j][3]});
+        }
+        const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
+        const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tb * 16 + 4 * l4 + r;
-            sm.o1[t][v] = sm.eg[t] * acc[r];
-          }
+        for (int cb = 0; cb < 8; ++cb) {
+          float4v acc = st[cb];
+          if (DECAY) acc *= gC;
+          acc = mfma32(ops64(sm.rt[cur], cb * 16 + l16, 0, l4), w01, acc);
+          acc = mfma32(ops64(sm.rt[cur], cb * 16 + l16, 32, l4), w23, acc);
+          st[cb] = acc;
+          if (cb & 1) GDR_FENCE();
+        }
+        // output: stage this wave's 64 x 16 block in LDS, then 16-byte stores
+        uint16_t *ost = &sm.vpt[cur][0][0] + wave * (kC * 16);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ost[(tb * 16 + 4 * l4 + r) * 16 + l16] = tobf(a.scale * (O1[tb][r] + O2[tb][r]));
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t = half * 32 + (lane >> 1), part = lane & 1;
+          const uint4 val = *reinterpret_cast<const uint4 *>(ost + t * 16 + part * 8);
+          if (t < n)
+            *reinterpret_cast<uint4 *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * wave +
+                                       part * 8) = val;
         }
       }
+      if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
     }
-    __syncthreads();
-
-    if (!BAND) {
-      // ============ Phase R1: T_{p,q} = -D_p (L_{p,q} D_q) for (p,q) = (1,0), (3,2) ============
-      if (wave < 2) {
-        const int p = 1 + 2 * wave, q = p - 1;
-        float4v z = {0.f, 0.f, 0.f, 0.f};
-        z = mfma16(ld4f(&sm.a[p * 16 + l16][q * 16 + 4 * l4]),
-                   ld4col(&sm.t[q * 16 + 4 * l4][q * 16 + l16], kLdc), z);
-        float4v tt = {0.f, 0.f, 0.f, 0.f};
-        tt = mfma16(ld4(&sm.t[p * 16 + l16][p * 16 + 4 * l4]), tobf4(z), tt);
+    if (a.state_out != nullptr) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = p * 16 + 4 * l4 + r, j = q * 16 + l16;
-          const bool keep = (i - j) <= a.N || a.N < 0;
-          sm.t[i][j] = keep ? tobf(-tt[r]) : 0;
-        }
-      }
-      __syncthreads();
-      // ==== Phase R2: T_ba = -T_b (L_ba T_a), rows 32..63, columns 0..31; wave q: 16-col block q ====
-      if (wave < 2) {
-        const int q = wave;
+      for (int cb = 0; cb < 8; ++cb)
+        *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4) =
+            make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+    }
+    return;
+  }
+
+  // ---------------- helper waves ----------------
+  // preconditioner accumulator: helper threads ht < 256 own channel ht / 2, token half ht % 2
+  const bool pc_thread = ht < 256;
+  const int pc_c = ht >> 1, pc_seg = ht & 1;
+  float hcarry = 0.f;
+  if (WK == kWkPrecond && pc_thread)
+    hcarry = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + pc_c] : a.h0;
+
+  if (nchunks > 0) {
+    load1(0);
+    load2(0);
+  }
+  for (int c = -1; c < nchunks; ++c) {
+    const int cur = c & 1, nxt = (c + 1) & 1;
+    const bool have_next = c + 1 < nchunks;
+
+    __syncthreads();   // (1)
+    if (c >= 0) {
+      if (hw < 2) {
+        // T_ba = T_b A_ba T_a, column block qb of the lower-left quadrant
+        const int qb = hw;
         float4v z[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          z[s] = float4v{0.f, 0.f, 0.f, 0.f};
+          z[s] = zero4();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            if (u < q) continue;   // T_a[u][q] = 0 above the diagonal
-            z[s] = mfma16(ld4f(&sm.a[32 + s * 16 + l16][u * 16 + 4 * l4]),
-                          ld4col(&sm.t[u * 16 + 4 * l4][q * 16 + l16], kLdc), z[s]);
+            if (u < qb) continue;
+            z[s] = mfma16(ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]),
+                          ld4col(&sm.t[cur][u * 16 + 4 * l4][qb * 16 + l16], kLdc), z[s]);
           }
         }
         const short4v z0 = tobf4(z[0]), z1 = tobf4(z[1]);
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-          float4v tt = {0.f, 0.f, 0.f, 0.f};
-          tt = mfma16(ld4(&sm.t[32 + sp * 16 + l16][32 + 4 * l4]), z0, tt);
-          if (sp == 1) tt = mfma16(ld4(&sm.t[48 + l16][48 + 4 * l4]), z1, tt);
+          float4v tt = mfma16(ld4(&sm.t[cur][32 + sp * 16 + l16][32 + 4 * l4]), z0, zero4());
+          if (sp == 1) tt = mfma16(ld4(&sm.t[cur][48 + l16][48 + 4 * l4]), z1, tt);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int i = 32 + sp * 16 + 4 * l4 + r, j = q * 16 + l16;
-            const bool keep = (i - j) <= a.N || a.N < 0;
-            sm.t[i][j] = keep ? tobf(-tt[r]) : 0;
+            const int i = 32 + sp * 16 + 4 * l4 + r, j = qb * 16 + l16;
+            sm.t[cur][i][j] = keep(i, j) ? tobf(tt[r]) : 0;
+          }
+        }
+      } else {
+        // P tiles (lower triangle incl. diagonal blocks)
+        const uint16_t *R = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
+        for (int job = hw - 2; job < 10; job += (kNW - NVW - 2)) {
+          const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
+          const int jb = job - ib * (ib + 1) / 2;
+          float4v acc = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = mfma32(opn128(sm.q, ib * 16 + l16, 32 * s, l4), opn128(R, jb * 16 + l16, 32 * s, l4), acc);
+          const int j = jb * 16 + l16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = ib * 16 + 4 * l4 + r;
+            float x = acc[r];
+            if (DECAY) x *= exp2f(sm.g2[cur][i] - sm.g2[cur][j]);
+            sm.p[i][j] = (j <= i) ? tobf(x) : 0;
           }
         }
       }
-      __syncthreads();
+    }
+    if (have_next) {
+      stage1(c + 1, nxt);
+      if (c + 2 < nchunks) load1(c + 2);
+    }
+    __syncthreads();   // (2)
+
+    if (WK == kWkPrecond) {
+      // write keys of chunk c + 1: u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2
+      if (have_next && pc_thread) {
+        const int nn = min(kC, T - (c + 1) * kC);
+        const int ch = pc_c, s0 = pc_seg * 32;
+        const int m = max(0, min(32, nn - s0));
+        float acc = 0.f, rm = 1.f;
+        for (int i = 0; i < m; ++i) {
+          const float kk = bf(sm.k[nxt][sw128(s0 + i, ch)]);
+          acc = fmaf(a.rho, acc, kk * kk);
+          rm *= a.rho;
+        }
+        // compose the two halves' affine maps h -> rm h + acc
+        const float rm0 = __shfl(rm, lane & ~1, 64), ac0 = __shfl(acc, lane & ~1, 64);
+        const float rm1 = __shfl(rm, lane | 1, 64), ac1 = __shfl(acc, lane | 1, 64);
+        const float mid = fmaf(rm0, hcarry, ac0);
+        float hv = pc_seg == 0 ? hcarry : mid;
+        for (int i = 0; i < 32; ++i) {
+          float u = 0.f;
+          if (i < m) {
+            const float kk = bf(sm.k[nxt][sw128(s0 + i, ch)]);
+            hv = fmaf(a.rho, hv, kk * kk);
+            u = kk / fmaf(hv, sm.ic[nxt][s0 + i], a.eps);
+          }
+          const uint16_t ub = tobf(u);
+          sm.r[nxt][sw128(s0 + i, ch)] = ub;
+          sm.rt[nxt][sw64(ch, s0 + i)] = ub;
+        }
+        hcarry = fmaf(rm1, mid, ac1);
+      }
+      __syncthreads();   // (3)
     }
 
-    // ================= Phase D: D = T X  ->  D^T, (e^{g_C - g} D)^T =================
-    for (int o = wave; o < NOT; o += kNW) {
-      const int tb = o / NVB, vb = o % NVB;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile_mma(acc, &sm.t[0][0], kLdc, &sm.xt[0][0], kLdc, tb * 16, vb * 16, 0, tb < 2 ? 1 : 2, lane);
-      const int v = vb * 16 + l16;
-      short4v d1, d2;
+    if (have_next) {
+      const int nb = nxt;
+      if (hw < 2) {
+        // diagonal blocks 2 hw, 2 hw + 1 and the block between them
+        const int p0 = 2 * hw, p1 = 2 * hw + 1;
+        const float4v n0 = a_tile(nb, p0, p0, false);
+        GDR_FENCE();
+        const float4v n0t = a_tile(nb, p0, p0, true);
+        GDR_FENCE();
+        const float4v n1 = a_tile(nb, p1, p1, false);
+        GDR_FENCE();
+        const float4v n1t = a_tile(nb, p1, p1, true);
+        GDR_FENCE();
+        const float4v a10t = a_tile(nb, p1, p0, true);
+        GDR_FENCE();
+        float4v d0, d1, d1t;
+        diag_inverse(n0, n0t, d0, nullptr, lane);
+        GDR_FENCE();
+        diag_inverse(n1, n1t, d1, &d1t, lane);
+        GDR_FENCE();
+        // T_10 = D_1 A_10 D_0
+        const float4v zz = mfma16(tobf4(a10t), tobf4(d0), zero4());
+        const float4v t10 = mfma16(tobf4(d1t), tobf4(zz), zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb * 16 + 4 * l4 + r;
-        d1[r] = static_cast<short>(tobf(acc[r]));
-        d2[r] = static_cast<short>(tobf(sm.wd[t] * acc[r]));
+        for (int r = 0; r < 4; ++r) {
+          const int il = 4 * l4 + r, jl = l16;
+          sm.t[nb][p0 * 16 + il][p0 * 16 + jl] = (il >= jl && keep(il, jl)) ? tobf(d0[r]) : 0;
+          sm.t[nb][p1 * 16 + il][p1 * 16 + jl] = (il >= jl && keep(il, jl)) ? tobf(d1[r]) : 0;
+          sm.t[nb][p1 * 16 + il][p0 * 16 + jl] = keep(p1 * 16 + il, p0 * 16 + jl) ? tobf(t10[r]) : 0;
+        }
+      } else if (hw == 2) {
+        // A_ba = -L_ba (rows 32..63, columns 0..31) for the next phase's quadrant product
+#pragma unroll
+        for (int ib = 2; ib < 4; ++ib) {
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            const float4v x = a_tile(nb, ib, jb, false);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.lba[(ib - 2) * 16 + 4 * l4 + r][jb * 16 + l16] = tobf(x[r]);
+            GDR_FENCE();
+          }
+        }
       }
-      *reinterpret_cast<short4v *>(&sm.dt[v][tb * 16 + 4 * l4]) = d1;
-      *reinterpret_cast<short4v *>(&sm.dt2[v][tb * 16 + 4 * l4]) = d2;
-    }
-    __syncthreads();
-
-    // ============ Phase H: O = scale (O1 + P D) -> HBM;  S <- e^{g_C} S + D~^T R ============
-    for (int o = wave; o < NOT; o += kNW) {
-      const int tb = o / NVB, vb = o % NVB;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile_mma(acc, &sm.p[0][0], kLdc, &sm.dt[0][0], kLdc, tb * 16, vb * 16, 0, tb < 2 ? 1 : 2, lane);
-      const int v = vb * 16 + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb * 16 + 4 * l4 + r;
-        if (t < n)
-          gout[head0 + static_cast<long long>(c0 + t) * tokstride + v0 + v] =
-              tobf(a.scale * (sm.o1[t][v] + acc[r]));
-      }
-    }
-    {
-      const float gC = DECAY ? sm.eg[kC - 1] : 1.f;   // padded tokens carry alpha = 1
-#pragma unroll
-      for (int u = 0; u < SPW; ++u) {
-        const int st = wave + u * kNW;
-        const int vb = st / 8, cb = st % 8;
-        float4v acc = sacc[u];
-        if (DECAY) acc *= gC;
-        acc = tile_mma(acc, &sm.dt2[0][0], kLdc, &sm.rt[0][0], kLdc, vb * 16, cb * 16, 0, 2, lane);
-        sacc[u] = acc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.s[vb * 16 + 4 * l4 + r][cb * 16 + l16] = tobf(acc[r]);
-      }
+      stage2();
+      if (c + 2 < nchunks) load2(c + 2);
     }
   }
-
-  // ---- final state and preconditioner accumulator ----
-  if (a.state_out != nullptr) {
-#pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      const int st = wave + u * kNW;
-      const int vb = st / 8, cb = st % 8;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = vb * 16 + 4 * l4 + r, c = cb * 16 + l16;
-        a.state_out[(static_cast<long long>(bh) * kD + v0 + v) * kD + c] = sacc[u][r];
-      }
-    }
-  }
-  if (WK == kWkPrecond && a.pc_h_out != nullptr && vt == 0 && pc_seg == 0)
+  if (WK == kWkPrecond && a.pc_h_out != nullptr && vt == 0 && pc_thread && pc_seg == 0)
     a.pc_h_out[static_cast<long long>(bh) * kD + pc_c] = hcarry;
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
 hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
   const int grid = a.B * a.H * (kD / BV);
-  const bool band = a.N >= 0 && a.N <= 15;
-  if (band)
-    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true>), dim3(grid), dim3(kNT), 0, s, a);
-  else
-    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false>), dim3(grid), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK>), dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
 template <int BV>
 hipError_t launch_bv(const ChunkArgs &a, hipStream_t s) {
-  const bool chan = a.gain == GDR_GAIN_CHANNEL, decay = a.decay == GDR_DECAY_SCALAR;
-  const int wk = a.wkey == GDR_WKEY_DIAG_PRECOND ? kWkPrecond : a.wkey == GDR_WKEY_EXPLICIT ? kWkExplicit : kWkSame;
-  if (chan) {
-    // channel gains with a separate write key exceed the LDS budget (not instantiated)
+  const bool decay = a.decay == GDR_DECAY_SCALAR;
+  if (a.gain == GDR_GAIN_CHANNEL)   // channel gains only with the write key equal to the key
     return decay ? launch4<BV, true, true, kWkSame>(a, s) : launch4<BV, true, false, kWkSame>(a, s);
-  }
-  switch (wk) {
-    case kWkPrecond:
+  switch (a.wkey) {
+    case GDR_WKEY_DIAG_PRECOND:
       return decay ? launch4<BV, false, true, kWkPrecond>(a, s) : launch4<BV, false, false, kWkPrecond>(a, s);
-    case kWkExplicit:
+    case GDR_WKEY_EXPLICIT:
       return decay ? launch4<BV, false, true, kWkExplicit>(a, s) : launch4<BV, false, false, kWkExplicit>(a, s);
     default:
       return decay ? launch4<BV, false, true, kWkSame>(a, s) : launch4<BV, false, false, kWkSame>(a, s);
@@ -590,14 +671,14 @@ bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const floa
                          const float *state_out) {
   if (d.io_dtype != GDR_BF16 || d.Dk != kD || d.Dv != kD || d.chunk != kC) return false;
   if (d.gain == GDR_GAIN_CHANNEL && d.wkey != GDR_WKEY_SAME) return false;
-  const void *p16[] = {in.q, in.k, in.v, in.erase, in.write, in.write_key, out};
+  const void *p16[] = {in.q, in.k, in.v, in.erase, in.write, in.write_key, out, state_in, state_out};
   for (const void *p : p16)
     if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
   return true;
 }
 
 // Value-tile width: the widest tile that still gives every CU a workgroup.
-int chunk_mfma_bv(int B, int H) { return (static_cast<long long>(B) * H * (kD / 32) >= 256) ? 32 : 16; }
+static int chunk_mfma_bv(int B, int H) { return (static_cast<long long>(B) * H * (kD / 32) >= 256) ? 32 : 16; }
 
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
   return chunk_mfma_bv(a.B, a.H) == 32 ? launch_bv<32>(a, s) : launch_bv<16>(a, s);
