@@ -69,16 +69,16 @@ __device__ __forceinline__ int sw64(int row, int col) {
 
 template <int BV, bool CHAN, int WK>
 struct __align__(16) Smem {
-  uint16_t q[kC * kD];                                     // Q (one buffer)
+  uint16_t q[2][kC * kD];                                  // Q
   uint16_t k[2][kC * kD];                                  // K
   uint16_t e[CHAN ? 2 : 1][CHAN ? kC * kD : 8];            // erase key b (.) k
   uint16_t r[WK != kWkSame ? 2 : 1][WK != kWkSame ? kC * kD : 8];   // write key if != k
-  uint16_t rt[2][kD * kC];                                 // R^T
-  uint16_t vpt[2][BV][kLdc];                               // V'^T; output staging later
+  uint16_t rt[kD * kC];                                    // R^T (current chunk)
+  uint16_t vp[2][kC][BV + 8];                              // v tile (w (.) v with channel gains)
   uint16_t t[2][kC][kLdc];                                 // T
   uint16_t p[kC][kLdc];                                    // P (one buffer)
   uint16_t lba[32][kLdl];                                  // A_ba = -L_ba
-  float g2[2][kC], eg[2][kC], wd[2][kC], cy[2][kC], beta[2][kC], ic[2][kC];
+  float g2[2][kC], eg[2][kC], wd[2][kC], beta[2][kC], ic[2][kC];
 };
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -88,11 +88,6 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 __device__ __forceinline__ float elem(const uint4 &v, int e) { return bf(word(v, e)); }
-__device__ __forceinline__ uint4 ldg16(const uint16_t *p, bool ok) {
-  uint4 r = make_uint4(0u, 0u, 0u, 0u);
-  if (ok) r = *reinterpret_cast<const uint4 *>(p);
-  return r;
-}
 
 __device__ __forceinline__ short8v ld8(const uint16_t *p) { return *reinterpret_cast<const short8v *>(p); }
 __device__ __forceinline__ short4v ld4(const uint16_t *p) { return *reinterpret_cast<const short4v *>(p); }
@@ -129,6 +124,13 @@ __device__ __forceinline__ short4v ld4col(const uint16_t *p, int ld) {
 }
 __device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ float4v zero4() { return float4v{0.f, 0.f, 0.f, 0.f}; }
+// the 16 x 16 identity as a K = 16 operand (A or B layout: 1.0 where K index == l % 16)
+__device__ __forceinline__ short4v ident4(int lane) {
+  short4v r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (4 * (lane >> 4) + i == (lane & 15)) ? static_cast<short>(0x3F80) : static_cast<short>(0);
+  return r;
+}
 // keep the scheduler from hoisting the next tile's operand loads above this point
 // (bounds register pressure; the hardware still overlaps the independent work)
 #define GDR_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -180,13 +182,11 @@ template <int BV, bool CHAN, bool DECAY, int WK>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
-  constexpr int NH = (kNW - NVW) * 64;     // helper threads
+  constexpr int NHW = kNW - NVW;           // helper waves
   constexpr int NVI = kC * BV / 8;         // V items (8 bf16 each)
-  // staging items: [k ... | r ... | v ...] staged in phase 1, [q ...] in phase 2
-  constexpr int NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
-  constexpr int N1 = NK + NR + NVI;
-  constexpr int S1 = (N1 + NH - 1) / NH;   // phase-1 slots per helper thread
-  constexpr int S2 = (1024 + NH - 1) / NH; // q slots
+  constexpr int LDV = BV + 8;              // padded row stride of the V' tile
+  // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
+  constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
   constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
   __shared__ Smem<BV, CHAN, WK> sm;
 
@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const bool vwave = wave < NVW;
   const int hw = wave - NVW;               // helper wave index
   const int ht = tid - NVW * 64;           // helper thread index
+  const short4v I16 = ident4(lane);
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
   const int G = static_cast<int>(gridDim.x);
@@ -222,152 +223,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
   uint16_t *gout = static_cast<uint16_t *>(a.out);
 
-  // ---------------- one-time init: zero T (upper blocks stay zero) ----------------
+  // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
   for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = 0;
   for (int i = tid; i < kC * kLdc; i += kNT) (&sm.p[0][0])[i] = 0;
-
-  // ---------------- helper prefetch registers ----------------
-  uint4 pa[S1], pb[S1], pqv[S2];
-  float pbeta_v[S1];
-#pragma unroll
-  for (int s = 0; s < S1; ++s) {
-    pa[s] = pb[s] = make_uint4(0u, 0u, 0u, 0u);
-    pbeta_v[s] = 0.f;
-  }
-#pragma unroll
-  for (int s = 0; s < S2; ++s) pqv[s] = make_uint4(0u, 0u, 0u, 0u);
-  float gla = 0.f, gbeta = 0.f;            // gate item (last helper wave)
-  const bool gate_wave = wave == kNW - 1;
-
-  auto load1 = [&](int c) {                // phase-1 items of chunk c
-    const int c0 = c * kC, n = min(kC, T - c0);
-#pragma unroll
-    for (int s = 0; s < S1; ++s) {
-      const int it = ht + s * NH;
-      if (it < NK + NR) {
-        const int u = it < NK ? it : it - NK;
-        const int t = u >> 4, col = (u & 15) * 8;
-        const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + col;
-        const bool ok = t < n;
-        if (it < NK) {
-          pa[s] = ldg16(gk + off, ok);
-          if (CHAN) pb[s] = ldg16(ger + off, ok);
-        } else {
-          pa[s] = ldg16(gwk + off, ok);
-        }
-      } else if (it < N1) {
-        const int u = it - NK - NR;
-        const int t = u / (BV / 8), col = (u % (BV / 8)) * 8;
-        const bool ok = t < n;
-        const long long off = head0 + static_cast<long long>(c0 + t) * tokstride + v0 + col;
-        pa[s] = ldg16(gv + off, ok);
-        if (CHAN) pb[s] = ldg16(gwr + off, ok);
-        else pbeta_v[s] = ok ? a.beta[gate0 + static_cast<long long>(c0 + t) * H] : 0.f;
-      }
-    }
-    if (gate_wave) {
-      const bool ok = lane < n;
-      const long long gi = gate0 + static_cast<long long>(c0 + lane) * H;
-      gla = (DECAY && ok) ? a.log_alpha[gi] : 0.f;
-      gbeta = (!CHAN && ok) ? a.beta[gi] : 0.f;
-    }
-  };
-  auto load2 = [&](int c) {                // q items of chunk c
-    const int c0 = c * kC, n = min(kC, T - c0);
-#pragma unroll
-    for (int s = 0; s < S2; ++s) {
-      const int u = ht + s * NH;
-      if (u < 1024) {
-        const int t = u >> 4, col = (u & 15) * 8;
-        pqv[s] = ldg16(gq + head0 + static_cast<long long>(c0 + t) * tokstride + col, t < n);
-      }
-    }
-  };
-  auto stage1 = [&](int c, int buf) {      // registers -> LDS, phase-1 items, and gates
-    const int n = min(kC, T - c * kC);
-#pragma unroll
-    for (int s = 0; s < S1; ++s) {
-      const int it = ht + s * NH;
-      if (it < NK + NR) {
-        const int u = it < NK ? it : it - NK;
-        const int t = u >> 4, col = (u & 15) * 8;
-        if (it < NK) {
-          *reinterpret_cast<uint4 *>(&sm.k[buf][sw128(t, col)]) = pa[s];
-          if (WK == kWkSame) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.rt[buf][sw64(col + e, t)] = static_cast<uint16_t>(word(pa[s], e));
-          }
-          if (CHAN) {
-            uint4 ev;
-            ev.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(pa[s], 0), elem(pb[s], 1) * elem(pa[s], 1));
-            ev.y = f32x2_to_bf16x2_bits(elem(pb[s], 2) * elem(pa[s], 2), elem(pb[s], 3) * elem(pa[s], 3));
-            ev.z = f32x2_to_bf16x2_bits(elem(pb[s], 4) * elem(pa[s], 4), elem(pb[s], 5) * elem(pa[s], 5));
-            ev.w = f32x2_to_bf16x2_bits(elem(pb[s], 6) * elem(pa[s], 6), elem(pb[s], 7) * elem(pa[s], 7));
-            *reinterpret_cast<uint4 *>(&sm.e[buf][sw128(t, col)]) = ev;
-          }
-        } else {
-          *reinterpret_cast<uint4 *>(&sm.r[buf][sw128(t, col)]) = pa[s];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.rt[buf][sw64(col + e, t)] = static_cast<uint16_t>(word(pa[s], e));
-        }
-      } else if (it < N1) {
-        const int u = it - NK - NR;
-        const int t = u / (BV / 8), col = (u % (BV / 8)) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sm.vpt[buf][col + e][t] = tobf(CHAN ? elem(pb[s], e) * elem(pa[s], e) : pbeta_v[s] * elem(pa[s], e));
-      }
-    }
-    if (gate_wave) {
-      float g = gla * kLog2e;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(g, d, 64);
-        if (lane >= d) g += y;
-      }
-      const float glast = __shfl(g, n - 1, 64);
-      const float egv = DECAY ? exp2f(g) : 1.f;
-      sm.g2[buf][lane] = g;
-      sm.eg[buf][lane] = egv;
-      sm.wd[buf][lane] = DECAY ? exp2f(glast - g) : 1.f;
-      sm.cy[buf][lane] = CHAN ? egv : gbeta * egv;
-      sm.beta[buf][lane] = gbeta;
-      if (WK == kWkPrecond) {
-        const float tg = static_cast<float>(a.t0 + static_cast<long long>(c) * kC + lane + 1);
-        sm.ic[buf][lane] = 1.f / (-expm1f(tg * a.log_rho));   // 1 / (1 - rho^t)
-      }
-    }
-  };
-  auto stage2 = [&]() {                    // q registers -> LDS
-#pragma unroll
-    for (int s = 0; s < S2; ++s) {
-      const int u = ht + s * NH;
-      if (u < 1024) *reinterpret_cast<uint4 *>(&sm.q[sw128(u >> 4, (u & 15) * 8)]) = pqv[s];
-    }
-  };
-
-  // raw (E R^T) tile for rows ib, cols jb (trans: the transposed tile), scaled to A = -L
-  auto a_tile = [&](int buf, int ib, int jb, bool trans) -> float4v {
-    const uint16_t *E = CHAN ? sm.e[buf] : sm.k[buf];
-    const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
-    const uint16_t *A = trans ? R : E;
-    const uint16_t *B = trans ? E : R;
-    const int ra = (trans ? jb : ib) * 16 + l16, rb = (trans ? ib : jb) * 16 + l16;
-    float4v acc = zero4();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma32(opn128(A, ra, 32 * s, l4), opn128(B, rb, 32 * s, l4), acc);
-    // lane holds element (i, j) of L for i = row index of L, j = column index of L
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = trans ? ib * 16 + l16 : ib * 16 + 4 * l4 + r;
-      const int j = trans ? jb * 16 + 4 * l4 + r : jb * 16 + l16;
-      float x = acc[r];
-      if (SCALED_E) x *= sm.beta[buf][i];
-      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
-      acc[r] = (j < i) ? -x : 0.f;
-    }
-    return acc;
-  };
 
   // Each role runs its own loop with the same barrier sequence, so the compiler allocates
   // registers for one role's loop-carried state at a time.
@@ -392,7 +250,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       float4v O1[4];
       __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
       if (c >= 0) {
-        // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - cy Y
+        // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y
         short8v sb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
@@ -403,21 +261,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             y = mfma32(ops128(E, tb * 16 + l16, 32 * j, l4), sb[j], y);
-            o = mfma32(ops128(sm.q, tb * 16 + l16, 32 * j, l4), sb[j], o);
+            o = mfma32(ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4), sb[j], o);
           }
+          // V' block (rows t, columns v) brought to the accumulator layout by an identity product
+          const float4v vpa = mfma16(ld4(&sm.vp[cur][tb * 16 + l16][16 * wave + 4 * l4]), I16, zero4());
           const int t0 = tb * 16 + 4 * l4;
-          const float4 cy = ld4f(&sm.cy[cur][t0]);
           const float4 eg = ld4f(&sm.eg[cur][t0]);
-          const short4v vp = ld4(&sm.vpt[cur][16 * wave + l16][t0]);
-          x4[tb] = tobf4(float4v{bf(static_cast<uint16_t>(vp[0])) - cy.x * y[0],
-                                 bf(static_cast<uint16_t>(vp[1])) - cy.y * y[1],
-                                 bf(static_cast<uint16_t>(vp[2])) - cy.z * y[2],
-                                 bf(static_cast<uint16_t>(vp[3])) - cy.w * y[3]});
+          float4v xv = float4v{vpa[0] - eg.x * y[0], vpa[1] - eg.y * y[1], vpa[2] - eg.z * y[2], vpa[3] - eg.w * y[3]};
+          if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
+            const float4 bt = ld4f(&sm.beta[cur][t0]);
+            xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
+          }
+          x4[tb] = tobf4(xv);
           O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
           GDR_FENCE();
         }
       }
-      __syncthreads();   // (2) T(c) and P(c) complete
+      __syncthreads();   // (2) T(c), P(c), R^T(c) complete
       if (c >= 0) {
         const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
         // D = T X
@@ -444,6 +304,20 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 0, l4), d01, zero4());
         O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 32, l4), d23, O2[3]);
         GDR_FENCE();
+        // output: transpose each 16 x 16 block by an identity product so a lane holds four
+        // consecutive values of one token, then 8-byte stores
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float4v o = a.scale * (O1[tb] + O2[tb]);
+          const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
+          const int t = tb * 16 + l16;
+          if (t < n) {
+            const short4v pk = tobf4(ot);
+            *reinterpret_cast<short4v *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * wave +
+                                         4 * l4) = pk;
+          }
+        }
+        GDR_FENCE();
         // state update S^T <- e^{g_C} S^T + R^T (wd (.) D)
         short4v w4[4];
 #pragma unroll
@@ -457,25 +331,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         for (int cb = 0; cb < 8; ++cb) {
           float4v acc = st[cb];
           if (DECAY) acc *= gC;
-          acc = mfma32(ops64(sm.rt[cur], cb * 16 + l16, 0, l4), w01, acc);
-          acc = mfma32(ops64(sm.rt[cur], cb * 16 + l16, 32, l4), w23, acc);
+          acc = mfma32(ops64(sm.rt, cb * 16 + l16, 0, l4), w01, acc);
+          acc = mfma32(ops64(sm.rt, cb * 16 + l16, 32, l4), w23, acc);
           st[cb] = acc;
           if (cb & 1) GDR_FENCE();
-        }
-        // output: stage this wave's 64 x 16 block in LDS, then 16-byte stores
-        uint16_t *ost = &sm.vpt[cur][0][0] + wave * (kC * 16);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ost[(tb * 16 + 4 * l4 + r) * 16 + l16] = tobf(a.scale * (O1[tb][r] + O2[tb][r]));
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t = half * 32 + (lane >> 1), part = lane & 1;
-          const uint4 val = *reinterpret_cast<const uint4 *>(ost + t * 16 + part * 8);
-          if (t < n)
-            *reinterpret_cast<uint4 *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * wave +
-                                       part * 8) = val;
         }
       }
       if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
@@ -489,7 +348,139 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     return;
   }
 
-  // ---------------- helper waves ----------------
+  // ============================== helper waves ==============================
+  // One staging point per chunk: every item of chunk c + 1 is written to LDS from registers
+  // loaded a full iteration earlier, then the loads of chunk c + 2 are issued.  Items are
+  // 16-byte granules in blocks of 64 (one wave-wide load): 16 blocks each of q, k and an
+  // explicit write key (64 x 128 bf16), then the blocks of the 64 x BV value tile.  Block
+  // s * NHW + hw is slot s of helper wave hw, so everything about a block (source, LDS
+  // destination, row / column split) is wave-uniform.  Every slot loads and is staged
+  // unconditionally -- a slot past the last block repeats it without storing -- so the
+  // registers of a load are first read one iteration after it was issued and the loads of
+  // a chunk issue back to back.  Rows past the end of the sequence are read clamped to the
+  // last row and zeroed when staged.
+  constexpr int NBP = (NQ + NK + NR) / 64;     // blocks of 64 x 128 arrays
+  constexpr int NB = NBP + NVI / 64;
+  constexpr int NSB = (NB + NHW - 1) / NHW;    // block slots per helper wave
+  constexpr int VSH = BV == 32 ? 2 : 1;        // log2(items per value-tile row)
+  uint4 pa[NSB], pb[NSB];
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) pa[s] = pb[s] = make_uint4(0u, 0u, 0u, 0u);
+  float gla = 0.f, gbeta = 0.f;                // gates of token `lane` of the staged chunk
+  const bool gate_wave = wave == kNW - 1;
+  const int tok32 = H * kD;                    // token stride; 64 * tok32 < 2^31 (H <= 65535)
+  auto slot_block = [&](int s) { return min(s * NHW + hw, NB - 1); };
+  // item u of block blk: row u >> sh, column col0 + (u & msk) * 8
+  auto item_rc = [&](int blk, int &t, int &col) {
+    const bool isv = blk >= NBP;
+    const int u = (isv ? blk - NBP : blk & 15) * 64 + lane;
+    t = isv ? u >> VSH : u >> 4;
+    col = isv ? (u & (BV / 8 - 1)) * 8 : (u & 15) * 8;
+  };
+
+  auto load_items = [&](int c) {
+    const int c0 = c * kC, nm1 = min(kC, T - c0) - 1;
+    const long long cb = head0 + static_cast<long long>(c0) * tokstride;   // chunk base (uniform)
+#pragma unroll
+    for (int s = 0; s < NSB; ++s) {
+      const int blk = slot_block(s);
+      const bool isv = blk >= NBP;
+      const int arr = blk >> 4;
+      int t, col;
+      item_rc(blk, t, col);
+      const int off = min(t, nm1) * tok32 + (isv ? v0 : 0) + col;
+      const uint16_t *src = isv ? gv : arr == 0 ? gq : arr == 1 ? gk : gwk;
+      pa[s] = *reinterpret_cast<const uint4 *>(src + cb + off);
+      if (CHAN) pb[s] = *reinterpret_cast<const uint4 *>((isv ? gwr : ger) + cb + off);
+    }
+    const long long gi = gate0 + static_cast<long long>(c0) * H + min(lane, nm1) * H;
+    if (DECAY) gla = a.log_alpha[gi];
+    if (!CHAN) gbeta = a.beta[gi];
+  };
+  auto stage_items = [&](int c, int buf) {
+    const int n = min(kC, T - c * kC);
+#pragma unroll
+    for (int s = 0; s < NSB; ++s) {
+      const int blk = slot_block(s);
+      const bool live = s * NHW + hw < NB;
+      const bool isv = blk >= NBP;
+      const int arr = blk >> 4;
+      int t, col;
+      item_rc(blk, t, col);
+      const uint32_t m = t < n ? 0xffffffffu : 0u;
+      const uint4 x = make_uint4(pa[s].x & m, pa[s].y & m, pa[s].z & m, pa[s].w & m);
+      uint4 xg = x;   // gated copy: erase (.) k, write (.) v
+      if (CHAN) {
+        xg.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(x, 0), elem(pb[s], 1) * elem(x, 1));
+        xg.y = f32x2_to_bf16x2_bits(elem(pb[s], 2) * elem(x, 2), elem(pb[s], 3) * elem(x, 3));
+        xg.z = f32x2_to_bf16x2_bits(elem(pb[s], 4) * elem(x, 4), elem(pb[s], 5) * elem(x, 5));
+        xg.w = f32x2_to_bf16x2_bits(elem(pb[s], 6) * elem(x, 6), elem(pb[s], 7) * elem(x, 7));
+      }
+      if (live) {
+        if (isv) {
+          *reinterpret_cast<uint4 *>(&sm.vp[buf][t][col]) = xg;
+        } else {
+          uint16_t *dst = arr == 0 ? sm.q[buf] : arr == 1 ? sm.k[buf] : sm.r[buf];
+          *reinterpret_cast<uint4 *>(&dst[sw128(t, col)]) = x;
+          if (CHAN && arr == 1) *reinterpret_cast<uint4 *>(&sm.e[buf][sw128(t, col)]) = xg;
+        }
+      }
+    }
+    // gates: cumulative log decay in log2 units and the quantities derived from it
+    const bool ok = lane < n;
+    const float beta_t = ok ? gbeta : 0.f;
+    float g = ok ? gla * kLog2e : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(g, d, 64);
+      if (lane >= d) g += y;
+    }
+    const float glast = __shfl(g, n - 1, 64);
+    if (gate_wave) {
+      sm.g2[buf][lane] = g;
+      sm.eg[buf][lane] = DECAY ? exp2f(g) : 1.f;
+      sm.wd[buf][lane] = DECAY ? exp2f(glast - g) : 1.f;
+      sm.beta[buf][lane] = beta_t;
+      if (WK == kWkPrecond) {
+        const float tg = static_cast<float>(a.t0 + static_cast<long long>(c) * kC + lane + 1);
+        sm.ic[buf][lane] = 1.f / (-expm1f(tg * a.log_rho));   // 1 / (1 - rho^t)
+      }
+    }
+  };
+  // (E R^T) tile for rows ib, cols jb (trans: the transposed tile), scaled to A = -L
+  auto a_tile = [&](int buf, int ib, int jb, bool trans) -> float4v {
+    const uint16_t *E = CHAN ? sm.e[buf] : sm.k[buf];
+    const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
+    const uint16_t *A = trans ? R : E;
+    const uint16_t *B = trans ? E : R;
+    const int ra = (trans ? jb : ib) * 16 + l16, rb = (trans ? ib : jb) * 16 + l16;
+    float4v acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma32(opn128(A, ra, 32 * s, l4), opn128(B, rb, 32 * s, l4), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = trans ? ib * 16 + l16 : ib * 16 + 4 * l4 + r;
+      const int j = trans ? jb * 16 + 4 * l4 + r : jb * 16 + l16;
+      float x = acc[r];
+      if (SCALED_E) x *= sm.beta[buf][i];
+      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
+      acc[r] = (j < i) ? -x : 0.f;
+    }
+    return acc;
+  };
+  // write acc(X^T) of the 16 x 16 block (rb, cb) of a row-major [64][kLdc] bf16 matrix as
+  // 8-byte rows (lane: row rb*16 + l16, columns cb*16 + 4 l4 .. + 3), band-masked
+  auto put_rows = [&](uint16_t *M, int rb, int cb, float4v xt, bool lower_only) {
+    const int i = rb * 16 + l16;
+    float4v v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = cb * 16 + 4 * l4 + r;
+      v[r] = (keep(i, j) && (!lower_only || j <= i)) ? xt[r] : 0.f;
+    }
+    *reinterpret_cast<short4v *>(M + i * kLdc + cb * 16 + 4 * l4) = tobf4(v);
+  };
+
   // preconditioner accumulator: helper threads ht < 256 own channel ht / 2, token half ht % 2
   const bool pc_thread = ht < 256;
   const int pc_c = ht >> 1, pc_seg = ht & 1;
@@ -497,15 +488,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   if (WK == kWkPrecond && pc_thread)
     hcarry = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + pc_c] : a.h0;
 
-  if (nchunks > 0) {
-    load1(0);
-    load2(0);
-  }
+  if (nchunks > 0) load_items(0);
   for (int c = -1; c < nchunks; ++c) {
     const int cur = c & 1, nxt = (c + 1) & 1;
     const bool have_next = c + 1 < nchunks;
 
     __syncthreads();   // (1)
+    if (have_next) {
+      stage_items(c + 1, nxt);
+      if (c + 2 < nchunks) load_items(c + 2);
+    }
     if (c >= 0) {
       if (hw < 2) {
         // T_ba = T_b A_ba T_a, column block qb of the lower-left quadrant
@@ -526,36 +518,41 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         for (int sp = 0; sp < 2; ++sp) {
           float4v tt = mfma16(ld4(&sm.t[cur][32 + sp * 16 + l16][32 + 4 * l4]), z0, zero4());
           if (sp == 1) tt = mfma16(ld4(&sm.t[cur][48 + l16][48 + 4 * l4]), z1, tt);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 32 + sp * 16 + 4 * l4 + r, j = qb * 16 + l16;
-            sm.t[cur][i][j] = keep(i, j) ? tobf(tt[r]) : 0;
-          }
+          put_rows(&sm.t[cur][0][0], 2 + sp, qb, mfma16(tobf4(tt), I16, zero4()), false);
         }
       } else {
-        // P tiles (lower triangle incl. diagonal blocks)
+        // P tiles, computed transposed (P^T = R Q^T) so each lane writes 4 columns of a row
         const uint16_t *R = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-        for (int job = hw - 2; job < 10; job += (kNW - NVW - 2)) {
+        for (int job = hw - 2; job < 10; job += (NHW - 2)) {
           const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
           const int jb = job - ib * (ib + 1) / 2;
           float4v acc = zero4();
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            acc = mfma32(opn128(sm.q, ib * 16 + l16, 32 * s, l4), opn128(R, jb * 16 + l16, 32 * s, l4), acc);
-          const int j = jb * 16 + l16;
+            acc = mfma32(opn128(R, jb * 16 + l16, 32 * s, l4), opn128(sm.q[cur], ib * 16 + l16, 32 * s, l4), acc);
+          // lane: P[i = ib*16 + l16][j = jb*16 + 4 l4 + r]
+          const int i = ib * 16 + l16;
+          float4v v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int i = ib * 16 + 4 * l4 + r;
+            const int j = jb * 16 + 4 * l4 + r;
             float x = acc[r];
             if (DECAY) x *= exp2f(sm.g2[cur][i] - sm.g2[cur][j]);
-            sm.p[i][j] = (j <= i) ? tobf(x) : 0;
+            v[r] = (j <= i) ? x : 0.f;
           }
+          *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(v);
         }
       }
-    }
-    if (have_next) {
-      stage1(c + 1, nxt);
-      if (c + 2 < nchunks) load1(c + 2);
+      // R^T of chunk c for the state update, by identity products on 16 x 16 blocks
+      {
+        const uint16_t *R = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
+        for (int job = hw; job < 32; job += NHW) {
+          const int tb = job >> 3, cb = job & 7;
+          const float4v x = mfma16(ld4(R + sw128(tb * 16 + l16, cb * 16 + 4 * l4)), I16, zero4());
+          // lane: R[t = tb*16 + 4 l4 + r][c = cb*16 + l16]
+          *reinterpret_cast<short4v *>(&sm.rt[sw64(cb * 16 + l16, tb * 16 + 4 * l4)]) = tobf4(x);
+        }
+      }
     }
     __syncthreads();   // (2)
 
@@ -583,9 +580,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             hv = fmaf(a.rho, hv, kk * kk);
             u = kk / fmaf(hv, sm.ic[nxt][s0 + i], a.eps);
           }
-          const uint16_t ub = tobf(u);
-          sm.r[nxt][sw128(s0 + i, ch)] = ub;
-          sm.rt[nxt][sw64(ch, s0 + i)] = ub;
+          sm.r[nxt][sw128(s0 + i, ch)] = tobf(u);
         }
         hcarry = fmaf(rm1, mid, ac1);
       }
@@ -598,45 +593,35 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // diagonal blocks 2 hw, 2 hw + 1 and the block between them
         const int p0 = 2 * hw, p1 = 2 * hw + 1;
         const float4v n0 = a_tile(nb, p0, p0, false);
-        GDR_FENCE();
         const float4v n0t = a_tile(nb, p0, p0, true);
         GDR_FENCE();
         const float4v n1 = a_tile(nb, p1, p1, false);
-        GDR_FENCE();
         const float4v n1t = a_tile(nb, p1, p1, true);
         GDR_FENCE();
         const float4v a10t = a_tile(nb, p1, p0, true);
         GDR_FENCE();
-        float4v d0, d1, d1t;
-        diag_inverse(n0, n0t, d0, nullptr, lane);
-        GDR_FENCE();
+        float4v d0, d0t, d1, d1t;
+        diag_inverse(n0, n0t, d0, &d0t, lane);
         diag_inverse(n1, n1t, d1, &d1t, lane);
         GDR_FENCE();
         // T_10 = D_1 A_10 D_0
         const float4v zz = mfma16(tobf4(a10t), tobf4(d0), zero4());
         const float4v t10 = mfma16(tobf4(d1t), tobf4(zz), zero4());
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int il = 4 * l4 + r, jl = l16;
-          sm.t[nb][p0 * 16 + il][p0 * 16 + jl] = (il >= jl && keep(il, jl)) ? tobf(d0[r]) : 0;
-          sm.t[nb][p1 * 16 + il][p1 * 16 + jl] = (il >= jl && keep(il, jl)) ? tobf(d1[r]) : 0;
-          sm.t[nb][p1 * 16 + il][p0 * 16 + jl] = keep(p1 * 16 + il, p0 * 16 + jl) ? tobf(t10[r]) : 0;
-        }
+        uint16_t *Tn = &sm.t[nb][0][0];
+        put_rows(Tn, p0, p0, d0t, true);
+        put_rows(Tn, p1, p1, d1t, true);
+        put_rows(Tn, p1, p0, mfma16(tobf4(t10), I16, zero4()), false);
       } else if (hw == 2) {
-        // A_ba = -L_ba (rows 32..63, columns 0..31) for the next phase's quadrant product
+        // A_ba = -L_ba (rows 32..63, columns 0..31), transposed tiles -> 8-byte rows
 #pragma unroll
         for (int ib = 2; ib < 4; ++ib) {
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
-            const float4v x = a_tile(nb, ib, jb, false);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.lba[(ib - 2) * 16 + 4 * l4 + r][jb * 16 + l16] = tobf(x[r]);
-            GDR_FENCE();
+            const float4v x = a_tile(nb, ib, jb, true);   // lane: A[ib*16 + l16][jb*16 + 4 l4 + r]
+            *reinterpret_cast<short4v *>(&sm.lba[(ib - 2) * 16 + l16][jb * 16 + 4 * l4]) = tobf4(x);
           }
         }
       }
-      stage2();
-      if (c + 2 < nchunks) load2(c + 2);
     }
   }
   if (WK == kWkPrecond && a.pc_h_out != nullptr && vt == 0 && pc_thread && pc_seg == 0)
