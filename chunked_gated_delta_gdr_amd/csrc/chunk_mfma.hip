@@ -63,9 +63,6 @@ enum : int { kWkSame = 0, kWkPrecond = 1, kWkExplicit = 2 };
 __device__ __forceinline__ int sw128(int row, int col) {
   return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
 }
-__device__ __forceinline__ int sw64(int row, int col) {
-  return row * 64 + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
-}
 
 template <int BV, bool CHAN, int WK>
 struct __align__(16) Smem {
@@ -73,7 +70,6 @@ struct __align__(16) Smem {
   uint16_t k[2][kC * kD];                                  // K
   uint16_t e[CHAN ? 2 : 1][CHAN ? kC * kD : 8];            // erase key b (.) k
   uint16_t r[WK != kWkSame ? 2 : 1][WK != kWkSame ? kC * kD : 8];   // write key if != k
-  uint16_t rt[kD * kC];                                    // R^T (current chunk)
   uint16_t vp[2][kC][BV + 8];                              // v tile (w (.) v with channel gains)
   uint16_t t[2][kC][kLdc];                                 // T
   uint16_t p[kC][kLdc];                                    // P (one buffer)
@@ -90,6 +86,14 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int e) {
 __device__ __forceinline__ float elem(const uint4 &v, int e) { return bf(word(v, e)); }
 
 __device__ __forceinline__ short8v ld8(const uint16_t *p) { return *reinterpret_cast<const short8v *>(p); }
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// receives element j % 4 of the 8-byte rows addressed by lanes 4 i + j / 4, i = 0..3.  If
+// lane s of group g addresses M[k0 + 4 g + s / 4][m0 + 4 (s % 4) ..], lane j of group g gets
+// M[k0 + 4 g + i][m0 + j]: the K = 16 operand (or accumulator) layout of the block's transpose.
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+__device__ __forceinline__ short4v ldtr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
+}
 __device__ __forceinline__ short4v ld4(const uint16_t *p) { return *reinterpret_cast<const short4v *>(p); }
 __device__ __forceinline__ short8v cat(short4v a, short4v b) {
   return short8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -114,14 +118,6 @@ __device__ __forceinline__ short4v tobf4(float4v v) {
   r[3] = static_cast<short>(hi >> 16);
   return r;
 }
-__device__ __forceinline__ short4v ld4col(const uint16_t *p, int ld) {
-  short4v r;
-  r[0] = static_cast<short>(p[0]);
-  r[1] = static_cast<short>(p[ld]);
-  r[2] = static_cast<short>(p[2 * ld]);
-  r[3] = static_cast<short>(p[3 * ld]);
-  return r;
-}
 __device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ float4v zero4() { return float4v{0.f, 0.f, 0.f, 0.f}; }
 // the 16 x 16 identity as a K = 16 operand (A or B layout: 1.0 where K index == l % 16)
@@ -144,8 +140,11 @@ __device__ __forceinline__ short8v opn128(const uint16_t *a, int row, int k0, in
 __device__ __forceinline__ short8v ops128(const uint16_t *a, int row, int k0, int l4) {
   return cat(ld4(a + sw128(row, k0 + 4 * l4)), ld4(a + sw128(row, k0 + 16 + 4 * l4)));
 }
-__device__ __forceinline__ short8v ops64(const uint16_t *a, int row, int k0, int l4) {
-  return cat(ld4(a + sw64(row, k0 + 4 * l4)), ld4(a + sw64(row, k0 + 16 + 4 * l4)));
+// split-K operand of M^T from a row-major swizzled [K][128] matrix: rows m0 + l % 16 of M^T,
+// K = k0 + 4 (l / 16) + i and k0 + 16 + 4 (l / 16) + i (transposing reads, see ldtr)
+__device__ __forceinline__ short8v optr128(const uint16_t *a, int m0, int k0, int lane) {
+  const int r = 4 * (lane >> 4) + ((lane & 15) >> 2), c = m0 + 4 * (lane & 3);
+  return cat(ldtr(a + sw128(k0 + r, c)), ldtr(a + sw128(k0 + 16 + r, c)));
 }
 __device__ __forceinline__ short8v opsp(const uint16_t *a, int ld, int row, int k0, int l4) {
   return cat(ld4(a + row * ld + k0 + 4 * l4), ld4(a + row * ld + k0 + 16 + 4 * l4));
@@ -263,8 +262,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             y = mfma32(ops128(E, tb * 16 + l16, 32 * j, l4), sb[j], y);
             o = mfma32(ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4), sb[j], o);
           }
-          // V' block (rows t, columns v) brought to the accumulator layout by an identity product
-          const float4v vpa = mfma16(ld4(&sm.vp[cur][tb * 16 + l16][16 * wave + 4 * l4]), I16, zero4());
+          // V' block (rows t, columns v) in the accumulator layout, read transposed
+          const short4v vt4 = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * wave + 4 * (l16 & 3)]);
+          const float4v vpa = float4v{bf(static_cast<uint16_t>(vt4[0])), bf(static_cast<uint16_t>(vt4[1])),
+                                      bf(static_cast<uint16_t>(vt4[2])), bf(static_cast<uint16_t>(vt4[3]))};
           const int t0 = tb * 16 + 4 * l4;
           const float4 eg = ld4f(&sm.eg[cur][t0]);
           float4v xv = float4v{vpa[0] - eg.x * y[0], vpa[1] - eg.y * y[1], vpa[2] - eg.z * y[2], vpa[3] - eg.w * y[3]};
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           GDR_FENCE();
         }
       }
-      __syncthreads();   // (2) T(c), P(c), R^T(c) complete
+      __syncthreads();   // (2) T(c), P(c) complete
       if (c >= 0) {
         const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
         // D = T X
@@ -327,12 +328,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         }
         const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
         const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
+        const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
           float4v acc = st[cb];
           if (DECAY) acc *= gC;
-          acc = mfma32(ops64(sm.rt, cb * 16 + l16, 0, l4), w01, acc);
-          acc = mfma32(ops64(sm.rt, cb * 16 + l16, 32, l4), w23, acc);
+          acc = mfma32(optr128(Rk, cb * 16, 0, lane), w01, acc);
+          acc = mfma32(optr128(Rk, cb * 16, 32, lane), w23, acc);
           st[cb] = acc;
           if (cb & 1) GDR_FENCE();
         }
@@ -468,6 +470,28 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     }
     return acc;
   };
+  // P tile job (blocks (ib, jb), jb <= ib, numbered row by row), computed transposed
+  // (P^T = R Q^T) so each lane writes 4 columns of one row of P
+  auto p_tile = [&](int buf, int job) {
+    const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
+    const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
+    const int jb = job - ib * (ib + 1) / 2;
+    float4v acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = mfma32(opn128(R, jb * 16 + l16, 32 * s, l4), opn128(sm.q[buf], ib * 16 + l16, 32 * s, l4), acc);
+    // lane: P[i = ib*16 + l16][j = jb*16 + 4 l4 + r]
+    const int i = ib * 16 + l16;
+    float4v v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = jb * 16 + 4 * l4 + r;
+      float x = acc[r];
+      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
+      v[r] = (j <= i) ? x : 0.f;
+    }
+    *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(v);
+  };
   // write acc(X^T) of the 16 x 16 block (rb, cb) of a row-major [64][kLdc] bf16 matrix as
   // 8-byte rows (lane: row rb*16 + l16, columns cb*16 + 4 l4 .. + 3), band-masked
   auto put_rows = [&](uint16_t *M, int rb, int cb, float4v xt, bool lower_only) {
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           for (int u = 0; u < 2; ++u) {
             if (u < qb) continue;
             z[s] = mfma16(ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]),
-                          ld4col(&sm.t[cur][u * 16 + 4 * l4][qb * 16 + l16], kLdc), z[s]);
+                          ldtr(&sm.t[cur][u * 16 + 4 * l4 + (l16 >> 2)][qb * 16 + 4 * (l16 & 3)]), z[s]);
           }
         }
         const short4v z0 = tobf4(z[0]), z1 = tobf4(z[1]);
@@ -520,38 +544,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           if (sp == 1) tt = mfma16(ld4(&sm.t[cur][48 + l16][48 + 4 * l4]), z1, tt);
           put_rows(&sm.t[cur][0][0], 2 + sp, qb, mfma16(tobf4(tt), I16, zero4()), false);
         }
-      } else {
-        // P tiles, computed transposed (P^T = R Q^T) so each lane writes 4 columns of a row
-        const uint16_t *R = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-        for (int job = hw - 2; job < 10; job += (NHW - 2)) {
-          const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-          const int jb = job - ib * (ib + 1) / 2;
-          float4v acc = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma32(opn128(R, jb * 16 + l16, 32 * s, l4), opn128(sm.q[cur], ib * 16 + l16, 32 * s, l4), acc);
-          // lane: P[i = ib*16 + l16][j = jb*16 + 4 l4 + r]
-          const int i = ib * 16 + l16;
-          float4v v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = jb * 16 + 4 * l4 + r;
-            float x = acc[r];
-            if (DECAY) x *= exp2f(sm.g2[cur][i] - sm.g2[cur][j]);
-            v[r] = (j <= i) ? x : 0.f;
-          }
-          *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(v);
-        }
       }
-      // R^T of chunk c for the state update, by identity products on 16 x 16 blocks
-      {
-        const uint16_t *R = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-        for (int job = hw; job < 32; job += NHW) {
-          const int tb = job >> 3, cb = job & 7;
-          const float4v x = mfma16(ld4(R + sw128(tb * 16 + l16, cb * 16 + 4 * l4)), I16, zero4());
-          // lane: R[t = tb*16 + 4 l4 + r][c = cb*16 + l16]
-          *reinterpret_cast<short4v *>(&sm.rt[sw64(cb * 16 + l16, tb * 16 + 4 * l4)]) = tobf4(x);
-        }
+      // P tiles (10 lower blocks): jobs 8, 9 on the two T_ba waves, 0..7 on the others
+      if (hw < 2) {
+        p_tile(cur, 8 + hw);
+      } else {
+        p_tile(cur, hw - 2);
+        if (hw - 2 + (NHW - 2) < 8) p_tile(cur, hw - 2 + (NHW - 2));
       }
     }
     __syncthreads();   // (2)
