@@ -23,8 +23,9 @@
 //    next inputs into LDS from registers prefetched a chunk earlier (only helpers load
 //    from HBM), build T and P.  T is formed blockwise: each 16 x 16 diagonal block
 //    D = (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) (N strictly lower, so N^16 = 0)
-//    on the matrix cores, then T_10 = D_1 A_10 D_0 (same for T_32), then
-//    T_ba = T_b A_ba T_a for the lower-left 32 x 32 quadrant.
+//    on the matrix cores, one block per helper wave, as soon as the chunk is staged; the
+//    off-diagonal blocks T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and the lower-left
+//    quadrant T_ba = T_b A_ba T_a follow in the next phase, beside the P tiles.
 //  * With a band limit N >= 0 (the truncated Neumann series with its diagonal mask, same
 //    summary, Metodologia 1-2) entries with i - j > N are dropped when T is written; by
 //    Lemma 3.1 the band of every product above depends only on the bands of its factors,
@@ -73,7 +74,8 @@ struct __align__(16) Smem {
   uint16_t vp[2][kC][BV + 8];                              // v tile (w (.) v with channel gains)
   uint16_t t[2][kC][kLdc];                                 // T
   uint16_t p[kC][kLdc];                                    // P (one buffer)
-  uint16_t lba[32][kLdl];                                  // A_ba = -L_ba
+  uint16_t lba[32][kLdl];                                  // A_ba = -L_ba (rows 32.., cols ..31)
+  uint16_t aod[2][16][20];                                 // A_10, A_32
   float g2[2][kC], eg[2][kC], wd[2][kC], beta[2][kC], ic[2][kC];
 };
 
@@ -524,26 +526,38 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     }
     if (c >= 0) {
       if (hw < 2) {
-        // T_ba = T_b A_ba T_a, column block qb of the lower-left quadrant
+        // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
+        // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a
         const int qb = hw;
-        float4v z[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          z[s] = zero4();
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            if (u < qb) continue;
-            z[s] = mfma16(ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]),
-                          ldtr(&sm.t[cur][u * 16 + 4 * l4 + (l16 >> 2)][qb * 16 + 4 * (l16 & 3)]), z[s]);
-          }
+        uint16_t *Tc = &sm.t[cur][0][0];
+        // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read
+        auto arow = [&](int rb, int kb) { return ld4(Tc + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
+        auto bcol = [&](int kb, int cb) {
+          return ldtr(Tc + (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3));
+        };
+        auto lrow = [&](int s, int u) { return ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]); };
+        const short4v a10 = ld4(&sm.aod[0][l16][4 * l4]), a32 = ld4(&sm.aod[1][l16][4 * l4]);
+        const float4v t32 = mfma16(arow(3, 3), tobf4(mfma16(a32, bcol(2, 2), zero4())), zero4());
+        const short4v t32a = tobf4(mfma16(tobf4(t32), I16, zero4()));   // A layout of T_32
+        float4v z0, z1;                                                  // Z = A_ba T_a[:, qb]
+        if (qb == 0) {
+          const short4v d0 = bcol(0, 0);
+          const float4v t10 = mfma16(arow(1, 1), tobf4(mfma16(a10, d0, zero4())), zero4());
+          const short4v t10b = tobf4(t10);
+          z0 = mfma16(lrow(0, 1), t10b, mfma16(lrow(0, 0), d0, zero4()));
+          z1 = mfma16(lrow(1, 1), t10b, mfma16(lrow(1, 0), d0, zero4()));
+          put_rows(Tc, 1, 0, mfma16(t10b, I16, zero4()), false);
+        } else {
+          const short4v d1 = bcol(1, 1);
+          z0 = mfma16(lrow(0, 1), d1, zero4());
+          z1 = mfma16(lrow(1, 1), d1, zero4());
+          put_rows(Tc, 3, 2, mfma16(tobf4(t32), I16, zero4()), false);
         }
-        const short4v z0 = tobf4(z[0]), z1 = tobf4(z[1]);
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          float4v tt = mfma16(ld4(&sm.t[cur][32 + sp * 16 + l16][32 + 4 * l4]), z0, zero4());
-          if (sp == 1) tt = mfma16(ld4(&sm.t[cur][48 + l16][48 + 4 * l4]), z1, tt);
-          put_rows(&sm.t[cur][0][0], 2 + sp, qb, mfma16(tobf4(tt), I16, zero4()), false);
-        }
+        const short4v z0b = tobf4(z0), z1b = tobf4(z1);
+        const float4v tb2 = mfma16(arow(2, 2), z0b, zero4());
+        const float4v tb3 = mfma16(arow(3, 3), z1b, mfma16(t32a, z0b, zero4()));
+        put_rows(Tc, 2, qb, mfma16(tobf4(tb2), I16, zero4()), false);
+        put_rows(Tc, 3, qb, mfma16(tobf4(tb3), I16, zero4()), false);
       }
       // P tiles (10 lower blocks): jobs 8, 9 on the two T_ba waves, 0..7 on the others
       if (hw < 2) {
@@ -588,37 +602,21 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 
     if (have_next) {
       const int nb = nxt;
-      if (hw < 2) {
-        // diagonal blocks 2 hw, 2 hw + 1 and the block between them
-        const int p0 = 2 * hw, p1 = 2 * hw + 1;
-        const float4v n0 = a_tile(nb, p0, p0, false);
-        const float4v n0t = a_tile(nb, p0, p0, true);
-        GDR_FENCE();
-        const float4v n1 = a_tile(nb, p1, p1, false);
-        const float4v n1t = a_tile(nb, p1, p1, true);
-        GDR_FENCE();
-        const float4v a10t = a_tile(nb, p1, p0, true);
-        GDR_FENCE();
-        float4v d0, d0t, d1, d1t;
-        diag_inverse(n0, n0t, d0, &d0t, lane);
-        diag_inverse(n1, n1t, d1, &d1t, lane);
-        GDR_FENCE();
-        // T_10 = D_1 A_10 D_0
-        const float4v zz = mfma16(tobf4(a10t), tobf4(d0), zero4());
-        const float4v t10 = mfma16(tobf4(d1t), tobf4(zz), zero4());
-        uint16_t *Tn = &sm.t[nb][0][0];
-        put_rows(Tn, p0, p0, d0t, true);
-        put_rows(Tn, p1, p1, d1t, true);
-        put_rows(Tn, p1, p0, mfma16(tobf4(t10), I16, zero4()), false);
-      } else if (hw == 2) {
-        // A_ba = -L_ba (rows 32..63, columns 0..31), transposed tiles -> 8-byte rows
-#pragma unroll
-        for (int ib = 2; ib < 4; ++ib) {
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb) {
-            const float4v x = a_tile(nb, ib, jb, true);   // lane: A[ib*16 + l16][jb*16 + 4 l4 + r]
-            *reinterpret_cast<short4v *>(&sm.lba[(ib - 2) * 16 + l16][jb * 16 + 4 * l4]) = tobf4(x);
-          }
+      if (hw < 4) {
+        // diagonal block hw of T: D = (I - A_pp)^-1
+        const float4v n = a_tile(nb, hw, hw, false);
+        const float4v nt = mfma16(tobf4(n), I16, zero4());
+        float4v d, dt;
+        diag_inverse(n, nt, d, &dt, lane);
+        put_rows(&sm.t[nb][0][0], hw, hw, dt, true);
+      } else {
+        // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba
+        for (int job = hw - 4; job < 6; job += NHW - 4) {
+          const int ib = job == 0 ? 1 : job == 1 ? 3 : 2 + ((job - 2) >> 1);
+          const int jb = job == 0 ? 0 : job == 1 ? 2 : (job - 2) & 1;
+          const float4v x = a_tile(nb, ib, jb, true);   // lane: A[ib*16 + l16][jb*16 + 4 l4 + r]
+          uint16_t *dst = job < 2 ? &sm.aod[job][l16][4 * l4] : &sm.lba[(ib - 2) * 16 + l16][jb * 16 + 4 * l4];
+          *reinterpret_cast<short4v *>(dst) = tobf4(x);
         }
       }
     }
