@@ -41,6 +41,8 @@
 // rows 4 (l / 16) + r of the first tile, slots 4..7 those of the second, and the A
 // operand is gathered from LDS in the same order.  A product X Y whose factors are both
 // accumulators needs acc(X^T) and acc(Y); transposed copies are computed where needed.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gdr {
@@ -189,6 +191,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
   constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
   constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
+  // with E = beta k and R = k, P = tril(Q K^T) is formed by the value waves from the K and Q
+  // operands they already hold for Y and O1; otherwise the helper waves form it
+  constexpr bool kPv = (WK == kWkSame) && !CHAN;
   __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
@@ -231,123 +236,186 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // Each role runs its own loop with the same barrier sequence, so the compiler allocates
   // registers for one role's loop-carried state at a time.
   if (vwave) {
-    // ---------------- value waves: S^T tiles in accumulators ----------------
-    // tile cb holds S^T[c = 16 cb + 4 l4 + r][v = 16 wave + l16]
-    float4v st[8];
-    const int vrow = v0 + 16 * wave + l16;   // this lane's state row
+    // the wave index is a template constant inside the value-wave loop, so every
+    // wave-dependent choice below (state rows, the P blocks a wave forms) is static
+    auto value_loop = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      // ---------------- value waves: S^T tiles in accumulators ----------------
+      // tile cb holds S^T[c = 16 cb + 4 l4 + r][v = 16 W + l16]
+      float4v st[8];
+      const int vrow = v0 + 16 * W + l16;   // this lane's state row
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      st[cb] = zero4();
-      if (a.state_in != nullptr) {
-        const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4);
-        st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
+      for (int cb = 0; cb < 8; ++cb) {
+        st[cb] = zero4();
+        if (a.state_in != nullptr) {
+          const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4);
+          st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
+        }
       }
-    }
-    for (int c = -1; c < nchunks; ++c) {
-      const int cur = c & 1;
-      const int c0 = c * kC;
-      const int n = min(kC, T - c0);
-      short4v x4[4];
-      float4v O1[4];
-      __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
-      if (c >= 0) {
-        // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y
-        short8v sb[4];
+      for (int c = -1; c < nchunks; ++c) {
+        const int cur = c & 1;
+        const int c0 = c * kC;
+        const int n = min(kC, T - c0);
+        short4v x4[4];
+        float4v O1[4];
+        __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
+        if (c >= 0) {
+          // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y.  The
+          // operands of block tb + 1 are read while block tb is multiplied.  With kPv the K
+          // operands of earlier blocks are kept and the blocks (tb, jb), jb <= tb, of P are
+          // formed here, split between the value waves by the parity of jb.
+          short8v sb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
-        const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
+          for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
+          const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
+          short8v ev[2][4], qv[2][4];
+          short8v mine[4 / NVW][4];   // kPv: K operands of the blocks jb = W (mod NVW) seen so far
+          short4v vt[2];
+          auto load_ops = [&](int tb, int slot) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          float4v y = zero4(), o = zero4();
+            for (int j = 0; j < 4; ++j) {
+              ev[slot][j] = ops128(E, tb * 16 + l16, 32 * j, l4);
+              qv[slot][j] = ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
+            }
+            // V' block (rows t, columns v) in the accumulator layout, read transposed
+            vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
+          };
+          load_ops(0, 0);
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const int sl = tb & 1;
+            if (tb + 1 < 4) load_ops(tb + 1, sl ^ 1);
+            float4v y = zero4(), o = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              y = mfma32(ev[sl][j], sb[j], y);
+              o = mfma32(qv[sl][j], sb[j], o);
+            }
+            const int t0 = tb * 16 + 4 * l4;
+            const float4 eg = ld4f(&sm.eg[cur][t0]);
+            float4v xv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xv[r] = bf(static_cast<uint16_t>(vt[sl][r])) - (&eg.x)[r] * y[r];
+            if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
+              const float4 bt = ld4f(&sm.beta[cur][t0]);
+              xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
+            }
+            x4[tb] = tobf4(xv);
+            O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
+            if constexpr (kPv) {
+              // P^T block (jb, tb) = K_jb Q_tb^T: lane holds P[i = tb*16 + l16][j = jb*16 + 4 l4 + r]
+              const int i = tb * 16 + l16;
+              const float gi = sm.g2[cur][i];
+              if (tb % NVW == W) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mine[tb / NVW][j] = ev[sl][j];
+              }
+#pragma unroll
+              for (int m = 0; m < 4 / NVW; ++m) {
+                const int jb = m * NVW + W;
+                if (jb > tb) continue;
+                float4v pt = zero4();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pt = mfma32(mine[m][j], qv[sl][j], pt);
+                const float4 gj = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
+                float4v pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int jj = jb * 16 + 4 * l4 + r;
+                  const float x = DECAY ? pt[r] * exp2f(gi - (&gj.x)[r]) : pt[r];
+                  pv[r] = jj <= i ? x : 0.f;
+                }
+                *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(pv);
+              }
+            }
+            GDR_FENCE();
+          }
+        }
+        __syncthreads();   // (2) T(c), P(c) complete
+        if (c >= 0) {
+          // every LDS operand of this phase is read up front: T and P blocks, R^T for the update
+          const uint16_t *Tm = &sm.t[cur][0][0], *Pm = &sm.p[0][0];
+          const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
+          const short4v t00 = ld4(Tm + l16 * kLdc + 4 * l4), t22 = ld4(Tm + (32 + l16) * kLdc + 32 + 4 * l4);
+          const short8v t10 = opsp(Tm, kLdc, 16 + l16, 0, l4), t20 = opsp(Tm, kLdc, 32 + l16, 0, l4);
+          const short8v t30 = opsp(Tm, kLdc, 48 + l16, 0, l4), t32 = opsp(Tm, kLdc, 48 + l16, 32, l4);
+          const short4v p00 = ld4(Pm + l16 * kLdc + 4 * l4), p22 = ld4(Pm + (32 + l16) * kLdc + 32 + 4 * l4);
+          const short8v p10 = opsp(Pm, kLdc, 16 + l16, 0, l4), p20 = opsp(Pm, kLdc, 32 + l16, 0, l4);
+          const short8v p30 = opsp(Pm, kLdc, 48 + l16, 0, l4), p32 = opsp(Pm, kLdc, 48 + l16, 32, l4);
+          short8v ra[4], rb[4];   // R^T operands of the first half of the update
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            ra[cb] = optr128(Rk, cb * 16, 0, lane);
+            rb[cb] = optr128(Rk, cb * 16, 32, lane);
+          }
+          float4 wdv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wdv[j] = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
+          const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
+
+          // D = T X
+          const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
+          float4v D[4];
+          D[0] = mfma16(t00, x4[0], zero4());
+          D[1] = mfma32(t10, x01, zero4());
+          D[2] = mfma16(t22, x4[2], mfma32(t20, x01, zero4()));
+          D[3] = mfma32(t32, x23, mfma32(t30, x01, zero4()));
+          // state update S^T <- e^{g_C} S^T + R^T (wd (.) D), interleaved with O2 = P D
+          short4v w4[4], d4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            y = mfma32(ops128(E, tb * 16 + l16, 32 * j, l4), sb[j], y);
-            o = mfma32(ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4), sb[j], o);
+            w4[j] = tobf4(float4v{wdv[j].x * D[j][0], wdv[j].y * D[j][1], wdv[j].z * D[j][2], wdv[j].w * D[j][3]});
+            d4[j] = tobf4(D[j]);
           }
-          // V' block (rows t, columns v) in the accumulator layout, read transposed
-          const short4v vt4 = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * wave + 4 * (l16 & 3)]);
-          const float4v vpa = float4v{bf(static_cast<uint16_t>(vt4[0])), bf(static_cast<uint16_t>(vt4[1])),
-                                      bf(static_cast<uint16_t>(vt4[2])), bf(static_cast<uint16_t>(vt4[3]))};
-          const int t0 = tb * 16 + 4 * l4;
-          const float4 eg = ld4f(&sm.eg[cur][t0]);
-          float4v xv = float4v{vpa[0] - eg.x * y[0], vpa[1] - eg.y * y[1], vpa[2] - eg.z * y[2], vpa[3] - eg.w * y[3]};
-          if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
-            const float4 bt = ld4f(&sm.beta[cur][t0]);
-            xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
+          const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
+          const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            float4v acc = st[cb];
+            if (DECAY) acc *= gC;
+            st[cb] = mfma32(rb[cb], w23, mfma32(ra[cb], w01, acc));
+            ra[cb] = optr128(Rk, (cb + 4) * 16, 0, lane);   // second half, read behind the first
+            rb[cb] = optr128(Rk, (cb + 4) * 16, 32, lane);
           }
-          x4[tb] = tobf4(xv);
-          O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
-          GDR_FENCE();
+#pragma unroll
+          for (int cb = 4; cb < 8; ++cb) {
+            float4v acc = st[cb];
+            if (DECAY) acc *= gC;
+            st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
+          }
+          float4v O2[4];
+          O2[0] = mfma16(p00, d4[0], zero4());
+          O2[1] = mfma32(p10, d01, zero4());
+          O2[2] = mfma16(p22, d4[2], mfma32(p20, d01, zero4()));
+          O2[3] = mfma32(p32, d23, mfma32(p30, d01, zero4()));
+          // output: transpose each 16 x 16 block by an identity product so a lane holds four
+          // consecutive values of one token, then 8-byte stores
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const float4v o = a.scale * (O1[tb] + O2[tb]);
+            const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
+            const int t = tb * 16 + l16;
+            if (t < n) {
+              const short4v pk = tobf4(ot);
+              *reinterpret_cast<short4v *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * W +
+                                           4 * l4) = pk;
+            }
+          }
         }
+        if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
       }
-      __syncthreads();   // (2) T(c), P(c) complete
-      if (c >= 0) {
-        const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
-        // D = T X
-        const uint16_t *Tm = &sm.t[cur][0][0];
-        float4v D[4];
-        D[0] = mfma16(ld4(Tm + l16 * kLdc + 4 * l4), x4[0], zero4());
-        D[1] = mfma32(opsp(Tm, kLdc, 16 + l16, 0, l4), x01, zero4());
-        D[2] = mfma32(opsp(Tm, kLdc, 32 + l16, 0, l4), x01, zero4());
-        D[2] = mfma16(ld4(Tm + (32 + l16) * kLdc + 32 + 4 * l4), x4[2], D[2]);
-        D[3] = mfma32(opsp(Tm, kLdc, 48 + l16, 0, l4), x01, zero4());
-        D[3] = mfma32(opsp(Tm, kLdc, 48 + l16, 32, l4), x23, D[3]);
-        GDR_FENCE();
-        // O2 = P D
-        short4v d4[4];
+      if (a.state_out != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d4[j] = tobf4(D[j]);
-        const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
-        const uint16_t *Pm = &sm.p[0][0];
-        float4v O2[4];
-        O2[0] = mfma16(ld4(Pm + l16 * kLdc + 4 * l4), d4[0], zero4());
-        O2[1] = mfma32(opsp(Pm, kLdc, 16 + l16, 0, l4), d01, zero4());
-        O2[2] = mfma32(opsp(Pm, kLdc, 32 + l16, 0, l4), d01, zero4());
-        O2[2] = mfma16(ld4(Pm + (32 + l16) * kLdc + 32 + 4 * l4), d4[2], O2[2]);
-        O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 0, l4), d01, zero4());
-        O2[3] = mfma32(opsp(Pm, kLdc, 48 + l16, 32, l4), d23, O2[3]);
-        GDR_FENCE();
-        // output: transpose each 16 x 16 block by an identity product so a lane holds four
-        // consecutive values of one token, then 8-byte stores
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const float4v o = a.scale * (O1[tb] + O2[tb]);
-          const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
-          const int t = tb * 16 + l16;
-          if (t < n) {
-            const short4v pk = tobf4(ot);
-            *reinterpret_cast<short4v *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * wave +
-                                         4 * l4) = pk;
-          }
-        }
-        GDR_FENCE();
-        // state update S^T <- e^{g_C} S^T + R^T (wd (.) D)
-        short4v w4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 wdv = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
-          w4[j] = tobf4(float4v{wdv.x * D[j][0], wdv.y * D[j][1], wdv.z * D[j][2], wdv.w * D[j][3]});
-        }
-        const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
-        const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
-        const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          float4v acc = st[cb];
-          if (DECAY) acc *= gC;
-          acc = mfma32(optr128(Rk, cb * 16, 0, lane), w01, acc);
-          acc = mfma32(optr128(Rk, cb * 16, 32, lane), w23, acc);
-          st[cb] = acc;
-          if (cb & 1) GDR_FENCE();
-        }
+        for (int cb = 0; cb < 8; ++cb)
+          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4) =
+              make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
       }
-      if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
-    }
-    if (a.state_out != nullptr) {
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4) =
-            make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+    };
+    if constexpr (NVW == 1) {
+      value_loop(std::integral_constant<int, 0>{});
+    } else {
+      if (wave == 0) value_loop(std::integral_constant<int, 0>{});
+      else value_loop(std::integral_constant<int, 1>{});
     }
     return;
   }
@@ -559,12 +627,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         put_rows(Tc, 2, qb, mfma16(tobf4(tb2), I16, zero4()), false);
         put_rows(Tc, 3, qb, mfma16(tobf4(tb3), I16, zero4()), false);
       }
-      // P tiles (10 lower blocks): jobs 8, 9 on the two T_ba waves, 0..7 on the others
-      if (hw < 2) {
-        p_tile(cur, 8 + hw);
-      } else {
-        p_tile(cur, hw - 2);
-        if (hw - 2 + (NHW - 2) < 8) p_tile(cur, hw - 2 + (NHW - 2));
+      // P tiles (10 lower blocks) unless the value waves form them: jobs 8, 9 on the two T_ba
+      // waves, 0..7 on the others
+      if constexpr (!kPv) {
+        if (hw < 2) {
+          p_tile(cur, 8 + hw);
+        } else {
+          p_tile(cur, hw - 2);
+          if (hw - 2 + (NHW - 2) < 8) p_tile(cur, hw - 2 + (NHW - 2));
+        }
       }
     }
     __syncthreads();   // (2)
