@@ -498,17 +498,21 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         }
       }
     }
-    // gates: cumulative log decay in log2 units and the quantities derived from it
-    const bool ok = lane < n;
-    const float beta_t = ok ? gbeta : 0.f;
-    float g = ok ? gla * kLog2e : 0.f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(g, d, 64);
-      if (lane >= d) g += y;
-    }
-    const float glast = __shfl(g, n - 1, 64);
+    // gates: cumulative log decay in log2 units and the quantities derived from it.  Every
+    // helper wave loaded the gate registers; all of them take delivery here (so no load is
+    // left pending on a path that skips it) and the gate wave forms the scan.
+    const float la = gla, bt = gbeta;
+    asm volatile("" ::"v"(la), "v"(bt));
     if (gate_wave) {
+      const bool ok = lane < n;
+      const float beta_t = ok ? bt : 0.f;
+      float g = ok ? la * kLog2e : 0.f;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(g, d, 64);
+        if (lane >= d) g += y;
+      }
+      const float glast = __shfl(g, n - 1, 64);
       sm.g2[buf][lane] = g;
       sm.eg[buf][lane] = DECAY ? exp2f(g) : 1.f;
       sm.wd[buf][lane] = DECAY ? exp2f(glast - g) : 1.f;
@@ -681,13 +685,47 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         diag_inverse(n, nt, d, &dt, lane);
         put_rows(&sm.t[nb][0][0], hw, hw, dt, true);
       } else {
-        // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba
-        for (int job = hw - 4; job < 6; job += NHW - 4) {
-          const int ib = job == 0 ? 1 : job == 1 ? 3 : 2 + ((job - 2) >> 1);
-          const int jb = job == 0 ? 0 : job == 1 ? 2 : (job - 2) & 1;
-          const float4v x = a_tile(nb, ib, jb, true);   // lane: A[ib*16 + l16][jb*16 + 4 l4 + r]
-          uint16_t *dst = job < 2 ? &sm.aod[job][l16][4 * l4] : &sm.lba[(ib - 2) * 16 + l16][jb * 16 + 4 * l4];
-          *reinterpret_cast<short4v *>(dst) = tobf4(x);
+        // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba,
+        // this wave's share formed together (operands first, then the product chains)
+        constexpr int NOW = NHW - 4;               // waves on these jobs
+        constexpr int NJW = (6 + NOW - 1) / NOW;   // jobs per wave
+        const uint16_t *E = CHAN ? sm.e[nb] : sm.k[nb];
+        const uint16_t *R = (WK == kWkSame) ? sm.k[nb] : sm.r[nb];
+        int ib[NJW], jb[NJW];
+        short8v ra[NJW][4], eb[NJW][4];
+#pragma unroll
+        for (int q = 0; q < NJW; ++q) {
+          const int job = min(hw - 4 + q * NOW, 5);   // a job past the last repeats it unstored
+          ib[q] = job == 0 ? 1 : job == 1 ? 3 : 2 + ((job - 2) >> 1);
+          jb[q] = job == 0 ? 0 : job == 1 ? 2 : (job - 2) & 1;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            ra[q][s2] = opn128(R, jb[q] * 16 + l16, 32 * s2, l4);
+            eb[q][s2] = opn128(E, ib[q] * 16 + l16, 32 * s2, l4);
+          }
+        }
+        float4v acc[NJW];
+#pragma unroll
+        for (int q = 0; q < NJW; ++q) acc[q] = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+          for (int q = 0; q < NJW; ++q) acc[q] = mfma32(ra[q][s2], eb[q][s2], acc[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < NJW; ++q) {
+          const int job = hw - 4 + q * NOW;
+          // lane: (E R^T)[i = ib*16 + l16][j = jb*16 + 4 l4 + r], scaled to A = -L (j < i always)
+          const int i = ib[q] * 16 + l16;
+          const float bi = SCALED_E ? sm.beta[nb][i] : 1.f, gi = sm.g2[nb][i];
+          const float4 gj = ld4f(&sm.g2[nb][jb[q] * 16 + 4 * l4]);
+          float4v x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = -(DECAY ? acc[q][r] * bi * exp2f(gi - (&gj.x)[r]) : acc[q][r] * bi);
+          if (job < 6) {
+            uint16_t *dst = job < 2 ? &sm.aod[job][l16][4 * l4] : &sm.lba[(ib[q] - 2) * 16 + l16][jb[q] * 16 + 4 * l4];
+            *reinterpret_cast<short4v *>(dst) = tobf4(x);
+          }
         }
       }
     }
