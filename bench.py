@@ -5,8 +5,12 @@ One step = one gdr_chunk_fwd call over one batch of synthetic input (every stage
 chunked forward runs inside it).  Default workload: scalar-gated delta rule, B4 H16 T4096
 Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain|decode]
                     [--neumann N] [--impl auto|generic|mfma] [--no-cpu-baseline]
+
+Counter helpers (used to produce the committed traffic summaries under profiles/):
+    python bench.py --copy-probe-mb 256          # calibration copy of known size
+    python bench.py --workload gdn --copy-probe-mb 256 --traffic-summary F.csv W.csv CF.csv CW.csv
 """
 from __future__ import annotations
 
@@ -103,13 +107,17 @@ def cpu_baseline(s, x, tokens: int, n_streams: int):
     pre = None
     if s.wkey == "precond":
         pre = dict(rho=s.pc_rho, eps=s.pc_eps, h_init=np.full(s.Dk, s.pc_h0), t0=0)
-    tasks = [({k: (v[b, :tokens, h] if v is not None else None) for k, v in x.items()}, pre)
+    # float32 copies travel to the workers: exact, since every input was rounded to fp32 (or
+    # further to bf16) when it was generated, and the oracle widens to fp64 itself
+    tasks = [({k: (np.ascontiguousarray(v[b, :tokens, h], dtype=np.float32) if v is not None else None)
+               for k, v in x.items()}, pre)
              for (b, h) in streams]
     ctx = mp.get_context("spawn")
     with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
-        pool.map(_cpu_task, tasks[:workers])   # warm the workers (imports)
-        t0 = time.perf_counter()
-        pool.map(_cpu_task, tasks)
+        pool.map(_cpu_task, [(
+            {k: (v[:4] if v is not None else None) for k, v in t[0].items()}, t[1]) for t in tasks[:workers]])
+        t0 = time.perf_counter()                # (the call above warmed the workers' imports)
+        cpu_s = sum(pool.map(_cpu_task, tasks, chunksize=1))
         wall = time.perf_counter() - t0
     token_heads = len(streams) * tokens
     return {
@@ -119,8 +127,154 @@ def cpu_baseline(s, x, tokens: int, n_streams: int):
         "kind": "oracle",
         "sample": f"fp64 token-by-token oracle on {len(streams)} of {s.B * s.H} (batch, head) streams x "
                   f"{tokens} of {s.T} tokens ({token_heads} token-heads, {wall:.2f} s wall on {workers} "
-                  f"processes); tokens/s = token-heads / H / wall",
+                  f"processes, {cpu_s:.1f} s of CPU work); tokens/s = token-heads / H / wall",
     }
+
+
+# ------------------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters: the chunk kernel's FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch), each scaled by what the same counter reads for a plain device copy of known size
+# ------------------------------------------------------------------------------------
+
+def copy_probe(mb: int):
+    """A plain device-to-device copy of `mb` MiB, three times (the calibration kernel)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mb * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: {mb} MiB x 3", file=sys.stderr)
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, name_has: str):
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching '{name_has}' in {csv_path}")
+    return sorted(per.values())
+
+
+def traffic_summary(args):
+    """Writes profiles/chunk_fwd_<impl>_<workload>_traffic.json from four counter CSVs."""
+    import statistics
+    kern = "chunk_mfma" if args.impl_name == "mfma" else "chunk_generic"
+    f_k = _counter_per_dispatch(args.traffic_summary[0], "FETCH_SIZE", kern)
+    w_k = _counter_per_dispatch(args.traffic_summary[1], "WRITE_SIZE", kern)
+    f_c = _counter_per_dispatch(args.traffic_summary[2], "FETCH_SIZE", "copy")
+    w_c = _counter_per_dispatch(args.traffic_summary[3], "WRITE_SIZE", "copy")
+    copy_kib = args.copy_probe_mb * 1024.0
+    # the last copy of the probe is the representative one (the first may find the source
+    # still in the last-level cache from the fill)
+    fac_f, fac_w = copy_kib / f_c[-1], copy_kib / w_c[-1]
+    fetch, write = statistics.median(f_k), statistics.median(w_k)
+    s = __import__("gdr_synth").spec(args.workload)
+    rec = {
+        "kernel": f"gdr_chunk_fwd/{args.impl_name}", "workload": args.workload,
+        "source_sha": source_sha(args.impl_name),
+        "fetch_kib_per_dispatch_median": fetch, "write_kib_per_dispatch_median": write,
+        "dispatches": [len(f_k), len(w_k)],
+        "copy_probe_mib": args.copy_probe_mb, "copy_fetch_kib": f_c[-1], "copy_write_kib": w_c[-1],
+        "scale_fetch": fac_f, "scale_write": fac_w,
+        "hbm_bytes_per_launch": round((fetch * fac_f + write * fac_w) * 1024.0),
+        "alg_bytes_per_launch": alg_bytes(s),
+    }
+    out = os.path.join(ROOT, "profiles", f"chunk_fwd_{args.impl_name}_{args.workload}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+# ------------------------------------------------------------------------------------
+# decode: gdr_recurrent_step at the long workload's decode batch (64 sequences x 32 heads)
+# ------------------------------------------------------------------------------------
+
+def decode_alg_bytes(Bd, H, Dk, Dv, esz=2) -> int:
+    """State read and written once (fp32) + q, k, v, beta, log alpha read + o written."""
+    return Bd * H * (2 * Dv * Dk * 4 + (2 * Dk + Dv) * esz + 8 + Dv * esz)
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import chunked_gated_delta_gdr_amd as G
+    import gdr_synth as gs
+
+    s = gs.spec("long")
+    Bd, H, Dk, Dv = s.decode_batch, s.H, s.Dk, s.Dv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nstage = 8   # distinct step inputs staged on the device, used in turn
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    steps_in = []
+    for i in range(nstage):
+        xi = gs.make_decode_inputs(s, i)
+        steps_in.append(dict(q=t(xi["q"], torch.bfloat16), k=t(xi["k"], torch.bfloat16),
+                             v=t(xi["v"], torch.bfloat16), beta=t(xi["beta"], torch.float32),
+                             log_alpha=t(xi["log_alpha"], torch.float32)))
+    rng = np.random.Generator(np.random.PCG64(s.seed + 7777))
+    s0 = (0.05 * rng.standard_normal((Bd, H, Dv, Dk))).astype(np.float32)
+    state = torch.from_numpy(s0).to(dev)
+    outs = [torch.empty((Bd, H, Dv), dtype=torch.bfloat16, device=dev) for _ in range(nstage)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        a = steps_in[i % nstage]
+        G.gdr_recurrent_step(a["q"], a["k"], a["v"], state, beta=a["beta"], log_alpha=a["log_alpha"],
+                             out=outs[i % nstage], stream=stream)
+
+    # parity first: one step from the known state, sampled streams vs the oracle
+    parity = None
+    if not args.no_parity:
+        import oracle
+        step(0)
+        torch.cuda.synchronize()
+        x0 = gs.make_decode_inputs(s, 0)
+        sub = {k: (None if v is None else v[:4]) for k, v in x0.items()}
+        o_ref, s_ref, _ = oracle.decode_step(sub, s0[:4].astype(np.float64))
+        parity = {"streams": "4 x 32 heads", "rel_l2_out": oracle.rel_l2(outs[0][:4].double().cpu().numpy(), o_ref),
+                  "rel_l2_state": oracle.rel_l2(state[:4].double().cpu().numpy(), s_ref)}
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    launch = [a.elapsed_time(b) for a, b in ev]
+    avg_s = sum(launch) / len(launch) / 1e3
+    print(f"[bench] decode {args.steps} steps: launch avg {avg_s * 1e6:.2f} us min {min(launch) * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+    ab = decode_alg_bytes(Bd, H, Dk, Dv)
+    gbs = ab / avg_s / 1e9
+    rec = {
+        "metric": "tokens/s gated-delta decode step (batch 64 x H32 d128, bf16 in, fp32 state in place)",
+        "value": round(Bd / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded decode inputs of the long workload; random fp32 start state)",
+        "config": {"workload": f"decode: batch {Bd} H{H} Dk{Dk} Dv{Dv} bf16 scalar gain+decay, state fp32 in place",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gdr_recurrent_step",
+                     "alg_bytes_per_launch": ab, "avg_launch_us": round(avg_s * 1e6, 2)},
+        "cpu_baseline": None, "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -128,12 +282,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "gdn2", "pdn", "long", "plain"])
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "gdn2", "pdn", "long", "plain", "decode"])
     ap.add_argument("--neumann", type=int, default=-1)
     ap.add_argument("--impl", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run only the counter-calibration copy of this many MiB")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                           "COPY_WRITE_CSV"),
+                    help="write the traffic summary of --workload from rocprofv3 counter CSVs")
+    ap.add_argument("--impl-name", default="mfma", choices=["mfma", "generic"])
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -141,6 +307,9 @@ def main():
               "(batch, head) stream is independent, so more GPUs would each run their own share of "
               "streams with no communication; this build measures the one-GPU share.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "decode":
+        bench_decode(args)
+        return
 
     import numpy as np
     import torch
@@ -252,7 +421,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(s, x, tokens=min(s.T, 2048), n_streams=min(s.B * s.H, 64))
+        # every (batch, head) stream, capped at 300k token-heads: about 10-15 s of single-core
+        # oracle work at ~45 us per token-head (the whole gdn / gdn2 / pdn workload)
+        cpu = cpu_baseline(s, x, tokens=min(s.T, max(64, 300_000 // (s.B * s.H))), n_streams=s.B * s.H)
 
     rec = {
         "metric": METRIC,
