@@ -70,6 +70,10 @@ __device__ __forceinline__ int sw128(int row, int col) {
 template <int BV, bool CHAN, int WK>
 struct __align__(16) Smem {
   uint16_t q[2][kC * kD];                                  // Q
+  // 16 bytes apart from a multiple of 512: the value waves read the same offsets of Q and K
+  // (or E), and the compiler would otherwise pair those reads into one two-address read whose
+  // halves then have to be moved into place
+  uint16_t pad_qk[8];
   uint16_t k[2][kC * kD];                                  // K
   uint16_t e[CHAN ? 2 : 1][CHAN ? kC * kD : 8];            // erase key b (.) k
   uint16_t r[WK != kWkSame ? 2 : 1][WK != kWkSame ? kC * kD : 8];   // write key if != k
@@ -82,6 +86,9 @@ struct __align__(16) Smem {
 };
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// 2^x by the hardware instruction alone: the arguments are decays between two tokens of a
+// chunk (x <= 0 wherever the result is kept); results below the normal range flush to zero
+__device__ __forceinline__ float decay2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint16_t tobf(float x) { return f32_to_bf16_bits(x); }
 __device__ __forceinline__ uint32_t word(const uint4 &v, int e) {
   const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
@@ -191,9 +198,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
   constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
   constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
-  // with E = beta k and R = k, P = tril(Q K^T) is formed by the value waves from the K and Q
-  // operands they already hold for Y and O1; otherwise the helper waves form it
-  constexpr bool kPv = (WK == kWkSame) && !CHAN;
+  // with E = beta k and R = k, P = tril(Q K^T) is formed by the two value waves from the K and
+  // Q operands they already hold for Y and O1; otherwise (and with a single value wave, which
+  // would have to keep every K block) the helper waves form it
+  constexpr bool kPv = (WK == kWkSame) && !CHAN && NVW == 2;
   __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
@@ -263,14 +271,24 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y.  The
           // operands of block tb + 1 are read while block tb is multiplied.  With kPv the K
           // operands of earlier blocks are kept and the blocks (tb, jb), jb <= tb, of P are
-          // formed here, split between the value waves by the parity of jb.
+          // formed here, split between the value waves by column block.
           short8v sb[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
           const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
           short8v ev[2][4], qv[2][4];
-          short8v mine[4 / NVW][4];   // kPv: K operands of the blocks jb = W (mod NVW) seen so far
+          // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
+          // wave 0, 1 and 2 to wave 1); each keeps the K operands of its own blocks
+          constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
+          constexpr auto p_slot = [](int jb) { return NVW == 1 ? jb : (jb < 2 ? 0 : 1); };
+          short8v mine[4 / NVW][4];
           short4v vt[2];
+          // Everything a block reads from LDS is read while the previous block is multiplied:
+          // LDS reads complete in order, so a read issued inside a block would also wait for
+          // the prefetch issued before it.
+          float4 egv[2], btv[2];
+          float giv[2];
+          float4 gjv[4 / NVW];   // kPv: cumulative decay at the columns of this wave's P blocks
           auto load_ops = [&](int tb, int slot) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -279,25 +297,33 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
             // V' block (rows t, columns v) in the accumulator layout, read transposed
             vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
+            egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
+            if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
+            if (kPv) giv[slot] = sm.g2[cur][tb * 16 + l16];
           };
+          if constexpr (kPv) {
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+              if (p_owner(jb) == W) gjv[p_slot(jb)] = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
+          }
           load_ops(0, 0);
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) {
             const int sl = tb & 1;
             if (tb + 1 < 4) load_ops(tb + 1, sl ^ 1);
+            GDR_FENCE();   // the prefetch issues before this block's products
             float4v y = zero4(), o = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               y = mfma32(ev[sl][j], sb[j], y);
               o = mfma32(qv[sl][j], sb[j], o);
             }
-            const int t0 = tb * 16 + 4 * l4;
-            const float4 eg = ld4f(&sm.eg[cur][t0]);
+            const float4 eg = egv[sl];
             float4v xv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) xv[r] = bf(static_cast<uint16_t>(vt[sl][r])) - (&eg.x)[r] * y[r];
             if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
-              const float4 bt = ld4f(&sm.beta[cur][t0]);
+              const float4 bt = btv[sl];
               xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
             }
             x4[tb] = tobf4(xv);
@@ -305,24 +331,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             if constexpr (kPv) {
               // P^T block (jb, tb) = K_jb Q_tb^T: lane holds P[i = tb*16 + l16][j = jb*16 + 4 l4 + r]
               const int i = tb * 16 + l16;
-              const float gi = sm.g2[cur][i];
-              if (tb % NVW == W) {
+              const float gi = giv[sl];
+              if (p_owner(tb) == W) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mine[tb / NVW][j] = ev[sl][j];
+                for (int j = 0; j < 4; ++j) mine[p_slot(tb)][j] = ev[sl][j];
               }
 #pragma unroll
-              for (int m = 0; m < 4 / NVW; ++m) {
-                const int jb = m * NVW + W;
-                if (jb > tb) continue;
+              for (int jb = 0; jb <= tb; ++jb) {
+                if (p_owner(jb) != W) continue;
                 float4v pt = zero4();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pt = mfma32(mine[m][j], qv[sl][j], pt);
-                const float4 gj = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
+                for (int j = 0; j < 4; ++j) pt = mfma32(mine[p_slot(jb)][j], qv[sl][j], pt);
+                const float4 gj = gjv[p_slot(jb)];
                 float4v pv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                   const int jj = jb * 16 + 4 * l4 + r;
-                  const float x = DECAY ? pt[r] * exp2f(gi - (&gj.x)[r]) : pt[r];
+                  const float x = DECAY ? pt[r] * decay2(gi - (&gj.x)[r]) : pt[r];
                   pv[r] = jj <= i ? x : 0.f;
                 }
                 *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(pv);
@@ -514,8 +539,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       }
       const float glast = __shfl(g, n - 1, 64);
       sm.g2[buf][lane] = g;
-      sm.eg[buf][lane] = DECAY ? exp2f(g) : 1.f;
-      sm.wd[buf][lane] = DECAY ? exp2f(glast - g) : 1.f;
+      sm.eg[buf][lane] = DECAY ? decay2(g) : 1.f;
+      sm.wd[buf][lane] = DECAY ? decay2(glast - g) : 1.f;
       sm.beta[buf][lane] = beta_t;
       if (WK == kWkPrecond) {
         const float tg = static_cast<float>(a.t0 + static_cast<long long>(c) * kC + lane + 1);
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       const int j = trans ? jb * 16 + 4 * l4 + r : jb * 16 + l16;
       float x = acc[r];
       if (SCALED_E) x *= sm.beta[buf][i];
-      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
+      if (DECAY) x *= decay2(sm.g2[buf][i] - sm.g2[buf][j]);
       acc[r] = (j < i) ? -x : 0.f;
     }
     return acc;
@@ -561,7 +586,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int j = jb * 16 + 4 * l4 + r;
       float x = acc[r];
-      if (DECAY) x *= exp2f(sm.g2[buf][i] - sm.g2[buf][j]);
+      if (DECAY) x *= decay2(sm.g2[buf][i] - sm.g2[buf][j]);
       v[r] = (j <= i) ? x : 0.f;
     }
     *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(v);
@@ -721,7 +746,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           const float4 gj = ld4f(&sm.g2[nb][jb[q] * 16 + 4 * l4]);
           float4v x;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = -(DECAY ? acc[q][r] * bi * exp2f(gi - (&gj.x)[r]) : acc[q][r] * bi);
+          for (int r = 0; r < 4; ++r) x[r] = -(DECAY ? acc[q][r] * bi * decay2(gi - (&gj.x)[r]) : acc[q][r] * bi);
           if (job < 6) {
             uint16_t *dst = job < 2 ? &sm.aod[job][l16][4 * l4] : &sm.lba[(ib[q] - 2) * 16 + l16][jb[q] * 16 + 4 * l4];
             *reinterpret_cast<short4v *>(dst) = tobf4(x);
