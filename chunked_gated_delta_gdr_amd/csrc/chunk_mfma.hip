@@ -276,12 +276,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
           const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
-          short8v ev[2][4], qv[2][4];
+          // one register set per block for the E operands (the wave keeps those of its own P column
+          // blocks alive; the others die after their block), double-buffered Q operands
+          short8v ev[4][4], qv[2][4];
           // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
-          // wave 0, 1 and 2 to wave 1); each keeps the K operands of its own blocks
+          // wave 0, 1 and 2 to wave 1)
           constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
           constexpr auto p_slot = [](int jb) { return NVW == 1 ? jb : (jb < 2 ? 0 : 1); };
-          short8v mine[4 / NVW][4];
           short4v vt[2];
           // Everything a block reads from LDS is read while the previous block is multiplied:
           // LDS reads complete in order, so a read issued inside a block would also wait for
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           auto load_ops = [&](int tb, int slot) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              ev[slot][j] = ops128(E, tb * 16 + l16, 32 * j, l4);
+              ev[tb][j] = ops128(E, tb * 16 + l16, 32 * j, l4);
               qv[slot][j] = ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
             }
             // V' block (rows t, columns v) in the accumulator layout, read transposed
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
               if (p_owner(jb) == W) gjv[p_slot(jb)] = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
           }
           load_ops(0, 0);
+          GDR_FENCE();   // (not fused with the next block's reads: 16 rows apart they would pair)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) {
             const int sl = tb & 1;
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             float4v y = zero4(), o = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              y = mfma32(ev[sl][j], sb[j], y);
+              y = mfma32(ev[tb][j], sb[j], y);
               o = mfma32(qv[sl][j], sb[j], o);
             }
             const float4 eg = egv[sl];
@@ -332,23 +334,19 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
               // P^T block (jb, tb) = K_jb Q_tb^T: lane holds P[i = tb*16 + l16][j = jb*16 + 4 l4 + r]
               const int i = tb * 16 + l16;
               const float gi = giv[sl];
-              if (p_owner(tb) == W) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) mine[p_slot(tb)][j] = ev[sl][j];
-              }
 #pragma unroll
               for (int jb = 0; jb <= tb; ++jb) {
                 if (p_owner(jb) != W) continue;
                 float4v pt = zero4();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pt = mfma32(mine[p_slot(jb)][j], qv[sl][j], pt);
+                for (int j = 0; j < 4; ++j) pt = mfma32(ev[jb][j], qv[sl][j], pt);
                 const float4 gj = gjv[p_slot(jb)];
                 float4v pv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                   const int jj = jb * 16 + 4 * l4 + r;
                   const float x = DECAY ? pt[r] * decay2(gi - (&gj.x)[r]) : pt[r];
-                  pv[r] = jj <= i ? x : 0.f;
+                  pv[r] = (jb < tb || jj <= i) ? x : 0.f;   // only the diagonal block is masked
                 }
                 *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(pv);
               }
@@ -361,11 +359,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // every LDS operand of this phase is read up front: T and P blocks, R^T for the update
           const uint16_t *Tm = &sm.t[cur][0][0], *Pm = &sm.p[0][0];
           const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-          const short4v t00 = ld4(Tm + l16 * kLdc + 4 * l4), t22 = ld4(Tm + (32 + l16) * kLdc + 32 + 4 * l4);
-          const short8v t10 = opsp(Tm, kLdc, 16 + l16, 0, l4), t20 = opsp(Tm, kLdc, 32 + l16, 0, l4);
+          // (T and P are lower triangular and their upper blocks stay zero in LDS, so the diagonal
+          // blocks are read as K = 32 operands together with the zero block beside them)
+          const short8v t00 = opsp(Tm, kLdc, l16, 0, l4), t10 = opsp(Tm, kLdc, 16 + l16, 0, l4);
+          const short8v t20 = opsp(Tm, kLdc, 32 + l16, 0, l4), t22 = opsp(Tm, kLdc, 32 + l16, 32, l4);
           const short8v t30 = opsp(Tm, kLdc, 48 + l16, 0, l4), t32 = opsp(Tm, kLdc, 48 + l16, 32, l4);
-          const short4v p00 = ld4(Pm + l16 * kLdc + 4 * l4), p22 = ld4(Pm + (32 + l16) * kLdc + 32 + 4 * l4);
-          const short8v p10 = opsp(Pm, kLdc, 16 + l16, 0, l4), p20 = opsp(Pm, kLdc, 32 + l16, 0, l4);
+          const short8v p00 = opsp(Pm, kLdc, l16, 0, l4), p10 = opsp(Pm, kLdc, 16 + l16, 0, l4);
+          const short8v p20 = opsp(Pm, kLdc, 32 + l16, 0, l4), p22 = opsp(Pm, kLdc, 32 + l16, 32, l4);
           const short8v p30 = opsp(Pm, kLdc, 48 + l16, 0, l4), p32 = opsp(Pm, kLdc, 48 + l16, 32, l4);
           short8v ra[4], rb[4];   // R^T operands of the first half of the update
 #pragma unroll
@@ -381,9 +381,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // D = T X
           const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
           float4v D[4];
-          D[0] = mfma16(t00, x4[0], zero4());
+          D[0] = mfma32(t00, x01, zero4());
           D[1] = mfma32(t10, x01, zero4());
-          D[2] = mfma16(t22, x4[2], mfma32(t20, x01, zero4()));
+          D[2] = mfma32(t22, x23, mfma32(t20, x01, zero4()));
           D[3] = mfma32(t32, x23, mfma32(t30, x01, zero4()));
           // state update S^T <- e^{g_C} S^T + R^T (wd (.) D), interleaved with O2 = P D
           short4v w4[4], d4[4];
@@ -409,15 +409,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
           }
           float4v O2[4];
-          O2[0] = mfma16(p00, d4[0], zero4());
-          O2[1] = mfma32(p10, d01, zero4());
-          O2[2] = mfma16(p22, d4[2], mfma32(p20, d01, zero4()));
-          O2[3] = mfma32(p32, d23, mfma32(p30, d01, zero4()));
+          // O1 seeds the accumulator: O = scale (O1 + P D)
+          O2[0] = mfma32(p00, d01, O1[0]);
+          O2[1] = mfma32(p10, d01, O1[1]);
+          O2[2] = mfma32(p22, d23, mfma32(p20, d01, O1[2]));
+          O2[3] = mfma32(p32, d23, mfma32(p30, d01, O1[3]));
           // output: transpose each 16 x 16 block by an identity product so a lane holds four
           // consecutive values of one token, then 8-byte stores
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) {
-            const float4v o = a.scale * (O1[tb] + O2[tb]);
+            const float4v o = a.scale * O2[tb];
             const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
             const int t = tb * 16 + l16;
             if (t < n) {
@@ -475,20 +476,36 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     col = isv ? (u & (BV / 8 - 1)) * 8 : (u & 15) * 8;
   };
 
+  // Per-slot addressing, fixed for the whole sequence: this lane's item of chunk 0 in global
+  // memory (row srow of the chunk) and its LDS byte offset in buffer 0 of its array, so the
+  // per-chunk work is a clamp, one multiply-add, the loads and the stores.
+  const uint16_t *gsrc[NSB], *gsrc2[NSB];
+  int srow[NSB], loff[NSB], lstr[NSB], eoff[NSB];
+  char *const smb = reinterpret_cast<char *>(&sm);
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) {
+    const int blk = slot_block(s);
+    const bool isv = blk >= NBP;
+    const int arr = blk >> 4;
+    int t, col;
+    item_rc(blk, t, col);
+    srow[s] = t;
+    const long long g0 = head0 + (isv ? v0 : 0) + col;
+    gsrc[s] = (isv ? gv : arr == 0 ? gq : arr == 1 ? gk : gwk) + g0;
+    gsrc2[s] = CHAN ? (isv ? gwr : ger) + g0 : gsrc[s];
+    uint16_t *d0 = isv ? &sm.vp[0][t][col] : (arr == 0 ? sm.q[0] : arr == 1 ? sm.k[0] : sm.r[0]) + sw128(t, col);
+    loff[s] = static_cast<int>(reinterpret_cast<char *>(d0) - smb);
+    lstr[s] = isv ? static_cast<int>(sizeof(sm.vp[0])) : kC * kD * 2;
+    eoff[s] = static_cast<int>(reinterpret_cast<char *>(sm.e[0] + (CHAN ? sw128(t, col) : 0)) - smb);
+  }
+
   auto load_items = [&](int c) {
     const int c0 = c * kC, nm1 = min(kC, T - c0) - 1;
-    const long long cb = head0 + static_cast<long long>(c0) * tokstride;   // chunk base (uniform)
 #pragma unroll
     for (int s = 0; s < NSB; ++s) {
-      const int blk = slot_block(s);
-      const bool isv = blk >= NBP;
-      const int arr = blk >> 4;
-      int t, col;
-      item_rc(blk, t, col);
-      const int off = min(t, nm1) * tok32 + (isv ? v0 : 0) + col;
-      const uint16_t *src = isv ? gv : arr == 0 ? gq : arr == 1 ? gk : gwk;
-      pa[s] = *reinterpret_cast<const uint4 *>(src + cb + off);
-      if (CHAN) pb[s] = *reinterpret_cast<const uint4 *>((isv ? gwr : ger) + cb + off);
+      const long long off = static_cast<long long>(c0 + min(srow[s], nm1)) * tokstride;
+      pa[s] = *reinterpret_cast<const uint4 *>(gsrc[s] + off);
+      if (CHAN) pb[s] = *reinterpret_cast<const uint4 *>(gsrc2[s] + off);
     }
     const long long gi = gate0 + static_cast<long long>(c0) * H + min(lane, nm1) * H;
     if (DECAY) gla = a.log_alpha[gi];
@@ -500,11 +517,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     for (int s = 0; s < NSB; ++s) {
       const int blk = slot_block(s);
       const bool live = s * NHW + hw < NB;
-      const bool isv = blk >= NBP;
-      const int arr = blk >> 4;
-      int t, col;
-      item_rc(blk, t, col);
-      const uint32_t m = t < n ? 0xffffffffu : 0u;
+      const bool isv = blk >= NBP, isk = !isv && (blk >> 4) == 1;
+      const uint32_t m = srow[s] < n ? 0xffffffffu : 0u;
       const uint4 x = make_uint4(pa[s].x & m, pa[s].y & m, pa[s].z & m, pa[s].w & m);
       uint4 xg = x;   // gated copy: erase (.) k, write (.) v
       if (CHAN) {
@@ -514,13 +528,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         xg.w = f32x2_to_bf16x2_bits(elem(pb[s], 6) * elem(x, 6), elem(pb[s], 7) * elem(x, 7));
       }
       if (live) {
-        if (isv) {
-          *reinterpret_cast<uint4 *>(&sm.vp[buf][t][col]) = xg;
-        } else {
-          uint16_t *dst = arr == 0 ? sm.q[buf] : arr == 1 ? sm.k[buf] : sm.r[buf];
-          *reinterpret_cast<uint4 *>(&dst[sw128(t, col)]) = x;
-          if (CHAN && arr == 1) *reinterpret_cast<uint4 *>(&sm.e[buf][sw128(t, col)]) = xg;
-        }
+        // (component-wise choice: a whole-vector choice by a run-time flag goes through memory)
+        const uint4 y = CHAN ? make_uint4(isv ? xg.x : x.x, isv ? xg.y : x.y, isv ? xg.z : x.z, isv ? xg.w : x.w) : x;
+        *reinterpret_cast<uint4 *>(smb + loff[s] + buf * lstr[s]) = y;
+        if (CHAN && isk) *reinterpret_cast<uint4 *>(smb + eoff[s] + buf * (kC * kD * 2)) = xg;
       }
     }
     // gates: cumulative log decay in log2 units and the quantities derived from it.  Every
