@@ -683,28 +683,40 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     if (WK == kWkPrecond) {
       // write keys of chunk c + 1: u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2
       if (have_next && pc_thread) {
+        // this thread: channel pc_c, tokens s0 .. s0 + 31 of chunk c + 1 (rows past the end of
+        // the sequence were staged as zero and are masked below); every LDS read is issued up
+        // front and both passes are unrolled, so only the arithmetic chain remains serial
+        const uint16_t *Kn = sm.k[nxt];
         const int nn = min(kC, T - (c + 1) * kC);
         const int ch = pc_c, s0 = pc_seg * 32;
         const int m = max(0, min(32, nn - s0));
-        float acc = 0.f, rm = 1.f;
-        for (int i = 0; i < m; ++i) {
-          const float kk = bf(sm.k[nxt][sw128(s0 + i, ch)]);
-          acc = fmaf(a.rho, acc, kk * kk);
-          rm *= a.rho;
+        float kv[32], icv[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) kv[i] = bf(Kn[sw128(s0 + i, ch)]);
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+          const float4 t4 = ld4f(&sm.ic[nxt][s0 + i]);
+          icv[i] = t4.x, icv[i + 1] = t4.y, icv[i + 2] = t4.z, icv[i + 3] = t4.w;
+        }
+        float acc = 0.f, rm = 1.f;   // this segment's affine map h -> rm h + acc
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const bool on = i < m;
+          acc = on ? fmaf(a.rho, acc, kv[i] * kv[i]) : acc;
+          rm = on ? rm * a.rho : rm;
         }
         // compose the two halves' affine maps h -> rm h + acc
         const float rm0 = __shfl(rm, lane & ~1, 64), ac0 = __shfl(acc, lane & ~1, 64);
         const float rm1 = __shfl(rm, lane | 1, 64), ac1 = __shfl(acc, lane | 1, 64);
         const float mid = fmaf(rm0, hcarry, ac0);
         float hv = pc_seg == 0 ? hcarry : mid;
+#pragma unroll
         for (int i = 0; i < 32; ++i) {
-          float u = 0.f;
-          if (i < m) {
-            const float kk = bf(sm.k[nxt][sw128(s0 + i, ch)]);
-            hv = fmaf(a.rho, hv, kk * kk);
-            u = kk / fmaf(hv, sm.ic[nxt][s0 + i], a.eps);
-          }
-          sm.r[nxt][sw128(s0 + i, ch)] = tobf(u);
+          const bool on = i < m;
+          hv = on ? fmaf(a.rho, hv, kv[i] * kv[i]) : hv;
+          // (the key is rounded to bf16 next, so the hardware reciprocal is accurate enough)
+          const float u = kv[i] * __builtin_amdgcn_rcpf(fmaf(hv, icv[i], a.eps));
+          sm.r[nxt][sw128(s0 + i, ch)] = tobf(on ? u : 0.f);
         }
         hcarry = fmaf(rm1, mid, ac1);
       }
