@@ -41,6 +41,7 @@
 // rows 4 (l / 16) + r of the first tile, slots 4..7 those of the second, and the A
 // operand is gathered from LDS in the same order.  A product X Y whose factors are both
 // accumulators needs acc(X^T) and acc(Y); transposed copies are computed where needed.
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -684,39 +685,49 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       // write keys of chunk c + 1: u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2
       if (have_next && pc_thread) {
         // this thread: channel pc_c, tokens s0 .. s0 + 31 of chunk c + 1 (rows past the end of
-        // the sequence were staged as zero and are masked below); every LDS read is issued up
-        // front and both passes are unrolled, so only the arithmetic chain remains serial
+        // the sequence were staged as zero and are masked below); the keys are read up front and
+        // both passes are unrolled, so only the arithmetic chain remains serial
         const uint16_t *Kn = sm.k[nxt];
         const int nn = min(kC, T - (c + 1) * kC);
         const int ch = pc_c, s0 = pc_seg * 32;
         const int m = max(0, min(32, nn - s0));
-        float kv[32], icv[32];
+        float kv[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) kv[i] = bf(Kn[sw128(s0 + i, ch)]);
+        float kk2[32];
 #pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-          const float4 t4 = ld4f(&sm.ic[nxt][s0 + i]);
-          icv[i] = t4.x, icv[i + 1] = t4.y, icv[i + 2] = t4.z, icv[i + 3] = t4.w;
-        }
+        for (int i = 0; i < 32; ++i) kk2[i] = kv[i] * kv[i];
         float acc = 0.f, rm = 1.f;   // this segment's affine map h -> rm h + acc
+        if (m == 32) {               // every token present (all but a partial last chunk)
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const bool on = i < m;
-          acc = on ? fmaf(a.rho, acc, kv[i] * kv[i]) : acc;
-          rm = on ? rm * a.rho : rm;
+          for (int i = 0; i < 32; ++i) acc = fmaf(a.rho, acc, kk2[i]);
+          const float r2 = a.rho * a.rho, r4 = r2 * r2, r8 = r4 * r4, r16 = r8 * r8;
+          rm = r16 * r16;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const bool on = i < m;
+            acc = on ? fmaf(a.rho, acc, kk2[i]) : acc;
+            rm = on ? rm * a.rho : rm;
+          }
         }
         // compose the two halves' affine maps h -> rm h + acc
         const float rm0 = __shfl(rm, lane & ~1, 64), ac0 = __shfl(acc, lane & ~1, 64);
         const float rm1 = __shfl(rm, lane | 1, 64), ac1 = __shfl(acc, lane | 1, 64);
         const float mid = fmaf(rm0, hcarry, ac0);
         float hv = pc_seg == 0 ? hcarry : mid;
+        uint16_t *Rn = sm.r[nxt] + s0 * kD + (ch & 7);
+        const int cg = ch >> 3;
+        float4 ic4;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
+          if ((i & 3) == 0) ic4 = ld4f(&sm.ic[nxt][s0 + i]);
+          const float icv = (&ic4.x)[i & 3];
           const bool on = i < m;
-          hv = on ? fmaf(a.rho, hv, kv[i] * kv[i]) : hv;
+          hv = on ? fmaf(a.rho, hv, kk2[i]) : hv;
           // (the key is rounded to bf16 next, so the hardware reciprocal is accurate enough)
-          const float u = kv[i] * __builtin_amdgcn_rcpf(fmaf(hv, icv[i], a.eps));
-          sm.r[nxt][sw128(s0 + i, ch)] = tobf(on ? u : 0.f);
+          const float u = kv[i] * __builtin_amdgcn_rcpf(fmaf(hv, icv, a.eps));
+          Rn[i * kD + ((cg ^ (i & 15)) << 3)] = tobf(on ? u : 0.f);   // sw128(s0 + i, ch), s0 % 16 == 0
         }
         hcarry = fmaf(rm1, mid, ac1);
       }
@@ -816,11 +827,21 @@ bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const floa
   return true;
 }
 
-// Value-tile width: the widest tile that still gives every CU a workgroup.
-static int chunk_mfma_bv(int B, int H) { return (static_cast<long long>(B) * H * (kD / 32) >= 256) ? 32 : 16; }
+// Value-tile width.  Every workgroup walks its whole sequence, so a call takes about
+// (chunks) x (time per chunk) once all workgroups are resident.  With scalar gains and write
+// key k the 32-row tile (two value waves forming P from their own operands) has the shorter
+// chunk time and is used even when it leaves CUs idle; the other variants keep the widest
+// tile that still gives every CU a workgroup.  GDR_MFMA_BV=16|32 overrides (tuning runs).
+static int chunk_mfma_bv(const ChunkArgs &a) {
+  const char *e = getenv("GDR_MFMA_BV");
+  const int forced = e == nullptr ? 0 : atoi(e);
+  if (forced == 16 || forced == 32) return forced;
+  if (a.gain == GDR_GAIN_SCALAR && a.wkey == GDR_WKEY_SAME) return 32;
+  return (static_cast<long long>(a.B) * a.H * (kD / 32) >= 256) ? 32 : 16;
+}
 
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
-  return chunk_mfma_bv(a.B, a.H) == 32 ? launch_bv<32>(a, s) : launch_bv<16>(a, s);
+  return chunk_mfma_bv(a) == 32 ? launch_bv<32>(a, s) : launch_bv<16>(a, s);
 }
 
 }  // namespace gdr

@@ -344,10 +344,16 @@ MFMA_VARIANTS = ["gdn", "plain", "gdn2", "gdn2_decay", "pdn", "pdn_decay", "expl
 
 
 @pytest.mark.parametrize("variant", MFMA_VARIANTS)
-@pytest.mark.parametrize("B,H,T", [(2, 2, 200), (4, 16, 130)])   # value tiles of 16 and 32 rows
-def test_mfma_variants(variant, B, H, T):
+@pytest.mark.parametrize("BV,B,H,T", [(16, 2, 2, 200), (32, 2, 2, 200), (0, 4, 16, 130)])
+def test_mfma_variants(variant, BV, B, H, T, monkeypatch):
+    """Every variant on the matrix-core kernel with value tiles of 16 and 32 state rows
+    (forced through GDR_MFMA_BV; 0 = the library's own choice)."""
+    if BV:
+        monkeypatch.setenv("GDR_MFMA_BV", str(BV))
+    else:
+        monkeypatch.delenv("GDR_MFMA_BV", raising=False)
     s = small(variant, "bf16", Dk=128, Dv=128, T=T, B=B, H=H)
-    announce(f"mfma {variant} B={B} H={H} T={T}")
+    announce(f"mfma {variant} BV={BV} B={B} H={H} T={T}")
     x = gs.make_inputs(s)
     rng = np.random.default_rng(3)
     S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
