@@ -57,8 +57,11 @@ constexpr int kC = 64;          // chunk
 constexpr int kD = 128;         // Dk = Dv
 constexpr int kNW = 8;          // waves per workgroup
 constexpr int kNT = kNW * 64;   // threads
-constexpr int kLdc = kC + 8;    // padded bf16 row stride of [*][64] tiles (T, P, V'^T)
-constexpr int kLdl = 32 + 8;    // bf16 row stride of the 32 x 32 block A_ba
+// padded bf16 row strides: 136 bytes (34 banks of 4) for the [64][64] tiles T and P and 72
+// bytes (18 banks) for the 32 x 32 block A_ba, so the 16 rows an 8-byte-per-lane access
+// touches land on distinct banks
+constexpr int kLdc = kC + 4;
+constexpr int kLdl = 32 + 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum : int { kWkSame = 0, kWkPrecond = 1, kWkExplicit = 2 };
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // consecutive values of one token, then 8-byte stores
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) {
-            const float4v o = a.scale * O2[tb];
+            const float4v o = a.scale == 1.f ? O2[tb] : a.scale * O2[tb];
             const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
             const int t = tb * 16 + l16;
             if (t < n) {
@@ -519,8 +522,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       const int blk = slot_block(s);
       const bool live = s * NHW + hw < NB;
       const bool isv = blk >= NBP, isk = !isv && (blk >> 4) == 1;
-      const uint32_t m = srow[s] < n ? 0xffffffffu : 0u;
-      const uint4 x = make_uint4(pa[s].x & m, pa[s].y & m, pa[s].z & m, pa[s].w & m);
+      uint4 x = pa[s];
+      if (n < kC) {   // rows past the end of the sequence (read clamped) are zeroed
+        const uint32_t m = srow[s] < n ? 0xffffffffu : 0u;
+        x = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+      }
       uint4 xg = x;   // gated copy: erase (.) k, write (.) v
       if (CHAN) {
         xg.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(x, 0), elem(pb[s], 1) * elem(x, 1));
