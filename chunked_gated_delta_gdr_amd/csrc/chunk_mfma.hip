@@ -202,10 +202,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
   constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
   constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
-  // with E = beta k and R = k, P = tril(Q K^T) is formed by the two value waves from the K and
-  // Q operands they already hold for Y and O1; otherwise (and with a single value wave, which
+  // with write key R = k, P = tril(Q K^T) is formed by the two value waves from the Q operands
+  // they already hold for O1 and the K operands of Y (scalar gains, E = beta k) or read
+  // beside them (channel gates, E = b (.) k); otherwise (and with a single value wave, which
   // would have to keep every K block) the helper waves form it
-  constexpr bool kPv = (WK == kWkSame) && !CHAN && NVW == 2;
+  constexpr bool kPv = (WK == kWkSame) && NVW == 2;
   __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // one register set per block for the E operands (the wave keeps those of its own P column
           // blocks alive; the others die after their block), double-buffered Q operands
           short8v ev[4][4], qv[2][4];
+          short8v kq[2][4];   // channel gates: K operands of this wave's two P column blocks
           // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
           // wave 0, 1 and 2 to wave 1)
           constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
@@ -302,6 +304,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
             // V' block (rows t, columns v) in the accumulator layout, read transposed
             vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
+            if (CHAN && kPv && p_owner(tb) == W) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = ops128(sm.k[cur], tb * 16 + l16, 32 * j, l4);
+            }
             egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
             if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
             if (kPv) giv[slot] = sm.g2[cur][tb * 16 + l16];
@@ -343,7 +349,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 if (p_owner(jb) != W) continue;
                 float4v pt = zero4();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pt = mfma32(ev[jb][j], qv[sl][j], pt);
+                for (int j = 0; j < 4; ++j) pt = mfma32(CHAN ? kq[p_slot(jb)][j] : ev[jb][j], qv[sl][j], pt);
                 const float4 gj = gjv[p_slot(jb)];
                 float4v pv;
 #pragma unroll
@@ -834,15 +840,15 @@ bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const floa
 }
 
 // Value-tile width.  Every workgroup walks its whole sequence, so a call takes about
-// (chunks) x (time per chunk) once all workgroups are resident.  With scalar gains and write
-// key k the 32-row tile (two value waves forming P from their own operands) has the shorter
-// chunk time and is used even when it leaves CUs idle; the other variants keep the widest
-// tile that still gives every CU a workgroup.  GDR_MFMA_BV=16|32 overrides (tuning runs).
+// (chunks) x (time per chunk) once all workgroups are resident.  With write key k the 32-row
+// tile (two value waves forming P from their own operands) has the shorter chunk time and is
+// used even when it leaves CUs idle; the other variants keep the widest tile that still gives
+// every CU a workgroup.  GDR_MFMA_BV=16|32 overrides (tuning runs).
 static int chunk_mfma_bv(const ChunkArgs &a) {
   const char *e = getenv("GDR_MFMA_BV");
   const int forced = e == nullptr ? 0 : atoi(e);
   if (forced == 16 || forced == 32) return forced;
-  if (a.gain == GDR_GAIN_SCALAR && a.wkey == GDR_WKEY_SAME) return 32;
+  if (a.wkey == GDR_WKEY_SAME) return 32;
   return (static_cast<long long>(a.B) * a.H * (kD / 32) >= 256) ? 32 : 16;
 }
 
