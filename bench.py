@@ -32,7 +32,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 KERNEL_SOURCES = {
     "mfma": ["chunked_gated_delta_gdr_amd/csrc/chunk_mfma.hip"],
     "generic": ["chunked_gated_delta_gdr_amd/csrc/chunk_generic.hip"],
+    "step": ["chunked_gated_delta_gdr_amd/csrc/recurrent_step.hip"],
 }
+KERNEL_SYMBOLS = {"mfma": "chunk_mfma", "generic": "chunk_generic", "step": "step_kernel"}
 
 
 def alg_bytes(s) -> int:
@@ -65,10 +67,14 @@ def source_sha(impl: str) -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_file(workload: str, impl: str) -> str:
+    return "step_decode_traffic.json" if impl == "step" else f"chunk_fwd_{impl}_{workload}_traffic.json"
+
+
 def traffic_from_profile(workload: str, impl: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"chunk_fwd_{impl}_{workload}_traffic.json")
+    p = os.path.join(ROOT, "profiles", traffic_file(workload, impl))
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -165,7 +171,7 @@ def _counter_per_dispatch(csv_path: str, counter: str, name_has: str):
 def traffic_summary(args):
     """Writes profiles/chunk_fwd_<impl>_<workload>_traffic.json from four counter CSVs."""
     import statistics
-    kern = "chunk_mfma" if args.impl_name == "mfma" else "chunk_generic"
+    kern = KERNEL_SYMBOLS[args.impl_name]
     f_k = _counter_per_dispatch(args.traffic_summary[0], "FETCH_SIZE", kern)
     w_k = _counter_per_dispatch(args.traffic_summary[1], "WRITE_SIZE", kern)
     f_c = _counter_per_dispatch(args.traffic_summary[2], "FETCH_SIZE", "copy")
@@ -175,18 +181,23 @@ def traffic_summary(args):
     # still in the last-level cache from the fill)
     fac_f, fac_w = copy_kib / f_c[-1], copy_kib / w_c[-1]
     fetch, write = statistics.median(f_k), statistics.median(w_k)
-    s = __import__("gdr_synth").spec(args.workload)
+    if args.workload == "decode":
+        sd = __import__("gdr_synth").spec("long")
+        ab = decode_alg_bytes(sd.decode_batch, sd.H, sd.Dk, sd.Dv)
+    else:
+        ab = alg_bytes(__import__("gdr_synth").spec(args.workload))
     rec = {
-        "kernel": f"gdr_chunk_fwd/{args.impl_name}", "workload": args.workload,
+        "kernel": "gdr_recurrent_step" if args.impl_name == "step" else f"gdr_chunk_fwd/{args.impl_name}",
+        "workload": args.workload,
         "source_sha": source_sha(args.impl_name),
         "fetch_kib_per_dispatch_median": fetch, "write_kib_per_dispatch_median": write,
         "dispatches": [len(f_k), len(w_k)],
         "copy_probe_mib": args.copy_probe_mb, "copy_fetch_kib": f_c[-1], "copy_write_kib": w_c[-1],
         "scale_fetch": fac_f, "scale_write": fac_w,
         "hbm_bytes_per_launch": round((fetch * fac_f + write * fac_w) * 1024.0),
-        "alg_bytes_per_launch": alg_bytes(s),
+        "alg_bytes_per_launch": ab,
     }
-    out = os.path.join(ROOT, "profiles", f"chunk_fwd_{args.impl_name}_{args.workload}_traffic.json")
+    out = os.path.join(ROOT, "profiles", traffic_file(args.workload, args.impl_name))
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -270,7 +281,8 @@ def bench_decode(args):
         "config": {"workload": f"decode: batch {Bd} H{H} Dk{Dk} Dv{Dv} bf16 scalar gain+decay, state fp32 in place",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gdr_recurrent_step",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("decode", "step"),
+                     "kernel": "gdr_recurrent_step",
                      "alg_bytes_per_launch": ab, "avg_launch_us": round(avg_s * 1e6, 2)},
         "cpu_baseline": None, "parity": parity,
     }
@@ -292,7 +304,7 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                            "COPY_WRITE_CSV"),
                     help="write the traffic summary of --workload from rocprofv3 counter CSVs")
-    ap.add_argument("--impl-name", default="mfma", choices=["mfma", "generic"])
+    ap.add_argument("--impl-name", default="mfma", choices=["mfma", "generic", "step"])
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args)
@@ -426,7 +438,8 @@ def main():
         cpu = cpu_baseline(s, x, tokens=min(s.T, max(64, 300_000 // (s.B * s.H))), n_streams=s.B * s.H)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "gdn" else
+        f"tokens/s chunked gated-delta fwd ({args.workload}: B{s.B} H{s.H} T{s.T} d{s.Dk} {s.dtype}); % MFMA/HBM peak",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
