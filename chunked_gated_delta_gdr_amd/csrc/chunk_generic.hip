@@ -27,6 +27,21 @@ constexpr int kThreads = 256;
 constexpr int kBV = 16;     // state rows per workgroup
 constexpr int kCMax = 64;   // largest chunk
 
+// dot product of two zero-padded DK-long LDS rows: four partial sums (shorter dependency
+// chains; the padding beyond Dk is zero on both sides, so it adds nothing)
+template <int DK>
+__device__ __forceinline__ float dotrow(const float *x, const float *y) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int c = 0; c < DK; c += 4) {
+    s0 = fmaf(x[c], y[c], s0);
+    s1 = fmaf(x[c + 1], y[c + 1], s1);
+    s2 = fmaf(x[c + 2], y[c + 2], s2);
+    s3 = fmaf(x[c + 3], y[c + 3], s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
 template <typename IO, int DK>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   const IO *__restrict__ q = static_cast<const IO *>(a.q);
@@ -116,8 +131,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     for (int idx = tid; idx < n * n; idx += kThreads) {
       const int i = idx / n, j = idx % n;
       if (j < i) {
-        float dot = 0.f;
-        for (int c = 0; c < Dk; ++c) dot = fmaf(Xs[i][c], Rs[j][c], dot);
+        const float dot = dotrow<DK>(Xs[i], Rs[j]);
         LT[i][j] = expf(gs[i] - gs[j]) * dot;
       }
     }
@@ -126,8 +140,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       const int t = idx / kBV, r = idx % kBV;
       float x = 0.f;
       if (r < nv) {
-        float dot = 0.f;
-        for (int c = 0; c < Dk; ++c) dot = fmaf(Xs[t][c], Ss[r][c], dot);
+        const float dot = dotrow<DK>(Xs[t], Ss[r]);
         const long long vi = tok(t) * Dv + v0 + r;
         const float vv = ld_f(v, vi);
         const float vp = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
@@ -136,19 +149,36 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       Xv[t][r] = x;
     }
     __syncthreads();
-    // T = (I - A)^-1, one thread per column; T_ij (i > j) stored at LT[j][i]
-    if (tid < n) {
-      const int j = tid;
-      for (int i = j + 1; i < n; ++i) {
-        float acc = 0.f;
-        if (a.N < 0 || i - j <= a.N) {
-          for (int l = j; l < i; ++l) {
-            const float A_il = -LT[i][l];
-            const float T_lj = (l == j) ? 1.f : LT[j][l];
-            acc = fmaf(A_il, T_lj, acc);
+    // T = (I - A)^-1, T_ij (i > j) stored at LT[j][i].  Right-looking order: thread
+    // (row i = tid / 4, columns 16 (tid % 4) .. + 15) adds the term A_il T_lj to T_ij at step
+    // l = j .. i - 1, so every entry sums its terms in the same order as column-by-column
+    // forward substitution (acc = 0; for l = j .. i-1: acc = fma(A_il, T_lj, acc)), but the
+    // steps run over all rows and columns at once; row l + 1 is final after step l and is
+    // published before the next step reads it.  Band entries (i - j > N) stay zero.
+    {
+      static_assert(kThreads == 4 * kCMax, "one thread per (row, 16-column group)");
+      const int i = tid >> 2, jg = (tid & 3) * 16;
+      float acc[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+      for (int l = 0; l + 1 < n; ++l) {
+        if (i > l && i < n) {
+          const float A_il = -LT[i][l];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int j = jg + q;
+            if (j <= l && (a.N < 0 || i - j <= a.N)) {
+              const float T_lj = (j == l) ? 1.f : LT[j][l];
+              acc[q] = fmaf(A_il, T_lj, acc[q]);
+            }
           }
         }
-        LT[j][i] = acc;
+        if (i == l + 1) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (jg + q < i) LT[jg + q][i] = acc[q];
+        }
+        __syncthreads();
       }
     }
     // queries replace the erase keys (last read before the barrier above)
@@ -161,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     for (int idx = tid; idx < n * kBV; idx += kThreads) {
       const int t = idx / kBV, r = idx % kBV;
       float acc = Xv[t][r];
+      #pragma unroll 8
       for (int s = 0; s < t; ++s) acc = fmaf(LT[s][t], Xv[s][r], acc);
       Dl[t][r] = acc;
     }
@@ -168,8 +199,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     for (int idx = tid; idx < n * n; idx += kThreads) {
       const int i = idx / n, j = idx % n;
       if (j <= i) {
-        float dot = 0.f;
-        for (int c = 0; c < Dk; ++c) dot = fmaf(Xs[i][c], Rs[j][c], dot);
+        const float dot = dotrow<DK>(Xs[i], Rs[j]);
         LT[i][j] = expf(gs[i] - gs[j]) * dot;
       }
     }
@@ -178,9 +208,9 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     for (int idx = tid; idx < n * kBV; idx += kThreads) {
       const int t = idx / kBV, r = idx % kBV;
       if (r < nv) {
-        float dot = 0.f;
-        for (int c = 0; c < Dk; ++c) dot = fmaf(Xs[t][c], Ss[r][c], dot);
+        const float dot = dotrow<DK>(Xs[t], Ss[r]);
         float acc = eg[t] * dot;
+        #pragma unroll 8
         for (int j = 0; j <= t; ++j) acc = fmaf(LT[t][j], Dl[j][r], acc);
         st_f(out, tok(t) * Dv + v0 + r, a.scale * acc);
       }
@@ -192,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       const int r = idx / DK, c = idx % DK;
       if (r < nv && c < Dk) {
         float acc = gl * Ss[r][c];
+        #pragma unroll 8
         for (int j = 0; j < n; ++j) acc = fmaf(Dl[j][r] * wd[j], Rs[j][c], acc);
         Ss[r][c] = acc;
       }
