@@ -9,11 +9,11 @@
 //   g      inclusive cumulative sum of log alpha inside the chunk
 //   L_ij   = exp(g_i - g_j) (e_i . r_j)              for j < i   (A = -L)
 //   X      = V' - (e^g (.) E) S^T                      (value tile only)
-//   T      = (I - A)^-1 by forward substitution, column by column; entry order
-//            acc = 0; for l = j .. i-1: acc = fma(A_il, T_lj, acc)
-//            With a band limit N only entries with i - j <= N are formed (they use only
-//            band entries of A: Lemma 3.1 of the same summary, Metodologia 1-2), so
-//            N >= n - 1 runs exactly the same instructions as the exact path.
+//   T      = (I - A)^-1: forward substitution inside the four 16 x 16 diagonal blocks, then
+//            the off-diagonal blocks as block products.  With a band limit N only entries
+//            with i - j <= N are kept (they use only band entries of the factors: Lemma 3.1
+//            of the same summary, Metodologia 1-2), so N >= n - 1 runs exactly the same
+//            instructions as the exact path.
 //   D      = T X                                     (= U - W S^T of the WY form)
 //   P_ij   = exp(g_i - g_j) (q_i . r_j)              for j <= i
 //   O      = scale ((e^g (.) Q) S^T + P D)
@@ -27,23 +27,21 @@ constexpr int kThreads = 256;
 constexpr int kBV = 16;     // state rows per workgroup
 constexpr int kCMax = 64;   // largest chunk
 
-// dot product of two zero-padded DK-long LDS rows: four partial sums (shorter dependency
-// chains; the padding beyond Dk is zero on both sides, so it adds nothing)
-template <int DK>
-__device__ __forceinline__ float dotrow(const float *x, const float *y) {
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-  for (int c = 0; c < DK; c += 4) {
-    s0 = fmaf(x[c], y[c], s0);
-    s1 = fmaf(x[c + 1], y[c + 1], s1);
-    s2 = fmaf(x[c + 2], y[c + 2], s2);
-    s3 = fmaf(x[c + 3], y[c + 3], s3);
-  }
-  return (s0 + s1) + (s2 + s3);
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+__device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &y) {
+  acc = fmaf(x.x, y.x, acc);
+  acc = fmaf(x.y, y.y, acc);
+  acc = fmaf(x.z, y.z, acc);
+  acc = fmaf(x.w, y.w, acc);
 }
 
 template <typename IO, int DK>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
+  // fp32 row stride of the [token][channel] tiles: 16-byte aligned rows whose starts fall on
+  // distinct 16-byte bank groups for 16 consecutive rows (conflict-free 16-byte reads)
+  constexpr int LD = DK + 4;
+  constexpr int kLoadIt = kCMax * DK / kThreads;   // elements per thread of one staged tile
   const IO *__restrict__ q = static_cast<const IO *>(a.q);
   const IO *__restrict__ k = static_cast<const IO *>(a.k);
   const IO *__restrict__ v = static_cast<const IO *>(a.v);
@@ -58,173 +56,365 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   const int nv = min(kBV, a.Dv - v0);
   const int Dk = a.Dk, Dv = a.Dv, H = a.H, T = a.T;
 
-  __shared__ float Rs[kCMax][DK + 1];     // write keys r
-  __shared__ float Xs[kCMax][DK + 1];     // erase keys e, then queries q
-  __shared__ float LT[kCMax][kCMax + 1];  // L (strict lower) | T^T (strict upper) | P (lower)
-  __shared__ float Ss[kBV][DK + 1];       // state tile
-  __shared__ float Xv[kCMax][kBV];        // X
-  __shared__ float Dl[kCMax][kBV];        // D
+  __shared__ __align__(16) float Rs[kCMax][LD];     // write keys r
+  __shared__ __align__(16) float Xs[kCMax][LD];     // erase keys e, then queries q
+  __shared__ float LP[kCMax][kCMax + 1];            // L (strict lower), then P (lower)
+  __shared__ __align__(16) float Tm[kCMax][kCMax + 4];   // T, row-major
+  __shared__ __align__(16) float Zs[32][32 + 4];         // block products in flight
+  __shared__ __align__(16) float Ss[kBV][LD];       // state tile
+  __shared__ __align__(16) float Xv[kCMax][kBV];    // X
+  __shared__ __align__(16) float Dl[kCMax][kBV];    // D
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
 
   const long long sh = static_cast<long long>(b) * H + h;  // (b, h) index
-  for (int idx = tid; idx < kBV * DK; idx += kThreads) {
-    const int r = idx / DK, c = idx % DK;
+  for (int idx = tid; idx < kBV * LD; idx += kThreads) {
+    const int r = idx / LD, c = idx % LD;
     float s = 0.f;
     if (a.state_in != nullptr && r < nv && c < Dk) s = a.state_in[(sh * Dv + v0 + r) * Dk + c];
     Ss[r][c] = s;
+  }
+  // the 16 x 16 blocks of T above the diagonal are never written: zero once
+  for (int idx = tid; idx < kCMax * kCMax; idx += kThreads) {
+    const int i = idx / kCMax, j = idx % kCMax;
+    if ((j >> 4) > (i >> 4)) Tm[i][j] = 0.f;
   }
   float hreg = 0.f;  // preconditioner accumulator of channel `tid`
   if (a.wkey == GDR_WKEY_DIAG_PRECOND && tid < Dk)
     hreg = a.pc_h_in != nullptr ? a.pc_h_in[sh * Dk + tid] : a.h0;
 
+  // thread tiles: 4 x 4 blocks of the C x C products, 2 x 2 blocks of the C x kBV ones
+  const int bi = tid >> 4, bj = tid & 15;      // rows 4 bi.., columns 4 bj..
+  const int t0 = 2 * (tid >> 3), r0 = 2 * (tid & 7);
+
   for (int c0 = 0; c0 < T; c0 += a.C) {
     const int n = min(a.C, T - c0);
     // token (b, c0 + t, h) row index in [B, T, H]
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
+    // Element (t, c) of a [B, T, H, Dk] tensor sits t * H * Dk + c after the chunk's first
+    // token row (a 32-bit offset: 64 H Dk < 2^31).  stage() copies rows 0..n-1 of such a tile
+    // into dst (zero beyond n and Dk); every load of the tile is issued before the first store.
+    const long long row0 = tok(0);
+    const int rstride = H * Dk;
+    auto stage = [&](float(*dst)[LD], auto &&load) {
+      float x[kLoadIt];
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        x[it] = (t < n && c < Dk) ? load(t, t * rstride + c) : 0.f;
+      }
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads;
+        dst[idx / DK][idx % DK] = x[it];
+      }
+    };
+    // LP[i][j] = exp(g_i - g_j) (Xs_i . Rs_j) for j < i (or j <= i), zero above; rows past n
+    // hold zero keys, so they come out zero
+    auto gram = [&](bool incl_diag) {
+      if (bj > bi) return;
+      float acc[4][4] = {};
+#pragma unroll 4
+      for (int c = 0; c < DK; c += 4) {
+        float4 x[4], r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u] = ld4(&Xs[4 * bi + u][c]);
+          r[u] = ld4(&Rs[4 * bj + u][c]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) fma4(acc[u][w], x[u], r[w]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = 4 * bi + u, j = 4 * bj + w;
+          LP[i][j] = (j < i || (incl_diag && j == i)) ? expf(gs[i] - gs[j]) * acc[u][w] : 0.f;
+        }
+    };
+    // (Xs_t . Ss_r) for the thread's 2 x 2 block of tokens t0.. and state rows r0..
+    auto dot_state = [&](float (&acc)[2][2]) {
+#pragma unroll 4
+      for (int c = 0; c < DK; c += 4) {
+        const float4 x0 = ld4(&Xs[t0][c]), x1 = ld4(&Xs[t0 + 1][c]);
+        const float4 s0 = ld4(&Ss[r0][c]), s1 = ld4(&Ss[r0 + 1][c]);
+        fma4(acc[0][0], x0, s0);
+        fma4(acc[0][1], x0, s1);
+        fma4(acc[1][0], x1, s0);
+        fma4(acc[1][1], x1, s1);
+      }
+    };
 
     __syncthreads();  // previous chunk done with every buffer
-    if (tid < n) gs[tid] = (a.decay == GDR_DECAY_SCALAR) ? a.log_alpha[tok(tid)] : 0.f;
-    // write keys
+    // write keys (the preconditioned ones are formed from the staged keys below)
+    const IO *kc = k + row0 * Dk;
+    {
+      const IO *src = ((a.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
+      stage(Rs, [&](int, int o) { return ld_f(src, o); });
+    }
+    // erase keys
+    if (a.gain == GDR_GAIN_SCALAR) {
+      const float *bc = a.beta + row0;
+      stage(Xs, [&](int t, int o) { return bc[t * H] * ld_f(kc, o); });
+    } else {
+      const IO *ec = er + row0 * Dk;
+      stage(Xs, [&](int, int o) { return ld_f(ec, o) * ld_f(kc, o); });
+    }
+    // gates: inclusive cumulative sum of log alpha over the chunk (one wave)
+    if (tid < kCMax) {
+      float g = (a.decay == GDR_DECAY_SCALAR && tid < n) ? a.log_alpha[tok(tid)] : 0.f;
+#pragma unroll
+      for (int d = 1; d < kCMax; d <<= 1) {
+        const float y = __shfl_up(g, d, kCMax);
+        if (tid >= d) g += y;
+      }
+      const float glast = __shfl(g, n - 1, kCMax);
+      gs[tid] = g;
+      eg[tid] = expf(g);
+      wd[tid] = expf(glast - g);
+    }
     if (a.wkey == GDR_WKEY_DIAG_PRECOND) {
+      __syncthreads();
+      // u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2: channel `tid` walks the chunk
       if (tid < Dk) {
         for (int t = 0; t < n; ++t) {
-          const float kk = ld_f(k, tok(t) * Dk + tid);
+          const float kk = Rs[t][tid];
           hreg = fmaf(a.rho, hreg, kk * kk);
           const float tg = static_cast<float>(a.t0 + c0 + t + 1);
           const float corr = -expm1f(tg * a.log_rho);  // 1 - rho^t
           Rs[t][tid] = kk / (hreg / corr + a.eps);
         }
-      } else if (tid < DK) {
-        for (int t = 0; t < n; ++t) Rs[t][tid] = 0.f;
-      }
-    } else {
-      const IO *src = (a.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
-      for (int idx = tid; idx < n * DK; idx += kThreads) {
-        const int t = idx / DK, c = idx % DK;
-        Rs[t][c] = c < Dk ? ld_f(src, tok(t) * Dk + c) : 0.f;
-      }
-    }
-    // erase keys
-    for (int idx = tid; idx < n * DK; idx += kThreads) {
-      const int t = idx / DK, c = idx % DK;
-      float e = 0.f;
-      if (c < Dk) {
-        const float kk = ld_f(k, tok(t) * Dk + c);
-        e = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * kk : ld_f(er, tok(t) * Dk + c) * kk;
-      }
-      Xs[t][c] = e;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float acc = 0.f;
-      for (int t = 0; t < n; ++t) {
-        acc += gs[t];
-        gs[t] = acc;
       }
     }
     __syncthreads();
-    if (tid < n) {
-      eg[tid] = expf(gs[tid]);
-      wd[tid] = expf(gs[n - 1] - gs[tid]);
-    }
     // L (strict lower)
-    for (int idx = tid; idx < n * n; idx += kThreads) {
-      const int i = idx / n, j = idx % n;
-      if (j < i) {
-        const float dot = dotrow<DK>(Xs[i], Rs[j]);
-        LT[i][j] = expf(gs[i] - gs[j]) * dot;
-      }
-    }
+    gram(false);
     // X = V' - (e^g (.) E) S^T on the value tile
-    for (int idx = tid; idx < n * kBV; idx += kThreads) {
-      const int t = idx / kBV, r = idx % kBV;
-      float x = 0.f;
-      if (r < nv) {
-        const float dot = dotrow<DK>(Xs[t], Ss[r]);
-        const long long vi = tok(t) * Dv + v0 + r;
-        const float vv = ld_f(v, vi);
-        const float vp = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
-        x = vp - expf(gs[t]) * dot;
-      }
-      Xv[t][r] = x;
-    }
-    __syncthreads();
-    // T = (I - A)^-1, T_ij (i > j) stored at LT[j][i].  Right-looking order: thread
-    // (row i = tid / 4, columns 16 (tid % 4) .. + 15) adds the term A_il T_lj to T_ij at step
-    // l = j .. i - 1, so every entry sums its terms in the same order as column-by-column
-    // forward substitution (acc = 0; for l = j .. i-1: acc = fma(A_il, T_lj, acc)), but the
-    // steps run over all rows and columns at once; row l + 1 is final after step l and is
-    // published before the next step reads it.  Band entries (i - j > N) stay zero.
     {
-      static_assert(kThreads == 4 * kCMax, "one thread per (row, 16-column group)");
-      const int i = tid >> 2, jg = (tid & 3) * 16;
-      float acc[16];
+      float vp[2][2];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-      for (int l = 0; l + 1 < n; ++l) {
-        if (i > l && i < n) {
-          const float A_il = -LT[i][l];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int j = jg + q;
-            if (j <= l && (a.N < 0 || i - j <= a.N)) {
-              const float T_lj = (j == l) ? 1.f : LT[j][l];
-              acc[q] = fmaf(A_il, T_lj, acc[q]);
-            }
+        for (int w = 0; w < 2; ++w) {
+          const int t = t0 + u, r = r0 + w;
+          vp[u][w] = 0.f;
+          if (t < n && r < nv) {
+            const long long vi = tok(t) * Dv + v0 + r;
+            const float vv = ld_f(v, vi);
+            vp[u][w] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
           }
         }
-        if (i == l + 1) {
+      float acc[2][2] = {};
+      dot_state(acc);
 #pragma unroll
-          for (int q = 0; q < 16; ++q)
-            if (jg + q < i) LT[jg + q][i] = acc[q];
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int t = t0 + u, r = r0 + w;
+          Xv[t][r] = (t < n && r < nv) ? vp[u][w] - eg[t] * acc[u][w] : 0.f;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    // T = (I - A)^-1 by 16 x 16 blocks.  With D_b = (I - A_bb)^-1 (the four diagonal blocks,
+    // solved at once, one wave each, by right-looking forward substitution: at step l every
+    // row i > l adds A_il T_lj, so each entry sums its terms in increasing l),
+    //   T_10 = D_1 A_10 D_0,  T_32 = D_3 A_32 D_2,  T_ba = T_b A_ba T_a
+    // where a, b are the 32 x 32 halves (T_a = [D_0 0; T_10 D_1], T_b likewise).  Every entry is
+    // band-masked as it is written: the band of each product depends only on the bands of its
+    // factors (Lemma 3.1), so the band entries are those of the exact path, bit for bit, and
+    // N >= n - 1 runs exactly the exact path's instructions.  Rows past n have zero A rows,
+    // so their T rows are unit rows.
+    {
+      auto keep = [&](int i, int j) { return a.N < 0 || i - j <= a.N; };
+      const int lane = tid & 63, w = tid >> 6;
+      {   // diagonal block w: lane = (block row ii, block columns jq .. jq + 3)
+        const int ii = lane >> 2, jq = (lane & 3) * 4;
+        const int o = 16 * w, gi = o + ii;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ii == 0) *reinterpret_cast<float4 *>(&Tm[o][o + jq]) = make_float4(jq == 0 ? 1.f : 0.f, 0.f, 0.f, 0.f);
+        // rows of the block are published and read by lanes of this wave only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int l = 0; l < 15; ++l) {
+          const float A_il = l < ii ? -LP[gi][o + l] : 0.f;
+          const float4 t = ld4(&Tm[o + l][o + jq]);
+          acc[0] = fmaf(A_il, t.x, acc[0]);
+          acc[1] = fmaf(A_il, t.y, acc[1]);
+          acc[2] = fmaf(A_il, t.z, acc[2]);
+          acc[3] = fmaf(A_il, t.w, acc[3]);
+          if (ii == l + 1) {
+            float r[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int jj = jq + u;
+              r[u] = jj == ii ? 1.f : (jj < ii && keep(ii, jj)) ? acc[u] : 0.f;
+            }
+            *reinterpret_cast<float4 *>(&Tm[gi][o + jq]) = make_float4(r[0], r[1], r[2], r[3]);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
       }
+      __syncthreads();
+      // two 16 x 16 products at once: thread = (product p, row r, columns c, c + 1)
+      const int p = tid >> 7, r = (tid >> 3) & 15, c = (tid & 7) * 2;
+      {   // Z_p = A_(2p+1, 2p) D_2p
+        const int ro = 32 * p + 16, co = 32 * p;
+        float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const float av = -LP[ro + r][co + m];
+          const float2 d = ld2(&Tm[co + m][co + c]);
+          z0 = fmaf(av, d.x, z0);
+          z1 = fmaf(av, d.y, z1);
+        }
+        *reinterpret_cast<float2 *>(&Zs[16 * p + r][c]) = make_float2(z0, z1);
+      }
+      __syncthreads();
+      {   // T_(2p+1, 2p) = D_(2p+1) Z_p
+        const int ro = 32 * p + 16, co = 32 * p;
+        float t0v = 0.f, t1v = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const float dv = Tm[ro + r][ro + m];
+          const float2 z = ld2(&Zs[16 * p + m][c]);
+          t0v = fmaf(dv, z.x, t0v);
+          t1v = fmaf(dv, z.y, t1v);
+        }
+        const int i = ro + r, j = co + c;
+        Tm[i][j] = keep(i, j) ? t0v : 0.f;
+        Tm[i][j + 1] = keep(i, j + 1) ? t1v : 0.f;
+      }
+      __syncthreads();
+      // 32 x 32 products: thread = (row r2, columns c4 .. c4 + 3)
+      const int r2 = tid >> 3, c4 = (tid & 7) * 4;
+      {   // Z = A_ba T_a
+        float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int m = 0; m < 32; ++m) {
+          const float av = -LP[32 + r2][m];
+          const float4 t = ld4(&Tm[m][c4]);
+          z[0] = fmaf(av, t.x, z[0]);
+          z[1] = fmaf(av, t.y, z[1]);
+          z[2] = fmaf(av, t.z, z[2]);
+          z[3] = fmaf(av, t.w, z[3]);
+        }
+        *reinterpret_cast<float4 *>(&Zs[r2][c4]) = make_float4(z[0], z[1], z[2], z[3]);
+      }
+      __syncthreads();
+      {   // T_ba = T_b Z
+        float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int m = 0; m < 32; ++m) {
+          const float tb = Tm[32 + r2][32 + m];
+          const float4 z = ld4(&Zs[m][c4]);
+          t[0] = fmaf(tb, z.x, t[0]);
+          t[1] = fmaf(tb, z.y, t[1]);
+          t[2] = fmaf(tb, z.z, t[2]);
+          t[3] = fmaf(tb, z.w, t[3]);
+        }
+        const int i = 32 + r2;
+        float4 o4;
+        o4.x = keep(i, c4) ? t[0] : 0.f;
+        o4.y = keep(i, c4 + 1) ? t[1] : 0.f;
+        o4.z = keep(i, c4 + 2) ? t[2] : 0.f;
+        o4.w = keep(i, c4 + 3) ? t[3] : 0.f;
+        *reinterpret_cast<float4 *>(&Tm[i][c4]) = o4;
+      }
+      __syncthreads();
     }
     // queries replace the erase keys (last read before the barrier above)
-    for (int idx = tid; idx < n * DK; idx += kThreads) {
-      const int t = idx / DK, c = idx % DK;
-      Xs[t][c] = c < Dk ? ld_f(q, tok(t) * Dk + c) : 0.f;
+    {
+      const IO *qc = q + row0 * Dk;
+      stage(Xs, [&](int, int o) { return ld_f(qc, o); });
     }
     __syncthreads();
-    // D = T X  (reads the strict upper part of LT)
-    for (int idx = tid; idx < n * kBV; idx += kThreads) {
-      const int t = idx / kBV, r = idx % kBV;
-      float acc = Xv[t][r];
-      #pragma unroll 8
-      for (int s = 0; s < t; ++s) acc = fmaf(LT[s][t], Xv[s][r], acc);
-      Dl[t][r] = acc;
-    }
-    // P (lower incl. diagonal; disjoint from the strict upper part read above)
-    for (int idx = tid; idx < n * n; idx += kThreads) {
-      const int i = idx / n, j = idx % n;
-      if (j <= i) {
-        const float dot = dotrow<DK>(Xs[i], Rs[j]);
-        LT[i][j] = expf(gs[i] - gs[j]) * dot;
+    // D = T X: acc = X_tr; for s < t: acc += T_ts X_sr
+    {
+      float acc[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float2 x = ld2(&Xv[t0 + u][r0]);
+        acc[u][0] = x.x;
+        acc[u][1] = x.y;
       }
+      for (int s = 0; s < t0; ++s) {
+        const float2 x = ld2(&Xv[s][r0]);
+        const float a0 = Tm[t0][s], a1 = Tm[t0 + 1][s];
+        acc[0][0] = fmaf(a0, x.x, acc[0][0]);
+        acc[0][1] = fmaf(a0, x.y, acc[0][1]);
+        acc[1][0] = fmaf(a1, x.x, acc[1][0]);
+        acc[1][1] = fmaf(a1, x.y, acc[1][1]);
+      }
+      {   // s = t0 for the second row
+        const float2 x = ld2(&Xv[t0][r0]);
+        const float a1 = Tm[t0 + 1][t0];
+        acc[1][0] = fmaf(a1, x.x, acc[1][0]);
+        acc[1][1] = fmaf(a1, x.y, acc[1][1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<float2 *>(&Dl[t0 + u][r0]) = make_float2(acc[u][0], acc[u][1]);
     }
+    // P (lower incl. diagonal; L is no longer needed)
+    gram(true);
     __syncthreads();
     // O = scale ((e^g (.) Q) S^T + P D)
-    for (int idx = tid; idx < n * kBV; idx += kThreads) {
-      const int t = idx / kBV, r = idx % kBV;
-      if (r < nv) {
-        const float dot = dotrow<DK>(Xs[t], Ss[r]);
-        float acc = eg[t] * dot;
-        #pragma unroll 8
-        for (int j = 0; j <= t; ++j) acc = fmaf(LT[t][j], Dl[j][r], acc);
-        st_f(out, tok(t) * Dv + v0 + r, a.scale * acc);
+    {
+      float acc[2][2] = {};
+      dot_state(acc);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        acc[u][0] *= eg[t0 + u];
+        acc[u][1] *= eg[t0 + u];
       }
+      for (int j = 0; j <= t0; ++j) {
+        const float2 d = ld2(&Dl[j][r0]);
+        const float p0 = LP[t0][j], p1 = LP[t0 + 1][j];
+        acc[0][0] = fmaf(p0, d.x, acc[0][0]);
+        acc[0][1] = fmaf(p0, d.y, acc[0][1]);
+        acc[1][0] = fmaf(p1, d.x, acc[1][0]);
+        acc[1][1] = fmaf(p1, d.y, acc[1][1]);
+      }
+      {   // j = t0 + 1 for the second row
+        const float2 d = ld2(&Dl[t0 + 1][r0]);
+        const float p1 = LP[t0 + 1][t0 + 1];
+        acc[1][0] = fmaf(p1, d.x, acc[1][0]);
+        acc[1][1] = fmaf(p1, d.y, acc[1][1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int t = t0 + u, r = r0 + w;
+          if (t < n && r < nv) st_f(out, tok(t) * Dv + v0 + r, a.scale * acc[u][w]);
+        }
     }
     __syncthreads();
-    // S <- e^{g_n} S + D^T (e^{g_n - g} (.) R)
-    const float gl = eg[n - 1];
-    for (int idx = tid; idx < kBV * DK; idx += kThreads) {
-      const int r = idx / DK, c = idx % DK;
-      if (r < nv && c < Dk) {
-        float acc = gl * Ss[r][c];
-        #pragma unroll 8
-        for (int j = 0; j < n; ++j) acc = fmaf(Dl[j][r] * wd[j], Rs[j][c], acc);
-        Ss[r][c] = acc;
+    // S <- e^{g_n} S + D^T (e^{g_n - g} (.) R): thread (row r, columns c..c+3); rows past nv
+    // and columns past Dk stay zero (their D rows and key columns are zero)
+    {
+      const float gl = eg[n - 1];
+      constexpr int NC4 = DK / 4;
+#pragma unroll
+      for (int u0 = 0; u0 < kBV * NC4; u0 += kThreads) {
+        const int u = u0 + tid;
+        if (kBV * NC4 % kThreads != 0 && u >= kBV * NC4) break;
+        const int r = u / NC4, c = (u % NC4) * 4;
+        const float4 s = ld4(&Ss[r][c]);
+        float4 acc = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        for (int j = 0; j < n; ++j) {
+          const float w = Dl[j][r] * wd[j];
+          const float4 rr = ld4(&Rs[j][c]);
+          acc.x = fmaf(w, rr.x, acc.x);
+          acc.y = fmaf(w, rr.y, acc.y);
+          acc.z = fmaf(w, rr.z, acc.z);
+          acc.w = fmaf(w, rr.w, acc.w);
+        }
+        *reinterpret_cast<float4 *>(&Ss[r][c]) = acc;
       }
     }
   }
