@@ -6,7 +6,7 @@ chunked forward runs inside it).  Default workload: scalar-gated delta rule, B4 
 Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain|decode]
-                    [--neumann N] [--impl auto|generic|mfma] [--no-cpu-baseline]
+                    [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
 
 Counter helpers (used to produce the committed traffic summaries under profiles/):
     python bench.py --copy-probe-mb 256          # calibration copy of known size
@@ -49,12 +49,16 @@ def alg_bytes(s) -> int:
     return s.B * s.T * s.H * per_tok + s.B * s.H * per_head
 
 
-def alg_flops(s, band=None) -> float:
+def alg_flops(s, band=None, residual=0) -> float:
     """Algorithmic FLOPs per call (triangular products counted triangular):
     per token-head MACs = 3 Dk Dv (W S^T, Q S^T, state update) + (C-1)/2 Dk (A)
-    + (C+1)/2 (2 Dk + 2 Dv) (W, U, Q R^T, P D) + C^2/6 (forward substitution)."""
+    + (C+1)/2 (2 Dk + 2 Dv) (W, U, Q R^T, P D) + C^2/6 (forward substitution), the last
+    term N (N + 1) / 2 for a band N; a residual correction of S steps adds S + 2 triangular
+    C x C x C products per chunk ((A T0, S times E Z, T0 Z): (S + 2) C^2 / 6 per token)."""
     C, Dk, Dv = s.chunk, s.Dk, s.Dv
     tri = C * C / 6.0 if band is None or band >= C - 1 else (band * (band + 1) / 2.0)
+    if band is not None and residual > 0:
+        tri += (residual + 2) * C * C / 6.0
     macs = 3 * Dk * Dv + (C - 1) / 2 * Dk + (C + 1) / 2 * (2 * Dk + 2 * Dv) + tri
     return 2.0 * macs * s.B * s.T * s.H
 
@@ -296,6 +300,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn", choices=["gdn", "gdn2", "pdn", "long", "plain", "decode"])
     ap.add_argument("--neumann", type=int, default=-1)
+    ap.add_argument("--residual", type=int, default=0,
+                    help="residual-correction steps on the band-N start (needs --neumann N)")
     ap.add_argument("--impl", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -359,7 +365,8 @@ def main():
         G.gdr_chunk_fwd(a["q"], a["k"], a["v"], beta=a["beta"], log_alpha=a["log_alpha"], erase=a["erase"],
                         write=a["write"], write_key=a["write_key"], precond=precond,
                         pc_h_out=hs[j] if precond else None, out=outs[j], state_out=states[j],
-                        chunk=s.chunk, neumann_order=args.neumann, impl=args.impl, stream=stream)
+                        chunk=s.chunk, neumann_order=args.neumann, residual_steps=args.residual,
+                        impl=args.impl, stream=stream)
 
     impl_code = G.gdr_chunk_fwd_impl(G.make_desc(
         B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
@@ -367,7 +374,7 @@ def main():
         gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
         decay=G.GDR_DECAY_SCALAR if s.decay == "scalar" else G.GDR_DECAY_NONE,
         wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=args.neumann,
-        impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
+        residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
     impl_name = {G.GDR_IMPL_MFMA: "mfma", G.GDR_IMPL_GENERIC: "generic"}.get(impl_code, "?")
     print(f"[bench] workload {args.workload} impl {impl_name} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
@@ -400,7 +407,7 @@ def main():
     tokens = s.B * s.T
     value = tokens / (ms_per_step / 1e3)
     ab = alg_bytes(s)
-    af = alg_flops(s, None if args.neumann < 0 else args.neumann)
+    af = alg_flops(s, None if args.neumann < 0 else args.neumann, args.residual)
     achieved_gbs = ab / avg_launch_s / 1e9
     roofline = {
         "bound": "hbm",
@@ -427,7 +434,8 @@ def main():
         if args.neumann < 0:
             o_ref, _, _ = oracle.recurrent(sub, precond=pre)
         else:
-            o_ref, _, _ = oracle.chunked(sub, chunk=s.chunk, t_mode=("neumann", args.neumann), precond=pre)
+            mode = ("neumann", args.neumann) if args.residual <= 0 else ("residual", args.neumann, args.residual)
+            o_ref, _, _ = oracle.chunked(sub, chunk=s.chunk, t_mode=mode, precond=pre)
         got = outs[j][:1, :n, :1].double().cpu().numpy()
         parity = {"stream": "(0,0)", "tokens": n, "rel_l2_out": oracle.rel_l2(got, o_ref)}
 
@@ -453,7 +461,8 @@ def main():
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), gates as the workload states)",
         "config": {"workload": f"{args.workload}: B{s.B} H{s.H} T{s.T} Dk{s.Dk} Dv{s.Dv} C{s.chunk} "
                                f"{s.dtype} gain={s.gain} decay={s.decay} wkey={s.wkey}"
-                               + (f" band N={args.neumann}" if args.neumann >= 0 else " exact T"),
+                               + (f" band N={args.neumann}" if args.neumann >= 0 else " exact T")
+                               + (f" + {args.residual} residual steps" if args.neumann >= 0 and args.residual > 0 else ""),
                    "B": s.B, "T": s.T, "H": s.H, "Dk": s.Dk, "Dv": s.Dv, "chunk": s.chunk,
                    "impl": impl_name, "parallelism": "single GPU"},
         "roofline": roofline,

@@ -24,7 +24,7 @@ class gdr_desc_t(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("io_dtype", ctypes.c_int32), ("gain", ctypes.c_int32), ("decay", ctypes.c_int32),
         ("wkey", ctypes.c_int32),
-        ("neumann_order", ctypes.c_int32), ("impl", ctypes.c_int32),
+        ("neumann_order", ctypes.c_int32), ("residual_steps", ctypes.c_int32), ("impl", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("pc_rho", ctypes.c_float), ("pc_eps", ctypes.c_float), ("pc_h0", ctypes.c_float),
         ("pc_t0", ctypes.c_int64),
@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_last_error.restype = ctypes.c_char_p
         L.gdr_abi_version.argtypes = []
         L.gdr_abi_version.restype = ctypes.c_int
-        if L.gdr_abi_version() != 1:
+        if L.gdr_abi_version() != 2:
             raise ImportError("libgdr ABI version mismatch")
         _LIB = L
     return _LIB
@@ -100,10 +100,11 @@ def gdr_abi_version() -> int:
 
 
 def make_desc(*, B, T, H, Dk, Dv, chunk=64, io_dtype=GDR_BF16, gain=GDR_GAIN_SCALAR,
-              decay=GDR_DECAY_NONE, wkey=GDR_WKEY_SAME, neumann_order=-1, impl=GDR_IMPL_AUTO,
-              scale=1.0, pc_rho=0.99, pc_eps=1e-3, pc_h0=1.0, pc_t0=0) -> gdr_desc_t:
+              decay=GDR_DECAY_NONE, wkey=GDR_WKEY_SAME, neumann_order=-1, residual_steps=0,
+              impl=GDR_IMPL_AUTO, scale=1.0, pc_rho=0.99, pc_eps=1e-3, pc_h0=1.0,
+              pc_t0=0) -> gdr_desc_t:
     return gdr_desc_t(ctypes.sizeof(gdr_desc_t), B, T, H, Dk, Dv, chunk, io_dtype, gain, decay, wkey,
-                      neumann_order, impl, scale, pc_rho, pc_eps, pc_h0, pc_t0)
+                      neumann_order, residual_steps, impl, scale, pc_rho, pc_eps, pc_h0, pc_t0)
 
 
 def gdr_validate(desc: gdr_desc_t, inputs: gdr_inputs_t, state_in=None, out=None, state_out=None,
@@ -168,15 +169,17 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
                   precond: bool = False, pc_h_in=None, pc_h_out=None, pc_rho: float = 0.99,
                   pc_eps: float = 1e-3, pc_h0: float = 1.0, pc_t0: int = 0,
                   state_in=None, out=None, state_out=None, return_state: bool = True,
-                  chunk: int = 64, neumann_order: int = -1, scale: float = 1.0, impl: str = "auto",
+                  chunk: int = 64, neumann_order: int = -1, residual_steps: int = 0,
+                  scale: float = 1.0, impl: str = "auto",
                   stream=None) -> Tuple[object, object, object]:
     """Chunked forward on torch tensors (q, k, v [B, T, H, D]).  Returns (out, state_out, pc_h_out).
 
     Gains: ``beta`` [B, T, H] fp32, or ``erase`` [B, T, H, Dk] and ``write`` [B, T, H, Dv].
     Decay: ``log_alpha`` [B, T, H] fp32 or None.  Write key: ``write_key`` [B, T, H, Dk],
     or ``precond=True`` for the diagonal preconditioner (accumulator ``pc_h_in`` [B, H, Dk]
-    fp32 or None for ``pc_h0``).  Outputs are allocated when not given; ``state_out`` is
-    allocated only if ``return_state``.
+    fp32 or None for ``pc_h0``).  T: exact (``neumann_order`` < 0), the band N
+    (``neumann_order`` = N), or that band corrected by ``residual_steps`` residual steps.
+    Outputs are allocated when not given; ``state_out`` is allocated only if ``return_state``.
     """
     torch = _torch()
     B, T, H, Dk = q.shape
@@ -210,7 +213,8 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
                      decay=GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE,
                      wkey=(GDR_WKEY_DIAG_PRECOND if precond else
                            GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME),
-                     neumann_order=neumann_order, impl=_IMPL[impl], scale=scale,
+                     neumann_order=neumann_order, residual_steps=residual_steps,
+                     impl=_IMPL[impl], scale=scale,
                      pc_rho=pc_rho, pc_eps=pc_eps, pc_h0=pc_h0, pc_t0=pc_t0)
     ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
                        _ptr(write_key), _ptr(pc_h_in) if precond else None,

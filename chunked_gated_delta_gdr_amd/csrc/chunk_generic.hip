@@ -14,6 +14,8 @@
 //            with i - j <= N are kept (they use only band entries of the factors: Lemma 3.1
 //            of the same summary, Metodologia 1-2), so N >= n - 1 runs exactly the same
 //            instructions as the exact path.
+//            Optionally (S > 0, band start N) the parallel residual correction of the
+//            same summary, Metodologia 3: T = T0 sum_{s<=S} E^s, E = I - (I - A) T0.
 //   D      = T X                                     (= U - W S^T of the WY form)
 //   P_ij   = exp(g_i - g_j) (q_i . r_j)              for j <= i
 //   O      = scale ((e^g (.) Q) S^T + P D)
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   __shared__ float LP[kCMax][kCMax + 1];            // L (strict lower), then P (lower)
   __shared__ __align__(16) float Tm[kCMax][kCMax + 4];   // T, row-major
   __shared__ __align__(16) float Zs[32][32 + 4];         // block products in flight
+  __shared__ __align__(16) float Zb[kCMax][kCMax + 4];   // residual-correction series
   __shared__ __align__(16) float Ss[kBV][LD];       // state tile
   __shared__ __align__(16) float Xv[kCMax][kBV];    // X
   __shared__ __align__(16) float Dl[kCMax][kBV];    // D
@@ -325,6 +328,71 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         o4.w = keep(i, c4 + 3) ? t[3] : 0.f;
         *reinterpret_cast<float4 *>(&Tm[i][c4]) = o4;
       }
+      __syncthreads();
+    }
+    // Parallel residual correction of the band start T0 (MatMul-only inversion summary,
+    // Metodologia 3): E = I - (I - A) T0, Z = I + E (I + E (... (I + E))) with S factors
+    // (= sum_{s<=S} E^s), T = T0 Z.  E and Z are strictly lower / unit lower triangular, so
+    // each product sums over l < i (l <= i for T0 Z).  Thread: row i, columns jg .. jg + 15;
+    // every product is formed in registers and written back after a barrier (E over L, Z
+    // in place, T over T0).
+    if (a.S > 0) {
+      const int i = tid >> 2, jg = (tid & 3) * 16;
+      float acc[16];
+      auto row_product = [&](const float(*Lm)[kCMax + 1], const float(*Tr)[kCMax + 4], int lend, bool neg) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+        for (int l = 0; l < lend; ++l) {
+          const float x = neg ? -Lm[i][l] : Lm[i][l];
+#pragma unroll
+          for (int u = 0; u < 16; u += 4) {
+            const float4 t = ld4(&Tr[l][jg + u]);
+            acc[u] = fmaf(x, t.x, acc[u]);
+            acc[u + 1] = fmaf(x, t.y, acc[u + 1]);
+            acc[u + 2] = fmaf(x, t.z, acc[u + 2]);
+            acc[u + 3] = fmaf(x, t.w, acc[u + 3]);
+          }
+        }
+      };
+      // E_ij = delta_ij - T0_ij + (A T0)_ij, A = -L
+      row_product(LP, Tm, i, true);
+      float e[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) e[u] = ((jg + u == i) ? 1.f : 0.f) - Tm[i][jg + u] + acc[u];
+      __syncthreads();   // every row of A has been read
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        LP[i][jg + u] = e[u];
+        Zb[i][jg + u] = (jg + u == i) ? 1.f : 0.f;
+      }
+      __syncthreads();
+      for (int st = 0; st < a.S; ++st) {   // Z <- I + E Z
+        row_product(LP, Zb, i, false);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 16; ++u) Zb[i][jg + u] = ((jg + u == i) ? 1.f : 0.f) + acc[u];
+        __syncthreads();
+      }
+      // T = T0 Z (T0 is lower triangular: l <= i)
+      {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+        for (int l = 0; l <= i; ++l) {
+          const float x = Tm[i][l];
+#pragma unroll
+          for (int u = 0; u < 16; u += 4) {
+            const float4 z = ld4(&Zb[l][jg + u]);
+            acc[u] = fmaf(x, z.x, acc[u]);
+            acc[u + 1] = fmaf(x, z.y, acc[u + 1]);
+            acc[u + 2] = fmaf(x, z.z, acc[u + 2]);
+            acc[u + 3] = fmaf(x, z.w, acc[u + 3]);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 16; u += 4)
+        *reinterpret_cast<float4 *>(&Tm[i][jg + u]) = make_float4(acc[u], acc[u + 1], acc[u + 2], acc[u + 3]);
       __syncthreads();
     }
     // queries replace the erase keys (last read before the barrier above)

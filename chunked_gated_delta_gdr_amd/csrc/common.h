@@ -21,6 +21,7 @@ struct ChunkArgs {
   float *state_out;
   int B, T, H, Dk, Dv, C;
   int gain, decay, wkey, N;   // N < 0: exact T; else band i - j <= N
+  int S;                      // residual-correction steps on the band start (0: none)
   float scale, rho, log_rho, eps, h0;
   long long t0;
 };

@@ -97,6 +97,14 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
   if (d->impl != GDR_IMPL_AUTO && d->impl != GDR_IMPL_GENERIC && d->impl != GDR_IMPL_MFMA)
     return fail(GDR_EINVAL, "impl = %d", d->impl);
   if (!std::isfinite(d->scale)) return fail(GDR_EINVAL, "scale must be finite");
+  if (!for_step) {
+    if (d->residual_steps < 0) return fail(GDR_EINVAL, "residual_steps = %d must be >= 0", d->residual_steps);
+    if (d->residual_steps > 0 && d->neumann_order < 0)
+      return fail(GDR_EINVAL, "residual_steps = %d needs a band start (neumann_order >= 0)", d->residual_steps);
+    if (d->residual_steps > 64)
+      return fail(GDR_ENOTSUP, "residual_steps = %d (max 64; E^s vanishes once s (N + 1) >= C)",
+                  d->residual_steps);
+  }
 
   const long double B = d->B, T = d->T, H = d->H, Dk = d->Dk, Dv = d->Dv;
   if (B * T * H * (Dk > Dv ? Dk : Dv) > kMaxElems || B * H * Dv * Dk > kMaxElems)
@@ -195,6 +203,7 @@ static gdr::ChunkArgs make_args(const gdr_desc_t *d, const gdr_inputs_t *in, con
   a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv; a.C = d->chunk;
   a.gain = d->gain; a.decay = d->decay; a.wkey = d->wkey;
   a.N = d->neumann_order < 0 ? -1 : d->neumann_order;
+  a.S = a.N < 0 ? 0 : d->residual_steps;
   a.scale = d->scale;
   a.rho = d->pc_rho; a.log_rho = d->wkey == GDR_WKEY_DIAG_PRECOND ? std::log(d->pc_rho) : 0.f;
   a.eps = d->pc_eps; a.h0 = d->pc_h0; a.t0 = d->pc_t0;
@@ -208,14 +217,15 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
   const bool mfma_ok = gdr::chunk_mfma_supports(*d, *in, state_in, out, state_out);
   if (d->impl == GDR_IMPL_MFMA && !mfma_ok)
     return fail(GDR_ENOTSUP, "the MFMA kernel does not cover this descriptor "
-                             "(needs bf16, Dk = Dv = 128, chunk 64, 16-byte aligned tensors)");
+                             "(needs bf16, Dk = Dv = 128, chunk 64, 16-byte aligned tensors, "
+                             "no residual correction)");
   const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
   const gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled())
-    std::fprintf(stderr, "[gdr] chunk_fwd %s B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d N=%d\n",
+    std::fprintf(stderr, "[gdr] chunk_fwd %s B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d N=%d S=%d\n",
                  use_mfma ? "mfma" : "generic", d->B, d->T, d->H, d->Dk, d->Dv, d->chunk,
-                 d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay, d->wkey, a.N);
+                 d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay, d->wkey, a.N, a.S);
   const hipError_t e = use_mfma ? gdr::launch_chunk_mfma(a, s) : gdr::launch_chunk_generic(a, d->io_dtype, s);
   if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

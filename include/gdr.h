@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum {
   GDR_OK = 0,
@@ -85,6 +85,12 @@ typedef struct gdr_desc {
                              truncated Neumann series sum_{n<=N} A^n, which equals the band
                              of the exact inverse); N >= C - 1 reproduces the exact path
                              bit for bit in fp32                                           */
+  int32_t residual_steps; /* S >= 0, only with neumann_order = N >= 0: when S > 0, T is the
+                             parallel residual correction of the band-N start
+                             T0 = band_N((I - A)^-1): E = I - (I - A) T0 and
+                             T = T0 (I + E + ... + E^S)  (MatMul-only inversion summary,
+                             Metodologia 3).  Exact once (S + 1)(N + 1) >= C.  Only the
+                             generic kernel implements it (GDR_ENOTSUP with impl MFMA)     */
   int32_t impl;           /* GDR_IMPL_AUTO picks the fastest kernel for the shape;
                              GENERIC forces the fp32 VALU kernel; MFMA forces the bf16
                              matrix-core kernel (GDR_ENOTSUP if the shape is outside it)   */

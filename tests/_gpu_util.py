@@ -29,8 +29,8 @@ def precond_opts(s):
     return dict(rho=s.pc_rho, eps=s.pc_eps, h0=s.pc_h0, t0=0) if s.wkey == "precond" else None
 
 
-def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, impl="auto",
-              scale=1.0, chunk=None, sync=True):
+def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, residual_steps=0,
+              impl="auto", scale=1.0, chunk=None, sync=True):
     """gdr_chunk_fwd on inputs ``x`` (numpy, from gdr_synth).  Returns torch tensors."""
     import torch
     import chunked_gated_delta_gdr_amd as G
@@ -44,6 +44,7 @@ def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, i
         precond=s.wkey == "precond", pc_h_in=dev(pc_h_in, f32), pc_rho=s.pc_rho, pc_eps=s.pc_eps,
         pc_h0=s.pc_h0, pc_t0=pc_t0,
         state_in=dev(state_in, f32), chunk=chunk or s.chunk, neumann_order=neumann_order,
+        residual_steps=residual_steps,
         scale=scale, impl=impl)
     if sync:
         torch.cuda.synchronize()

@@ -31,14 +31,14 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert G.gdr_abi_version() == 1
+    assert G.gdr_abi_version() == 2
     for s in (G.GDR_OK, G.GDR_EINVAL, G.GDR_ENOTSUP, G.GDR_EHIP):
         assert G.gdr_status_str(s).startswith("GDR_")
     assert "UNKNOWN" in G.gdr_status_str(42)
 
 
 def test_struct_layout_matches_header():
-    # int32 fields and an int64 at the end: 4 + 12*4 + 4*4 + 8 = 76 -> padded to 80
+    # uint32 + 13 int32 + 4 float = 72 bytes, then the int64: 80
     assert ctypes.sizeof(G.gdr_desc_t) == 80
     assert ctypes.sizeof(G.gdr_inputs_t) == 10 * 8
 
@@ -96,6 +96,21 @@ def test_bad_descriptor(field, value, status):
     d = desc()
     setattr(d, field, value)
     check(status, d=d)
+
+
+@pytest.mark.parametrize("N,S,status", [(-1, 1, G.GDR_EINVAL), (3, -1, G.GDR_EINVAL),
+                                        (3, 65, G.GDR_ENOTSUP), (3, 8, G.GDR_OK), (-1, 0, G.GDR_OK)])
+def test_residual_steps(N, S, status):
+    check(status, d=desc(neumann_order=N, residual_steps=S))
+
+
+def test_residual_correction_is_generic_only():
+    d = desc(Dk=128, Dv=128, neumann_order=3, residual_steps=8)
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
+    d.impl = G.GDR_IMPL_MFMA
+    assert G.gdr_chunk_fwd_impl(d) == -1
+    d.residual_steps = 0
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_MFMA
 
 
 def test_huge_problem_rejected():

@@ -74,6 +74,37 @@ def test_band_fp32_matches_literal_neumann(N):
     assert O.rel_l2(host(S), S_ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("N,S", [(3, 8), (0, 3), (1, 5), (3, 15)])
+def test_residual_fp32_matches_oracle(N, S):
+    """Band-N start corrected by S residual steps (T0 sum_{s<=S} E^s) vs the oracle's literal
+    steps; (0, 3) and (1, 5) differ from the exact inverse by 1.5e-2 and 5e-4 on this data, so
+    the check separates them from it.  Exact once (S + 1)(N + 1) >= C: (3, 15)."""
+    s = gs.spec("plain")
+    announce(f"plain f32 residual N={N} S={S}")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=("residual", N, S))
+    o, St, _ = run_chunk(s, x, neumann_order=N, residual_steps=S)
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(St), S_ref) <= TOL_F32
+    if (S + 1) * (N + 1) >= 64:
+        o_ex, S_ex, _ = O.recurrent(x)
+        assert O.rel_l2(host(o), o_ex) <= TOL_F32 and O.rel_l2(host(St), S_ex) <= TOL_F32
+
+
+@pytest.mark.parametrize("variant,dtype,chunk", [("pdn", "f32", 64), ("gdn", "f32", 32), ("gdn2_decay", "f32", 16),
+                                                 ("pdn", "bf16", 64), ("gdn", "bf16", 64)])
+def test_residual_variants(variant, dtype, chunk):
+    """The residual correction in every gain / decay / write-key combination and chunk size
+    (generic kernel; the auto dispatch picks it for a residual descriptor)."""
+    s = small(variant, dtype, chunk=chunk, Dk=64 if dtype == "f32" else 128, Dv=48 if dtype == "f32" else 128)
+    announce(f"residual N=2 S=4 {variant} {dtype} C{chunk} {s}")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.chunked(x, chunk=chunk, t_mode=("residual", 2, 4), precond=precond_opts(s))
+    o, St, _ = run_chunk(s, x, neumann_order=2, residual_steps=4)
+    assert O.rel_l2(host(o), o_ref) <= tol(s)
+    assert O.rel_l2(host(St), S_ref) <= tol(s)
+
+
 @pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay"])
 @pytest.mark.parametrize("chunk,Dk,Dv,T", [(64, 64, 48, 150), (16, 32, 16, 37), (32, 128, 128, 200),
                                            (64, 128, 20, 64)])
@@ -250,6 +281,23 @@ def test_precond_band3_vs_exact():
     gpu_gap = O.rel_l2(host(ob), host(oe))
     print(f"  rel-L2(exact, band3) on the GPU, whole output: {gpu_gap:.3e}", flush=True)
     assert gpu_gap > 1e-2   # the band approximation is far from exact on this data
+
+
+@pytest.mark.timeout(300)
+def test_precond_residual_full_size():
+    """Preconditioned workload at full size with the band-3 start and 8 residual steps (the
+    page's defaults) vs the oracle's residual steps on sampled streams; the distance to the
+    exact path is reported."""
+    s = gs.spec("pdn")
+    announce(f"pdn band3 + residual 8 {s}")
+    x = gs.make_inputs(s)
+    o, St, _ = run_chunk(s, x, neumann_order=3, residual_steps=8)
+    streams = [(0, 0), (3, 15)]
+    for eo, eS in _sampled(s, x, o, St, streams, precond=precond_opts(s), t_mode=("residual", 3, 8)):
+        print(f"  residual vs oracle residual: out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+    for eo, eS in _sampled(s, x, o, St, streams, precond=precond_opts(s)):
+        print(f"  residual vs exact oracle: out {eo:.3e} state {eS:.3e}", flush=True)
 
 
 @pytest.mark.timeout(600)
