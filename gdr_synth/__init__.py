@@ -16,6 +16,8 @@ Preconditioned DeltaNet, technical summary section 2; Gated DeltaNet-2 news item
 * ``pdn``    - diagonal-preconditioned write key, B4 H16 T4096 d128, bf16, C64.
 * ``long``   - scalar-gated, B1 H32 T32768 d128, bf16, C64, then decode steps at
                batch 64 (step ``s`` drawn from seed ``5001 + s``).
+* ``kda``    - one decay per key channel (the diagonal gate of Kimi Delta Attention),
+               otherwise as ``gdn``: B4 H16 T4096 d128, bf16, C64.
 
 Recipe (one generator per call, ``numpy.random.Generator(PCG64(seed))``, draws in
 the order q, k, v, then the gate logits):
@@ -24,6 +26,7 @@ the order q, k, v, then the gate logits):
 * v ~ N(0, 1);
 * beta = sigmoid(N(0, 1))                      [B, T, H]     (scalar gain);
 * log_alpha = -0.1 * softplus(N(0, 1))         [B, T, H]     (scalar decay);
+* log_alpha = -0.1 * softplus(N(0, 1))         [B, T, H, Dk] (per-channel decay);
 * erase = sigmoid(N(2, 1))                     [B, T, H, Dk] (channel gain, key axis);
 * write = sigmoid(N(0, 1))                     [B, T, H, Dv] (channel gain, value axis).
 
@@ -58,7 +61,7 @@ class Spec:
     chunk: int = 64
     dtype: str = "bf16"          # storage dtype of q, k, v, o (and erase/write gates)
     gain: str = "scalar"         # "scalar" (beta) | "channel" (erase, write)
-    decay: str = "none"          # "none" | "scalar" (log_alpha)
+    decay: str = "none"          # "none" | "scalar" (log_alpha [B,T,H]) | "channel" ([B,T,H,Dk])
     wkey: str = "same"           # "same" | "precond" | "explicit"
     seed: int = 0
     # diagonal preconditioner constants (used when wkey == "precond")
@@ -85,6 +88,8 @@ WORKLOADS: Dict[str, Spec] = {
     "long": Spec("long", B=1, H=32, T=32768, Dk=128, Dv=128, dtype="bf16",
                  gain="scalar", decay="scalar", seed=5000,
                  decode_batch=64, decode_steps=1024),
+    "kda": Spec("kda", B=4, H=16, T=4096, Dk=128, Dv=128, dtype="bf16",
+                gain="scalar", decay="channel", seed=6000),
 }
 
 
@@ -137,6 +142,8 @@ def _draw(rng: np.random.Generator, s: Spec, lead: tuple) -> Dict[str, np.ndarra
         out["write"] = _store(_sigmoid(rng.standard_normal(lead + (s.Dv,))), s.dtype)
     if s.decay == "scalar":
         out["log_alpha"] = round_to_f32(-0.1 * _softplus(rng.standard_normal(lead)))
+    elif s.decay == "channel":
+        out["log_alpha"] = round_to_f32(-0.1 * _softplus(rng.standard_normal(lead + (s.Dk,))))
     if s.wkey == "explicit":
         out["write_key"] = _store(rng.standard_normal(lead + (s.Dk,)) / np.sqrt(s.Dk), s.dtype)
     return out

@@ -3,10 +3,12 @@
 Notation.  One (batch, head) stream has tokens t = 1..T with query q_t and key k_t
 in R^{Dk} and value v_t in R^{Dv}.  The state S is Dv x Dk and the output is
 o_t = S_t (scale * q_t).  Every supported variant is one rank-1 template with an
-erase (read) key e_t, a write key r_t, a written value v'_t and a scalar decay
-alpha_t = exp(log_alpha_t):
+erase (read) key e_t, a write key r_t, a written value v'_t and a decay: a scalar
+alpha_t = exp(log_alpha_t), or one decay per key channel, a_t = exp(log_alpha_t) in
+R^{Dk} (the diagonal gate S_{t-1} Diag(a_t) of Kimi Delta Attention):
 
     S_t = alpha_t S_{t-1} (I - e_t r_t^T) + v'_t r_t^T
+    S_t = S_{t-1} Diag(a_t) (I - e_t r_t^T) + v'_t r_t^T        (per-channel decay)
 
     variant                         alpha_t   e_t          r_t          v'_t
     delta rule                      1         beta k       k            beta v
@@ -24,7 +26,8 @@ The chunk form and T = (I - A)^-1 follow [MMI "Declaracao do Problema"].  Page
 titles are listed in ``oracle/__init__.py``.
 
 Readings where the pages are silent (each pinned by a test):
-* The decay multiplies the old state only; the write term is not decayed.
+* The decay multiplies the old state only; the write term is not decayed.  A
+  per-channel decay scales the state's key channels (its columns), before the erase.
 * The output reads the state after token t's own update.
 * A carries the minus sign: A = -tril_{-1}((E R^T) (.) Gamma), so T = (I + L)^-1.
 * Channel gates: the erase gate scales the key in the erase term and the write gate
@@ -78,7 +81,8 @@ def variant_vectors(x: Dict[str, np.ndarray], *, precond: Optional[dict] = None
     keys q, k, v and either ``beta`` (scalar gain) or ``erase``/``write`` (channel
     gain); optionally ``log_alpha`` (scalar decay) and ``write_key`` (explicit write
     key).  ``precond`` = dict(rho, eps, h_init, t0) selects the diagonal
-    preconditioner for the write key.
+    preconditioner for the write key.  ``log_alpha`` is [T] (scalar decay) or [T, Dk]
+    (one decay per key channel).
     """
     k = np.asarray(x["k"], dtype=F64)
     v = np.asarray(x["v"], dtype=F64)
@@ -112,6 +116,8 @@ def recurrent_stream(x: Dict[str, np.ndarray], *, scale: float = 1.0,
                      ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
     """One stream, token by token: S <- alpha S; d = v' - S e; S <- S + d r^T; o = S (scale q).
 
+    With a per-channel decay the first step is S <- S Diag(a_t) (column c scaled by a_tc;
+    numpy broadcasts the [Dk] row of decays over the rows of S).
     Returns (o [T, Dv], S_T [Dv, Dk], h_T or None).
     """
     e, r, vp, la, h_final = variant_vectors(x, precond=precond)
@@ -272,6 +278,9 @@ def chunked_stream(x: Dict[str, np.ndarray], *, chunk: int, t_mode="exact",
     Returns (o [T, Dv], S_T, h_T or None).
     """
     e, r, vp, la, h_final = variant_vectors(x, precond=precond)
+    if la.ndim == 2:
+        return _chunked_stream_channel_decay(e, r, vp, la, h_final, x, chunk=chunk, t_mode=t_mode,
+                                             scale=scale, S0=S0)
     q = np.asarray(x["q"], dtype=F64) * scale
     T, Dk = e.shape
     Dv = vp.shape[1]
@@ -294,6 +303,42 @@ def chunked_stream(x: Dict[str, np.ndarray], *, chunk: int, t_mode="exact",
         P = np.where(causal, (Q @ R.T) * Gam, 0.0)
         o[sl] = (np.exp(g)[:, None] * Q) @ S.T + P @ D
         S = np.exp(g[-1]) * S + D.T @ (np.exp(g[-1] - g)[:, None] * R)
+    return o, S, h_final
+
+
+def _chunked_stream_channel_decay(e, r, vp, la, h_final, x, *, chunk, t_mode, scale, S0):
+    """Chunk form with one decay per key channel.  With G the inclusive in-chunk cumulative
+    sum of log a (a [n, Dk] array) the pairwise decay of channel c between tokens j <= i is
+    exp(G_ic - G_jc), so it moves inside the key products:
+        L_ij = sum_c e_ic r_jc exp(G_ic - G_jc)  (j < i),  A = -L,  T = (I - A)^-1
+        D    = T (V' - (e^G (.) E) S_c^T)
+        P_ij = sum_c q_ic r_jc exp(G_ic - G_jc)  (j <= i)
+        O    = (e^G (.) Q) S_c^T + P D
+        S_{c+1} = S_c Diag(e^{G_C}) + D^T (e^{G_C - G} (.) R)
+    (the same derivation as the scalar chunk form: unroll S_t = S_{t-1} Diag(a_t) + d_t r_t^T
+    with d_t = v'_t - S_{t-1} Diag(a_t) e_t over the chunk and collect the d_j terms).
+    """
+    q = np.asarray(x["q"], dtype=F64) * scale
+    T, Dk = e.shape
+    Dv = vp.shape[1]
+    S = np.zeros((Dv, Dk), dtype=F64) if S0 is None else np.array(S0, dtype=F64, copy=True)
+    o = np.empty((T, Dv), dtype=F64)
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, min(c0 + chunk, T))
+        E, R, V, Q = e[sl], r[sl], vp[sl], q[sl]
+        n = E.shape[0]
+        G = np.cumsum(la[sl], axis=0)
+        i, j = np.indices((n, n))
+        causal = j <= i
+        # exp(G_ic - G_jc) where j <= i, else 0 (the exponent is never formed above the diagonal)
+        dG = np.where(causal[:, :, None], G[:, None, :] - G[None, :, :], 0.0)
+        Gam = np.where(causal[:, :, None], np.exp(dG), 0.0)
+        L = np.where(j < i, np.einsum("ic,jc,ijc->ij", E, R, Gam), 0.0)
+        Tm = tri_inverse(-L, t_mode)
+        D = Tm @ (V - (np.exp(G) * E) @ S.T)
+        P = np.where(causal, np.einsum("ic,jc,ijc->ij", Q, R, Gam), 0.0)
+        o[sl] = (np.exp(G) * Q) @ S.T + P @ D
+        S = S * np.exp(G[-1])[None, :] + D.T @ (np.exp(G[-1][None, :] - G) * R)
     return o, S, h_final
 
 

@@ -18,13 +18,15 @@ import oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
 
-VARIANTS = ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay"]
+VARIANTS = ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay", "kda", "kda_gdn2"]
 
 
 def small_inputs(variant, B=1, H=2, T=70, Dk=8, Dv=6, seed=7):
     base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "pdn": "pdn", "explicit": "gdn",
-            "gdn2_decay": "gdn2", "pdn_decay": "pdn"}[variant]
+            "gdn2_decay": "gdn2", "pdn_decay": "pdn", "kda": "kda", "kda_gdn2": "gdn2"}[variant]
     over = dict(B=B, H=H, T=T, Dk=Dk, Dv=Dv, seed=seed, dtype="f32")
+    if variant == "kda_gdn2":
+        over["decay"] = "channel"
     if variant == "explicit":
         over["wkey"] = "explicit"
     if variant.endswith("_decay"):
@@ -49,12 +51,14 @@ def _matmul(A, B):
 
 
 def _brute(q, k, v, alpha, e, r, vp, S0):
-    """S_t = S_{t-1} M_t + v'_t r_t^T with M_t = alpha_t (I - e_t r_t^T); o_t = S_t q_t."""
+    """S_t = S_{t-1} M_t + v'_t r_t^T with M_t = Diag(a_t) (I - e_t r_t^T); o_t = S_t q_t.
+    ``alpha[t]`` is a scalar (a_t = alpha_t 1) or a list of Dk per-channel decays."""
     Dk = len(k[0])
     S = [row[:] for row in S0]
     outs, Ms = [], []
     for t in range(len(q)):
-        M = [[alpha[t] * ((1 if i == j else 0) - e[t][i] * r[t][j]) for j in range(Dk)] for i in range(Dk)]
+        a = alpha[t] if isinstance(alpha[t], list) else [alpha[t]] * Dk
+        M = [[a[i] * ((1 if i == j else 0) - e[t][i] * r[t][j]) for j in range(Dk)] for i in range(Dk)]
         Ms.append(M)
         S = _matmul(S, M)
         S = [[S[a][j] + vp[t][a] * r[t][j] for j in range(Dk)] for a in range(len(S))]
@@ -66,7 +70,7 @@ def _rat(rng, shape, den=8):
     return [[Fraction(int(rng.integers(-den, den + 1)), den) for _ in range(shape[1])] for _ in range(shape[0])]
 
 
-@pytest.mark.parametrize("variant", ["plain", "gated", "channel", "precond", "explicit"])
+@pytest.mark.parametrize("variant", ["plain", "gated", "channel", "precond", "explicit", "diag"])
 def test_brute_force_exact_rationals(variant):
     rng = np.random.default_rng(99 + len(variant))
     T, Dk, Dv = 6, 3, 2
@@ -75,6 +79,8 @@ def test_brute_force_exact_rationals(variant):
     alpha = [Fraction(1)] * T
     if variant == "gated":
         alpha = [Fraction(int(rng.integers(4, 9)), 8) for _ in range(T)]
+    if variant == "diag":   # one decay per key channel
+        alpha = [[Fraction(int(rng.integers(2, 9)), 8) for _ in range(Dk)] for _ in range(T)]
     S0 = _rat(rng, (Dv, Dk), den=4)
     x = {"q": np.array(q, float), "k": np.array(k, float), "v": np.array(v, float)}
     precond = None
@@ -104,6 +110,8 @@ def test_brute_force_exact_rationals(variant):
             x["write_key"] = np.array(r, float)
     if variant == "gated":
         x["log_alpha"] = np.log(np.array([float(a) for a in alpha]))
+    if variant == "diag":
+        x["log_alpha"] = np.log(np.array([[float(a) for a in row] for row in alpha]))
     outs, S_T, Ms = _brute(q, k, v, alpha, e, r, vp, S0)
 
     # the unrolled sum: S_T = S_0 prod_t M_t + sum_t v'_t r_t^T prod_{s>t} M_s
@@ -167,6 +175,34 @@ def test_zero_gain_is_pure_decay(form):
     g = np.cumsum(x["log_alpha"])
     np.testing.assert_allclose(S, np.exp(g[-1]) * S0, rtol=1e-13)
     np.testing.assert_allclose(o, np.exp(g)[:, None] * (x["q"] @ S0.T), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_equal_channel_decays_are_the_scalar_decay(form):
+    """A per-channel decay with every channel equal to log alpha_t is the scalar-gated rule."""
+    s, x, _ = small_inputs("gdn", T=45)
+    xc = dict(x, log_alpha=np.repeat(x["log_alpha"][..., None], s.Dk, axis=-1))
+    S0 = RNG.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.3
+    f = O.recurrent if form == "recurrent" else (lambda x, **kw: O.chunked(x, chunk=16, **kw))
+    o1, S1, _ = f(x, state0=S0)
+    o2, S2, _ = f(xc, state0=S0)
+    assert O.rel_l2(o2, o1) < 1e-13 and O.rel_l2(S2, S1) < 1e-13
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_zero_gain_is_pure_channel_decay(form):
+    """beta = 0 with per-channel decays: S_t = S_0 Diag(exp(G_t)) and o_t = S_0 (exp(G_t) (.) q_t),
+    G the cumulative log decay of each channel."""
+    T, Dk, Dv = 29, 6, 5
+    x = {"q": RNG.standard_normal((T, Dk)), "k": RNG.standard_normal((T, Dk)),
+         "v": RNG.standard_normal((T, Dv)), "beta": np.zeros(T),
+         "log_alpha": -0.3 * RNG.random((T, Dk))}
+    S0 = RNG.standard_normal((Dv, Dk))
+    fn = O.recurrent_stream if form == "recurrent" else (lambda x, **kw: O.chunked_stream(x, chunk=8, **kw))
+    o, S, _ = fn(x, S0=S0)
+    G = np.cumsum(x["log_alpha"], axis=0)
+    np.testing.assert_allclose(S, S0 * np.exp(G[-1])[None, :], rtol=1e-13)
+    np.testing.assert_allclose(o, (np.exp(G) * x["q"]) @ S0.T, rtol=1e-12, atol=1e-14)
 
 
 def test_orthonormal_keys_exact_retrieval():
@@ -376,7 +412,7 @@ def test_exact_preconditioner_is_ridge_regression(form):
 # State I/O: decode steps and resumption.
 # ----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2", "pdn"])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "pdn", "kda"])
 def test_decode_steps_equal_recurrence(variant):
     s, x, pc = small_inputs(variant, B=2, H=2, T=9)
     o_ref, S_ref, h_ref = O.recurrent(x, precond=pc)
@@ -392,7 +428,7 @@ def test_decode_steps_equal_recurrence(variant):
     np.testing.assert_allclose(S, S_ref, atol=1e-13)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "pdn"])
+@pytest.mark.parametrize("variant", ["gdn", "pdn", "kda"])
 def test_split_sequence_resume(variant):
     s, x, pc = small_inputs(variant, T=100)
     o, S, h = O.chunked(x, chunk=16, precond=pc)
