@@ -5,7 +5,7 @@ One step = one gdr_chunk_fwd call over one batch of synthetic input (every stage
 chunked forward runs inside it).  Default workload: scalar-gated delta rule, B4 H16 T4096
 Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain|kda|decode]
                     [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
 
 Counter helpers (used to produce the committed traffic summaries under profiles/):
@@ -43,7 +43,7 @@ def alg_bytes(s) -> int:
     esz = 2 if s.dtype == "bf16" else 4
     per_tok = (2 * s.Dk + 2 * s.Dv) * esz
     per_tok += 4 if s.gain == "scalar" else (s.Dk + s.Dv) * esz
-    per_tok += 4 if s.decay == "scalar" else 0
+    per_tok += {"scalar": 4, "channel": 4 * s.Dk}.get(s.decay, 0)
     per_tok += s.Dk * esz if s.wkey == "explicit" else 0
     per_head = s.Dv * s.Dk * 4 + (s.Dk * 4 if s.wkey == "precond" else 0)
     return s.B * s.T * s.H * per_tok + s.B * s.H * per_head
@@ -298,7 +298,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "gdn2", "pdn", "long", "plain", "decode"])
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "gdn2", "pdn", "long", "plain", "kda", "decode"])
     ap.add_argument("--neumann", type=int, default=-1)
     ap.add_argument("--residual", type=int, default=0,
                     help="residual-correction steps on the band-N start (needs --neumann N)")
@@ -372,7 +372,7 @@ def main():
         B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
         io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
         gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
-        decay=G.GDR_DECAY_SCALAR if s.decay == "scalar" else G.GDR_DECAY_NONE,
+        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
         wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=args.neumann,
         residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
     impl_name = {G.GDR_IMPL_MFMA: "mfma", G.GDR_IMPL_GENERIC: "generic"}.get(impl_code, "?")

@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     GDR_OK, GDR_EINVAL, GDR_ENOTSUP, GDR_EHIP,
     GDR_F32, GDR_BF16,
     GDR_GAIN_SCALAR, GDR_GAIN_CHANNEL,
-    GDR_DECAY_NONE, GDR_DECAY_SCALAR,
+    GDR_DECAY_NONE, GDR_DECAY_SCALAR, GDR_DECAY_CHANNEL,
     GDR_WKEY_SAME, GDR_WKEY_DIAG_PRECOND, GDR_WKEY_EXPLICIT,
     GDR_IMPL_AUTO, GDR_IMPL_GENERIC, GDR_IMPL_MFMA,
     GdrError, gdr_desc_t, gdr_inputs_t,

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 GDR_OK, GDR_EINVAL, GDR_ENOTSUP, GDR_EHIP = 0, 1, 2, 3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GAIN_SCALAR, GDR_GAIN_CHANNEL = 0, 1
-GDR_DECAY_NONE, GDR_DECAY_SCALAR = 0, 1
+GDR_DECAY_NONE, GDR_DECAY_SCALAR, GDR_DECAY_CHANNEL = 0, 1, 2
 GDR_WKEY_SAME, GDR_WKEY_DIAG_PRECOND, GDR_WKEY_EXPLICIT = 0, 1, 2
 GDR_IMPL_AUTO, GDR_IMPL_GENERIC, GDR_IMPL_MFMA = 0, 1, 2
 _IMPL = {"auto": GDR_IMPL_AUTO, "generic": GDR_IMPL_GENERIC, "mfma": GDR_IMPL_MFMA}
@@ -175,7 +175,8 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
     """Chunked forward on torch tensors (q, k, v [B, T, H, D]).  Returns (out, state_out, pc_h_out).
 
     Gains: ``beta`` [B, T, H] fp32, or ``erase`` [B, T, H, Dk] and ``write`` [B, T, H, Dv].
-    Decay: ``log_alpha`` [B, T, H] fp32 or None.  Write key: ``write_key`` [B, T, H, Dk],
+    Decay: ``log_alpha`` [B, T, H] fp32 (one per token), [B, T, H, Dk] fp32 (one per key
+    channel) or None.  Write key: ``write_key`` [B, T, H, Dk],
     or ``precond=True`` for the diagonal preconditioner (accumulator ``pc_h_in`` [B, H, Dk]
     fp32 or None for ``pc_h0``).  T: exact (``neumann_order`` < 0), the band N
     (``neumann_order`` = N), or that band corrected by ``residual_steps`` residual steps.
@@ -192,7 +193,8 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
     _check("k", k, (B, T, H, Dk), io, dev)
     _check("v", v, (B, T, H, Dv), io, dev)
     _check("beta", beta, (B, T, H), f32, dev)
-    _check("log_alpha", log_alpha, (B, T, H), f32, dev)
+    chd = log_alpha is not None and log_alpha.dim() == 4
+    _check("log_alpha", log_alpha, (B, T, H, Dk) if chd else (B, T, H), f32, dev)
     _check("erase", erase, (B, T, H, Dk), io, dev)
     _check("write", write, (B, T, H, Dv), io, dev)
     _check("write_key", write_key, (B, T, H, Dk), io, dev)
@@ -210,7 +212,8 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
         _check("pc_h_out", pc_h_out, (B, H, Dk), f32, dev)
     desc = make_desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, io_dtype=_io_code(io),
                      gain=GDR_GAIN_CHANNEL if erase is not None else GDR_GAIN_SCALAR,
-                     decay=GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE,
+                     decay=(GDR_DECAY_CHANNEL if chd else
+                            GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE),
                      wkey=(GDR_WKEY_DIAG_PRECOND if precond else
                            GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME),
                      neumann_order=neumann_order, residual_steps=residual_steps,
@@ -242,7 +245,8 @@ def gdr_recurrent_step(q, k, v, state, *, beta=None, log_alpha=None, erase=None,
     _check("k", k, (B, H, Dk), io, dev)
     _check("v", v, (B, H, Dv), io, dev)
     _check("beta", beta, (B, H), f32, dev)
-    _check("log_alpha", log_alpha, (B, H), f32, dev)
+    chd = log_alpha is not None and log_alpha.dim() == 3
+    _check("log_alpha", log_alpha, (B, H, Dk) if chd else (B, H), f32, dev)
     _check("erase", erase, (B, H, Dk), io, dev)
     _check("write", write, (B, H, Dv), io, dev)
     _check("write_key", write_key, (B, H, Dk), io, dev)
@@ -257,7 +261,8 @@ def gdr_recurrent_step(q, k, v, state, *, beta=None, log_alpha=None, erase=None,
         _check("pc_h_out", pc_h_out, (B, H, Dk), f32, dev)
     desc = make_desc(B=B, T=1, H=H, Dk=Dk, Dv=Dv, chunk=64, io_dtype=_io_code(io),
                      gain=GDR_GAIN_CHANNEL if erase is not None else GDR_GAIN_SCALAR,
-                     decay=GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE,
+                     decay=(GDR_DECAY_CHANNEL if chd else
+                            GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE),
                      wkey=(GDR_WKEY_DIAG_PRECOND if precond else
                            GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME),
                      scale=scale, pc_rho=pc_rho, pc_eps=pc_eps, pc_h0=pc_h0, pc_t0=pc_t0)

@@ -28,6 +28,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBV = 16;     // state rows per workgroup
 constexpr int kCMax = 64;   // largest chunk
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
@@ -38,8 +39,13 @@ __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &
   acc = fmaf(x.w, y.w, acc);
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHD>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
+  // CHD: one decay per key channel (log_alpha [B, T, H, Dk]).  The pairwise decay of channel
+  // c between tokens j <= i is 2^(G_ic - G_jc) with G the in-chunk cumulative log2 decay, so it
+  // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise), the
+  // state is read through e^G (.) e and e^G (.) q, and the update uses e^{G_C - G} (.) r and
+  // S Diag(e^{G_C}).  Every exponent that is kept is <= 0.
   // fp32 row stride of the [token][channel] tiles: 16-byte aligned rows whose starts fall on
   // distinct 16-byte bank groups for 16 consecutive rows (conflict-free 16-byte reads)
   constexpr int LD = DK + 4;
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   __shared__ float LP[kCMax][kCMax + 1];            // L (strict lower), then P (lower)
   __shared__ __align__(16) float Tm[kCMax][kCMax + 4];   // T, row-major
   __shared__ __align__(16) float Zs[32][32 + 4];         // block products in flight
-  __shared__ __align__(16) float Zb[kCMax][kCMax + 4];   // residual-correction series
+  __shared__ __align__(16) float Zb[CHD ? 1 : kCMax][kCMax + 4];   // residual-correction series
+  __shared__ __align__(16) float Gs[CHD ? kCMax : 1][CHD ? LD : 4];  // cumulative log2 decays
   __shared__ __align__(16) float Ss[kBV][LD];       // state tile
   __shared__ __align__(16) float Xv[kCMax][kBV];    // X
   __shared__ __align__(16) float Dl[kCMax][kBV];    // D
@@ -95,7 +102,9 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
     // Element (t, c) of a [B, T, H, Dk] tensor sits t * H * Dk + c after the chunk's first
     // token row (a 32-bit offset: 64 H Dk < 2^31).  stage() copies rows 0..n-1 of such a tile
-    // into dst (zero beyond n and Dk); every load of the tile is issued before the first store.
+    // into dst (zero beyond n and Dk).  Every load reads a valid element (indices clamped into
+    // the tile) and the mask is applied afterwards, so the loads carry no branch and all of a
+    // tile's loads are in flight together.
     const long long row0 = tok(0);
     const int rstride = H * Dk;
     auto stage = [&](float(*dst)[LD], auto &&load) {
@@ -103,7 +112,13 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
 #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
         const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        x[it] = (t < n && c < Dk) ? load(t, t * rstride + c) : 0.f;
+        const int tc = min(t, n - 1), cc = min(c, Dk - 1);
+        x[it] = load(tc, tc * rstride + cc);
+      }
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        if (!(t < n && c < Dk)) x[it] = 0.f;
       }
 #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
@@ -116,32 +131,62 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     auto gram = [&](bool incl_diag) {
       if (bj > bi) return;
       float acc[4][4] = {};
-#pragma unroll 4
-      for (int c = 0; c < DK; c += 4) {
-        float4 x[4], r[4];
+      if constexpr (CHD) {
+#pragma unroll 2
+        for (int c = 0; c < DK; c += 4) {
+          float4 x[4], r[4], gi[4], gj[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[u] = ld4(&Xs[4 * bi + u][c]);
-          r[u] = ld4(&Rs[4 * bj + u][c]);
+          for (int u = 0; u < 4; ++u) {
+            x[u] = ld4(&Xs[4 * bi + u][c]);
+            r[u] = ld4(&Rs[4 * bj + u][c]);
+            gi[u] = ld4(&Gs[4 * bi + u][c]);
+            gj[u] = ld4(&Gs[4 * bj + u][c]);
+          }
+          // (entries above the diagonal may overflow here; they are discarded below)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const float4 d = make_float4(x[u].x * exp2f(gi[u].x - gj[w].x), x[u].y * exp2f(gi[u].y - gj[w].y),
+                                           x[u].z * exp2f(gi[u].z - gj[w].z), x[u].w * exp2f(gi[u].w - gj[w].w));
+              fma4(acc[u][w], d, r[w]);
+            }
         }
+      } else {
+#pragma unroll 4
+        for (int c = 0; c < DK; c += 4) {
+          float4 x[4], r[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 4; ++u) {
+            x[u] = ld4(&Xs[4 * bi + u][c]);
+            r[u] = ld4(&Rs[4 * bj + u][c]);
+          }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) fma4(acc[u][w], x[u], r[w]);
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) fma4(acc[u][w], x[u], r[w]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int i = 4 * bi + u, j = 4 * bj + w;
-          LP[i][j] = (j < i || (incl_diag && j == i)) ? expf(gs[i] - gs[j]) * acc[u][w] : 0.f;
+          const float dec = CHD ? 1.f : expf(gs[i] - gs[j]);
+          LP[i][j] = (j < i || (incl_diag && j == i)) ? dec * acc[u][w] : 0.f;
         }
     };
     // (Xs_t . Ss_r) for the thread's 2 x 2 block of tokens t0.. and state rows r0..
+    // (with per-channel decays: the rows are read as 2^G (.) x)
     auto dot_state = [&](float (&acc)[2][2]) {
 #pragma unroll 4
       for (int c = 0; c < DK; c += 4) {
-        const float4 x0 = ld4(&Xs[t0][c]), x1 = ld4(&Xs[t0 + 1][c]);
+        float4 x0 = ld4(&Xs[t0][c]), x1 = ld4(&Xs[t0 + 1][c]);
+        if constexpr (CHD) {
+          const float4 g0 = ld4(&Gs[t0][c]), g1 = ld4(&Gs[t0 + 1][c]);
+          x0 = make_float4(x0.x * exp2f(g0.x), x0.y * exp2f(g0.y), x0.z * exp2f(g0.z), x0.w * exp2f(g0.w));
+          x1 = make_float4(x1.x * exp2f(g1.x), x1.y * exp2f(g1.y), x1.z * exp2f(g1.z), x1.w * exp2f(g1.w));
+        }
         const float4 s0 = ld4(&Ss[r0][c]), s1 = ld4(&Ss[r0 + 1][c]);
         fma4(acc[0][0], x0, s0);
         fma4(acc[0][1], x0, s1);
@@ -165,6 +210,24 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       const IO *ec = er + row0 * Dk;
       stage(Xs, [&](int, int o) { return ld_f(ec, o) * ld_f(kc, o); });
     }
+    if constexpr (CHD) {
+      // per-channel decays: stage, then each channel's inclusive cumulative sum in log2 units
+      // (rows past n are zero, so the sums stay flat there)
+      const float *lac = a.log_alpha + row0 * Dk;
+      stage(Gs, [&](int, int o) { return lac[o]; });
+      __syncthreads();
+      if (tid < DK) {
+        float gv[kCMax];
+#pragma unroll
+        for (int t = 0; t < kCMax; ++t) gv[t] = Gs[t][tid];
+        float g = 0.f;
+#pragma unroll
+        for (int t = 0; t < kCMax; ++t) {
+          g = fmaf(gv[t], kLog2e, g);
+          Gs[t][tid] = g;
+        }
+      }
+    }
     // gates: inclusive cumulative sum of log alpha over the chunk (one wave)
     if (tid < kCMax) {
       float g = (a.decay == GDR_DECAY_SCALAR && tid < n) ? a.log_alpha[tok(tid)] : 0.f;
@@ -179,15 +242,25 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       wd[tid] = expf(glast - g);
     }
     if (a.wkey == GDR_WKEY_DIAG_PRECOND) {
+      // u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2.  The bias corrections of the
+      // chunk's tokens first (one thread each), then channel `tid` walks the chunk: its keys
+      // are read up front, so only the accumulator chain is serial.
+      float *icorr = &Zs[0][0];   // (free until the inverse is built)
+      if (tid < kCMax) {
+        const float tg = static_cast<float>(a.t0 + c0 + tid + 1);
+        icorr[tid] = 1.f / -expm1f(tg * a.log_rho);   // 1 / (1 - rho^t)
+      }
       __syncthreads();
-      // u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2: channel `tid` walks the chunk
       if (tid < Dk) {
-        for (int t = 0; t < n; ++t) {
-          const float kk = Rs[t][tid];
-          hreg = fmaf(a.rho, hreg, kk * kk);
-          const float tg = static_cast<float>(a.t0 + c0 + t + 1);
-          const float corr = -expm1f(tg * a.log_rho);  // 1 - rho^t
-          Rs[t][tid] = kk / (hreg / corr + a.eps);
+        // rows past n hold zero keys (their u comes out zero); the accumulator skips them
+        float kv[kCMax];
+#pragma unroll
+        for (int t = 0; t < kCMax; ++t) kv[t] = Rs[t][tid];
+#pragma unroll
+        for (int t = 0; t < kCMax; ++t) {
+          const float hn = fmaf(a.rho, hreg, kv[t] * kv[t]);
+          hreg = t < n ? hn : hreg;
+          Rs[t][tid] = kv[t] / fmaf(hreg, icorr[t], a.eps);
         }
       }
     }
@@ -196,18 +269,15 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     gram(false);
     // X = V' - (e^g (.) E) S^T on the value tile
     {
-      float vp[2][2];
+      float vp[2][2];   // (loads from clamped indices; entries outside the tile are masked below)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          vp[u][w] = 0.f;
-          if (t < n && r < nv) {
-            const long long vi = tok(t) * Dv + v0 + r;
-            const float vv = ld_f(v, vi);
-            vp[u][w] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
-          }
+          const int t = min(t0 + u, n - 1), r = min(r0 + w, nv - 1);
+          const long long vi = tok(t) * Dv + v0 + r;
+          const float vv = ld_f(v, vi);
+          vp[u][w] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
         }
       float acc[2][2] = {};
       dot_state(acc);
@@ -336,22 +406,35 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     // each product sums over l < i (l <= i for T0 Z).  Thread: row i, columns jg .. jg + 15;
     // every product is formed in registers and written back after a barrier (E over L, Z
     // in place, T over T0).
-    if (a.S > 0) {
+    if (CHD ? false : a.S > 0) {
       const int i = tid >> 2, jg = (tid & 3) * 16;
+      // the rows of wave w are 16 w .. 16 w + 15, so every sum below ends before l = 16 (w + 1):
+      // a wave-uniform bound; the coefficients past the row's own bound are masked to zero
+      const int lwave = 16 * ((tid >> 6) + 1);
       float acc[16];
-      auto row_product = [&](const float(*Lm)[kCMax + 1], const float(*Tr)[kCMax + 4], int lend, bool neg) {
+      // acc = sum_{l < lend} (+-Lm[i][l]) Tr[l][jg ..], four rows of Tr per batch of reads
+      auto row_product = [&](const auto *Lm, const float(*Tr)[kCMax + 4], int lend, bool neg) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-        for (int l = 0; l < lend; ++l) {
-          const float x = neg ? -Lm[i][l] : Lm[i][l];
+        for (int l0 = 0; l0 < lwave; l0 += 4) {
+          float x[4];
+          float4 t[4][4];
 #pragma unroll
-          for (int u = 0; u < 16; u += 4) {
-            const float4 t = ld4(&Tr[l][jg + u]);
-            acc[u] = fmaf(x, t.x, acc[u]);
-            acc[u + 1] = fmaf(x, t.y, acc[u + 1]);
-            acc[u + 2] = fmaf(x, t.z, acc[u + 2]);
-            acc[u + 3] = fmaf(x, t.w, acc[u + 3]);
+          for (int q = 0; q < 4; ++q) {
+            const float m = Lm[i][l0 + q];
+            x[q] = l0 + q < lend ? (neg ? -m : m) : 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[q][u] = ld4(&Tr[l0 + q][jg + 4 * u]);
           }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              acc[4 * u] = fmaf(x[q], t[q][u].x, acc[4 * u]);
+              acc[4 * u + 1] = fmaf(x[q], t[q][u].y, acc[4 * u + 1]);
+              acc[4 * u + 2] = fmaf(x[q], t[q][u].z, acc[4 * u + 2]);
+              acc[4 * u + 3] = fmaf(x[q], t[q][u].w, acc[4 * u + 3]);
+            }
         }
       };
       // E_ij = delta_ij - T0_ij + (A T0)_ij, A = -L
@@ -374,21 +457,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         __syncthreads();
       }
       // T = T0 Z (T0 is lower triangular: l <= i)
-      {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-        for (int l = 0; l <= i; ++l) {
-          const float x = Tm[i][l];
-#pragma unroll
-          for (int u = 0; u < 16; u += 4) {
-            const float4 z = ld4(&Zb[l][jg + u]);
-            acc[u] = fmaf(x, z.x, acc[u]);
-            acc[u + 1] = fmaf(x, z.y, acc[u + 1]);
-            acc[u + 2] = fmaf(x, z.z, acc[u + 2]);
-            acc[u + 3] = fmaf(x, z.w, acc[u + 3]);
-          }
-        }
-      }
+      row_product(Tm, Zb, i + 1, false);
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 16; u += 4)
@@ -434,10 +503,12 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     {
       float acc[2][2] = {};
       dot_state(acc);
+      if constexpr (!CHD) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        acc[u][0] *= eg[t0 + u];
-        acc[u][1] *= eg[t0 + u];
+        for (int u = 0; u < 2; ++u) {
+          acc[u][0] *= eg[t0 + u];
+          acc[u][1] *= eg[t0 + u];
+        }
       }
       for (int j = 0; j <= t0; ++j) {
         const float2 d = ld2(&Dl[j][r0]);
@@ -461,9 +532,17 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
           if (t < n && r < nv) st_f(out, tok(t) * Dv + v0 + r, a.scale * acc[u][w]);
         }
     }
+    if constexpr (CHD) {   // R <- 2^(G_C - G) (.) R for the update (P, its last other use, is done)
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        Rs[t][c] *= exp2f(Gs[n - 1][c] - Gs[t][c]);
+      }
+    }
     __syncthreads();
     // S <- e^{g_n} S + D^T (e^{g_n - g} (.) R): thread (row r, columns c..c+3); rows past nv
-    // and columns past Dk stay zero (their D rows and key columns are zero)
+    // and columns past Dk stay zero (their D rows and key columns are zero).  Per-channel
+    // decays: S Diag(2^{G_C}) + D^T R with R already scaled.
     {
       const float gl = eg[n - 1];
       constexpr int NC4 = DK / 4;
@@ -474,6 +553,10 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         const int r = u / NC4, c = (u % NC4) * 4;
         const float4 s = ld4(&Ss[r][c]);
         float4 acc = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        if constexpr (CHD) {
+          const float4 gc = ld4(&Gs[n - 1][c]);
+          acc = make_float4(exp2f(gc.x) * s.x, exp2f(gc.y) * s.y, exp2f(gc.z) * s.z, exp2f(gc.w) * s.w);
+        }
         for (int j = 0; j < n; ++j) {
           const float w = Dl[j][r] * wd[j];
           const float4 rr = ld4(&Rs[j][c]);
@@ -497,16 +580,21 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     a.pc_h_out[sh * Dk + tid] = hreg;
 }
 
-template <typename IO>
-hipError_t launch_io(const ChunkArgs &a, hipStream_t s) {
+template <typename IO, bool CHD>
+hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
   const dim3 grid((a.Dv + kBV - 1) / kBV, a.H, a.B);
   if (a.Dk <= 32)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32, CHD>), grid, dim3(kThreads), 0, s, a);
   else if (a.Dk <= 64)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64, CHD>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128, CHD>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const ChunkArgs &a, hipStream_t s) {
+  return a.decay == GDR_DECAY_CHANNEL ? launch_dk<IO, true>(a, s) : launch_dk<IO, false>(a, s);
 }
 
 }  // namespace

@@ -834,6 +834,7 @@ bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const floa
   if (d.io_dtype != GDR_BF16 || d.Dk != kD || d.Dv != kD || d.chunk != kC) return false;
   if (d.gain == GDR_GAIN_CHANNEL && d.wkey != GDR_WKEY_SAME) return false;
   if (d.neumann_order >= 0 && d.residual_steps > 0) return false;
+  if (d.decay == GDR_DECAY_CHANNEL) return false;
   const void *p16[] = {in.q, in.k, in.v, in.erase, in.write, in.write_key, out, state_in, state_out};
   for (const void *p : p16)
     if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;

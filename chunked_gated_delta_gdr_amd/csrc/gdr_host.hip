@@ -91,7 +91,8 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
   if (d->io_dtype != GDR_F32 && d->io_dtype != GDR_BF16)
     return fail(GDR_EINVAL, "io_dtype = %d", d->io_dtype);
   if (d->gain != GDR_GAIN_SCALAR && d->gain != GDR_GAIN_CHANNEL) return fail(GDR_EINVAL, "gain = %d", d->gain);
-  if (d->decay != GDR_DECAY_NONE && d->decay != GDR_DECAY_SCALAR) return fail(GDR_EINVAL, "decay = %d", d->decay);
+  if (d->decay != GDR_DECAY_NONE && d->decay != GDR_DECAY_SCALAR && d->decay != GDR_DECAY_CHANNEL)
+    return fail(GDR_EINVAL, "decay = %d", d->decay);
   if (d->wkey != GDR_WKEY_SAME && d->wkey != GDR_WKEY_DIAG_PRECOND && d->wkey != GDR_WKEY_EXPLICIT)
     return fail(GDR_EINVAL, "wkey = %d", d->wkey);
   if (d->impl != GDR_IMPL_AUTO && d->impl != GDR_IMPL_GENERIC && d->impl != GDR_IMPL_MFMA)
@@ -101,6 +102,8 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
     if (d->residual_steps < 0) return fail(GDR_EINVAL, "residual_steps = %d must be >= 0", d->residual_steps);
     if (d->residual_steps > 0 && d->neumann_order < 0)
       return fail(GDR_EINVAL, "residual_steps = %d needs a band start (neumann_order >= 0)", d->residual_steps);
+    if (d->residual_steps > 0 && d->decay == GDR_DECAY_CHANNEL)
+      return fail(GDR_ENOTSUP, "residual_steps with decay CHANNEL (no room for both in one workgroup's LDS)");
     if (d->residual_steps > 64)
       return fail(GDR_ENOTSUP, "residual_steps = %d (max 64; E^s vanishes once s (N + 1) >= C)",
                   d->residual_steps);
@@ -124,8 +127,8 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
       return fail(GDR_EINVAL, "gain CHANNEL needs erase and write");
     if (in->beta != nullptr) return fail(GDR_EINVAL, "beta given with gain CHANNEL");
   }
-  if (d->decay == GDR_DECAY_SCALAR) {
-    if (need && in->log_alpha == nullptr) return fail(GDR_EINVAL, "decay SCALAR needs log_alpha");
+  if (d->decay != GDR_DECAY_NONE) {
+    if (need && in->log_alpha == nullptr) return fail(GDR_EINVAL, "decay SCALAR / CHANNEL needs log_alpha");
   } else if (in->log_alpha != nullptr) {
     return fail(GDR_EINVAL, "log_alpha given with decay NONE");
   }
@@ -160,7 +163,8 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
   const Range inputs[] = {
       rng("q", in->q, ntok * Dk * esz), rng("k", in->k, ntok * Dk * esz),
       rng("v", in->v, ntok * Dv * esz), rng("beta", in->beta, ntok * 4),
-      rng("log_alpha", in->log_alpha, ntok * 4), rng("erase", in->erase, ntok * Dk * esz),
+      rng("log_alpha", in->log_alpha, ntok * (d->decay == GDR_DECAY_CHANNEL ? Dk : 1) * 4),
+      rng("erase", in->erase, ntok * Dk * esz),
       rng("write", in->write, ntok * Dv * esz), rng("write_key", in->write_key, ntok * Dk * esz),
       rng("pc_h_in", in->pc_h_in, B * H * Dk * 4)};
   const Range r_sin = rng("state_in", for_step ? nullptr : state_in, B * H * Dv * Dk * 4);

@@ -8,6 +8,9 @@
 //     d_v = v'_v - alpha x_v
 //     o_v = scale (alpha y_v + d_v (r . q))
 //     S_v <- alpha S_v + d_v r
+// With one decay per key channel (S <- S Diag(a)) the decays move into the vectors:
+// x_v = S_v . (a (.) e), y_v = S_v . (a (.) q), d_v = v'_v - x_v, o_v = scale (y_v + d_v (r . q)),
+// S_v <- a (.) S_v + d_v r.
 // so the kernel makes one pass over the state: one read and one write of every entry,
 // which makes it HBM-bound.  One workgroup per (batch, head): its 256 threads cover 16
 // rows at a time, 16 lanes per row, each lane holding DK/16 consecutive-in-float4 columns.
@@ -20,7 +23,8 @@ constexpr int kThreads = 256;
 
 template <typename IO>
 __device__ __forceinline__ void load_vectors(const ChunkArgs &a, long long sh, float *es,
-                                             float *rs, float *qs, float *vps, float *misc) {
+                                             float *rs, float *qs, float *vps, float *as,
+                                             float *misc) {
   const IO *q = static_cast<const IO *>(a.q);
   const IO *k = static_cast<const IO *>(a.k);
   const IO *v = static_cast<const IO *>(a.v);
@@ -45,6 +49,7 @@ __device__ __forceinline__ void load_vectors(const ChunkArgs &a, long long sh, f
       if (a.pc_h_out != nullptr) a.pc_h_out[sh * Dk + c] = hh;  // same thread read it
     }
     rs[c] = r;
+    as[c] = (a.decay == GDR_DECAY_CHANNEL) ? expf(a.log_alpha[sh * Dk + c]) : 1.f;
   }
   for (int c = tid; c < Dv; c += kThreads) {
     const float vv = ld_f(v, sh * Dv + c);
@@ -59,10 +64,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(ChunkArgs a) {
   constexpr int F4 = DK / 64;     // float4 per lane per row
   constexpr int kRowsPerPass = kThreads / 16;
   constexpr int kPasses = 4;      // rows in flight per lane
-  __shared__ float es[DK], rs[DK], qs[DK], vps[512], misc[2];
+  __shared__ float es[DK], rs[DK], qs[DK], as[DK], vps[512], misc[2];
   const int tid = threadIdx.x;
   const long long sh = static_cast<long long>(blockIdx.y) * a.H + blockIdx.x;
-  load_vectors<IO>(a, sh, es, rs, qs, vps, misc);
+  load_vectors<IO>(a, sh, es, rs, qs, vps, as, misc);
   __syncthreads();
   if (tid < 64) {  // r . q by wave 0
     float p = 0.f;
@@ -72,14 +77,22 @@ __global__ __launch_bounds__(kThreads) void step_kernel(ChunkArgs a) {
   }
   __syncthreads();
   const float alpha = misc[0], rq = misc[1];
+  const bool chd = a.decay == GDR_DECAY_CHANNEL;
+  const float xs = chd ? 1.f : alpha;   // scale of x and y (per-channel decays sit in e, q)
   const int lane = tid & 15, grp = tid >> 4;
-  float4 ef[F4], qf[F4], rf[F4];
+  float4 ef[F4], qf[F4], rf[F4], af[F4];
 #pragma unroll
   for (int f = 0; f < F4; ++f) {
     const int c = f * 64 + lane * 4;
     ef[f] = make_float4(es[c], es[c + 1], es[c + 2], es[c + 3]);
     qf[f] = make_float4(qs[c], qs[c + 1], qs[c + 2], qs[c + 3]);
     rf[f] = make_float4(rs[c], rs[c + 1], rs[c + 2], rs[c + 3]);
+    af[f] = make_float4(alpha, alpha, alpha, alpha);
+    if (chd) {
+      af[f] = make_float4(as[c], as[c + 1], as[c + 2], as[c + 3]);
+      ef[f] = make_float4(af[f].x * ef[f].x, af[f].y * ef[f].y, af[f].z * ef[f].z, af[f].w * ef[f].w);
+      qf[f] = make_float4(af[f].x * qf[f].x, af[f].y * qf[f].y, af[f].z * qf[f].z, af[f].w * qf[f].w);
+    }
   }
   float4 *S = reinterpret_cast<float4 *>(a.state_out) + sh * a.Dv * (DK / 4);
   IO *out = static_cast<IO *>(a.out);
@@ -109,15 +122,15 @@ __global__ __launch_bounds__(kThreads) void step_kernel(ChunkArgs a) {
         y += __shfl_xor(y, m, 16);
       }
       if (row < a.Dv) {
-        const float d = vps[row] - alpha * x;
-        if (lane == 0) st_f(out, sh * a.Dv + row, a.scale * fmaf(d, rq, alpha * y));
+        const float d = vps[row] - xs * x;
+        if (lane == 0) st_f(out, sh * a.Dv + row, a.scale * fmaf(d, rq, xs * y));
 #pragma unroll
         for (int f = 0; f < F4; ++f) {
           float4 s = sv[p][f];
-          s.x = fmaf(d, rf[f].x, alpha * s.x);
-          s.y = fmaf(d, rf[f].y, alpha * s.y);
-          s.z = fmaf(d, rf[f].z, alpha * s.z);
-          s.w = fmaf(d, rf[f].w, alpha * s.w);
+          s.x = fmaf(d, rf[f].x, af[f].x * s.x);
+          s.y = fmaf(d, rf[f].y, af[f].y * s.y);
+          s.z = fmaf(d, rf[f].z, af[f].z * s.z);
+          s.w = fmaf(d, rf[f].w, af[f].w * s.w);
           S[row * (DK / 4) + f * 16 + lane] = s;
         }
       }
@@ -128,10 +141,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(ChunkArgs a) {
 // Any Dk <= 128, Dv <= 512, any alignment: one thread per state row.
 template <typename IO>
 __global__ __launch_bounds__(kThreads) void step_kernel_any(ChunkArgs a) {
-  __shared__ float es[128], rs[128], qs[128], vps[512], misc[2];
+  __shared__ float es[128], rs[128], qs[128], as[128], vps[512], misc[2];
   const int tid = threadIdx.x;
   const long long sh = static_cast<long long>(blockIdx.y) * a.H + blockIdx.x;
-  load_vectors<IO>(a, sh, es, rs, qs, vps, misc);
+  load_vectors<IO>(a, sh, es, rs, qs, vps, as, misc);
   __syncthreads();
   if (tid == 0) {
     float p = 0.f;
@@ -140,17 +153,20 @@ __global__ __launch_bounds__(kThreads) void step_kernel_any(ChunkArgs a) {
   }
   __syncthreads();
   const float alpha = misc[0], rq = misc[1];
+  const bool chd = a.decay == GDR_DECAY_CHANNEL;
+  const float xs = chd ? 1.f : alpha;
   IO *out = static_cast<IO *>(a.out);
   for (int row = tid; row < a.Dv; row += kThreads) {
     float *S = a.state_out + (sh * a.Dv + row) * a.Dk;
     float x = 0.f, y = 0.f;
     for (int c = 0; c < a.Dk; ++c) {
-      x = fmaf(S[c], es[c], x);
-      y = fmaf(S[c], qs[c], y);
+      const float ac = chd ? as[c] : 1.f;
+      x = fmaf(S[c], ac * es[c], x);
+      y = fmaf(S[c], ac * qs[c], y);
     }
-    const float d = vps[row] - alpha * x;
-    st_f(out, sh * a.Dv + row, a.scale * fmaf(d, rq, alpha * y));
-    for (int c = 0; c < a.Dk; ++c) S[c] = fmaf(d, rs[c], alpha * S[c]);
+    const float d = vps[row] - xs * x;
+    st_f(out, sh * a.Dv + row, a.scale * fmaf(d, rq, xs * y));
+    for (int c = 0; c < a.Dk; ++c) S[c] = fmaf(d, rs[c], (chd ? as[c] : alpha) * S[c]);
   }
 }
 

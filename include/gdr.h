@@ -67,7 +67,7 @@ typedef enum {
 
 enum { GDR_F32 = 0, GDR_BF16 = 1 };                                     /* io_dtype */
 enum { GDR_GAIN_SCALAR = 0, GDR_GAIN_CHANNEL = 1 };                     /* gain     */
-enum { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1 };                      /* decay    */
+enum { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1, GDR_DECAY_CHANNEL = 2 }; /* decay  */
 enum { GDR_WKEY_SAME = 0, GDR_WKEY_DIAG_PRECOND = 1, GDR_WKEY_EXPLICIT = 2 }; /* wkey */
 enum { GDR_IMPL_AUTO = 0, GDR_IMPL_GENERIC = 1, GDR_IMPL_MFMA = 2 };    /* impl     */
 
@@ -104,7 +104,13 @@ typedef struct gdr_desc {
 typedef struct gdr_inputs {
   const void *q, *k, *v;    /* io_dtype; required                                         */
   const float *beta;        /* [B,T,H] fp32; required iff gain == SCALAR                   */
-  const float *log_alpha;   /* [B,T,H] fp32 (<= 0); required iff decay == SCALAR           */
+  const float *log_alpha;   /* decay SCALAR: [B,T,H] fp32 (<= 0), one decay per token;
+                               decay CHANNEL: [B,T,H,Dk] fp32 (<= 0), one decay per key
+                               channel (S_t = S_{t-1} Diag(a_t) (I - e r^T) + v' r^T, the
+                               diagonal gate named beside Kimi Delta Attention in the
+                               Preconditioned DeltaNet summary); required iff decay != NONE.
+                               The chunked form with CHANNEL runs on the generic kernel and
+                               takes no residual correction                               */
   const void *erase;        /* [B,T,H,Dk] io_dtype; required iff gain == CHANNEL           */
   const void *write;        /* [B,T,H,Dv] io_dtype; required iff gain == CHANNEL           */
   const void *write_key;    /* [B,T,H,Dk] io_dtype; required iff wkey == EXPLICIT          */

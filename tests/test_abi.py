@@ -104,6 +104,18 @@ def test_residual_steps(N, S, status):
     check(status, d=desc(neumann_order=N, residual_steps=S))
 
 
+def test_channel_decay_descriptor():
+    p = ptrs()
+    check(G.GDR_EINVAL, d=desc(decay=G.GDR_DECAY_CHANNEL))                     # no log_alpha
+    check(G.GDR_OK, d=desc(decay=G.GDR_DECAY_CHANNEL), ins=inputs(log_alpha=p[4]))
+    check(G.GDR_EINVAL, d=desc(decay=G.GDR_DECAY_CHANNEL), ins=inputs(log_alpha=p[4]),
+          out=p[4] + 2 * 100 * 3 * 4)   # out inside the [B, T, H, Dk] fp32 gates (not [B, T, H])
+    check(G.GDR_ENOTSUP, d=desc(decay=G.GDR_DECAY_CHANNEL, neumann_order=3, residual_steps=2),
+          ins=inputs(log_alpha=p[4]))
+    d = desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL)
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
+
+
 def test_residual_correction_is_generic_only():
     d = desc(Dk=128, Dv=128, neumann_order=3, residual_steps=8)
     assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC

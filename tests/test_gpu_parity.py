@@ -23,8 +23,11 @@ def tol(s):
 
 def small(variant, dtype="f32", **kw):
     base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "pdn": "pdn", "explicit": "gdn",
-            "gdn2_decay": "gdn2", "pdn_decay": "pdn"}[variant]
+            "gdn2_decay": "gdn2", "pdn_decay": "pdn", "kda": "kda", "kda_gdn2": "gdn2",
+            "kda_pdn": "pdn"}[variant]
     over = dict(B=2, H=3, T=150, Dk=64, Dv=48, dtype=dtype, seed=11)
+    if variant in ("kda_gdn2", "kda_pdn"):
+        over["decay"] = "channel"
     over.update(kw)
     if variant == "explicit":
         over["wkey"] = "explicit"
@@ -105,7 +108,8 @@ def test_residual_variants(variant, dtype, chunk):
     assert O.rel_l2(host(St), S_ref) <= tol(s)
 
 
-@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay"])
+@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "pdn", "explicit", "gdn2_decay", "pdn_decay",
+                                     "kda", "kda_gdn2", "kda_pdn"])
 @pytest.mark.parametrize("chunk,Dk,Dv,T", [(64, 64, 48, 150), (16, 32, 16, 37), (32, 128, 128, 200),
                                            (64, 128, 20, 64)])
 def test_variants_fp32(variant, chunk, Dk, Dv, T):
@@ -223,7 +227,7 @@ def test_nan_stays_in_its_head(dtype):
 # The bf16 path
 # ---------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2", "pdn", "explicit", "plain"])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "pdn", "explicit", "plain", "kda"])
 @pytest.mark.parametrize("impl", ["generic", "auto"])
 def test_variants_bf16_small(variant, impl):
     s = small(variant, "bf16", Dk=128, Dv=128, T=200, B=2, H=2)
@@ -284,6 +288,24 @@ def test_precond_band3_vs_exact():
 
 
 @pytest.mark.timeout(300)
+def test_kda_full_size_and_band():
+    """Per-key-channel decay at the benchmark's shape (B4 H16 T4096 d128 bf16) on sampled
+    streams, exact T and band N = 3 (each against its oracle)."""
+    s = gs.spec("kda")
+    announce(f"kda full size {s}")
+    x = gs.make_inputs(s)
+    o, St, _ = run_chunk(s, x)
+    streams = [(0, 0), (3, 15)]
+    for eo, eS in _sampled(s, x, o, St, streams):
+        print(f"  kda exact vs oracle: out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+    ob, Sb, _ = run_chunk(s, x, neumann_order=3)
+    for eo, eS in _sampled(s, x, ob, Sb, [(1, 3)], t_mode=("neumann", 3)):
+        print(f"  kda band3 vs oracle band3: out {eo:.3e} state {eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+@pytest.mark.timeout(300)
 def test_precond_residual_full_size():
     """Preconditioned workload at full size with the band-3 start and 8 residual steps (the
     page's defaults) vs the oracle's residual steps on sampled streams; the distance to the
@@ -317,7 +339,8 @@ def test_long_prefill_sampled():
 
 @pytest.mark.parametrize("variant,dtype,Dk", [("gdn", "bf16", 128), ("gdn", "f32", 64), ("gdn2", "bf16", 128),
                                               ("pdn", "bf16", 128), ("explicit", "f32", 40),
-                                              ("gdn", "f32", 100)])
+                                              ("gdn", "f32", 100), ("kda", "bf16", 128), ("kda", "f32", 64),
+                                              ("kda", "f32", 100)])
 def test_steps_equal_chunk_fwd_and_oracle(variant, dtype, Dk):
     """n x gdr_recurrent_step == oracle recurrence == gdr_chunk_fwd over the same tokens."""
     import torch
