@@ -39,8 +39,10 @@
 // An accumulator tile is therefore the B-operand layout of its K = 16 rows.  For K = 32
 // products fed from two accumulator tiles the K-slot order is "split": slots 0..3 are
 // rows 4 (l / 16) + r of the first tile, slots 4..7 those of the second, and the A
-// operand is gathered from LDS in the same order.  A product X Y whose factors are both
-// accumulators needs acc(X^T) and acc(Y); transposed copies are computed where needed.
+// operand is gathered from LDS in the same order (against the state the tiles keep their
+// channels in an order that makes this the natural order, see the value waves).  A product
+// X Y whose factors are both accumulators needs acc(X^T) and acc(Y); transposed copies are
+// computed where needed.
 #include <cstdlib>
 #include <type_traits>
 
@@ -142,6 +144,24 @@ __device__ __forceinline__ short4v ident4(int lane) {
   for (int i = 0; i < 4; ++i) r[i] = (4 * (lane >> 4) + i == (lane & 15)) ? static_cast<short>(0x3F80) : static_cast<short>(0);
   return r;
 }
+// One data-parallel-primitive move of a float across lanes (CTRL: the DPP control word; lanes
+// with no source, and rows outside ROW_MASK, read 0)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+// inclusive prefix sum over the 64 lanes of a wave, in registers: shifts by 1, 2, 4, 8 inside
+// each 16-lane row, then the last lane of row 0 (2) added to row 1 (3), then the last lane of
+// row 1 (now the total of rows 0-1) added to rows 2 and 3
+__device__ __forceinline__ float wave_scan_add(float x) {
+  x += dppf<0x111, 0xf>(x);   // row_shr:1
+  x += dppf<0x112, 0xf>(x);   // row_shr:2
+  x += dppf<0x114, 0xf>(x);   // row_shr:4
+  x += dppf<0x118, 0xf>(x);   // row_shr:8
+  x += dppf<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dppf<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
 // keep the scheduler from hoisting the next tile's operand loads above this point
 // (bounds register pressure; the hardware still overlaps the independent work)
 #define GDR_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -151,14 +171,13 @@ __device__ __forceinline__ short4v ident4(int lane) {
 __device__ __forceinline__ short8v opn128(const uint16_t *a, int row, int k0, int l4) {
   return ld8(a + sw128(row, k0 + 8 * l4));
 }
-// split K order (see header): K = k0 + 4 l4 + i and k0 + 16 + 4 l4 + i
-__device__ __forceinline__ short8v ops128(const uint16_t *a, int row, int k0, int l4) {
-  return cat(ld4(a + sw128(row, k0 + 4 * l4)), ld4(a + sw128(row, k0 + 16 + 4 * l4)));
-}
-// split-K operand of M^T from a row-major swizzled [K][128] matrix: rows m0 + l % 16 of M^T,
-// K = k0 + 4 (l / 16) + i and k0 + 16 + 4 (l / 16) + i (transposing reads, see ldtr)
-__device__ __forceinline__ short8v optr128(const uint16_t *a, int m0, int k0, int lane) {
-  const int r = 4 * (lane >> 4) + ((lane & 15) >> 2), c = m0 + 4 * (lane & 3);
+// split-K operand of M^T from a row-major swizzled [K][128] matrix (transposing reads, see
+// ldtr): K = k0 + 4 (l / 16) + i and k0 + 16 + 4 (l / 16) + i; the 16 rows of M^T (columns of
+// M) are those of state tile cb in the state's channel order (see chan()), so lane l gets
+// column chan(16 cb + l % 16): the four lanes of each quad read one 4-column piece
+__device__ __forceinline__ short8v optr_state(const uint16_t *a, int cb, int k0, int lane) {
+  const int r = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int c = 32 * (cb >> 1) + 4 * (cb & 1) + 8 * (lane & 3);
   return cat(ldtr(a + sw128(k0 + r, c)), ldtr(a + sw128(k0 + 16 + r, c)));
 }
 __device__ __forceinline__ short8v opsp(const uint16_t *a, int ld, int row, int k0, int l4) {
@@ -254,14 +273,22 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     auto value_loop = [&](auto wc) {
       constexpr int W = decltype(wc)::value;
       // ---------------- value waves: S^T tiles in accumulators ----------------
-      // tile cb holds S^T[c = 16 cb + 4 l4 + r][v = 16 W + l16]
+      // Tile cb holds S^T[c][v = 16 W + l16] for the channels c = chan(16 cb + 4 l4 + r) =
+      // 32 (cb / 2) + 8 l4 + 4 (cb % 2) + r: with this order the bf16 concatenation of tiles
+      // 2j and 2j + 1 (the K = 32 B operand of Y and O1) covers channels 32 j + 8 l4 .. + 7 in
+      // natural order, so the E / Q / K operands beside it are single 16-byte LDS reads; the
+      // update reads R^T in the same order (optr_state) and the state is loaded and stored
+      // through it once.
       float4v st[8];
       const int vrow = v0 + 16 * W + l16;   // this lane's state row
+      // output element (token l16 of a 16-token block, values 4 l4 .. + 3 of this wave's rows)
+      uint16_t *const obase = gout + head0 + static_cast<long long>(l16) * tokstride + v0 + 16 * W + 4 * l4;
+      auto chan0 = [&](int cb) { return 32 * (cb >> 1) + 8 * l4 + 4 * (cb & 1); };
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         st[cb] = zero4();
         if (a.state_in != nullptr) {
-          const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4);
+          const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb));
           st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
         }
       }
@@ -296,17 +323,19 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           float4 egv[2], btv[2];
           float giv[2];
           float4 gjv[4 / NVW];   // kPv: cumulative decay at the columns of this wave's P blocks
-          auto load_ops = [&](int tb, int slot) {
+          auto load_e = [&](int tb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              ev[tb][j] = ops128(E, tb * 16 + l16, 32 * j, l4);
-              qv[slot][j] = ops128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
-            }
+            for (int j = 0; j < 4; ++j) ev[tb][j] = opn128(E, tb * 16 + l16, 32 * j, l4);
+          };
+          auto load_ops = [&](int tb, int slot) {
+            if constexpr (!kPv) load_e(tb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[slot][j] = opn128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
             // V' block (rows t, columns v) in the accumulator layout, read transposed
             vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
             if (CHAN && kPv && p_owner(tb) == W) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = ops128(sm.k[cur], tb * 16 + l16, 32 * j, l4);
+              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = opn128(sm.k[cur], tb * 16 + l16, 32 * j, l4);
             }
             egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
             if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
@@ -318,7 +347,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
               if (p_owner(jb) == W) gjv[p_slot(jb)] = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
           }
           load_ops(0, 0);
-          GDR_FENCE();   // (not fused with the next block's reads: 16 rows apart they would pair)
+          if constexpr (kPv) {
+            // the E operands of every block stay live for P anyway: all of them are requested
+            // now, so the phase waits for one LDS round trip instead of one per block
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) load_e(tb);
+          }
+          GDR_FENCE();
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) {
             const int sl = tb & 1;
@@ -380,8 +415,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           short8v ra[4], rb[4];   // R^T operands of the first half of the update
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            ra[cb] = optr128(Rk, cb * 16, 0, lane);
-            rb[cb] = optr128(Rk, cb * 16, 32, lane);
+            ra[cb] = optr_state(Rk, cb, 0, lane);
+            rb[cb] = optr_state(Rk, cb, 32, lane);
           }
           float4 wdv[4];
 #pragma unroll
@@ -409,8 +444,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             float4v acc = st[cb];
             if (DECAY) acc *= gC;
             st[cb] = mfma32(rb[cb], w23, mfma32(ra[cb], w01, acc));
-            ra[cb] = optr128(Rk, (cb + 4) * 16, 0, lane);   // second half, read behind the first
-            rb[cb] = optr128(Rk, (cb + 4) * 16, 32, lane);
+            ra[cb] = optr_state(Rk, cb + 4, 0, lane);   // second half, read behind the first
+            rb[cb] = optr_state(Rk, cb + 4, 32, lane);
           }
 #pragma unroll
           for (int cb = 4; cb < 8; ++cb) {
@@ -425,17 +460,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           O2[2] = mfma32(p22, d23, mfma32(p20, d01, O1[2]));
           O2[3] = mfma32(p32, d23, mfma32(p30, d01, O1[3]));
           // output: transpose each 16 x 16 block by an identity product so a lane holds four
-          // consecutive values of one token, then 8-byte stores
+          // consecutive values of one token (the four products issue back to back), then 8-byte
+          // stores from a per-lane base and uniform offsets; only a partial last chunk masks
+          if (a.scale != 1.f) {
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            const float4v o = a.scale == 1.f ? O2[tb] : a.scale * O2[tb];
-            const float4v ot = mfma16(tobf4(o), I16, zero4());   // lane: token tb*16 + l16, values 4 l4 + r
-            const int t = tb * 16 + l16;
-            if (t < n) {
-              const short4v pk = tobf4(ot);
-              *reinterpret_cast<short4v *>(gout + head0 + static_cast<long long>(c0 + t) * tokstride + v0 + 16 * W +
-                                           4 * l4) = pk;
-            }
+            for (int tb = 0; tb < 4; ++tb) O2[tb] = a.scale * O2[tb];
+          }
+          short4v pk[4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) pk[tb] = tobf4(mfma16(tobf4(O2[tb]), I16, zero4()));
+          uint16_t *ob = obase + static_cast<long long>(c0) * tokstride;
+          if (n == kC) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
+          } else {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              if (tb * 16 + l16 < n) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
           }
         }
         if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
@@ -443,7 +484,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       if (a.state_out != nullptr) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
-          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + 16 * cb + 4 * l4) =
+          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb)) =
               make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
       }
     };
@@ -555,13 +596,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     if (gate_wave) {
       const bool ok = lane < n;
       const float beta_t = ok ? bt : 0.f;
-      float g = ok ? la * kLog2e : 0.f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(g, d, 64);
-        if (lane >= d) g += y;
-      }
-      const float glast = __shfl(g, n - 1, 64);
+      // (a scan in registers: a shuffle through LDS would cost one LDS round trip per step)
+      const float g = wave_scan_add(ok ? la * kLog2e : 0.f);
+      const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), n - 1));
       sm.g2[buf][lane] = g;
       sm.eg[buf][lane] = DECAY ? decay2(g) : 1.f;
       sm.wd[buf][lane] = DECAY ? decay2(glast - g) : 1.f;
@@ -641,6 +678,36 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const bool have_next = c + 1 < nchunks;
 
     __syncthreads();   // (1)
+    // The two T_ba waves read every operand of their block products (T blocks and A blocks of
+    // chunk c, formed before the barrier) ahead of their staging writes: LDS operations of a
+    // wave complete in order, so reads issued after the writes would wait for them to drain,
+    // while issued first they let the writes drain under the products.
+    uint16_t *Tc = &sm.t[cur][0][0];
+    const int qb = hw;   // column block of the lower-left quadrant formed by this wave
+    // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read
+    auto arow = [&](int rb, int kb) { return ld4(Tc + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
+    auto bcol = [&](int kb, int cb) {
+      return ldtr(Tc + (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3));
+    };
+    auto lrow = [&](int s, int u) { return ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]); };
+    short4v o_a33, o_b22, o_a22, o_a32, o_a10, o_d, o_a11, o_l00, o_l01, o_l10, o_l11;
+    if (c >= 0 && hw < 2) {
+      o_a33 = arow(3, 3);
+      o_b22 = bcol(2, 2);
+      o_a22 = arow(2, 2);
+      o_a32 = ld4(&sm.aod[1][l16][4 * l4]);
+      o_l01 = lrow(0, 1);
+      o_l11 = lrow(1, 1);
+      if (qb == 0) {
+        o_a10 = ld4(&sm.aod[0][l16][4 * l4]);
+        o_d = bcol(0, 0);
+        o_a11 = arow(1, 1);
+        o_l00 = lrow(0, 0);
+        o_l10 = lrow(1, 0);
+      } else {
+        o_d = bcol(1, 1);
+      }
+    }
     if (have_next) {
       stage_items(c + 1, nxt);
       if (c + 2 < nchunks) load_items(c + 2);
@@ -649,34 +716,25 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       if (hw < 2) {
         // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
         // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a
-        const int qb = hw;
-        uint16_t *Tc = &sm.t[cur][0][0];
-        // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read
-        auto arow = [&](int rb, int kb) { return ld4(Tc + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
-        auto bcol = [&](int kb, int cb) {
-          return ldtr(Tc + (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3));
-        };
-        auto lrow = [&](int s, int u) { return ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]); };
-        const short4v a10 = ld4(&sm.aod[0][l16][4 * l4]), a32 = ld4(&sm.aod[1][l16][4 * l4]);
-        const float4v t32 = mfma16(arow(3, 3), tobf4(mfma16(a32, bcol(2, 2), zero4())), zero4());
+        const float4v t32 = mfma16(o_a33, tobf4(mfma16(o_a32, o_b22, zero4())), zero4());
         const short4v t32a = tobf4(mfma16(tobf4(t32), I16, zero4()));   // A layout of T_32
         float4v z0, z1;                                                  // Z = A_ba T_a[:, qb]
         if (qb == 0) {
-          const short4v d0 = bcol(0, 0);
-          const float4v t10 = mfma16(arow(1, 1), tobf4(mfma16(a10, d0, zero4())), zero4());
+          const short4v d0 = o_d;
+          const float4v t10 = mfma16(o_a11, tobf4(mfma16(o_a10, d0, zero4())), zero4());
           const short4v t10b = tobf4(t10);
-          z0 = mfma16(lrow(0, 1), t10b, mfma16(lrow(0, 0), d0, zero4()));
-          z1 = mfma16(lrow(1, 1), t10b, mfma16(lrow(1, 0), d0, zero4()));
+          z0 = mfma16(o_l01, t10b, mfma16(o_l00, d0, zero4()));
+          z1 = mfma16(o_l11, t10b, mfma16(o_l10, d0, zero4()));
           put_rows(Tc, 1, 0, mfma16(t10b, I16, zero4()), false);
         } else {
-          const short4v d1 = bcol(1, 1);
-          z0 = mfma16(lrow(0, 1), d1, zero4());
-          z1 = mfma16(lrow(1, 1), d1, zero4());
+          const short4v d1 = o_d;
+          z0 = mfma16(o_l01, d1, zero4());
+          z1 = mfma16(o_l11, d1, zero4());
           put_rows(Tc, 3, 2, mfma16(tobf4(t32), I16, zero4()), false);
         }
         const short4v z0b = tobf4(z0), z1b = tobf4(z1);
-        const float4v tb2 = mfma16(arow(2, 2), z0b, zero4());
-        const float4v tb3 = mfma16(arow(3, 3), z1b, mfma16(t32a, z0b, zero4()));
+        const float4v tb2 = mfma16(o_a22, z0b, zero4());
+        const float4v tb3 = mfma16(o_a33, z1b, mfma16(t32a, z0b, zero4()));
         put_rows(Tc, 2, qb, mfma16(tobf4(tb2), I16, zero4()), false);
         put_rows(Tc, 3, qb, mfma16(tobf4(tb3), I16, zero4()), false);
       }
