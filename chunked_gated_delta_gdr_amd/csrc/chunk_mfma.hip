@@ -806,25 +806,18 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 
     if (have_next) {
       const int nb = nxt;
-      if (hw < 4) {
-        // diagonal block hw of T: D = (I - A_pp)^-1
-        const float4v n = a_tile(nb, hw, hw, false);
-        const float4v nt = mfma16(tobf4(n), I16, zero4());
-        float4v d, dt;
-        diag_inverse(n, nt, d, &dt, lane);
-        put_rows(&sm.t[nb][0][0], hw, hw, dt, true);
-      } else {
-        // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba,
-        // this wave's share formed together (operands first, then the product chains)
-        constexpr int NOW = NHW - 4;               // waves on these jobs
-        constexpr int NJW = (6 + NOW - 1) / NOW;   // jobs per wave
+      // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba (jobs
+      // 0..5); a wave forms its share together (operands first, then the product chains).  Job
+      // q of a batch is job0 + q * jstep; jobs past the last repeat it without storing.
+      auto a_jobs = [&](auto njc, int job0, int jstep) {
+        constexpr int NJ = decltype(njc)::value;
         const uint16_t *E = CHAN ? sm.e[nb] : sm.k[nb];
         const uint16_t *R = (WK == kWkSame) ? sm.k[nb] : sm.r[nb];
-        int ib[NJW], jb[NJW];
-        short8v ra[NJW][4], eb[NJW][4];
+        int ib[NJ], jb[NJ];
+        short8v ra[NJ][4], eb[NJ][4];
 #pragma unroll
-        for (int q = 0; q < NJW; ++q) {
-          const int job = min(hw - 4 + q * NOW, 5);   // a job past the last repeats it unstored
+        for (int q = 0; q < NJ; ++q) {
+          const int job = min(job0 + q * jstep, 5);
           ib[q] = job == 0 ? 1 : job == 1 ? 3 : 2 + ((job - 2) >> 1);
           jb[q] = job == 0 ? 0 : job == 1 ? 2 : (job - 2) & 1;
 #pragma unroll
@@ -833,17 +826,17 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             eb[q][s2] = opn128(E, ib[q] * 16 + l16, 32 * s2, l4);
           }
         }
-        float4v acc[NJW];
+        float4v acc[NJ];
 #pragma unroll
-        for (int q = 0; q < NJW; ++q) acc[q] = zero4();
+        for (int q = 0; q < NJ; ++q) acc[q] = zero4();
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
-          for (int q = 0; q < NJW; ++q) acc[q] = mfma32(ra[q][s2], eb[q][s2], acc[q]);
+          for (int q = 0; q < NJ; ++q) acc[q] = mfma32(ra[q][s2], eb[q][s2], acc[q]);
         }
 #pragma unroll
-        for (int q = 0; q < NJW; ++q) {
-          const int job = hw - 4 + q * NOW;
+        for (int q = 0; q < NJ; ++q) {
+          const int job = job0 + q * jstep;
           // lane: (E R^T)[i = ib*16 + l16][j = jb*16 + 4 l4 + r], scaled to A = -L (j < i always)
           const int i = ib[q] * 16 + l16;
           const float bi = SCALED_E ? sm.beta[nb][i] : 1.f, gi = sm.g2[nb][i];
@@ -856,6 +849,26 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             *reinterpret_cast<short4v *>(dst) = tobf4(x);
           }
         }
+      };
+      // With six helpers the two A waves would carry three jobs each against one diagonal
+      // inverse per other wave, so waves 0 and 1 (the lightest: their other work is before the
+      // second barrier) take jobs 4 and 5 after their inverse.
+      constexpr int NOW = NHW - 4;               // waves on A jobs only
+      constexpr bool kSplitA = NOW == 2;
+      if (hw < 4) {
+        // diagonal block hw of T: D = (I - A_pp)^-1
+        const float4v n = a_tile(nb, hw, hw, false);
+        const float4v nt = mfma16(tobf4(n), I16, zero4());
+        float4v d, dt;
+        diag_inverse(n, nt, d, &dt, lane);
+        put_rows(&sm.t[nb][0][0], hw, hw, dt, true);
+        if constexpr (kSplitA) {
+          if (hw < 2) a_jobs(std::integral_constant<int, 1>{}, 4 + hw, 1);
+        }
+      } else if constexpr (kSplitA) {
+        a_jobs(std::integral_constant<int, 2>{}, hw - 4, 2);
+      } else {
+        a_jobs(std::integral_constant<int, (6 + NOW - 1) / NOW>{}, hw - 4, NOW);
       }
     }
   }
