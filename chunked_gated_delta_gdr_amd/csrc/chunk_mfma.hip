@@ -162,6 +162,11 @@ __device__ __forceinline__ float wave_scan_add(float x) {
   x += dppf<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
   return x;
 }
+// lane (lane & ~3) + perm[lane & 3] of a float (quad_perm DPP move, in registers)
+template <int PERM>
+__device__ __forceinline__ float quadf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), PERM, 0xf, 0xf, false));
+}
 // keep the scheduler from hoisting the next tile's operand loads above this point
 // (bounds register pressure; the hardware still overlaps the independent work)
 #define GDR_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -665,12 +670,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     *reinterpret_cast<short4v *>(M + i * kLdc + cb * 16 + 4 * l4) = tobf4(v);
   };
 
-  // preconditioner accumulator: helper threads ht < 256 own channel ht / 2, token half ht % 2
+  // preconditioner accumulator: helper threads ht < 256 own channels 2 p, 2 p + 1 (p = ht / 4)
+  // and tokens 16 s .. 16 s + 15 (s = ht % 4) of a chunk; the four segments of a channel pair
+  // are the four lanes of a quad.  The accumulator entering the chunk is kept in all four.
   const bool pc_thread = ht < 256;
-  const int pc_c = ht >> 1, pc_seg = ht & 1;
-  float hcarry = 0.f;
-  if (WK == kWkPrecond && pc_thread)
-    hcarry = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + pc_c] : a.h0;
+  const int pc_p = ht >> 2, pc_seg = ht & 3;
+  float hc0 = 0.f, hc1 = 0.f;
+  if (WK == kWkPrecond && pc_thread) {
+    hc0 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p] : a.h0;
+    hc1 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p + 1] : a.h0;
+  }
 
   if (nchunks > 0) load_items(0);
   for (int c = -1; c < nchunks; ++c) {
@@ -754,52 +763,77 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     if (WK == kWkPrecond) {
       // write keys of chunk c + 1: u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2
       if (have_next && pc_thread) {
-        // this thread: channel pc_c, tokens s0 .. s0 + 31 of chunk c + 1 (rows past the end of
-        // the sequence were staged as zero and are masked below); the keys are read up front and
-        // both passes are unrolled, so only the arithmetic chain remains serial
+        // this thread: channels 2 p, 2 p + 1, tokens s0 .. s0 + 15 of chunk c + 1 (rows past the
+        // end of the sequence were staged as zero and are masked below).  Pass 1 forms the
+        // segment's affine map h -> rm h + acc; the four segments' maps are composed across the
+        // quad by register moves (an inclusive scan of two steps, then a shift by one); pass 2
+        // reruns the segment from its entering accumulator and writes u.  Keys and write keys
+        // move as bf16 pairs (4-byte LDS accesses).
         const uint16_t *Kn = sm.k[nxt];
         const int nn = min(kC, T - (c + 1) * kC);
-        const int ch = pc_c, s0 = pc_seg * 32;
-        const int m = max(0, min(32, nn - s0));
-        float kv[32];
+        const int s0 = pc_seg * 16, cp = 2 * pc_p;
+        const int m = max(0, min(16, nn - s0));
+        float k0[16], k1[16];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) kv[i] = bf(Kn[sw128(s0 + i, ch)]);
-        float kk2[32];
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t w = *reinterpret_cast<const uint32_t *>(Kn + sw128(s0 + i, cp));
+          k0[i] = bf(w & 0xffffu);
+          k1[i] = bf(w >> 16);
+        }
+        float a0 = 0.f, a1 = 0.f, rm = 1.f;
+        if (m == 16) {   // every token present (all but a partial last chunk)
 #pragma unroll
-        for (int i = 0; i < 32; ++i) kk2[i] = kv[i] * kv[i];
-        float acc = 0.f, rm = 1.f;   // this segment's affine map h -> rm h + acc
-        if (m == 32) {               // every token present (all but a partial last chunk)
-#pragma unroll
-          for (int i = 0; i < 32; ++i) acc = fmaf(a.rho, acc, kk2[i]);
-          const float r2 = a.rho * a.rho, r4 = r2 * r2, r8 = r4 * r4, r16 = r8 * r8;
-          rm = r16 * r16;
+          for (int i = 0; i < 16; ++i) {
+            a0 = fmaf(a.rho, a0, k0[i] * k0[i]);
+            a1 = fmaf(a.rho, a1, k1[i] * k1[i]);
+          }
+          const float r2 = a.rho * a.rho, r4 = r2 * r2, r8 = r4 * r4;
+          rm = r8 * r8;
         } else {
 #pragma unroll
-          for (int i = 0; i < 32; ++i) {
+          for (int i = 0; i < 16; ++i) {
             const bool on = i < m;
-            acc = on ? fmaf(a.rho, acc, kk2[i]) : acc;
+            a0 = on ? fmaf(a.rho, a0, k0[i] * k0[i]) : a0;
+            a1 = on ? fmaf(a.rho, a1, k1[i] * k1[i]) : a1;
             rm = on ? rm * a.rho : rm;
           }
         }
-        // compose the two halves' affine maps h -> rm h + acc
-        const float rm0 = __shfl(rm, lane & ~1, 64), ac0 = __shfl(acc, lane & ~1, 64);
-        const float rm1 = __shfl(rm, lane | 1, 64), ac1 = __shfl(acc, lane | 1, 64);
-        const float mid = fmaf(rm0, hcarry, ac0);
-        float hv = pc_seg == 0 ? hcarry : mid;
-        uint16_t *Rn = sm.r[nxt] + s0 * kD + (ch & 7);
-        const int cg = ch >> 3;
+        // inclusive scan over the quad: F_s = f_s o F_{s-1} = (rm_s R, rm_s A + acc_s)
+        {
+          const float pr = quadf<0x90>(rm), p0 = quadf<0x90>(a0), p1 = quadf<0x90>(a1);   // lane s - 1
+          if (pc_seg >= 1) {
+            a0 = fmaf(rm, p0, a0);
+            a1 = fmaf(rm, p1, a1);
+            rm *= pr;
+          }
+          const float qr = quadf<0x44>(rm), q0 = quadf<0x44>(a0), q1 = quadf<0x44>(a1);   // lane s - 2
+          if (pc_seg >= 2) {
+            a0 = fmaf(rm, q0, a0);
+            a1 = fmaf(rm, q1, a1);
+            rm *= qr;
+          }
+        }
+        // entering accumulator of this segment: F_{s-1}(h_chunk); the next chunk's: F_3(h_chunk)
+        const float er = quadf<0x90>(rm), e0 = quadf<0x90>(a0), e1 = quadf<0x90>(a1);
+        float h0v = pc_seg == 0 ? hc0 : fmaf(er, hc0, e0);
+        float h1v = pc_seg == 0 ? hc1 : fmaf(er, hc1, e1);
+        const float lr = quadf<0xff>(rm), l0 = quadf<0xff>(a0), l1 = quadf<0xff>(a1);
+        uint16_t *Rn = sm.r[nxt];
         float4 ic4;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < 16; ++i) {
           if ((i & 3) == 0) ic4 = ld4f(&sm.ic[nxt][s0 + i]);
           const float icv = (&ic4.x)[i & 3];
           const bool on = i < m;
-          hv = on ? fmaf(a.rho, hv, kk2[i]) : hv;
+          h0v = on ? fmaf(a.rho, h0v, k0[i] * k0[i]) : h0v;
+          h1v = on ? fmaf(a.rho, h1v, k1[i] * k1[i]) : h1v;
           // (the key is rounded to bf16 next, so the hardware reciprocal is accurate enough)
-          const float u = kv[i] * __builtin_amdgcn_rcpf(fmaf(hv, icv, a.eps));
-          Rn[i * kD + ((cg ^ (i & 15)) << 3)] = tobf(on ? u : 0.f);   // sw128(s0 + i, ch), s0 % 16 == 0
+          const float u0 = k0[i] * __builtin_amdgcn_rcpf(fmaf(h0v, icv, a.eps));
+          const float u1 = k1[i] * __builtin_amdgcn_rcpf(fmaf(h1v, icv, a.eps));
+          *reinterpret_cast<uint32_t *>(Rn + sw128(s0 + i, cp)) = f32x2_to_bf16x2_bits(on ? u0 : 0.f, on ? u1 : 0.f);
         }
-        hcarry = fmaf(rm1, mid, ac1);
+        hc0 = fmaf(lr, hc0, l0);
+        hc1 = fmaf(lr, hc1, l1);
       }
       __syncthreads();   // (3)
     }
@@ -873,7 +907,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     }
   }
   if (WK == kWkPrecond && a.pc_h_out != nullptr && vt == 0 && pc_thread && pc_seg == 0)
-    a.pc_h_out[static_cast<long long>(bh) * kD + pc_c] = hcarry;
+  {
+    a.pc_h_out[static_cast<long long>(bh) * kD + 2 * pc_p] = hc0;
+    a.pc_h_out[static_cast<long long>(bh) * kD + 2 * pc_p + 1] = hc1;
+  }
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
