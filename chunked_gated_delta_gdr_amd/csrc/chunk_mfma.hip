@@ -226,11 +226,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
   constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
   constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
-  // with write key R = k, P = tril(Q K^T) is formed by the two value waves from the Q operands
-  // they already hold for O1 and the K operands of Y (scalar gains, E = beta k) or read
-  // beside them (channel gates, E = b (.) k); otherwise (and with a single value wave, which
-  // would have to keep every K block) the helper waves form it
-  constexpr bool kPv = (WK == kWkSame) && NVW == 2;
+  // with two value waves, P = tril(Q R^T) is formed by the value waves from the Q operands
+  // they already hold for O1 and the R operands: those of Y when R = k and E = beta k (scalar
+  // gains), else read beside them (channel gates: R = k, E = b (.) k; a preconditioned or
+  // explicit write key: R in its own array); with a single value wave, which would have to
+  // keep every R block, the helper waves form it
+  constexpr bool kPv = NVW == 2;
+  constexpr bool kRq = kPv && (CHAN || WK != kWkSame);   // P's R operands read separately
   __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           // one register set per block for the E operands (the wave keeps those of its own P column
           // blocks alive; the others die after their block), double-buffered Q operands
           short8v ev[4][4], qv[2][4];
-          short8v kq[2][4];   // channel gates: K operands of this wave's two P column blocks
+          short8v kq[2][4];   // kRq: R operands of this wave's two P column blocks
           // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
           // wave 0, 1 and 2 to wave 1)
           constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
@@ -338,9 +340,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) qv[slot][j] = opn128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
             // V' block (rows t, columns v) in the accumulator layout, read transposed
             vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
-            if (CHAN && kPv && p_owner(tb) == W) {
+            if (kRq && p_owner(tb) == W) {
+              const uint16_t *Rp = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = opn128(sm.k[cur], tb * 16 + l16, 32 * j, l4);
+              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = opn128(Rp, tb * 16 + l16, 32 * j, l4);
             }
             egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
             if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 if (p_owner(jb) != W) continue;
                 float4v pt = zero4();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pt = mfma32(CHAN ? kq[p_slot(jb)][j] : ev[jb][j], qv[sl][j], pt);
+                for (int j = 0; j < 4; ++j) pt = mfma32(kRq ? kq[p_slot(jb)][j] : ev[jb][j], qv[sl][j], pt);
                 const float4 gj = gjv[p_slot(jb)];
                 float4v pv;
 #pragma unroll
