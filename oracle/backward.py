@@ -1,0 +1,151 @@
+"""fp64 gradients of the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Reverse-mode differentiation of the token-by-token recurrence of ``core.recurrent_stream``
+(the pages train these layers but print no backward pass; the gradient is the plain
+derivative of the forward definition, taken step by step in reverse).  For one stream,
+with the state before token t written S_{t-1}, the decay step Sa = alpha_t S_{t-1}
+(or S_{t-1} Diag(a_t)), the corrected value d_t = v'_t - Sa e_t and
+S_t = Sa + d_t r_t^T, o_t = S_t (scale q_t).  Given the loss gradients dO and dS_T, the
+reverse sweep carries G = dL/dS_t:
+
+    G      += do_t (scale q_t)^T              dq_t  = scale S_t^T do_t
+    dd_t    = G r_t                            dr_t  = G^T d_t
+    dSa     = G - dd_t e_t^T                   de_t  = -Sa^T dd_t,   dv'_t = dd_t
+    scalar decay:      dlog_alpha_t = <dSa, Sa>,                    G <- alpha_t dSa
+    per-channel decay: dlog_alpha_tc = sum_v dSa_vc Sa_vc,          G <- dSa Diag(a_t)
+    no decay:          G <- dSa
+
+and dS_0 = G at the end.  The variant vectors are then differentiated by the chain rule:
+e = beta k | b (.) k, v' = beta v | w (.) v, r = k | given write key.
+
+Pinned in ``tests/test_oracle_pins.py`` by central finite differences of the forward
+oracle (every input element, every variant) and by the causal linear-attention special
+case, whose gradients are textbook.  The diagonal preconditioner is not differentiated
+here.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from .core import F64, _stream, variant_vectors
+
+
+def recurrent_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray,
+                          dS_T: Optional[np.ndarray] = None, *, scale: float = 1.0,
+                          S0: Optional[np.ndarray] = None, checkpoint: int = 0
+                          ) -> Dict[str, np.ndarray]:
+    """Gradients of one stream's loss with respect to its inputs.
+
+    ``x`` holds one stream's [T, D] / [T] arrays as for ``core.recurrent_stream``; ``dO`` is
+    dL/do [T, Dv], ``dS_T`` dL/dS_T [Dv, Dk] (zero if None).  ``checkpoint`` > 0 keeps the
+    state only every ``checkpoint`` tokens and recomputes the states in between during the
+    reverse sweep (for long sequences); 0 keeps every state.
+
+    Returns dq, dk, dv, dS0 and, as the variant has them, dbeta | (derase, dwrite),
+    dlog_alpha ([T] or [T, Dk]) and dwrite_key.
+    """
+    e, r, vp, la, _ = variant_vectors(x)
+    q = np.asarray(x["q"], dtype=F64) * scale
+    dO = np.asarray(dO, dtype=F64)
+    T, Dk = e.shape
+    Dv = vp.shape[1]
+    chd = la.ndim == 2
+    S = np.zeros((Dv, Dk), dtype=F64) if S0 is None else np.array(S0, dtype=F64, copy=True)
+
+    def step(S_prev, t):
+        """(Sa, d, S_t) of token t from the state before it."""
+        a = np.exp(la[t])
+        Sa = S_prev * (a[None, :] if chd else a)
+        d = vp[t] - Sa @ e[t]
+        return Sa, d, Sa + np.outer(d, r[t])
+
+    # forward sweep: the state before every token (or before every checkpoint-th token)
+    seg = checkpoint if checkpoint > 0 else 1
+    saved = {}
+    for t in range(T):
+        if t % seg == 0:
+            saved[t] = S.copy()
+        S = step(S, t)[2]
+
+    de = np.zeros_like(e)
+    dr = np.zeros_like(r)
+    dvp = np.zeros_like(vp)
+    dq = np.zeros_like(q)
+    dla = np.zeros_like(la)
+    G = np.zeros((Dv, Dk), dtype=F64) if dS_T is None else np.array(dS_T, dtype=F64, copy=True)
+    for s0 in reversed(range(0, T, seg)):
+        # states before tokens s0 .. s1 - 1 of this segment
+        s1 = min(s0 + seg, T)
+        before = [saved[s0]]
+        for t in range(s0, s1 - 1):
+            before.append(step(before[-1], t)[2])
+        for t in reversed(range(s0, s1)):
+            S_prev = before[t - s0]
+            Sa, d, St = step(S_prev, t)
+            G = G + np.outer(dO[t], q[t])
+            dq[t] = St.T @ dO[t]
+            dd = G @ r[t]
+            dr[t] = G.T @ d
+            dSa = G - np.outer(dd, e[t])
+            de[t] = -(Sa.T @ dd)
+            dvp[t] = dd
+            if chd:
+                dla[t] = np.sum(dSa * Sa, axis=0)
+                G = dSa * np.exp(la[t])[None, :]
+            else:
+                dla[t] = np.sum(dSa * Sa)
+                G = dSa * np.exp(la[t])
+    dq *= scale   # q above is scale * q
+
+    k = np.asarray(x["k"], dtype=F64)
+    v = np.asarray(x["v"], dtype=F64)
+    g: Dict[str, np.ndarray] = {"dq": dq, "dS0": G}
+    if x.get("erase") is not None:
+        b = np.asarray(x["erase"], dtype=F64)
+        w = np.asarray(x["write"], dtype=F64)
+        dk = b * de
+        g["derase"] = k * de
+        g["dwrite"] = v * dvp
+        g["dv"] = w * dvp
+    else:
+        beta = np.asarray(x["beta"], dtype=F64)
+        dk = beta[:, None] * de
+        g["dbeta"] = np.sum(k * de, axis=1) + np.sum(v * dvp, axis=1)
+        g["dv"] = beta[:, None] * dvp
+    if x.get("write_key") is not None:
+        g["dwrite_key"] = dr
+    else:
+        dk = dk + dr
+    g["dk"] = dk
+    if x.get("log_alpha") is not None:
+        g["dlog_alpha"] = dla
+    return g
+
+
+def recurrent_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.ndarray] = None,
+                   *, scale: float = 1.0, state0: Optional[np.ndarray] = None, streams=None,
+                   checkpoint: int = 0) -> Dict[str, np.ndarray]:
+    """Gradients over [B, T, H, D] inputs (every stream, or the listed (b, h) pairs; the
+    other entries stay zero).  ``dO`` is [B, T, H, Dv], ``dS_T`` [B, H, Dv, Dk] or None.
+    The results have the inputs' shapes; dS0 is [B, H, Dv, Dk]."""
+    B, T, H, _ = x["q"].shape
+    Dk = x["k"].shape[-1]
+    Dv = x["v"].shape[-1]
+    out: Dict[str, np.ndarray] = {}
+    todo = streams if streams is not None else [(b, h) for b in range(B) for h in range(H)]
+    for (b, h) in todo:
+        gb = recurrent_stream_grad(_stream(x, b, h), np.asarray(dO)[b, :, h],
+                                   None if dS_T is None else dS_T[b, h], scale=scale,
+                                   S0=None if state0 is None else state0[b, h],
+                                   checkpoint=checkpoint)
+        for key, val in gb.items():
+            if key not in out:
+                shape = (B, H, Dv, Dk) if key == "dS0" else (B, T, H) + val.shape[1:]
+                out[key] = np.zeros(shape, dtype=F64)
+            if key == "dS0":
+                out[key][b, h] = val
+            else:
+                out[key][b, :, h] = val
+    return out
