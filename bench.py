@@ -7,6 +7,7 @@ Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|gdn2|pdn|long|plain|kda|decode]
                     [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
+    python bench.py --bwd [--workload gdn|gdn2|plain]   # gdr_chunk_bwd instead
 
 Counter helpers (used to produce the committed traffic summaries under profiles/):
     python bench.py --copy-probe-mb 256          # calibration copy of known size
@@ -28,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "tokens/s chunked gated-delta fwd (B4 H16 T4096 d128 bf16); % MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 KERNEL_SOURCES = {
     "mfma": ["chunked_gated_delta_gdr_amd/csrc/chunk_mfma.hip"],
@@ -293,6 +295,130 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bwd_alg_bytes(s) -> int:
+    """Bytes the backward must move per call: the forward's inputs, dO, the initial state
+    and dL/dS_T read once; every gradient (fp32) written once."""
+    esz = 2 if s.dtype == "bf16" else 4
+    per_tok = (2 * s.Dk + 2 * s.Dv) * esz                       # q, k, v, dO
+    per_tok += (2 * s.Dk + s.Dv) * 4                            # dq, dk, dv
+    per_tok += 8 if s.gain == "scalar" else (s.Dk + s.Dv) * (esz + 4)   # gains and their grads
+    per_tok += 8 if s.decay == "scalar" else 0                  # log alpha and its grad
+    per_head = 3 * s.Dv * s.Dk * 4                              # S_0, dS_T, dS_0
+    return s.B * s.T * s.H * per_tok + s.B * s.H * per_head
+
+
+def bwd_alg_flops(s) -> float:
+    """Algorithmic FLOPs of one backward call: the forward recompute (alg_flops) plus, per
+    token-head, the reverse sweep (R dS^T, the state-gradient update: 3 Dk Dv; P^T dO and
+    T^T dD: 2 (C+1)/2 Dv MACs) and the per-chunk products (dO S, dX S, D dS': 3 Dk Dv;
+    dO D^T, dX D^T: 2 (C+1)/2 Dv; dM R, dL' R, dM^T Q, dL'^T E: 4 (C+1)/2 Dk MACs)."""
+    C, Dk, Dv = s.chunk, s.Dk, s.Dv
+    macs = 6 * Dk * Dv + 2 * (C + 1) * Dv + 2 * (C + 1) * Dk
+    return alg_flops(s) + 2.0 * macs * s.B * s.T * s.H
+
+
+def bench_backward(args):
+    """One step = one gdr_chunk_bwd call (forward recompute, reverse sweep, per-chunk pass)."""
+    import numpy as np
+    import torch
+
+    import chunked_gated_delta_gdr_amd as G
+    import gdr_synth as gs
+
+    s = gs.spec(args.workload)
+    if s.wkey == "precond" or s.decay == "channel":
+        print(f"bench.py --bwd: the {args.workload} workload's variant has no backward here", file=sys.stderr)
+        sys.exit(2)
+    x, cot = gs.make_inputs(s), gs.make_cotangents(s)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    io = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    f32 = torch.float32
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    a = dict(q=t(x["q"], io), k=t(x["k"], io), v=t(x["v"], io), beta=t(x.get("beta"), f32),
+             log_alpha=t(x.get("log_alpha"), f32), erase=t(x.get("erase"), io), write=t(x.get("write"), io),
+             write_key=t(x.get("write_key"), io))
+    rng = np.random.Generator(np.random.PCG64(s.seed + 31))
+    s0 = (0.1 * rng.standard_normal((s.B, s.H, s.Dv, s.Dk))).astype(np.float32)
+    S0, dO, dST = t(s0, f32), t(cot["d_out"], io), t(cot["d_state_out"], f32)
+    desc = G.make_desc(B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk, io_dtype=G.GDR_BF16 if
+                       s.dtype == "bf16" else G.GDR_F32,
+                       gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
+                       decay=G.GDR_DECAY_SCALAR if s.decay == "scalar" else G.GDR_DECAY_NONE)
+    ws = torch.empty(G.gdr_chunk_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] backward {args.workload}: workspace {ws.numel() / 2**20:.1f} MiB, steps {args.steps} "
+          f"warmup {args.warmup}", file=sys.stderr, flush=True)
+
+    def step():
+        return G.gdr_chunk_bwd(a["q"], a["k"], a["v"], dO, beta=a["beta"], log_alpha=a["log_alpha"],
+                               erase=a["erase"], write=a["write"], write_key=a["write_key"], state_in=S0,
+                               d_state_out=dST, chunk=s.chunk, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        g = step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        g = step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg_s = sum(call_ms) / len(call_ms) / 1e3
+    print(f"[bench] backward call avg {avg_s * 1e6:.1f} us min {min(call_ms) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    af = bwd_alg_flops(s)
+    ab = bwd_alg_bytes(s)
+    parity = None
+    if not args.no_parity:
+        import oracle
+        ref = oracle.recurrent_grad(x, cot["d_out"], cot["d_state_out"], state0=s0, streams=[(0, 0)],
+                                    checkpoint=64)
+        parity = {"stream": "(0,0)", "tokens": s.T}
+        for name in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "derase", "dwrite"):
+            if name in ref:
+                parity[f"rel_l2_{name}"] = oracle.rel_l2(g[name][0, :, 0].double().cpu().numpy(),
+                                                         ref[name][0, :, 0])
+        parity["rel_l2_dstate_in"] = oracle.rel_l2(g["dstate_in"][0, 0].double().cpu().numpy(),
+                                                   ref["dS0"][0, 0])
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(s.T, 1024)
+        sub = {k: (None if v is None else v[:1, :n, :1]) for k, v in x.items()}
+        w0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - w0 < 10.0:
+            oracle.recurrent_grad(sub, cot["d_out"][:1, :n, :1], None)
+            reps += 1
+        wall = time.perf_counter() - w0
+        cpu = {"value": round(reps * n / wall / s.H, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"fp64 token-by-token reverse sweep on stream (0,0), {n} tokens, {reps} repetitions "
+                         f"in {wall:.1f} s on one core; tokens/s = token-heads / H / wall"}
+    rec = {
+        "metric": f"tokens/s chunked gated-delta backward ({args.workload}: B{s.B} H{s.H} T{s.T} d{s.Dk} {s.dtype})",
+        "value": round(s.B * s.T / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded inputs of the workload; dO, dL/dS_T ~ N(0,1); random fp32 start state)",
+        "config": {"workload": f"{args.workload} backward: B{s.B} H{s.H} T{s.T} Dk{s.Dk} Dv{s.Dv} C{s.chunk} "
+                               f"{s.dtype} in, fp32 arithmetic and gradients, gain={s.gain} decay={s.decay}",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": round(af / avg_s / 1e12, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(af / avg_s / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "gdr_chunk_bwd (forward recompute + reverse sweep + per-chunk pass)",
+                     "alg_gflop_per_launch": round(af / 1e9, 3), "avg_launch_us": round(avg_s * 1e6, 2),
+                     "alg_bytes_per_launch": ab, "hbm_frac_of_alg_bytes": round(ab / avg_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu, "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +429,7 @@ def main():
     ap.add_argument("--residual", type=int, default=0,
                     help="residual-correction steps on the band-N start (needs --neumann N)")
     ap.add_argument("--impl", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--bwd", action="store_true", help="time gdr_chunk_bwd instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -327,6 +454,9 @@ def main():
         sys.exit(2)
     if args.workload == "decode":
         bench_decode(args)
+        return
+    if args.bwd:
+        bench_backward(args)
         return
 
     import numpy as np

@@ -14,8 +14,9 @@ from ._binding import (  # noqa: F401
     GDR_DECAY_NONE, GDR_DECAY_SCALAR, GDR_DECAY_CHANNEL,
     GDR_WKEY_SAME, GDR_WKEY_DIAG_PRECOND, GDR_WKEY_EXPLICIT,
     GDR_IMPL_AUTO, GDR_IMPL_GENERIC, GDR_IMPL_MFMA,
-    GdrError, gdr_desc_t, gdr_inputs_t,
+    GdrError, gdr_desc_t, gdr_inputs_t, gdr_grads_t,
     lib, lib_path, make_desc,
     gdr_chunk_fwd, gdr_recurrent_step, gdr_validate, gdr_chunk_fwd_impl,
+    gdr_chunk_bwd, gdr_chunk_bwd_workspace_size, gdr_validate_bwd,
     gdr_status_str, gdr_last_error, gdr_abi_version,
 )

@@ -41,6 +41,15 @@ class gdr_inputs_t(ctypes.Structure):
     ]
 
 
+class gdr_grads_t(ctypes.Structure):
+    _fields_ = [
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dbeta", ctypes.c_void_p), ("derase", ctypes.c_void_p), ("dwrite", ctypes.c_void_p),
+        ("dlog_alpha", ctypes.c_void_p), ("dwrite_key", ctypes.c_void_p),
+        ("dstate_in", ctypes.c_void_p),
+    ]
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{gdr_status_str(status)}: {msg}")
@@ -73,6 +82,15 @@ def lib() -> ctypes.CDLL:
         L.gdr_validate.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_int]
         L.gdr_validate.restype = ctypes.c_int
+        L.gdr_chunk_bwd.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, P(gdr_grads_t), ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_void_p]
+        L.gdr_chunk_bwd.restype = ctypes.c_int
+        L.gdr_chunk_bwd_workspace_size.argtypes = [P(gdr_desc_t)]
+        L.gdr_chunk_bwd_workspace_size.restype = ctypes.c_uint64
+        L.gdr_validate_bwd.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, P(gdr_grads_t), ctypes.c_void_p, ctypes.c_uint64]
+        L.gdr_validate_bwd.restype = ctypes.c_int
         L.gdr_chunk_fwd_impl.argtypes = [P(gdr_desc_t)]
         L.gdr_chunk_fwd_impl.restype = ctypes.c_int
         L.gdr_status_str.argtypes = [ctypes.c_int]
@@ -81,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_last_error.restype = ctypes.c_char_p
         L.gdr_abi_version.argtypes = []
         L.gdr_abi_version.restype = ctypes.c_int
-        if L.gdr_abi_version() != 2:
+        if L.gdr_abi_version() != 3:
             raise ImportError("libgdr ABI version mismatch")
         _LIB = L
     return _LIB
@@ -112,6 +130,19 @@ def gdr_validate(desc: gdr_desc_t, inputs: gdr_inputs_t, state_in=None, out=None
     """Host-side argument check (no HIP call).  Pointers are ints or None."""
     return lib().gdr_validate(ctypes.byref(desc), ctypes.byref(inputs), state_in, out, state_out,
                               int(for_step))
+
+
+def gdr_chunk_bwd_workspace_size(desc: gdr_desc_t) -> int:
+    return int(lib().gdr_chunk_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def gdr_validate_bwd(desc: gdr_desc_t, inputs: gdr_inputs_t, state_in=None, d_out=None,
+                     d_state_out=None, grads: Optional[gdr_grads_t] = None, workspace=None,
+                     workspace_bytes: int = 0) -> int:
+    """gdr_chunk_bwd's host-side argument check (no HIP call).  Pointers are ints or None."""
+    g = grads if grads is not None else gdr_grads_t()
+    return lib().gdr_validate_bwd(ctypes.byref(desc), ctypes.byref(inputs), state_in, d_out, d_state_out,
+                                  ctypes.byref(g), workspace, workspace_bytes)
 
 
 def gdr_chunk_fwd_impl(desc: gdr_desc_t) -> int:
@@ -273,3 +304,65 @@ def gdr_recurrent_step(q, k, v, state, *, beta=None, log_alpha=None, erase=None,
                                   _stream(stream, dev))
     _raise(st)
     return out, (pc_h_out if precond else None)
+
+
+def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, write=None,
+                  write_key=None, state_in=None, d_state_out=None, want_dstate_in: bool = True,
+                  chunk: int = 64, scale: float = 1.0, workspace=None, stream=None) -> dict:
+    """Gradients through ``gdr_chunk_fwd`` on torch tensors.  ``d_out`` [B, T, H, Dv] (io dtype)
+    and ``d_state_out`` [B, H, Dv, Dk] fp32 (or None) are the loss gradients of the forward's
+    outputs.  Returns a dict of fp32 tensors: dq, dk, dv, and as the variant has them dbeta |
+    derase, dwrite, dlog_alpha, dwrite_key, and dstate_in (if ``want_dstate_in``).  The
+    workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is allocated when not given."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    io = q.dtype
+    f32 = torch.float32
+    _io_code(io)
+    _check("q", q, (B, T, H, Dk), io, dev)
+    _check("k", k, (B, T, H, Dk), io, dev)
+    _check("v", v, (B, T, H, Dv), io, dev)
+    _check("d_out", d_out, (B, T, H, Dv), io, dev)
+    _check("beta", beta, (B, T, H), f32, dev)
+    _check("log_alpha", log_alpha, (B, T, H), f32, dev)
+    _check("erase", erase, (B, T, H, Dk), io, dev)
+    _check("write", write, (B, T, H, Dv), io, dev)
+    _check("write_key", write_key, (B, T, H, Dk), io, dev)
+    _check("state_in", state_in, (B, H, Dv, Dk), f32, dev)
+    _check("d_state_out", d_state_out, (B, H, Dv, Dk), f32, dev)
+    desc = make_desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, io_dtype=_io_code(io),
+                     gain=GDR_GAIN_CHANNEL if erase is not None else GDR_GAIN_SCALAR,
+                     decay=GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE,
+                     wkey=GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME,
+                     scale=scale, impl=GDR_IMPL_GENERIC)
+
+    def new(shape):
+        return torch.empty(shape, dtype=f32, device=dev)
+
+    g = {"dq": new((B, T, H, Dk)), "dk": new((B, T, H, Dk)), "dv": new((B, T, H, Dv))}
+    if erase is not None:
+        g["derase"] = new((B, T, H, Dk))
+        g["dwrite"] = new((B, T, H, Dv))
+    else:
+        g["dbeta"] = new((B, T, H))
+    if log_alpha is not None:
+        g["dlog_alpha"] = new((B, T, H))
+    if write_key is not None:
+        g["dwrite_key"] = new((B, T, H, Dk))
+    if want_dstate_in:
+        g["dstate_in"] = new((B, H, Dv, Dk))
+    nbytes = gdr_chunk_bwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {nbytes}")
+    grads = gdr_grads_t(*[_ptr(g.get(name)) for name, _ in gdr_grads_t._fields_])
+    ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
+                       _ptr(write_key), None, None)
+    st = lib().gdr_chunk_bwd(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(d_out),
+                             _ptr(d_state_out), ctypes.byref(grads), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    _raise(st)
+    return g

@@ -196,6 +196,11 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     };
 
     __syncthreads();  // previous chunk done with every buffer
+    const int ci = c0 / a.C;
+    if (a.ws_h != nullptr) {   // the state at this chunk's start, for the backward pass
+      float *hc = a.ws_h + ((sh * a.NC + ci) * Dv + v0) * static_cast<long long>(Dk);
+      for (int idx = tid; idx < nv * Dk; idx += kThreads) hc[idx] = Ss[idx / Dk][idx % Dk];
+    }
     // write keys (the preconditioned ones are formed from the staged keys below)
     const IO *kc = k + row0 * Dk;
     {
@@ -464,6 +469,10 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         *reinterpret_cast<float4 *>(&Tm[i][jg + u]) = make_float4(acc[u], acc[u + 1], acc[u + 2], acc[u + 3]);
       __syncthreads();
     }
+    if (a.ws_t != nullptr && vt == 0) {   // T of this chunk (C x C), for the backward pass
+      float *tc = a.ws_t + (sh * a.NC + ci) * static_cast<long long>(a.C * a.C);
+      for (int idx = tid; idx < a.C * a.C; idx += kThreads) tc[idx] = Tm[idx / a.C][idx % a.C];
+    }
     // queries replace the erase keys (last read before the barrier above)
     {
       const IO *qc = q + row0 * Dk;
@@ -495,10 +504,21 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<float2 *>(&Dl[t0 + u][r0]) = make_float2(acc[u][0], acc[u][1]);
+      if (a.ws_d != nullptr) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int w = 0; w < 2; ++w)
+            if (t0 + u < n && r0 + w < nv) a.ws_d[tok(t0 + u) * Dv + v0 + r0 + w] = acc[u][w];
+      }
     }
     // P (lower incl. diagonal; L is no longer needed)
     gram(true);
     __syncthreads();
+    if (a.ws_p != nullptr && vt == 0) {   // P of this chunk (C x C), for the backward pass
+      float *pc = a.ws_p + (sh * a.NC + ci) * static_cast<long long>(a.C * a.C);
+      for (int idx = tid; idx < a.C * a.C; idx += kThreads) pc[idx] = LP[idx / a.C][idx % a.C];
+    }
     // O = scale ((e^g (.) Q) S^T + P D)
     {
       float acc[2][2] = {};
@@ -529,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
           const int t = t0 + u, r = r0 + w;
-          if (t < n && r < nv) st_f(out, tok(t) * Dv + v0 + r, a.scale * acc[u][w]);
+          if (out != nullptr && t < n && r < nv) st_f(out, tok(t) * Dv + v0 + r, a.scale * acc[u][w]);
         }
     }
     if constexpr (CHD) {   // R <- 2^(G_C - G) (.) R for the update (P, its last other use, is done)

@@ -54,6 +54,29 @@ Range rng(const char *name, const void *p, long double bytes) {
 // Largest element count of any one tensor the library accepts (2^40 elements).
 constexpr long double kMaxElems = 1099511627776.0L;
 
+// Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
+struct BwdLayout {
+  uint64_t h, dh, D, dX, T, P, total;
+  int NC;
+};
+
+BwdLayout bwd_layout(const gdr_desc_t &d) {
+  const uint64_t B = d.B, T = d.T, H = d.H, Dk = d.Dk, Dv = d.Dv, C = d.chunk;
+  const uint64_t NC = (T + C - 1) / C;
+  auto al = [](uint64_t x) { return (x + 255u) & ~static_cast<uint64_t>(255u); };
+  const uint64_t st = al(B * H * NC * Dv * Dk * 4u), tk = al(B * T * H * Dv * 4u), cc = al(B * H * NC * C * C * 4u);
+  BwdLayout L{};
+  L.h = 0;
+  L.dh = st;
+  L.D = 2 * st;
+  L.dX = L.D + tk;
+  L.T = L.dX + tk;
+  L.P = L.T + cc;
+  L.total = L.P + cc;
+  L.NC = static_cast<int>(NC);
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +254,120 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
                  use_mfma ? "mfma" : "generic", d->B, d->T, d->H, d->Dk, d->Dv, d->chunk,
                  d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay, d->wkey, a.N, a.S);
   const hipError_t e = use_mfma ? gdr::launch_chunk_mfma(a, s) : gdr::launch_chunk_generic(a, d->io_dtype, s);
+  if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *d) {
+  if (d == nullptr || d->struct_size != sizeof(gdr_desc_t) || d->B < 1 || d->H < 1 || d->T < 0 ||
+      d->Dk < 1 || d->Dv < 1 || (d->chunk != 16 && d->chunk != 32 && d->chunk != 64))
+    return 0;
+  return bwd_layout(*d).total;
+}
+
+gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                              const void *d_out, const float *d_state_out, const gdr_grads_t *g,
+                              const void *ws, uint64_t ws_bytes) {
+  // the forward's own contract, with d_out in the place of out
+  gdr_status_t st = gdr_validate(d, in, state_in, d_out, nullptr, 0);
+  if (st != GDR_OK) return fail(st, "forward arguments (d_out checked as out): %s", g_last_error.c_str());
+  if (g == nullptr) return fail(GDR_EINVAL, "grads must be non-NULL");
+  if (d->wkey == GDR_WKEY_DIAG_PRECOND) return fail(GDR_ENOTSUP, "backward of the preconditioned write key");
+  if (d->decay == GDR_DECAY_CHANNEL) return fail(GDR_ENOTSUP, "backward of the per-channel decay");
+  if (d->neumann_order >= 0) return fail(GDR_ENOTSUP, "backward of the band-limited T (exact T only)");
+  const bool need = d->T > 0;
+  struct Opt {
+    const char *name;
+    const float *p;
+    bool wanted;
+    long double elems;
+  };
+  const long double B = d->B, T = d->T, H = d->H, Dk = d->Dk, Dv = d->Dv, ntok = B * T * H;
+  const Opt outs[] = {
+      {"dq", g->dq, true, ntok * Dk},
+      {"dk", g->dk, true, ntok * Dk},
+      {"dv", g->dv, true, ntok * Dv},
+      {"dbeta", g->dbeta, d->gain == GDR_GAIN_SCALAR, ntok},
+      {"derase", g->derase, d->gain == GDR_GAIN_CHANNEL, ntok * Dk},
+      {"dwrite", g->dwrite, d->gain == GDR_GAIN_CHANNEL, ntok * Dv},
+      {"dlog_alpha", g->dlog_alpha, d->decay == GDR_DECAY_SCALAR, ntok},
+      {"dwrite_key", g->dwrite_key, d->wkey == GDR_WKEY_EXPLICIT, ntok * Dk},
+  };
+  for (const Opt &o : outs) {
+    if (o.wanted && need && o.p == nullptr) return fail(GDR_EINVAL, "grads->%s is required", o.name);
+    if (!o.wanted && o.p != nullptr) return fail(GDR_EINVAL, "grads->%s given but the variant has no such input", o.name);
+    if ((reinterpret_cast<uintptr_t>(o.p) & 3u) != 0) return fail(GDR_EINVAL, "grads->%s misaligned", o.name);
+  }
+  if ((reinterpret_cast<uintptr_t>(g->dstate_in) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d_state_out) & 3u) != 0)
+    return fail(GDR_EINVAL, "misaligned fp32 state pointer");
+  const uint64_t need_ws = bwd_layout(*d).total;
+  if (ws_bytes < need_ws)
+    return fail(GDR_EINVAL, "workspace_bytes = %llu, need %llu", static_cast<unsigned long long>(ws_bytes),
+                static_cast<unsigned long long>(need_ws));
+  if (need_ws > 0 && ws == nullptr) return fail(GDR_EINVAL, "workspace is required");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(GDR_EINVAL, "workspace must be 256-byte aligned");
+
+  // overlap: every output against every input, every other output and the workspace
+  const long double esz = d->io_dtype == GDR_BF16 ? 2.0L : 4.0L;
+  const Range inputs[] = {
+      rng("q", in->q, ntok * Dk * esz), rng("k", in->k, ntok * Dk * esz),
+      rng("v", in->v, ntok * Dv * esz), rng("beta", in->beta, ntok * 4),
+      rng("log_alpha", in->log_alpha, ntok * 4), rng("erase", in->erase, ntok * Dk * esz),
+      rng("write", in->write, ntok * Dv * esz), rng("write_key", in->write_key, ntok * Dk * esz),
+      rng("state_in", state_in, B * H * Dv * Dk * 4), rng("d_out", d_out, ntok * Dv * esz),
+      rng("d_state_out", d_state_out, B * H * Dv * Dk * 4)};
+  Range written[10];
+  int nw = 0;
+  for (const Opt &o : outs) written[nw++] = rng(o.name, o.p, o.elems * 4);
+  written[nw++] = rng("dstate_in", g->dstate_in, B * H * Dv * Dk * 4);
+  written[nw++] = rng("workspace", ws, static_cast<long double>(need_ws));
+  for (int i = 0; i < nw; ++i) {
+    for (const Range &r : inputs)
+      if (overlap(written[i], r)) return fail(GDR_EINVAL, "%s overlaps %s", written[i].name, r.name);
+    for (int j = i + 1; j < nw; ++j)
+      if (overlap(written[i], written[j])) return fail(GDR_EINVAL, "%s overlaps %s", written[i].name, written[j].name);
+  }
+  return ok();
+}
+
+gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                           const void *d_out, const float *d_state_out, const gdr_grads_t *g,
+                           void *workspace, uint64_t workspace_bytes, void *stream) {
+  gdr_status_t st = gdr_validate_bwd(d, in, state_in, d_out, d_state_out, g, workspace, workspace_bytes);
+  if (st != GDR_OK) return st;
+  const BwdLayout L = bwd_layout(*d);
+  char *ws = static_cast<char *>(workspace);
+  gdr::BwdArgs b{};
+  b.f = make_args(d, in, state_in, nullptr, nullptr);
+  b.NC = L.NC;
+  if (L.total > 0) {
+    b.h = reinterpret_cast<float *>(ws + L.h);
+    b.dh = reinterpret_cast<float *>(ws + L.dh);
+    b.D = reinterpret_cast<float *>(ws + L.D);
+    b.dX = reinterpret_cast<float *>(ws + L.dX);
+    b.Tw = reinterpret_cast<float *>(ws + L.T);
+    b.Pw = reinterpret_cast<float *>(ws + L.P);
+  }
+  b.dout = d_out;
+  b.dstate_out = d_state_out;
+  b.dq = g->dq; b.dk = g->dk; b.dv = g->dv; b.dbeta = g->dbeta;
+  b.derase = g->derase; b.dwrite = g->dwrite; b.dla = g->dlog_alpha; b.dwk = g->dwrite_key;
+  b.dstate_in = g->dstate_in;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[gdr] chunk_bwd B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d ws=%llu\n",
+                 d->B, d->T, d->H, d->Dk, d->Dv, d->chunk, d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain,
+                 d->decay, d->wkey, static_cast<unsigned long long>(L.total));
+  hipError_t e = hipSuccess;
+  if (d->T > 0) {   // 1. forward recompute, saving S at every chunk start, D, T and P
+    gdr::ChunkArgs fa = b.f;
+    fa.ws_h = b.h; fa.ws_d = b.D; fa.ws_t = b.Tw; fa.ws_p = b.Pw; fa.NC = L.NC;
+    e = gdr::launch_chunk_generic(fa, d->io_dtype, s);
+  }
+  if (e == hipSuccess && (d->T > 0 || g->dstate_in != nullptr))   // 2. reverse sweep
+    e = gdr::launch_bwd_sweep(b, d->io_dtype, s);
+  if (e == hipSuccess && d->T > 0)   // 3. per-chunk gradients
+    e = gdr::launch_bwd_chunk(b, d->io_dtype, s);
   if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -30,6 +30,10 @@ the order q, k, v, then the gate logits):
 * erase = sigmoid(N(2, 1))                     [B, T, H, Dk] (channel gain, key axis);
 * write = sigmoid(N(0, 1))                     [B, T, H, Dv] (channel gain, value axis).
 
+Loss gradients for the backward pass (``make_cotangents``, seed ``spec.seed + 7919`` unless
+given): d_out ~ N(0, 1) [B, T, H, Dv] stored like v, and d_state_out ~ N(0, 1) [B, H, Dv, Dk]
+fp32, drawn in that order.
+
 Every value is produced in fp64, cast to fp32, then (for bf16 workloads, and only
 for q, k, v, erase, write) rounded to bf16 with round-to-nearest-even, once.  Both
 the oracle and the GPU path consume exactly those bits.  beta and log_alpha stay
@@ -44,7 +48,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "Spec", "WORKLOADS", "spec", "make_inputs", "make_decode_inputs",
+    "Spec", "WORKLOADS", "spec", "make_inputs", "make_decode_inputs", "make_cotangents",
     "round_to_bf16", "round_to_f32",
 ]
 
@@ -162,3 +166,12 @@ def make_decode_inputs(s: Spec, step: int) -> Dict[str, np.ndarray]:
     """
     rng = np.random.Generator(np.random.PCG64(s.seed + 1 + step))
     return _draw(rng, s, (s.decode_batch, s.H))
+
+
+def make_cotangents(s: Spec, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Loss gradients of one forward call's outputs: d_out [B, T, H, Dv] (stored like v) and
+    d_state_out [B, H, Dv, Dk] fp32."""
+    rng = np.random.Generator(np.random.PCG64(s.seed + 7919 if seed is None else seed))
+    d_out = _store(rng.standard_normal((s.B, s.T, s.H, s.Dv)), s.dtype)
+    d_state_out = round_to_f32(rng.standard_normal((s.B, s.H, s.Dv, s.Dk)))
+    return {"d_out": d_out, "d_state_out": d_state_out}

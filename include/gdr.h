@@ -36,7 +36,8 @@
  *  - Element types: q, k, v, erase, write, write_key and out use io_dtype (fp32 or bf16);
  *    beta, log_alpha, state and pc_h are always fp32.
  *  - Memory: every pointer is a device pointer owned by the caller.  The library never
- *    allocates, frees or keeps a pointer after the call returns, and needs no workspace.
+ *    allocates, frees or keeps a pointer after the call returns.  Only gdr_chunk_bwd needs
+ *    scratch memory, and the caller passes it in (gdr_chunk_bwd_workspace_size).
  *  - Execution: the work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the null stream) and the call returns without synchronising.
  *  - Errors: arguments are validated on the host before anything is enqueued.  On
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum {
   GDR_OK = 0,
@@ -163,6 +164,66 @@ gdr_status_t gdr_recurrent_step(const gdr_desc_t *desc, const gdr_inputs_t *in,
 gdr_status_t gdr_validate(const gdr_desc_t *desc, const gdr_inputs_t *in,
                           const float *state_in, const void *out, const float *state_out,
                           int for_step);
+
+/* Gradients written by gdr_chunk_bwd: fp32 device buffers owned by the caller, laid out
+ * like the inputs they belong to.  Every buffer the descriptor's variant has is required. */
+typedef struct gdr_grads {
+  float *dq;          /* [B,T,H,Dk]                                                       */
+  float *dk;          /* [B,T,H,Dk] (through e and, with wkey SAME, through r = k)         */
+  float *dv;          /* [B,T,H,Dv]                                                       */
+  float *dbeta;       /* [B,T,H]; iff gain == SCALAR, else NULL                            */
+  float *derase;      /* [B,T,H,Dk]; iff gain == CHANNEL, else NULL                        */
+  float *dwrite;      /* [B,T,H,Dv]; iff gain == CHANNEL, else NULL                        */
+  float *dlog_alpha;  /* [B,T,H]; iff decay == SCALAR, else NULL                           */
+  float *dwrite_key;  /* [B,T,H,Dk]; iff wkey == EXPLICIT, else NULL                       */
+  float *dstate_in;   /* [B,H,Dv,Dk] or NULL (not written)                                 */
+} gdr_grads_t;
+
+/*
+ * gdr_chunk_bwd -- gradients of a scalar loss through gdr_chunk_fwd.
+ *
+ * The pages train these layers (Preconditioned DeltaNet summary: chunk-wise forms are what
+ * makes training on GPUs efficient, section 2b; models trained at 340M and 1B parameters,
+ * section 4) but give no backward pass.  This is the derivative of the forward above,
+ * taken through its chunk-wise form ("Declaracao do Problema" of the MatMul-only inversion
+ * summary) in three launches:
+ *   1. forward recompute: the state at every chunk start, D, T and P of every chunk;
+ *   2. reverse sweep over chunks (per value tile): with dS the gradient at the chunk end,
+ *        dD = e^{g_C - g} (.) (R dS^T) + scale P^T dO,   dX = T^T dD   (= dV'),
+ *        dS <- e^{g_C} dS + scale dO^T (e^g (.) Q) - dX^T (e^g (.) E);
+ *   3. per chunk, in parallel: dQ, dE, dR and the gate gradient from the stored states,
+ *      the state gradients, D and dX, then the chain rule to the variant's inputs.
+ * All arithmetic is fp32 (inputs in io_dtype are widened once).
+ *
+ * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR, wkey SAME | EXPLICIT, exact T
+ * (neumann_order < 0), chunk 16 | 32 | 64, Dk <= 128, Dv <= 512, io fp32 | bf16; anything
+ * else returns GDR_ENOTSUP (desc->impl is ignored).
+ *
+ *   in, state_in  the forward's inputs and initial state (NULL for zeros), unchanged.
+ *   d_out         [B,T,H,Dv] io_dtype: dL/dout.  May be NULL only if T == 0.
+ *   d_state_out   [B,H,Dv,Dk] fp32: dL/dstate_out, or NULL for zeros.
+ *   grads         the outputs; none may overlap an input, another output or the workspace.
+ *   workspace     device memory of at least gdr_chunk_bwd_workspace_size(desc) bytes,
+ *                 256-byte aligned, owned by the caller; its contents on entry do not
+ *                 matter and on return are unspecified.  May be NULL if that size is 0.
+ * Enqueued on `stream`; the workspace and the outputs must stay allocated until the work
+ * has run.  Deterministic (no atomics).
+ */
+gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const float *state_in,
+                           const void *d_out, const float *d_state_out, const gdr_grads_t *grads,
+                           void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gdr_chunk_bwd needs for this descriptor (0 if it is rejected or
+ * T == 0): the chunk-start states and their gradients (2 B H ceil(T/C) Dv Dk floats), D
+ * and dX (2 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats), each 256-byte
+ * aligned.  No HIP call. */
+uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
+
+/* gdr_chunk_bwd's argument check on its own (no HIP call). */
+gdr_status_t gdr_validate_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
+                              const float *state_in, const void *d_out, const float *d_state_out,
+                              const gdr_grads_t *grads, const void *workspace,
+                              uint64_t workspace_bytes);
 
 /* Which kernel gdr_chunk_fwd would launch for this descriptor: GDR_IMPL_GENERIC or
  * GDR_IMPL_MFMA, or a negative value if the descriptor is rejected.  No HIP call. */

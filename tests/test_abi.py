@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert G.gdr_abi_version() == 2
+    assert G.gdr_abi_version() == 3
     for s in (G.GDR_OK, G.GDR_EINVAL, G.GDR_ENOTSUP, G.GDR_EHIP):
         assert G.gdr_status_str(s).startswith("GDR_")
     assert "UNKNOWN" in G.gdr_status_str(42)
@@ -41,6 +41,7 @@ def test_struct_layout_matches_header():
     # uint32 + 13 int32 + 4 float = 72 bytes, then the int64: 80
     assert ctypes.sizeof(G.gdr_desc_t) == 80
     assert ctypes.sizeof(G.gdr_inputs_t) == 10 * 8
+    assert ctypes.sizeof(G.gdr_grads_t) == 9 * 8
 
 
 def desc(**kw):
@@ -206,3 +207,119 @@ def test_impl_choice():
     assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=32)) == G.GDR_IMPL_GENERIC
     assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, impl=G.GDR_IMPL_GENERIC)) == G.GDR_IMPL_GENERIC
     assert G.gdr_chunk_fwd_impl(desc(Dk=64, impl=G.GDR_IMPL_MFMA)) == -1
+
+
+# ----------------------------------------------------------------------------------
+# gdr_chunk_bwd: workspace size and host-side validation
+# ----------------------------------------------------------------------------------
+
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T,C", [(100, 64), (64, 64), (1, 16), (4096, 32), (0, 64)])
+def test_bwd_workspace_size_formula(T, C):
+    d = desc(T=T, chunk=C)
+    B, H, Dk, Dv = 2, 3, 64, 32
+    NC = (T + C - 1) // C
+    want = 2 * _al(B * H * NC * Dv * Dk * 4) + 2 * _al(B * T * H * Dv * 4) + 2 * _al(B * H * NC * C * C * 4)
+    assert G.gdr_chunk_bwd_workspace_size(d) == want
+    assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
+
+
+def bwd_args(d, **over):
+    """Well-formed, disjoint fake pointers for a backward call of descriptor d."""
+    p = [BASE + i * MB for i in range(40)]
+    ins = dict(q=p[0], k=p[1], v=p[2])
+    if d.gain == G.GDR_GAIN_SCALAR:
+        ins["beta"] = p[3]
+    else:
+        ins["erase"], ins["write"] = p[4], p[5]
+    if d.decay == G.GDR_DECAY_SCALAR:
+        ins["log_alpha"] = p[6]
+    if d.wkey == G.GDR_WKEY_EXPLICIT:
+        ins["write_key"] = p[7]
+    gr = dict(dq=p[10], dk=p[11], dv=p[12], dstate_in=p[19])
+    if d.gain == G.GDR_GAIN_SCALAR:
+        gr["dbeta"] = p[13]
+    else:
+        gr["derase"], gr["dwrite"] = p[14], p[15]
+    if d.decay == G.GDR_DECAY_SCALAR:
+        gr["dlog_alpha"] = p[16]
+    if d.wkey == G.GDR_WKEY_EXPLICIT:
+        gr["dwrite_key"] = p[17]
+    a = dict(state_in=p[8], d_out=p[9], d_state_out=p[18], workspace=p[24],
+             workspace_bytes=G.gdr_chunk_bwd_workspace_size(d))
+    gr.update(over.pop("grads", {}))
+    ins.update(over.pop("ins", {}))
+    a.update(over)
+    return G.gdr_inputs_t(**ins), G.gdr_grads_t(**gr), a
+
+
+def call_validate_bwd(d, **over):
+    ins, gr, a = bwd_args(d, **over)
+    return G.gdr_validate_bwd(d, ins, a["state_in"], a["d_out"], a["d_state_out"], gr, a["workspace"],
+                              a["workspace_bytes"])
+
+
+@pytest.mark.parametrize("gain", [G.GDR_GAIN_SCALAR, G.GDR_GAIN_CHANNEL])
+@pytest.mark.parametrize("decay", [G.GDR_DECAY_NONE, G.GDR_DECAY_SCALAR])
+@pytest.mark.parametrize("wkey", [G.GDR_WKEY_SAME, G.GDR_WKEY_EXPLICIT])
+def test_bwd_accepts_supported_variants(gain, decay, wkey):
+    d = desc(gain=gain, decay=decay, wkey=wkey)
+    assert call_validate_bwd(d) == G.GDR_OK, G.gdr_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(wkey=G.GDR_WKEY_DIAG_PRECOND), dict(decay=G.GDR_DECAY_CHANNEL),
+                                dict(neumann_order=3)])
+def test_bwd_rejects_unsupported_variants(kw):
+    d = desc(**kw)
+    ins, gr, a = bwd_args(d)
+    if kw.get("decay") == G.GDR_DECAY_CHANNEL:
+        ins.log_alpha = BASE + 6 * MB
+    assert G.gdr_validate_bwd(d, ins, None, a["d_out"], None, gr, a["workspace"],
+                              a["workspace_bytes"]) == G.GDR_ENOTSUP, G.gdr_last_error()
+
+
+def test_bwd_rejects_missing_and_extra_grads():
+    d = desc(decay=G.GDR_DECAY_SCALAR)
+    assert call_validate_bwd(d, grads=dict(dk=None)) == G.GDR_EINVAL
+    assert "dk" in G.gdr_last_error()
+    assert call_validate_bwd(d, grads=dict(dlog_alpha=None)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, grads=dict(derase=BASE + 30 * MB)) == G.GDR_EINVAL
+    assert call_validate_bwd(desc(), grads=dict(dlog_alpha=BASE + 30 * MB)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, grads=dict(dstate_in=None), d_state_out=None, state_in=None) == G.GDR_OK
+    assert call_validate_bwd(d, d_out=None) == G.GDR_EINVAL
+
+
+def test_bwd_workspace_checks():
+    d = desc()
+    need = G.gdr_chunk_bwd_workspace_size(d)
+    assert call_validate_bwd(d, workspace_bytes=need - 1) == G.GDR_EINVAL
+    assert "workspace" in G.gdr_last_error()
+    assert call_validate_bwd(d, workspace=BASE + 24 * MB + 128) == G.GDR_EINVAL
+    assert call_validate_bwd(d, workspace=None) == G.GDR_EINVAL
+    # T == 0 needs none
+    d0 = desc(T=0)
+    assert G.gdr_chunk_bwd_workspace_size(d0) == 0
+    ins, gr, a = bwd_args(d0)
+    assert G.gdr_validate_bwd(d0, ins, None, None, None, gr, None, 0) == G.GDR_OK, G.gdr_last_error()
+
+
+def test_bwd_overlap_rules():
+    d = desc()
+    # an output on an input, on another output, on the workspace
+    assert call_validate_bwd(d, grads=dict(dq=BASE + 0 * MB)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, grads=dict(dk=BASE + 10 * MB + 64)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, grads=dict(dv=BASE + 24 * MB + 4096)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, grads=dict(dstate_in=BASE + 18 * MB)) == G.GDR_EINVAL
+    # the workspace on an input
+    assert call_validate_bwd(d, workspace=BASE + 9 * MB) == G.GDR_EINVAL
+
+
+def test_bwd_entry_point_rejects_before_launch():
+    d = desc()
+    ins, gr, a = bwd_args(d, grads=dict(dq=None))
+    st = G.lib().gdr_chunk_bwd(ctypes.byref(d), ctypes.byref(ins), None, a["d_out"], None, ctypes.byref(gr),
+                               a["workspace"], a["workspace_bytes"], None)
+    assert st == G.GDR_EINVAL

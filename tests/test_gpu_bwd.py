@@ -1,0 +1,164 @@
+"""GPU parity of gdr_chunk_bwd against the fp64 oracle's gradients (``oracle.backward``).
+
+The backward computes in fp32 whatever the io dtype (bf16 inputs are widened exactly), so
+every gradient is held to the fp32 bound: rel-L2 <= 1e-4 over each gradient tensor.  Every
+test prints the case it runs before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import gdr_synth as gs
+import oracle as O
+from _gpu_util import TOL_F32, dev, host, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+GRAD_NAMES = ["dq", "dk", "dv", "dbeta", "derase", "dwrite", "dlog_alpha", "dwrite_key", "dstate_in"]
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def spec(variant, **kw):
+    base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "explicit": "gdn",
+            "gdn2_decay": "gdn2"}[variant]
+    over = dict(B=2, H=2, T=200, Dk=64, Dv=48, dtype="f32", seed=21)
+    over.update(kw)
+    if variant == "explicit":
+        over["wkey"] = "explicit"
+    if variant == "gdn2_decay":
+        over["decay"] = "scalar"
+    return gs.spec(base, **over)
+
+
+def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None):
+    import torch
+    import chunked_gated_delta_gdr_amd as G
+    io = torch_dtype(s.dtype)
+    f32 = torch.float32
+    g = G.gdr_chunk_bwd(
+        dev(x["q"], io), dev(x["k"], io), dev(x["v"], io), dev(cot["d_out"], io),
+        beta=dev(x.get("beta"), f32), log_alpha=dev(x.get("log_alpha"), f32),
+        erase=dev(x.get("erase"), io), write=dev(x.get("write"), io),
+        write_key=dev(x.get("write_key"), io), state_in=dev(state_in, f32),
+        d_state_out=dev(cot["d_state_out"], f32) if d_state_out else None,
+        chunk=chunk or s.chunk, scale=scale)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in g.items()}
+
+
+def oracle_grads(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, streams=None,
+                 checkpoint=0):
+    g = O.recurrent_grad(x, cot["d_out"], cot["d_state_out"] if d_state_out else None,
+                         scale=scale, state0=state_in, streams=streams, checkpoint=checkpoint)
+    g["dstate_in"] = g.pop("dS0")
+    return g
+
+
+def compare(got, ref, streams=None, tol=TOL_F32):
+    assert set(got) == set(ref), (sorted(got), sorted(ref))
+    for name in GRAD_NAMES:
+        if name not in ref:
+            continue
+        a, b = got[name], ref[name]
+        if streams is not None:
+            if name == "dstate_in":
+                a = np.stack([a[bb, hh] for bb, hh in streams])
+                b = np.stack([b[bb, hh] for bb, hh in streams])
+            else:
+                a = np.stack([a[bb, :, hh] for bb, hh in streams])
+                b = np.stack([b[bb, :, hh] for bb, hh in streams])
+        assert np.all(np.isfinite(a)), name
+        err = O.rel_l2(a, b)
+        print(f"  {name}: rel-L2 {err:.2e}", flush=True)
+        assert err <= tol, (name, err)
+
+
+def state(s, seed=5, amp=0.3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * amp).astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "explicit", "gdn2_decay"])
+def test_bwd_variants_fp32(variant):
+    s = spec(variant)
+    announce(f"bwd {variant} f32 {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    got = run_bwd(s, x, cot, state_in=S0, scale=0.8)
+    compare(got, oracle_grads(s, x, cot, state_in=S0, scale=0.8))
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2_decay"])
+def test_bwd_chunk_sizes(variant, chunk):
+    s = spec(variant, T=77, chunk=chunk)
+    announce(f"bwd {variant} f32 chunk {chunk} {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (32, 16), (16, 200)])
+def test_bwd_head_dims(Dk, Dv):
+    s = spec("gdn", Dk=Dk, Dv=Dv, T=130)
+    announce(f"bwd gdn f32 Dk={Dk} Dv={Dv} {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "explicit"])
+def test_bwd_bf16(variant):
+    s = spec(variant, dtype="bf16", Dk=128, Dv=128, T=200)
+    announce(f"bwd {variant} bf16 {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65])
+def test_bwd_short_and_ragged(T):
+    s = spec("gdn", T=T)
+    announce(f"bwd gdn f32 T={T}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+def test_bwd_zero_state_and_no_state_gradient():
+    s = spec("gdn2_decay", T=150)
+    announce(f"bwd gdn2_decay f32 no state_in, no d_state_out {s}")
+    x, cot = gs.make_inputs(s), gs.make_cotangents(s)
+    got = run_bwd(s, x, cot, state_in=None, d_state_out=False)
+    compare(got, oracle_grads(s, x, cot, state_in=None, d_state_out=False))
+
+
+def test_bwd_empty_sequence():
+    """T = 0: no token gradients, and dL/dstate_in = dL/dstate_out."""
+    s = spec("gdn", T=0)
+    announce("bwd gdn f32 T=0")
+    x, cot = gs.make_inputs(s), gs.make_cotangents(s)
+    got = run_bwd(s, x, cot, state_in=state(s))
+    np.testing.assert_array_equal(got["dstate_in"], cot["d_state_out"])
+    assert got["dq"].size == 0 and got["dlog_alpha"].size == 0
+
+
+def test_bwd_is_deterministic():
+    s = spec("gdn", T=150)
+    announce("bwd gdn f32 twice, bitwise")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    a = run_bwd(s, x, cot, state_in=S0)
+    b = run_bwd(s, x, cot, state_in=S0)
+    for name in a:
+        np.testing.assert_array_equal(a[name], b[name])
+
+
+def test_bwd_full_size_gdn_sampled():
+    """The gdn workload at full size (B4 H16 T4096 d128 bf16): two streams against the oracle
+    (checkpointed reverse sweep), every gradient finite everywhere."""
+    s = gs.spec("gdn")
+    streams = [(0, 0), (3, 15)]
+    announce(f"bwd gdn full size {s}, streams {streams}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s, amp=0.1)
+    got = run_bwd(s, x, cot, state_in=S0)
+    for name, val in got.items():
+        assert np.all(np.isfinite(val)), name
+    ref = oracle_grads(s, x, cot, state_in=S0, streams=streams, checkpoint=64)
+    compare(got, ref, streams=streams)
