@@ -24,11 +24,6 @@ struct ChunkArgs {
   int S;                      // residual-correction steps on the band start (0: none)
   float scale, rho, log_rho, eps, h0;
   long long t0;
-  // Saved for the backward pass when non-null (generic kernel only; NC = chunks per
-  // stream): the state at every chunk start [B,H,NC,Dv,Dk], D [B,T,H,Dv], and T and P of
-  // every chunk [B,H,NC,C,C].  out may then be null (no output is written).
-  float *ws_h, *ws_d, *ws_t, *ws_p;
-  int NC;
 };
 
 // Backward pass (gdr_chunk_bwd): the forward's arguments plus the incoming gradients, the
@@ -38,8 +33,10 @@ struct BwdArgs {
   const void *dout;          // [B,T,H,Dv] io dtype
   const float *dstate_out;   // [B,H,Dv,Dk] or null (zero)
   float *dq, *dk, *dv, *dbeta, *derase, *dwrite, *dla, *dwk, *dstate_in;
-  float *h, *dh, *D, *dX, *Tw, *Pw;
-  int NC;
+  // workspace: states at chunk starts and their gradients [B,H,NC,Dv,Dk], D and dX
+  // [B,T,H,Dv], T and P [B,H,NC,C,C], W [B,H,NC,C,Dk], U [B,T,H,Dv]
+  float *h, *dh, *D, *dX, *Tw, *Pw, *Ww, *Uw;
+  int NC;   // chunks per stream
 };
 
 // Host launchers (return hipSuccess or the launch error).
@@ -48,6 +45,7 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in,
                          const void *out, const float *state_out);
 hipError_t launch_step(const ChunkArgs &a, int io_dtype, hipStream_t s);
+hipError_t launch_bwd_prep_state(const BwdArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int io_dtype, hipStream_t s);
 

@@ -56,7 +56,7 @@ constexpr long double kMaxElems = 1099511627776.0L;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
-  uint64_t h, dh, D, dX, T, P, total;
+  uint64_t h, dh, D, dX, T, P, W, U, total;
   int NC;
 };
 
@@ -72,7 +72,9 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   L.dX = L.D + tk;
   L.T = L.dX + tk;
   L.P = L.T + cc;
-  L.total = L.P + cc;
+  L.W = L.P + cc;
+  L.U = L.W + al(B * H * NC * C * Dk * 4u);
+  L.total = L.U + tk;
   L.NC = static_cast<int>(NC);
   return L;
 }
@@ -347,6 +349,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
     b.dX = reinterpret_cast<float *>(ws + L.dX);
     b.Tw = reinterpret_cast<float *>(ws + L.T);
     b.Pw = reinterpret_cast<float *>(ws + L.P);
+    b.Ww = reinterpret_cast<float *>(ws + L.W);
+    b.Uw = reinterpret_cast<float *>(ws + L.U);
   }
   b.dout = d_out;
   b.dstate_out = d_state_out;
@@ -359,11 +363,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
                  d->B, d->T, d->H, d->Dk, d->Dv, d->chunk, d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain,
                  d->decay, d->wkey, static_cast<unsigned long long>(L.total));
   hipError_t e = hipSuccess;
-  if (d->T > 0) {   // 1. forward recompute, saving S at every chunk start, D, T and P
-    gdr::ChunkArgs fa = b.f;
-    fa.ws_h = b.h; fa.ws_d = b.D; fa.ws_t = b.Tw; fa.ws_p = b.Pw; fa.NC = L.NC;
-    e = gdr::launch_chunk_generic(fa, d->io_dtype, s);
-  }
+  if (d->T > 0)   // 1. forward recompute: T, P, W, U of every chunk, then D and the chunk states
+    e = gdr::launch_bwd_prep_state(b, d->io_dtype, s);
   if (e == hipSuccess && (d->T > 0 || g->dstate_in != nullptr))   // 2. reverse sweep
     e = gdr::launch_bwd_sweep(b, d->io_dtype, s);
   if (e == hipSuccess && d->T > 0)   // 3. per-chunk gradients

@@ -186,12 +186,13 @@ typedef struct gdr_grads {
  * makes training on GPUs efficient, section 2b; models trained at 340M and 1B parameters,
  * section 4) but give no backward pass.  This is the derivative of the forward above,
  * taken through its chunk-wise form ("Declaracao do Problema" of the MatMul-only inversion
- * summary) in three launches:
- *   1. forward recompute: the state at every chunk start, D, T and P of every chunk;
- *   2. reverse sweep over chunks (per value tile): with dS the gradient at the chunk end,
+ * summary) in four launches:
+ *   1. per chunk, in parallel: T, P, W = T (e^g (.) E) and U = T V';
+ *   2. forward state pass (per value tile): D = U - W S^T and the state at every chunk start;
+ *   3. reverse sweep over chunks (per value tile): with dS the gradient at the chunk end,
  *        dD = e^{g_C - g} (.) (R dS^T) + scale P^T dO,   dX = T^T dD   (= dV'),
  *        dS <- e^{g_C} dS + scale dO^T (e^g (.) Q) - dX^T (e^g (.) E);
- *   3. per chunk, in parallel: dQ, dE, dR and the gate gradient from the stored states,
+ *   4. per chunk, in parallel: dQ, dE, dR and the gate gradient from the stored states,
  *      the state gradients, D and dX, then the chain rule to the variant's inputs.
  * All arithmetic is fp32 (inputs in io_dtype are widened once).
  *
@@ -214,9 +215,9 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
                            void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* Bytes of workspace gdr_chunk_bwd needs for this descriptor (0 if it is rejected or
- * T == 0): the chunk-start states and their gradients (2 B H ceil(T/C) Dv Dk floats), D
- * and dX (2 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats), each 256-byte
- * aligned.  No HIP call. */
+ * T == 0): the chunk-start states and their gradients (2 B H ceil(T/C) Dv Dk floats), D,
+ * dX and U (3 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats) and W
+ * (B H ceil(T/C) C Dk floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 
 /* gdr_chunk_bwd's argument check on its own (no HIP call). */

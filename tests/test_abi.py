@@ -222,7 +222,8 @@ def test_bwd_workspace_size_formula(T, C):
     d = desc(T=T, chunk=C)
     B, H, Dk, Dv = 2, 3, 64, 32
     NC = (T + C - 1) // C
-    want = 2 * _al(B * H * NC * Dv * Dk * 4) + 2 * _al(B * T * H * Dv * 4) + 2 * _al(B * H * NC * C * C * 4)
+    want = (2 * _al(B * H * NC * Dv * Dk * 4) + 3 * _al(B * T * H * Dv * 4) + 2 * _al(B * H * NC * C * C * 4)
+            + _al(B * H * NC * C * Dk * 4))
     assert G.gdr_chunk_bwd_workspace_size(d) == want
     assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
 
