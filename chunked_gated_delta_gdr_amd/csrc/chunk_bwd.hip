@@ -45,11 +45,27 @@ __device__ __forceinline__ float at(const float4 &v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
+// W consecutive floats (W = 2 or 4, aligned to 4 W bytes) into registers
+template <int W>
+__device__ __forceinline__ void ldw(const float *p, float (&x)[W]) {
+  if constexpr (W == 4) {
+    const float4 v = ld4(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+    const float2 v = ld2(p);
+    x[0] = v.x; x[1] = v.y;
+  }
+}
+
+// log alpha of token `lane` of the chunk starting at token row row0 (0 past n or without decay)
+__device__ __forceinline__ float chunk_log_alpha(const ChunkArgs &f, long long row0, int n, int lane) {
+  return (f.decay == GDR_DECAY_SCALAR && lane < n) ? f.log_alpha[row0 + static_cast<long long>(lane) * f.H] : 0.f;
+}
+
 // g (inclusive cumulative sum of log alpha over tokens 0..n-1, flat past n), e^g and
-// e^{g_{n-1} - g} of one chunk; called by the first wave.
-__device__ __forceinline__ void chunk_gates(const ChunkArgs &f, long long row0, int n, int lane,
-                                            float *gs, float *eg, float *wd) {
-  float g = (f.decay == GDR_DECAY_SCALAR && lane < n) ? f.log_alpha[row0 + static_cast<long long>(lane) * f.H] : 0.f;
+// e^{g_{n-1} - g} of one chunk from lane's log alpha `la`; called by the first wave.
+__device__ __forceinline__ void chunk_gates_from(float la, int n, int lane, float *gs, float *eg, float *wd) {
+  float g = la;
 #pragma unroll
   for (int d = 1; d < kCMax; d <<= 1) {
     const float y = __shfl_up(g, d, kCMax);
@@ -61,17 +77,24 @@ __device__ __forceinline__ void chunk_gates(const ChunkArgs &f, long long row0, 
   wd[lane] = expf(glast - g);
 }
 
+__device__ __forceinline__ void chunk_gates(const ChunkArgs &f, long long row0, int n, int lane,
+                                            float *gs, float *eg, float *wd) {
+  chunk_gates_from(chunk_log_alpha(f, row0, n, lane), n, lane, gs, eg, wd);
+}
+
 // ---------------------------------------------------------------------------------------
 // Chunk preparation: one workgroup per (batch, head, chunk), all chunks at once.  Everything
 // of a chunk that does not depend on the state: T = (I + L)^-1 and P (C x C, for the sweep),
 // W = T (e^g (.) E) (C x Dk) and U = T V' (C x Dv, for the state pass).
 // ---------------------------------------------------------------------------------------
+constexpr int kPrThreads = 512;
+
 template <typename IO, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
-  static_assert(DK == 64 || DK == 128, "channel groups of 64");
+__global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
+  static_assert(DK == 64 || DK == 128, "32 channel groups of 2 or 4");
+  constexpr int kThreads = kPrThreads;
   constexpr int LD = DK + 4;
-  constexpr int NG = DK / 64;
-  constexpr int CW = 4 * NG;
+  constexpr int CW = DK / 32;
   constexpr int kLoadIt = kCMax * DK / kThreads;
   const ChunkArgs &f = a.f;
   const IO *__restrict__ q = static_cast<const IO *>(f.q);
@@ -127,37 +150,38 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
+  // thread (ti, cj): rows 4 ti .. 4 ti + 3 and columns 2 cj, 2 cj + 1 of the C x C products;
+  // rows 4 ti .. and columns CW cj .. CW cj + CW - 1 of W and U
+  const int ti = tid >> 5, cj = tid & 31;
   // LP[i][j] = exp(g_i - g_j) (X_i . R_j) for j < i (or j <= i), zero elsewhere
-  const int bi = tid >> 4, bj = tid & 15;
   auto gram = [&](const float(*X)[LD], bool incl_diag) {
-    float acc[4][4] = {};
-    if (bj <= bi) {
+    float acc[4][2] = {};
+    if (2 * cj <= 4 * ti + 3) {
 #pragma unroll 4
       for (int c = 0; c < DK; c += 4) {
-        float4 x[4], r[4];
+        float4 x[4], r[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[u] = ld4(&X[4 * bi + u][c]);
-          r[u] = ld4(&Rs[4 * bj + u][c]);
-        }
+        for (int u = 0; u < 4; ++u) x[u] = ld4(&X[4 * ti + u][c]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) r[w] = ld4(&Rs[2 * cj + w][c]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) fma4(acc[u][w], x[u], r[w]);
+          for (int w = 0; w < 2; ++w) fma4(acc[u][w], x[u], r[w]);
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int i = 4 * bi + u, j = 4 * bj + w;
+      for (int w = 0; w < 2; ++w) {
+        const int i = 4 * ti + u, j = 2 * cj + w;
         const bool keep = j < i || (incl_diag && j == i);
         LP[i][j] = keep ? expf(gs[i] - gs[j]) * acc[u][w] : 0.f;
       }
   };
   gram(Es, false);
   __syncthreads();
-  tri::inverse_blocks(LP, Tm, Zs, -1, tid);
+  tri::inverse_blocks(LP, Tm, Zs, -1, tid, tid < 256);
   gram(Xs, true);
   __syncthreads();
   {   // T and P of the chunk (C x C) for the sweep
@@ -167,8 +191,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
       a.Pw[cc + idx] = LP[idx / C][idx % C];
     }
   }
-  // thread (ti, cj): rows 4 ti .. 4 ti + 3, columns 64 g + 4 cj .. + 3 of W and U
-  const int ti = tid >> 4, cj = tid & 15;
+  const int ch0 = CW * cj;
   // acc = T[rows] (Y (.) s) over the thread's columns, with row s of Y scaled by scl(s)
   auto tri_product = [&](const float(*Y)[LD], auto &&scl, float (&acc)[4][CW]) {
 #pragma unroll
@@ -178,17 +201,14 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
     const int send = min(4 * ti + 4, n);
 #pragma unroll 4
     for (int s0 = 0; s0 < send; ++s0) {
-      float4 y[NG];
+      float y[CW];
       const float sc = scl(s0);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) y[g] = ld4(&Y[s0][64 * g + 4 * cj]);
+      ldw<CW>(&Y[s0][ch0], y);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float tv = sc * Tm[4 * ti + u][s0];   // zero above the diagonal
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[u][4 * g + e] = fmaf(tv, at(y[g], e), acc[u][4 * g + e]);
+        for (int e = 0; e < CW; ++e) acc[u][e] = fmaf(tv, y[e], acc[u][e]);
       }
     }
   };
@@ -201,12 +221,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
       const int t = 4 * ti + u;
       if (t >= n) continue;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = 64 * g + 4 * cj + e;
-          if (c < Dk) Wc[static_cast<long long>(t) * Dk + c] = acc[u][4 * g + e];
-        }
+      for (int e = 0; e < CW; ++e)
+        if (ch0 + e < Dk) Wc[static_cast<long long>(t) * Dk + ch0 + e] = acc[u][e];
     }
   }
   // U = T V' by blocks of DK value columns, [B, T, H, Dv]
@@ -237,12 +253,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
       const int t = 4 * ti + u;
       if (t >= n) continue;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = vb + 64 * g + 4 * cj + e;
-          if (c < Dv) a.Uw[tok(t) * Dv + c] = acc[u][4 * g + e];
-        }
+      for (int e = 0; e < CW; ++e) {
+        const int c = vb + ch0 + e;
+        if (c < Dv) a.Uw[tok(t) * Dv + c] = acc[u][e];
+      }
     }
   }
 }
@@ -351,29 +365,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     __syncthreads();
-    // S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R: thread (row r, columns c .. c + 3)
+    // S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R: thread (rows r + RS m for m < NR, columns
+    // c .. c + 3); each row of R read from LDS serves all NR rows
     {
       const float gl = eg[n - 1];
       constexpr int NC4 = DK / 4;
+      constexpr int NR = (kBV * NC4 + kThreads - 1) / kThreads;
+      constexpr int RS = kThreads / NC4;
+      const int r = tid / NC4, c = (tid % NC4) * 4;
+      if (r < RS && r < kBV) {
+        float4 acc[NR];
 #pragma unroll
-      for (int u0 = 0; u0 < kBV * NC4; u0 += kThreads) {
-        const int u = u0 + tid;
-        if (kBV * NC4 % kThreads != 0 && u >= kBV * NC4) break;
-        const int r = u / NC4, c = (u % NC4) * 4;
-        const float4 s = ld4(&Ss[r][c]);
-        float4 acc = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        for (int m = 0; m < NR; ++m) {
+          const float4 s = r + RS * m < kBV ? ld4(&Ss[r + RS * m][c]) : make_float4(0.f, 0.f, 0.f, 0.f);
+          acc[m] = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        }
         // rows past n hold zeros, so the sum may run to the next multiple of 8
         for (int j0 = 0; j0 < n; j0 += 8) {
 #pragma unroll
           for (int j = j0; j < j0 + 8; ++j) {
-            const float w = Dl[j][r];
-            acc.x = fmaf(w, ld_f(&Rs[j][c], 0), acc.x);
-            acc.y = fmaf(w, ld_f(&Rs[j][c], 1), acc.y);
-            acc.z = fmaf(w, ld_f(&Rs[j][c], 2), acc.z);
-            acc.w = fmaf(w, ld_f(&Rs[j][c], 3), acc.w);
+            const float r0f = ld_f(&Rs[j][c], 0), r1f = ld_f(&Rs[j][c], 1);
+            const float r2f = ld_f(&Rs[j][c], 2), r3f = ld_f(&Rs[j][c], 3);
+#pragma unroll
+            for (int m = 0; m < NR; ++m) {
+              const float w = Dl[j][min(r + RS * m, kBV - 1)];
+              acc[m].x = fmaf(w, r0f, acc[m].x);
+              acc[m].y = fmaf(w, r1f, acc[m].y);
+              acc[m].z = fmaf(w, r2f, acc[m].z);
+              acc[m].w = fmaf(w, r3f, acc[m].w);
+            }
           }
         }
-        *reinterpret_cast<float4 *>(&Ss[r][c]) = acc;
+#pragma unroll
+        for (int m = 0; m < NR; ++m)
+          if (r + RS * m < kBV) *reinterpret_cast<float4 *>(&Ss[r + RS * m][c]) = acc[m];
       }
     }
   }
@@ -424,48 +449,58 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     dS[r][c] = s;
   }
   const int t0 = 2 * (tid >> 4), r0 = 2 * (tid & 15);   // 2 x 2 block of the C x kBV tiles
+  // Loads of chunk ci into registers (indices clamped into the chunk, masks applied when they
+  // are written to LDS): write keys, keys, gains, T, P and dO are loaded one chunk ahead, so
+  // they are in flight during the previous chunk's products; the queries, needed only after
+  // the first two barriers of a chunk, are loaded at its start.
+  constexpr int kCC = kCMax * kCMax / kThreads, kOIt = kCMax * kBV / kThreads;
+  float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xq[kLoadIt], xt[kCC], xp[kCC], xo[kOIt], xla = 0.f;
+  const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
+  auto cload = [&](int ci) {
+    const int c0 = ci * C, n = min(C, T - c0);
+    const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
+    if (tid < kCMax) xla = chunk_log_alpha(f, row0, n, tid);
+    const IO *rsrc = rbase + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
+    const float *bc = f.beta + row0;
+#pragma unroll
+    for (int it = 0; it < kLoadIt; ++it) {
+      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+      const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
+      xr[it] = ld_f(rsrc, o);
+      xk[it] = ld_f(kc, o);
+      xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
+    }
+    const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
+#pragma unroll
+    for (int it = 0; it < kCC; ++it) {
+      const int idx = min(tid + it * kThreads, C * C - 1);
+      xt[it] = a.Tw[cc + idx];
+      xp[it] = a.Pw[cc + idx];
+    }
+#pragma unroll
+    for (int it = 0; it < kOIt; ++it) {
+      const int idx = tid + it * kThreads, t = min(idx / kBV, n - 1), r = min(idx % kBV, nv - 1);
+      xo[it] = ld_f(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + r);
+    }
+  };
+  if (a.NC > 0) cload(a.NC - 1);
 
   for (int ci = a.NC - 1; ci >= 0; --ci) {
     const int c0 = ci * C;
     const int n = min(C, T - c0);
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
     const long long row0 = tok(0);
-    const int rstride = H * Dk;
 
     __syncthreads();   // previous chunk done with every buffer
-    // Every load of the chunk is issued before the first LDS store (indices clamped into the
-    // chunk, masks applied afterwards), so they are in flight together: write keys, keys,
-    // gains, queries (kept in registers until the write keys are dead), T, P and dO.
-    constexpr int kCC = kCMax * kCMax / kThreads, kOIt = kCMax * kBV / kThreads;
-    float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xq[kLoadIt], xt[kCC], xp[kCC], xo[kOIt];
     {
-      const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
-      const IO *kc = k + row0 * Dk, *qc = q + row0 * Dk;
-      const IO *ec = er + row0 * Dk;
-      const float *bc = f.beta + row0;
+      const IO *qc = q + row0 * Dk;
 #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
         const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        const int tc = min(t, n - 1), o = tc * rstride + min(c, Dk - 1);
-        xr[it] = ld_f(rsrc, o);
-        xk[it] = ld_f(kc, o);
-        xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-        xq[it] = ld_f(qc, o);
-      }
-      const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
-#pragma unroll
-      for (int it = 0; it < kCC; ++it) {
-        const int idx = min(tid + it * kThreads, C * C - 1);
-        xt[it] = a.Tw[cc + idx];
-        xp[it] = a.Pw[cc + idx];
-      }
-#pragma unroll
-      for (int it = 0; it < kOIt; ++it) {
-        const int idx = tid + it * kThreads, t = min(idx / kBV, n - 1), r = min(idx % kBV, nv - 1);
-        xo[it] = ld_f(dout, tok(t) * Dv + v0 + r);
+        xq[it] = ld_f(qc, min(t, n - 1) * H * Dk + min(c, Dk - 1));
       }
     }
-    if (tid < kCMax) chunk_gates(f, row0, n, tid, gs, eg, wd);
+    if (tid < kCMax) chunk_gates_from(xla, n, tid, gs, eg, wd);
     {   // the gradient at this chunk's end, for the per-chunk pass
       float *dhc = a.dh + ((sh * a.NC + ci) * Dv + v0) * static_cast<long long>(Dk);
       for (int idx = tid; idx < nv * Dk; idx += kThreads) dhc[idx] = dS[idx / Dk][idx % Dk];
@@ -490,6 +525,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       const int idx = tid + it * kThreads, t = idx / kBV, r = idx % kBV;
       dOs[t][r] = (t < n && r < nv) ? xo[it] : 0.f;
     }
+    if (ci > 0) cload(ci - 1);   // in flight during this chunk's products
     __syncthreads();
     // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO on the thread's 2 x 2 block
     {
@@ -559,29 +595,39 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       Ks[t][c] = (t < n && c < Dk) ? xq[it] : 0.f;
     }
     __syncthreads();
-    // dS <- e^{g_n} dS + A^T Q - B^T E: thread (row r, columns c .. c + 3)
+    // dS <- e^{g_n} dS + A^T Q - B^T E: thread (rows r + 8 m for m < NR, columns c .. c + 3);
+    // each row of Q and E read from LDS serves all NR rows
     {
       const float gl = eg[n - 1];
       constexpr int NC4 = DK / 4;
+      constexpr int NR = (kBV * NC4 + kThreads - 1) / kThreads;   // rows per thread
+      constexpr int RS = kThreads / NC4;                          // row step between them
+      const int r = tid / NC4, c = (tid % NC4) * 4;
+      if (r < RS && r < kBV) {
+        float4 acc[NR];
 #pragma unroll
-      for (int u0 = 0; u0 < kBV * NC4; u0 += kThreads) {
-        const int u = u0 + tid;
-        if (kBV * NC4 % kThreads != 0 && u >= kBV * NC4) break;
-        const int r = u / NC4, c = (u % NC4) * 4;
-        const float4 s = ld4(&dS[r][c]);
-        float4 acc = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        for (int m = 0; m < NR; ++m) {
+          const float4 s = r + RS * m < kBV ? ld4(&dS[r + RS * m][c]) : make_float4(0.f, 0.f, 0.f, 0.f);
+          acc[m] = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+        }
         for (int j0 = 0; j0 < n; j0 += 8) {
 #pragma unroll
           for (int j = j0; j < j0 + 8; ++j) {
-            const float am = Am[j][r], bm = Bm[j][r];
             const float4 qq = ld4(&Ks[j][c]), ee = ld4(&Es[j][c]);
-            acc.x = fmaf(am, qq.x, fmaf(-bm, ee.x, acc.x));
-            acc.y = fmaf(am, qq.y, fmaf(-bm, ee.y, acc.y));
-            acc.z = fmaf(am, qq.z, fmaf(-bm, ee.z, acc.z));
-            acc.w = fmaf(am, qq.w, fmaf(-bm, ee.w, acc.w));
+#pragma unroll
+            for (int m = 0; m < NR; ++m) {
+              const int rr = min(r + RS * m, kBV - 1);
+              const float am = Am[j][rr], bm = Bm[j][rr];
+              acc[m].x = fmaf(am, qq.x, fmaf(-bm, ee.x, acc[m].x));
+              acc[m].y = fmaf(am, qq.y, fmaf(-bm, ee.y, acc[m].y));
+              acc[m].z = fmaf(am, qq.z, fmaf(-bm, ee.z, acc[m].z));
+              acc[m].w = fmaf(am, qq.w, fmaf(-bm, ee.w, acc[m].w));
+            }
           }
         }
-        *reinterpret_cast<float4 *>(&dS[r][c]) = acc;
+#pragma unroll
+        for (int m = 0; m < NR; ++m)
+          if (r + RS * m < kBV) *reinterpret_cast<float4 *>(&dS[r + RS * m][c]) = acc[m];
       }
     }
   }
@@ -595,16 +641,19 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-chunk pass: one workgroup per (batch, head, chunk).  Thread (ti, cj) owns tokens
-// 4 ti .. 4 ti + 3 and key channels 64 g + 4 cj .. + 3 of the C x Dk gradients, and the
-// 4 x 4 block (tokens 4 ti.., tokens 4 cj..) of the C x C ones.
+// Per-chunk pass: one workgroup of kCkThreads per (batch, head, chunk).  Thread (ti, cj)
+// owns tokens 4 ti .. 4 ti + 3 and key channels CW cj .. CW cj + CW - 1 of the C x Dk
+// gradients, and the 4 x 2 block (tokens 4 ti.., tokens 2 cj..) of the C x C ones.
 // ---------------------------------------------------------------------------------------
+constexpr int kCkThreads = 512;
+
 template <typename IO, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
-  static_assert(DK == 64 || DK == 128, "channel groups of 64");
+__global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
+  static_assert(DK == 64 || DK == 128, "32 channel groups of 2 or 4");
+  constexpr int kThreads = kCkThreads;
+  constexpr int kWaves = kThreads / 64;
   constexpr int LD = DK + 4;
-  constexpr int NG = DK / 64;      // float4 channel groups per thread
-  constexpr int CW = 4 * NG;       // channels per thread
+  constexpr int CW = DK / 32;      // channels per thread
   constexpr int kVB = 16;          // value rows per step of the value loop
   constexpr int LT = kCMax + 4;    // row stride of [value][token] and C x C tiles
   constexpr int kLoadIt = kCMax * DK / kThreads;
@@ -622,7 +671,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
   const int c0 = ci * C;
   const int n = min(C, T - c0);
-  const int ti = tid >> 4, cj = tid & 15;
+  const int ti = tid >> 5, cj = tid & 31;
+  const int ch0 = CW * cj;   // the thread's first key channel
   const long long sh = static_cast<long long>(b) * H + h;
   auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
   const long long row0 = tok(0);
@@ -638,20 +688,20 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     TilesB B;
   } sm;
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax], dgs[kCMax], vdx[kCMax];
-  __shared__ float red[2][kThreads / 64];
+  __shared__ float red[2][kWaves];
 
   if (tid < kCMax) chunk_gates(f, row0, n, tid, gs, eg, wd);
 
-  float AQ[4][CW], AE[4][CW], AR[4][CW], MP[4][4], ML[4][4];
+  float AQ[4][CW], AE[4][CW], AR[4][CW], MP[4][2], ML[4][2];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
     for (int e = 0; e < CW; ++e) AQ[u][e] = AE[u][e] = AR[u][e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) MP[u][w] = ML[u][w] = 0.f;
+    for (int w = 0; w < 2; ++w) MP[u][w] = ML[u][w] = 0.f;
   }
   float sdot = 0.f;   // this thread's share of <dS', S>
-  float vsum = 0.f;   // this thread's share of v_t . dX_t (scalar gain), t = tid >> 2
+  float vsum = 0.f;   // this thread's share of v_t . dX_t (scalar gain), t = tid >> 3
   const float *hc = a.h + (sh * a.NC + ci) * static_cast<long long>(Dv) * Dk;
   const float *dhc = a.dh + (sh * a.NC + ci) * static_cast<long long>(Dv) * Dk;
 
@@ -660,8 +710,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   // masks applied when the registers are written to LDS), so its loads are in flight while
   // the previous block is multiplied.
   constexpr int kSIt = kVB * DK / kThreads;   // state elements per thread and block
-  float ps[kSIt], pds[kSIt], po[4], px[4], pd[4], pv[4], pw[4];
-  const int lt = tid >> 2, rq = 4 * (tid & 3);   // token-tile element (token lt, rows rq ..)
+  float ps[kSIt], pds[kSIt], po[2], px[2], pd[2], pv[2], pw[2];
+  const int lt = tid >> 3, rq = 2 * (tid & 7);   // token-tile element (token lt, rows rq, rq + 1)
   auto vload = [&](int vb) {
 #pragma unroll
     for (int it = 0; it < kSIt; ++it) {
@@ -672,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     const int tt = min(lt, n - 1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const long long idx = tok(tt) * Dv + min(vb + rq + u, Dv - 1);
       po[u] = ld_f(dout, idx);
       px[u] = a.dX[idx];
@@ -695,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
       sdot = fmaf(s, ds, sdot);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int r = rq + u;
       const bool in = lt < n && r < nvb;
       const float gx = in ? px[u] : 0.f;
@@ -713,37 +763,34 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (vb + kVB < Dv) vload(vb + kVB);
+#pragma unroll 2
     for (int r = 0; r < nvb; ++r) {
       const float4 o4 = ld4(&sm.A.dOT[r][4 * ti]), x4 = ld4(&sm.A.dXT[r][4 * ti]);
-      const float4 d4 = ld4(&sm.A.DT[r][4 * ti]), dj = ld4(&sm.A.DT[r][4 * cj]);
-      float4 s[NG], ds[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        s[g] = ld4(&sm.A.S[r][64 * g + 4 * cj]);
-        ds[g] = ld4(&sm.A.dS[r][64 * g + 4 * cj]);
-      }
+      const float4 d4 = ld4(&sm.A.DT[r][4 * ti]);
+      const float2 dj = ld2(&sm.A.DT[r][2 * cj]);
+      float s[CW], ds[CW];
+      ldw<CW>(&sm.A.S[r][ch0], s);
+      ldw<CW>(&sm.A.dS[r][ch0], ds);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float ou = at(o4, u), xu = at(x4, u), du = at(d4, u);
+        MP[u][0] = fmaf(ou, dj.x, MP[u][0]);
+        MP[u][1] = fmaf(ou, dj.y, MP[u][1]);
+        ML[u][0] = fmaf(xu, dj.x, ML[u][0]);
+        ML[u][1] = fmaf(xu, dj.y, ML[u][1]);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          MP[u][w] = fmaf(ou, at(dj, w), MP[u][w]);
-          ML[u][w] = fmaf(xu, at(dj, w), ML[u][w]);
+        for (int e = 0; e < CW; ++e) {
+          AQ[u][e] = fmaf(ou, s[e], AQ[u][e]);
+          AE[u][e] = fmaf(xu, s[e], AE[u][e]);
+          AR[u][e] = fmaf(du, ds[e], AR[u][e]);
         }
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            AQ[u][4 * g + e] = fmaf(ou, at(s[g], e), AQ[u][4 * g + e]);
-            AE[u][4 * g + e] = fmaf(xu, at(s[g], e), AE[u][4 * g + e]);
-            AR[u][4 * g + e] = fmaf(du, at(ds[g], e), AR[u][4 * g + e]);
-          }
       }
     }
   }
   vsum += __shfl_xor(vsum, 1);
   vsum += __shfl_xor(vsum, 2);
-  if ((tid & 3) == 0) vdx[tid >> 2] = vsum;
+  vsum += __shfl_xor(vsum, 4);
+  if ((tid & 7) == 0) vdx[lt] = vsum;
 
   // ---- key products -------------------------------------------------------------------
   __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
@@ -782,8 +829,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
       AR[u][e] *= sr;
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = 4 * cj + w;
+    for (int w = 0; w < 2; ++w) {
+      const int j = 2 * cj + w;
       // (the exponent above the diagonal may overflow; it is discarded)
       const float dec = expf(gs[t] - gs[j]);
       sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MP[u][w] * dec : 0.f;
@@ -794,71 +841,66 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   // lambda: this thread's share of sum_j r_j . (e^{g_n - g_j} dS'^T d_j)
   float lam = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u) {
+    float rr[CW];
+    ldw<CW>(&sm.B.R[4 * ti + u][ch0], rr);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float4 rr = ld4(&sm.B.R[4 * ti + u][64 * g + 4 * cj]);
+    for (int e = 0; e < CW; ++e) lam = fmaf(rr[e], AR[u][e], lam);
+  }
+  // dQ += dM R, dE += dL' R (rows past n of dM and dL' are zero: whole blocks of 8)
+  for (int j0 = 0; j0 < n; j0 += 8) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lam = fmaf(at(rr, e), AR[u][4 * g + e], lam);
-    }
-  // dQ += dM R, dE += dL' R
-  for (int j = 0; j < n; ++j) {
-    float4 rr[NG];
+    for (int j = j0; j < j0 + 8; ++j) {
+      float rr[CW];
+      ldw<CW>(&sm.B.R[j][ch0], rr);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) rr[g] = ld4(&sm.B.R[j][64 * g + 4 * cj]);
+      for (int u = 0; u < 4; ++u) {
+        const float m = sm.B.dM[4 * ti + u][j], l = sm.B.dL[4 * ti + u][j];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float m = sm.B.dM[4 * ti + u][j], l = sm.B.dL[4 * ti + u][j];
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          AQ[u][4 * g + e] = fmaf(m, at(rr[g], e), AQ[u][4 * g + e]);
-          AE[u][4 * g + e] = fmaf(l, at(rr[g], e), AE[u][4 * g + e]);
+        for (int e = 0; e < CW; ++e) {
+          AQ[u][e] = fmaf(m, rr[e], AQ[u][e]);
+          AE[u][e] = fmaf(l, rr[e], AE[u][e]);
         }
+      }
     }
   }
   // dR += dM^T Q + dL'^T E
-  for (int i = 0; i < n; ++i) {
-    const float4 m4 = ld4(&sm.B.dM[i][4 * ti]), l4 = ld4(&sm.B.dL[i][4 * ti]);
-    float4 qq[NG], ee[NG];
+  for (int i0 = 0; i0 < n; i0 += 8) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      qq[g] = ld4(&sm.B.Q[i][64 * g + 4 * cj]);
-      ee[g] = ld4(&sm.B.E[i][64 * g + 4 * cj]);
-    }
+    for (int i = i0; i < i0 + 8; ++i) {
+      const float4 m4 = ld4(&sm.B.dM[i][4 * ti]), l4 = ld4(&sm.B.dL[i][4 * ti]);
+      float qq[CW], ee[CW];
+      ldw<CW>(&sm.B.Q[i][ch0], qq);
+      ldw<CW>(&sm.B.E[i][ch0], ee);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float m = at(m4, u), l = at(l4, u);
+      for (int u = 0; u < 4; ++u) {
+        const float m = at(m4, u), l = at(l4, u);
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          AR[u][4 * g + e] = fmaf(m, at(qq[g], e), fmaf(l, at(ee[g], e), AR[u][4 * g + e]));
+        for (int e = 0; e < CW; ++e) AR[u][e] = fmaf(m, qq[e], fmaf(l, ee[e], AR[u][e]));
+      }
     }
   }
   // gate gradient per token: q . dQ + e . dE - r . dR over the thread's channels, summed
-  // over the 16 lanes that share the tokens
+  // over the 32 lanes that share the tokens
   float pg[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int t = 4 * ti + u;
+    float qq[CW], ee[CW], rr[CW];
+    ldw<CW>(&sm.B.Q[t][ch0], qq);
+    ldw<CW>(&sm.B.E[t][ch0], ee);
+    ldw<CW>(&sm.B.R[t][ch0], rr);
     float acc = 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float4 qq = ld4(&sm.B.Q[t][64 * g + 4 * cj]), ee = ld4(&sm.B.E[t][64 * g + 4 * cj]);
-      const float4 rr = ld4(&sm.B.R[t][64 * g + 4 * cj]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(at(qq, e), AQ[u][4 * g + e], acc);
-        acc = fmaf(at(ee, e), AE[u][4 * g + e], acc);
-        acc = fmaf(-at(rr, e), AR[u][4 * g + e], acc);
-      }
+    for (int e = 0; e < CW; ++e) {
+      acc = fmaf(qq[e], AQ[u][e], acc);
+      acc = fmaf(ee[e], AE[u][e], acc);
+      acc = fmaf(-rr[e], AR[u][e], acc);
     }
     pg[u] = acc;
   }
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1)
+  for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
     for (int u = 0; u < 4; ++u) pg[u] += __shfl_xor(pg[u], m);
   // block sums of <dS', S> and lambda
@@ -880,13 +922,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     // dlog_alpha_t = sum_{i >= t} dg_i inside the chunk
     float x = tid < n ? dgs[tid] : 0.f;
     if (tid == n - 1) {
-      float st = 0.f, lt = 0.f;
+      float st = 0.f, lt2 = 0.f;
 #pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         st += red[0][w];
-        lt += red[1][w];
+        lt2 += red[1][w];
       }
-      x += eg[n - 1] * st + lt;
+      x += eg[n - 1] * st + lt2;
     }
 #pragma unroll
     for (int d = 1; d < kCMax; d <<= 1) {
@@ -904,32 +946,30 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     const long long rowk = tok(t) * Dk;
     const float bt = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(t)] : 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 64 * g + 4 * cj + e;
-        if (c >= Dk) continue;
-        const float de = AE[u][4 * g + e], dr = AR[u][4 * g + e];
-        const float kk = ld_f(k, rowk + c);
-        a.dq[rowk + c] = AQ[u][4 * g + e];
-        float dkv;
-        if (f.gain == GDR_GAIN_SCALAR) {
-          dkv = bt * de;
-          pk[u] = fmaf(kk, de, pk[u]);
-        } else {
-          dkv = ld_f(er, rowk + c) * de;
-          a.derase[rowk + c] = kk * de;
-        }
-        if (f.wkey == GDR_WKEY_EXPLICIT)
-          a.dwk[rowk + c] = dr;
-        else
-          dkv += dr;
-        a.dk[rowk + c] = dkv;
+    for (int e = 0; e < CW; ++e) {
+      const int c = ch0 + e;
+      if (c >= Dk) continue;
+      const float de = AE[u][e], dr = AR[u][e];
+      const float kk = ld_f(k, rowk + c);
+      a.dq[rowk + c] = AQ[u][e];
+      float dkv;
+      if (f.gain == GDR_GAIN_SCALAR) {
+        dkv = bt * de;
+        pk[u] = fmaf(kk, de, pk[u]);
+      } else {
+        dkv = ld_f(er, rowk + c) * de;
+        a.derase[rowk + c] = kk * de;
       }
+      if (f.wkey == GDR_WKEY_EXPLICIT)
+        a.dwk[rowk + c] = dr;
+      else
+        dkv += dr;
+      a.dk[rowk + c] = dkv;
+    }
   }
   if (f.gain == GDR_GAIN_SCALAR) {
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+    for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
       for (int u = 0; u < 4; ++u) pk[u] += __shfl_xor(pk[u], m);
     if (cj == 0) {
@@ -947,9 +987,9 @@ hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   if (a.NC == 0) return hipSuccess;
   const dim3 gp(a.NC, a.f.H, a.f.B);
   if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_prep_kernel<IO, 64>), gp, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<IO, 64>), gp, dim3(kPrThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_prep_kernel<IO, 128>), gp, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<IO, 128>), gp, dim3(kPrThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gs((a.f.Dv + kBV - 1) / kBV, a.f.H, a.f.B);
@@ -979,9 +1019,9 @@ hipError_t chunk_io(const BwdArgs &a, hipStream_t s) {
   if (a.NC == 0) return hipSuccess;
   const dim3 grid(a.NC, a.f.H, a.f.B);
   if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64>), grid, dim3(kCkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128>), grid, dim3(kCkThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -22,14 +22,15 @@ __device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast
 // entries are those of the exact path, bit for bit, and N >= n - 1 runs exactly the exact
 // path's instructions.  Rows of L past the chunk must be zero (their T rows come out unit
 // rows), and the 16 x 16 blocks of Tm above the diagonal must hold zero on entry (they are
-// never written).  Zs is 32 x 36 scratch.  Starts reading L without a barrier (the caller
-// publishes it) and ends with a workgroup barrier.
+// never written).  Zs is 32 x 36 scratch.  Threads 0..255 do the work; in a larger workgroup
+// the others pass active = false and only take part in the barriers.  Starts reading L
+// without a barrier (the caller publishes it) and ends with a workgroup barrier.
 template <int LDL, int LDT>
 __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*Tm)[LDT], float (*Zs)[36], int N,
-                                               int tid) {
+                                               int tid, bool active = true) {
   auto keep = [&](int i, int j) { return N < 0 || i - j <= N; };
   const int lane = tid & 63, w = tid >> 6;
-  {   // diagonal block w: lane = (block row ii, block columns jq .. jq + 3)
+  if (active) {   // diagonal block w: lane = (block row ii, block columns jq .. jq + 3)
     const int ii = lane >> 2, jq = (lane & 3) * 4;
     const int o = 16 * w, gi = o + ii;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -62,7 +63,7 @@ __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*T
   __syncthreads();
   // two 16 x 16 products at once: thread = (product p, row r, columns c, c + 1)
   const int p = tid >> 7, r = (tid >> 3) & 15, c = (tid & 7) * 2;
-  {   // Z_p = A_(2p+1, 2p) D_2p
+  if (active) {   // Z_p = A_(2p+1, 2p) D_2p
     const int ro = 32 * p + 16, co = 32 * p;
     float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -75,7 +76,7 @@ __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*T
     *reinterpret_cast<float2 *>(&Zs[16 * p + r][c]) = make_float2(z0, z1);
   }
   __syncthreads();
-  {   // T_(2p+1, 2p) = D_(2p+1) Z_p
+  if (active) {   // T_(2p+1, 2p) = D_(2p+1) Z_p
     const int ro = 32 * p + 16, co = 32 * p;
     float t0v = 0.f, t1v = 0.f;
 #pragma unroll
@@ -92,7 +93,7 @@ __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*T
   __syncthreads();
   // 32 x 32 products: thread = (row r2, columns c4 .. c4 + 3)
   const int r2 = tid >> 3, c4 = (tid & 7) * 4;
-  {   // Z = A_ba T_a
+  if (active) {   // Z = A_ba T_a
     float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int m = 0; m < 32; ++m) {
@@ -106,7 +107,7 @@ __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*T
     *reinterpret_cast<float4 *>(&Zs[r2][c4]) = make_float4(z[0], z[1], z[2], z[3]);
   }
   __syncthreads();
-  {   // T_ba = T_b Z
+  if (active) {   // T_ba = T_b Z
     float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int m = 0; m < 32; ++m) {
