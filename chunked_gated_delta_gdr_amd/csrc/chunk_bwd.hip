@@ -28,8 +28,6 @@
 namespace gdr {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBV = 16;     // state rows per workgroup of the sweep
 constexpr int kCMax = 64;   // largest chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -43,6 +41,14 @@ __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &
 }
 __device__ __forceinline__ float at(const float4 &v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// fp32 matrix-core product D = A B + C of 16 x 16 x 4 tiles: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16], r < 4 (v_mfma_f32_16x16x4_f32)
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4v mfma4(float a, float b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // W consecutive floats (W = 2 or 4, aligned to 4 W bytes) into registers
@@ -262,16 +268,26 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// State pass: one workgroup per (batch, head, tile of kBV value rows), chunks first to last.
-// With W and U of every chunk at hand only the state-dependent part remains:
-// D = U - W S^T (saved) and S <- e^{g_n} S + D^T (e^{g_n - g} (.) R); the state at every
-// chunk start is saved too.  The next chunk's W, R and U are loaded during this chunk.
+// State pass: one workgroup of kStThreads (8 waves) per (batch, head, tile of kStBV value
+// rows), chunks first to last, on the fp32 matrix cores.  With W and U of every chunk at
+// hand only the state-dependent part remains: D = U - W S^T (saved) and
+// S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R; the state at every chunk start is saved too.  S
+// lives in the waves' accumulators (16 x 16 tiles), mirrored in LDS for D's product; wave w
+// owns the tile (token block w % 4, value-row block w / 4) of D.  The next chunk's W, R and U
+// are loaded during this chunk.
 // ---------------------------------------------------------------------------------------
+constexpr int kStBV = 32;
+constexpr int kStThreads = 512;
+
 template <typename IO, int DK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_state_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
+  constexpr int kBV = kStBV, kThreads = kStThreads;
   constexpr int kLoadIt = kCMax * DK / kThreads;
   constexpr int kUIt = kCMax * kBV / kThreads;
+  constexpr int NCB = DK / 16;
+  constexpr int NTS = (kBV / 16) * NCB;
+  constexpr int NTW = (NTS + 7) / 8;
   const ChunkArgs &f = a.f;
   const IO *__restrict__ k = static_cast<const IO *>(f.k);
   const IO *__restrict__ wk = static_cast<const IO *>(f.write_key);
@@ -282,14 +298,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int nv = min(kBV, f.Dv - v0);
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
   const long long sh = static_cast<long long>(b) * H + h;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kq = lane >> 4;
+  const int tb = wave & 3, rb = wave >> 2;
 
   __shared__ __align__(16) float Ws[kCMax][LD];   // W of the chunk
   __shared__ __align__(16) IO Rs[kCMax][LD];      // write keys (in the io type: exact)
-  __shared__ __align__(16) float Ss[kBV][LD];     // state tile
-  __shared__ __align__(16) float Dl[kCMax][kBV];  // D, then e^{g_n - g} D
+  __shared__ __align__(16) float Ss[kBV][LD];     // mirror of the state
+  __shared__ __align__(16) float Dl[kCMax][kBV];  // e^{g_n - g} D
   __shared__ __align__(16) float Us[kCMax][kBV];  // U
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
 
+  float4v Sacc[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int u = wave + 8 * m;
+    const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = 0.f;
+      if (u < NTS && f.state_in != nullptr && row + r < nv && c < Dk)
+        x = f.state_in[(sh * Dv + v0 + row + r) * Dk + c];
+      Sacc[m][r] = x;
+    }
+  }
   for (int idx = tid; idx < kBV * LD; idx += kThreads) {
     const int r = idx / LD, c = idx % LD;
     float s = 0.f;
@@ -316,16 +347,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       pu[it] = a.Uw[(row0 + static_cast<long long>(t) * H) * Dv + v0 + r];
     }
   };
-  const int t0 = 2 * (tid >> 3), r0 = 2 * (tid & 7);
   if (a.NC > 0) cload(0);
   for (int ci = 0; ci < a.NC; ++ci) {
     const int c0 = ci * C;
     const int n = min(C, T - c0);
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
     __syncthreads();   // previous chunk done with every buffer
-    {   // the state at this chunk's start
+    {   // the state at this chunk's start (from the accumulators)
       float *hc = a.h + ((sh * a.NC + ci) * Dv + v0) * static_cast<long long>(Dk);
-      for (int idx = tid; idx < nv * Dk; idx += kThreads) hc[idx] = Ss[idx / Dk][idx % Dk];
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const int u = wave + 8 * m;
+        const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+        if (u < NTS && c < Dk) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row + r < nv) hc[static_cast<long long>(row + r) * Dk + c] = Sacc[m][r];
+        }
+      }
     }
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
@@ -342,81 +381,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (tid < kCMax) chunk_gates(f, tok(0), n, tid, gs, eg, wd);
     __syncthreads();
     if (ci + 1 < a.NC) cload(ci + 1);   // in flight during this chunk's products
-    {   // D = U - W S^T on the thread's 2 x 2 block
-      float acc[2][2] = {};
-#pragma unroll 4
-      for (int c = 0; c < DK; c += 4) {
-        const float4 x0 = ld4(&Ws[t0][c]), x1 = ld4(&Ws[t0 + 1][c]);
-        const float4 s0 = ld4(&Ss[r0][c]), s1 = ld4(&Ss[r0 + 1][c]);
-        fma4(acc[0][0], x0, s0);
-        fma4(acc[0][1], x0, s1);
-        fma4(acc[1][0], x1, s0);
-        fma4(acc[1][1], x1, s1);
+    {   // D = U - W S^T, tile (tb, rb)
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int ks = 0; ks < DK; ks += 4)
+        acc = mfma4(Ws[16 * tb + col][ks + kq], Ss[16 * rb + col][ks + kq], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
+        const bool in = t < n && rr < nv;
+        const float d = Us[t][rr] - acc[r];
+        if (in) a.D[tok(t) * Dv + v0 + rr] = d;
+        Dl[t][rr] = in ? wd[t] * d : 0.f;
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          const bool in = t < n && r < nv;
-          const float d = Us[t][r] - acc[u][w];
-          if (in) a.D[tok(t) * Dv + v0 + r] = d;
-          Dl[t][r] = in ? wd[t] * d : 0.f;
-        }
     }
     __syncthreads();
-    // S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R: thread (rows r + RS m for m < NR, columns
-    // c .. c + 3); each row of R read from LDS serves all NR rows
+    // S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R on the wave's tiles (rows of Dl past n are zero)
     {
       const float gl = eg[n - 1];
-      constexpr int NC4 = DK / 4;
-      constexpr int NR = (kBV * NC4 + kThreads - 1) / kThreads;
-      constexpr int RS = kThreads / NC4;
-      const int r = tid / NC4, c = (tid % NC4) * 4;
-      if (r < RS && r < kBV) {
-        float4 acc[NR];
 #pragma unroll
-        for (int m = 0; m < NR; ++m) {
-          const float4 s = r + RS * m < kBV ? ld4(&Ss[r + RS * m][c]) : make_float4(0.f, 0.f, 0.f, 0.f);
-          acc[m] = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
-        }
-        // rows past n hold zeros, so the sum may run to the next multiple of 8
-        for (int j0 = 0; j0 < n; j0 += 8) {
+      for (int m = 0; m < NTW; ++m) {
+        const int u = wave + 8 * m;
+        if (u >= NTS) continue;
+        const int rbs = u / NCB, cbs = u % NCB;
+        float4v acc = Sacc[m] * gl;
+        for (int t0 = 0; t0 < n; t0 += 4)
+          acc = mfma4(Dl[t0 + kq][16 * rbs + col], ld_f(&Rs[t0 + kq][16 * cbs + col], 0), acc);
+        Sacc[m] = acc;
+        // the LDS mirror for the next chunk's W S^T (its reads of this chunk are done)
 #pragma unroll
-          for (int j = j0; j < j0 + 8; ++j) {
-            const float r0f = ld_f(&Rs[j][c], 0), r1f = ld_f(&Rs[j][c], 1);
-            const float r2f = ld_f(&Rs[j][c], 2), r3f = ld_f(&Rs[j][c], 3);
-#pragma unroll
-            for (int m = 0; m < NR; ++m) {
-              const float w = Dl[j][min(r + RS * m, kBV - 1)];
-              acc[m].x = fmaf(w, r0f, acc[m].x);
-              acc[m].y = fmaf(w, r1f, acc[m].y);
-              acc[m].z = fmaf(w, r2f, acc[m].z);
-              acc[m].w = fmaf(w, r3f, acc[m].w);
-            }
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < NR; ++m)
-          if (r + RS * m < kBV) *reinterpret_cast<float4 *>(&Ss[r + RS * m][c]) = acc[m];
+        for (int r = 0; r < 4; ++r) Ss[16 * rbs + 4 * kq + r][16 * cbs + col] = acc[r];
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Reverse sweep: one workgroup of kSwThreads per (batch, head, tile of kSwBV value rows),
-// chunks last to first.  dS (kSwBV x Dk) stays in LDS.  Two waves per SIMD, so one wave's
-// LDS and global latencies overlap the other's arithmetic.
+// Reverse sweep: one workgroup of kSwThreads (8 waves) per (batch, head, tile of kSwBV value
+// rows), chunks last to first, every product on the fp32 matrix cores (v_mfma_f32_16x16x4_f32,
+// lane layout as in the per-chunk pass below).  The gradient dS (kSwBV x Dk) lives in the
+// waves' accumulators for the whole sequence (16 x 16 tiles, a few per wave), mirrored in LDS
+// for the products that read it as an operand.  Per chunk, wave w owns the 16 x 16 tile
+// (token block w % 4, value-row block w / 4) of dD and dX.
 // ---------------------------------------------------------------------------------------
 constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
+
 
 template <typename IO, int DK>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kSwBV, kThreads = kSwThreads;
   constexpr int kLoadIt = kCMax * DK / kThreads;
+  constexpr int NCB = DK / 16;                   // channel blocks
+  constexpr int NTS = (kBV / 16) * NCB;          // dS tiles
+  constexpr int NTW = (NTS + 7) / 8;             // dS tiles per wave
   const ChunkArgs &f = a.f;
   const IO *__restrict__ q = static_cast<const IO *>(f.q);
   const IO *__restrict__ k = static_cast<const IO *>(f.k);
@@ -429,12 +448,14 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   const int v0 = vt * kBV;
   const int nv = min(kBV, f.Dv - v0);
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kq = lane >> 4;
+  const int tb = wave & 3, rb = wave >> 2;        // this wave's dD / dX tile
 
   __shared__ __align__(16) float Ks[kCMax][LD];     // write keys r, then queries q
   __shared__ __align__(16) float Es[kCMax][LD];     // erase keys e
   __shared__ float Tm[kCMax][kCMax + 1];            // T (unit lower)
   __shared__ float Pm[kCMax][kCMax + 1];            // P (lower)
-  __shared__ __align__(16) float dS[kBV][LD];       // gradient at the current chunk's end
+  __shared__ __align__(16) float dS[kBV][LD];       // mirror of the gradient at the chunk's end
   __shared__ __align__(16) float dOs[kCMax][kBV];   // dO
   __shared__ __align__(16) float dDs[kCMax][kBV];   // dD
   __shared__ __align__(16) float Am[kCMax][kBV];    // scale e^g dO
@@ -442,17 +463,30 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
 
   const long long sh = static_cast<long long>(b) * H + h;
+  // dS tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
+  float4v dSacc[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int u = wave + 8 * m;
+    const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = 0.f;
+      if (u < NTS && a.dstate_out != nullptr && row + r < nv && c < Dk)
+        x = a.dstate_out[(sh * Dv + v0 + row + r) * Dk + c];
+      dSacc[m][r] = x;
+    }
+  }
   for (int idx = tid; idx < kBV * LD; idx += kThreads) {
     const int r = idx / LD, c = idx % LD;
     float s = 0.f;
     if (a.dstate_out != nullptr && r < nv && c < Dk) s = a.dstate_out[(sh * Dv + v0 + r) * Dk + c];
     dS[r][c] = s;
   }
-  const int t0 = 2 * (tid >> 4), r0 = 2 * (tid & 15);   // 2 x 2 block of the C x kBV tiles
   // Loads of chunk ci into registers (indices clamped into the chunk, masks applied when they
-  // are written to LDS): write keys, keys, gains, T, P and dO are loaded one chunk ahead, so
-  // they are in flight during the previous chunk's products; the queries, needed only after
-  // the first two barriers of a chunk, are loaded at its start.
+  // are written to LDS): write keys, keys, gains, T, P, dO and log alpha are loaded one chunk
+  // ahead, so they are in flight during the previous chunk's products; the queries, needed
+  // only after the first two barriers of a chunk, are loaded at its start.
   constexpr int kCC = kCMax * kCMax / kThreads, kOIt = kCMax * kBV / kThreads;
   float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xq[kLoadIt], xt[kCC], xp[kCC], xo[kOIt], xla = 0.f;
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
@@ -501,9 +535,18 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       }
     }
     if (tid < kCMax) chunk_gates_from(xla, n, tid, gs, eg, wd);
-    {   // the gradient at this chunk's end, for the per-chunk pass
+    {   // the gradient at this chunk's end, for the per-chunk pass (from the accumulators)
       float *dhc = a.dh + ((sh * a.NC + ci) * Dv + v0) * static_cast<long long>(Dk);
-      for (int idx = tid; idx < nv * Dk; idx += kThreads) dhc[idx] = dS[idx / Dk][idx % Dk];
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const int u = wave + 8 * m;
+        const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+        if (u < NTS && c < Dk) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row + r < nv) dhc[static_cast<long long>(row + r) * Dk + c] = dSacc[m][r];
+        }
+      }
     }
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
@@ -525,68 +568,40 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       const int idx = tid + it * kThreads, t = idx / kBV, r = idx % kBV;
       dOs[t][r] = (t < n && r < nv) ? xo[it] : 0.f;
     }
-    if (ci > 0) cload(ci - 1);   // in flight during this chunk's products
     __syncthreads();
-    // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO on the thread's 2 x 2 block
+    if (ci > 0) cload(ci - 1);   // in flight during this chunk's products
+    const int tr0 = 16 * tb + 4 * kq;   // the lane's result rows (tokens) of the dD / dX tile
+    // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO, tile (tb, rb); P is zero above the
+    // diagonal and T, P, dO rows past n (inside the chunk) are zero
     {
-      float acc[2][2] = {};
-#pragma unroll 4
-      for (int c = 0; c < DK; c += 4) {
-        const float4 x0 = ld4(&Ks[t0][c]), x1 = ld4(&Ks[t0 + 1][c]);
-        const float4 s0 = ld4(&dS[r0][c]), s1 = ld4(&dS[r0 + 1][c]);
-        fma4(acc[0][0], x0, s0);
-        fma4(acc[0][1], x0, s1);
-        fma4(acc[1][0], x1, s0);
-        fma4(acc[1][1], x1, s1);
+      float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int ks = 0; ks < DK; ks += 4)
+        a1 = mfma4(Ks[16 * tb + col][ks + kq], dS[16 * rb + col][ks + kq], a1);
+      // (i0 < n keeps every row read below C, where T and P were loaded)
+      for (int i0 = 16 * tb; i0 < n; i0 += 4)
+        a2 = mfma4(Pm[i0 + kq][16 * tb + col], dOs[i0 + kq][16 * rb + col], a2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tr0 + r, rr = 16 * rb + col;
+        dDs[t][rr] = (t < n && rr < nv) ? fmaf(wd[t], a1[r], f.scale * a2[r]) : 0.f;
       }
-      float p[2][2] = {};
-      // P is zero above the diagonal, and T, P and dO rows past n (up to the next multiple of
-      // 8, inside the chunk) hold zeros, so the sums run over whole blocks of 8 rows
-      for (int i0 = t0 & ~7; i0 < n; i0 += 8) {
-#pragma unroll
-        for (int i = i0; i < i0 + 8; ++i) {
-          const float2 o = ld2(&dOs[i][r0]);
-          const float p0 = Pm[i][t0], p1 = Pm[i][t0 + 1];
-          p[0][0] = fmaf(p0, o.x, p[0][0]);
-          p[0][1] = fmaf(p0, o.y, p[0][1]);
-          p[1][0] = fmaf(p1, o.x, p[1][0]);
-          p[1][1] = fmaf(p1, o.y, p[1][1]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          dDs[t][r] = (t < n && r < nv) ? fmaf(wd[t], acc[u][w], f.scale * p[u][w]) : 0.f;
-        }
     }
     __syncthreads();
-    // dX = T^T dD (T unit lower, zero above the diagonal); written out for the per-chunk
-    // pass, and folded with e^g into the state-gradient update
+    // dX = T^T dD, tile (tb, rb); written out for the per-chunk pass, and folded with e^g
+    // into the state-gradient update
     {
-      float x[2][2] = {};
-      for (int i0 = t0 & ~7; i0 < n; i0 += 8) {
+      float4v x = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 16 * tb; i0 < n; i0 += 4)
+        x = mfma4(Tm[i0 + kq][16 * tb + col], dDs[i0 + kq][16 * rb + col], x);
 #pragma unroll
-        for (int i = i0; i < i0 + 8; ++i) {
-          const float2 d = ld2(&dDs[i][r0]);
-          const float a0 = Tm[i][t0], a1 = Tm[i][t0 + 1];
-          x[0][0] = fmaf(a0, d.x, x[0][0]);
-          x[0][1] = fmaf(a0, d.y, x[0][1]);
-          x[1][0] = fmaf(a1, d.x, x[1][0]);
-          x[1][1] = fmaf(a1, d.y, x[1][1]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = tr0 + r, rr = 16 * rb + col;
+        const bool in = t < n && rr < nv;
+        if (in) a.dX[tok(t) * Dv + v0 + rr] = x[r];
+        Bm[t][rr] = in ? eg[t] * x[r] : 0.f;
+        Am[t][rr] = in ? f.scale * eg[t] * dOs[t][rr] : 0.f;
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          const bool in = t < n && r < nv;
-          if (in) a.dX[tok(t) * Dv + v0 + r] = x[u][w];
-          Bm[t][r] = in ? eg[t] * x[u][w] : 0.f;
-          Am[t][r] = in ? f.scale * eg[t] * dOs[t][r] : 0.f;
-        }
     }
     // queries replace the write keys (their last read was before the barrier above)
 #pragma unroll
@@ -595,66 +610,59 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       Ks[t][c] = (t < n && c < Dk) ? xq[it] : 0.f;
     }
     __syncthreads();
-    // dS <- e^{g_n} dS + A^T Q - B^T E: thread (rows r + 8 m for m < NR, columns c .. c + 3);
-    // each row of Q and E read from LDS serves all NR rows
+    // dS <- e^{g_n} dS + A^T Q - B^T E on the wave's tiles; rows of A, B past n are zero
     {
       const float gl = eg[n - 1];
-      constexpr int NC4 = DK / 4;
-      constexpr int NR = (kBV * NC4 + kThreads - 1) / kThreads;   // rows per thread
-      constexpr int RS = kThreads / NC4;                          // row step between them
-      const int r = tid / NC4, c = (tid % NC4) * 4;
-      if (r < RS && r < kBV) {
-        float4 acc[NR];
 #pragma unroll
-        for (int m = 0; m < NR; ++m) {
-          const float4 s = r + RS * m < kBV ? ld4(&dS[r + RS * m][c]) : make_float4(0.f, 0.f, 0.f, 0.f);
-          acc[m] = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+      for (int m = 0; m < NTW; ++m) {
+        const int u = wave + 8 * m;
+        if (u >= NTS) continue;
+        const int rbs = u / NCB, cbs = u % NCB;
+        float4v acc = dSacc[m] * gl;
+        for (int t0 = 0; t0 < n; t0 += 4) {
+          acc = mfma4(Am[t0 + kq][16 * rbs + col], Ks[t0 + kq][16 * cbs + col], acc);
+          acc = mfma4(-Bm[t0 + kq][16 * rbs + col], Es[t0 + kq][16 * cbs + col], acc);
         }
-        for (int j0 = 0; j0 < n; j0 += 8) {
+        dSacc[m] = acc;
+        // the LDS mirror for the next chunk's R dS^T (its reads of this chunk are done)
 #pragma unroll
-          for (int j = j0; j < j0 + 8; ++j) {
-            const float4 qq = ld4(&Ks[j][c]), ee = ld4(&Es[j][c]);
-#pragma unroll
-            for (int m = 0; m < NR; ++m) {
-              const int rr = min(r + RS * m, kBV - 1);
-              const float am = Am[j][rr], bm = Bm[j][rr];
-              acc[m].x = fmaf(am, qq.x, fmaf(-bm, ee.x, acc[m].x));
-              acc[m].y = fmaf(am, qq.y, fmaf(-bm, ee.y, acc[m].y));
-              acc[m].z = fmaf(am, qq.z, fmaf(-bm, ee.z, acc[m].z));
-              acc[m].w = fmaf(am, qq.w, fmaf(-bm, ee.w, acc[m].w));
-            }
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < NR; ++m)
-          if (r + RS * m < kBV) *reinterpret_cast<float4 *>(&dS[r + RS * m][c]) = acc[m];
+        for (int r = 0; r < 4; ++r) dS[16 * rbs + 4 * kq + r][16 * cbs + col] = acc[r];
       }
     }
   }
-  __syncthreads();
   if (a.dstate_in != nullptr) {
-    for (int idx = tid; idx < nv * Dk; idx += kThreads) {
-      const int r = idx / Dk, c = idx % Dk;
-      a.dstate_in[(sh * Dv + v0 + r) * Dk + c] = dS[r][c];
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const int u = wave + 8 * m;
+      const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+      if (u < NTS && c < Dk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (row + r < nv) a.dstate_in[(sh * Dv + v0 + row + r) * Dk + c] = dSacc[m][r];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-chunk pass: one workgroup of kCkThreads per (batch, head, chunk).  Thread (ti, cj)
-// owns tokens 4 ti .. 4 ti + 3 and key channels CW cj .. CW cj + CW - 1 of the C x Dk
-// gradients, and the 4 x 2 block (tokens 4 ti.., tokens 2 cj..) of the C x C ones.
+// Per-chunk pass: one workgroup of kCkThreads (8 waves) per (batch, head, chunk); every
+// product on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][l / 16]
+// and B[l / 16][l % 16], and holds D[4 (l / 16) + r][l % 16], r < 4).  Wave w owns token
+// block tb = w % 4 (16 tokens) and channel half hh = w / 4: the 16 x 16 tiles of dQ, dE, dR
+// at (tb, channel tiles of that half); the half-0 waves also own the tiles of dO D^T in row
+// block tb (on and below the diagonal), the half-1 waves those of dX D^T.
 // ---------------------------------------------------------------------------------------
 constexpr int kCkThreads = 512;
 
+
 template <typename IO, int DK>
 __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
-  static_assert(DK == 64 || DK == 128, "32 channel groups of 2 or 4");
+  static_assert(DK == 64 || DK == 128, "two halves of 16-channel tiles");
   constexpr int kThreads = kCkThreads;
   constexpr int kWaves = kThreads / 64;
   constexpr int LD = DK + 4;
-  constexpr int CW = DK / 32;      // channels per thread
-  constexpr int kVB = 16;          // value rows per step of the value loop
+  constexpr int MT = DK / 32;      // channel tiles per wave
+  constexpr int kVB = 32;          // value rows per step of the value loop
   constexpr int LT = kCMax + 4;    // row stride of [value][token] and C x C tiles
   constexpr int kLoadIt = kCMax * DK / kThreads;
   const ChunkArgs &f = a.f;
@@ -671,11 +679,14 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
   const int c0 = ci * C;
   const int n = min(C, T - c0);
-  const int ti = tid >> 5, cj = tid & 31;
-  const int ch0 = CW * cj;   // the thread's first key channel
+  const int wave = tid >> 6, lane = tid & 63;
+  const int tb = wave & 3, hh = wave >> 2;
+  const int col = lane & 15, kq = lane >> 4;
+  const int tr0 = 16 * tb + 4 * kq;   // first of the lane's 4 result rows (tokens)
   const long long sh = static_cast<long long>(b) * H + h;
   auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
   const long long row0 = tok(0);
+  auto chan = [&](int m) { return 16 * (MT * hh + m) + col; };   // the lane's column of tile m
 
   struct TilesA {   // value loop: state rows, their gradients, token tiles by value row
     float S[kVB][LD], dS[kVB][LD], dOT[kVB][LT], dXT[kVB][LT], DT[kVB][LT];
@@ -687,19 +698,17 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     TilesA A;
     TilesB B;
   } sm;
-  __shared__ float gs[kCMax], eg[kCMax], wd[kCMax], dgs[kCMax], vdx[kCMax];
+  __shared__ float gs[kCMax], eg[kCMax], wd[kCMax], vdx[kCMax];
+  __shared__ float dgs[2][kCMax], pks[2][kCMax];
   __shared__ float red[2][kWaves];
 
   if (tid < kCMax) chunk_gates(f, row0, n, tid, gs, eg, wd);
 
-  float AQ[4][CW], AE[4][CW], AR[4][CW], MP[4][2], ML[4][2];
+  float4v AQ[MT], AE[MT], AR[MT], MPL[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int m = 0; m < MT; ++m) AQ[m] = AE[m] = AR[m] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < CW; ++e) AQ[u][e] = AE[u][e] = AR[u][e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) MP[u][w] = ML[u][w] = 0.f;
-  }
+  for (int jb = 0; jb < 4; ++jb) MPL[jb] = float4v{0.f, 0.f, 0.f, 0.f};
   float sdot = 0.f;   // this thread's share of <dS', S>
   float vsum = 0.f;   // this thread's share of v_t . dX_t (scalar gain), t = tid >> 3
   const float *hc = a.h + (sh * a.NC + ci) * static_cast<long long>(Dv) * Dk;
@@ -710,8 +719,8 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   // masks applied when the registers are written to LDS), so its loads are in flight while
   // the previous block is multiplied.
   constexpr int kSIt = kVB * DK / kThreads;   // state elements per thread and block
-  float ps[kSIt], pds[kSIt], po[2], px[2], pd[2], pv[2], pw[2];
-  const int lt = tid >> 3, rq = 2 * (tid & 7);   // token-tile element (token lt, rows rq, rq + 1)
+  float ps[kSIt], pds[kSIt], po[4], px[4], pd[4], pv[4], pw[4];
+  const int lt = tid >> 3, rq = 4 * (tid & 7);   // token-tile element (token lt, rows rq .. rq + 3)
   auto vload = [&](int vb) {
 #pragma unroll
     for (int it = 0; it < kSIt; ++it) {
@@ -722,7 +731,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     const int tt = min(lt, n - 1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const long long idx = tok(tt) * Dv + min(vb + rq + u, Dv - 1);
       po[u] = ld_f(dout, idx);
       px[u] = a.dX[idx];
@@ -745,7 +754,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       sdot = fmaf(s, ds, sdot);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int r = rq + u;
       const bool in = lt < n && r < nvb;
       const float gx = in ? px[u] : 0.f;
@@ -763,28 +772,23 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (vb + kVB < Dv) vload(vb + kVB);
-#pragma unroll 2
-    for (int r = 0; r < nvb; ++r) {
-      const float4 o4 = ld4(&sm.A.dOT[r][4 * ti]), x4 = ld4(&sm.A.dXT[r][4 * ti]);
-      const float4 d4 = ld4(&sm.A.DT[r][4 * ti]);
-      const float2 dj = ld2(&sm.A.DT[r][2 * cj]);
-      float s[CW], ds[CW];
-      ldw<CW>(&sm.A.S[r][ch0], s);
-      ldw<CW>(&sm.A.dS[r][ch0], ds);
+    // K = kVB value rows in steps of 4 (rows past nvb are zero)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float ou = at(o4, u), xu = at(x4, u), du = at(d4, u);
-        MP[u][0] = fmaf(ou, dj.x, MP[u][0]);
-        MP[u][1] = fmaf(ou, dj.y, MP[u][1]);
-        ML[u][0] = fmaf(xu, dj.x, ML[u][0]);
-        ML[u][1] = fmaf(xu, dj.y, ML[u][1]);
+    for (int ks = 0; ks < kVB; ks += 4) {
+      const int kr = ks + kq;
+      const float ao = sm.A.dOT[kr][16 * tb + col], ax = sm.A.dXT[kr][16 * tb + col];
+      const float ad = sm.A.DT[kr][16 * tb + col];
 #pragma unroll
-        for (int e = 0; e < CW; ++e) {
-          AQ[u][e] = fmaf(ou, s[e], AQ[u][e]);
-          AE[u][e] = fmaf(xu, s[e], AE[u][e]);
-          AR[u][e] = fmaf(du, ds[e], AR[u][e]);
-        }
+      for (int m = 0; m < MT; ++m) {
+        const float bs = sm.A.S[kr][chan(m)], bds = sm.A.dS[kr][chan(m)];
+        AQ[m] = mfma4(ao, bs, AQ[m]);
+        AE[m] = mfma4(ax, bs, AE[m]);
+        AR[m] = mfma4(ad, bds, AR[m]);
       }
+      const float am = hh == 0 ? ao : ax;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        if (jb <= tb) MPL[jb] = mfma4(am, sm.A.DT[kr][16 * jb + col], MPL[jb]);
     }
   }
   vsum += __shfl_xor(vsum, 1);
@@ -817,167 +821,150 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       sm.B.R[t][c] = in ? xr[it] : 0.f;
     }
   }
-  // the decay factors of the state terms, and the C x C gradients
+  // the decay factors of the state terms, and the C x C gradients (tiles on and below the
+  // diagonal; the products below never read the others)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = 4 * ti + u;
+  for (int r = 0; r < 4; ++r) {
+    const int t = tr0 + r;
     const float sq = f.scale * eg[t], se = -eg[t], sr = wd[t];
 #pragma unroll
-    for (int e = 0; e < CW; ++e) {
-      AQ[u][e] *= sq;
-      AE[u][e] *= se;
-      AR[u][e] *= sr;
+    for (int m = 0; m < MT; ++m) {
+      AQ[m][r] *= sq;
+      AE[m][r] *= se;
+      AR[m][r] *= sr;
     }
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int j = 2 * cj + w;
+    for (int jb = 0; jb < 4; ++jb) {
+      if (jb > tb) continue;
+      const int j = 16 * jb + col;
       // (the exponent above the diagonal may overflow; it is discarded)
       const float dec = expf(gs[t] - gs[j]);
-      sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MP[u][w] * dec : 0.f;
-      sm.B.dL[t][j] = (j < t && t < n) ? -ML[u][w] * dec : 0.f;
+      if (hh == 0)
+        sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MPL[jb][r] * dec : 0.f;
+      else
+        sm.B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] * dec : 0.f;
     }
   }
   __syncthreads();
-  // lambda: this thread's share of sum_j r_j . (e^{g_n - g_j} dS'^T d_j)
+  // lambda: this lane's share of sum_j r_j . (e^{g_n - g_j} dS'^T d_j)
   float lam = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float rr[CW];
-    ldw<CW>(&sm.B.R[4 * ti + u][ch0], rr);
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int e = 0; e < CW; ++e) lam = fmaf(rr[e], AR[u][e], lam);
-  }
-  // dQ += dM R, dE += dL' R (rows past n of dM and dL' are zero: whole blocks of 8)
-  for (int j0 = 0; j0 < n; j0 += 8) {
+    for (int r = 0; r < 4; ++r) lam = fmaf(sm.B.R[tr0 + r][chan(m)], AR[m][r], lam);
+  // dQ += dM R, dE += dL' R over tokens j < 16 (tb + 1)
+  for (int j0 = 0; j0 < 16 * (tb + 1); j0 += 4) {
+    const int jr = j0 + kq;
+    const float am = sm.B.dM[16 * tb + col][jr], al = sm.B.dL[16 * tb + col][jr];
 #pragma unroll
-    for (int j = j0; j < j0 + 8; ++j) {
-      float rr[CW];
-      ldw<CW>(&sm.B.R[j][ch0], rr);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float m = sm.B.dM[4 * ti + u][j], l = sm.B.dL[4 * ti + u][j];
-#pragma unroll
-        for (int e = 0; e < CW; ++e) {
-          AQ[u][e] = fmaf(m, rr[e], AQ[u][e]);
-          AE[u][e] = fmaf(l, rr[e], AE[u][e]);
-        }
-      }
+    for (int m = 0; m < MT; ++m) {
+      const float br = sm.B.R[jr][chan(m)];
+      AQ[m] = mfma4(am, br, AQ[m]);
+      AE[m] = mfma4(al, br, AE[m]);
     }
   }
-  // dR += dM^T Q + dL'^T E
-  for (int i0 = 0; i0 < n; i0 += 8) {
+  // dR += dM^T Q + dL'^T E over tokens i >= 16 tb
+  for (int i0 = 16 * tb; i0 < kCMax; i0 += 4) {
+    const int ir = i0 + kq;
+    const float am = sm.B.dM[ir][16 * tb + col], al = sm.B.dL[ir][16 * tb + col];
 #pragma unroll
-    for (int i = i0; i < i0 + 8; ++i) {
-      const float4 m4 = ld4(&sm.B.dM[i][4 * ti]), l4 = ld4(&sm.B.dL[i][4 * ti]);
-      float qq[CW], ee[CW];
-      ldw<CW>(&sm.B.Q[i][ch0], qq);
-      ldw<CW>(&sm.B.E[i][ch0], ee);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float m = at(m4, u), l = at(l4, u);
-#pragma unroll
-        for (int e = 0; e < CW; ++e) AR[u][e] = fmaf(m, qq[e], fmaf(l, ee[e], AR[u][e]));
-      }
+    for (int m = 0; m < MT; ++m) {
+      AR[m] = mfma4(am, sm.B.Q[ir][chan(m)], AR[m]);
+      AR[m] = mfma4(al, sm.B.E[ir][chan(m)], AR[m]);
     }
   }
-  // gate gradient per token: q . dQ + e . dE - r . dR over the thread's channels, summed
-  // over the 32 lanes that share the tokens
-  float pg[4];
+  // per token: q . dQ + e . dE - r . dR (gate) and k . dE (scalar gain) over the lane's
+  // channels, summed over the 16 lanes of the row group, then over the two channel halves
+  float pg[4], pk[4];
+  const long long rowk0 = row0 * Dk;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = 4 * ti + u;
-    float qq[CW], ee[CW], rr[CW];
-    ldw<CW>(&sm.B.Q[t][ch0], qq);
-    ldw<CW>(&sm.B.E[t][ch0], ee);
-    ldw<CW>(&sm.B.R[t][ch0], rr);
-    float acc = 0.f;
+  for (int r = 0; r < 4; ++r) {
+    const int t = tr0 + r;
+    float acc = 0.f, acck = 0.f;
 #pragma unroll
-    for (int e = 0; e < CW; ++e) {
-      acc = fmaf(qq[e], AQ[u][e], acc);
-      acc = fmaf(ee[e], AE[u][e], acc);
-      acc = fmaf(-rr[e], AR[u][e], acc);
+    for (int m = 0; m < MT; ++m) {
+      const int c = chan(m);
+      acc = fmaf(sm.B.Q[t][c], AQ[m][r], acc);
+      acc = fmaf(sm.B.E[t][c], AE[m][r], acc);
+      acc = fmaf(-sm.B.R[t][c], AR[m][r], acc);
+      if (f.gain == GDR_GAIN_SCALAR && t < n && c < Dk)
+        acck = fmaf(ld_f(k, rowk0 + static_cast<long long>(t) * H * Dk + c), AE[m][r], acck);
     }
-    pg[u] = acc;
+    pg[r] = acc;
+    pk[r] = acck;
   }
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1)
+  for (int mm = 1; mm < 16; mm <<= 1)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pg[u] += __shfl_xor(pg[u], m);
+    for (int r = 0; r < 4; ++r) {
+      pg[r] += __shfl_xor(pg[r], mm);
+      pk[r] += __shfl_xor(pk[r], mm);
+    }
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dgs[hh][tr0 + r] = pg[r];
+      pks[hh][tr0 + r] = pk[r];
+    }
+  }
   // block sums of <dS', S> and lambda
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    sdot += __shfl_xor(sdot, m);
-    lam += __shfl_xor(lam, m);
+  for (int mm = 1; mm < 64; mm <<= 1) {
+    sdot += __shfl_xor(sdot, mm);
+    lam += __shfl_xor(lam, mm);
   }
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = sdot;
-    red[1][tid >> 6] = lam;
-  }
-  if (cj == 0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dgs[4 * ti + u] = pg[u];
+  if (lane == 0) {
+    red[0][wave] = sdot;
+    red[1][wave] = lam;
   }
   __syncthreads();
-  if (f.decay == GDR_DECAY_SCALAR && tid < kCMax) {
-    // dlog_alpha_t = sum_{i >= t} dg_i inside the chunk
-    float x = tid < n ? dgs[tid] : 0.f;
-    if (tid == n - 1) {
-      float st = 0.f, lt2 = 0.f;
+  if (tid < kCMax) {
+    if (f.decay == GDR_DECAY_SCALAR) {
+      // dlog_alpha_t = sum_{i >= t} dg_i inside the chunk
+      float x = tid < n ? dgs[0][tid] + dgs[1][tid] : 0.f;
+      if (tid == n - 1) {
+        float st = 0.f, lt2 = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        st += red[0][w];
-        lt2 += red[1][w];
+        for (int w = 0; w < kWaves; ++w) {
+          st += red[0][w];
+          lt2 += red[1][w];
+        }
+        x += eg[n - 1] * st + lt2;
       }
-      x += eg[n - 1] * st + lt2;
-    }
 #pragma unroll
-    for (int d = 1; d < kCMax; d <<= 1) {
-      const float y = __shfl_down(x, d, kCMax);
-      if (tid + d < kCMax) x += y;
+      for (int d = 1; d < kCMax; d <<= 1) {
+        const float y = __shfl_down(x, d, kCMax);
+        if (tid + d < kCMax) x += y;
+      }
+      if (tid < n) a.dla[tok(tid)] = x;
     }
-    if (tid < n) a.dla[tok(tid)] = x;
+    if (f.gain == GDR_GAIN_SCALAR && tid < n) a.dbeta[tok(tid)] = pks[0][tid] + pks[1][tid] + vdx[tid];
   }
   // ---- chain rule to the variant's inputs, stores ------------------------------------
-  float pk[4] = {0.f, 0.f, 0.f, 0.f};   // k . dE per token (scalar gain)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = 4 * ti + u;
+  for (int r = 0; r < 4; ++r) {
+    const int t = tr0 + r;
     if (t >= n) continue;
     const long long rowk = tok(t) * Dk;
     const float bt = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(t)] : 0.f;
 #pragma unroll
-    for (int e = 0; e < CW; ++e) {
-      const int c = ch0 + e;
+    for (int m = 0; m < MT; ++m) {
+      const int c = chan(m);
       if (c >= Dk) continue;
-      const float de = AE[u][e], dr = AR[u][e];
-      const float kk = ld_f(k, rowk + c);
-      a.dq[rowk + c] = AQ[u][e];
+      const float de = AE[m][r], dr = AR[m][r];
+      a.dq[rowk + c] = AQ[m][r];
       float dkv;
       if (f.gain == GDR_GAIN_SCALAR) {
         dkv = bt * de;
-        pk[u] = fmaf(kk, de, pk[u]);
       } else {
         dkv = ld_f(er, rowk + c) * de;
-        a.derase[rowk + c] = kk * de;
+        a.derase[rowk + c] = ld_f(k, rowk + c) * de;
       }
       if (f.wkey == GDR_WKEY_EXPLICIT)
         a.dwk[rowk + c] = dr;
       else
         dkv += dr;
       a.dk[rowk + c] = dkv;
-    }
-  }
-  if (f.gain == GDR_GAIN_SCALAR) {
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pk[u] += __shfl_xor(pk[u], m);
-    if (cj == 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 4 * ti + u;
-        if (t < n) a.dbeta[tok(t)] = pk[u] + vdx[t];
-      }
     }
   }
 }
@@ -992,13 +979,13 @@ hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_prep_kernel<IO, 128>), gp, dim3(kPrThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gs((a.f.Dv + kBV - 1) / kBV, a.f.H, a.f.B);
+  const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);
   if (a.f.Dk <= 32)
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 32>), gs, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_state_kernel<IO, 32>), gs, dim3(kStThreads), 0, s, a);
   else if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 64>), gs, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_state_kernel<IO, 64>), gs, dim3(kStThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 128>), gs, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_state_kernel<IO, 128>), gs, dim3(kStThreads), 0, s, a);
   return hipGetLastError();
 }
 
