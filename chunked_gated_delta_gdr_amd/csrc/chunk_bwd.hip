@@ -156,79 +156,64 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // thread (ti, cj): rows 4 ti .. 4 ti + 3 and columns 2 cj, 2 cj + 1 of the C x C products;
-  // rows 4 ti .. and columns CW cj .. CW cj + CW - 1 of W and U
-  const int ti = tid >> 5, cj = tid & 31;
-  // LP[i][j] = exp(g_i - g_j) (X_i . R_j) for j < i (or j <= i), zero elsewhere
+  // fp32 MFMA tiles (lane layout as for mfma4): wave w, lane (col, kq)
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kq = lane >> 4;
+  // LP[i][j] = exp(g_i - g_j) (X_i . R_j) on the 10 tiles on and below the diagonal (j < i,
+  // or j <= i), tile u = wave and wave + 8; the tiles above are never read
   auto gram = [&](const float(*X)[LD], bool incl_diag) {
-    float acc[4][2] = {};
-    if (2 * cj <= 4 * ti + 3) {
-#pragma unroll 4
-      for (int c = 0; c < DK; c += 4) {
-        float4 x[4], r[2];
+    for (int u = wave; u < 10; u += 8) {
+      const int ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+      const int jb = u - ib * (ib + 1) / 2;
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int ks = 0; ks < DK; ks += 4) acc = mfma4(X[16 * ib + col][ks + kq], Rs[16 * jb + col][ks + kq], acc);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = ld4(&X[4 * ti + u][c]);
-#pragma unroll
-        for (int w = 0; w < 2; ++w) r[w] = ld4(&Rs[2 * cj + w][c]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int w = 0; w < 2; ++w) fma4(acc[u][w], x[u], r[w]);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+        const bool keep = j < i || (incl_diag && j == i);
+        LP[i][j] = keep ? expf(gs[i] - gs[j]) * acc[r] : 0.f;
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int i = 4 * ti + u, j = 2 * cj + w;
-        const bool keep = j < i || (incl_diag && j == i);
-        LP[i][j] = keep ? expf(gs[i] - gs[j]) * acc[u][w] : 0.f;
-      }
   };
   gram(Es, false);
   __syncthreads();
   tri::inverse_blocks(LP, Tm, Zs, -1, tid, tid < 256);
   gram(Xs, true);
   __syncthreads();
-  {   // T and P of the chunk (C x C) for the sweep
+  {   // T and P of the chunk (C x C) for the sweep (P is zero above the diagonal)
     const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
     for (int idx = tid; idx < C * C; idx += kThreads) {
-      a.Tw[cc + idx] = Tm[idx / C][idx % C];
-      a.Pw[cc + idx] = LP[idx / C][idx % C];
+      const int i = idx / C, j = idx % C;
+      a.Tw[cc + idx] = Tm[i][j];
+      a.Pw[cc + idx] = j <= i ? LP[i][j] : 0.f;
     }
   }
-  const int ch0 = CW * cj;
-  // acc = T[rows] (Y (.) s) over the thread's columns, with row s of Y scaled by scl(s)
-  auto tri_product = [&](const float(*Y)[LD], auto &&scl, float (&acc)[4][CW]) {
+  // T (Y (.) scl) on the tiles (token block ib = wave % 4, channel blocks MT (wave / 4) + m):
+  // T is lower triangular, so the sum over tokens s ends with block ib
+  constexpr int MT = DK / 32;
+  const int ib = wave & 3, cb0 = MT * (wave >> 2);
+  auto tri_product = [&](const float(*Y)[LD], auto &&scl, float4v (&acc)[MT]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int m = 0; m < MT; ++m) acc[m] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < 16 * (ib + 1); s0 += 4) {
+      const float at_ = Tm[16 * ib + col][s0 + kq];
+      const float sc = scl(s0 + kq);
 #pragma unroll
-      for (int e = 0; e < CW; ++e) acc[u][e] = 0.f;
-    const int send = min(4 * ti + 4, n);
-#pragma unroll 4
-    for (int s0 = 0; s0 < send; ++s0) {
-      float y[CW];
-      const float sc = scl(s0);
-      ldw<CW>(&Y[s0][ch0], y);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float tv = sc * Tm[4 * ti + u][s0];   // zero above the diagonal
-#pragma unroll
-        for (int e = 0; e < CW; ++e) acc[u][e] = fmaf(tv, y[e], acc[u][e]);
-      }
+      for (int m = 0; m < MT; ++m) acc[m] = mfma4(at_, sc * Y[s0 + kq][16 * (cb0 + m) + col], acc[m]);
     }
   };
   {   // W = T (e^g (.) E), [B, H, NC, C, Dk]
-    float acc[4][CW];
+    float4v acc[MT];
     tri_product(Es, [&](int s0) { return eg[s0]; }, acc);
     float *Wc = a.Ww + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * ti + u;
-      if (t >= n) continue;
+    for (int m = 0; m < MT; ++m) {
+      const int c = 16 * (cb0 + m) + col;
 #pragma unroll
-      for (int e = 0; e < CW; ++e)
-        if (ch0 + e < Dk) Wc[static_cast<long long>(t) * Dk + ch0 + e] = acc[u][e];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ib + 4 * kq + r;
+        if (t < n && c < Dk) Wc[static_cast<long long>(t) * Dk + c] = acc[m][r];
+      }
     }
   }
   // U = T V' by blocks of DK value columns, [B, T, H, Dv]
@@ -252,16 +237,15 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    float acc[4][CW];
+    float4v acc[MT];
     tri_product(Xs, [&](int) { return 1.f; }, acc);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * ti + u;
-      if (t >= n) continue;
+    for (int m = 0; m < MT; ++m) {
+      const int c = vb + 16 * (cb0 + m) + col;
 #pragma unroll
-      for (int e = 0; e < CW; ++e) {
-        const int c = vb + ch0 + e;
-        if (c < Dv) a.Uw[tok(t) * Dv + c] = acc[u][e];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ib + 4 * kq + r;
+        if (t < n && c < Dv) a.Uw[tok(t) * Dv + c] = acc[m][r];
       }
     }
   }
