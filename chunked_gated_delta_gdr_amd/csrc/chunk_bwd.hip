@@ -164,9 +164,15 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     for (int u = wave; u < 10; u += 8) {
       const int ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
       const int jb = u - ib * (ib + 1) / 2;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int ks = 0; ks < DK; ks += 4) acc = mfma4(X[16 * ib + col][ks + kq], Rs[16 * jb + col][ks + kq], acc);
+      float4v ap[4];   // four independent accumulator chains, summed below
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK; ks += 16)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          ap[p] = mfma4(X[16 * ib + col][ks + 4 * p + kq], Rs[16 * jb + col][ks + 4 * p + kq], ap[p]);
+      const float4v acc = (ap[0] + ap[1]) + (ap[2] + ap[3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
@@ -366,10 +372,15 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     __syncthreads();
     if (ci + 1 < a.NC) cload(ci + 1);   // in flight during this chunk's products
     {   // D = U - W S^T, tile (tb, rb)
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int ks = 0; ks < DK; ks += 4)
-        acc = mfma4(Ws[16 * tb + col][ks + kq], Ss[16 * rb + col][ks + kq], acc);
+      float4v ap[4];   // four independent accumulator chains, summed below
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK; ks += 16)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          ap[p] = mfma4(Ws[16 * tb + col][ks + 4 * p + kq], Ss[16 * rb + col][ks + 4 * p + kq], ap[p]);
+      const float4v acc = (ap[0] + ap[1]) + (ap[2] + ap[3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
@@ -388,9 +399,13 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
         const int u = wave + 8 * m;
         if (u >= NTS) continue;
         const int rbs = u / NCB, cbs = u % NCB;
-        float4v acc = Sacc[m] * gl;
-        for (int t0 = 0; t0 < n; t0 += 4)
+        float4v acc = Sacc[m] * gl, acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
+        // (rows past n of Dl are zero, and n + 7 < 64 + 8: the pairs stay inside the tiles)
+        for (int t0 = 0; t0 < n; t0 += 8) {
           acc = mfma4(Dl[t0 + kq][16 * rbs + col], ld_f(&Rs[t0 + kq][16 * cbs + col], 0), acc);
+          acc2 = mfma4(Dl[t0 + 4 + kq][16 * rbs + col], ld_f(&Rs[t0 + 4 + kq][16 * cbs + col], 0), acc2);
+        }
+        acc += acc2;
         Sacc[m] = acc;
         // the LDS mirror for the next chunk's W S^T (its reads of this chunk are done)
 #pragma unroll
@@ -558,17 +573,23 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO, tile (tb, rb); P is zero above the
     // diagonal and T, P, dO rows past n (inside the chunk) are zero
     {
-      float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int ks = 0; ks < DK; ks += 4)
-        a1 = mfma4(Ks[16 * tb + col][ks + kq], dS[16 * rb + col][ks + kq], a1);
+      // two independent accumulator chains for R dS^T (summed below), one for P^T dO
+      float4v a1[2], a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) a1[p] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ks = 0; ks < DK; ks += 8)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          a1[p] = mfma4(Ks[16 * tb + col][ks + 4 * p + kq], dS[16 * rb + col][ks + 4 * p + kq], a1[p]);
+      a1[0] += a1[1];
       // (i0 < n keeps every row read below C, where T and P were loaded)
       for (int i0 = 16 * tb; i0 < n; i0 += 4)
         a2 = mfma4(Pm[i0 + kq][16 * tb + col], dOs[i0 + kq][16 * rb + col], a2);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tr0 + r, rr = 16 * rb + col;
-        dDs[t][rr] = (t < n && rr < nv) ? fmaf(wd[t], a1[r], f.scale * a2[r]) : 0.f;
+        dDs[t][rr] = (t < n && rr < nv) ? fmaf(wd[t], a1[0][r], f.scale * a2[r]) : 0.f;
       }
     }
     __syncthreads();
@@ -602,11 +623,12 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
         const int u = wave + 8 * m;
         if (u >= NTS) continue;
         const int rbs = u / NCB, cbs = u % NCB;
-        float4v acc = dSacc[m] * gl;
+        float4v acc = dSacc[m] * gl, acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
         for (int t0 = 0; t0 < n; t0 += 4) {
           acc = mfma4(Am[t0 + kq][16 * rbs + col], Ks[t0 + kq][16 * cbs + col], acc);
-          acc = mfma4(-Bm[t0 + kq][16 * rbs + col], Es[t0 + kq][16 * cbs + col], acc);
+          acc2 = mfma4(Bm[t0 + kq][16 * rbs + col], Es[t0 + kq][16 * cbs + col], acc2);
         }
+        acc -= acc2;
         dSacc[m] = acc;
         // the LDS mirror for the next chunk's R dS^T (its reads of this chunk are done)
 #pragma unroll
