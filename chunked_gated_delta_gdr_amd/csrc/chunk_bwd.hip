@@ -1,4 +1,4 @@
-// Backward pass of the chunked gated delta rule: fp32 arithmetic on the vector ALUs.
+// Backward pass of the chunked gated delta rule: fp32 arithmetic, products on the matrix cores.
 //
 // The pages give no backward; this is the derivative of the chunk-wise forward
 // ("Declaracao do Problema" of the MatMul-only inversion summary).  Per chunk of n tokens
