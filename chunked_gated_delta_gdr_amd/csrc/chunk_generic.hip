@@ -1,38 +1,48 @@
-// Generic chunk-parallel gated delta-rule forward: fp32 arithmetic on the vector ALUs.
+// Generic chunk-parallel gated delta-rule forward: fp32 arithmetic, products on the fp32
+// matrix cores.
 //
-// This is the fp32 path (and the fallback for shapes the matrix-core kernel does not
-// cover).  One workgroup owns one (batch, head, value tile of BV state rows) and walks
-// the sequence chunk by chunk; the state tile stays in LDS for the whole sequence.
+// This is the fp32 path (and the kernel for every shape and option the bf16 matrix-core
+// kernel does not cover).  One workgroup of 8 waves owns one (batch, head, value tile of BV
+// state rows) and walks the sequence chunk by chunk; the state tile lives in the waves' MFMA
+// accumulators for the whole sequence (16 x 16 tiles), mirrored in LDS for the products that
+// read it as an operand.
 //
-// Per chunk of n <= C tokens (chunk-wise form and T = (I - A)^-1 of the MatMul-only
-// inversion summary, "Declaracao do Problema"):
+// Per chunk of n <= C tokens (chunk-wise form and T = (I - A)^-1 of the MatMul-only inversion
+// summary, "Declaracao do Problema"):
 //   g      inclusive cumulative sum of log alpha inside the chunk
 //   L_ij   = exp(g_i - g_j) (e_i . r_j)              for j < i   (A = -L)
 //   X      = V' - (e^g (.) E) S^T                      (value tile only)
 //   T      = (I - A)^-1: forward substitution inside the four 16 x 16 diagonal blocks, then
-//            the off-diagonal blocks as block products.  With a band limit N only entries
-//            with i - j <= N are kept (they use only band entries of the factors: Lemma 3.1
-//            of the same summary, Metodologia 1-2), so N >= n - 1 runs exactly the same
-//            instructions as the exact path.
+//            the off-diagonal blocks as block products (tri_blocks.h).  With a band limit N
+//            only entries with i - j <= N are kept (they use only band entries of the
+//            factors: Lemma 3.1 of the same summary, Metodologia 1-2), so N >= n - 1 runs
+//            exactly the same instructions as the exact path.
 //            Optionally (S > 0, band start N) the parallel residual correction of the
 //            same summary, Metodologia 3: T = T0 sum_{s<=S} E^s, E = I - (I - A) T0.
 //   D      = T X                                     (= U - W S^T of the WY form)
 //   P_ij   = exp(g_i - g_j) (q_i . r_j)              for j <= i
 //   O      = scale ((e^g (.) Q) S^T + P D)
 //   S      <- e^{g_n} S + D^T (e^{g_n - g} (.) R)
+// Products: v_mfma_f32_16x16x4_f32 (fp32 operands and accumulation; lane l gives A[l % 16]
+// [l / 16] and B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16], r < 4).  The tiles of
+// X, D and O are spread one per wave; the ten C x C tiles on and below the diagonal two per
+// wave at most.
 #include "common.h"
 #include "tri_blocks.h"
 
 namespace gdr {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBV = 16;     // state rows per workgroup
-constexpr int kCMax = 64;   // largest chunk
+constexpr int kThreads = 512;   // 8 waves
+constexpr int kCMax = 64;       // largest chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4v mfma4(float a, float b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
 __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &y) {
   acc = fmaf(x.x, y.x, acc);
   acc = fmaf(x.y, y.y, acc);
@@ -40,17 +50,26 @@ __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &
   acc = fmaf(x.w, y.w, acc);
 }
 
-template <typename IO, int DK, bool CHD>
+// tile u (0..9) of the ten 16 x 16 tiles on and below the diagonal of a 64 x 64 matrix
+__device__ __forceinline__ void lower_tile(int u, int &ib, int &jb) {
+  ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+  jb = u - ib * (ib + 1) / 2;
+}
+
+template <typename IO, int DK, bool CHD, int BV>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   // CHD: one decay per key channel (log_alpha [B, T, H, Dk]).  The pairwise decay of channel
   // c between tokens j <= i is 2^(G_ic - G_jc) with G the in-chunk cumulative log2 decay, so it
-  // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise), the
-  // state is read through e^G (.) e and e^G (.) q, and the update uses e^{G_C - G} (.) r and
-  // S Diag(e^{G_C}).  Every exponent that is kept is <= 0.
-  // fp32 row stride of the [token][channel] tiles: 16-byte aligned rows whose starts fall on
-  // distinct 16-byte bank groups for 16 consecutive rows (conflict-free 16-byte reads)
-  constexpr int LD = DK + 4;
-  constexpr int kLoadIt = kCMax * DK / kThreads;   // elements per thread of one staged tile
+  // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise, both on
+  // the vector ALUs), the state is read through 2^G (.) e and 2^G (.) q, and the update uses
+  // 2^(G_C - G) (.) r and S Diag(2^G_C).  Every exponent that is kept is <= 0.
+  constexpr int LD = DK + 4;            // fp32 row stride of the [token][channel] tiles
+  constexpr int kLoadIt = kCMax * DK / kThreads;
+  constexpr int NCB = DK / 16;          // channel blocks
+  constexpr int NRB = BV / 16;          // value-row blocks
+  constexpr int NTS = NRB * NCB;        // state tiles
+  constexpr int NTW = (NTS + 7) / 8;    // state tiles per wave
+  constexpr int NXT = 4 * NRB;          // tiles of the C x BV products X, D, O
   const IO *__restrict__ q = static_cast<const IO *>(a.q);
   const IO *__restrict__ k = static_cast<const IO *>(a.k);
   const IO *__restrict__ v = static_cast<const IO *>(a.v);
@@ -61,24 +80,41 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
 
   const int tid = threadIdx.x;
   const int vt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int v0 = vt * kBV;
-  const int nv = min(kBV, a.Dv - v0);
+  const int v0 = vt * BV;
+  const int nv = min(BV, a.Dv - v0);
   const int Dk = a.Dk, Dv = a.Dv, H = a.H, T = a.T;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kq = lane >> 4;
+  const bool xwave = wave < NXT;        // owns the (tb, rb) tile of X, D and O
+  const int tb = wave & 3, rb = wave >> 2;
 
   __shared__ __align__(16) float Rs[kCMax][LD];     // write keys r
   __shared__ __align__(16) float Xs[kCMax][LD];     // erase keys e, then queries q
-  __shared__ float LP[kCMax][kCMax + 1];            // L (strict lower), then P (lower)
+  __shared__ float LP[kCMax][kCMax + 1];            // L (then E of the residual), then P
   __shared__ __align__(16) float Tm[kCMax][kCMax + 4];   // T, row-major
-  __shared__ __align__(16) float Zs[32][32 + 4];         // block products in flight
+  __shared__ __align__(16) float Zs[32][36];             // block products in flight
   __shared__ __align__(16) float Zb[CHD ? 1 : kCMax][kCMax + 4];   // residual-correction series
   __shared__ __align__(16) float Gs[CHD ? kCMax : 1][CHD ? LD : 4];  // cumulative log2 decays
-  __shared__ __align__(16) float Ss[kBV][LD];       // state tile
-  __shared__ __align__(16) float Xv[kCMax][kBV];    // X
-  __shared__ __align__(16) float Dl[kCMax][kBV];    // D
+  __shared__ __align__(16) float Ss[BV][LD];        // mirror of the state tile
+  __shared__ __align__(16) float Xv[kCMax][BV];     // X
+  __shared__ __align__(16) float Dl[kCMax][BV];     // D
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
 
   const long long sh = static_cast<long long>(b) * H + h;  // (b, h) index
-  for (int idx = tid; idx < kBV * LD; idx += kThreads) {
+  // state tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
+  float4v Sacc[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int u = wave + 8 * m;
+    const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = 0.f;
+      if (u < NTS && a.state_in != nullptr && row + r < nv && c < Dk)
+        x = a.state_in[(sh * Dv + v0 + row + r) * Dk + c];
+      Sacc[m][r] = x;
+    }
+  }
+  for (int idx = tid; idx < BV * LD; idx += kThreads) {
     const int r = idx / LD, c = idx % LD;
     float s = 0.f;
     if (a.state_in != nullptr && r < nv && c < Dk) s = a.state_in[(sh * Dv + v0 + r) * Dk + c];
@@ -93,143 +129,52 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   if (a.wkey == GDR_WKEY_DIAG_PRECOND && tid < Dk)
     hreg = a.pc_h_in != nullptr ? a.pc_h_in[sh * Dk + tid] : a.h0;
 
-  // thread tiles: 4 x 4 blocks of the C x C products, 2 x 2 blocks of the C x kBV ones
-  const int bi = tid >> 4, bj = tid & 15;      // rows 4 bi.., columns 4 bj..
-  const int t0 = 2 * (tid >> 3), r0 = 2 * (tid & 7);
+  // one of the ten lower 16 x 16 tiles (ib, jb) of a C x C product of lower-triangular
+  // factors: sum over k from column block jb to row block ib of (sgnX X)[rows][k] Y[k][cols],
+  // X and Y row-major in LDS (row strides LX, LY)
+  auto lower_mm = [&](const float *X, int LX, const float *Y, int LY, int u, float sgnX) {
+    int ib, jb;
+    lower_tile(u, ib, jb);
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 16 * jb; k0 < 16 * ib + 16; k0 += 4)
+      acc = mfma4(sgnX * X[(16 * ib + col) * LX + k0 + kq], Y[(k0 + kq) * LY + 16 * jb + col], acc);
+    return acc;
+  };
 
   for (int c0 = 0; c0 < T; c0 += a.C) {
     const int n = min(a.C, T - c0);
     // token (b, c0 + t, h) row index in [B, T, H]
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
-    // Element (t, c) of a [B, T, H, Dk] tensor sits t * H * Dk + c after the chunk's first
-    // token row (a 32-bit offset: 64 H Dk < 2^31).  stage() copies rows 0..n-1 of such a tile
-    // into dst (zero beyond n and Dk).  Every load reads a valid element (indices clamped into
-    // the tile) and the mask is applied afterwards, so the loads carry no branch and all of a
-    // tile's loads are in flight together.
     const long long row0 = tok(0);
     const int rstride = H * Dk;
-    auto stage = [&](float(*dst)[LD], auto &&load) {
-      float x[kLoadIt];
-#pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        const int tc = min(t, n - 1), cc = min(c, Dk - 1);
-        x[it] = load(tc, tc * rstride + cc);
-      }
-#pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        if (!(t < n && c < Dk)) x[it] = 0.f;
-      }
-#pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads;
-        dst[idx / DK][idx % DK] = x[it];
-      }
-    };
-    // LP[i][j] = exp(g_i - g_j) (Xs_i . Rs_j) for j < i (or j <= i), zero above; rows past n
-    // hold zero keys, so they come out zero
-    auto gram = [&](bool incl_diag) {
-      if (bj > bi) return;
-      float acc[4][4] = {};
-      if constexpr (CHD) {
-#pragma unroll 2
-        for (int c = 0; c < DK; c += 4) {
-          float4 x[4], r[4], gi[4], gj[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            x[u] = ld4(&Xs[4 * bi + u][c]);
-            r[u] = ld4(&Rs[4 * bj + u][c]);
-            gi[u] = ld4(&Gs[4 * bi + u][c]);
-            gj[u] = ld4(&Gs[4 * bj + u][c]);
-          }
-          // (entries above the diagonal may overflow here; they are discarded below)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float4 d = make_float4(x[u].x * exp2f(gi[u].x - gj[w].x), x[u].y * exp2f(gi[u].y - gj[w].y),
-                                           x[u].z * exp2f(gi[u].z - gj[w].z), x[u].w * exp2f(gi[u].w - gj[w].w));
-              fma4(acc[u][w], d, r[w]);
-            }
-        }
-      } else {
-#pragma unroll 4
-        for (int c = 0; c < DK; c += 4) {
-          float4 x[4], r[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            x[u] = ld4(&Xs[4 * bi + u][c]);
-            r[u] = ld4(&Rs[4 * bj + u][c]);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) fma4(acc[u][w], x[u], r[w]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int i = 4 * bi + u, j = 4 * bj + w;
-          const float dec = CHD ? 1.f : expf(gs[i] - gs[j]);
-          LP[i][j] = (j < i || (incl_diag && j == i)) ? dec * acc[u][w] : 0.f;
-        }
-    };
-    // (Xs_t . Ss_r) for the thread's 2 x 2 block of tokens t0.. and state rows r0..
-    // (with per-channel decays: the rows are read as 2^G (.) x)
-    auto dot_state = [&](float (&acc)[2][2]) {
-#pragma unroll 4
-      for (int c = 0; c < DK; c += 4) {
-        float4 x0 = ld4(&Xs[t0][c]), x1 = ld4(&Xs[t0 + 1][c]);
-        if constexpr (CHD) {
-          const float4 g0 = ld4(&Gs[t0][c]), g1 = ld4(&Gs[t0 + 1][c]);
-          x0 = make_float4(x0.x * exp2f(g0.x), x0.y * exp2f(g0.y), x0.z * exp2f(g0.z), x0.w * exp2f(g0.w));
-          x1 = make_float4(x1.x * exp2f(g1.x), x1.y * exp2f(g1.y), x1.z * exp2f(g1.z), x1.w * exp2f(g1.w));
-        }
-        const float4 s0 = ld4(&Ss[r0][c]), s1 = ld4(&Ss[r0 + 1][c]);
-        fma4(acc[0][0], x0, s0);
-        fma4(acc[0][1], x0, s1);
-        fma4(acc[1][0], x1, s0);
-        fma4(acc[1][1], x1, s1);
-      }
-    };
 
     __syncthreads();  // previous chunk done with every buffer
-    // write keys (the preconditioned ones are formed from the staged keys below)
-    const IO *kc = k + row0 * Dk;
-    {
-      const IO *src = ((a.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
-      stage(Rs, [&](int, int o) { return ld_f(src, o); });
-    }
-    // erase keys
-    if (a.gain == GDR_GAIN_SCALAR) {
-      const float *bc = a.beta + row0;
-      stage(Xs, [&](int t, int o) { return bc[t * H] * ld_f(kc, o); });
-    } else {
+    {   // write keys (the preconditioned ones are formed from them below), erase keys and, with
+        // per-channel decays, the log decays: all loads first (clamped), then the masked stores
+      float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xl[CHD ? kLoadIt : 1];
+      const IO *rsrc = ((a.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk, *kc = k + row0 * Dk;
       const IO *ec = er + row0 * Dk;
-      stage(Xs, [&](int, int o) { return ld_f(ec, o) * ld_f(kc, o); });
-    }
-    if constexpr (CHD) {
-      // per-channel decays: stage, then each channel's inclusive cumulative sum in log2 units
-      // (rows past n are zero, so the sums stay flat there)
-      const float *lac = a.log_alpha + row0 * Dk;
-      stage(Gs, [&](int, int o) { return lac[o]; });
-      __syncthreads();
-      if (tid < DK) {
-        float gv[kCMax];
+      const float *bc = a.beta + row0;
 #pragma unroll
-        for (int t = 0; t < kCMax; ++t) gv[t] = Gs[t][tid];
-        float g = 0.f;
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const int tc = min(t, n - 1), o = tc * rstride + min(c, Dk - 1);
+        xr[it] = ld_f(rsrc, o);
+        xk[it] = ld_f(kc, o);
+        xg[it] = a.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
+        if constexpr (CHD) xl[it] = a.log_alpha[row0 * Dk + o];
+      }
 #pragma unroll
-        for (int t = 0; t < kCMax; ++t) {
-          g = fmaf(gv[t], kLog2e, g);
-          Gs[t][tid] = g;
-        }
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const bool in = t < n && c < Dk;
+        Rs[t][c] = in ? xr[it] : 0.f;
+        Xs[t][c] = in ? xg[it] * xk[it] : 0.f;
+        if constexpr (CHD) Gs[t][c] = in ? xl[it] : 0.f;
       }
     }
-    // gates: inclusive cumulative sum of log alpha over the chunk (one wave)
+    // gates: inclusive cumulative sum of log alpha over the chunk (one wave; zero without a
+    // scalar decay)
     if (tid < kCMax) {
       float g = (a.decay == GDR_DECAY_SCALAR && tid < n) ? a.log_alpha[tok(tid)] : 0.f;
 #pragma unroll
@@ -253,241 +198,298 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       }
       __syncthreads();
       if (tid < Dk) {
-        // rows past n hold zero keys (their u comes out zero); the accumulator skips them
-        float kv[kCMax];
+        // rows past n hold zero keys (their u comes out zero); the accumulator skips them.
+        // Keys are read 16 at a time ahead of the serial chain.
+        for (int t0 = 0; t0 < kCMax; t0 += 16) {
+          float kv[16];
 #pragma unroll
-        for (int t = 0; t < kCMax; ++t) kv[t] = Rs[t][tid];
+          for (int t = 0; t < 16; ++t) kv[t] = Rs[t0 + t][tid];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const float hn = fmaf(a.rho, hreg, kv[t] * kv[t]);
+            hreg = t0 + t < n ? hn : hreg;
+            Rs[t0 + t][tid] = kv[t] / fmaf(hreg, icorr[t0 + t], a.eps);
+          }
+        }
+      }
+    }
+    if constexpr (CHD) {
+      // each channel's inclusive cumulative sum of log decays in log2 units (rows past n are
+      // zero, so the sums stay flat there)
+      __syncthreads();
+      if (tid < DK) {
+        float gv[kCMax];
+#pragma unroll
+        for (int t = 0; t < kCMax; ++t) gv[t] = Gs[t][tid];
+        float g = 0.f;
 #pragma unroll
         for (int t = 0; t < kCMax; ++t) {
-          const float hn = fmaf(a.rho, hreg, kv[t] * kv[t]);
-          hreg = t < n ? hn : hreg;
-          Rs[t][tid] = kv[t] / fmaf(hreg, icorr[t], a.eps);
+          g = fmaf(gv[t], kLog2e, g);
+          Gs[t][tid] = g;
         }
       }
     }
     __syncthreads();
+
+    // LP[i][j] = decay_ij (X_i . R_j) for j < i (or j <= i) on the tiles on and below the
+    // diagonal; rows past n hold zero keys, so they come out zero
+    auto gram = [&](bool incl_diag) {
+      if constexpr (CHD) {
+        // vector ALUs (the decay depends on the channel): thread = rows 4 ti .. 4 ti + 3,
+        // columns 2 cj, 2 cj + 1
+        const int ti = tid >> 5, cj = tid & 31;
+        float acc[4][2] = {};
+        if (2 * cj <= 4 * ti + 3) {
+#pragma unroll 2
+          for (int c = 0; c < DK; c += 4) {
+            float4 x[4], gi[4], r[2], gj[2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              x[u] = ld4(&Xs[4 * ti + u][c]);
+              gi[u] = ld4(&Gs[4 * ti + u][c]);
+            }
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              r[w] = ld4(&Rs[2 * cj + w][c]);
+              gj[w] = ld4(&Gs[2 * cj + w][c]);
+            }
+            // (entries above the diagonal may overflow here; they are discarded below)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const float4 d = make_float4(x[u].x * exp2f(gi[u].x - gj[w].x), x[u].y * exp2f(gi[u].y - gj[w].y),
+                                             x[u].z * exp2f(gi[u].z - gj[w].z), x[u].w * exp2f(gi[u].w - gj[w].w));
+                fma4(acc[u][w], d, r[w]);
+              }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const int i = 4 * ti + u, j = 2 * cj + w;
+            LP[i][j] = (j < i || (incl_diag && j == i)) ? acc[u][w] : 0.f;
+          }
+      } else {
+        for (int u = wave; u < 10; u += 8) {
+          int ib, jb;
+          lower_tile(u, ib, jb);
+          float4v ap[2];   // two independent accumulator chains, summed below
+#pragma unroll
+          for (int p = 0; p < 2; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+          for (int ks = 0; ks < DK; ks += 8)
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+              ap[p] = mfma4(Xs[16 * ib + col][ks + 4 * p + kq], Rs[16 * jb + col][ks + 4 * p + kq], ap[p]);
+          const float4v acc = ap[0] + ap[1];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+            LP[i][j] = (j < i || (incl_diag && j == i)) ? expf(gs[i] - gs[j]) * acc[r] : 0.f;
+          }
+        }
+      }
+    };
+    // the read of the state through row t of Y (E or Q): e^g_t Y_t, or 2^G_t (.) Y_t
+    auto state_read = [&](const float(*Y)[LD], float4v &acc) {
+      acc = float4v{0.f, 0.f, 0.f, 0.f};
+      const int t = 16 * tb + col;
+#pragma unroll 8
+      for (int ks = 0; ks < DK; ks += 4) {
+        float y = Y[t][ks + kq];
+        if constexpr (CHD) y *= exp2f(Gs[t][ks + kq]);
+        acc = mfma4(y, Ss[16 * rb + col][ks + kq], acc);
+      }
+      if constexpr (!CHD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= eg[16 * tb + 4 * kq + r];
+      }
+    };
+
     // L (strict lower)
     gram(false);
     // X = V' - (e^g (.) E) S^T on the value tile
-    {
-      float vp[2][2];   // (loads from clamped indices; entries outside the tile are masked below)
+    if (xwave) {
+      float vp[4];   // (loads from clamped indices; entries outside the tile are masked below)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int r = 0; r < 4; ++r) {
+        const int t = min(16 * tb + 4 * kq + r, n - 1), rr = min(16 * rb + col, nv - 1);
+        const long long vi = tok(t) * Dv + v0 + rr;
+        const float vv = ld_f(v, vi);
+        vp[r] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
+      }
+      float4v acc;
+      state_read(Xs, acc);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = min(t0 + u, n - 1), r = min(r0 + w, nv - 1);
-          const long long vi = tok(t) * Dv + v0 + r;
-          const float vv = ld_f(v, vi);
-          vp[u][w] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
-        }
-      float acc[2][2] = {};
-      dot_state(acc);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          Xv[t][r] = (t < n && r < nv) ? vp[u][w] - eg[t] * acc[u][w] : 0.f;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
+        Xv[t][rr] = (t < n && rr < nv) ? vp[r] - acc[r] : 0.f;
+      }
     }
     __syncthreads();
     // T = (I - A)^-1 by 16 x 16 blocks (exact, or its band i - j <= N)
-    tri::inverse_blocks(LP, Tm, Zs, a.N, tid);
+    tri::inverse_blocks(LP, Tm, Zs, a.N, tid, tid < 256);
     // Parallel residual correction of the band start T0 (MatMul-only inversion summary,
-    // Metodologia 3): E = I - (I - A) T0, Z = I + E (I + E (... (I + E))) with S factors
-    // (= sum_{s<=S} E^s), T = T0 Z.  E and Z are strictly lower / unit lower triangular, so
-    // each product sums over l < i (l <= i for T0 Z).  Thread: row i, columns jg .. jg + 15;
-    // every product is formed in registers and written back after a barrier (E over L, Z
-    // in place, T over T0).
+    // Metodologia 3): E = I - (I - A) T0 = I - T0 + A T0, Z = I + E (I + E (... (I + E))) with S
+    // factors (= sum_{s<=S} E^s), T = T0 Z.  All factors are lower triangular, so each product
+    // is formed on the ten lower tiles, each tile summing over the k-blocks between its
+    // column and row blocks; every product is formed in registers and written back after a
+    // barrier (E over L, Z in place, T over T0).
     if (CHD ? false : a.S > 0) {
-      const int i = tid >> 2, jg = (tid & 3) * 16;
-      // the rows of wave w are 16 w .. 16 w + 15, so every sum below ends before l = 16 (w + 1):
-      // a wave-uniform bound; the coefficients past the row's own bound are masked to zero
-      const int lwave = 16 * ((tid >> 6) + 1);
-      float acc[16];
-      // acc = sum_{l < lend} (+-Lm[i][l]) Tr[l][jg ..], four rows of Tr per batch of reads
-      auto row_product = [&](const auto *Lm, const float(*Tr)[kCMax + 4], int lend, bool neg) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-        for (int l0 = 0; l0 < lwave; l0 += 4) {
-          float x[4];
-          float4 t[4][4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float m = Lm[i][l0 + q];
-            x[q] = l0 + q < lend ? (neg ? -m : m) : 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t[q][u] = ld4(&Tr[l0 + q][jg + 4 * u]);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              acc[4 * u] = fmaf(x[q], t[q][u].x, acc[4 * u]);
-              acc[4 * u + 1] = fmaf(x[q], t[q][u].y, acc[4 * u + 1]);
-              acc[4 * u + 2] = fmaf(x[q], t[q][u].z, acc[4 * u + 2]);
-              acc[4 * u + 3] = fmaf(x[q], t[q][u].w, acc[4 * u + 3]);
-            }
-        }
-      };
-      // E_ij = delta_ij - T0_ij + (A T0)_ij, A = -L
-      row_product(LP, Tm, i, true);
-      float e[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) e[u] = ((jg + u == i) ? 1.f : 0.f) - Tm[i][jg + u] + acc[u];
+      float4v e[2];
+      for (int u = wave, m = 0; u < 10; u += 8, ++m) e[m] = lower_mm(&LP[0][0], kCMax + 1, &Tm[0][0], kCMax + 4, u, -1.f);
       __syncthreads();   // every row of A has been read
+      for (int u = wave, m = 0; u < 10; u += 8, ++m) {
+        int ib, jb;
+        lower_tile(u, ib, jb);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        LP[i][jg + u] = e[u];
-        Zb[i][jg + u] = (jg + u == i) ? 1.f : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+          LP[i][j] = ((i == j) ? 1.f : 0.f) - Tm[i][j] + e[m][r];
+        }
+      }
+      for (int idx = tid; idx < kCMax * kCMax; idx += kThreads) {
+        const int i = idx / kCMax, j = idx % kCMax;
+        Zb[i][j] = i == j ? 1.f : 0.f;
       }
       __syncthreads();
       for (int st = 0; st < a.S; ++st) {   // Z <- I + E Z
-        row_product(LP, Zb, i, false);
+        float4v z[2];
+        for (int u = wave, m = 0; u < 10; u += 8, ++m) z[m] = lower_mm(&LP[0][0], kCMax + 1, &Zb[0][0], kCMax + 4, u, 1.f);
         __syncthreads();
+        for (int u = wave, m = 0; u < 10; u += 8, ++m) {
+          int ib, jb;
+          lower_tile(u, ib, jb);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) Zb[i][jg + u] = ((jg + u == i) ? 1.f : 0.f) + acc[u];
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+            Zb[i][j] = ((i == j) ? 1.f : 0.f) + z[m][r];
+          }
+        }
         __syncthreads();
       }
-      // T = T0 Z (T0 is lower triangular: l <= i)
-      row_product(Tm, Zb, i + 1, false);
+      // T = T0 Z
+      float4v tz[2];
+      for (int u = wave, m = 0; u < 10; u += 8, ++m) tz[m] = lower_mm(&Tm[0][0], kCMax + 4, &Zb[0][0], kCMax + 4, u, 1.f);
       __syncthreads();
+      for (int u = wave, m = 0; u < 10; u += 8, ++m) {
+        int ib, jb;
+        lower_tile(u, ib, jb);
 #pragma unroll
-      for (int u = 0; u < 16; u += 4)
-        *reinterpret_cast<float4 *>(&Tm[i][jg + u]) = make_float4(acc[u], acc[u + 1], acc[u + 2], acc[u + 3]);
-      __syncthreads();
+        for (int r = 0; r < 4; ++r) Tm[16 * ib + 4 * kq + r][16 * jb + col] = tz[m][r];
+      }
     }
-    // queries replace the erase keys (last read before the barrier above)
-    {
+    {   // queries replace the erase keys (their last reads, L and X, were before the barriers above)
+      float xq[kLoadIt];
       const IO *qc = q + row0 * Dk;
-      stage(Xs, [&](int, int o) { return ld_f(qc, o); });
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        xq[it] = ld_f(qc, min(t, n - 1) * rstride + min(c, Dk - 1));
+      }
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        Xs[t][c] = (t < n && c < Dk) ? xq[it] : 0.f;
+      }
     }
     __syncthreads();
-    // D = T X: acc = X_tr; for s < t: acc += T_ts X_sr
-    {
-      float acc[2][2];
+    // D = T X (T lower triangular: the sum ends with the row block)
+    if (xwave) {
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < 16 * (tb + 1); s0 += 4)
+        acc = mfma4(Tm[16 * tb + col][s0 + kq], Xv[s0 + kq][16 * rb + col], acc);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float2 x = ld2(&Xv[t0 + u][r0]);
-        acc[u][0] = x.x;
-        acc[u][1] = x.y;
-      }
-      for (int s = 0; s < t0; ++s) {
-        const float2 x = ld2(&Xv[s][r0]);
-        const float a0 = Tm[t0][s], a1 = Tm[t0 + 1][s];
-        acc[0][0] = fmaf(a0, x.x, acc[0][0]);
-        acc[0][1] = fmaf(a0, x.y, acc[0][1]);
-        acc[1][0] = fmaf(a1, x.x, acc[1][0]);
-        acc[1][1] = fmaf(a1, x.y, acc[1][1]);
-      }
-      {   // s = t0 for the second row
-        const float2 x = ld2(&Xv[t0][r0]);
-        const float a1 = Tm[t0 + 1][t0];
-        acc[1][0] = fmaf(a1, x.x, acc[1][0]);
-        acc[1][1] = fmaf(a1, x.y, acc[1][1]);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<float2 *>(&Dl[t0 + u][r0]) = make_float2(acc[u][0], acc[u][1]);
+      for (int r = 0; r < 4; ++r) Dl[16 * tb + 4 * kq + r][16 * rb + col] = acc[r];
     }
     // P (lower incl. diagonal; L is no longer needed)
     gram(true);
     __syncthreads();
     // O = scale ((e^g (.) Q) S^T + P D)
-    {
-      float acc[2][2] = {};
-      dot_state(acc);
-      if constexpr (!CHD) {
+    if (xwave) {
+      float4v acc;
+      state_read(Xs, acc);
+      for (int j0 = 0; j0 < 16 * (tb + 1); j0 += 4)
+        acc = mfma4(LP[16 * tb + col][j0 + kq], Dl[j0 + kq][16 * rb + col], acc);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          acc[u][0] *= eg[t0 + u];
-          acc[u][1] *= eg[t0 + u];
-        }
-      }
-      for (int j = 0; j <= t0; ++j) {
-        const float2 d = ld2(&Dl[j][r0]);
-        const float p0 = LP[t0][j], p1 = LP[t0 + 1][j];
-        acc[0][0] = fmaf(p0, d.x, acc[0][0]);
-        acc[0][1] = fmaf(p0, d.y, acc[0][1]);
-        acc[1][0] = fmaf(p1, d.x, acc[1][0]);
-        acc[1][1] = fmaf(p1, d.y, acc[1][1]);
-      }
-      {   // j = t0 + 1 for the second row
-        const float2 d = ld2(&Dl[t0 + 1][r0]);
-        const float p1 = LP[t0 + 1][t0 + 1];
-        acc[1][0] = fmaf(p1, d.x, acc[1][0]);
-        acc[1][1] = fmaf(p1, d.y, acc[1][1]);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int t = t0 + u, r = r0 + w;
-          if (t < n && r < nv) st_f(out, tok(t) * Dv + v0 + r, a.scale * acc[u][w]);
-        }
-    }
-    if constexpr (CHD) {   // R <- 2^(G_C - G) (.) R for the update (P, its last other use, is done)
-#pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        Rs[t][c] *= exp2f(Gs[n - 1][c] - Gs[t][c]);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
+        if (t < n && rr < nv) st_f(out, tok(t) * Dv + v0 + rr, a.scale * acc[r]);
       }
     }
-    __syncthreads();
-    // S <- e^{g_n} S + D^T (e^{g_n - g} (.) R): thread (row r, columns c..c+3); rows past nv
-    // and columns past Dk stay zero (their D rows and key columns are zero).  Per-channel
-    // decays: S Diag(2^{G_C}) + D^T R with R already scaled.
+    __syncthreads();   // every read of the state mirror is done
+    // S <- e^{g_n} S + D^T (e^{g_n - g} (.) R); per-channel decays: S Diag(2^{G_C}) +
+    // D^T (2^(G_C - G) (.) R).  Rows of D past n are zero.
     {
       const float gl = eg[n - 1];
-      constexpr int NC4 = DK / 4;
 #pragma unroll
-      for (int u0 = 0; u0 < kBV * NC4; u0 += kThreads) {
-        const int u = u0 + tid;
-        if (kBV * NC4 % kThreads != 0 && u >= kBV * NC4) break;
-        const int r = u / NC4, c = (u % NC4) * 4;
-        const float4 s = ld4(&Ss[r][c]);
-        float4 acc = make_float4(gl * s.x, gl * s.y, gl * s.z, gl * s.w);
+      for (int m = 0; m < NTW; ++m) {
+        const int u = wave + 8 * m;
+        if (u >= NTS) continue;
+        const int rbs = u / NCB, cbs = u % NCB, c = 16 * cbs + col;
+        float4v acc = Sacc[m], acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
         if constexpr (CHD) {
-          const float4 gc = ld4(&Gs[n - 1][c]);
-          acc = make_float4(exp2f(gc.x) * s.x, exp2f(gc.y) * s.y, exp2f(gc.z) * s.z, exp2f(gc.w) * s.w);
+          acc *= exp2f(Gs[n - 1][c]);
+        } else {
+          acc *= gl;
         }
-        for (int j = 0; j < n; ++j) {
-          const float w = Dl[j][r] * wd[j];
-          const float4 rr = ld4(&Rs[j][c]);
-          acc.x = fmaf(w, rr.x, acc.x);
-          acc.y = fmaf(w, rr.y, acc.y);
-          acc.z = fmaf(w, rr.z, acc.z);
-          acc.w = fmaf(w, rr.w, acc.w);
+        for (int t0 = 0; t0 < n; t0 += 8) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int t = t0 + 4 * p + kq;
+            float am = Dl[t][16 * rbs + col], br = Rs[t][c];
+            if constexpr (CHD)
+              br *= exp2f(Gs[n - 1][c] - Gs[t][c]);
+            else
+              am *= wd[t];
+            if (p == 0)
+              acc = mfma4(am, br, acc);
+            else
+              acc2 = mfma4(am, br, acc2);
+          }
         }
-        *reinterpret_cast<float4 *>(&Ss[r][c]) = acc;
+        acc += acc2;
+        Sacc[m] = acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ss[16 * rbs + 4 * kq + r][c] = acc[r];
       }
     }
   }
-  __syncthreads();
   if (a.state_out != nullptr) {
-    for (int idx = tid; idx < kBV * DK; idx += kThreads) {
-      const int r = idx / DK, c = idx % DK;
-      if (r < nv && c < Dk) a.state_out[(sh * Dv + v0 + r) * Dk + c] = Ss[r][c];
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const int u = wave + 8 * m;
+      const int row = 16 * (u / NCB) + 4 * kq, c = 16 * (u % NCB) + col;
+      if (u < NTS && c < Dk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (row + r < nv) a.state_out[(sh * Dv + v0 + row + r) * Dk + c] = Sacc[m][r];
+      }
     }
   }
   if (a.wkey == GDR_WKEY_DIAG_PRECOND && a.pc_h_out != nullptr && vt == 0 && tid < Dk)
     a.pc_h_out[sh * Dk + tid] = hreg;
 }
 
-template <typename IO, bool CHD>
+template <typename IO, bool CHD, int BV>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
-  const dim3 grid((a.Dv + kBV - 1) / kBV, a.H, a.B);
+  const dim3 grid((a.Dv + BV - 1) / BV, a.H, a.B);
   if (a.Dk <= 32)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32, CHD>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32, CHD, BV>), grid, dim3(kThreads), 0, s, a);
   else if (a.Dk <= 64)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64, CHD>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64, CHD, BV>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128, CHD>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128, CHD, BV>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
+// With per-channel decays the 64 x Dk tile of cumulative decays takes the LDS of 16 state rows,
+// so those workgroups own 16 value rows; the others own 32.
 template <typename IO>
 hipError_t launch_io(const ChunkArgs &a, hipStream_t s) {
-  return a.decay == GDR_DECAY_CHANNEL ? launch_dk<IO, true>(a, s) : launch_dk<IO, false>(a, s);
+  return a.decay == GDR_DECAY_CHANNEL ? launch_dk<IO, true, 16>(a, s) : launch_dk<IO, false, 32>(a, s);
 }
 
 }  // namespace
