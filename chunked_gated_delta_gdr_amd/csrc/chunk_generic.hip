@@ -60,8 +60,9 @@ template <typename IO, int DK, bool CHD, int BV>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   // CHD: one decay per key channel (log_alpha [B, T, H, Dk]).  The pairwise decay of channel
   // c between tokens j <= i is 2^(G_ic - G_jc) with G the in-chunk cumulative log2 decay, so it
-  // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise, both on
-  // the vector ALUs), the state is read through 2^G (.) e and 2^G (.) q, and the update uses
+  // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise; factored
+  // into the operands below the diagonal tiles, per pair on them), the state is read through
+  // 2^G (.) e and 2^G (.) q, and the update uses
   // 2^(G_C - G) (.) r and S Diag(2^G_C).  Every exponent that is kept is <= 0.
   constexpr int LD = DK + 4;            // fp32 row stride of the [token][channel] tiles
   constexpr int kLoadIt = kCMax * DK / kThreads;
@@ -235,42 +236,52 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     // diagonal; rows past n hold zero keys, so they come out zero
     auto gram = [&](bool incl_diag) {
       if constexpr (CHD) {
-        // vector ALUs (the decay depends on the channel): thread = rows 4 ti .. 4 ti + 3,
-        // columns 2 cj, 2 cj + 1
-        const int ti = tid >> 5, cj = tid & 31;
-        float acc[4][2] = {};
-        if (2 * cj <= 4 * ti + 3) {
-#pragma unroll 2
-          for (int c = 0; c < DK; c += 4) {
-            float4 x[4], gi[4], r[2], gj[2];
+        // The six tiles below the diagonal (row block ib > column block jb) on the matrix
+        // cores: the pairwise decay splits at the last row of block jb, ref = 16 jb + 15, as
+        // 2^(G_ic - G_ref,c) 2^(G_ref,c - G_jc), both exponents <= 0 (G does not increase
+        // along the chunk), so each factor goes into its operand.
+        for (int u = wave; u < 6; u += 8) {
+          const int ib = u < 1 ? 1 : u < 3 ? 2 : 3, jb = u - (ib - 1) * ib / 2;
+          const int ref = 16 * jb + 15, i = 16 * ib + col, j = 16 * jb + col;
+          float4v ap[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+          for (int ks = 0; ks < DK; ks += 8)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              x[u] = ld4(&Xs[4 * ti + u][c]);
-              gi[u] = ld4(&Gs[4 * ti + u][c]);
+            for (int p = 0; p < 2; ++p) {
+              const int kk = ks + 4 * p + kq;
+              const float gr = Gs[ref][kk];
+              ap[p] = mfma4(Xs[i][kk] * exp2f(Gs[i][kk] - gr), Rs[j][kk] * exp2f(gr - Gs[j][kk]), ap[p]);
             }
+          const float4v acc = ap[0] + ap[1];
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-              r[w] = ld4(&Rs[2 * cj + w][c]);
-              gj[w] = ld4(&Gs[2 * cj + w][c]);
-            }
-            // (entries above the diagonal may overflow here; they are discarded below)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
+          for (int r = 0; r < 4; ++r) LP[16 * ib + 4 * kq + r][j] = acc[r];
+        }
+        // The four diagonal tiles on the vector ALUs, one exponential per pair and channel:
+        // thread = tile d, row il, columns jl, jl + 1 (pairs wholly above the diagonal skipped)
+        {
+          const int d = tid >> 7, e = tid & 127, il = e >> 3, jl = 2 * (e & 7);
+          const int i = 16 * d + il, j0 = 16 * d + jl;
+          float acc[2] = {0.f, 0.f};
+          if (jl <= il) {
+#pragma unroll 4
+            for (int c = 0; c < DK; c += 4) {
+              const float4 x = ld4(&Xs[i][c]), gi = ld4(&Gs[i][c]);
+              // (entries above the diagonal may overflow here; they are discarded below)
 #pragma unroll
               for (int w = 0; w < 2; ++w) {
-                const float4 d = make_float4(x[u].x * exp2f(gi[u].x - gj[w].x), x[u].y * exp2f(gi[u].y - gj[w].y),
-                                             x[u].z * exp2f(gi[u].z - gj[w].z), x[u].w * exp2f(gi[u].w - gj[w].w));
-                fma4(acc[u][w], d, r[w]);
+                const float4 r = ld4(&Rs[j0 + w][c]), gj = ld4(&Gs[j0 + w][c]);
+                const float4 dd = make_float4(x.x * exp2f(gi.x - gj.x), x.y * exp2f(gi.y - gj.y),
+                                              x.z * exp2f(gi.z - gj.z), x.w * exp2f(gi.w - gj.w));
+                fma4(acc[w], dd, r);
               }
+            }
           }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
-            const int i = 4 * ti + u, j = 2 * cj + w;
-            LP[i][j] = (j < i || (incl_diag && j == i)) ? acc[u][w] : 0.f;
+            const int j = j0 + w;
+            LP[i][j] = (j < i || (incl_diag && j == i)) ? acc[w] : 0.f;
           }
+        }
       } else {
         for (int u = wave; u < 10; u += 8) {
           int ib, jb;
