@@ -257,29 +257,63 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
           for (int r = 0; r < 4; ++r) LP[16 * ib + 4 * kq + r][j] = acc[r];
         }
         // The four diagonal tiles on the vector ALUs, one exponential per pair and channel:
-        // thread = tile d, row il, columns jl, jl + 1 (pairs wholly above the diagonal skipped)
+        // thread = (tile d, 4 x 4 block (bi, bj) on or below the block diagonal, channel group
+        // g of 16); the 8 channel groups of a block are adjacent lanes, summed by shuffles
+        // (threads 0..319; the rest only join the shuffles of their own idle waves)
         {
-          const int d = tid >> 7, e = tid & 127, il = e >> 3, jl = 2 * (e & 7);
-          const int i = 16 * d + il, j0 = 16 * d + jl;
-          float acc[2] = {0.f, 0.f};
-          if (jl <= il) {
-#pragma unroll 4
-            for (int c = 0; c < DK; c += 4) {
-              const float4 x = ld4(&Xs[i][c]), gi = ld4(&Gs[i][c]);
+          const int g = tid & 7, blk = tid >> 3;
+          const bool act = blk < 40;
+          int bi = 0, bj = 0;
+          lower_tile(blk % 10, bi, bj);
+          const int d = act ? blk / 10 : 0;
+          const int i0 = 16 * d + 4 * bi, j0 = 16 * d + 4 * bj, c0g = 16 * g;
+          float acc[4][4] = {};
+          if (act) {
+#pragma unroll 1
+            for (int cc = 0; cc < 16; cc += 4) {
+              const int c = c0g + cc;
+              if (c >= DK) break;
+              float4 x[4], gi[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                x[u] = ld4(&Xs[i0 + u][c]);
+                gi[u] = ld4(&Gs[i0 + u][c]);
+              }
               // (entries above the diagonal may overflow here; they are discarded below)
 #pragma unroll
-              for (int w = 0; w < 2; ++w) {
+              for (int w = 0; w < 4; ++w) {
                 const float4 r = ld4(&Rs[j0 + w][c]), gj = ld4(&Gs[j0 + w][c]);
-                const float4 dd = make_float4(x.x * exp2f(gi.x - gj.x), x.y * exp2f(gi.y - gj.y),
-                                              x.z * exp2f(gi.z - gj.z), x.w * exp2f(gi.w - gj.w));
-                fma4(acc[w], dd, r);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const float4 dd = make_float4(x[u].x * exp2f(gi[u].x - gj.x), x[u].y * exp2f(gi[u].y - gj.y),
+                                                x[u].z * exp2f(gi[u].z - gj.z), x[u].w * exp2f(gi[u].w - gj.w));
+                  fma4(acc[u][w], dd, r);
+                }
               }
             }
           }
 #pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const int j = j0 + w;
-            LP[i][j] = (j < i || (incl_diag && j == i)) ? acc[w] : 0.f;
+          for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) acc[u][w] += __shfl_xor(acc[u][w], m);
+          if (act && g == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const int i = i0 + u, j = j0 + w;
+                LP[i][j] = (j < i || (incl_diag && j == i)) ? acc[u][w] : 0.f;
+              }
+          }
+          // the six 4 x 4 blocks above the block diagonal of each diagonal tile hold zeros (the
+          // products with P read whole diagonal tiles): one entry per thread
+          if (tid < 4 * 6 * 16) {
+            const int dt = tid / 96, ub = (tid % 96) / 16, en = tid % 16;
+            const int ubi = ub < 3 ? 0 : ub < 5 ? 1 : 2;
+            const int ubj = ub < 3 ? ub + 1 : ub < 5 ? ub - 1 : 3;
+            LP[16 * dt + 4 * ubi + (en >> 2)][16 * dt + 4 * ubj + (en & 3)] = 0.f;
           }
         }
       } else {
@@ -307,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     auto state_read = [&](const float(*Y)[LD], float4v &acc) {
       acc = float4v{0.f, 0.f, 0.f, 0.f};
       const int t = 16 * tb + col;
-#pragma unroll 8
+#pragma unroll(CHD ? 4 : 8)
       for (int ks = 0; ks < DK; ks += 4) {
         float y = Y[t][ks + kq];
         if constexpr (CHD) y *= exp2f(Gs[t][ks + kq]);
