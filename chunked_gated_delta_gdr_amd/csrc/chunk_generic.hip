@@ -50,6 +50,24 @@ __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &
   acc = fmaf(x.w, y.w, acc);
 }
 
+// sum over k < K of A[i][k] B[k][j] for the lane's row i (row pointer ra) and column j (row
+// pointer rb of B^T), both with k contiguous in LDS: the K order is permuted so that sub-step
+// u of block s takes k = s + 4 kq + u, and each lane reads its 4 k with one 16-byte read per
+// operand; two independent accumulator chains
+template <int K>
+__device__ __forceinline__ float4v dot_kc(const float *ra, const float *rb, int kq) {
+  float4v a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < K; s += 16) {
+    const float4 x = ld4(ra + s + 4 * kq), y = ld4(rb + s + 4 * kq);
+    a0 = mfma4(x.x, y.x, a0);
+    a1 = mfma4(x.y, y.y, a1);
+    a0 = mfma4(x.z, y.z, a0);
+    a1 = mfma4(x.w, y.w, a1);
+  }
+  return a0 + a1;
+}
+
 // tile u (0..9) of the ten 16 x 16 tiles on and below the diagonal of a 64 x 64 matrix
 __device__ __forceinline__ void lower_tile(int u, int &ib, int &jb) {
   ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
@@ -243,15 +261,18 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         for (int u = wave; u < 6; u += 8) {
           const int ib = u < 1 ? 1 : u < 3 ? 2 : 3, jb = u - (ib - 1) * ib / 2;
           const int ref = 16 * jb + 15, i = 16 * ib + col, j = 16 * jb + col;
+          // (k order permuted as in dot_kc: 16-byte reads of 4 consecutive channels per lane)
           float4v ap[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
-          for (int ks = 0; ks < DK; ks += 8)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              const int kk = ks + 4 * p + kq;
-              const float gr = Gs[ref][kk];
-              ap[p] = mfma4(Xs[i][kk] * exp2f(Gs[i][kk] - gr), Rs[j][kk] * exp2f(gr - Gs[j][kk]), ap[p]);
-            }
+#pragma unroll 2
+          for (int ks = 0; ks < DK; ks += 16) {
+            const int kk = ks + 4 * kq;
+            const float4 x = ld4(&Xs[i][kk]), gx = ld4(&Gs[i][kk]), gr = ld4(&Gs[ref][kk]);
+            const float4 r = ld4(&Rs[j][kk]), gy = ld4(&Gs[j][kk]);
+            ap[0] = mfma4(x.x * exp2f(gx.x - gr.x), r.x * exp2f(gr.x - gy.x), ap[0]);
+            ap[1] = mfma4(x.y * exp2f(gx.y - gr.y), r.y * exp2f(gr.y - gy.y), ap[1]);
+            ap[0] = mfma4(x.z * exp2f(gx.z - gr.z), r.z * exp2f(gr.z - gy.z), ap[0]);
+            ap[1] = mfma4(x.w * exp2f(gx.w - gr.w), r.w * exp2f(gr.w - gy.w), ap[1]);
+          }
           const float4v acc = ap[0] + ap[1];
 #pragma unroll
           for (int r = 0; r < 4; ++r) LP[16 * ib + 4 * kq + r][j] = acc[r];
@@ -320,15 +341,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         for (int u = wave; u < 10; u += 8) {
           int ib, jb;
           lower_tile(u, ib, jb);
-          float4v ap[2];   // two independent accumulator chains, summed below
-#pragma unroll
-          for (int p = 0; p < 2; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-          for (int ks = 0; ks < DK; ks += 8)
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-              ap[p] = mfma4(Xs[16 * ib + col][ks + 4 * p + kq], Rs[16 * jb + col][ks + 4 * p + kq], ap[p]);
-          const float4v acc = ap[0] + ap[1];
+          const float4v acc = dot_kc<DK>(&Xs[16 * ib + col][0], &Rs[16 * jb + col][0], kq);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
@@ -339,15 +352,23 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     };
     // the read of the state through row t of Y (E or Q): e^g_t Y_t, or 2^G_t (.) Y_t
     auto state_read = [&](const float(*Y)[LD], float4v &acc) {
-      acc = float4v{0.f, 0.f, 0.f, 0.f};
       const int t = 16 * tb + col;
-#pragma unroll(CHD ? 4 : 8)
-      for (int ks = 0; ks < DK; ks += 4) {
-        float y = Y[t][ks + kq];
-        if constexpr (CHD) y *= exp2f(Gs[t][ks + kq]);
-        acc = mfma4(y, Ss[16 * rb + col][ks + kq], acc);
-      }
-      if constexpr (!CHD) {
+      if constexpr (CHD) {
+        // (k order permuted as in dot_kc)
+        float4v a1 = {0.f, 0.f, 0.f, 0.f};
+        acc = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int ks = 0; ks < DK; ks += 16) {
+          const int kk = ks + 4 * kq;
+          const float4 y = ld4(&Y[t][kk]), g = ld4(&Gs[t][kk]), z = ld4(&Ss[16 * rb + col][kk]);
+          acc = mfma4(y.x * exp2f(g.x), z.x, acc);
+          a1 = mfma4(y.y * exp2f(g.y), z.y, a1);
+          acc = mfma4(y.z * exp2f(g.z), z.z, acc);
+          a1 = mfma4(y.w * exp2f(g.w), z.w, a1);
+        }
+        acc += a1;
+      } else {
+        acc = dot_kc<DK>(&Y[t][0], &Ss[16 * rb + col][0], kq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= eg[16 * tb + 4 * kq + r];
       }
