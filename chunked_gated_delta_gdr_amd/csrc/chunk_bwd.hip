@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   };
   gram(Es, false);
   __syncthreads();
-  tri::inverse_blocks(LP, Tm, Zs, -1, tid, tid < 256);
+  tri::inverse_blocks(LP, Tm, Zs, -1, tid);
   gram(Xs, true);
   __syncthreads();
   {   // T and P of the chunk (C x C) for the sweep (P is zero above the diagonal)

@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // T = (I - A)^-1 by 16 x 16 blocks (exact, or its band i - j <= N)
-    tri::inverse_blocks(LP, Tm, Zs, a.N, tid, tid < 256);
+    tri::inverse_blocks(LP, Tm, Zs, a.N, tid);
     // Parallel residual correction of the band start T0 (MatMul-only inversion summary,
     // Metodologia 3): E = I - (I - A) T0 = I - T0 + A T0, Z = I + E (I + E (... (I + E))) with S
     // factors (= sum_{s<=S} E^s), T = T0 Z.  All factors are lower triangular, so each product

@@ -1,5 +1,5 @@
 // Blocked inverse of a chunk's unit lower-triangular matrix, shared by the forward and
-// backward kernels.
+// backward kernels (fp32 on the matrix cores).
 #pragma once
 
 #include "common.h"
@@ -7,124 +7,109 @@
 namespace gdr {
 namespace tri {
 
-__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// one 16 x 16 x 4 fp32 matrix-core step: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16]
+// and holds D[4 (l / 16) + r][l % 16], r < 4
+__device__ __forceinline__ f4v mma(float a, float b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+
+// LDS writes of this wave become visible to its own later reads
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // T = (I - A)^-1 for the strictly lower-triangular A = -L of one chunk of up to 64 tokens
-// (chunk-wise form of the MatMul-only inversion summary, "Declaracao do Problema"), by one
-// workgroup of 256 threads, in 16 x 16 blocks.  With D_b = (I - A_bb)^-1 (the four diagonal
-// blocks, solved at once, one wave each, by right-looking forward substitution: at step l
-// every row i > l adds A_il T_lj, so each entry sums its terms in increasing l),
-//   T_10 = D_1 A_10 D_0,  T_32 = D_3 A_32 D_2,  T_ba = T_b A_ba T_a
-// where a, b are the 32 x 32 halves (T_a = [D_0 0; T_10 D_1], T_b likewise).  Every entry is
-// band-masked as it is written (N >= 0 keeps i - j <= N; N < 0 keeps all): the band of each
-// product depends only on the bands of its factors (Lemma 3.1, Metodologia 1), so the band
-// entries are those of the exact path, bit for bit, and N >= n - 1 runs exactly the exact
+// (chunk-wise form of the MatMul-only inversion summary, "Declaracao do Problema"), by a
+// workgroup of at least 4 waves, in 16 x 16 blocks on the fp32 matrix cores.  The four
+// diagonal blocks D_b = (I - A_bb)^-1 = (I + A_bb)(I + A_bb^2)(I + A_bb^4)(I + A_bb^8) (A_bb is
+// strictly lower, so A_bb^16 = 0), one wave each, by three squarings and three products;
+// then T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and the lower-left quadrant
+// T_ba = T_b A_ba T_a (a, b the 32 x 32 halves) as block products.  Every block is band-masked
+// when it is written (N >= 0 keeps i - j <= N; N < 0 keeps all): an in-band entry of a product
+// of lower-triangular factors reads only in-band entries of them (Lemma 3.1, Metodologia 1),
+// so the band entries are those of the exact path, bit for bit, and N >= n - 1 runs the exact
 // path's instructions.  Rows of L past the chunk must be zero (their T rows come out unit
 // rows), and the 16 x 16 blocks of Tm above the diagonal must hold zero on entry (they are
-// never written).  Zs is 32 x 36 scratch.  Threads 0..255 do the work; in a larger workgroup
-// the others pass active = false and only take part in the barriers.  Starts reading L
-// without a barrier (the caller publishes it) and ends with a workgroup barrier.
+// never written).  Zs is 32 x 36 scratch.  Starts reading L without a barrier (the caller
+// publishes it) and ends with a workgroup barrier.
 template <int LDL, int LDT>
 __device__ __forceinline__ void inverse_blocks(const float (*LP)[LDL], float (*Tm)[LDT], float (*Zs)[36], int N,
-                                               int tid, bool active = true) {
+                                               int tid) {
   auto keep = [&](int i, int j) { return N < 0 || i - j <= N; };
-  const int lane = tid & 63, w = tid >> 6;
-  if (active) {   // diagonal block w: lane = (block row ii, block columns jq .. jq + 3)
-    const int ii = lane >> 2, jq = (lane & 3) * 4;
-    const int o = 16 * w, gi = o + ii;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ii == 0) *reinterpret_cast<float4 *>(&Tm[o][o + jq]) = make_float4(jq == 0 ? 1.f : 0.f, 0.f, 0.f, 0.f);
-    // rows of the block are published and read by lanes of this wave only
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int l = 0; l < 15; ++l) {
-      const float A_il = l < ii ? -LP[gi][o + l] : 0.f;
-      const float4 t = ld4(&Tm[o + l][o + jq]);
-      acc[0] = fmaf(A_il, t.x, acc[0]);
-      acc[1] = fmaf(A_il, t.y, acc[1]);
-      acc[2] = fmaf(A_il, t.z, acc[2]);
-      acc[3] = fmaf(A_il, t.w, acc[3]);
-      if (ii == l + 1) {
-        float r[4];
+  const int lane = tid & 63, w = tid >> 6, col = lane & 15, kq = lane >> 4;
+  if (w < 4) {   // diagonal block w: M = (I + P)(I + P^2)..., P = A_bb held in the wave's scratch
+    const int o = 16 * w;
+    float *Pw = &Zs[0][0] + 288 * w;   // 16 x 16, row stride 16
+    for (int e = lane; e < 256; e += 64) {
+      const int i = e >> 4, j = e & 15;
+      const float a = j < i ? -LP[o + i][o + j] : 0.f;
+      Pw[e] = a;
+      Tm[o + i][o + j] = (i == j ? 1.f : 0.f) + a;
+    }
+    wave_sync();
+#pragma unroll 1
+    for (int step = 0; step < 3; ++step) {
+      f4v acc = {0.f, 0.f, 0.f, 0.f};   // P <- P P
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int jj = jq + u;
-          r[u] = jj == ii ? 1.f : (jj < ii && keep(ii, jj)) ? acc[u] : 0.f;
-        }
-        *reinterpret_cast<float4 *>(&Tm[gi][o + jq]) = make_float4(r[0], r[1], r[2], r[3]);
+      for (int s = 0; s < 4; ++s) acc = mma(Pw[16 * col + 4 * s + kq], Pw[16 * (4 * s + kq) + col], acc);
+      wave_sync();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pw[16 * (4 * kq + r) + col] = acc[r];
+      wave_sync();
+      acc = f4v{0.f, 0.f, 0.f, 0.f};    // M <- M + M P
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mma(Tm[o + col][o + 4 * s + kq], Pw[16 * (4 * s + kq) + col], acc);
+      wave_sync();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * kq + r;
+        const float m = Tm[o + i][o + col] + acc[r];
+        Tm[o + i][o + col] = (step < 2 || keep(i, col)) ? m : 0.f;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
     }
   }
   __syncthreads();
-  // two 16 x 16 products at once: thread = (product p, row r, columns c, c + 1)
-  const int p = tid >> 7, r = (tid >> 3) & 15, c = (tid & 7) * 2;
-  if (active) {   // Z_p = A_(2p+1, 2p) D_2p
-    const int ro = 32 * p + 16, co = 32 * p;
-    float z0 = 0.f, z1 = 0.f;
+  if (w < 2) {   // Z_p = A_(2p+1, 2p) D_2p, p = w
+    const int ro = 32 * w + 16, co = 32 * w;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float av = -LP[ro + r][co + m];
-      const float2 d = ld2(&Tm[co + m][co + c]);
-      z0 = fmaf(av, d.x, z0);
-      z1 = fmaf(av, d.y, z1);
-    }
-    *reinterpret_cast<float2 *>(&Zs[16 * p + r][c]) = make_float2(z0, z1);
-  }
-  __syncthreads();
-  if (active) {   // T_(2p+1, 2p) = D_(2p+1) Z_p
-    const int ro = 32 * p + 16, co = 32 * p;
-    float t0v = 0.f, t1v = 0.f;
+    for (int s = 0; s < 4; ++s) acc = mma(-LP[ro + col][co + 4 * s + kq], Tm[co + 4 * s + kq][co + col], acc);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float dv = Tm[ro + r][ro + m];
-      const float2 z = ld2(&Zs[16 * p + m][c]);
-      t0v = fmaf(dv, z.x, t0v);
-      t1v = fmaf(dv, z.y, t1v);
-    }
-    const int i = ro + r, j = co + c;
-    Tm[i][j] = keep(i, j) ? t0v : 0.f;
-    Tm[i][j + 1] = keep(i, j + 1) ? t1v : 0.f;
+    for (int r = 0; r < 4; ++r) Zs[16 * w + 4 * kq + r][col] = acc[r];
   }
   __syncthreads();
-  // 32 x 32 products: thread = (row r2, columns c4 .. c4 + 3)
-  const int r2 = tid >> 3, c4 = (tid & 7) * 4;
-  if (active) {   // Z = A_ba T_a
-    float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int m = 0; m < 32; ++m) {
-      const float av = -LP[32 + r2][m];
-      const float4 t = ld4(&Tm[m][c4]);
-      z[0] = fmaf(av, t.x, z[0]);
-      z[1] = fmaf(av, t.y, z[1]);
-      z[2] = fmaf(av, t.z, z[2]);
-      z[3] = fmaf(av, t.w, z[3]);
+  if (w < 2) {   // T_(2p+1, 2p) = D_(2p+1) Z_p
+    const int ro = 32 * w + 16, co = 32 * w;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mma(Tm[ro + col][ro + 4 * s + kq], Zs[16 * w + 4 * s + kq][col], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ro + 4 * kq + r, j = co + col;
+      Tm[i][j] = keep(i, j) ? acc[r] : 0.f;
     }
-    *reinterpret_cast<float4 *>(&Zs[r2][c4]) = make_float4(z[0], z[1], z[2], z[3]);
   }
   __syncthreads();
-  if (active) {   // T_ba = T_b Z
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int m = 0; m < 32; ++m) {
-      const float tb = Tm[32 + r2][32 + m];
-      const float4 z = ld4(&Zs[m][c4]);
-      t[0] = fmaf(tb, z.x, t[0]);
-      t[1] = fmaf(tb, z.y, t[1]);
-      t[2] = fmaf(tb, z.z, t[2]);
-      t[3] = fmaf(tb, z.w, t[3]);
+  const int zi = (w >> 1) & 1, zj = w & 1;   // 16 x 16 tile of the 32 x 32 products (waves 0..3)
+  if (w < 4) {   // Z = A_ba T_a (T_a lower: k from 16 zj)
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 4 * zj; s < 8; ++s) acc = mma(-LP[32 + 16 * zi + col][4 * s + kq], Tm[4 * s + kq][16 * zj + col], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Zs[16 * zi + 4 * kq + r][16 * zj + col] = acc[r];
+  }
+  __syncthreads();
+  if (w < 4) {   // T_ba = T_b Z (T_b lower: k below 16 zi + 16)
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * (zi + 1); ++s)
+      acc = mma(Tm[32 + 16 * zi + col][32 + 4 * s + kq], Zs[4 * s + kq][16 * zj + col], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 32 + 16 * zi + 4 * kq + r, j = 16 * zj + col;
+      Tm[i][j] = keep(i, j) ? acc[r] : 0.f;
     }
-    const int i = 32 + r2;
-    float4 o4;
-    o4.x = keep(i, c4) ? t[0] : 0.f;
-    o4.y = keep(i, c4 + 1) ? t[1] : 0.f;
-    o4.z = keep(i, c4 + 2) ? t[2] : 0.f;
-    o4.w = keep(i, c4 + 3) ? t[3] : 0.f;
-    *reinterpret_cast<float4 *>(&Tm[i][c4]) = o4;
   }
   __syncthreads();
 }
