@@ -68,6 +68,24 @@ __device__ __forceinline__ float chunk_log_alpha(const ChunkArgs &f, long long r
   return (f.decay == GDR_DECAY_SCALAR && lane < n) ? f.log_alpha[row0 + static_cast<long long>(lane) * f.H] : 0.f;
 }
 
+// sum over k < K of A[i][k] B[k][j] for the lane's row i (row pointer ra) and column j (row
+// pointer rb of B^T), both with k contiguous in LDS: the K order is permuted so that sub-step
+// u of block s takes k = s + 4 kq + u, and each lane reads its 4 k with one 16-byte read per
+// operand; two independent accumulator chains
+template <int K>
+__device__ __forceinline__ float4v dot_kc(const float *ra, const float *rb, int kq) {
+  float4v a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < K; s += 16) {
+    const float4 x = ld4(ra + s + 4 * kq), y = ld4(rb + s + 4 * kq);
+    a0 = mfma4(x.x, y.x, a0);
+    a1 = mfma4(x.y, y.y, a1);
+    a0 = mfma4(x.z, y.z, a0);
+    a1 = mfma4(x.w, y.w, a1);
+  }
+  return a0 + a1;
+}
+
 // g (inclusive cumulative sum of log alpha over tokens 0..n-1, flat past n), e^g and
 // e^{g_{n-1} - g} of one chunk from lane's log alpha `la`; called by the first wave.
 __device__ __forceinline__ void chunk_gates_from(float la, int n, int lane, float *gs, float *eg, float *wd) {
@@ -164,15 +182,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     for (int u = wave; u < 10; u += 8) {
       const int ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
       const int jb = u - ib * (ib + 1) / 2;
-      float4v ap[4];   // four independent accumulator chains, summed below
-#pragma unroll
-      for (int p = 0; p < 4; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DK; ks += 16)
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          ap[p] = mfma4(X[16 * ib + col][ks + 4 * p + kq], Rs[16 * jb + col][ks + 4 * p + kq], ap[p]);
-      const float4v acc = (ap[0] + ap[1]) + (ap[2] + ap[3]);
+      const float4v acc = dot_kc<DK>(&X[16 * ib + col][0], &Rs[16 * jb + col][0], kq);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
@@ -372,15 +382,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     __syncthreads();
     if (ci + 1 < a.NC) cload(ci + 1);   // in flight during this chunk's products
     {   // D = U - W S^T, tile (tb, rb)
-      float4v ap[4];   // four independent accumulator chains, summed below
-#pragma unroll
-      for (int p = 0; p < 4; ++p) ap[p] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DK; ks += 16)
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          ap[p] = mfma4(Ws[16 * tb + col][ks + 4 * p + kq], Ss[16 * rb + col][ks + 4 * p + kq], ap[p]);
-      const float4v acc = (ap[0] + ap[1]) + (ap[2] + ap[3]);
+      const float4v acc = dot_kc<DK>(&Ws[16 * tb + col][0], &Ss[16 * rb + col][0], kq);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
@@ -573,16 +575,9 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO, tile (tb, rb); P is zero above the
     // diagonal and T, P, dO rows past n (inside the chunk) are zero
     {
-      // two independent accumulator chains for R dS^T (summed below), one for P^T dO
-      float4v a1[2], a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < 2; ++p) a1[p] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int ks = 0; ks < DK; ks += 8)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          a1[p] = mfma4(Ks[16 * tb + col][ks + 4 * p + kq], dS[16 * rb + col][ks + 4 * p + kq], a1[p]);
-      a1[0] += a1[1];
+      // R dS^T (16-byte operand reads), then P^T dO
+      float4v a1[1], a2 = {0.f, 0.f, 0.f, 0.f};
+      a1[0] = dot_kc<DK>(&Ks[16 * tb + col][0], &dS[16 * rb + col][0], kq);
       // (i0 < n keeps every row read below C, where T and P were loaded)
       for (int i0 = 16 * tb; i0 < n; i0 += 4)
         a2 = mfma4(Pm[i0 + kq][16 * tb + col], dOs[i0 + kq][16 * rb + col], a2);
