@@ -395,6 +395,17 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
+    // the queries' loads are issued here, so they are in flight during the inverse; they
+    // replace the erase keys in LDS after it
+    float xq[kLoadIt];
+    {
+      const IO *qc = q + row0 * Dk;
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        xq[it] = ld_f(qc, min(t, n - 1) * rstride + min(c, Dk - 1));
+      }
+    }
     // T = (I - A)^-1 by 16 x 16 blocks (exact, or its band i - j <= N)
     tri::inverse_blocks(LP, Tm, Zs, a.N, tid);
     // Parallel residual correction of the band start T0 (MatMul-only inversion summary,
@@ -448,13 +459,6 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       }
     }
     {   // queries replace the erase keys (their last reads, L and X, were before the barriers above)
-      float xq[kLoadIt];
-      const IO *qc = q + row0 * Dk;
-#pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        xq[it] = ld_f(qc, min(t, n - 1) * rstride + min(c, Dk - 1));
-      }
 #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
         const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
