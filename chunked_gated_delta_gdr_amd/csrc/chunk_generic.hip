@@ -258,7 +258,8 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         // cores: the pairwise decay splits at the last row of block jb, ref = 16 jb + 15, as
         // 2^(G_ic - G_ref,c) 2^(G_ref,c - G_jc), both exponents <= 0 (G does not increase
         // along the chunk), so each factor goes into its operand.
-        for (int u = wave; u < 6; u += 8) {
+        // (on waves 5..7, two tiles each: waves 0..4 take the diagonal tiles below)
+        for (int u = wave - 5; u >= 0 && u < 6; u += 3) {
           const int ib = u < 1 ? 1 : u < 3 ? 2 : 3, jb = u - (ib - 1) * ib / 2;
           const int ref = 16 * jb + 15, i = 16 * ib + col, j = 16 * jb + col;
           // (k order permuted as in dot_kc: 16-byte reads of 4 consecutive channels per lane)
