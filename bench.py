@@ -7,7 +7,7 @@ Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s 1.0] [--workload gdn|gdn2|pdn|long|plain|kda|decode]
                     [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
-    python bench.py --bwd [--workload gdn|gdn2|plain]   # gdr_chunk_bwd instead
+    python bench.py --bwd [--workload gdn|gdn2|plain|kda]   # gdr_chunk_bwd instead
 
 Counter helpers (used to produce the committed traffic summaries under profiles/):
     python bench.py --copy-probe-mb 256          # calibration copy of known size
@@ -318,7 +318,7 @@ def bwd_alg_bytes(s) -> int:
     per_tok = (2 * s.Dk + 2 * s.Dv) * esz                       # q, k, v, dO
     per_tok += (2 * s.Dk + s.Dv) * 4                            # dq, dk, dv
     per_tok += 8 if s.gain == "scalar" else (s.Dk + s.Dv) * (esz + 4)   # gains and their grads
-    per_tok += 8 if s.decay == "scalar" else 0                  # log alpha and its grad
+    per_tok += {"scalar": 8, "channel": 8 * s.Dk}.get(s.decay, 0)   # log alpha and its grad
     per_head = 3 * s.Dv * s.Dk * 4                              # S_0, dS_T, dS_0
     return s.B * s.T * s.H * per_tok + s.B * s.H * per_head
 
@@ -342,7 +342,7 @@ def bench_backward(args):
     import gdr_synth as gs
 
     s = gs.spec(args.workload)
-    if s.wkey == "precond" or s.decay == "channel":
+    if s.wkey == "precond":
         print(f"bench.py --bwd: the {args.workload} workload's variant has no backward here", file=sys.stderr)
         sys.exit(2)
     x, cot = gs.make_inputs(s), gs.make_cotangents(s)
@@ -360,7 +360,7 @@ def bench_backward(args):
     desc = G.make_desc(B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk, io_dtype=G.GDR_BF16 if
                        s.dtype == "bf16" else G.GDR_F32,
                        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
-                       decay=G.GDR_DECAY_SCALAR if s.decay == "scalar" else G.GDR_DECAY_NONE)
+                       decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE))
     ws = torch.empty(G.gdr_chunk_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] backward {args.workload}: workspace {ws.numel() / 2**20:.1f} MiB, steps {args.steps} "

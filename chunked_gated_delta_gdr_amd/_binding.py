@@ -326,7 +326,8 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
     _check("v", v, (B, T, H, Dv), io, dev)
     _check("d_out", d_out, (B, T, H, Dv), io, dev)
     _check("beta", beta, (B, T, H), f32, dev)
-    _check("log_alpha", log_alpha, (B, T, H), f32, dev)
+    chd = log_alpha is not None and log_alpha.dim() == 4
+    _check("log_alpha", log_alpha, (B, T, H, Dk) if chd else (B, T, H), f32, dev)
     _check("erase", erase, (B, T, H, Dk), io, dev)
     _check("write", write, (B, T, H, Dv), io, dev)
     _check("write_key", write_key, (B, T, H, Dk), io, dev)
@@ -334,7 +335,8 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
     _check("d_state_out", d_state_out, (B, H, Dv, Dk), f32, dev)
     desc = make_desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, io_dtype=_io_code(io),
                      gain=GDR_GAIN_CHANNEL if erase is not None else GDR_GAIN_SCALAR,
-                     decay=GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE,
+                     decay=(GDR_DECAY_CHANNEL if chd else
+                            GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE),
                      wkey=GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME,
                      scale=scale, impl=GDR_IMPL_GENERIC)
 
@@ -348,7 +350,7 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
     else:
         g["dbeta"] = new((B, T, H))
     if log_alpha is not None:
-        g["dlog_alpha"] = new((B, T, H))
+        g["dlog_alpha"] = new((B, T, H, Dk) if chd else (B, T, H))
     if write_key is not None:
         g["dwrite_key"] = new((B, T, H, Dk))
     if want_dstate_in:

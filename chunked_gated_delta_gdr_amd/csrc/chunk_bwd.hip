@@ -22,8 +22,11 @@
 // state at every chunk start), the reverse sweep (sequential over chunks, per value tile,
 // last to first: carries dS, emits dX and the gradient at each chunk's end) and the
 // per-chunk pass (parallel over chunks; everything else).
+#include <type_traits>
+
 #include "common.h"
 #include "tri_blocks.h"
+#include "chd_gram.h"
 
 namespace gdr {
 namespace {
@@ -109,11 +112,14 @@ __device__ __forceinline__ void chunk_gates(const ChunkArgs &f, long long row0, 
 // ---------------------------------------------------------------------------------------
 // Chunk preparation: one workgroup per (batch, head, chunk), all chunks at once.  Everything
 // of a chunk that does not depend on the state: T = (I + L)^-1 and P (C x C, for the sweep),
-// W = T (e^g (.) E) (C x Dk) and U = T V' (C x Dv, for the state pass).
+// W = T (e^g (.) E) (C x Dk) and U = T V' (C x Dv, for the state pass).  With per-channel
+// decay (CHD) also G, the in-chunk cumulative log2 decay of every token and channel, for the
+// other three kernels; the Gram tiles take the decay inside their channel sums, W the factor
+// 2^G elementwise.
 // ---------------------------------------------------------------------------------------
 constexpr int kPrThreads = 512;
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHD>
 __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   static_assert(DK == 64 || DK == 128, "32 channel groups of 2 or 4");
   constexpr int kThreads = kPrThreads;
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 
   __shared__ __align__(16) float Es[kCMax][LD];   // erase keys e
   __shared__ __align__(16) float Rs[kCMax][LD];   // write keys r
-  __shared__ __align__(16) float Xs[kCMax][LD];   // queries, then blocks of V'
+  __shared__ __align__(16) float Xs[kCMax][LD];   // queries (CHD: G), then blocks of V'
   __shared__ float LP[kCMax][kCMax + 1];          // L, then P
   __shared__ __align__(16) float Tm[kCMax][kCMax + 4];
   __shared__ __align__(16) float Zs[32][36];
@@ -150,9 +156,10 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     const int i = idx / kCMax, j = idx % kCMax;
     if ((j >> 4) > (i >> 4)) Tm[i][j] = 0.f;
   }
-  {   // E, R, Q: all loads first (clamped), then the masked stores
+  const IO *qc = q + row0 * Dk;
+  {   // E, R, Q (CHD: log alpha): all loads first (clamped), then the masked stores
     float xk[kLoadIt], xg[kLoadIt], xr[kLoadIt], xq[kLoadIt];
-    const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
+    const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
     const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
     const float *bc = f.beta + row0;
 #pragma unroll
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
       xk[it] = ld_f(kc, o);
       xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
       xr[it] = ld_f(rsrc, o);
-      xq[it] = ld_f(qc, o);
+      xq[it] = CHD ? f.log_alpha[row0 * Dk + o] : ld_f(qc, o);
     }
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
@@ -174,6 +181,20 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
+  if constexpr (CHD) {
+    // G: cumulative sum of log2 alpha over the chunk per channel (zero past n: flat there),
+    // in place of the log alphas, and to the workspace for the other kernels
+    if (tid < DK) {
+      float g = 0.f;
+      float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
+      for (int t = 0; t < kCMax; ++t) {
+        g = fmaf(Xs[t][tid], kLog2e, g);
+        Xs[t][tid] = g;
+        if (t < n && tid < Dk) Gc[static_cast<long long>(t) * Dk + tid] = g;
+      }
+    }
+    __syncthreads();
+  }
   // fp32 MFMA tiles (lane layout as for mfma4): wave w, lane (col, kq)
   const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kq = lane >> 4;
   // LP[i][j] = exp(g_i - g_j) (X_i . R_j) on the 10 tiles on and below the diagonal (j < i,
@@ -191,19 +212,12 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
       }
     }
   };
-  gram(Es, false);
+  if constexpr (CHD)
+    chd::gram<DK, LD>(Es, Rs, Xs, LP, false, tid);
+  else
+    gram(Es, false);
   __syncthreads();
   tri::inverse_blocks(LP, Tm, Zs, -1, tid);
-  gram(Xs, true);
-  __syncthreads();
-  {   // T and P of the chunk (C x C) for the sweep (P is zero above the diagonal)
-    const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-      const int i = idx / C, j = idx % C;
-      a.Tw[cc + idx] = Tm[i][j];
-      a.Pw[cc + idx] = j <= i ? LP[i][j] : 0.f;
-    }
-  }
   // T (Y (.) scl) on the tiles (token block ib = wave % 4, channel blocks MT (wave / 4) + m):
   // T is lower triangular, so the sum over tokens s ends with block ib
   constexpr int MT = DK / 32;
@@ -213,14 +227,19 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     for (int m = 0; m < MT; ++m) acc[m] = float4v{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < 16 * (ib + 1); s0 += 4) {
       const float at_ = Tm[16 * ib + col][s0 + kq];
-      const float sc = scl(s0 + kq);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = mfma4(at_, sc * Y[s0 + kq][16 * (cb0 + m) + col], acc[m]);
+      for (int m = 0; m < MT; ++m) {
+        const int c = 16 * (cb0 + m) + col;
+        acc[m] = mfma4(at_, scl(s0 + kq, c) * Y[s0 + kq][c], acc[m]);
+      }
     }
   };
-  {   // W = T (e^g (.) E), [B, H, NC, C, Dk]
+  auto store_w = [&]() {   // W = T (e^g (.) E), [B, H, NC, C, Dk]
     float4v acc[MT];
-    tri_product(Es, [&](int s0) { return eg[s0]; }, acc);
+    if constexpr (CHD)
+      tri_product(Es, [&](int s, int c) { return exp2f(Xs[s][c]); }, acc);
+    else
+      tri_product(Es, [&](int s, int) { return eg[s]; }, acc);
     float *Wc = a.Ww + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -231,7 +250,32 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
         if (t < n && c < Dk) Wc[static_cast<long long>(t) * Dk + c] = acc[m][r];
       }
     }
+  };
+  if constexpr (CHD) {
+    // W before P: the queries then take the erase keys' place (G stays in Xs for P)
+    store_w();
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kLoadIt; ++it) {
+      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+      const float x = ld_f(qc, min(t, n - 1) * H * Dk + min(c, Dk - 1));
+      Es[t][c] = (t < n && c < Dk) ? x : 0.f;
+    }
+    __syncthreads();
+    chd::gram<DK, LD>(Es, Rs, Xs, LP, true, tid);
+  } else {
+    gram(Xs, true);
   }
+  __syncthreads();
+  {   // T and P of the chunk (C x C) for the sweep (P is zero above the diagonal)
+    const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int i = idx / C, j = idx % C;
+      a.Tw[cc + idx] = Tm[i][j];
+      a.Pw[cc + idx] = j <= i ? LP[i][j] : 0.f;
+    }
+  }
+  if constexpr (!CHD) store_w();
   // U = T V' by blocks of DK value columns, [B, T, H, Dv]
   for (int vb = 0; vb < Dv; vb += DK) {
     __syncthreads();   // Xs free (P formed / previous block used)
@@ -254,7 +298,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
     float4v acc[MT];
-    tri_product(Xs, [&](int) { return 1.f; }, acc);
+    tri_product(Xs, [&](int, int) { return 1.f; }, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int c = vb + 16 * (cb0 + m) + col;
@@ -274,12 +318,14 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 // S <- e^{g_n} S + (e^{g_n - g} (.) D)^T R; the state at every chunk start is saved too.  S
 // lives in the waves' accumulators (16 x 16 tiles), mirrored in LDS for D's product; wave w
 // owns the tile (token block w % 4, value-row block w / 4) of D.  The next chunk's W, R and U
-// are loaded during this chunk.
+// are loaded during this chunk.  With per-channel decay (CHD) the update is
+// S <- S Diag(2^G_n) + D^T (2^(G_n - G) (.) R): the write keys are decayed elementwise as
+// they are staged and the state's columns scaled.
 // ---------------------------------------------------------------------------------------
 constexpr int kStBV = 32;
 constexpr int kStThreads = 512;
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHD>
 __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kStBV, kThreads = kStThreads;
@@ -302,11 +348,13 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   const int tb = wave & 3, rb = wave >> 2;
 
   __shared__ __align__(16) float Ws[kCMax][LD];   // W of the chunk
-  __shared__ __align__(16) IO Rs[kCMax][LD];      // write keys (in the io type: exact)
+  using RT = std::conditional_t<CHD, float, IO>;
+  __shared__ __align__(16) RT Rs[kCMax][LD];      // write keys (io type: exact; CHD: decayed, fp32)
   __shared__ __align__(16) float Ss[kBV][LD];     // mirror of the state
   __shared__ __align__(16) float Dl[kCMax][kBV];  // e^{g_n - g} D
   __shared__ __align__(16) float Us[kCMax][kBV];  // U
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
+  __shared__ float gcn[CHD ? DK : 1];            // CHD: 2^G_n per channel
 
   float4v Sacc[NTW];
 #pragma unroll
@@ -330,6 +378,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
   float pw[kLoadIt], pu[kUIt];
   IO pr[kLoadIt];
+  float pg[CHD ? kLoadIt : 1], pgn = 0.f;   // CHD: G of the staged elements, G_n of the thread's channel
   // loads of chunk ci into registers (indices clamped into the chunk)
   auto cload = [&](int ci) {
     const int c0 = ci * C, n = min(C, T - c0);
@@ -340,6 +389,16 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
       pw[it] = Wc[static_cast<long long>(t) * Dk + c];
       pr[it] = rbase[(row0 + static_cast<long long>(t) * H) * Dk + c];
+    }
+    if constexpr (CHD) {
+      // (kThreads is a multiple of DK: the thread's channel is the same in every item)
+      const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
+#pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
+        pg[it] = Gc[static_cast<long long>(t) * Dk + c];
+      }
+      pgn = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
     }
 #pragma unroll
     for (int it = 0; it < kUIt; ++it) {
@@ -371,7 +430,13 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
       const bool in = t < n && c < Dk;
       Ws[t][c] = in ? pw[it] : 0.f;
-      Rs[t][c] = in ? pr[it] : IO(0);
+      if constexpr (CHD)
+        Rs[t][c] = in ? ld_f(pr, it) * exp2f(pgn - pg[it]) : 0.f;
+      else
+        Rs[t][c] = in ? pr[it] : IO(0);
+    }
+    if constexpr (CHD) {
+      if (tid < DK) gcn[tid] = exp2f(pgn);
     }
 #pragma unroll
     for (int it = 0; it < kUIt; ++it) {
@@ -401,7 +466,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
         const int u = wave + 8 * m;
         if (u >= NTS) continue;
         const int rbs = u / NCB, cbs = u % NCB;
-        float4v acc = Sacc[m] * gl, acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
+        float4v acc = Sacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
         // (rows past n of Dl are zero, and n + 7 < 64 + 8: the pairs stay inside the tiles)
         for (int t0 = 0; t0 < n; t0 += 8) {
           acc = mfma4(Dl[t0 + kq][16 * rbs + col], ld_f(&Rs[t0 + kq][16 * cbs + col], 0), acc);
@@ -423,13 +488,15 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
 // lane layout as in the per-chunk pass below).  The gradient dS (kSwBV x Dk) lives in the
 // waves' accumulators for the whole sequence (16 x 16 tiles, a few per wave), mirrored in LDS
 // for the products that read it as an operand.  Per chunk, wave w owns the 16 x 16 tile
-// (token block w % 4, value-row block w / 4) of dD and dX.
+// (token block w % 4, value-row block w / 4) of dD and dX.  With per-channel decay (CHD) the
+// keys are decayed elementwise as they are staged (2^(G_n - G) (.) R, 2^G (.) E, 2^G (.) Q)
+// and dS <- dS Diag(2^G_n) + ... scales the gradient's columns.
 // ---------------------------------------------------------------------------------------
 constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
 
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHD>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kSwBV, kThreads = kSwThreads;
@@ -462,6 +529,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   __shared__ __align__(16) float Am[kCMax][kBV];    // scale e^g dO
   __shared__ __align__(16) float Bm[kCMax][kBV];    // e^g dX
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
+  __shared__ float gcn[CHD ? DK : 1];   // CHD: 2^G_n per channel
 
   const long long sh = static_cast<long long>(b) * H + h;
   // dS tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
@@ -490,6 +558,9 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   // only after the first two barriers of a chunk, are loaded at its start.
   constexpr int kCC = kCMax * kCMax / kThreads, kOIt = kCMax * kBV / kThreads;
   float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xq[kLoadIt], xt[kCC], xp[kCC], xo[kOIt], xla = 0.f;
+  // CHD: G of the staged elements and G_n of the thread's channel (the same in every item:
+  // kThreads is a multiple of DK), loaded a chunk ahead once this chunk's queries are staged
+  float xgv[CHD ? kLoadIt : 1], xgn = 0.f;
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
   auto cload = [&](int ci) {
     const int c0 = ci * C, n = min(C, T - c0);
@@ -518,7 +589,20 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       xo[it] = ld_f(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + r);
     }
   };
-  if (a.NC > 0) cload(a.NC - 1);
+  auto gload = [&](int ci) {
+    const int n = min(C, T - ci * C);
+    const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
+#pragma unroll
+    for (int it = 0; it < kLoadIt; ++it) {
+      const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
+      xgv[it] = Gc[static_cast<long long>(t) * Dk + c];
+    }
+    xgn = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
+  };
+  if (a.NC > 0) {
+    cload(a.NC - 1);
+    if constexpr (CHD) gload(a.NC - 1);
+  }
 
   for (int ci = a.NC - 1; ci >= 0; --ci) {
     const int c0 = ci * C;
@@ -553,8 +637,16 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
       const bool in = t < n && c < Dk;
-      Ks[t][c] = in ? xr[it] : 0.f;
-      Es[t][c] = in ? xg[it] * xk[it] : 0.f;
+      if constexpr (CHD) {
+        Ks[t][c] = in ? xr[it] * exp2f(xgn - xgv[it]) : 0.f;
+        Es[t][c] = in ? xg[it] * xk[it] * exp2f(xgv[it]) : 0.f;
+      } else {
+        Ks[t][c] = in ? xr[it] : 0.f;
+        Es[t][c] = in ? xg[it] * xk[it] : 0.f;
+      }
+    }
+    if constexpr (CHD) {
+      if (tid < DK) gcn[tid] = exp2f(xgn);
     }
 #pragma unroll
     for (int it = 0; it < kCC; ++it) {
@@ -607,7 +699,10 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      Ks[t][c] = (t < n && c < Dk) ? xq[it] : 0.f;
+      Ks[t][c] = (t < n && c < Dk) ? (CHD ? xq[it] * exp2f(xgv[it]) : xq[it]) : 0.f;
+    }
+    if constexpr (CHD) {
+      if (ci > 0) gload(ci - 1);   // this chunk's G is no longer needed
     }
     __syncthreads();
     // dS <- e^{g_n} dS + A^T Q - B^T E on the wave's tiles; rows of A, B past n are zero
@@ -618,7 +713,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
         const int u = wave + 8 * m;
         if (u >= NTS) continue;
         const int rbs = u / NCB, cbs = u % NCB;
-        float4v acc = dSacc[m] * gl, acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
+        float4v acc = dSacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
         for (int t0 = 0; t0 < n; t0 += 4) {
           acc = mfma4(Am[t0 + kq][16 * rbs + col], Ks[t0 + kq][16 * cbs + col], acc);
           acc2 = mfma4(Bm[t0 + kq][16 * rbs + col], Es[t0 + kq][16 * cbs + col], acc2);
@@ -652,11 +747,16 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 // block tb = w % 4 (16 tokens) and channel half hh = w / 4: the 16 x 16 tiles of dQ, dE, dR
 // at (tb, channel tiles of that half); the half-0 waves also own the tiles of dO D^T in row
 // block tb (on and below the diagonal), the half-1 waves those of dX D^T.
+// With per-channel decay (CHD) the wave's channel tiles are two in each 64-channel half, and
+// the key products run over the halves in turn (Q, E, R, G of one half in LDS): the pairwise
+// decay 2^(G_ic - G_jc) sits inside the sums over tokens, split at a reference row for the
+// blocks off the diagonal (matrix cores, every exponent <= 0) and taken pair by pair on the
+// diagonal block; the gate gradient is one per token and channel.
 // ---------------------------------------------------------------------------------------
 constexpr int kCkThreads = 512;
 
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHD>
 __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(DK == 64 || DK == 128, "two halves of 16-channel tiles");
   constexpr int kThreads = kCkThreads;
@@ -687,7 +787,8 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   const long long sh = static_cast<long long>(b) * H + h;
   auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
   const long long row0 = tok(0);
-  auto chan = [&](int m) { return 16 * (MT * hh + m) + col; };   // the lane's column of tile m
+  // the lane's channel in its tile m (CHD: tiles 2 hh, 2 hh + 1 of each 64-channel half)
+  auto chan = [&](int m) { return CHD ? 16 * (4 * (m >> 1) + 2 * hh + (m & 1)) + col : 16 * (MT * hh + m) + col; };
 
   struct TilesA {   // value loop: state rows, their gradients, token tiles by value row
     float S[kVB][LD], dS[kVB][LD], dOT[kVB][LT], dXT[kVB][LT], DT[kVB][LT];
@@ -695,13 +796,20 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   struct TilesB {   // key products: Q, E, R and the C x C gradients dM, dL'
     float Q[kCMax][LD], E[kCMax][LD], R[kCMax][LD], dM[kCMax][LT], dL[kCMax][LT];
   };
+  constexpr int LC = 68;   // (CHD) row stride of the 64-channel half tiles
+  struct TilesC {          // (CHD) key products by channel halves: Q, E, R, G of one half; dM, dL'
+    float Q[kCMax][LC], E[kCMax][LC], R[kCMax][LC], G[kCMax][LC], dM[kCMax][LT], dL[kCMax][LT];
+  };
   __shared__ __align__(16) union {
     TilesA A;
-    TilesB B;
+    std::conditional_t<CHD, TilesC, TilesB> B;
   } sm;
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax], vdx[kCMax];
   __shared__ float dgs[2][kCMax], pks[2][kCMax];
   __shared__ float red[2][kWaves];
+  // (CHD) per-thread shares of <dS'_c, S_c> (the thread's channel is tid % DK), and per token
+  // block: the channel sums of dg and of r (.) (2^(G_n - G) D dS')
+  __shared__ float sdp[CHD ? kThreads : 1], tsum[CHD ? 4 : 1][64], lsum[CHD ? 4 : 1][64];
 
   if (tid < kCMax) chunk_gates(f, row0, n, tid, gs, eg, wd);
 
@@ -797,175 +905,379 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   vsum += __shfl_xor(vsum, 4);
   if ((tid & 7) == 0) vdx[lt] = vsum;
 
-  // ---- key products -------------------------------------------------------------------
-  __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
-  {   // Q, E, R: all loads first (clamped), then the masked LDS stores
-    float xq[kLoadIt], xk[kLoadIt], xg[kLoadIt], xr[kLoadIt];
+  if constexpr (CHD) {
+    // ---- key products, per-channel decay --------------------------------------------------
+    constexpr int NH = DK / 64;                   // channel halves
+    constexpr int kHIt = kCMax * 64 / kThreads;   // staged elements per thread and half
+    auto &B = sm.B;
+    __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
+    sdp[tid] = sdot;
+    // dM = scale dO D^T (j <= i), dL' = -dX D^T (j < i) on the tiles on and below the diagonal
+    // (the decay, per channel, goes inside the products over tokens below)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tr0 + r;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (jb > tb) continue;
+        const int j = 16 * jb + col;
+        if (hh == 0)
+          B.dM[t][j] = (j <= t && t < n) ? f.scale * MPL[jb][r] : 0.f;
+        else
+          B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] : 0.f;
+      }
+    }
     const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
     const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
     const float *bc = f.beta + row0;
+    const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
+    float pk[4] = {0.f, 0.f, 0.f, 0.f};   // k . dE over the lane's channels (scalar gain)
+    for (int hc = 0; hc < NH; ++hc) {
+      {   // Q, E, R, G of channels 64 hc .. 64 hc + 63: loads first (clamped), then masked stores
+        float xq[kHIt], xk[kHIt], xg[kHIt], xr[kHIt], xG[kHIt];
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-      xq[it] = ld_f(qc, o);
-      xk[it] = ld_f(kc, o);
-      xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-      xr[it] = ld_f(rsrc, o);
-    }
-#pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      const bool in = t < n && c < Dk;
-      sm.B.Q[t][c] = in ? xq[it] : 0.f;
-      sm.B.E[t][c] = in ? xg[it] * xk[it] : 0.f;
-      sm.B.R[t][c] = in ? xr[it] : 0.f;
-    }
-  }
-  // the decay factors of the state terms, and the C x C gradients (tiles on and below the
-  // diagonal; the products below never read the others)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = tr0 + r;
-    const float sq = f.scale * eg[t], se = -eg[t], sr = wd[t];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      AQ[m][r] *= sq;
-      AE[m][r] *= se;
-      AR[m][r] *= sr;
-    }
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (jb > tb) continue;
-      const int j = 16 * jb + col;
-      // (the exponent above the diagonal may overflow; it is discarded)
-      const float dec = expf(gs[t] - gs[j]);
-      if (hh == 0)
-        sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MPL[jb][r] * dec : 0.f;
-      else
-        sm.B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] * dec : 0.f;
-    }
-  }
-  __syncthreads();
-  // lambda: this lane's share of sum_j r_j . (e^{g_n - g_j} dS'^T d_j)
-  float lam = 0.f;
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lam = fmaf(sm.B.R[tr0 + r][chan(m)], AR[m][r], lam);
-  // dQ += dM R, dE += dL' R over tokens j < 16 (tb + 1)
-  for (int j0 = 0; j0 < 16 * (tb + 1); j0 += 4) {
-    const int jr = j0 + kq;
-    const float am = sm.B.dM[16 * tb + col][jr], al = sm.B.dL[16 * tb + col][jr];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float br = sm.B.R[jr][chan(m)];
-      AQ[m] = mfma4(am, br, AQ[m]);
-      AE[m] = mfma4(al, br, AE[m]);
-    }
-  }
-  // dR += dM^T Q + dL'^T E over tokens i >= 16 tb
-  for (int i0 = 16 * tb; i0 < kCMax; i0 += 4) {
-    const int ir = i0 + kq;
-    const float am = sm.B.dM[ir][16 * tb + col], al = sm.B.dL[ir][16 * tb + col];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      AR[m] = mfma4(am, sm.B.Q[ir][chan(m)], AR[m]);
-      AR[m] = mfma4(al, sm.B.E[ir][chan(m)], AR[m]);
-    }
-  }
-  // per token: q . dQ + e . dE - r . dR (gate) and k . dE (scalar gain) over the lane's
-  // channels, summed over the 16 lanes of the row group, then over the two channel halves
-  float pg[4], pk[4];
-  const long long rowk0 = row0 * Dk;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = tr0 + r;
-    float acc = 0.f, acck = 0.f;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int c = chan(m);
-      acc = fmaf(sm.B.Q[t][c], AQ[m][r], acc);
-      acc = fmaf(sm.B.E[t][c], AE[m][r], acc);
-      acc = fmaf(-sm.B.R[t][c], AR[m][r], acc);
-      if (f.gain == GDR_GAIN_SCALAR && t < n && c < Dk)
-        acck = fmaf(ld_f(k, rowk0 + static_cast<long long>(t) * H * Dk + c), AE[m][r], acck);
-    }
-    pg[r] = acc;
-    pk[r] = acck;
-  }
-#pragma unroll
-  for (int mm = 1; mm < 16; mm <<= 1)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pg[r] += __shfl_xor(pg[r], mm);
-      pk[r] += __shfl_xor(pk[r], mm);
-    }
-  if (col == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dgs[hh][tr0 + r] = pg[r];
-      pks[hh][tr0 + r] = pk[r];
-    }
-  }
-  // block sums of <dS', S> and lambda
-#pragma unroll
-  for (int mm = 1; mm < 64; mm <<= 1) {
-    sdot += __shfl_xor(sdot, mm);
-    lam += __shfl_xor(lam, mm);
-  }
-  if (lane == 0) {
-    red[0][wave] = sdot;
-    red[1][wave] = lam;
-  }
-  __syncthreads();
-  if (tid < kCMax) {
-    if (f.decay == GDR_DECAY_SCALAR) {
-      // dlog_alpha_t = sum_{i >= t} dg_i inside the chunk
-      float x = tid < n ? dgs[0][tid] + dgs[1][tid] : 0.f;
-      if (tid == n - 1) {
-        float st = 0.f, lt2 = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          st += red[0][w];
-          lt2 += red[1][w];
+        for (int it = 0; it < kHIt; ++it) {
+          const int idx = tid + it * kThreads, t = idx >> 6, c = 64 * hc + (idx & 63);
+          const int tc = min(t, n - 1), cc = min(c, Dk - 1), o = tc * H * Dk + cc;
+          xq[it] = ld_f(qc, o);
+          xk[it] = ld_f(kc, o);
+          xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
+          xr[it] = ld_f(rsrc, o);
+          xG[it] = Gc[static_cast<long long>(tc) * Dk + cc];   // (flat past n)
         }
-        x += eg[n - 1] * st + lt2;
-      }
+        __syncthreads();   // the previous half's tiles are consumed
 #pragma unroll
-      for (int d = 1; d < kCMax; d <<= 1) {
-        const float y = __shfl_down(x, d, kCMax);
-        if (tid + d < kCMax) x += y;
+        for (int it = 0; it < kHIt; ++it) {
+          const int idx = tid + it * kThreads, t = idx >> 6, cl = idx & 63, c = 64 * hc + cl;
+          const bool in = t < n && c < Dk;
+          B.Q[t][cl] = in ? xq[it] : 0.f;
+          B.E[t][cl] = in ? xg[it] * xk[it] : 0.f;
+          B.R[t][cl] = in ? xr[it] : 0.f;
+          B.G[t][cl] = c < Dk ? xG[it] : 0.f;
+        }
       }
-      if (tid < n) a.dla[tok(tid)] = x;
+      __syncthreads();
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int m = 2 * hc + mm;
+        const int cl = 16 * (2 * hh + mm) + col, c = 64 * hc + cl;   // = chan(m)
+        float gt[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gt[r] = B.G[tr0 + r][cl];
+        const float gn = B.G[n - 1][cl];
+        // the state terms' decays; this lane's share of sum_j r_j (.) (2^(G_n - G_j) (D dS')_j)
+        float lam = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2f(gt[r]);
+          AQ[m][r] *= f.scale * e;
+          AE[m][r] *= -e;
+          AR[m][r] *= exp2f(gn - gt[r]);
+          lam = fmaf(B.R[tr0 + r][cl], AR[m][r], lam);
+        }
+        // dQ += dM R, dE += dL' R with 2^(G_i - G_j): the blocks before block tb through their
+        // reference, the row before the block (2^(G_i - G_ref) 2^(G_ref - G_j)), then the
+        // diagonal block pair by pair
+        if (tb > 0) {
+          const float gr = B.G[16 * tb - 1][cl];
+          float4v tq = {0.f, 0.f, 0.f, 0.f}, te = {0.f, 0.f, 0.f, 0.f};
+          #pragma unroll 1
+          for (int j0 = 0; j0 < 16 * tb; j0 += 4) {
+            const int jr = j0 + kq;
+            const float br = B.R[jr][cl] * exp2f(gr - B.G[jr][cl]);
+            tq = mfma4(B.dM[16 * tb + col][jr], br, tq);
+            te = mfma4(B.dL[16 * tb + col][jr], br, te);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sc = exp2f(gt[r] - gr);
+            AQ[m][r] = fmaf(sc, tq[r], AQ[m][r]);
+            AE[m][r] = fmaf(sc, te[r], AE[m][r]);
+          }
+        }
+        #pragma unroll 2
+        for (int jj = 0; jj < 16; ++jj) {
+          const int j = 16 * tb + jj;
+          const float rj = B.R[j][cl], gj = B.G[j][cl];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = tr0 + r;
+            // (the exponent above the diagonal may overflow; it is discarded)
+            const float w = j <= i ? rj * exp2f(gt[r] - gj) : 0.f;
+            AQ[m][r] = fmaf(B.dM[i][j], w, AQ[m][r]);
+            AE[m][r] = fmaf(B.dL[i][j], w, AE[m][r]);
+          }
+        }
+        // dR += dM^T Q + dL'^T E with 2^(G_i - G_j): the blocks after block tb through the
+        // block's last row, then the diagonal block pair by pair
+        {
+          const float gr = B.G[16 * tb + 15][cl];
+          float4v tr = {0.f, 0.f, 0.f, 0.f};
+          // (i0 < n keeps every row read below 64; rows past n are zero)
+          #pragma unroll 1
+          for (int i0 = 16 * (tb + 1); i0 < n; i0 += 4) {
+            const int ir = i0 + kq;
+            const float sc = exp2f(B.G[ir][cl] - gr);
+            tr = mfma4(B.dM[ir][16 * tb + col], B.Q[ir][cl] * sc, tr);
+            tr = mfma4(B.dL[ir][16 * tb + col], B.E[ir][cl] * sc, tr);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) AR[m][r] = fmaf(exp2f(gr - gt[r]), tr[r], AR[m][r]);
+        }
+        #pragma unroll 2
+        for (int ii = 0; ii < 16; ++ii) {
+          const int i = 16 * tb + ii;
+          const float qi = B.Q[i][cl], ei = B.E[i][cl], gi = B.G[i][cl];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = tr0 + r;
+            const float w = i >= j ? exp2f(gi - gt[r]) : 0.f;
+            AR[m][r] = fmaf(fmaf(B.dM[i][j], qi, B.dL[i][j] * ei), w, AR[m][r]);
+          }
+        }
+        // dg_tc = q . dQ + e . dE - r . dR per token and channel; dlog alpha is its reverse
+        // cumulative sum along the chunk (rows past n are zero): within the lane's 4 rows, over
+        // the 4 lane groups of the channel, over the 4 token blocks (LDS)
+        float suf[4];
+#pragma unroll
+        for (int r = 3; r >= 0; --r) {
+          const int t = tr0 + r;
+          const float dg = B.Q[t][cl] * AQ[m][r] + B.E[t][cl] * AE[m][r] - B.R[t][cl] * AR[m][r];
+          suf[r] = r == 3 ? dg : dg + suf[r + 1];
+        }
+        float above = 0.f, wtot = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float x = __shfl(suf[0], col + 16 * g);
+          wtot += x;
+          if (g > kq) above += x;
+        }
+        lam += __shfl_xor(lam, 16);
+        lam += __shfl_xor(lam, 32);
+        if (kq == 0) {
+          tsum[tb][cl] = wtot;
+          lsum[tb][cl] = lam;
+        }
+        __syncthreads();
+        float later = 0.f, lamc = 0.f, sdc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (w > tb) later += tsum[w][cl];
+          lamc += lsum[w][cl];
+        }
+#pragma unroll
+        for (int p = 0; p < kThreads / DK; ++p) sdc += sdp[p * DK + min(c, DK - 1)];
+        // the end-of-chunk terms (state decay and 2^(G_n - G) R) enter dg at token n - 1,
+        // so every earlier token's sum holds them
+        const float tail = above + later + exp2f(gn) * sdc + lamc;
+        // chain rule to the variant's inputs, stores
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tr0 + r;
+          if (t >= n || c >= Dk) continue;
+          const long long rowk = tok(t) * Dk;
+          const float de = AE[m][r], dr = AR[m][r];
+          a.dla[rowk + c] = suf[r] + tail;
+          a.dq[rowk + c] = AQ[m][r];
+          float dkv;
+          if (f.gain == GDR_GAIN_SCALAR) {
+            dkv = f.beta[tok(t)] * de;
+            pk[r] = fmaf(ld_f(k, rowk + c), de, pk[r]);
+          } else {
+            dkv = ld_f(er, rowk + c) * de;
+            a.derase[rowk + c] = ld_f(k, rowk + c) * de;
+          }
+          if (f.wkey == GDR_WKEY_EXPLICIT)
+            a.dwk[rowk + c] = dr;
+          else
+            dkv += dr;
+          a.dk[rowk + c] = dkv;
+        }
+      }
     }
-    if (f.gain == GDR_GAIN_SCALAR && tid < n) a.dbeta[tok(tid)] = pks[0][tid] + pks[1][tid] + vdx[tid];
-  }
-  // ---- chain rule to the variant's inputs, stores ------------------------------------
+    if (f.gain == GDR_GAIN_SCALAR) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = tr0 + r;
-    if (t >= n) continue;
-    const long long rowk = tok(t) * Dk;
-    const float bt = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(t)] : 0.f;
+      for (int mm2 = 1; mm2 < 16; mm2 <<= 1)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int c = chan(m);
-      if (c >= Dk) continue;
-      const float de = AE[m][r], dr = AR[m][r];
-      a.dq[rowk + c] = AQ[m][r];
-      float dkv;
-      if (f.gain == GDR_GAIN_SCALAR) {
-        dkv = bt * de;
-      } else {
-        dkv = ld_f(er, rowk + c) * de;
-        a.derase[rowk + c] = ld_f(k, rowk + c) * de;
+        for (int r = 0; r < 4; ++r) pk[r] += __shfl_xor(pk[r], mm2);
+      if (col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pks[hh][tr0 + r] = pk[r];
       }
-      if (f.wkey == GDR_WKEY_EXPLICIT)
-        a.dwk[rowk + c] = dr;
-      else
-        dkv += dr;
-      a.dk[rowk + c] = dkv;
+      __syncthreads();
+      if (tid < n) a.dbeta[tok(tid)] = pks[0][tid] + pks[1][tid] + vdx[tid];
+    }
+  } else {
+    // ---- key products -------------------------------------------------------------------
+    __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
+    {   // Q, E, R: all loads first (clamped), then the masked LDS stores
+      float xq[kLoadIt], xk[kLoadIt], xg[kLoadIt], xr[kLoadIt];
+      const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
+      const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
+      const float *bc = f.beta + row0;
+  #pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
+        xq[it] = ld_f(qc, o);
+        xk[it] = ld_f(kc, o);
+        xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
+        xr[it] = ld_f(rsrc, o);
+      }
+  #pragma unroll
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const bool in = t < n && c < Dk;
+        sm.B.Q[t][c] = in ? xq[it] : 0.f;
+        sm.B.E[t][c] = in ? xg[it] * xk[it] : 0.f;
+        sm.B.R[t][c] = in ? xr[it] : 0.f;
+      }
+    }
+    // the decay factors of the state terms, and the C x C gradients (tiles on and below the
+    // diagonal; the products below never read the others)
+  #pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tr0 + r;
+      const float sq = f.scale * eg[t], se = -eg[t], sr = wd[t];
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        AQ[m][r] *= sq;
+        AE[m][r] *= se;
+        AR[m][r] *= sr;
+      }
+  #pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (jb > tb) continue;
+        const int j = 16 * jb + col;
+        // (the exponent above the diagonal may overflow; it is discarded)
+        const float dec = expf(gs[t] - gs[j]);
+        if (hh == 0)
+          sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MPL[jb][r] * dec : 0.f;
+        else
+          sm.B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] * dec : 0.f;
+      }
+    }
+    __syncthreads();
+    // lambda: this lane's share of sum_j r_j . (e^{g_n - g_j} dS'^T d_j)
+    float lam = 0.f;
+  #pragma unroll
+    for (int m = 0; m < MT; ++m)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) lam = fmaf(sm.B.R[tr0 + r][chan(m)], AR[m][r], lam);
+    // dQ += dM R, dE += dL' R over tokens j < 16 (tb + 1)
+    for (int j0 = 0; j0 < 16 * (tb + 1); j0 += 4) {
+      const int jr = j0 + kq;
+      const float am = sm.B.dM[16 * tb + col][jr], al = sm.B.dL[16 * tb + col][jr];
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float br = sm.B.R[jr][chan(m)];
+        AQ[m] = mfma4(am, br, AQ[m]);
+        AE[m] = mfma4(al, br, AE[m]);
+      }
+    }
+    // dR += dM^T Q + dL'^T E over tokens i >= 16 tb
+    for (int i0 = 16 * tb; i0 < kCMax; i0 += 4) {
+      const int ir = i0 + kq;
+      const float am = sm.B.dM[ir][16 * tb + col], al = sm.B.dL[ir][16 * tb + col];
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        AR[m] = mfma4(am, sm.B.Q[ir][chan(m)], AR[m]);
+        AR[m] = mfma4(al, sm.B.E[ir][chan(m)], AR[m]);
+      }
+    }
+    // per token: q . dQ + e . dE - r . dR (gate) and k . dE (scalar gain) over the lane's
+    // channels, summed over the 16 lanes of the row group, then over the two channel halves
+    float pg[4], pk[4];
+    const long long rowk0 = row0 * Dk;
+  #pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tr0 + r;
+      float acc = 0.f, acck = 0.f;
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int c = chan(m);
+        acc = fmaf(sm.B.Q[t][c], AQ[m][r], acc);
+        acc = fmaf(sm.B.E[t][c], AE[m][r], acc);
+        acc = fmaf(-sm.B.R[t][c], AR[m][r], acc);
+        if (f.gain == GDR_GAIN_SCALAR && t < n && c < Dk)
+          acck = fmaf(ld_f(k, rowk0 + static_cast<long long>(t) * H * Dk + c), AE[m][r], acck);
+      }
+      pg[r] = acc;
+      pk[r] = acck;
+    }
+  #pragma unroll
+    for (int mm = 1; mm < 16; mm <<= 1)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pg[r] += __shfl_xor(pg[r], mm);
+        pk[r] += __shfl_xor(pk[r], mm);
+      }
+    if (col == 0) {
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dgs[hh][tr0 + r] = pg[r];
+        pks[hh][tr0 + r] = pk[r];
+      }
+    }
+    // block sums of <dS', S> and lambda
+  #pragma unroll
+    for (int mm = 1; mm < 64; mm <<= 1) {
+      sdot += __shfl_xor(sdot, mm);
+      lam += __shfl_xor(lam, mm);
+    }
+    if (lane == 0) {
+      red[0][wave] = sdot;
+      red[1][wave] = lam;
+    }
+    __syncthreads();
+    if (tid < kCMax) {
+      if (f.decay == GDR_DECAY_SCALAR) {
+        // dlog_alpha_t = sum_{i >= t} dg_i inside the chunk
+        float x = tid < n ? dgs[0][tid] + dgs[1][tid] : 0.f;
+        if (tid == n - 1) {
+          float st = 0.f, lt2 = 0.f;
+  #pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            st += red[0][w];
+            lt2 += red[1][w];
+          }
+          x += eg[n - 1] * st + lt2;
+        }
+  #pragma unroll
+        for (int d = 1; d < kCMax; d <<= 1) {
+          const float y = __shfl_down(x, d, kCMax);
+          if (tid + d < kCMax) x += y;
+        }
+        if (tid < n) a.dla[tok(tid)] = x;
+      }
+      if (f.gain == GDR_GAIN_SCALAR && tid < n) a.dbeta[tok(tid)] = pks[0][tid] + pks[1][tid] + vdx[tid];
+    }
+    // ---- chain rule to the variant's inputs, stores ------------------------------------
+  #pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tr0 + r;
+      if (t >= n) continue;
+      const long long rowk = tok(t) * Dk;
+      const float bt = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(t)] : 0.f;
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int c = chan(m);
+        if (c >= Dk) continue;
+        const float de = AE[m][r], dr = AR[m][r];
+        a.dq[rowk + c] = AQ[m][r];
+        float dkv;
+        if (f.gain == GDR_GAIN_SCALAR) {
+          dkv = bt * de;
+        } else {
+          dkv = ld_f(er, rowk + c) * de;
+          a.derase[rowk + c] = ld_f(k, rowk + c) * de;
+        }
+        if (f.wkey == GDR_WKEY_EXPLICIT)
+          a.dwk[rowk + c] = dr;
+        else
+          dkv += dr;
+        a.dk[rowk + c] = dkv;
+      }
     }
   }
 }
@@ -974,31 +1286,60 @@ template <typename IO>
 hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   if (a.NC == 0) return hipSuccess;
   const dim3 gp(a.NC, a.f.H, a.f.B);
-  if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_prep_kernel<IO, 64>), gp, dim3(kPrThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_prep_kernel<IO, 128>), gp, dim3(kPrThreads), 0, s, a);
+  const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
+  if (a.f.Dk <= 64) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, true>), gp, dim3(kPrThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, false>), gp, dim3(kPrThreads), 0, s, a);
+  } else {
+    if (chd)
+      hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, true>), gp, dim3(kPrThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, false>), gp, dim3(kPrThreads), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);
-  if (a.f.Dk <= 32)
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 32>), gs, dim3(kStThreads), 0, s, a);
-  else if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 64>), gs, dim3(kStThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_state_kernel<IO, 128>), gs, dim3(kStThreads), 0, s, a);
+  if (a.f.Dk <= 32) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true>), gs, dim3(kStThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false>), gs, dim3(kStThreads), 0, s, a);
+  } else if (a.f.Dk <= 64) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true>), gs, dim3(kStThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false>), gs, dim3(kStThreads), 0, s, a);
+  } else {
+    if (chd)
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true>), gs, dim3(kStThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false>), gs, dim3(kStThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <typename IO>
 hipError_t sweep_io(const BwdArgs &a, hipStream_t s) {
   const dim3 grid((a.f.Dv + kSwBV - 1) / kSwBV, a.f.H, a.f.B);
-  if (a.f.Dk <= 32)
-    hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32>), grid, dim3(kSwThreads), 0, s, a);
-  else if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64>), grid, dim3(kSwThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128>), grid, dim3(kSwThreads), 0, s, a);
+  const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
+  if (a.f.Dk <= 32) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true>), grid, dim3(kSwThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false>), grid, dim3(kSwThreads), 0, s, a);
+  } else if (a.f.Dk <= 64) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true>), grid, dim3(kSwThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false>), grid, dim3(kSwThreads), 0, s, a);
+  } else {
+    if (chd)
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true>), grid, dim3(kSwThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false>), grid, dim3(kSwThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -1006,10 +1347,18 @@ template <typename IO>
 hipError_t chunk_io(const BwdArgs &a, hipStream_t s) {
   if (a.NC == 0) return hipSuccess;
   const dim3 grid(a.NC, a.f.H, a.f.B);
-  if (a.f.Dk <= 64)
-    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64>), grid, dim3(kCkThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128>), grid, dim3(kCkThreads), 0, s, a);
+  const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
+  if (a.f.Dk <= 64) {
+    if (chd)
+      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, true>), grid, dim3(kCkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, false>), grid, dim3(kCkThreads), 0, s, a);
+  } else {
+    if (chd)
+      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, true>), grid, dim3(kCkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, false>), grid, dim3(kCkThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -34,8 +34,9 @@ struct BwdArgs {
   const float *dstate_out;   // [B,H,Dv,Dk] or null (zero)
   float *dq, *dk, *dv, *dbeta, *derase, *dwrite, *dla, *dwk, *dstate_in;
   // workspace: states at chunk starts and their gradients [B,H,NC,Dv,Dk], D and dX
-  // [B,T,H,Dv], T and P [B,H,NC,C,C], W [B,H,NC,C,Dk], U [B,T,H,Dv]
-  float *h, *dh, *D, *dX, *Tw, *Pw, *Ww, *Uw;
+  // [B,T,H,Dv], T and P [B,H,NC,C,C], W [B,H,NC,C,Dk], U [B,T,H,Dv]; with per-channel decay
+  // also G [B,H,NC,C,Dk], the in-chunk cumulative log2 decay (null otherwise)
+  float *h, *dh, *D, *dX, *Tw, *Pw, *Ww, *Uw, *Gw;
   int NC;   // chunks per stream
 };
 

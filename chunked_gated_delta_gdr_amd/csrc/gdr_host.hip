@@ -56,7 +56,7 @@ constexpr long double kMaxElems = 1099511627776.0L;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
-  uint64_t h, dh, D, dX, T, P, W, U, total;
+  uint64_t h, dh, D, dX, T, P, W, U, G, total;
   int NC;
 };
 
@@ -74,7 +74,8 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   L.P = L.T + cc;
   L.W = L.P + cc;
   L.U = L.W + al(B * H * NC * C * Dk * 4u);
-  L.total = L.U + tk;
+  L.G = L.U + tk;
+  L.total = L.G + (d.decay == GDR_DECAY_CHANNEL ? al(B * H * NC * C * Dk * 4u) : 0u);
   L.NC = static_cast<int>(NC);
   return L;
 }
@@ -275,7 +276,6 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   if (st != GDR_OK) return fail(st, "forward arguments (d_out checked as out): %s", g_last_error.c_str());
   if (g == nullptr) return fail(GDR_EINVAL, "grads must be non-NULL");
   if (d->wkey == GDR_WKEY_DIAG_PRECOND) return fail(GDR_ENOTSUP, "backward of the preconditioned write key");
-  if (d->decay == GDR_DECAY_CHANNEL) return fail(GDR_ENOTSUP, "backward of the per-channel decay");
   if (d->neumann_order >= 0) return fail(GDR_ENOTSUP, "backward of the band-limited T (exact T only)");
   const bool need = d->T > 0;
   struct Opt {
@@ -292,7 +292,7 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
       {"dbeta", g->dbeta, d->gain == GDR_GAIN_SCALAR, ntok},
       {"derase", g->derase, d->gain == GDR_GAIN_CHANNEL, ntok * Dk},
       {"dwrite", g->dwrite, d->gain == GDR_GAIN_CHANNEL, ntok * Dv},
-      {"dlog_alpha", g->dlog_alpha, d->decay == GDR_DECAY_SCALAR, ntok},
+      {"dlog_alpha", g->dlog_alpha, d->decay != GDR_DECAY_NONE, d->decay == GDR_DECAY_CHANNEL ? ntok * Dk : ntok},
       {"dwrite_key", g->dwrite_key, d->wkey == GDR_WKEY_EXPLICIT, ntok * Dk},
   };
   for (const Opt &o : outs) {
@@ -314,7 +314,8 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   const Range inputs[] = {
       rng("q", in->q, ntok * Dk * esz), rng("k", in->k, ntok * Dk * esz),
       rng("v", in->v, ntok * Dv * esz), rng("beta", in->beta, ntok * 4),
-      rng("log_alpha", in->log_alpha, ntok * 4), rng("erase", in->erase, ntok * Dk * esz),
+      rng("log_alpha", in->log_alpha, (d->decay == GDR_DECAY_CHANNEL ? ntok * Dk : ntok) * 4),
+      rng("erase", in->erase, ntok * Dk * esz),
       rng("write", in->write, ntok * Dv * esz), rng("write_key", in->write_key, ntok * Dk * esz),
       rng("state_in", state_in, B * H * Dv * Dk * 4), rng("d_out", d_out, ntok * Dv * esz),
       rng("d_state_out", d_state_out, B * H * Dv * Dk * 4)};
@@ -351,6 +352,7 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
     b.Pw = reinterpret_cast<float *>(ws + L.P);
     b.Ww = reinterpret_cast<float *>(ws + L.W);
     b.Uw = reinterpret_cast<float *>(ws + L.U);
+    b.Gw = d->decay == GDR_DECAY_CHANNEL ? reinterpret_cast<float *>(ws + L.G) : nullptr;
   }
   b.dout = d_out;
   b.dstate_out = d_state_out;

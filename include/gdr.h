@@ -174,7 +174,7 @@ typedef struct gdr_grads {
   float *dbeta;       /* [B,T,H]; iff gain == SCALAR, else NULL                            */
   float *derase;      /* [B,T,H,Dk]; iff gain == CHANNEL, else NULL                        */
   float *dwrite;      /* [B,T,H,Dv]; iff gain == CHANNEL, else NULL                        */
-  float *dlog_alpha;  /* [B,T,H]; iff decay == SCALAR, else NULL                           */
+  float *dlog_alpha;  /* [B,T,H] if decay == SCALAR, [B,T,H,Dk] if CHANNEL, else NULL       */
   float *dwrite_key;  /* [B,T,H,Dk]; iff wkey == EXPLICIT, else NULL                       */
   float *dstate_in;   /* [B,H,Dv,Dk] or NULL (not written)                                 */
 } gdr_grads_t;
@@ -194,9 +194,14 @@ typedef struct gdr_grads {
  *        dS <- e^{g_C} dS + scale dO^T (e^g (.) Q) - dX^T (e^g (.) E);
  *   4. per chunk, in parallel: dQ, dE, dR and the gate gradient from the stored states,
  *      the state gradients, D and dX, then the chain rule to the variant's inputs.
+ * With per-channel decay (the Diag gate; Kimi Delta Attention in the pages' related-work
+ * sections) every e^g above is per key channel: e^g (.) E, e^g (.) Q and e^{g_C - g} (.) R
+ * elementwise, e^{g_C} dS scales the state's columns, the pairwise decay sits inside the
+ * products over channels (L, P) and over tokens (dQ, dE, dR), and the gate gradient is one
+ * per token and channel.
  * All arithmetic is fp32 (inputs in io_dtype are widened once).
  *
- * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR, wkey SAME | EXPLICIT, exact T
+ * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR | CHANNEL, wkey SAME | EXPLICIT, exact T
  * (neumann_order < 0), chunk 16 | 32 | 64, Dk <= 128, Dv <= 512, io fp32 | bf16; anything
  * else returns GDR_ENOTSUP (desc->impl is ignored).
  *
@@ -217,6 +222,7 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
 /* Bytes of workspace gdr_chunk_bwd needs for this descriptor (0 if it is rejected or
  * T == 0): the chunk-start states and their gradients (2 B H ceil(T/C) Dv Dk floats), D,
  * dX and U (3 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats) and W
+ * (B H ceil(T/C) C Dk floats), with decay CHANNEL also the cumulative decays G
  * (B H ceil(T/C) C Dk floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 

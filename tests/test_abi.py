@@ -217,13 +217,16 @@ def _al(x):
     return (x + 255) // 256 * 256
 
 
+@pytest.mark.parametrize("decay", [G.GDR_DECAY_SCALAR, G.GDR_DECAY_CHANNEL])
 @pytest.mark.parametrize("T,C", [(100, 64), (64, 64), (1, 16), (4096, 32), (0, 64)])
-def test_bwd_workspace_size_formula(T, C):
-    d = desc(T=T, chunk=C)
+def test_bwd_workspace_size_formula(T, C, decay):
+    d = desc(T=T, chunk=C, decay=decay)
     B, H, Dk, Dv = 2, 3, 64, 32
     NC = (T + C - 1) // C
     want = (2 * _al(B * H * NC * Dv * Dk * 4) + 3 * _al(B * T * H * Dv * 4) + 2 * _al(B * H * NC * C * C * 4)
             + _al(B * H * NC * C * Dk * 4))
+    if decay == G.GDR_DECAY_CHANNEL:   # the cumulative decays G
+        want += _al(B * H * NC * C * Dk * 4)
     assert G.gdr_chunk_bwd_workspace_size(d) == want
     assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
 
@@ -236,7 +239,7 @@ def bwd_args(d, **over):
         ins["beta"] = p[3]
     else:
         ins["erase"], ins["write"] = p[4], p[5]
-    if d.decay == G.GDR_DECAY_SCALAR:
+    if d.decay != G.GDR_DECAY_NONE:
         ins["log_alpha"] = p[6]
     if d.wkey == G.GDR_WKEY_EXPLICIT:
         ins["write_key"] = p[7]
@@ -245,7 +248,7 @@ def bwd_args(d, **over):
         gr["dbeta"] = p[13]
     else:
         gr["derase"], gr["dwrite"] = p[14], p[15]
-    if d.decay == G.GDR_DECAY_SCALAR:
+    if d.decay != G.GDR_DECAY_NONE:
         gr["dlog_alpha"] = p[16]
     if d.wkey == G.GDR_WKEY_EXPLICIT:
         gr["dwrite_key"] = p[17]
@@ -264,20 +267,17 @@ def call_validate_bwd(d, **over):
 
 
 @pytest.mark.parametrize("gain", [G.GDR_GAIN_SCALAR, G.GDR_GAIN_CHANNEL])
-@pytest.mark.parametrize("decay", [G.GDR_DECAY_NONE, G.GDR_DECAY_SCALAR])
+@pytest.mark.parametrize("decay", [G.GDR_DECAY_NONE, G.GDR_DECAY_SCALAR, G.GDR_DECAY_CHANNEL])
 @pytest.mark.parametrize("wkey", [G.GDR_WKEY_SAME, G.GDR_WKEY_EXPLICIT])
 def test_bwd_accepts_supported_variants(gain, decay, wkey):
     d = desc(gain=gain, decay=decay, wkey=wkey)
     assert call_validate_bwd(d) == G.GDR_OK, G.gdr_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(wkey=G.GDR_WKEY_DIAG_PRECOND), dict(decay=G.GDR_DECAY_CHANNEL),
-                                dict(neumann_order=3)])
+@pytest.mark.parametrize("kw", [dict(wkey=G.GDR_WKEY_DIAG_PRECOND), dict(neumann_order=3)])
 def test_bwd_rejects_unsupported_variants(kw):
     d = desc(**kw)
     ins, gr, a = bwd_args(d)
-    if kw.get("decay") == G.GDR_DECAY_CHANNEL:
-        ins.log_alpha = BASE + 6 * MB
     assert G.gdr_validate_bwd(d, ins, None, a["d_out"], None, gr, a["workspace"],
                               a["workspace_bytes"]) == G.GDR_ENOTSUP, G.gdr_last_error()
 

@@ -22,13 +22,15 @@ def announce(msg):
 
 def spec(variant, **kw):
     base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "explicit": "gdn",
-            "gdn2_decay": "gdn2"}[variant]
+            "gdn2_decay": "gdn2", "kda": "kda", "kda_gdn2": "kda", "kda_explicit": "kda"}[variant]
     over = dict(B=2, H=2, T=200, Dk=64, Dv=48, dtype="f32", seed=21)
     over.update(kw)
-    if variant == "explicit":
+    if variant in ("explicit", "kda_explicit"):
         over["wkey"] = "explicit"
     if variant == "gdn2_decay":
         over["decay"] = "scalar"
+    if variant == "kda_gdn2":
+        over["gain"] = "channel"
     return gs.spec(base, **over)
 
 
@@ -80,7 +82,8 @@ def state(s, seed=5, amp=0.3):
     return (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * amp).astype(np.float32)
 
 
-@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "explicit", "gdn2_decay"])
+@pytest.mark.parametrize("variant", ["plain", "gdn", "gdn2", "explicit", "gdn2_decay", "kda", "kda_gdn2",
+                                     "kda_explicit"])
 def test_bwd_variants_fp32(variant):
     s = spec(variant)
     announce(f"bwd {variant} f32 {s}")
@@ -90,7 +93,7 @@ def test_bwd_variants_fp32(variant):
 
 
 @pytest.mark.parametrize("chunk", [16, 32])
-@pytest.mark.parametrize("variant", ["gdn", "gdn2_decay"])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2_decay", "kda"])
 def test_bwd_chunk_sizes(variant, chunk):
     s = spec(variant, T=77, chunk=chunk)
     announce(f"bwd {variant} f32 chunk {chunk} {s}")
@@ -106,7 +109,7 @@ def test_bwd_head_dims(Dk, Dv):
     compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2", "explicit"])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "explicit", "kda"])
 def test_bwd_bf16(variant):
     s = spec(variant, dtype="bf16", Dk=128, Dv=128, T=200)
     announce(f"bwd {variant} bf16 {s}")
@@ -156,6 +159,64 @@ def test_bwd_full_size_gdn_sampled():
     s = gs.spec("gdn")
     streams = [(0, 0), (3, 15)]
     announce(f"bwd gdn full size {s}, streams {streams}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s, amp=0.1)
+    got = run_bwd(s, x, cot, state_in=S0)
+    for name, val in got.items():
+        assert np.all(np.isfinite(val)), name
+    ref = oracle_grads(s, x, cot, state_in=S0, streams=streams, checkpoint=64)
+    compare(got, ref, streams=streams)
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (32, 16)])
+def test_bwd_kda_head_dims(Dk, Dv):
+    s = spec("kda", Dk=Dk, Dv=Dv, T=130)
+    announce(f"bwd kda f32 Dk={Dk} Dv={Dv} {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65])
+def test_bwd_kda_short_and_ragged(T):
+    s = spec("kda", T=T)
+    announce(f"bwd kda f32 T={T}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
+
+
+def test_bwd_kda_no_state():
+    s = spec("kda", T=150)
+    announce(f"bwd kda f32 no state_in, no d_state_out {s}")
+    x, cot = gs.make_inputs(s), gs.make_cotangents(s)
+    compare(run_bwd(s, x, cot, state_in=None, d_state_out=False),
+            oracle_grads(s, x, cot, state_in=None, d_state_out=False))
+
+
+def test_bwd_kda_equal_channels_is_scalar_decay():
+    """Per-channel decays that are equal across the channels give the scalar-decay gradients,
+    with dlog_alpha (scalar) the channel sum of dlog_alpha (per channel)."""
+    s = spec("kda", T=150)
+    announce(f"bwd kda equal channels vs gdn {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    la = x["log_alpha"][..., 0].copy()
+    xc = dict(x, log_alpha=np.ascontiguousarray(np.repeat(la[..., None], s.Dk, axis=-1)))
+    xs = dict(x, log_alpha=la)
+    gc = run_bwd(s, xc, cot, state_in=S0)
+    gsc = run_bwd(spec("gdn", T=150), xs, cot, state_in=S0)
+    for name in ("dq", "dk", "dv", "dbeta", "dstate_in"):
+        err = O.rel_l2(gc[name], gsc[name])
+        print(f"  {name}: rel-L2 {err:.2e}", flush=True)
+        assert err <= TOL_F32, (name, err)
+    err = O.rel_l2(gc["dlog_alpha"].sum(-1), gsc["dlog_alpha"])
+    print(f"  dlog_alpha (channel sum): rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL_F32
+
+
+def test_bwd_full_size_kda_sampled():
+    """The kda workload at full size (B4 H16 T4096 d128 bf16): two streams against the oracle
+    (checkpointed reverse sweep), every gradient finite everywhere."""
+    s = gs.spec("kda")
+    streams = [(0, 0), (3, 15)]
+    announce(f"bwd kda full size {s}, streams {streams}")
     x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s, amp=0.1)
     got = run_bwd(s, x, cot, state_in=S0)
     for name, val in got.items():
