@@ -184,11 +184,15 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   if constexpr (CHD) {
     // G: cumulative sum of log2 alpha over the chunk per channel (zero past n: flat there),
     // in place of the log alphas, and to the workspace for the other kernels
-    if (tid < DK) {
+    if (tid < DK) {   // (all reads first, so they are in flight together)
+      float gv[kCMax];
+#pragma unroll
+      for (int t = 0; t < kCMax; ++t) gv[t] = Xs[t][tid];
       float g = 0.f;
       float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
+#pragma unroll
       for (int t = 0; t < kCMax; ++t) {
-        g = fmaf(Xs[t][tid], kLog2e, g);
+        g = fmaf(gv[t], kLog2e, g);
         Xs[t][tid] = g;
         if (t < n && tid < Dk) Gc[static_cast<long long>(t) * Dk + tid] = g;
       }
