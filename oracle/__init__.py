@@ -44,4 +44,4 @@ from .core import (  # noqa: F401
     rel_l2,
     snr_db,
 )
-from .backward import recurrent_grad, recurrent_stream_grad  # noqa: F401
+from .backward import precond_grad, recurrent_grad, recurrent_stream_grad  # noqa: F401

@@ -18,10 +18,16 @@ reverse sweep carries G = dL/dS_t:
 and dS_0 = G at the end.  The variant vectors are then differentiated by the chain rule:
 e = beta k | b (.) k, v' = beta v | w (.) v, r = k | given write key.
 
-Pinned in ``tests/test_oracle_pins.py`` by central finite differences of the forward
-oracle (every input element, every variant) and by the causal linear-attention special
-case, whose gradients are textbook.  The diagonal preconditioner is not differentiated
-here.
+With the diagonal preconditioner [PDN section 2b] the write key is r_t = k_t (.) p_t,
+p_t = 1 / (h_t / b_t + eps), b_t = 1 - rho^(t0 + t + 1), h_t = rho h_{t-1} + k_t (.) k_t
+(per channel, h_0 the accumulator given), so dr_t reaches k through p_t as well: with
+a_t = -(dr_t (.) k_t (.) p_t (.) p_t) / b_t (dL/dh_t through p_t alone) and the accumulator's
+total gradient H_t = a_t + rho H_{t+1} (H_{T+1} = 0: the final accumulator is not part of
+the loss), dk_t gets dr_t (.) p_t + 2 k_t (.) H_t and the initial accumulator rho H_1.
+
+Pinned in ``tests/test_oracle_grad_pins.py`` by central finite differences of the forward
+oracle (every input element, every variant, the preconditioner included) and by the causal
+linear-attention special case, whose gradients are textbook.
 """
 from __future__ import annotations
 
@@ -29,13 +35,36 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .core import F64, _stream, variant_vectors
+from .core import F64, _precond_for, _stream, variant_vectors
+
+
+def precond_grad(k: np.ndarray, dr: np.ndarray, rho: float, eps: float, h_init: np.ndarray,
+                 t0: int):
+    """Chain rule through the diagonal preconditioner of one stream: given dr = dL/dr_t for
+    the write keys r_t = k_t (.) p_t, returns (dL/dk_t through r, dL/dh_init)."""
+    k = np.asarray(k, dtype=F64)
+    dr = np.asarray(dr, dtype=F64)
+    T = k.shape[0]
+    # the forward prefix: p_t and b_t of every token
+    h = np.array(h_init, dtype=F64, copy=True)
+    p = np.empty_like(k)
+    bt = np.empty(T, dtype=F64)
+    for t in range(T):
+        h = rho * h + k[t] * k[t]
+        bt[t] = 1.0 - rho ** (t0 + t + 1)
+        p[t] = 1.0 / (h / bt[t] + eps)
+    dk = np.empty_like(k)
+    Ht = np.zeros(k.shape[1], dtype=F64)
+    for t in reversed(range(T)):
+        Ht = -(dr[t] * k[t] * p[t] * p[t]) / bt[t] + rho * Ht
+        dk[t] = dr[t] * p[t] + 2.0 * k[t] * Ht
+    return dk, rho * Ht
 
 
 def recurrent_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray,
                           dS_T: Optional[np.ndarray] = None, *, scale: float = 1.0,
-                          S0: Optional[np.ndarray] = None, checkpoint: int = 0
-                          ) -> Dict[str, np.ndarray]:
+                          S0: Optional[np.ndarray] = None, checkpoint: int = 0,
+                          precond: Optional[dict] = None) -> Dict[str, np.ndarray]:
     """Gradients of one stream's loss with respect to its inputs.
 
     ``x`` holds one stream's [T, D] / [T] arrays as for ``core.recurrent_stream``; ``dO`` is
@@ -44,9 +73,11 @@ def recurrent_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray,
     reverse sweep (for long sequences); 0 keeps every state.
 
     Returns dq, dk, dv, dS0 and, as the variant has them, dbeta | (derase, dwrite),
-    dlog_alpha ([T] or [T, Dk]) and dwrite_key.
+    dlog_alpha ([T] or [T, Dk]) and dwrite_key.  ``precond`` = dict(rho, eps, h_init, t0)
+    selects the diagonal preconditioner for the write key; then dpc_h_init (dL/dh_init,
+    [Dk]) is returned as well.
     """
-    e, r, vp, la, _ = variant_vectors(x)
+    e, r, vp, la, _ = variant_vectors(x, precond=precond)
     q = np.asarray(x["q"], dtype=F64) * scale
     dO = np.asarray(dO, dtype=F64)
     T, Dk = e.shape
@@ -114,7 +145,11 @@ def recurrent_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray,
         dk = beta[:, None] * de
         g["dbeta"] = np.sum(k * de, axis=1) + np.sum(v * dvp, axis=1)
         g["dv"] = beta[:, None] * dvp
-    if x.get("write_key") is not None:
+    if precond is not None:
+        dkp, dh0 = precond_grad(k, dr, precond["rho"], precond["eps"], precond["h_init"], precond["t0"])
+        dk = dk + dkp
+        g["dpc_h_init"] = dh0
+    elif x.get("write_key") is not None:
         g["dwrite_key"] = dr
     else:
         dk = dk + dr
@@ -126,10 +161,11 @@ def recurrent_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray,
 
 def recurrent_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.ndarray] = None,
                    *, scale: float = 1.0, state0: Optional[np.ndarray] = None, streams=None,
-                   checkpoint: int = 0) -> Dict[str, np.ndarray]:
+                   checkpoint: int = 0, precond: Optional[dict] = None) -> Dict[str, np.ndarray]:
     """Gradients over [B, T, H, D] inputs (every stream, or the listed (b, h) pairs; the
     other entries stay zero).  ``dO`` is [B, T, H, Dv], ``dS_T`` [B, H, Dv, Dk] or None.
-    The results have the inputs' shapes; dS0 is [B, H, Dv, Dk]."""
+    ``precond`` = dict(rho, eps, h0 or h_init [B, H, Dk], t0) as for ``core.recurrent``.
+    The results have the inputs' shapes; dS0 is [B, H, Dv, Dk], dpc_h_init [B, H, Dk]."""
     B, T, H, _ = x["q"].shape
     Dk = x["k"].shape[-1]
     Dv = x["v"].shape[-1]
@@ -139,12 +175,12 @@ def recurrent_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.n
         gb = recurrent_stream_grad(_stream(x, b, h), np.asarray(dO)[b, :, h],
                                    None if dS_T is None else dS_T[b, h], scale=scale,
                                    S0=None if state0 is None else state0[b, h],
-                                   checkpoint=checkpoint)
+                                   checkpoint=checkpoint, precond=_precond_for(precond, b, h, Dk))
         for key, val in gb.items():
             if key not in out:
-                shape = (B, H, Dv, Dk) if key == "dS0" else (B, T, H) + val.shape[1:]
+                shape = {"dS0": (B, H, Dv, Dk), "dpc_h_init": (B, H, Dk)}.get(key, (B, T, H) + val.shape[1:])
                 out[key] = np.zeros(shape, dtype=F64)
-            if key == "dS0":
+            if key in ("dS0", "dpc_h_init"):
                 out[key][b, h] = val
             else:
                 out[key][b, :, h] = val

@@ -112,3 +112,50 @@ def test_batched_wrapper_places_streams():
     np.testing.assert_array_equal(g["dlog_alpha"][1, :, 2], one["dlog_alpha"])
     np.testing.assert_array_equal(g["dS0"][1, 2], one["dS0"])
     assert np.all(g["dk"][0] == 0) and np.all(g["dS0"][1, 1] == 0)
+
+
+PRECOND_VARIANTS = ["gdn", "gdn2", "kda", "plain"]
+
+
+@pytest.mark.parametrize("variant", PRECOND_VARIANTS)
+def test_preconditioner_gradients_match_central_differences(variant):
+    """The diagonal preconditioner on the write key (r_t = k_t (.) p_t): dk through both the
+    erase and the write key, and dL/dh_init, against central differences of the forward."""
+    x, S0, dO, dST = tiny_stream(variant, T=6, seed=40 + PRECOND_VARIANTS.index(variant))
+    rng = np.random.default_rng(7)
+    pre = dict(rho=0.8, eps=0.1, h_init=rng.uniform(0.1, 0.6, x["k"].shape[1]), t0=3)
+    scale = 0.9
+
+    def loss(xx, h_init):
+        o, S, _ = O.recurrent_stream(xx, scale=scale, S0=S0, precond=dict(pre, h_init=h_init))
+        return float(np.sum(o * dO) + np.sum(S * dST))
+
+    g = O.recurrent_stream_grad(x, dO, dST, scale=scale, S0=S0, precond=pre)
+    assert "dwrite_key" not in g
+    h = 1e-6
+    for key, gname in [("k", "dk"), ("q", "dq"), ("h_init", "dpc_h_init")]:
+        base = pre["h_init"] if key == "h_init" else x[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                pert = base.copy()
+                pert[idx] += sgn * h
+                vals.append(loss(x, pert) if key == "h_init" else loss({**x, key: pert}, pre["h_init"]))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        err = np.max(np.abs(g[gname] - fd))
+        assert err <= 1e-7 * (1.0 + np.max(np.abs(fd))), (gname, err)
+
+
+def test_preconditioner_gradient_of_a_constant_accumulator():
+    """rho -> 0 with a zero initial accumulator: p_t = 1 / (k_t^2 + eps) elementwise, so
+    r_t = k_t / (k_t^2 + eps) and dr/dk = (eps - k^2) / (k^2 + eps)^2: the chain rule
+    reduces to that closed form (rho = 1e-300 leaves the accumulator the current key's
+    square to fp64 precision)."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((5, 4))
+    dr = rng.standard_normal((5, 4))
+    eps = 0.3
+    dk, dh0 = O.precond_grad(k, dr, 1e-300, eps, np.zeros(4), 0)
+    np.testing.assert_allclose(dk, dr * (eps - k * k) / (k * k + eps) ** 2, rtol=1e-12, atol=1e-14)
+    assert np.all(np.abs(dh0) < 1e-250)
