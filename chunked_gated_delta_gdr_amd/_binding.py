@@ -46,7 +46,7 @@ class gdr_grads_t(ctypes.Structure):
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
         ("dbeta", ctypes.c_void_p), ("derase", ctypes.c_void_p), ("dwrite", ctypes.c_void_p),
         ("dlog_alpha", ctypes.c_void_p), ("dwrite_key", ctypes.c_void_p),
-        ("dstate_in", ctypes.c_void_p),
+        ("dstate_in", ctypes.c_void_p), ("dpc_h_in", ctypes.c_void_p),
     ]
 
 
@@ -99,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_last_error.restype = ctypes.c_char_p
         L.gdr_abi_version.argtypes = []
         L.gdr_abi_version.restype = ctypes.c_int
-        if L.gdr_abi_version() != 3:
+        if L.gdr_abi_version() != 4:
             raise ImportError("libgdr ABI version mismatch")
         _LIB = L
     return _LIB
@@ -307,13 +307,16 @@ def gdr_recurrent_step(q, k, v, state, *, beta=None, log_alpha=None, erase=None,
 
 
 def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, write=None,
-                  write_key=None, state_in=None, d_state_out=None, want_dstate_in: bool = True,
+                  write_key=None, precond: bool = False, pc_h_in=None, pc_rho: float = 0.99,
+                  pc_eps: float = 1e-3, pc_h0: float = 1.0, pc_t0: int = 0,
+                  state_in=None, d_state_out=None, want_dstate_in: bool = True,
                   chunk: int = 64, scale: float = 1.0, workspace=None, stream=None) -> dict:
     """Gradients through ``gdr_chunk_fwd`` on torch tensors.  ``d_out`` [B, T, H, Dv] (io dtype)
     and ``d_state_out`` [B, H, Dv, Dk] fp32 (or None) are the loss gradients of the forward's
     outputs.  Returns a dict of fp32 tensors: dq, dk, dv, and as the variant has them dbeta |
-    derase, dwrite, dlog_alpha, dwrite_key, and dstate_in (if ``want_dstate_in``).  The
-    workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is allocated when not given."""
+    derase, dwrite, dlog_alpha, dwrite_key, dpc_h_in (``precond``), and dstate_in (if
+    ``want_dstate_in``).  The workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is
+    allocated when not given."""
     torch = _torch()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -333,12 +336,16 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
     _check("write_key", write_key, (B, T, H, Dk), io, dev)
     _check("state_in", state_in, (B, H, Dv, Dk), f32, dev)
     _check("d_state_out", d_state_out, (B, H, Dv, Dk), f32, dev)
+    if precond:
+        _check("pc_h_in", pc_h_in, (B, H, Dk), f32, dev)
     desc = make_desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, io_dtype=_io_code(io),
                      gain=GDR_GAIN_CHANNEL if erase is not None else GDR_GAIN_SCALAR,
                      decay=(GDR_DECAY_CHANNEL if chd else
                             GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE),
-                     wkey=GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME,
-                     scale=scale, impl=GDR_IMPL_GENERIC)
+                     wkey=(GDR_WKEY_DIAG_PRECOND if precond else
+                           GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME),
+                     scale=scale, impl=GDR_IMPL_GENERIC,
+                     pc_rho=pc_rho, pc_eps=pc_eps, pc_h0=pc_h0, pc_t0=pc_t0)
 
     def new(shape):
         return torch.empty(shape, dtype=f32, device=dev)
@@ -355,6 +362,8 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
         g["dwrite_key"] = new((B, T, H, Dk))
     if want_dstate_in:
         g["dstate_in"] = new((B, H, Dv, Dk))
+    if precond:
+        g["dpc_h_in"] = new((B, H, Dk))
     nbytes = gdr_chunk_bwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -362,7 +371,7 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {nbytes}")
     grads = gdr_grads_t(*[_ptr(g.get(name)) for name, _ in gdr_grads_t._fields_])
     ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
-                       _ptr(write_key), None, None)
+                       _ptr(write_key), _ptr(pc_h_in) if precond else None, None)
     st = lib().gdr_chunk_bwd(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(d_out),
                              _ptr(d_state_out), ctypes.byref(grads), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream, dev))

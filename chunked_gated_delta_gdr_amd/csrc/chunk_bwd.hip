@@ -71,6 +71,13 @@ __device__ __forceinline__ float chunk_log_alpha(const ChunkArgs &f, long long r
   return (f.decay == GDR_DECAY_SCALAR && lane < n) ? f.log_alpha[row0 + static_cast<long long>(lane) * f.H] : 0.f;
 }
 
+// the write key at offset o (token row, channel) of the chunk whose first element is row0k:
+// the formed preconditioned key (fp32) when there is one, else k or the explicit write key
+template <typename IO>
+__device__ __forceinline__ float ld_wkey(const BwdArgs &a, const IO *rbase, long long row0k, long long o) {
+  return a.Rk != nullptr ? a.Rk[row0k + o] : ld_f(rbase + row0k, o);
+}
+
 // sum over k < K of A[i][k] B[k][j] for the lane's row i (row pointer ra) and column j (row
 // pointer rb of B^T), both with k contiguous in LDS: the K order is permuted so that sub-step
 // u of block s takes k = s + 4 kq + u, and each lane reads its 4 k with one 16-byte read per
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   {   // E, R, Q (CHD: log alpha): all loads first (clamped), then the masked stores
     float xk[kLoadIt], xg[kLoadIt], xr[kLoadIt], xq[kLoadIt];
     const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
-    const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
+    const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
     const float *bc = f.beta + row0;
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
       const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
       xk[it] = ld_f(kc, o);
       xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-      xr[it] = ld_f(rsrc, o);
+      xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
       xq[it] = CHD ? f.log_alpha[row0 * Dk + o] : ld_f(qc, o);
     }
 #pragma unroll
@@ -352,8 +359,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   const int tb = wave & 3, rb = wave >> 2;
 
   __shared__ __align__(16) float Ws[kCMax][LD];   // W of the chunk
-  using RT = std::conditional_t<CHD, float, IO>;
-  __shared__ __align__(16) RT Rs[kCMax][LD];      // write keys (io type: exact; CHD: decayed, fp32)
+  __shared__ __align__(16) float Rs[kCMax][LD];   // write keys (CHD: decayed)
   __shared__ __align__(16) float Ss[kBV][LD];     // mirror of the state
   __shared__ __align__(16) float Dl[kCMax][kBV];  // e^{g_n - g} D
   __shared__ __align__(16) float Us[kCMax][kBV];  // U
@@ -380,8 +386,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     Ss[r][c] = s;
   }
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
-  float pw[kLoadIt], pu[kUIt];
-  IO pr[kLoadIt];
+  float pw[kLoadIt], pu[kUIt], pr[kLoadIt];
   float pg[CHD ? kLoadIt : 1], pgn = 0.f;   // CHD: G of the staged elements, G_n of the thread's channel
   // loads of chunk ci into registers (indices clamped into the chunk)
   auto cload = [&](int ci) {
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
       pw[it] = Wc[static_cast<long long>(t) * Dk + c];
-      pr[it] = rbase[(row0 + static_cast<long long>(t) * H) * Dk + c];
+      pr[it] = ld_wkey(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c);
     }
     if constexpr (CHD) {
       // (kThreads is a multiple of DK: the thread's channel is the same in every item)
@@ -435,9 +440,9 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       const bool in = t < n && c < Dk;
       Ws[t][c] = in ? pw[it] : 0.f;
       if constexpr (CHD)
-        Rs[t][c] = in ? ld_f(pr, it) * exp2f(pgn - pg[it]) : 0.f;
+        Rs[t][c] = in ? pr[it] * exp2f(pgn - pg[it]) : 0.f;
       else
-        Rs[t][c] = in ? pr[it] : IO(0);
+        Rs[t][c] = in ? pr[it] : 0.f;
     }
     if constexpr (CHD) {
       if (tid < DK) gcn[tid] = exp2f(pgn);
@@ -473,8 +478,8 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
         float4v acc = Sacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
         // (rows past n of Dl are zero, and n + 7 < 64 + 8: the pairs stay inside the tiles)
         for (int t0 = 0; t0 < n; t0 += 8) {
-          acc = mfma4(Dl[t0 + kq][16 * rbs + col], ld_f(&Rs[t0 + kq][16 * cbs + col], 0), acc);
-          acc2 = mfma4(Dl[t0 + 4 + kq][16 * rbs + col], ld_f(&Rs[t0 + 4 + kq][16 * cbs + col], 0), acc2);
+          acc = mfma4(Dl[t0 + kq][16 * rbs + col], Rs[t0 + kq][16 * cbs + col], acc);
+          acc2 = mfma4(Dl[t0 + 4 + kq][16 * rbs + col], Rs[t0 + 4 + kq][16 * cbs + col], acc2);
         }
         acc += acc2;
         Sacc[m] = acc;
@@ -570,13 +575,13 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     const int c0 = ci * C, n = min(C, T - c0);
     const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
     if (tid < kCMax) xla = chunk_log_alpha(f, row0, n, tid);
-    const IO *rsrc = rbase + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
+    const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
     const float *bc = f.beta + row0;
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
       const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-      xr[it] = ld_f(rsrc, o);
+      xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
       xk[it] = ld_f(kc, o);
       xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
     }
@@ -932,7 +937,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
     const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
-    const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
+    const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
     const float *bc = f.beta + row0;
     const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
     float pk[4] = {0.f, 0.f, 0.f, 0.f};   // k . dE over the lane's channels (scalar gain)
@@ -946,7 +951,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           xq[it] = ld_f(qc, o);
           xk[it] = ld_f(kc, o);
           xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-          xr[it] = ld_f(rsrc, o);
+          xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
           xG[it] = Gc[static_cast<long long>(tc) * Dk + cc];   // (flat past n)
         }
         __syncthreads();   // the previous half's tiles are consumed
@@ -1091,7 +1096,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
             dkv = ld_f(er, rowk + c) * de;
             a.derase[rowk + c] = ld_f(k, rowk + c) * de;
           }
-          if (f.wkey == GDR_WKEY_EXPLICIT)
+          if (f.wkey != GDR_WKEY_SAME)   // (preconditioned: to the workspace, then through p_t)
             a.dwk[rowk + c] = dr;
           else
             dkv += dr;
@@ -1117,7 +1122,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     {   // Q, E, R: all loads first (clamped), then the masked LDS stores
       float xq[kLoadIt], xk[kLoadIt], xg[kLoadIt], xr[kLoadIt];
       const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
-      const IO *rsrc = ((f.wkey == GDR_WKEY_EXPLICIT) ? wk : k) + row0 * Dk;
+      const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
       const float *bc = f.beta + row0;
   #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
@@ -1126,7 +1131,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         xq[it] = ld_f(qc, o);
         xk[it] = ld_f(kc, o);
         xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-        xr[it] = ld_f(rsrc, o);
+        xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
       }
   #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
@@ -1276,7 +1281,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           dkv = ld_f(er, rowk + c) * de;
           a.derase[rowk + c] = ld_f(k, rowk + c) * de;
         }
-        if (f.wkey == GDR_WKEY_EXPLICIT)
+        if (f.wkey != GDR_WKEY_SAME)   // (preconditioned: to the workspace, then through p_t)
           a.dwk[rowk + c] = dr;
         else
           dkv += dr;
@@ -1284,6 +1289,82 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Preconditioned write key (diagonal second-moment preconditioner, Preconditioned DeltaNet
+// section 2b): per (batch, head, channel) a scan over the whole sequence.  Forward: the
+// accumulator h_t = rho h_{t-1} + k_t^2 from pc_h_in (or pc_h0), p_t = 1 / (h_t / b_t + eps)
+// with b_t = 1 - rho^(pc_t0 + t + 1), the write key r_t = k_t p_t; r and p to the workspace.
+// Backward: with dr_t the write-key gradient of the kernels above, the accumulator's gradient
+// H_t = -(dr_t k_t p_t^2) / b_t + rho H_{t+1} (H past the end zero: the final accumulator is
+// not in the loss), dk_t += dr_t p_t + 2 k_t H_t, and dL/dpc_h_in = rho H_1.  One thread per
+// channel; the loads of 8 tokens are issued ahead of their steps.
+// ---------------------------------------------------------------------------------------
+constexpr int kPcThreads = 64;
+constexpr int kPcU = 8;
+
+template <typename IO>
+__global__ __launch_bounds__(kPcThreads) void bwd_pc_keys_kernel(BwdArgs a) {
+  const ChunkArgs &f = a.f;
+  const IO *__restrict__ k = static_cast<const IO *>(f.k);
+  const int c = blockIdx.x * kPcThreads + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T;
+  if (c >= Dk) return;
+  const long long sh = static_cast<long long>(b) * H + h;
+  float acc = f.pc_h_in != nullptr ? f.pc_h_in[sh * Dk + c] : f.h0;
+  for (int t0 = 0; t0 < T; t0 += kPcU) {
+    float kv[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = min(t0 + u, T - 1);
+      kv[u] = ld_f(k, ((static_cast<long long>(b) * T + t) * H + h) * Dk + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = t0 + u;
+      if (t >= T) break;
+      acc = fmaf(f.rho, acc, kv[u] * kv[u]);
+      const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
+      const float p = 1.f / (acc / bt + f.eps);
+      const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
+      a.Pk[o] = p;
+      a.Rk[o] = kv[u] * p;
+    }
+  }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(kPcThreads) void bwd_pc_grad_kernel(BwdArgs a) {
+  const ChunkArgs &f = a.f;
+  const IO *__restrict__ k = static_cast<const IO *>(f.k);
+  const int c = blockIdx.x * kPcThreads + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T;
+  if (c >= Dk) return;
+  const long long sh = static_cast<long long>(b) * H + h;
+  float Hs = 0.f;
+  for (int t1 = T; t1 > 0; t1 -= kPcU) {   // tokens t1 - kPcU .. t1 - 1, last first
+    float kv[kPcU], pv[kPcU], gv[kPcU], dk0[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = max(t1 - 1 - u, 0);
+      const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
+      kv[u] = ld_f(k, o);
+      pv[u] = a.Pk[o];
+      gv[u] = a.dRk[o];
+      dk0[u] = a.dk[o];
+    }
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = t1 - 1 - u;
+      if (t < 0) break;
+      const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
+      Hs = fmaf(f.rho, Hs, -(gv[u] * kv[u] * pv[u] * pv[u]) / bt);
+      const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
+      a.dk[o] = dk0[u] + gv[u] * pv[u] + 2.f * kv[u] * Hs;
+    }
+  }
+  if (a.dpc_h_in != nullptr) a.dpc_h_in[sh * Dk + c] = f.rho * Hs;
 }
 
 template <typename IO>
@@ -1378,6 +1459,24 @@ hipError_t launch_bwd_sweep(const BwdArgs &a, int io_dtype, hipStream_t s) {
 
 hipError_t launch_bwd_chunk(const BwdArgs &a, int io_dtype, hipStream_t s) {
   return io_dtype == GDR_BF16 ? chunk_io<uint16_t>(a, s) : chunk_io<float>(a, s);
+}
+
+hipError_t launch_bwd_pc_keys(const BwdArgs &a, int io_dtype, hipStream_t s) {
+  const dim3 grid((a.f.Dk + kPcThreads - 1) / kPcThreads, a.f.H, a.f.B);
+  if (io_dtype == GDR_BF16)
+    hipLaunchKernelGGL((bwd_pc_keys_kernel<uint16_t>), grid, dim3(kPcThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_pc_keys_kernel<float>), grid, dim3(kPcThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pc_grad(const BwdArgs &a, int io_dtype, hipStream_t s) {
+  const dim3 grid((a.f.Dk + kPcThreads - 1) / kPcThreads, a.f.H, a.f.B);
+  if (io_dtype == GDR_BF16)
+    hipLaunchKernelGGL((bwd_pc_grad_kernel<uint16_t>), grid, dim3(kPcThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_pc_grad_kernel<float>), grid, dim3(kPcThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace gdr

@@ -37,6 +37,10 @@ struct BwdArgs {
   // [B,T,H,Dv], T and P [B,H,NC,C,C], W [B,H,NC,C,Dk], U [B,T,H,Dv]; with per-channel decay
   // also G [B,H,NC,C,Dk], the in-chunk cumulative log2 decay (null otherwise)
   float *h, *dh, *D, *dX, *Tw, *Pw, *Ww, *Uw, *Gw;
+  // preconditioned write key: the write keys r = k (.) p and p [B,T,H,Dk] (formed before the
+  // other kernels; the kernels read the write key from Rk whenever it is set), the write-key
+  // gradients dR [B,T,H,Dk] (null otherwise); dL/dpc_h_in [B,H,Dk] or null
+  float *Rk, *Pk, *dRk, *dpc_h_in;
   int NC;   // chunks per stream
 };
 
@@ -49,6 +53,8 @@ hipError_t launch_step(const ChunkArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_prep_state(const BwdArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int io_dtype, hipStream_t s);
+hipError_t launch_bwd_pc_keys(const BwdArgs &a, int io_dtype, hipStream_t s);
+hipError_t launch_bwd_pc_grad(const BwdArgs &a, int io_dtype, hipStream_t s);
 
 // ---------------------------------------------------------------------------------
 // Device helpers: storage conversions.  bf16 is stored as uint16_t bit patterns.

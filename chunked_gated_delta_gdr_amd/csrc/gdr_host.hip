@@ -56,7 +56,7 @@ constexpr long double kMaxElems = 1099511627776.0L;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
-  uint64_t h, dh, D, dX, T, P, W, U, G, total;
+  uint64_t h, dh, D, dX, T, P, W, U, G, R, Pk, dR, total;
   int NC;
 };
 
@@ -75,7 +75,11 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   L.W = L.P + cc;
   L.U = L.W + al(B * H * NC * C * Dk * 4u);
   L.G = L.U + tk;
-  L.total = L.G + (d.decay == GDR_DECAY_CHANNEL ? al(B * H * NC * C * Dk * 4u) : 0u);
+  L.R = L.G + (d.decay == GDR_DECAY_CHANNEL ? al(B * H * NC * C * Dk * 4u) : 0u);
+  const uint64_t kk = d.wkey == GDR_WKEY_DIAG_PRECOND ? al(B * T * H * Dk * 4u) : 0u;
+  L.Pk = L.R + kk;
+  L.dR = L.Pk + kk;
+  L.total = L.dR + kk;
   L.NC = static_cast<int>(NC);
   return L;
 }
@@ -275,7 +279,10 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   gdr_status_t st = gdr_validate(d, in, state_in, d_out, nullptr, 0);
   if (st != GDR_OK) return fail(st, "forward arguments (d_out checked as out): %s", g_last_error.c_str());
   if (g == nullptr) return fail(GDR_EINVAL, "grads must be non-NULL");
-  if (d->wkey == GDR_WKEY_DIAG_PRECOND) return fail(GDR_ENOTSUP, "backward of the preconditioned write key");
+  if (in->pc_h_out != nullptr) return fail(GDR_EINVAL, "pc_h_out must be NULL (the backward does not write it)");
+  if (g->dpc_h_in != nullptr && d->wkey != GDR_WKEY_DIAG_PRECOND)
+    return fail(GDR_EINVAL, "grads->dpc_h_in given without wkey DIAG_PRECOND");
+  if ((reinterpret_cast<uintptr_t>(g->dpc_h_in) & 3u) != 0) return fail(GDR_EINVAL, "grads->dpc_h_in misaligned");
   if (d->neumann_order >= 0) return fail(GDR_ENOTSUP, "backward of the band-limited T (exact T only)");
   const bool need = d->T > 0;
   struct Opt {
@@ -318,11 +325,12 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
       rng("erase", in->erase, ntok * Dk * esz),
       rng("write", in->write, ntok * Dv * esz), rng("write_key", in->write_key, ntok * Dk * esz),
       rng("state_in", state_in, B * H * Dv * Dk * 4), rng("d_out", d_out, ntok * Dv * esz),
-      rng("d_state_out", d_state_out, B * H * Dv * Dk * 4)};
-  Range written[10];
+      rng("d_state_out", d_state_out, B * H * Dv * Dk * 4), rng("pc_h_in", in->pc_h_in, B * H * Dk * 4)};
+  Range written[11];
   int nw = 0;
   for (const Opt &o : outs) written[nw++] = rng(o.name, o.p, o.elems * 4);
   written[nw++] = rng("dstate_in", g->dstate_in, B * H * Dv * Dk * 4);
+  written[nw++] = rng("dpc_h_in", g->dpc_h_in, B * H * Dk * 4);
   written[nw++] = rng("workspace", ws, static_cast<long double>(need_ws));
   for (int i = 0; i < nw; ++i) {
     for (const Range &r : inputs)
@@ -353,24 +361,36 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
     b.Ww = reinterpret_cast<float *>(ws + L.W);
     b.Uw = reinterpret_cast<float *>(ws + L.U);
     b.Gw = d->decay == GDR_DECAY_CHANNEL ? reinterpret_cast<float *>(ws + L.G) : nullptr;
+    if (d->wkey == GDR_WKEY_DIAG_PRECOND) {
+      b.Rk = reinterpret_cast<float *>(ws + L.R);
+      b.Pk = reinterpret_cast<float *>(ws + L.Pk);
+      b.dRk = reinterpret_cast<float *>(ws + L.dR);
+    }
   }
   b.dout = d_out;
   b.dstate_out = d_state_out;
   b.dq = g->dq; b.dk = g->dk; b.dv = g->dv; b.dbeta = g->dbeta;
   b.derase = g->derase; b.dwrite = g->dwrite; b.dla = g->dlog_alpha; b.dwk = g->dwrite_key;
   b.dstate_in = g->dstate_in;
+  const bool pc = d->wkey == GDR_WKEY_DIAG_PRECOND;
+  if (pc) b.dwk = b.dRk;   // the write-key gradients go to the workspace, then through p_t
+  b.dpc_h_in = g->dpc_h_in;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled())
     std::fprintf(stderr, "[gdr] chunk_bwd B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d ws=%llu\n",
                  d->B, d->T, d->H, d->Dk, d->Dv, d->chunk, d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain,
                  d->decay, d->wkey, static_cast<unsigned long long>(L.total));
   hipError_t e = hipSuccess;
-  if (d->T > 0)   // 1. forward recompute: T, P, W, U of every chunk, then D and the chunk states
+  if (pc && d->T > 0)   // 0. the preconditioned write keys
+    e = gdr::launch_bwd_pc_keys(b, d->io_dtype, s);
+  if (e == hipSuccess && d->T > 0)   // 1. forward recompute: T, P, W, U of every chunk, then D and the chunk states
     e = gdr::launch_bwd_prep_state(b, d->io_dtype, s);
   if (e == hipSuccess && (d->T > 0 || g->dstate_in != nullptr))   // 2. reverse sweep
     e = gdr::launch_bwd_sweep(b, d->io_dtype, s);
   if (e == hipSuccess && d->T > 0)   // 3. per-chunk gradients
     e = gdr::launch_bwd_chunk(b, d->io_dtype, s);
+  if (e == hipSuccess && pc && (d->T > 0 || g->dpc_h_in != nullptr))   // 4. through the preconditioner
+    e = gdr::launch_bwd_pc_grad(b, d->io_dtype, s);
   if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

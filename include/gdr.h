@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum {
   GDR_OK = 0,
@@ -177,6 +177,8 @@ typedef struct gdr_grads {
   float *dlog_alpha;  /* [B,T,H] if decay == SCALAR, [B,T,H,Dk] if CHANNEL, else NULL       */
   float *dwrite_key;  /* [B,T,H,Dk]; iff wkey == EXPLICIT, else NULL                       */
   float *dstate_in;   /* [B,H,Dv,Dk] or NULL (not written)                                 */
+  float *dpc_h_in;    /* [B,H,Dk] dL/dpc_h_in (every entry, also when pc_h_in is NULL: the
+                         gradient of the pc_h0 start); wkey DIAG_PRECOND only, or NULL      */
 } gdr_grads_t;
 
 /*
@@ -199,9 +201,16 @@ typedef struct gdr_grads {
  * elementwise, e^{g_C} dS scales the state's columns, the pairwise decay sits inside the
  * products over channels (L, P) and over tokens (dQ, dE, dR), and the gate gradient is one
  * per token and channel.
+ * With the preconditioned write key (DIAG_PRECOND) two more launches bracket these: a scan
+ * per channel that forms the write keys r_t = k_t (.) p_t (fp32) before, and after, the chain
+ * rule through p_t: the accumulator's gradient H_t = -(dr_t k_t p_t^2) / b_t + rho H_{t+1}
+ * (reverse scan per channel, the final accumulator outside the loss) adds
+ * dr_t (.) p_t + 2 k_t (.) H_t to dk and gives dL/dpc_h_in = rho H_1.  The final
+ * accumulator (pc_h_out) is not written.
  * All arithmetic is fp32 (inputs in io_dtype are widened once).
  *
- * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR | CHANNEL, wkey SAME | EXPLICIT, exact T
+ * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR | CHANNEL, wkey SAME | EXPLICIT |
+ * DIAG_PRECOND, exact T
  * (neumann_order < 0), chunk 16 | 32 | 64, Dk <= 128, Dv <= 512, io fp32 | bf16; anything
  * else returns GDR_ENOTSUP (desc->impl is ignored).
  *
@@ -223,7 +232,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
  * T == 0): the chunk-start states and their gradients (2 B H ceil(T/C) Dv Dk floats), D,
  * dX and U (3 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats) and W
  * (B H ceil(T/C) C Dk floats), with decay CHANNEL also the cumulative decays G
- * (B H ceil(T/C) C Dk floats), each section 256-byte aligned.  No HIP call. */
+ * (B H ceil(T/C) C Dk floats), with wkey DIAG_PRECOND also the write keys, p_t and the
+ * write-key gradients (3 B T H Dk floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 
 /* gdr_chunk_bwd's argument check on its own (no HIP call). */

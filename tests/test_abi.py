@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert G.gdr_abi_version() == 3
+    assert G.gdr_abi_version() == 4
     for s in (G.GDR_OK, G.GDR_EINVAL, G.GDR_ENOTSUP, G.GDR_EHIP):
         assert G.gdr_status_str(s).startswith("GDR_")
     assert "UNKNOWN" in G.gdr_status_str(42)
@@ -41,7 +41,7 @@ def test_struct_layout_matches_header():
     # uint32 + 13 int32 + 4 float = 72 bytes, then the int64: 80
     assert ctypes.sizeof(G.gdr_desc_t) == 80
     assert ctypes.sizeof(G.gdr_inputs_t) == 10 * 8
-    assert ctypes.sizeof(G.gdr_grads_t) == 9 * 8
+    assert ctypes.sizeof(G.gdr_grads_t) == 10 * 8
 
 
 def desc(**kw):
@@ -217,16 +217,20 @@ def _al(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("decay", [G.GDR_DECAY_SCALAR, G.GDR_DECAY_CHANNEL])
+@pytest.mark.parametrize("decay,wkey", [(G.GDR_DECAY_SCALAR, G.GDR_WKEY_SAME),
+                                        (G.GDR_DECAY_CHANNEL, G.GDR_WKEY_SAME),
+                                        (G.GDR_DECAY_CHANNEL, G.GDR_WKEY_DIAG_PRECOND)])
 @pytest.mark.parametrize("T,C", [(100, 64), (64, 64), (1, 16), (4096, 32), (0, 64)])
-def test_bwd_workspace_size_formula(T, C, decay):
-    d = desc(T=T, chunk=C, decay=decay)
+def test_bwd_workspace_size_formula(T, C, decay, wkey):
+    d = desc(T=T, chunk=C, decay=decay, wkey=wkey)
     B, H, Dk, Dv = 2, 3, 64, 32
     NC = (T + C - 1) // C
     want = (2 * _al(B * H * NC * Dv * Dk * 4) + 3 * _al(B * T * H * Dv * 4) + 2 * _al(B * H * NC * C * C * 4)
             + _al(B * H * NC * C * Dk * 4))
     if decay == G.GDR_DECAY_CHANNEL:   # the cumulative decays G
         want += _al(B * H * NC * C * Dk * 4)
+    if wkey == G.GDR_WKEY_DIAG_PRECOND:   # write keys, p_t, write-key gradients
+        want += 3 * _al(B * T * H * Dk * 4)
     assert G.gdr_chunk_bwd_workspace_size(d) == want
     assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
 
@@ -268,13 +272,13 @@ def call_validate_bwd(d, **over):
 
 @pytest.mark.parametrize("gain", [G.GDR_GAIN_SCALAR, G.GDR_GAIN_CHANNEL])
 @pytest.mark.parametrize("decay", [G.GDR_DECAY_NONE, G.GDR_DECAY_SCALAR, G.GDR_DECAY_CHANNEL])
-@pytest.mark.parametrize("wkey", [G.GDR_WKEY_SAME, G.GDR_WKEY_EXPLICIT])
+@pytest.mark.parametrize("wkey", [G.GDR_WKEY_SAME, G.GDR_WKEY_EXPLICIT, G.GDR_WKEY_DIAG_PRECOND])
 def test_bwd_accepts_supported_variants(gain, decay, wkey):
     d = desc(gain=gain, decay=decay, wkey=wkey)
     assert call_validate_bwd(d) == G.GDR_OK, G.gdr_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(wkey=G.GDR_WKEY_DIAG_PRECOND), dict(neumann_order=3)])
+@pytest.mark.parametrize("kw", [dict(neumann_order=3), dict(neumann_order=3, residual_steps=2)])
 def test_bwd_rejects_unsupported_variants(kw):
     d = desc(**kw)
     ins, gr, a = bwd_args(d)
@@ -324,3 +328,16 @@ def test_bwd_entry_point_rejects_before_launch():
     st = G.lib().gdr_chunk_bwd(ctypes.byref(d), ctypes.byref(ins), None, a["d_out"], None, ctypes.byref(gr),
                                a["workspace"], a["workspace_bytes"], None)
     assert st == G.GDR_EINVAL
+
+
+def test_bwd_preconditioner_arguments():
+    d = desc(wkey=G.GDR_WKEY_DIAG_PRECOND, decay=G.GDR_DECAY_SCALAR)
+    assert call_validate_bwd(d) == G.GDR_OK, G.gdr_last_error()
+    assert call_validate_bwd(d, ins=dict(pc_h_in=BASE + 31 * MB), grads=dict(dpc_h_in=BASE + 32 * MB)) == G.GDR_OK
+    # the backward does not write the final accumulator
+    assert call_validate_bwd(d, ins=dict(pc_h_out=BASE + 31 * MB)) == G.GDR_EINVAL
+    # dL/dpc_h_in exists only with the preconditioner, and must not overlap an input
+    assert call_validate_bwd(desc(), grads=dict(dpc_h_in=BASE + 32 * MB)) == G.GDR_EINVAL
+    assert call_validate_bwd(d, ins=dict(pc_h_in=BASE + 31 * MB), grads=dict(dpc_h_in=BASE + 31 * MB)) == G.GDR_EINVAL
+    assert "overlaps" in G.gdr_last_error()
+    assert call_validate_bwd(d, grads=dict(dpc_h_in=BASE + 32 * MB + 2)) == G.GDR_EINVAL

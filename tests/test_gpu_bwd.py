@@ -13,7 +13,8 @@ from _gpu_util import TOL_F32, dev, host, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
-GRAD_NAMES = ["dq", "dk", "dv", "dbeta", "derase", "dwrite", "dlog_alpha", "dwrite_key", "dstate_in"]
+GRAD_NAMES = ["dq", "dk", "dv", "dbeta", "derase", "dwrite", "dlog_alpha", "dwrite_key", "dstate_in",
+              "dpc_h_in"]
 
 
 def announce(msg):
@@ -22,7 +23,8 @@ def announce(msg):
 
 def spec(variant, **kw):
     base = {"plain": "plain", "gdn": "gdn", "gdn2": "gdn2", "explicit": "gdn",
-            "gdn2_decay": "gdn2", "kda": "kda", "kda_gdn2": "kda", "kda_explicit": "kda"}[variant]
+            "gdn2_decay": "gdn2", "kda": "kda", "kda_gdn2": "kda", "kda_explicit": "kda",
+            "pdn": "pdn", "pdn_decay": "gdn", "pdn_kda": "kda", "pdn_gdn2": "gdn2"}[variant]
     over = dict(B=2, H=2, T=200, Dk=64, Dv=48, dtype="f32", seed=21)
     over.update(kw)
     if variant in ("explicit", "kda_explicit"):
@@ -31,30 +33,39 @@ def spec(variant, **kw):
         over["decay"] = "scalar"
     if variant == "kda_gdn2":
         over["gain"] = "channel"
+    if variant.startswith("pdn"):
+        over["wkey"] = "precond"
     return gs.spec(base, **over)
 
 
-def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None):
+def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None, pre=None):
     import torch
     import chunked_gated_delta_gdr_amd as G
     io = torch_dtype(s.dtype)
     f32 = torch.float32
+    pk = {}
+    if pre is not None:
+        pk = dict(precond=True, pc_h_in=dev(pre.get("h_init"), f32), pc_rho=pre["rho"], pc_eps=pre["eps"],
+                  pc_h0=pre.get("h0", 1.0), pc_t0=pre["t0"])
     g = G.gdr_chunk_bwd(
         dev(x["q"], io), dev(x["k"], io), dev(x["v"], io), dev(cot["d_out"], io),
         beta=dev(x.get("beta"), f32), log_alpha=dev(x.get("log_alpha"), f32),
         erase=dev(x.get("erase"), io), write=dev(x.get("write"), io),
         write_key=dev(x.get("write_key"), io), state_in=dev(state_in, f32),
         d_state_out=dev(cot["d_state_out"], f32) if d_state_out else None,
-        chunk=chunk or s.chunk, scale=scale)
+        chunk=chunk or s.chunk, scale=scale, **pk)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in g.items()}
 
 
 def oracle_grads(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, streams=None,
-                 checkpoint=0):
+                 checkpoint=0, pre=None):
     g = O.recurrent_grad(x, cot["d_out"], cot["d_state_out"] if d_state_out else None,
-                         scale=scale, state0=state_in, streams=streams, checkpoint=checkpoint)
+                         scale=scale, state0=state_in, streams=streams, checkpoint=checkpoint,
+                         precond=pre)
     g["dstate_in"] = g.pop("dS0")
+    if "dpc_h_init" in g:
+        g["dpc_h_in"] = g.pop("dpc_h_init")
     return g
 
 
@@ -65,7 +76,7 @@ def compare(got, ref, streams=None, tol=TOL_F32):
             continue
         a, b = got[name], ref[name]
         if streams is not None:
-            if name == "dstate_in":
+            if name in ("dstate_in", "dpc_h_in"):
                 a = np.stack([a[bb, hh] for bb, hh in streams])
                 b = np.stack([b[bb, hh] for bb, hh in streams])
             else:
@@ -222,4 +233,66 @@ def test_bwd_full_size_kda_sampled():
     for name, val in got.items():
         assert np.all(np.isfinite(val)), name
     ref = oracle_grads(s, x, cot, state_in=S0, streams=streams, checkpoint=64)
+    compare(got, ref, streams=streams)
+
+
+def precond_args(s, given=False, seed=9):
+    """The workload's preconditioner, or (given) a random accumulator and a later start."""
+    if not given:
+        return dict(rho=s.pc_rho, eps=s.pc_eps, h0=s.pc_h0, t0=0)
+    rng = np.random.default_rng(seed)
+    h_init = rng.uniform(0.002, 0.02, (s.B, s.H, s.Dk)).astype(np.float32)
+    return dict(rho=0.95, eps=1e-2, h_init=h_init, t0=37)
+
+
+@pytest.mark.parametrize("given", [False, True])
+@pytest.mark.parametrize("variant", ["pdn", "pdn_decay", "pdn_kda", "pdn_gdn2"])
+def test_bwd_precond_fp32(variant, given):
+    s = spec(variant)
+    pre = precond_args(s, given)
+    announce(f"bwd {variant} f32 precond {'given accumulator' if given else 'h0'} {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    got = run_bwd(s, x, cot, state_in=S0, scale=0.8, pre=pre)
+    compare(got, oracle_grads(s, x, cot, state_in=S0, scale=0.8, pre=pre))
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 64), (37, 16), (65, 32), (130, 64)])
+def test_bwd_precond_lengths(T, chunk):
+    s = spec("pdn_decay", T=T, chunk=chunk)
+    pre = precond_args(s, True)
+    announce(f"bwd pdn_decay f32 T={T} chunk {chunk}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0, pre=pre), oracle_grads(s, x, cot, state_in=S0, pre=pre))
+
+
+def test_bwd_precond_bf16():
+    s = spec("pdn", dtype="bf16", Dk=128, Dv=128, T=200)
+    pre = precond_args(s)
+    announce(f"bwd pdn bf16 {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0, pre=pre), oracle_grads(s, x, cot, state_in=S0, pre=pre))
+
+
+def test_bwd_precond_empty_sequence():
+    """T = 0: dL/dpc_h_in is zero (the accumulator reaches no output)."""
+    s = spec("pdn", T=0)
+    announce("bwd pdn f32 T=0")
+    x, cot = gs.make_inputs(s), gs.make_cotangents(s)
+    got = run_bwd(s, x, cot, state_in=state(s), pre=precond_args(s, True))
+    np.testing.assert_array_equal(got["dpc_h_in"], 0.0)
+    np.testing.assert_array_equal(got["dstate_in"], cot["d_state_out"])
+
+
+def test_bwd_full_size_pdn_sampled():
+    """The pdn workload at full size (B4 H16 T4096 d128 bf16, preconditioned write key): two
+    streams against the oracle (checkpointed reverse sweep), every gradient finite everywhere."""
+    s = gs.spec("pdn")
+    pre = precond_args(s)
+    streams = [(0, 0), (3, 15)]
+    announce(f"bwd pdn full size {s}, streams {streams}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s, amp=0.1)
+    got = run_bwd(s, x, cot, state_in=S0, pre=pre)
+    for name, val in got.items():
+        assert np.all(np.isfinite(val)), name
+    ref = oracle_grads(s, x, cot, state_in=S0, streams=streams, checkpoint=64, pre=pre)
     compare(got, ref, streams=streams)
