@@ -7,7 +7,7 @@ Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s 1.0] [--workload gdn|gdn2|pdn|long|plain|kda|decode]
                     [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
-    python bench.py --bwd [--workload gdn|gdn2|plain|kda]   # gdr_chunk_bwd instead
+    python bench.py --bwd [--workload gdn|gdn2|plain|kda|pdn]   # gdr_chunk_bwd instead
 
 Counter helpers (used to produce the committed traffic summaries under profiles/):
     python bench.py --copy-probe-mb 256          # calibration copy of known size
@@ -342,9 +342,9 @@ def bench_backward(args):
     import gdr_synth as gs
 
     s = gs.spec(args.workload)
-    if s.wkey == "precond":
-        print(f"bench.py --bwd: the {args.workload} workload's variant has no backward here", file=sys.stderr)
-        sys.exit(2)
+    pc = s.wkey == "precond"
+    pre = dict(rho=s.pc_rho, eps=s.pc_eps, h0=s.pc_h0, t0=0) if pc else None
+    pcargs = dict(precond=True, pc_rho=s.pc_rho, pc_eps=s.pc_eps, pc_h0=s.pc_h0, pc_t0=0) if pc else {}
     x, cot = gs.make_inputs(s), gs.make_cotangents(s)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -360,7 +360,8 @@ def bench_backward(args):
     desc = G.make_desc(B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk, io_dtype=G.GDR_BF16 if
                        s.dtype == "bf16" else G.GDR_F32,
                        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
-                       decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE))
+                       decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
+                       wkey=G.GDR_WKEY_DIAG_PRECOND if pc else G.GDR_WKEY_SAME)
     ws = torch.empty(G.gdr_chunk_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] backward {args.workload}: workspace {ws.numel() / 2**20:.1f} MiB, steps {args.steps} "
@@ -369,7 +370,7 @@ def bench_backward(args):
     def step():
         return G.gdr_chunk_bwd(a["q"], a["k"], a["v"], dO, beta=a["beta"], log_alpha=a["log_alpha"],
                                erase=a["erase"], write=a["write"], write_key=a["write_key"], state_in=S0,
-                               d_state_out=dST, chunk=s.chunk, workspace=ws, stream=stream)
+                               d_state_out=dST, chunk=s.chunk, workspace=ws, stream=stream, **pcargs)
 
     for _ in range(args.warmup):
         g = step()
@@ -394,7 +395,7 @@ def bench_backward(args):
     parity = None
     if not args.no_parity:
         import oracle
-        ref = oracle.recurrent_grad(x, cot["d_out"], cot["d_state_out"], state0=s0, streams=[(0, 0)],
+        ref = oracle.recurrent_grad(x, cot["d_out"], cot["d_state_out"], state0=s0, streams=[(0, 0)], precond=pre,
                                     checkpoint=64)
         parity = {"stream": "(0,0)", "tokens": s.T}
         for name in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "derase", "dwrite"):
@@ -403,6 +404,9 @@ def bench_backward(args):
                                                          ref[name][0, :, 0])
         parity["rel_l2_dstate_in"] = oracle.rel_l2(g["dstate_in"][0, 0].double().cpu().numpy(),
                                                    ref["dS0"][0, 0])
+        if pc:
+            parity["rel_l2_dpc_h_in"] = oracle.rel_l2(g["dpc_h_in"][0, 0].double().cpu().numpy(),
+                                                      ref["dpc_h_init"][0, 0])
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -411,7 +415,7 @@ def bench_backward(args):
         w0 = time.perf_counter()
         reps = 0
         while time.perf_counter() - w0 < 10.0:
-            oracle.recurrent_grad(sub, cot["d_out"][:1, :n, :1], None)
+            oracle.recurrent_grad(sub, cot["d_out"][:1, :n, :1], None, precond=pre)
             reps += 1
         wall = time.perf_counter() - w0
         cpu = {"value": round(reps * n / wall / s.H, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",

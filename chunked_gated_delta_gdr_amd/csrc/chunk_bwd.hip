@@ -1293,37 +1293,76 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Preconditioned write key (diagonal second-moment preconditioner, Preconditioned DeltaNet
-// section 2b): per (batch, head, channel) a scan over the whole sequence.  Forward: the
-// accumulator h_t = rho h_{t-1} + k_t^2 from pc_h_in (or pc_h0), p_t = 1 / (h_t / b_t + eps)
-// with b_t = 1 - rho^(pc_t0 + t + 1), the write key r_t = k_t p_t; r and p to the workspace.
-// Backward: with dr_t the write-key gradient of the kernels above, the accumulator's gradient
-// H_t = -(dr_t k_t p_t^2) / b_t + rho H_{t+1} (H past the end zero: the final accumulator is
-// not in the loss), dk_t += dr_t p_t + 2 k_t H_t, and dL/dpc_h_in = rho H_1.  One thread per
-// channel; the loads of 8 tokens are issued ahead of their steps.
+// section 2b), per (batch, head, channel).  Forward: the accumulator h_t = rho h_{t-1} + k_t^2
+// from pc_h_in (or pc_h0), p_t = 1 / (h_t / b_t + eps) with b_t = 1 - rho^(pc_t0 + t + 1), the
+// write key r_t = k_t p_t; r and p go to the workspace.  Backward: with dr_t the write-key
+// gradient of the kernels above, the accumulator's gradient H_t = a_t + rho H_{t+1},
+// a_t = -(dr_t k_t p_t^2) / b_t (H past the end zero: the final accumulator is not in the
+// loss), dk_t += dr_t p_t + 2 k_t H_t, and dL/dpc_h_in = rho H_0.
+// Both recurrences are affine, so each runs as two parallel passes over the chunks (one
+// workgroup per (chunk, head, batch), one thread per channel): the first takes every chunk's
+// own sum from a zero start (the chunk's contribution to the accumulator at its end, or to H
+// at its start); the second composes the sums of the chunks before it (after it, for H) into
+// its start value, from loads all issued at once, and runs the chunk's tokens from there.
 // ---------------------------------------------------------------------------------------
-constexpr int kPcThreads = 64;
-constexpr int kPcU = 8;
+constexpr int kPcThreads = 128;   // channels (Dk <= 128)
+
+__global__ void bwd_zero_kernel(float *p, long long n) {
+  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+constexpr int kPcU = 16;          // tokens whose loads are issued together
+
+template <typename IO>
+__global__ __launch_bounds__(kPcThreads) void bwd_pc_keys_sum_kernel(BwdArgs a) {
+  const ChunkArgs &f = a.f;
+  const IO *__restrict__ k = static_cast<const IO *>(f.k);
+  const int c = threadIdx.x, ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T, C = f.C;
+  if (c >= Dk) return;
+  const int t0 = ci * C, n = min(C, T - t0);
+  float acc = 0.f;
+  for (int u0 = 0; u0 < n; u0 += kPcU) {
+    float kv[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u)
+      kv[u] = ld_f(k, ((static_cast<long long>(b) * T + t0 + min(u0 + u, n - 1)) * H + h) * Dk + c);
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u)
+      if (u0 + u < n) acc = fmaf(f.rho, acc, kv[u] * kv[u]);
+  }
+  a.Sg[((static_cast<long long>(b) * H + h) * a.NC + ci) * Dk + c] = acc;
+}
 
 template <typename IO>
 __global__ __launch_bounds__(kPcThreads) void bwd_pc_keys_kernel(BwdArgs a) {
   const ChunkArgs &f = a.f;
   const IO *__restrict__ k = static_cast<const IO *>(f.k);
-  const int c = blockIdx.x * kPcThreads + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int Dk = f.Dk, H = f.H, T = f.T;
+  const int c = threadIdx.x, ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T, C = f.C;
   if (c >= Dk) return;
   const long long sh = static_cast<long long>(b) * H + h;
+  const int t0 = ci * C, n = min(C, T - t0);
+  // the accumulator at this chunk's start: the chunks before it composed (each full, C tokens)
   float acc = f.pc_h_in != nullptr ? f.pc_h_in[sh * Dk + c] : f.h0;
-  for (int t0 = 0; t0 < T; t0 += kPcU) {
+  const float rc = expf(static_cast<float>(C) * f.log_rho);   // rho^C
+  for (int j0 = 0; j0 < ci; j0 += kPcU) {
+    float sv[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) sv[u] = a.Sg[(sh * a.NC + min(j0 + u, ci - 1)) * Dk + c];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u)
+      if (j0 + u < ci) acc = fmaf(rc, acc, sv[u]);
+  }
+  for (int u0 = 0; u0 < n; u0 += kPcU) {
     float kv[kPcU];
 #pragma unroll
-    for (int u = 0; u < kPcU; ++u) {
-      const int t = min(t0 + u, T - 1);
-      kv[u] = ld_f(k, ((static_cast<long long>(b) * T + t) * H + h) * Dk + c);
-    }
+    for (int u = 0; u < kPcU; ++u)
+      kv[u] = ld_f(k, ((static_cast<long long>(b) * T + t0 + min(u0 + u, n - 1)) * H + h) * Dk + c);
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
-      const int t = t0 + u;
-      if (t >= T) break;
+      const int t = t0 + u0 + u;
+      if (u0 + u >= n) break;
       acc = fmaf(f.rho, acc, kv[u] * kv[u]);
       const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
       const float p = 1.f / (acc / bt + f.eps);
@@ -1334,37 +1373,84 @@ __global__ __launch_bounds__(kPcThreads) void bwd_pc_keys_kernel(BwdArgs a) {
   }
 }
 
+// a_t = -(dr_t k_t p_t^2) / b_t of token t (o its element offset)
+template <typename IO>
+__device__ __forceinline__ float pc_local_grad(const BwdArgs &a, const IO *k, long long o, int t, float &kt,
+                                               float &pt, float &gt) {
+  kt = ld_f(k, o);
+  pt = a.Pk[o];
+  gt = a.dRk[o];
+  const float bt = -expm1f(static_cast<float>(a.f.t0 + t + 1) * a.f.log_rho);
+  return -(gt * kt * pt * pt) / bt;
+}
+
+template <typename IO>
+__global__ __launch_bounds__(kPcThreads) void bwd_pc_grad_sum_kernel(BwdArgs a) {
+  const ChunkArgs &f = a.f;
+  const IO *__restrict__ k = static_cast<const IO *>(f.k);
+  const int c = threadIdx.x, ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T, C = f.C;
+  if (c >= Dk) return;
+  const int t0 = ci * C, n = min(C, T - t0);
+  float Hs = 0.f;   // H at the chunk's first token with nothing after the chunk
+  for (int u1 = n; u1 > 0; u1 -= kPcU) {   // tokens u1 - kPcU .. u1 - 1 of the chunk, last first
+    float av[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = t0 + max(u1 - 1 - u, 0);
+      float kt, pt, gt;
+      av[u] = pc_local_grad(a, k, ((static_cast<long long>(b) * T + t) * H + h) * Dk + c, t, kt, pt, gt);
+    }
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u)
+      if (u1 - 1 - u >= 0) Hs = fmaf(f.rho, Hs, av[u]);
+  }
+  a.Sg[((static_cast<long long>(b) * H + h) * a.NC + ci) * Dk + c] = Hs;
+}
+
 template <typename IO>
 __global__ __launch_bounds__(kPcThreads) void bwd_pc_grad_kernel(BwdArgs a) {
   const ChunkArgs &f = a.f;
   const IO *__restrict__ k = static_cast<const IO *>(f.k);
-  const int c = blockIdx.x * kPcThreads + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int Dk = f.Dk, H = f.H, T = f.T;
+  const int c = threadIdx.x, ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Dk = f.Dk, H = f.H, T = f.T, C = f.C, NC = a.NC;
   if (c >= Dk) return;
   const long long sh = static_cast<long long>(b) * H + h;
+  const int t0 = ci * C, n = min(C, T - t0);
+  // H at the first token after this chunk: the chunks after it composed, last first (every
+  // chunk full but the last, of T - (NC - 1) C tokens)
   float Hs = 0.f;
-  for (int t1 = T; t1 > 0; t1 -= kPcU) {   // tokens t1 - kPcU .. t1 - 1, last first
-    float kv[kPcU], pv[kPcU], gv[kPcU], dk0[kPcU];
+  const float rc = expf(static_cast<float>(C) * f.log_rho);
+  const float rl = expf(static_cast<float>(T - (NC - 1) * C) * f.log_rho);
+  for (int j1 = NC - 1; j1 > ci; j1 -= kPcU) {   // chunks j1 - kPcU + 1 .. j1, last first
+    float sv[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) sv[u] = a.Sg[(sh * NC + max(j1 - u, ci + 1)) * Dk + c];
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
-      const int t = max(t1 - 1 - u, 0);
+      const int j = j1 - u;
+      if (j <= ci) break;
+      Hs = fmaf(j == NC - 1 ? rl : rc, Hs, sv[u]);
+    }
+  }
+  for (int u1 = n; u1 > 0; u1 -= kPcU) {
+    float av[kPcU], kv[kPcU], pv[kPcU], gv[kPcU], dk0[kPcU];
+#pragma unroll
+    for (int u = 0; u < kPcU; ++u) {
+      const int t = t0 + max(u1 - 1 - u, 0);
       const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
-      kv[u] = ld_f(k, o);
-      pv[u] = a.Pk[o];
-      gv[u] = a.dRk[o];
+      av[u] = pc_local_grad(a, k, o, t, kv[u], pv[u], gv[u]);
       dk0[u] = a.dk[o];
     }
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
-      const int t = t1 - 1 - u;
-      if (t < 0) break;
-      const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
-      Hs = fmaf(f.rho, Hs, -(gv[u] * kv[u] * pv[u] * pv[u]) / bt);
-      const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
-      a.dk[o] = dk0[u] + gv[u] * pv[u] + 2.f * kv[u] * Hs;
+      if (u1 - 1 - u < 0) break;
+      const int t = t0 + u1 - 1 - u;
+      Hs = fmaf(f.rho, Hs, av[u]);
+      a.dk[((static_cast<long long>(b) * T + t) * H + h) * Dk + c] = dk0[u] + gv[u] * pv[u] + 2.f * kv[u] * Hs;
     }
   }
-  if (a.dpc_h_in != nullptr) a.dpc_h_in[sh * Dk + c] = f.rho * Hs;
+  if (ci == 0 && a.dpc_h_in != nullptr) a.dpc_h_in[sh * Dk + c] = f.rho * Hs;
 }
 
 template <typename IO>
@@ -1461,22 +1547,39 @@ hipError_t launch_bwd_chunk(const BwdArgs &a, int io_dtype, hipStream_t s) {
   return io_dtype == GDR_BF16 ? chunk_io<uint16_t>(a, s) : chunk_io<float>(a, s);
 }
 
-hipError_t launch_bwd_pc_keys(const BwdArgs &a, int io_dtype, hipStream_t s) {
-  const dim3 grid((a.f.Dk + kPcThreads - 1) / kPcThreads, a.f.H, a.f.B);
-  if (io_dtype == GDR_BF16)
-    hipLaunchKernelGGL((bwd_pc_keys_kernel<uint16_t>), grid, dim3(kPcThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_pc_keys_kernel<float>), grid, dim3(kPcThreads), 0, s, a);
+template <typename IO>
+hipError_t pc_keys_io(const BwdArgs &a, hipStream_t s) {
+  const dim3 grid(a.NC, a.f.H, a.f.B);
+  hipLaunchKernelGGL((bwd_pc_keys_sum_kernel<IO>), grid, dim3(kPcThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_pc_keys_kernel<IO>), grid, dim3(kPcThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pc_grad(const BwdArgs &a, int io_dtype, hipStream_t s) {
-  const dim3 grid((a.f.Dk + kPcThreads - 1) / kPcThreads, a.f.H, a.f.B);
-  if (io_dtype == GDR_BF16)
-    hipLaunchKernelGGL((bwd_pc_grad_kernel<uint16_t>), grid, dim3(kPcThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_pc_grad_kernel<float>), grid, dim3(kPcThreads), 0, s, a);
+template <typename IO>
+hipError_t pc_grad_io(const BwdArgs &a, hipStream_t s) {
+  if (a.NC == 0) {   // T = 0: the accumulator reaches no output
+    if (a.dpc_h_in == nullptr) return hipSuccess;
+    const long long nz = static_cast<long long>(a.f.B) * a.f.H * a.f.Dk;
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(static_cast<unsigned>((nz + 255) / 256)), dim3(256), 0, s,
+                       a.dpc_h_in, nz);
+    return hipGetLastError();
+  }
+  const dim3 grid(a.NC, a.f.H, a.f.B);
+  hipLaunchKernelGGL((bwd_pc_grad_sum_kernel<IO>), grid, dim3(kPcThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_pc_grad_kernel<IO>), grid, dim3(kPcThreads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_pc_keys(const BwdArgs &a, int io_dtype, hipStream_t s) {
+  return io_dtype == GDR_BF16 ? pc_keys_io<uint16_t>(a, s) : pc_keys_io<float>(a, s);
+}
+
+hipError_t launch_bwd_pc_grad(const BwdArgs &a, int io_dtype, hipStream_t s) {
+  return io_dtype == GDR_BF16 ? pc_grad_io<uint16_t>(a, s) : pc_grad_io<float>(a, s);
 }
 
 }  // namespace gdr

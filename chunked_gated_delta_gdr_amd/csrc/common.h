@@ -41,6 +41,7 @@ struct BwdArgs {
   // other kernels; the kernels read the write key from Rk whenever it is set), the write-key
   // gradients dR [B,T,H,Dk] (null otherwise); dL/dpc_h_in [B,H,Dk] or null
   float *Rk, *Pk, *dRk, *dpc_h_in;
+  float *Sg;   // preconditioned write key: per-chunk partial sums of its scans [B,H,NC,Dk]
   int NC;   // chunks per stream
 };
 

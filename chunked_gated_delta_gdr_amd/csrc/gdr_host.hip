@@ -56,7 +56,7 @@ constexpr long double kMaxElems = 1099511627776.0L;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
-  uint64_t h, dh, D, dX, T, P, W, U, G, R, Pk, dR, total;
+  uint64_t h, dh, D, dX, T, P, W, U, G, R, Pk, dR, Sg, total;
   int NC;
 };
 
@@ -79,7 +79,8 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   const uint64_t kk = d.wkey == GDR_WKEY_DIAG_PRECOND ? al(B * T * H * Dk * 4u) : 0u;
   L.Pk = L.R + kk;
   L.dR = L.Pk + kk;
-  L.total = L.dR + kk;
+  L.Sg = L.dR + kk;
+  L.total = L.Sg + (d.wkey == GDR_WKEY_DIAG_PRECOND ? al(B * H * NC * Dk * 4u) : 0u);
   L.NC = static_cast<int>(NC);
   return L;
 }
@@ -365,6 +366,7 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
       b.Rk = reinterpret_cast<float *>(ws + L.R);
       b.Pk = reinterpret_cast<float *>(ws + L.Pk);
       b.dRk = reinterpret_cast<float *>(ws + L.dR);
+      b.Sg = reinterpret_cast<float *>(ws + L.Sg);
     }
   }
   b.dout = d_out;

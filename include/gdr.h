@@ -233,7 +233,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
  * dX and U (3 B T H Dv floats), T and P (2 B H ceil(T/C) C^2 floats) and W
  * (B H ceil(T/C) C Dk floats), with decay CHANNEL also the cumulative decays G
  * (B H ceil(T/C) C Dk floats), with wkey DIAG_PRECOND also the write keys, p_t and the
- * write-key gradients (3 B T H Dk floats), each section 256-byte aligned.  No HIP call. */
+ * write-key gradients (3 B T H Dk floats) and per-chunk sums of the preconditioner's scans
+ * (B H ceil(T/C) Dk floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 
 /* gdr_chunk_bwd's argument check on its own (no HIP call). */

@@ -229,8 +229,8 @@ def test_bwd_workspace_size_formula(T, C, decay, wkey):
             + _al(B * H * NC * C * Dk * 4))
     if decay == G.GDR_DECAY_CHANNEL:   # the cumulative decays G
         want += _al(B * H * NC * C * Dk * 4)
-    if wkey == G.GDR_WKEY_DIAG_PRECOND:   # write keys, p_t, write-key gradients
-        want += 3 * _al(B * T * H * Dk * 4)
+    if wkey == G.GDR_WKEY_DIAG_PRECOND:   # write keys, p_t, write-key gradients, chunk sums
+        want += 3 * _al(B * T * H * Dk * 4) + _al(B * H * NC * Dk * 4)
     assert G.gdr_chunk_bwd_workspace_size(d) == want
     assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
 
