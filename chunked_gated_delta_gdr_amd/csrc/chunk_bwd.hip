@@ -72,10 +72,15 @@ __device__ __forceinline__ float chunk_log_alpha(const ChunkArgs &f, long long r
 }
 
 // the write key at offset o (token row, channel) of the chunk whose first element is row0k:
-// the formed preconditioned key (fp32) when there is one, else k or the explicit write key
-template <typename IO>
+// the formed preconditioned key (fp32) with the preconditioner (PC), else k or the explicit
+// write key (chosen at compile time: a load inside a run-time branch would have to complete
+// before the branch ends)
+template <bool PC, typename IO>
 __device__ __forceinline__ float ld_wkey(const BwdArgs &a, const IO *rbase, long long row0k, long long o) {
-  return a.Rk != nullptr ? a.Rk[row0k + o] : ld_f(rbase + row0k, o);
+  if constexpr (PC)
+    return a.Rk[row0k + o];
+  else
+    return ld_f(rbase + row0k, o);
 }
 
 // sum over k < K of A[i][k] B[k][j] for the lane's row i (row pointer ra) and column j (row
@@ -126,12 +131,11 @@ __device__ __forceinline__ void chunk_gates(const ChunkArgs &f, long long row0, 
 // ---------------------------------------------------------------------------------------
 constexpr int kPrThreads = 512;
 
-template <typename IO, int DK, bool CHD>
+template <typename IO, int DK, bool CHD, bool PC>
 __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   static_assert(DK == 64 || DK == 128, "32 channel groups of 2 or 4");
   constexpr int kThreads = kPrThreads;
   constexpr int LD = DK + 4;
-  constexpr int CW = DK / 32;
   constexpr int kLoadIt = kCMax * DK / kThreads;
   const ChunkArgs &f = a.f;
   const IO *__restrict__ q = static_cast<const IO *>(f.q);
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
       const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
       xk[it] = ld_f(kc, o);
       xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-      xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
+      xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
       xq[it] = CHD ? f.log_alpha[row0 * Dk + o] : ld_f(qc, o);
     }
 #pragma unroll
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 constexpr int kStBV = 32;
 constexpr int kStThreads = 512;
 
-template <typename IO, int DK, bool CHD>
+template <typename IO, int DK, bool CHD, bool PC>
 __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kStBV, kThreads = kStThreads;
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
       pw[it] = Wc[static_cast<long long>(t) * Dk + c];
-      pr[it] = ld_wkey(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c);
+      pr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c);
     }
     if constexpr (CHD) {
       // (kThreads is a multiple of DK: the thread's channel is the same in every item)
@@ -505,7 +509,7 @@ constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
 
 
-template <typename IO, int DK, bool CHD>
+template <typename IO, int DK, bool CHD, bool PC>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kSwBV, kThreads = kSwThreads;
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
       const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-      xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
+      xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
       xk[it] = ld_f(kc, o);
       xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
     }
@@ -765,7 +769,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 constexpr int kCkThreads = 512;
 
 
-template <typename IO, int DK, bool CHD>
+template <typename IO, int DK, bool CHD, bool PC>
 __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(DK == 64 || DK == 128, "two halves of 16-channel tiles");
   constexpr int kThreads = kCkThreads;
@@ -951,7 +955,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           xq[it] = ld_f(qc, o);
           xk[it] = ld_f(kc, o);
           xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-          xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
+          xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
           xG[it] = Gc[static_cast<long long>(tc) * Dk + cc];   // (flat past n)
         }
         __syncthreads();   // the previous half's tiles are consumed
@@ -1131,7 +1135,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         xq[it] = ld_f(qc, o);
         xk[it] = ld_f(kc, o);
         xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-        xr[it] = ld_wkey(a, rbase, row0 * Dk, o);
+        xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
       }
   #pragma unroll
       for (int it = 0; it < kLoadIt; ++it) {
@@ -1362,13 +1366,14 @@ __global__ __launch_bounds__(kPcThreads) void bwd_pc_keys_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
       const int t = t0 + u0 + u;
-      if (u0 + u >= n) break;
-      acc = fmaf(f.rho, acc, kv[u] * kv[u]);
-      const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
-      const float p = 1.f / (acc / bt + f.eps);
-      const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
-      a.Pk[o] = p;
-      a.Rk[o] = kv[u] * p;
+      if (u0 + u < n) {
+        acc = fmaf(f.rho, acc, kv[u] * kv[u]);
+        const float bt = -expm1f(static_cast<float>(f.t0 + t + 1) * f.log_rho);
+        const float p = 1.f / (acc / bt + f.eps);
+        const long long o = ((static_cast<long long>(b) * T + t) * H + h) * Dk + c;
+        a.Pk[o] = p;
+        a.Rk[o] = kv[u] * p;
+      }
     }
   }
 }
@@ -1429,8 +1434,7 @@ __global__ __launch_bounds__(kPcThreads) void bwd_pc_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
       const int j = j1 - u;
-      if (j <= ci) break;
-      Hs = fmaf(j == NC - 1 ? rl : rc, Hs, sv[u]);
+      if (j > ci) Hs = fmaf(j == NC - 1 ? rl : rc, Hs, sv[u]);
     }
   }
   for (int u1 = n; u1 > 0; u1 -= kPcU) {
@@ -1444,13 +1448,23 @@ __global__ __launch_bounds__(kPcThreads) void bwd_pc_grad_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kPcU; ++u) {
-      if (u1 - 1 - u < 0) break;
       const int t = t0 + u1 - 1 - u;
-      Hs = fmaf(f.rho, Hs, av[u]);
-      a.dk[((static_cast<long long>(b) * T + t) * H + h) * Dk + c] = dk0[u] + gv[u] * pv[u] + 2.f * kv[u] * Hs;
+      if (u1 - 1 - u >= 0) {
+        Hs = fmaf(f.rho, Hs, av[u]);
+        a.dk[((static_cast<long long>(b) * T + t) * H + h) * Dk + c] = dk0[u] + gv[u] * pv[u] + 2.f * kv[u] * Hs;
+      }
     }
   }
   if (ci == 0 && a.dpc_h_in != nullptr) a.dpc_h_in[sh * Dk + c] = f.rho * Hs;
+}
+
+// calls fn with std::true_type for the preconditioned write key, std::false_type otherwise
+template <typename F>
+void launch_pc(const BwdArgs &a, F &&fn) {
+  if (a.f.wkey == GDR_WKEY_DIAG_PRECOND)
+    fn(std::true_type{});
+  else
+    fn(std::false_type{});
 }
 
 template <typename IO>
@@ -1460,33 +1474,33 @@ hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 64) {
     if (chd)
-      hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, true>), gp, dim3(kPrThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, true, decltype(pc)::value>), gp, dim3(kPrThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, false>), gp, dim3(kPrThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_prep_kernel<IO, 64, false, decltype(pc)::value>), gp, dim3(kPrThreads), 0, s, a); });
   } else {
     if (chd)
-      hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, true>), gp, dim3(kPrThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, true, decltype(pc)::value>), gp, dim3(kPrThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, false>), gp, dim3(kPrThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_prep_kernel<IO, 128, false, decltype(pc)::value>), gp, dim3(kPrThreads), 0, s, a); });
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);
   if (a.f.Dk <= 32) {
     if (chd)
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
   } else {
     if (chd)
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false>), gs, dim3(kStThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
@@ -1497,19 +1511,19 @@ hipError_t sweep_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 32) {
     if (chd)
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
   } else {
     if (chd)
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false>), grid, dim3(kSwThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
@@ -1521,14 +1535,14 @@ hipError_t chunk_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 64) {
     if (chd)
-      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, true>), grid, dim3(kCkThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, true, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, false>), grid, dim3(kCkThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, false, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
   } else {
     if (chd)
-      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, true>), grid, dim3(kCkThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, true, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
     else
-      hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, false>), grid, dim3(kCkThreads), 0, s, a);
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, false, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
