@@ -44,4 +44,6 @@ from .core import (  # noqa: F401
     rel_l2,
     snr_db,
 )
-from .backward import precond_grad, recurrent_grad, recurrent_stream_grad  # noqa: F401
+from .backward import (  # noqa: F401
+    chunked_grad, chunked_stream_grad, precond_grad, recurrent_grad, recurrent_stream_grad,
+)

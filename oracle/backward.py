@@ -185,3 +185,148 @@ def recurrent_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.n
             else:
                 out[key][b, :, h] = val
     return out
+
+
+def chunked_stream_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.ndarray] = None,
+                        *, chunk: int, band: int, scale: float = 1.0, S0: Optional[np.ndarray] = None,
+                        precond: Optional[dict] = None) -> Dict[str, np.ndarray]:
+    """Gradients of one stream's loss through the chunk form with the band-limited T
+    (``core.chunked_stream`` with t_mode ("neumann", band): T_b = M (.) sum_{n<=band} A^n, M the
+    band i - j <= band), scalar or no decay.  The band entries of the truncated series equal
+    those of (I - A)^-1 for strictly lower A (Lemma 3.1 of the MatMul-only inversion summary),
+    so T_b = M (.) T as functions of A and dA = T^T (M (.) dT_b) T^T on the strictly lower part.
+    Everything else is the chain rule through the chunk form's steps, chunk by chunk in reverse:
+        o = (e^g (.) Q) S^T + P D,   D = T_b X,   X = V' - (e^g (.) E) S^T,
+        S' = e^{g_n} S + D^T (e^{g_n - g} (.) R),   P = causal (.) (Q R^T) (.) Gamma,
+        L = strict lower (.) (E R^T) (.) Gamma,     A = -L.
+    Returns the same dictionary as ``recurrent_stream_grad``.
+    """
+    e, r, vp, la, _ = variant_vectors(x, precond=precond)
+    if la.ndim != 1:
+        raise ValueError("chunked_stream_grad: scalar or no decay only")
+    q = np.asarray(x["q"], dtype=F64) * scale
+    dO = np.asarray(dO, dtype=F64)
+    T, Dk = e.shape
+    Dv = vp.shape[1]
+    S = np.zeros((Dv, Dk), dtype=F64) if S0 is None else np.array(S0, dtype=F64, copy=True)
+    # forward, keeping every chunk's operands
+    saved = []
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, min(c0 + chunk, T))
+        E, R, V, Q = e[sl], r[sl], vp[sl], q[sl]
+        n = E.shape[0]
+        g = np.cumsum(la[sl])
+        i, j = np.indices((n, n))
+        causal = j <= i
+        Gam = np.where(causal, np.exp(np.where(causal, g[:, None] - g[None, :], 0.0)), 0.0)
+        L = np.where(j < i, (E @ R.T) * Gam, 0.0)
+        Tf = np.linalg.inv(np.eye(n) + L)          # the exact inverse, for the derivative
+        Tb = np.where(i - j <= band, Tf, 0.0)       # the band (the forward's T_b)
+        Et = np.exp(g)[:, None] * E
+        X = V - Et @ S.T
+        D = Tb @ X
+        P = np.where(causal, (Q @ R.T) * Gam, 0.0)
+        saved.append((sl, S.copy(), g, Gam, L, Tf, Tb, Et, X, D, P))
+        S = np.exp(g[-1]) * S + D.T @ (np.exp(g[-1] - g)[:, None] * R)
+    # reverse
+    de = np.zeros_like(e)
+    dr = np.zeros_like(r)
+    dvp = np.zeros_like(vp)
+    dq = np.zeros_like(q)
+    dla = np.zeros_like(la)
+    G = np.zeros((Dv, Dk), dtype=F64) if dS_T is None else np.array(dS_T, dtype=F64, copy=True)
+    for (sl, Sc, g, Gam, L, Tf, Tb, Et, X, D, P) in reversed(saved):
+        E, R, Q, dOc = e[sl], r[sl], q[sl], dO[sl]
+        n = E.shape[0]
+        i, j = np.indices((n, n))
+        dg = np.zeros(n)
+        gn = g[-1]
+        Rb = np.exp(gn - g)[:, None] * R
+        Qt = np.exp(g)[:, None] * Q
+        # S' = e^{g_n} S + D^T Rb
+        dD = Rb @ G.T
+        dRb = D @ G
+        dg[-1] += np.sum(G * Sc) * np.exp(gn) + np.sum(dRb * Rb)
+        dg -= np.sum(dRb * Rb, axis=1)
+        dR = np.exp(gn - g)[:, None] * dRb
+        dS = np.exp(gn) * G
+        # o = Qt S^T + P D
+        dQt = dOc @ Sc
+        dS = dS + dOc.T @ Qt
+        dg += np.sum(dQt * Qt, axis=1)
+        dQ = np.exp(g)[:, None] * dQt
+        dP = np.where(j <= i, dOc @ D.T, 0.0)
+        dD = dD + P.T @ dOc
+        # P = causal (.) (Q R^T) (.) Gamma
+        dg += np.sum(dP * P, axis=1) - np.sum(dP * P, axis=0)
+        dQ = dQ + (dP * Gam) @ R
+        dR = dR + (dP * Gam).T @ Q
+        # D = T_b X,  X = V' - Et S^T
+        dX = Tb.T @ dD
+        dTb = np.where(i - j <= band, dD @ X.T, 0.0)
+        dL = -np.where(j < i, Tf.T @ dTb @ Tf.T, 0.0)   # A = -L, dA = T^T (M (.) dT_b) T^T
+        dvp[sl] = dX
+        dEt = -dX @ Sc
+        dS = dS - dX.T @ Et
+        dg += np.sum(dEt * Et, axis=1)
+        dE = np.exp(g)[:, None] * dEt
+        # L = strict lower (.) (E R^T) (.) Gamma
+        dg += np.sum(dL * L, axis=1) - np.sum(dL * L, axis=0)
+        dE = dE + (dL * Gam) @ R
+        dR = dR + (dL * Gam).T @ E
+        de[sl], dr[sl], dq[sl] = dE, dR, dQ
+        dla[sl] = np.cumsum(dg[::-1])[::-1]
+        G = dS
+    dq *= scale
+    k = np.asarray(x["k"], dtype=F64)
+    v = np.asarray(x["v"], dtype=F64)
+    out: Dict[str, np.ndarray] = {"dq": dq, "dS0": G}
+    if x.get("erase") is not None:
+        b = np.asarray(x["erase"], dtype=F64)
+        w = np.asarray(x["write"], dtype=F64)
+        dk = b * de
+        out["derase"] = k * de
+        out["dwrite"] = v * dvp
+        out["dv"] = w * dvp
+    else:
+        beta = np.asarray(x["beta"], dtype=F64)
+        dk = beta[:, None] * de
+        out["dbeta"] = np.sum(k * de, axis=1) + np.sum(v * dvp, axis=1)
+        out["dv"] = beta[:, None] * dvp
+    if precond is not None:
+        dkp, dh0 = precond_grad(k, dr, precond["rho"], precond["eps"], precond["h_init"], precond["t0"])
+        dk = dk + dkp
+        out["dpc_h_init"] = dh0
+    elif x.get("write_key") is not None:
+        out["dwrite_key"] = dr
+    else:
+        dk = dk + dr
+    out["dk"] = dk
+    if x.get("log_alpha") is not None:
+        out["dlog_alpha"] = dla
+    return out
+
+
+def chunked_grad(x: Dict[str, np.ndarray], dO: np.ndarray, dS_T: Optional[np.ndarray] = None,
+                 *, chunk: int, band: int, scale: float = 1.0, state0: Optional[np.ndarray] = None,
+                 streams=None, precond: Optional[dict] = None) -> Dict[str, np.ndarray]:
+    """``chunked_stream_grad`` over [B, T, H, D] inputs, laid out as ``recurrent_grad``."""
+    B, T, H, _ = x["q"].shape
+    Dk = x["k"].shape[-1]
+    Dv = x["v"].shape[-1]
+    out: Dict[str, np.ndarray] = {}
+    todo = streams if streams is not None else [(b, h) for b in range(B) for h in range(H)]
+    for (b, h) in todo:
+        gb = chunked_stream_grad(_stream(x, b, h), np.asarray(dO)[b, :, h],
+                                 None if dS_T is None else dS_T[b, h], chunk=chunk, band=band, scale=scale,
+                                 S0=None if state0 is None else state0[b, h],
+                                 precond=_precond_for(precond, b, h, Dk))
+        for key, val in gb.items():
+            if key not in out:
+                shape = {"dS0": (B, H, Dv, Dk), "dpc_h_init": (B, H, Dk)}.get(key, (B, T, H) + val.shape[1:])
+                out[key] = np.zeros(shape, dtype=F64)
+            if key in ("dS0", "dpc_h_init"):
+                out[key][b, h] = val
+            else:
+                out[key][b, :, h] = val
+    return out

@@ -159,3 +159,58 @@ def test_preconditioner_gradient_of_a_constant_accumulator():
     dk, dh0 = O.precond_grad(k, dr, 1e-300, eps, np.zeros(4), 0)
     np.testing.assert_allclose(dk, dr * (eps - k * k) / (k * k + eps) ** 2, rtol=1e-12, atol=1e-14)
     assert np.all(np.abs(dh0) < 1e-250)
+
+
+BAND_VARIANTS = ["gdn", "gdn2_decay", "explicit", "plain"]
+
+
+@pytest.mark.parametrize("variant", BAND_VARIANTS)
+def test_chunk_form_gradient_with_exact_t_is_the_recurrence_gradient(variant):
+    """band >= C - 1 keeps all of T: the chunk-form gradient equals the reverse sweep of the
+    recurrence (two independent derivations)."""
+    x, S0, dO, dST = tiny_stream(variant, T=13, Dk=4, Dv=3, seed=60 + BAND_VARIANTS.index(variant))
+    a = O.recurrent_stream_grad(x, dO, dST, scale=0.6, S0=S0)
+    b = O.chunked_stream_grad(x, dO, dST, chunk=5, band=4, scale=0.6, S0=S0)
+    assert a.keys() == b.keys()
+    for key in a:
+        np.testing.assert_allclose(b[key], a[key], rtol=1e-10, atol=1e-11, err_msg=key)
+
+
+@pytest.mark.parametrize("band", [0, 1, 2])
+@pytest.mark.parametrize("variant", BAND_VARIANTS)
+def test_band_gradients_match_central_differences(variant, band):
+    """The band-limited T (t_mode ("neumann", band)): every input's gradient against central
+    differences of the oracle's chunk form, a ragged last chunk included."""
+    x, S0, dO, dST = tiny_stream(variant, T=11, Dk=3, Dv=2, seed=70 + band)
+    scale, C = 0.8, 4
+
+    def loss(xx, s0):
+        o, S, _ = O.chunked_stream(xx, chunk=C, t_mode=("neumann", band), scale=scale, S0=s0)
+        return float(np.sum(o * dO) + np.sum(S * dST))
+
+    g = O.chunked_stream_grad(x, dO, dST, chunk=C, band=band, scale=scale, S0=S0)
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "erase": "derase",
+             "write": "dwrite", "log_alpha": "dlog_alpha", "write_key": "dwrite_key"}
+    h = 1e-6
+    for key, gname in list(names.items()) + [("S0", "dS0")]:
+        base = S0 if key == "S0" else x.get(key)
+        if base is None:
+            continue
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                pert = base.copy()
+                pert[idx] += sgn * h
+                vals.append(loss(x, pert) if key == "S0" else loss({**x, key: pert}, S0))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        err = np.max(np.abs(g[gname] - fd))
+        assert err <= 1e-7 * (1.0 + np.max(np.abs(fd))), (gname, err)
+
+
+def test_band_gradient_differs_from_the_recurrence_gradient():
+    """A narrow band is a different function: its gradient is not the recurrence's."""
+    x, S0, dO, dST = tiny_stream("gdn", T=12, Dk=4, Dv=3, seed=80)
+    a = O.recurrent_stream_grad(x, dO, dST, S0=S0)
+    b = O.chunked_stream_grad(x, dO, dST, chunk=6, band=1, S0=S0)
+    assert O.rel_l2(b["dk"], a["dk"]) > 1e-3
