@@ -310,13 +310,15 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
                   write_key=None, precond: bool = False, pc_h_in=None, pc_rho: float = 0.99,
                   pc_eps: float = 1e-3, pc_h0: float = 1.0, pc_t0: int = 0,
                   state_in=None, d_state_out=None, want_dstate_in: bool = True,
-                  chunk: int = 64, scale: float = 1.0, workspace=None, stream=None) -> dict:
+                  chunk: int = 64, neumann_order: int = -1, scale: float = 1.0, workspace=None,
+                  stream=None) -> dict:
     """Gradients through ``gdr_chunk_fwd`` on torch tensors.  ``d_out`` [B, T, H, Dv] (io dtype)
     and ``d_state_out`` [B, H, Dv, Dk] fp32 (or None) are the loss gradients of the forward's
     outputs.  Returns a dict of fp32 tensors: dq, dk, dv, and as the variant has them dbeta |
     derase, dwrite, dlog_alpha, dwrite_key, dpc_h_in (``precond``), and dstate_in (if
-    ``want_dstate_in``).  The workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is
-    allocated when not given."""
+    ``want_dstate_in``).  ``neumann_order`` = N >= 0 differentiates the forward with the
+    band-limited T.  The workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is allocated
+    when not given."""
     torch = _torch()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -344,7 +346,7 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
                             GDR_DECAY_SCALAR if log_alpha is not None else GDR_DECAY_NONE),
                      wkey=(GDR_WKEY_DIAG_PRECOND if precond else
                            GDR_WKEY_EXPLICIT if write_key is not None else GDR_WKEY_SAME),
-                     scale=scale, impl=GDR_IMPL_GENERIC,
+                     scale=scale, impl=GDR_IMPL_GENERIC, neumann_order=neumann_order,
                      pc_rho=pc_rho, pc_eps=pc_eps, pc_h0=pc_h0, pc_t0=pc_t0)
 
     def new(shape):

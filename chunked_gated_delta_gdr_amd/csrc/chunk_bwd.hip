@@ -83,6 +83,12 @@ __device__ __forceinline__ float ld_wkey(const BwdArgs &a, const IO *rbase, long
     return ld_f(rbase + row0k, o);
 }
 
+// tile u < 10 of the ten 16 x 16 tiles on and below the diagonal of a 64 x 64 matrix
+__device__ __forceinline__ void lower_tile10(int u, int &ib, int &jb) {
+  ib = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+  jb = u - ib * (ib + 1) / 2;
+}
+
 // sum over k < K of A[i][k] B[k][j] for the lane's row i (row pointer ra) and column j (row
 // pointer rb of B^T), both with k contiguous in LDS: the K order is permuted so that sub-step
 // u of block s takes k = s + 4 kq + u, and each lane reads its 4 k with one 16-byte read per
@@ -241,7 +247,8 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = float4v{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < 16 * (ib + 1); s0 += 4) {
-      const float at_ = Tm[16 * ib + col][s0 + kq];
+      // (band-limited T: the band of the inverse, T_b, the forward's T)
+      const float at_ = (f.N < 0 || 16 * ib + col - (s0 + kq) <= f.N) ? Tm[16 * ib + col][s0 + kq] : 0.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int c = 16 * (cb0 + m) + col;
@@ -286,7 +293,8 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int i = idx / C, j = idx % C;
-      a.Tw[cc + idx] = Tm[i][j];
+      a.Tw[cc + idx] = (f.N < 0 || i - j <= f.N) ? Tm[i][j] : 0.f;   // T_b with a band
+      if (f.N >= 0) a.Tfw[cc + idx] = Tm[i][j];                       // and the whole inverse
       a.Pw[cc + idx] = j <= i ? LP[i][j] : 0.f;
     }
   }
@@ -689,7 +697,9 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tr0 + r, rr = 16 * rb + col;
-        dDs[t][rr] = (t < n && rr < nv) ? fmaf(wd[t], a1[0][r], f.scale * a2[r]) : 0.f;
+        const float dd = fmaf(wd[t], a1[0][r], f.scale * a2[r]);
+        dDs[t][rr] = (t < n && rr < nv) ? dd : 0.f;
+        if (a.dDw != nullptr && t < n && rr < nv) a.dDw[tok(t) * Dv + v0 + rr] = dd;   // (band-limited T)
       }
     }
     __syncthreads();
@@ -804,7 +814,10 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   auto chan = [&](int m) { return CHD ? 16 * (4 * (m >> 1) + 2 * hh + (m & 1)) + col : 16 * (MT * hh + m) + col; };
 
   struct TilesA {   // value loop: state rows, their gradients, token tiles by value row
-    float S[kVB][LD], dS[kVB][LD], dOT[kVB][LT], dXT[kVB][LT], DT[kVB][LT];
+    float S[kVB][LD], dS[kVB][LD], dOT[kVB][LT], dXT[kVB][LT], DT[kVB][LT], dDT[kVB][LT];
+  };
+  struct TilesBand {   // band-limited T: Z = dD D^T, then W1^T; L for T_b^-1; T_b^-1; T; T^T
+    float Z[kCMax][LT], Lb[kCMax][LT], Ti[kCMax][LT], Tf[kCMax][LT], TT[kCMax][LT], Zs[32][36];
   };
   struct TilesB {   // key products: Q, E, R and the C x C gradients dM, dL'
     float Q[kCMax][LD], E[kCMax][LD], R[kCMax][LD], dM[kCMax][LT], dL[kCMax][LT];
@@ -816,6 +829,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __align__(16) union {
     TilesA A;
     std::conditional_t<CHD, TilesC, TilesB> B;
+    TilesBand Bd;
   } sm;
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax], vdx[kCMax];
   __shared__ float dgs[2][kCMax], pks[2][kCMax];
@@ -841,8 +855,11 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   // masks applied when the registers are written to LDS), so its loads are in flight while
   // the previous block is multiplied.
   constexpr int kSIt = kVB * DK / kThreads;   // state elements per thread and block
-  float ps[kSIt], pds[kSIt], po[4], px[4], pd[4], pv[4], pw[4];
+  float ps[kSIt], pds[kSIt], po[4], px[4], pd[4], pv[4], pw[4], pdd[4];
   const int lt = tid >> 3, rq = 4 * (tid & 7);   // token-tile element (token lt, rows rq .. rq + 3)
+  // band-limited T: the hh = 1 waves form Z = dD D^T (every tile) instead of dX D^T
+  const bool band = f.N >= 0;
+  const float *dDsrc = band ? a.dDw : a.dX;   // (a valid source either way: the load is unconditional)
   auto vload = [&](int vb) {
 #pragma unroll
     for (int it = 0; it < kSIt; ++it) {
@@ -858,6 +875,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       po[u] = ld_f(dout, idx);
       px[u] = a.dX[idx];
       pd[u] = a.D[idx];
+      pdd[u] = dDsrc[idx];
       pv[u] = ld_f(v, idx);
       pw[u] = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(tt)] : ld_f(wr, idx);
     }
@@ -883,6 +901,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       sm.A.dOT[r][lt] = in ? po[u] : 0.f;
       sm.A.dXT[r][lt] = gx;
       sm.A.DT[r][lt] = in ? pd[u] : 0.f;
+      sm.A.dDT[r][lt] = in ? pdd[u] : 0.f;
       if (in) {   // dv (and dwrite) are elementwise in dX
         const long long idx = tok(lt) * Dv + vb + r;
         a.dv[idx] = pw[u] * gx;
@@ -907,10 +926,10 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         AE[m] = mfma4(ax, bs, AE[m]);
         AR[m] = mfma4(ad, bds, AR[m]);
       }
-      const float am = hh == 0 ? ao : ax;
+      const float am = hh == 0 ? ao : band ? sm.A.dDT[kr][16 * tb + col] : ax;
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
-        if (jb <= tb) MPL[jb] = mfma4(am, sm.A.DT[kr][16 * jb + col], MPL[jb]);
+        if (jb <= tb || (band && hh == 1)) MPL[jb] = mfma4(am, sm.A.DT[kr][16 * jb + col], MPL[jb]);
     }
   }
   vsum += __shfl_xor(vsum, 1);
@@ -1121,6 +1140,75 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       if (tid < n) a.dbeta[tok(tid)] = pks[0][tid] + pks[1][tid] + vdx[tid];
     }
   } else {
+    // ---- band-limited T: dL = -T^T (M (.) dT_b) T^T with dT_b = dD X^T = (dD D^T) T_b^-T
+    // (X = T_b^-1 D), M the band i - j <= N below the diagonal; T_b^-1 by the shared blocked
+    // inverse of T_b, the products as 16 x 16 tiles on the matrix cores (LDS scratch over the
+    // key tiles, which are loaded after it)
+    float4v dlb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (band) {
+      auto &Bd = sm.Bd;
+      __syncthreads();   // the value-loop tiles are dead
+      if (hh == 1) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Bd.Z[tr0 + r][16 * jb + col] = MPL[jb][r];
+      }
+      {
+        const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
+        for (int idx = tid; idx < kCMax * kCMax; idx += kThreads) {
+          const int i = idx / kCMax, j = idx % kCMax;
+          const bool in = i < C && j < C;
+          const float tb_ = in ? a.Tw[cc + i * C + j] : 0.f, tf = in ? a.Tfw[cc + i * C + j] : 0.f;
+          Bd.Lb[i][j] = j < i ? tb_ : 0.f;   // T_b = I + Lb: T_b^-1 = (I + Lb)^-1
+          Bd.Tf[i][j] = tf;
+          Bd.TT[j][i] = tf;
+          if ((j >> 4) > (i >> 4)) Bd.Ti[i][j] = 0.f;
+        }
+      }
+      __syncthreads();
+      tri::inverse_blocks(Bd.Lb, Bd.Ti, Bd.Zs, -1, tid);   // (ends with a barrier)
+      // Zm = M (.) (Z T_b^-T) on every tile (zero above the diagonal and outside the band)
+      float4v zt[2];
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = wave + 8 * u2, ib = u >> 2, jb = u & 3;
+        zt[u2] = jb <= ib ? dot_kc<kCMax>(&Bd.Z[16 * ib + col][0], &Bd.Ti[16 * jb + col][0], kq)
+                          : float4v{0.f, 0.f, 0.f, 0.f};
+      }
+      __syncthreads();   // every read of Z done
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = wave + 8 * u2, ib = u >> 2, jb = u & 3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+          Bd.Lb[i][j] = (j < i && i - j <= f.N) ? zt[u2][r] : 0.f;   // (Lb is free: Zm)
+        }
+      }
+      __syncthreads();
+      // W1 = Zm T^T, stored transposed (W1T[j][m] = W1[m][j]); only its part below the
+      // diagonal is read with a non-zero factor, the rest is zero
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = wave + 8 * u2, ib = u >> 2, jb = u & 3;
+        const float4v w = jb <= ib ? dot_kc<kCMax>(&Bd.Lb[16 * ib + col][0], &Bd.Tf[16 * jb + col][0], kq)
+                                   : float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Bd.Z[16 * jb + col][16 * ib + 4 * kq + r] = w[r];
+      }
+      __syncthreads();
+      // dL = -T^T W1 on the ten tiles on and below the diagonal (kept in registers)
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = wave + 8 * u2;
+        if (u < 10) {
+          int ib, jb;
+          lower_tile10(u, ib, jb);
+          dlb[u2] = -dot_kc<kCMax>(&Bd.TT[16 * ib + col][0], &Bd.Z[16 * jb + col][0], kq);
+        }
+      }
+    }
     // ---- key products -------------------------------------------------------------------
     __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
     {   // Q, E, R: all loads first (clamped), then the masked LDS stores
@@ -1166,8 +1254,23 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         const float dec = expf(gs[t] - gs[j]);
         if (hh == 0)
           sm.B.dM[t][j] = (j <= t && t < n) ? f.scale * MPL[jb][r] * dec : 0.f;
-        else
+        else if (!band)
           sm.B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] * dec : 0.f;
+      }
+    }
+    if (band) {   // dL' = dL (.) Gamma below the diagonal, from the band block's tiles
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = wave + 8 * u2;
+        if (u < 10) {
+          int ib, jb;
+          lower_tile10(u, ib, jb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * ib + 4 * kq + r, j = 16 * jb + col;
+            sm.B.dL[t][j] = (j < t && t < n) ? dlb[u2][r] * expf(gs[t] - gs[j]) : 0.f;
+          }
+        }
       }
     }
     __syncthreads();

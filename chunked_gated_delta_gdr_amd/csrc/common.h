@@ -42,6 +42,9 @@ struct BwdArgs {
   // gradients dR [B,T,H,Dk] (null otherwise); dL/dpc_h_in [B,H,Dk] or null
   float *Rk, *Pk, *dRk, *dpc_h_in;
   float *Sg;   // preconditioned write key: per-chunk partial sums of its scans [B,H,NC,Dk]
+  // band-limited T (f.N >= 0): Tw holds the band T_b, Tfw the whole inverse T [B,H,NC,C,C];
+  // dDw the sweep's dD [B,T,H,Dv] (null otherwise)
+  float *Tfw, *dDw;
   int NC;   // chunks per stream
 };
 

@@ -56,7 +56,7 @@ constexpr long double kMaxElems = 1099511627776.0L;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
-  uint64_t h, dh, D, dX, T, P, W, U, G, R, Pk, dR, Sg, total;
+  uint64_t h, dh, D, dX, T, P, W, U, G, R, Pk, dR, Sg, Tf, dD, total;
   int NC;
 };
 
@@ -80,7 +80,10 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   L.Pk = L.R + kk;
   L.dR = L.Pk + kk;
   L.Sg = L.dR + kk;
-  L.total = L.Sg + (d.wkey == GDR_WKEY_DIAG_PRECOND ? al(B * H * NC * Dk * 4u) : 0u);
+  L.Tf = L.Sg + (d.wkey == GDR_WKEY_DIAG_PRECOND ? al(B * H * NC * Dk * 4u) : 0u);
+  const bool band = d.neumann_order >= 0;
+  L.dD = L.Tf + (band ? cc : 0u);
+  L.total = L.dD + (band ? tk : 0u);
   L.NC = static_cast<int>(NC);
   return L;
 }
@@ -284,7 +287,10 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   if (g->dpc_h_in != nullptr && d->wkey != GDR_WKEY_DIAG_PRECOND)
     return fail(GDR_EINVAL, "grads->dpc_h_in given without wkey DIAG_PRECOND");
   if ((reinterpret_cast<uintptr_t>(g->dpc_h_in) & 3u) != 0) return fail(GDR_EINVAL, "grads->dpc_h_in misaligned");
-  if (d->neumann_order >= 0) return fail(GDR_ENOTSUP, "backward of the band-limited T (exact T only)");
+  if (d->neumann_order >= 0 && d->residual_steps > 0)
+    return fail(GDR_ENOTSUP, "backward of the residual-corrected T (exact or band-limited T only)");
+  if (d->neumann_order >= 0 && d->decay == GDR_DECAY_CHANNEL)
+    return fail(GDR_ENOTSUP, "backward of the band-limited T with the per-channel decay");
   const bool need = d->T > 0;
   struct Opt {
     const char *name;
@@ -367,6 +373,10 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
       b.Pk = reinterpret_cast<float *>(ws + L.Pk);
       b.dRk = reinterpret_cast<float *>(ws + L.dR);
       b.Sg = reinterpret_cast<float *>(ws + L.Sg);
+    }
+    if (d->neumann_order >= 0) {
+      b.Tfw = reinterpret_cast<float *>(ws + L.Tf);
+      b.dDw = reinterpret_cast<float *>(ws + L.dD);
     }
   }
   b.dout = d_out;

@@ -209,8 +209,14 @@ typedef struct gdr_grads {
  * accumulator (pc_h_out) is not written.
  * All arithmetic is fp32 (inputs in io_dtype are widened once).
  *
+ * With the band-limited T (neumann_order = N >= 0) the forward is D = T_b X with T_b the band
+ * i - j <= N of T; its derivative adds dT_b = dD X^T = (dD D^T) T_b^-T, masked to the band, and
+ * takes dA = T^T (M (.) dT_b) T^T (the band of the truncated series is that of T, so the
+ * derivative is that of the band of the inverse) in place of -dX D^T; the sweep keeps dD for
+ * it, the preparation both T and T_b.
+ *
  * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR | CHANNEL, wkey SAME | EXPLICIT |
- * DIAG_PRECOND, exact T
+ * DIAG_PRECOND, exact T or the band-limited T (not with decay CHANNEL), no residual steps
  * (neumann_order < 0), chunk 16 | 32 | 64, Dk <= 128, Dv <= 512, io fp32 | bf16; anything
  * else returns GDR_ENOTSUP (desc->impl is ignored).
  *
@@ -234,7 +240,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
  * (B H ceil(T/C) C Dk floats), with decay CHANNEL also the cumulative decays G
  * (B H ceil(T/C) C Dk floats), with wkey DIAG_PRECOND also the write keys, p_t and the
  * write-key gradients (3 B T H Dk floats) and per-chunk sums of the preconditioner's scans
- * (B H ceil(T/C) Dk floats), each section 256-byte aligned.  No HIP call. */
+ * (B H ceil(T/C) Dk floats), with neumann_order >= 0 also the whole T (B H ceil(T/C) C^2
+ * floats) and dD (B T H Dv floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 
 /* gdr_chunk_bwd's argument check on its own (no HIP call). */

@@ -278,7 +278,8 @@ def test_bwd_accepts_supported_variants(gain, decay, wkey):
     assert call_validate_bwd(d) == G.GDR_OK, G.gdr_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(neumann_order=3), dict(neumann_order=3, residual_steps=2)])
+@pytest.mark.parametrize("kw", [dict(neumann_order=3, residual_steps=2),
+                                dict(neumann_order=3, decay=G.GDR_DECAY_CHANNEL)])
 def test_bwd_rejects_unsupported_variants(kw):
     d = desc(**kw)
     ins, gr, a = bwd_args(d)

@@ -38,7 +38,7 @@ def spec(variant, **kw):
     return gs.spec(base, **over)
 
 
-def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None, pre=None):
+def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None, pre=None, band=-1):
     import torch
     import chunked_gated_delta_gdr_amd as G
     io = torch_dtype(s.dtype)
@@ -53,16 +53,20 @@ def run_bwd(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, chunk=None
         erase=dev(x.get("erase"), io), write=dev(x.get("write"), io),
         write_key=dev(x.get("write_key"), io), state_in=dev(state_in, f32),
         d_state_out=dev(cot["d_state_out"], f32) if d_state_out else None,
-        chunk=chunk or s.chunk, scale=scale, **pk)
+        chunk=chunk or s.chunk, scale=scale, neumann_order=band, **pk)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in g.items()}
 
 
 def oracle_grads(s, x, cot, *, state_in=None, d_state_out=True, scale=1.0, streams=None,
-                 checkpoint=0, pre=None):
-    g = O.recurrent_grad(x, cot["d_out"], cot["d_state_out"] if d_state_out else None,
-                         scale=scale, state0=state_in, streams=streams, checkpoint=checkpoint,
-                         precond=pre)
+                 checkpoint=0, pre=None, band=-1):
+    dST = cot["d_state_out"] if d_state_out else None
+    if band >= 0:   # the chunk form with the band-limited T
+        g = O.chunked_grad(x, cot["d_out"], dST, chunk=s.chunk, band=band, scale=scale, state0=state_in,
+                           streams=streams, precond=pre)
+    else:
+        g = O.recurrent_grad(x, cot["d_out"], dST, scale=scale, state0=state_in, streams=streams,
+                             checkpoint=checkpoint, precond=pre)
     g["dstate_in"] = g.pop("dS0")
     if "dpc_h_init" in g:
         g["dpc_h_in"] = g.pop("dpc_h_init")
@@ -296,3 +300,57 @@ def test_bwd_full_size_pdn_sampled():
         assert np.all(np.isfinite(val)), name
     ref = oracle_grads(s, x, cot, state_in=S0, streams=streams, checkpoint=64, pre=pre)
     compare(got, ref, streams=streams)
+
+
+@pytest.mark.parametrize("band", [0, 1, 3, 8])
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "plain", "explicit", "pdn_decay"])
+def test_bwd_band_fp32(variant, band):
+    """The forward with the band-limited T (neumann_order = band) differentiated: against the
+    oracle's chunk-form gradient (dA = T^T (M (.) dT_b) T^T)."""
+    s = spec(variant, T=150)
+    pre = precond_args(s) if variant.startswith("pdn") else None
+    announce(f"bwd {variant} f32 band {band} {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    got = run_bwd(s, x, cot, state_in=S0, scale=0.9, pre=pre, band=band)
+    compare(got, oracle_grads(s, x, cot, state_in=S0, scale=0.9, pre=pre, band=band))
+
+
+@pytest.mark.parametrize("chunk,T", [(16, 37), (32, 65), (64, 64)])
+def test_bwd_band_chunks(chunk, T):
+    s = spec("gdn", T=T, chunk=chunk)
+    announce(f"bwd gdn f32 band 2 chunk {chunk} T {T}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0, band=2), oracle_grads(s, x, cot, state_in=S0, band=2))
+
+
+def test_bwd_band_covering_the_chunk_is_exact():
+    """band >= C - 1 keeps all of T: the band path's gradients are the exact path's."""
+    s = spec("gdn", T=150)
+    announce("bwd gdn f32 band 63 vs exact")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    a = run_bwd(s, x, cot, state_in=S0)
+    b = run_bwd(s, x, cot, state_in=S0, band=63)
+    for name in a:
+        err = O.rel_l2(b[name], a[name])
+        print(f"  {name}: rel-L2 {err:.2e}", flush=True)
+        assert err <= TOL_F32, (name, err)
+
+
+def test_bwd_band_bf16():
+    s = spec("gdn", dtype="bf16", Dk=128, Dv=128, T=200)
+    announce(f"bwd gdn bf16 band 3 {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    compare(run_bwd(s, x, cot, state_in=S0, band=3), oracle_grads(s, x, cot, state_in=S0, band=3))
+
+
+def test_bwd_full_size_gdn_band_sampled():
+    """The gdn workload at full size with the band-limited T (N = 3): two streams against the
+    oracle's chunk-form gradient, every gradient finite everywhere."""
+    s = gs.spec("gdn")
+    streams = [(0, 0), (3, 15)]
+    announce(f"bwd gdn full size band 3 {s}, streams {streams}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s, amp=0.1)
+    got = run_bwd(s, x, cot, state_in=S0, band=3)
+    for name, val in got.items():
+        assert np.all(np.isfinite(val)), name
+    compare(got, oracle_grads(s, x, cot, state_in=S0, streams=streams, band=3), streams=streams)
