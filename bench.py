@@ -361,7 +361,7 @@ def bench_backward(args):
                        s.dtype == "bf16" else G.GDR_F32,
                        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
                        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
-                       wkey=G.GDR_WKEY_DIAG_PRECOND if pc else G.GDR_WKEY_SAME)
+                       wkey=G.GDR_WKEY_DIAG_PRECOND if pc else G.GDR_WKEY_SAME, neumann_order=args.neumann)
     ws = torch.empty(G.gdr_chunk_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] backward {args.workload}: workspace {ws.numel() / 2**20:.1f} MiB, steps {args.steps} "
@@ -370,7 +370,8 @@ def bench_backward(args):
     def step():
         return G.gdr_chunk_bwd(a["q"], a["k"], a["v"], dO, beta=a["beta"], log_alpha=a["log_alpha"],
                                erase=a["erase"], write=a["write"], write_key=a["write_key"], state_in=S0,
-                               d_state_out=dST, chunk=s.chunk, workspace=ws, stream=stream, **pcargs)
+                               d_state_out=dST, chunk=s.chunk, neumann_order=args.neumann, workspace=ws,
+                               stream=stream, **pcargs)
 
     for _ in range(args.warmup):
         g = step()
@@ -395,8 +396,12 @@ def bench_backward(args):
     parity = None
     if not args.no_parity:
         import oracle
-        ref = oracle.recurrent_grad(x, cot["d_out"], cot["d_state_out"], state0=s0, streams=[(0, 0)], precond=pre,
-                                    checkpoint=64)
+        if args.neumann >= 0:   # the band-limited T: the chunk form's own gradient
+            ref = oracle.chunked_grad(x, cot["d_out"], cot["d_state_out"], chunk=s.chunk, band=args.neumann,
+                                      state0=s0, streams=[(0, 0)], precond=pre)
+        else:
+            ref = oracle.recurrent_grad(x, cot["d_out"], cot["d_state_out"], state0=s0, streams=[(0, 0)],
+                                        precond=pre, checkpoint=64)
         parity = {"stream": "(0,0)", "tokens": s.T}
         for name in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "derase", "dwrite"):
             if name in ref:
@@ -428,7 +433,8 @@ def bench_backward(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded inputs of the workload; dO, dL/dS_T ~ N(0,1); random fp32 start state)",
         "config": {"workload": f"{args.workload} backward: B{s.B} H{s.H} T{s.T} Dk{s.Dk} Dv{s.Dv} C{s.chunk} "
-                               f"{s.dtype} in, fp32 arithmetic and gradients, gain={s.gain} decay={s.decay}",
+                               f"{s.dtype} in, fp32 arithmetic and gradients, gain={s.gain} decay={s.decay} "
+                               f"wkey={s.wkey}" + (f" band N={args.neumann}" if args.neumann >= 0 else " exact T"),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "alu", "achieved": round(af / avg_s / 1e12, 2), "peak": FP32_VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(af / avg_s / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),

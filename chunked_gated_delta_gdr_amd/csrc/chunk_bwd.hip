@@ -517,7 +517,7 @@ constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
 
 
-template <typename IO, int DK, bool CHD, bool PC>
+template <typename IO, int DK, bool CHD, bool PC, bool BAND>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   constexpr int LD = DK + 4;
   constexpr int kBV = kSwBV, kThreads = kSwThreads;
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
         const int t = tr0 + r, rr = 16 * rb + col;
         const float dd = fmaf(wd[t], a1[0][r], f.scale * a2[r]);
         dDs[t][rr] = (t < n && rr < nv) ? dd : 0.f;
-        if (a.dDw != nullptr && t < n && rr < nv) a.dDw[tok(t) * Dv + v0 + rr] = dd;   // (band-limited T)
+        if (BAND && t < n && rr < nv) a.dDw[tok(t) * Dv + v0 + rr] = dd;   // (band-limited T)
       }
     }
     __syncthreads();
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 constexpr int kCkThreads = 512;
 
 
-template <typename IO, int DK, bool CHD, bool PC>
+template <typename IO, int DK, bool CHD, bool PC, bool BAND>
 __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(DK == 64 || DK == 128, "two halves of 16-channel tiles");
   constexpr int kThreads = kCkThreads;
@@ -858,8 +858,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
   float ps[kSIt], pds[kSIt], po[4], px[4], pd[4], pv[4], pw[4], pdd[4];
   const int lt = tid >> 3, rq = 4 * (tid & 7);   // token-tile element (token lt, rows rq .. rq + 3)
   // band-limited T: the hh = 1 waves form Z = dD D^T (every tile) instead of dX D^T
-  const bool band = f.N >= 0;
-  const float *dDsrc = band ? a.dDw : a.dX;   // (a valid source either way: the load is unconditional)
+  constexpr bool band = BAND;
   auto vload = [&](int vb) {
 #pragma unroll
     for (int it = 0; it < kSIt; ++it) {
@@ -875,7 +874,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       po[u] = ld_f(dout, idx);
       px[u] = a.dX[idx];
       pd[u] = a.D[idx];
-      pdd[u] = dDsrc[idx];
+      if constexpr (BAND) pdd[u] = a.dDw[idx];
       pv[u] = ld_f(v, idx);
       pw[u] = f.gain == GDR_GAIN_SCALAR ? f.beta[tok(tt)] : ld_f(wr, idx);
     }
@@ -901,7 +900,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
       sm.A.dOT[r][lt] = in ? po[u] : 0.f;
       sm.A.dXT[r][lt] = gx;
       sm.A.DT[r][lt] = in ? pd[u] : 0.f;
-      sm.A.dDT[r][lt] = in ? pdd[u] : 0.f;
+      if constexpr (BAND) sm.A.dDT[r][lt] = in ? pdd[u] : 0.f;
       if (in) {   // dv (and dwrite) are elementwise in dX
         const long long idx = tok(lt) * Dv + vb + r;
         a.dv[idx] = pw[u] * gx;
@@ -1145,7 +1144,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     // inverse of T_b, the products as 16 x 16 tiles on the matrix cores (LDS scratch over the
     // key tiles, which are loaded after it)
     float4v dlb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (band) {
+    if constexpr (BAND) {
       auto &Bd = sm.Bd;
       __syncthreads();   // the value-loop tiles are dead
       if (hh == 1) {
@@ -1258,7 +1257,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           sm.B.dL[t][j] = (j < t && t < n) ? -MPL[jb][r] * dec : 0.f;
       }
     }
-    if (band) {   // dL' = dL (.) Gamma below the diagonal, from the band block's tiles
+    if constexpr (BAND) {   // dL' = dL (.) Gamma below the diagonal, from the band block's tiles
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = wave + 8 * u2;
@@ -1570,6 +1569,21 @@ void launch_pc(const BwdArgs &a, F &&fn) {
     fn(std::false_type{});
 }
 
+// launch_pc with a second flag, the band-limited T (never with the per-channel decay: the host
+// rejects that combination, and no such kernel is built)
+template <bool CHD, typename F>
+void launch_var(const BwdArgs &a, F &&fn) {
+  launch_pc(a, [&](auto pc) {
+    if constexpr (!CHD) {
+      if (a.f.N >= 0) {
+        fn(pc, std::true_type{});
+        return;
+      }
+    }
+    fn(pc, std::false_type{});
+  });
+}
+
 template <typename IO>
 hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   if (a.NC == 0) return hipSuccess;
@@ -1614,19 +1628,19 @@ hipError_t sweep_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 32) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
   } else {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
@@ -1638,14 +1652,14 @@ hipError_t chunk_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 64) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, true, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kCkThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, false, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kCkThreads), 0, s, a); });
   } else {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, true, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kCkThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, false, decltype(pc)::value>), grid, dim3(kCkThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_chunk_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kCkThreads), 0, s, a); });
   }
   return hipGetLastError();
 }

@@ -232,6 +232,9 @@ def test_bwd_workspace_size_formula(T, C, decay, wkey):
     if wkey == G.GDR_WKEY_DIAG_PRECOND:   # write keys, p_t, write-key gradients, chunk sums
         want += 3 * _al(B * T * H * Dk * 4) + _al(B * H * NC * Dk * 4)
     assert G.gdr_chunk_bwd_workspace_size(d) == want
+    # the band-limited T adds the whole T and dD
+    band = want + _al(B * H * NC * C * C * 4) + _al(B * T * H * Dv * 4)
+    assert G.gdr_chunk_bwd_workspace_size(desc(T=T, chunk=C, decay=decay, wkey=wkey, neumann_order=3)) == band
     assert G.gdr_chunk_bwd_workspace_size(desc(chunk=48)) == 0
 
 
