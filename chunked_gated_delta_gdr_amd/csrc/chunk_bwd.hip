@@ -21,7 +21,10 @@
 // U = T V'), the state pass (sequential over chunks, per value tile: D = U - W S^T and the
 // state at every chunk start), the reverse sweep (sequential over chunks, per value tile,
 // last to first: carries dS, emits dX and the gradient at each chunk's end) and the
-// per-chunk pass (parallel over chunks; everything else).
+// per-chunk pass (parallel over chunks; everything else).  Variants, each a compile-time
+// flag of the kernels it touches: the per-channel decay (CHD), the preconditioned write key
+// (PC: two scans per channel before and after the four kernels) and the band-limited T
+// (BAND: dL = -T^T (M (.) dD X^T) T^T in place of -dX D^T).
 #include <type_traits>
 
 #include "common.h"
@@ -769,7 +772,8 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 // and B[l / 16][l % 16], and holds D[4 (l / 16) + r][l % 16], r < 4).  Wave w owns token
 // block tb = w % 4 (16 tokens) and channel half hh = w / 4: the 16 x 16 tiles of dQ, dE, dR
 // at (tb, channel tiles of that half); the half-0 waves also own the tiles of dO D^T in row
-// block tb (on and below the diagonal), the half-1 waves those of dX D^T.
+// block tb (on and below the diagonal), the half-1 waves those of dX D^T (with the band-limited
+// T (BAND): of dD D^T, every tile, for the band block that replaces -dX D^T).
 // With per-channel decay (CHD) the wave's channel tiles are two in each 64-channel half, and
 // the key products run over the halves in turn (Q, E, R, G of one half in LDS): the pairwise
 // decay 2^(G_ic - G_jc) sits inside the sums over tokens, split at a reference row for the
