@@ -10,6 +10,12 @@ namespace chd {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f4v mma(float a, float b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+
+// 2^x by one v_exp_f32: for the decay factors, whose exponents are <= 0 (or discarded), a
+// result below 2^-126 is flushed where exp2f would go on into denormals (then both are
+// negligible against the O(1) terms they are summed with); exp2f's range handling costs five
+// more instructions per call, and these factors are most of the per-channel decay's work
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ void fma4(float &acc, const float4 &x, const float4 &y) {
   acc = fmaf(x.x, y.x, acc);
@@ -52,10 +58,10 @@ __device__ __forceinline__ void gram(const float (*Xs)[LD], const float (*Rs)[LD
         const int kk = ks + 4 * kq;
         const float4 x = ld4(&Xs[i][kk]), gx = ld4(&Gs[i][kk]), gr = ld4(&Gs[ref][kk]);
         const float4 r = ld4(&Rs[j][kk]), gy = ld4(&Gs[j][kk]);
-        ap[0] = mma(x.x * exp2f(gx.x - gr.x), r.x * exp2f(gr.x - gy.x), ap[0]);
-        ap[1] = mma(x.y * exp2f(gx.y - gr.y), r.y * exp2f(gr.y - gy.y), ap[1]);
-        ap[0] = mma(x.z * exp2f(gx.z - gr.z), r.z * exp2f(gr.z - gy.z), ap[0]);
-        ap[1] = mma(x.w * exp2f(gx.w - gr.w), r.w * exp2f(gr.w - gy.w), ap[1]);
+        ap[0] = mma(x.x * ex2(gx.x - gr.x), r.x * ex2(gr.x - gy.x), ap[0]);
+        ap[1] = mma(x.y * ex2(gx.y - gr.y), r.y * ex2(gr.y - gy.y), ap[1]);
+        ap[0] = mma(x.z * ex2(gx.z - gr.z), r.z * ex2(gr.z - gy.z), ap[0]);
+        ap[1] = mma(x.w * ex2(gx.w - gr.w), r.w * ex2(gr.w - gy.w), ap[1]);
       }
       const f4v acc = ap[0] + ap[1];
 #pragma unroll
@@ -83,8 +89,8 @@ __device__ __forceinline__ void gram(const float (*Xs)[LD], const float (*Rs)[LD
             if (u == w) {
               fma4(acc[u][w], x[u], r);
             } else {
-              const float4 dd = make_float4(x[u].x * exp2f(gi[u].x - gj.x), x[u].y * exp2f(gi[u].y - gj.y),
-                                            x[u].z * exp2f(gi[u].z - gj.z), x[u].w * exp2f(gi[u].w - gj.w));
+              const float4 dd = make_float4(x[u].x * ex2(gi[u].x - gj.x), x[u].y * ex2(gi[u].y - gj.y),
+                                            x[u].z * ex2(gi[u].z - gj.z), x[u].w * ex2(gi[u].w - gj.w));
               fma4(acc[u][w], dd, r);
             }
           }
@@ -120,14 +126,14 @@ __device__ __forceinline__ void gram(const float (*Xs)[LD], const float (*Rs)[LD
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float4 xv = ld4(&Xs[i0 + u][c]), gv = ld4(&Gs[i0 + u][c]);
-          x[u] = make_float4(xv.x * exp2f(gv.x - gr.x), xv.y * exp2f(gv.y - gr.y), xv.z * exp2f(gv.z - gr.z),
-                             xv.w * exp2f(gv.w - gr.w));
+          x[u] = make_float4(xv.x * ex2(gv.x - gr.x), xv.y * ex2(gv.y - gr.y), xv.z * ex2(gv.z - gr.z),
+                             xv.w * ex2(gv.w - gr.w));
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float4 rv = ld4(&Rs[j0 + w][c]), gv = ld4(&Gs[j0 + w][c]);
-          const float4 r = make_float4(rv.x * exp2f(gr.x - gv.x), rv.y * exp2f(gr.y - gv.y), rv.z * exp2f(gr.z - gv.z),
-                                       rv.w * exp2f(gr.w - gv.w));
+          const float4 r = make_float4(rv.x * ex2(gr.x - gv.x), rv.y * ex2(gr.y - gv.y), rv.z * ex2(gr.z - gv.z),
+                                       rv.w * ex2(gr.w - gv.w));
 #pragma unroll
           for (int u = 0; u < 4; ++u) fma4(acc[u][w], x[u], r);
         }

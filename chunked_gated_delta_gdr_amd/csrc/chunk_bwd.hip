@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
   auto store_w = [&]() {   // W = T (e^g (.) E), [B, H, NC, C, Dk]
     float4v acc[MT];
     if constexpr (CHD)
-      tri_product(Es, [&](int s, int c) { return exp2f(Xs[s][c]); }, acc);
+      tri_product(Es, [&](int s, int c) { return chd::ex2(Xs[s][c]); }, acc);
     else
       tri_product(Es, [&](int s, int) { return eg[s]; }, acc);
     float *Wc = a.Ww + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
@@ -455,12 +455,12 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       const bool in = t < n && c < Dk;
       Ws[t][c] = in ? pw[it] : 0.f;
       if constexpr (CHD)
-        Rs[t][c] = in ? pr[it] * exp2f(pgn - pg[it]) : 0.f;
+        Rs[t][c] = in ? pr[it] * chd::ex2(pgn - pg[it]) : 0.f;
       else
         Rs[t][c] = in ? pr[it] : 0.f;
     }
     if constexpr (CHD) {
-      if (tid < DK) gcn[tid] = exp2f(pgn);
+      if (tid < DK) gcn[tid] = chd::ex2(pgn);
     }
 #pragma unroll
     for (int it = 0; it < kUIt; ++it) {
@@ -662,15 +662,15 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
       const bool in = t < n && c < Dk;
       if constexpr (CHD) {
-        Ks[t][c] = in ? xr[it] * exp2f(xgn - xgv[it]) : 0.f;
-        Es[t][c] = in ? xg[it] * xk[it] * exp2f(xgv[it]) : 0.f;
+        Ks[t][c] = in ? xr[it] * chd::ex2(xgn - xgv[it]) : 0.f;
+        Es[t][c] = in ? xg[it] * xk[it] * chd::ex2(xgv[it]) : 0.f;
       } else {
         Ks[t][c] = in ? xr[it] : 0.f;
         Es[t][c] = in ? xg[it] * xk[it] : 0.f;
       }
     }
     if constexpr (CHD) {
-      if (tid < DK) gcn[tid] = exp2f(xgn);
+      if (tid < DK) gcn[tid] = chd::ex2(xgn);
     }
 #pragma unroll
     for (int it = 0; it < kCC; ++it) {
@@ -725,7 +725,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < kLoadIt; ++it) {
       const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      Ks[t][c] = (t < n && c < Dk) ? (CHD ? xq[it] * exp2f(xgv[it]) : xq[it]) : 0.f;
+      Ks[t][c] = (t < n && c < Dk) ? (CHD ? xq[it] * chd::ex2(xgv[it]) : xq[it]) : 0.f;
     }
     if constexpr (CHD) {
       if (ci > 0) gload(ci - 1);   // this chunk's G is no longer needed
@@ -1004,10 +1004,10 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         float lam = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = exp2f(gt[r]);
+          const float e = chd::ex2(gt[r]);
           AQ[m][r] *= f.scale * e;
           AE[m][r] *= -e;
-          AR[m][r] *= exp2f(gn - gt[r]);
+          AR[m][r] *= chd::ex2(gn - gt[r]);
           lam = fmaf(B.R[tr0 + r][cl], AR[m][r], lam);
         }
         // dQ += dM R, dE += dL' R with 2^(G_i - G_j): the blocks before block tb through their
@@ -1019,13 +1019,13 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           #pragma unroll 1
           for (int j0 = 0; j0 < 16 * tb; j0 += 4) {
             const int jr = j0 + kq;
-            const float br = B.R[jr][cl] * exp2f(gr - B.G[jr][cl]);
+            const float br = B.R[jr][cl] * chd::ex2(gr - B.G[jr][cl]);
             tq = mfma4(B.dM[16 * tb + col][jr], br, tq);
             te = mfma4(B.dL[16 * tb + col][jr], br, te);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float sc = exp2f(gt[r] - gr);
+            const float sc = chd::ex2(gt[r] - gr);
             AQ[m][r] = fmaf(sc, tq[r], AQ[m][r]);
             AE[m][r] = fmaf(sc, te[r], AE[m][r]);
           }
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int i = tr0 + r;
             // (the exponent above the diagonal may overflow; it is discarded)
-            const float w = j <= i ? rj * exp2f(gt[r] - gj) : 0.f;
+            const float w = j <= i ? rj * chd::ex2(gt[r] - gj) : 0.f;
             AQ[m][r] = fmaf(B.dM[i][j], w, AQ[m][r]);
             AE[m][r] = fmaf(B.dL[i][j], w, AE[m][r]);
           }
@@ -1052,12 +1052,12 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
           #pragma unroll 1
           for (int i0 = 16 * (tb + 1); i0 < n; i0 += 4) {
             const int ir = i0 + kq;
-            const float sc = exp2f(B.G[ir][cl] - gr);
+            const float sc = chd::ex2(B.G[ir][cl] - gr);
             tr = mfma4(B.dM[ir][16 * tb + col], B.Q[ir][cl] * sc, tr);
             tr = mfma4(B.dL[ir][16 * tb + col], B.E[ir][cl] * sc, tr);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) AR[m][r] = fmaf(exp2f(gr - gt[r]), tr[r], AR[m][r]);
+          for (int r = 0; r < 4; ++r) AR[m][r] = fmaf(chd::ex2(gr - gt[r]), tr[r], AR[m][r]);
         }
         #pragma unroll 2
         for (int ii = 0; ii < 16; ++ii) {
@@ -1066,7 +1066,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = tr0 + r;
-            const float w = i >= j ? exp2f(gi - gt[r]) : 0.f;
+            const float w = i >= j ? chd::ex2(gi - gt[r]) : 0.f;
             AR[m][r] = fmaf(fmaf(B.dM[i][j], qi, B.dL[i][j] * ei), w, AR[m][r]);
           }
         }
@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
         for (int p = 0; p < kThreads / DK; ++p) sdc += sdp[p * DK + min(c, DK - 1)];
         // the end-of-chunk terms (state decay and 2^(G_n - G) R) enter dg at token n - 1,
         // so every earlier token's sum holds them
-        const float tail = above + later + exp2f(gn) * sdc + lamc;
+        const float tail = above + later + chd::ex2(gn) * sdc + lamc;
         // chain rule to the variant's inputs, stores
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

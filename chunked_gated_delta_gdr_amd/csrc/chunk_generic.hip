@@ -280,10 +280,10 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         for (int ks = 0; ks < DK; ks += 16) {
           const int kk = ks + 4 * kq;
           const float4 y = ld4(&Y[t][kk]), g = ld4(&Gs[t][kk]), z = ld4(&Ss[16 * rb + col][kk]);
-          acc = mfma4(y.x * exp2f(g.x), z.x, acc);
-          a1 = mfma4(y.y * exp2f(g.y), z.y, a1);
-          acc = mfma4(y.z * exp2f(g.z), z.z, acc);
-          a1 = mfma4(y.w * exp2f(g.w), z.w, a1);
+          acc = mfma4(y.x * chd::ex2(g.x), z.x, acc);
+          a1 = mfma4(y.y * chd::ex2(g.y), z.y, a1);
+          acc = mfma4(y.z * chd::ex2(g.z), z.z, acc);
+          a1 = mfma4(y.w * chd::ex2(g.w), z.w, a1);
         }
         acc += a1;
       } else {
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         const int rbs = u / NCB, cbs = u % NCB, c = 16 * cbs + col;
         float4v acc = Sacc[m], acc2 = {0.f, 0.f, 0.f, 0.f};   // two independent chains
         if constexpr (CHD) {
-          acc *= exp2f(Gs[n - 1][c]);
+          acc *= chd::ex2(Gs[n - 1][c]);
         } else {
           acc *= gl;
         }
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
             const int t = t0 + 4 * p + kq;
             float am = Dl[t][16 * rbs + col], br = Rs[t][c];
             if constexpr (CHD)
-              br *= exp2f(Gs[n - 1][c] - Gs[t][c]);
+              br *= chd::ex2(Gs[n - 1][c] - Gs[t][c]);
             else
               am *= wd[t];
             if (p == 0)
