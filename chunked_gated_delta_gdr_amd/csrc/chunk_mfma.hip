@@ -823,17 +823,30 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         const float lr = quadf<0xff>(rm), l0 = quadf<0xff>(a0), l1 = quadf<0xff>(a1);
         uint16_t *Rn = sm.r[nxt];
         float4 ic4;
+        // (the key is rounded to bf16 next, so the hardware reciprocal is accurate enough)
+        if (m == 16) {   // no masking: a compare and four selects fewer per token
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if ((i & 3) == 0) ic4 = ld4f(&sm.ic[nxt][s0 + i]);
-          const float icv = (&ic4.x)[i & 3];
-          const bool on = i < m;
-          h0v = on ? fmaf(a.rho, h0v, k0[i] * k0[i]) : h0v;
-          h1v = on ? fmaf(a.rho, h1v, k1[i] * k1[i]) : h1v;
-          // (the key is rounded to bf16 next, so the hardware reciprocal is accurate enough)
-          const float u0 = k0[i] * __builtin_amdgcn_rcpf(fmaf(h0v, icv, a.eps));
-          const float u1 = k1[i] * __builtin_amdgcn_rcpf(fmaf(h1v, icv, a.eps));
-          *reinterpret_cast<uint32_t *>(Rn + sw128(s0 + i, cp)) = f32x2_to_bf16x2_bits(on ? u0 : 0.f, on ? u1 : 0.f);
+          for (int i = 0; i < 16; ++i) {
+            if ((i & 3) == 0) ic4 = ld4f(&sm.ic[nxt][s0 + i]);
+            const float icv = (&ic4.x)[i & 3];
+            h0v = fmaf(a.rho, h0v, k0[i] * k0[i]);
+            h1v = fmaf(a.rho, h1v, k1[i] * k1[i]);
+            const float u0 = k0[i] * __builtin_amdgcn_rcpf(fmaf(h0v, icv, a.eps));
+            const float u1 = k1[i] * __builtin_amdgcn_rcpf(fmaf(h1v, icv, a.eps));
+            *reinterpret_cast<uint32_t *>(Rn + sw128(s0 + i, cp)) = f32x2_to_bf16x2_bits(u0, u1);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if ((i & 3) == 0) ic4 = ld4f(&sm.ic[nxt][s0 + i]);
+            const float icv = (&ic4.x)[i & 3];
+            const bool on = i < m;
+            h0v = on ? fmaf(a.rho, h0v, k0[i] * k0[i]) : h0v;
+            h1v = on ? fmaf(a.rho, h1v, k1[i] * k1[i]) : h1v;
+            const float u0 = k0[i] * __builtin_amdgcn_rcpf(fmaf(h0v, icv, a.eps));
+            const float u1 = k1[i] * __builtin_amdgcn_rcpf(fmaf(h1v, icv, a.eps));
+            *reinterpret_cast<uint32_t *>(Rn + sw128(s0 + i, cp)) = f32x2_to_bf16x2_bits(on ? u0 : 0.f, on ? u1 : 0.f);
+          }
         }
         hc0 = fmaf(lr, hc0, l0);
         hc1 = fmaf(lr, hc1, l1);
