@@ -27,6 +27,8 @@
 // [l / 16] and B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16], r < 4).  The tiles of
 // X, D and O are spread one per wave; the ten C x C tiles on and below the diagonal two per
 // wave at most.
+#include <cstdlib>
+
 #include "common.h"
 #include "tri_blocks.h"
 #include "chd_gram.h"
@@ -107,17 +109,24 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   const bool xwave = wave < NXT;        // owns the (tb, rb) tile of X, D and O
   const int tb = wave & 3, rb = wave >> 2;
 
+  // With per-channel decays (the cumulative decays take a 64 x Dk tile) LDS is tight: D
+  // overwrites X once every read of X is done, the inverse's scratch lives in the erase-key
+  // tile (dead between X and the queries) and the preconditioner's bias corrections in Zb.
+  constexpr bool kTight = CHD;
   __shared__ __align__(16) float Rs[kCMax][LD];     // write keys r
   __shared__ __align__(16) float Xs[kCMax][LD];     // erase keys e, then queries q
   __shared__ float LP[kCMax][kCMax + 1];            // L (then E of the residual), then P
   __shared__ __align__(16) float Tm[kCMax][kCMax + 4];   // T, row-major
-  __shared__ __align__(16) float Zs[32][36];             // block products in flight
+  __shared__ __align__(16) float Zs_[kTight ? 1 : 32][36];            // block products in flight
   __shared__ __align__(16) float Zb[CHD ? 1 : kCMax][kCMax + 4];   // residual-correction series
   __shared__ __align__(16) float Gs[CHD ? kCMax : 1][CHD ? LD : 4];  // cumulative log2 decays
   __shared__ __align__(16) float Ss[BV][LD];        // mirror of the state tile
   __shared__ __align__(16) float Xv[kCMax][BV];     // X
-  __shared__ __align__(16) float Dl[kCMax][BV];     // D
+  __shared__ __align__(16) float Dl_[kTight ? 1 : kCMax][BV];   // D
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
+  float(*const Zs)[36] = kTight ? reinterpret_cast<float(*)[36]>(&Xs[0][0]) : Zs_;
+  float(*const Dl)[BV] = kTight ? Xv : Dl_;
+  static_assert(!kTight || 32 * 36 <= kCMax * LD, "the inverse's scratch must fit the key tile");
 
   const long long sh = static_cast<long long>(b) * H + h;  // (b, h) index
   // state tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
       // u = k / (h / (1 - rho^t) + eps), h_t = rho h_{t-1} + k_t^2.  The bias corrections of the
       // chunk's tokens first (one thread each), then channel `tid` walks the chunk: its keys
       // are read up front, so only the accumulator chain is serial.
-      float *icorr = &Zs[0][0];   // (free until the inverse is built)
+      float *icorr = kTight ? &Zb[0][0] : &Zs[0][0];   // (free until the inverse is built)
       if (tid < kCMax) {
         const float tg = static_cast<float>(a.t0 + c0 + tid + 1);
         icorr[tid] = 1.f / -expm1f(tg * a.log_rho);   // 1 / (1 - rho^t)
@@ -386,16 +395,25 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // D = T X (T lower triangular: the sum ends with the row block)
+    float4v dacc = {0.f, 0.f, 0.f, 0.f};
     if (xwave) {
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
       for (int s0 = 0; s0 < 16 * (tb + 1); s0 += 4)
-        acc = mfma4(Tm[16 * tb + col][s0 + kq], Xv[s0 + kq][16 * rb + col], acc);
+        dacc = mfma4(Tm[16 * tb + col][s0 + kq], Xv[s0 + kq][16 * rb + col], dacc);
+      if constexpr (!kTight) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Dl[16 * tb + 4 * kq + r][16 * rb + col] = acc[r];
+        for (int r = 0; r < 4; ++r) Dl[16 * tb + 4 * kq + r][16 * rb + col] = dacc[r];
+      }
     }
     // P (lower incl. diagonal; L is no longer needed)
     gram(true);
     __syncthreads();
+    if constexpr (kTight) {   // every read of X is done: D takes its place
+      if (xwave) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Dl[16 * tb + 4 * kq + r][16 * rb + col] = dacc[r];
+      }
+      __syncthreads();
+    }
     // O = scale ((e^g (.) Q) S^T + P D)
     if (xwave) {
       float4v acc;
@@ -474,11 +492,19 @@ hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// With per-channel decays the 64 x Dk tile of cumulative decays takes the LDS of 16 state rows,
-// so those workgroups own 16 value rows; the others own 32.
+// Workgroups own 32 value rows.  With per-channel decays the Gram tiles (the larger part of a
+// chunk) do not depend on the value tile, so 32 rows halve their total against 16; 16 rows
+// are kept only where 32 would leave CUs without a workgroup.  GDR_GENERIC_BV=16|32
+// overrides that choice (tuning and tests).
 template <typename IO>
 hipError_t launch_io(const ChunkArgs &a, hipStream_t s) {
-  return a.decay == GDR_DECAY_CHANNEL ? launch_dk<IO, true, 16>(a, s) : launch_dk<IO, false, 32>(a, s);
+  if (a.decay != GDR_DECAY_CHANNEL) return launch_dk<IO, false, 32>(a, s);
+  const char *e = getenv("GDR_GENERIC_BV");
+  const int forced = e == nullptr ? 0 : atoi(e);
+  const bool wide = forced == 16 || forced == 32
+                        ? forced == 32
+                        : static_cast<long long>(a.B) * a.H * ((a.Dv + 31) / 32) >= 256;
+  return wide ? launch_dk<IO, true, 32>(a, s) : launch_dk<IO, true, 16>(a, s);
 }
 
 }  // namespace

@@ -411,6 +411,31 @@ def test_long_decode_batch64():
 # The bf16 matrix-core kernel, forced (impl="mfma")
 # ---------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("variant", ["kda", "kda_gdn2", "kda_pdn"])
+@pytest.mark.parametrize("BV", [16, 32])
+@pytest.mark.parametrize("chunk,Dk,Dv,T", [(64, 128, 48, 150), (16, 32, 20, 37), (32, 64, 96, 200)])
+def test_kda_value_tiles_fp32(variant, BV, chunk, Dk, Dv, T, monkeypatch):
+    """Per-channel decay with value tiles of 16 and 32 state rows (forced through
+    GDR_GENERIC_BV; ragged last tiles): fp32 within 1e-4 of the recurrence."""
+    monkeypatch.setenv("GDR_GENERIC_BV", str(BV))
+    s = small(variant, "f32", Dk=Dk, Dv=Dv, T=T, chunk=chunk)
+    announce(f"{variant} f32 BV={BV} C={chunk} Dk={Dk} Dv={Dv} T={T}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(8)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    pc = precond_opts(s)
+    h_in = None
+    if pc is not None:
+        h_in = (1.0 + rng.random((s.B, s.H, s.Dk))).astype(np.float32)
+        pc = dict(pc, h_init=h_in.astype(np.float64), t0=5)
+    o_ref, S_ref, h_ref = O.recurrent(x, state0=S0.astype(np.float64), precond=pc, scale=0.7)
+    o, S, h = run_chunk(s, x, state_in=S0, pc_h_in=h_in, pc_t0=5 if pc else 0, scale=0.7)
+    assert O.rel_l2(host(o), o_ref) <= TOL_F32
+    assert O.rel_l2(host(S), S_ref) <= TOL_F32
+    if pc is not None:
+        assert O.rel_l2(host(h), h_ref) <= 1e-6
+
+
 MFMA_VARIANTS = ["gdn", "plain", "gdn2", "gdn2_decay", "pdn", "pdn_decay", "explicit"]
 
 
