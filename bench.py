@@ -576,7 +576,8 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-        "traffic": traffic_from_profile(args.workload, impl_name),
+        # (the counters are taken on the exact-T configuration of the workload)
+        "traffic": traffic_from_profile(args.workload, impl_name) if args.neumann < 0 else None,
         "kernel": f"gdr_chunk_fwd/{impl_name}",
         "alg_bytes_per_launch": ab,
         "avg_launch_us": round(avg_launch_s * 1e6, 2),

@@ -101,7 +101,15 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   IO *__restrict__ out = static_cast<IO *>(a.out);
 
   const int tid = threadIdx.x;
-  const int vt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware tile order: workgroups are dealt to the 8 XCDs in turn, so consecutive logical
+  // tiles (the value tiles of one head, which read the same keys, queries and decays) get ids
+  // 8 apart and share an XCD's L2
+  const int nvt = static_cast<int>(gridDim.x);
+  const int G = nvt * static_cast<int>(gridDim.y * gridDim.z);
+  const int bid = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int vt = logical % nvt, h = (logical / nvt) % static_cast<int>(gridDim.y),
+            b = logical / nvt / static_cast<int>(gridDim.y);
   const int v0 = vt * BV;
   const int nv = min(BV, a.Dv - v0);
   const int Dk = a.Dk, Dv = a.Dv, H = a.H, T = a.T;
