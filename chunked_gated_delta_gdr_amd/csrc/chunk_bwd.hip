@@ -34,6 +34,19 @@
 namespace gdr {
 namespace {
 
+// XCD-aware order of a (value tile, head, batch) grid: workgroups are dealt to the 8 XCDs in
+// turn, so consecutive logical tiles (the value tiles of one head, which read the same keys
+// and gates) get ids 8 apart and share an XCD's L2
+__device__ __forceinline__ void xcd_tile(int &vt, int &h, int &b) {
+  const int nvt = static_cast<int>(gridDim.x), nh = static_cast<int>(gridDim.y);
+  const int G = nvt * nh * static_cast<int>(gridDim.z);
+  const int bid = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  vt = logical % nvt;
+  h = (logical / nvt) % nh;
+  b = logical / nvt / nh;
+}
+
 constexpr int kCMax = 64;   // largest chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -365,7 +378,8 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   const IO *__restrict__ wk = static_cast<const IO *>(f.write_key);
 
   const int tid = threadIdx.x;
-  const int vt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int vt, h, b;
+  xcd_tile(vt, h, b);
   const int v0 = vt * kBV;
   const int nv = min(kBV, f.Dv - v0);
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
@@ -536,7 +550,8 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   const IO *__restrict__ dout = static_cast<const IO *>(a.dout);
 
   const int tid = threadIdx.x;
-  const int vt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int vt, h, b;
+  xcd_tile(vt, h, b);
   const int v0 = vt * kBV;
   const int nv = min(kBV, f.Dv - v0);
   const int Dk = f.Dk, Dv = f.Dv, H = f.H, T = f.T, C = f.C;
