@@ -9,9 +9,14 @@ Dk = Dv = 128, bf16 inputs, fp32 state, chunk 64.  Prints ONE JSON line.
                     [--neumann N [--residual S]] [--impl auto|generic|mfma] [--no-cpu-baseline]
     python bench.py --bwd [--workload gdn|gdn2|plain|kda|pdn]   # gdr_chunk_bwd instead
 
-Counter helpers (used to produce the committed traffic summaries under profiles/):
+With --neumann N (and --residual S) the line also carries `exact_vs_approx`: the rel-L2 between
+the exact-T output and the band-limited (residual-corrected) one, from the GPU (every stream, and
+stream (0,0)) and from the fp64 oracle (stream (0,0), every token).
+
+Counter helpers (used to produce the committed counter summaries under profiles/):
     python bench.py --copy-probe-mb 256          # calibration copy of known size
     python bench.py --workload gdn --copy-probe-mb 256 --traffic-summary F.csv W.csv CF.csv CW.csv
+    python bench.py --workload gdn --mfma-summary PMC.csv   # matrix-core counters of the kernel
 """
 from __future__ import annotations
 
@@ -73,6 +78,53 @@ def source_sha(impl: str) -> str:
     return h.hexdigest()[:16]
 
 
+def mfma_counter_file(workload: str, impl: str) -> str:
+    return f"chunk_fwd_{impl}_{workload}_mfma_counters.json"
+
+
+def mfma_counters_from_profile(workload: str, impl: str):
+    """The committed matrix-core counter summary of the kernel, if it was taken on the current
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", mfma_counter_file(workload, impl))
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    return rec if rec.get("source_sha") == source_sha(impl) else None
+
+
+def mfma_summary(args):
+    """Writes profiles/chunk_fwd_<impl>_<workload>_mfma_counters.json from a rocprofv3 --pmc CSV
+    holding SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 matrix operations in units of 512 FLOPs),
+    SQ_VALU_MFMA_BUSY_CYCLES (matrix-core busy cycles, summed over SIMDs), SQ_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE (GPU active cycles) and SQ_LDS_BANK_CONFLICT."""
+    import statistics
+    kern = KERNEL_SYMBOLS[args.impl_name]
+    names = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+             "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_WAVES"]
+    med = {}
+    for n in names:
+        try:
+            med[n] = statistics.median(_counter_per_dispatch(args.mfma_summary, n, kern))
+        except SystemExit:
+            pass
+    s = __import__("gdr_synth").spec(args.workload)
+    rec = {
+        "kernel": f"gdr_chunk_fwd/{args.impl_name}", "workload": args.workload,
+        "source_sha": source_sha(args.impl_name),
+        "counters_median_per_dispatch": med,
+        "mfma_bf16_flop_per_dispatch": med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512.0,
+        "alg_flop_per_dispatch": alg_flops(s),
+        "cu": 256, "simd_per_cu": 4,
+    }
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        rec["mfma_busy_frac"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * 256 * 4)
+    out = os.path.join(ROOT, "profiles", mfma_counter_file(args.workload, args.impl_name))
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def traffic_file(workload: str, impl: str) -> str:
     return "step_decode_traffic.json" if impl == "step" else f"chunk_fwd_{impl}_{workload}_traffic.json"
 
@@ -107,14 +159,34 @@ def _cpu_task(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(s, x, tokens: int, n_streams: int):
-    import multiprocessing as mp
-    import numpy as np
+def host_cpu():
+    """(CPU model from /proc/cpuinfo, logical cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    workers = max(1, min(16, cores, n_streams))
+    return model, cores
+
+
+def cpu_baseline(s, x, tokens: int, n_streams: int, min_cpu_s: float = 10.0):
+    """The fp64 oracle on every sampled stream, one stream per task, over every core this
+    process may use, capped by OMP_NUM_THREADS when the environment sets it (a GPU machine's share
+    of its host), and by the number of streams.  Passes over the sample repeat until at least
+    `min_cpu_s` of CPU work has been timed."""
+    import multiprocessing as mp
+    import numpy as np
+    model, cores = host_cpu()
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    workers = max(1, min(cores, n_streams, share if share > 0 else cores))
     streams = [(b, h) for b in range(s.B) for h in range(s.H)][:n_streams]
     pre = None
     if s.wkey == "precond":
@@ -128,18 +200,25 @@ def cpu_baseline(s, x, tokens: int, n_streams: int):
     with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
         pool.map(_cpu_task, [(
             {k: (v[:4] if v is not None else None) for k, v in t[0].items()}, t[1]) for t in tasks[:workers]])
-        t0 = time.perf_counter()                # (the call above warmed the workers' imports)
-        cpu_s = sum(pool.map(_cpu_task, tasks, chunksize=1))
-        wall = time.perf_counter() - t0
-    token_heads = len(streams) * tokens
+        cpu_s, wall, passes = 0.0, 0.0, 0
+        while cpu_s < min_cpu_s and passes < 8:   # (the call above warmed the workers' imports)
+            t0 = time.perf_counter()
+            cpu_s += sum(pool.map(_cpu_task, tasks, chunksize=1))
+            wall += time.perf_counter() - t0
+            passes += 1
+    token_heads = len(streams) * tokens * passes
     return {
         "value": token_heads / s.H / wall,
         "unit": "tokens/s",
         "cores": workers,
+        "host_cores": cores,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"fp64 token-by-token oracle on {len(streams)} of {s.B * s.H} (batch, head) streams x "
-                  f"{tokens} of {s.T} tokens ({token_heads} token-heads, {wall:.2f} s wall on {workers} "
-                  f"processes, {cpu_s:.1f} s of CPU work); tokens/s = token-heads / H / wall",
+                  f"{tokens} of {s.T} tokens, {passes} pass(es) ({token_heads} token-heads, {wall:.2f} s wall "
+                  f"on {workers} processes of the {cores} logical cores available"
+                  f"{' (OMP_NUM_THREADS=' + str(share) + ' caps the pool)' if 0 < share < cores else ''}, "
+                  f"{cpu_s:.1f} s of CPU work); tokens/s = token-heads / H / wall",
     }
 
 
@@ -468,9 +547,14 @@ def main():
                                                            "COPY_WRITE_CSV"),
                     help="write the traffic summary of --workload from rocprofv3 counter CSVs")
     ap.add_argument("--impl-name", default="mfma", choices=["mfma", "generic", "step"])
+    ap.add_argument("--mfma-summary", metavar="PMC_CSV",
+                    help="write the matrix-core counter summary of --workload from a rocprofv3 counter CSV")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args)
+        return
+    if args.mfma_summary:
+        mfma_summary(args)
         return
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
@@ -584,6 +668,13 @@ def main():
         "mfma_bf16_frac": round(af / avg_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "alg_gflop_per_launch": round(af / 1e9, 3),
     }
+    mc = mfma_counters_from_profile(args.workload, impl_name) if args.neumann < 0 and args.residual == 0 else None
+    if mc is not None:
+        # the matrix-core work the counters saw per dispatch (dense tiles, padding and the split
+        # products included), over this run's launch time
+        roofline["mfma_bf16_frac_counters"] = round(mc["mfma_bf16_flop_per_dispatch"] / avg_launch_s / 1e12
+                                                    / MFMA_BF16_PEAK_TFLOPS, 4)
+        roofline["mfma_busy_frac_counters"] = round(mc.get("mfma_busy_frac", float("nan")), 4)
 
     parity = None
     if not args.no_parity:
@@ -600,6 +691,37 @@ def main():
             o_ref, _, _ = oracle.chunked(sub, chunk=s.chunk, t_mode=mode, precond=pre)
         got = outs[j][:1, :n, :1].double().cpu().numpy()
         parity = {"stream": "(0,0)", "tokens": n, "rel_l2_out": oracle.rel_l2(got, o_ref)}
+
+    exact_vs_approx = None
+    if args.neumann >= 0 and not args.no_parity:
+        # the error between the exact T and the band-limited (or residual-corrected) T: on the GPU
+        # over the whole output of the last timed input set and over stream (0,0), and the same
+        # quantity from the oracle on stream (0,0), every token
+        import oracle
+        j = (args.steps - 1) % 2
+        xs = x if j == 0 else rolled
+        ex = torch.empty_like(outs[j])
+        a = sets[j]
+        G.gdr_chunk_fwd(a["q"], a["k"], a["v"], beta=a["beta"], log_alpha=a["log_alpha"], erase=a["erase"],
+                        write=a["write"], write_key=a["write_key"], precond=precond, out=ex, chunk=s.chunk,
+                        impl=args.impl, stream=stream)
+        torch.cuda.synchronize()
+        ap = outs[j].double()
+        exd = ex.double()
+        gpu_all = float(torch.linalg.vector_norm(ap - exd) / torch.linalg.vector_norm(exd))
+        gpu_00 = float(torch.linalg.vector_norm(ap[0, :, 0] - exd[0, :, 0]) / torch.linalg.vector_norm(exd[0, :, 0]))
+        sub = {k: (None if v is None else v[:1, :, :1]) for k, v in xs.items()}
+        pre = dict(rho=s.pc_rho, eps=s.pc_eps, h0=s.pc_h0, t0=0) if precond else None
+        o_ex, _, _ = oracle.recurrent(sub, precond=pre)
+        mode = ("neumann", args.neumann) if args.residual <= 0 else ("residual", args.neumann, args.residual)
+        o_ap, _, _ = oracle.chunked(sub, chunk=s.chunk, t_mode=mode, precond=pre)
+        exact_vs_approx = {
+            "approx": f"band N={args.neumann}" + (f" + {args.residual} residual steps" if args.residual > 0 else ""),
+            "rel_l2_exact_vs_approx_gpu_all_streams": gpu_all,
+            "rel_l2_exact_vs_approx_gpu_stream00": gpu_00,
+            "rel_l2_exact_vs_approx_oracle_stream00": oracle.rel_l2(o_ap, o_ex),
+            "stream": "(0,0)", "tokens": s.T,
+        }
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -631,6 +753,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if exact_vs_approx is not None:
+        rec["exact_vs_approx"] = exact_vs_approx
     print(json.dumps(rec), flush=True)
 
 

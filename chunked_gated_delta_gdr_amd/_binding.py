@@ -366,14 +366,14 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
         g["dstate_in"] = new((B, H, Dv, Dk))
     if precond:
         g["dpc_h_in"] = new((B, H, Dk))
+    grads = gdr_grads_t(*[_ptr(g.get(name)) for name, _ in gdr_grads_t._fields_])
+    ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
+                       _ptr(write_key), _ptr(pc_h_in) if precond else None, None)
     nbytes = gdr_chunk_bwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, need {nbytes}")
-    grads = gdr_grads_t(*[_ptr(g.get(name)) for name, _ in gdr_grads_t._fields_])
-    ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
-                       _ptr(write_key), _ptr(pc_h_in) if precond else None, None)
     st = lib().gdr_chunk_bwd(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(d_out),
                              _ptr(d_state_out), ctypes.byref(grads), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream, dev))

@@ -37,14 +37,15 @@ namespace {
 // XCD-aware order of a (value tile, head, batch) grid: workgroups are dealt to the 8 XCDs in
 // turn, so consecutive logical tiles (the value tiles of one head, which read the same keys
 // and gates) get ids 8 apart and share an XCD's L2
+// (indices in 64 bits: the grid may hold up to 2^24 workgroups, and the host bounds it)
 __device__ __forceinline__ void xcd_tile(int &vt, int &h, int &b) {
-  const int nvt = static_cast<int>(gridDim.x), nh = static_cast<int>(gridDim.y);
-  const int G = nvt * nh * static_cast<int>(gridDim.z);
-  const int bid = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  vt = logical % nvt;
-  h = (logical / nvt) % nh;
-  b = logical / nvt / nh;
+  const uint64_t nvt = gridDim.x, nh = gridDim.y;
+  const uint64_t G = nvt * nh * gridDim.z;
+  const uint64_t bid = blockIdx.x + nvt * (blockIdx.y + nh * static_cast<uint64_t>(blockIdx.z));
+  const uint64_t logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  vt = static_cast<int>(logical % nvt);
+  h = static_cast<int>((logical / nvt) % nh);
+  b = static_cast<int>(logical / nvt / nh);
 }
 
 constexpr int kCMax = 64;   // largest chunk

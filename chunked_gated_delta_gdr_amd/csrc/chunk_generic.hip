@@ -104,12 +104,13 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   // XCD-aware tile order: workgroups are dealt to the 8 XCDs in turn, so consecutive logical
   // tiles (the value tiles of one head, which read the same keys, queries and decays) get ids
   // 8 apart and share an XCD's L2
-  const int nvt = static_cast<int>(gridDim.x);
-  const int G = nvt * static_cast<int>(gridDim.y * gridDim.z);
-  const int bid = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int vt = logical % nvt, h = (logical / nvt) % static_cast<int>(gridDim.y),
-            b = logical / nvt / static_cast<int>(gridDim.y);
+  // (indices in 64 bits: the grid may hold up to 2^24 workgroups, and the host bounds it)
+  const uint64_t nvt = gridDim.x, nh = gridDim.y;
+  const uint64_t G = nvt * nh * gridDim.z;
+  const uint64_t bid = blockIdx.x + nvt * (blockIdx.y + nh * static_cast<uint64_t>(blockIdx.z));
+  const uint64_t logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int vt = static_cast<int>(logical % nvt), h = static_cast<int>((logical / nvt) % nh),
+            b = static_cast<int>(logical / nvt / nh);
   const int v0 = vt * BV;
   const int nv = min(BV, a.Dv - v0);
   const int Dk = a.Dk, Dv = a.Dv, H = a.H, T = a.T;

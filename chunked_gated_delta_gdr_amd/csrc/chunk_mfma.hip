@@ -21,9 +21,10 @@
 //    waves store to HBM.
 //  * helper waves prepare chunk c + 1 while the value waves run chunk c: they stage the
 //    next inputs into LDS from registers prefetched a chunk earlier (only helpers load
-//    from HBM), build T and P.  T is formed blockwise: each 16 x 16 diagonal block
-//    D = (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) (N strictly lower, so N^16 = 0)
-//    on the matrix cores, one block per helper wave, as soon as the chunk is staged; the
+//    from HBM), build T and P.  T is formed by blocked forward substitution: each 16 x 16
+//    diagonal block D = (I - N)^-1 (one per helper wave, as soon as the chunk is staged) by
+//    substitution inside its 4 x 4 diagonal sub-blocks in fp32 and two levels of block
+//    products on the matrix cores with every factor carried as a bf16 pair (hi + lo); the
 //    off-diagonal blocks T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and the lower-left
 //    quadrant T_ba = T_b A_ba T_a follow in the next phase, beside the P tiles.
 //  * With a band limit N >= 0 (the truncated Neumann series with its diagonal mask, same
@@ -84,10 +85,11 @@ struct __align__(16) Smem {
   uint16_t e[CHAN ? 2 : 1][CHAN ? kC * kD : 8];            // erase key b (.) k
   uint16_t r[WK != kWkSame ? 2 : 1][WK != kWkSame ? kC * kD : 8];   // write key if != k
   uint16_t vp[2][kC][BV + 8];                              // v tile (w (.) v with channel gains)
-  uint16_t t[2][kC][kLdc];                                 // T
+  uint16_t t[2][kC][kLdc];                                 // T, bf16 hi part
+  uint16_t tl[2][kC][kLdc];                                // T, bf16 lo part (T - hi, rounded)
   uint16_t p[kC][kLdc];                                    // P (one buffer)
-  uint16_t lba[32][kLdl];                                  // A_ba = -L_ba (rows 32.., cols ..31)
-  uint16_t aod[2][16][20];                                 // A_10, A_32
+  uint16_t lba[32][kLdl], lbal[32][kLdl];                  // A_ba = -L_ba (rows 32.., cols ..31), hi / lo
+  uint16_t aod[2][16][20], aodl[2][16][20];                // A_10, A_32, hi / lo
   float g2[2][kC], eg[2][kC], wd[2][kC], beta[2][kC], ic[2][kC];
 };
 
@@ -189,31 +191,81 @@ __device__ __forceinline__ short8v opsp(const uint16_t *a, int ld, int row, int 
   return cat(ld4(a + row * ld + k0 + 4 * l4), ld4(a + row * ld + k0 + 16 + 4 * l4));
 }
 
-// D = (I - N)^-1 for a strictly lower 16 x 16 N given as acc(N) and acc(N^T); returns
-// acc(D) and, when wanted, acc(D^T).  Doubling: N^16 = 0 so (I - N)^-1 = prod (I + N^(2^k)).
-__device__ __forceinline__ void diag_inverse(float4v nA, float4v ntA, float4v &d, float4v *dt, int lane) {
-  const short4v n = tobf4(nA), nt = tobf4(ntA);   // B-layout(N), B-layout(N^T)
-  const float4v z = zero4();
-  const short4v b2 = tobf4(mfma16(nt, n, z)), b2t = tobf4(mfma16(n, nt, z));
-  const short4v b4 = tobf4(mfma16(b2t, b2, z)), b4t = tobf4(mfma16(b2, b2t, z));
-  const short4v b8t = tobf4(mfma16(b4, b4t, z));
+__device__ __forceinline__ float4v unbf4(short4v v) {
+  return float4v{bf(static_cast<uint16_t>(v[0])), bf(static_cast<uint16_t>(v[1])), bf(static_cast<uint16_t>(v[2])),
+                 bf(static_cast<uint16_t>(v[3]))};
+}
+// c + X Y for 16 x 16 X, Y given as fp32 acc(X^T) (the A operand of X) and acc(Y), each carried
+// as a bf16 pair hi + lo (about 16 significant bits).  The hi / lo pair of X fills the K slots
+// a K = 16 product would pad with zeros: X_hi Y_hi + X_lo Y_hi in one instruction, X_hi Y_lo in
+// a second (the X_lo Y_lo term, ~2^-16 relative, is dropped).
+__device__ __forceinline__ float4v mfma_split(float4v a, float4v b, float4v c) {
+  const short4v ah = tobf4(a), bh = tobf4(b);
+  const short4v al = tobf4(a - unbf4(ah)), bl = tobf4(b - unbf4(bh));
+  return mfma16(ah, bl, mfma32(cat(ah, al), cat(bh, bh), c));
+}
+// fp32 values as a bf16 pair: x[0] = bf16(v), x[1] = bf16(v - x[0])
+struct Pair {
+  short4v h, l;
+};
+__device__ __forceinline__ Pair split4(float4v v) {
+  const short4v h = tobf4(v);
+  return Pair{h, tobf4(v - unbf4(h))};
+}
+// c + X Y for operands already held as pairs (x: A operand of X, y: B operand of Y)
+__device__ __forceinline__ float4v mm2(const Pair &x, const Pair &y, float4v c) {
+  return mfma16(x.h, y.l, mfma32(cat(x.h, x.l), cat(y.h, y.h), c));
+}
+__device__ __forceinline__ float4v mm2(const Pair &x, const Pair &y) { return mm2(x, y, float4v{0.f, 0.f, 0.f, 0.f}); }
+
+// acc(D^T) of D = (I - N)^-1 for a strictly lower 16 x 16 N given in fp32 as acc(N) and acc(N^T),
+// by blocked forward substitution (chunk-wise form of the MatMul-only inversion summary,
+// "Declaracao do Problema"):
+//  * the four 4 x 4 diagonal sub-blocks by substitution in fp32.  Each sub-block sits in one
+//    lane quad (in acc(N) quad lane l holds its column l, in acc(N^T) its row l), so the
+//    entries of N it needs arrive by quad broadcasts: columns of D1 = blockdiag(sub-block
+//    inverses) from acc(N) (x_r = [r == j] + sum_{l < r} N_rl x_l), rows from acc(N^T)
+//    (y_r = [r == i] + sum_{l > r} y_l N_lr);
+//  * two levels of block products D <- D + D N_m D, N_m the part of N that joins the blocks of
+//    the level (the 4 x 4 blocks (1, 0) and (3, 2), then the 8 x 8 block (1, 0)): the inverse of
+//    [[P, 0], [M, Q]] has P^-1 and Q^-1 on its diagonal and Q^-1 M P^-1 below it.
+// Every intermediate is part of the inverse itself, so no factor grows past |D| (the series
+// (I + N)(I + N^2)(I + N^4)(I + N^8) is exact too, but its powers of N are far larger than D
+// when keys are correlated or gains exceed 1, and rounded to bf16 they swamp it).
+__device__ __forceinline__ float4v diag_inverse_t(float4v n, float4v nt, int lane) {
   const int l16 = lane & 15, l4 = lane >> 4;
-  float4v id;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) id[r] = (4 * l4 + r == l16) ? 1.f : 0.f;
-  float4v R = nA + id;
-  R = mfma16(b2t, tobf4(R), R);
-  R = mfma16(b4t, tobf4(R), R);
-  R = mfma16(b8t, tobf4(R), R);
-  d = R;
-  if (dt != nullptr) {
-    const short4v b8 = tobf4(mfma16(b4t, b4, z));
-    float4v Rt = ntA + id;
-    Rt = mfma16(b2, tobf4(Rt), Rt);
-    Rt = mfma16(b4, tobf4(Rt), Rt);
-    Rt = mfma16(b8, tobf4(Rt), Rt);
-    *dt = Rt;
+  const bool dq = (l16 >> 2) == l4;        // this quad holds a diagonal sub-block
+  const int jq = l16 & 3;                  // the lane's column (acc(N)) or row (acc(N^T)) in it
+  const float one0 = jq == 0 ? 1.f : 0.f, one1 = jq == 1 ? 1.f : 0.f, one2 = jq == 2 ? 1.f : 0.f,
+              one3 = jq == 3 ? 1.f : 0.f;
+  float4v d1, dt1;
+  {   // columns: N_rl is register r of quad lane l
+    const float n10 = quadf<0x00>(n[1]), n20 = quadf<0x00>(n[2]), n30 = quadf<0x00>(n[3]);
+    const float n21 = quadf<0x55>(n[2]), n31 = quadf<0x55>(n[3]), n32 = quadf<0xaa>(n[3]);
+    const float x0 = one0;
+    const float x1 = fmaf(n10, x0, one1);
+    const float x2 = fmaf(n21, x1, fmaf(n20, x0, one2));
+    const float x3 = fmaf(n32, x2, fmaf(n31, x1, fmaf(n30, x0, one3)));
+    d1 = dq ? float4v{x0, x1, x2, x3} : zero4();
   }
+  {   // rows: N_lr is register r of quad lane l
+    const float n10 = quadf<0x55>(nt[0]), n20 = quadf<0xaa>(nt[0]), n21 = quadf<0xaa>(nt[1]);
+    const float n30 = quadf<0xff>(nt[0]), n31 = quadf<0xff>(nt[1]), n32 = quadf<0xff>(nt[2]);
+    const float y3 = one3;
+    const float y2 = fmaf(y3, n32, one2);
+    const float y1 = fmaf(y3, n31, fmaf(y2, n21, one1));
+    const float y0 = fmaf(y3, n30, fmaf(y2, n20, fmaf(y1, n10, one0)));
+    dt1 = dq ? float4v{y0, y1, y2, y3} : zero4();
+  }
+  // acc(N_m^T): lane (row l16, column block l4) of N
+  const int rb4 = l16 >> 2;
+  const float4v n1t = ((rb4 & 1) != 0 && l4 == rb4 - 1) ? nt : zero4();
+  const float4v n2t = ((l16 >> 3) == 1 && (l4 >> 1) == 0) ? nt : zero4();
+  const float4v z1 = mfma_split(n1t, d1, zero4());   // N_1 D_1
+  const float4v d2 = mfma_split(dt1, z1, d1);        // D_2 = D_1 + D_1 Z_1
+  const float4v dt2 = mfma_split(z1, dt1, dt1);      // D_2^T = D_1^T + Z_1^T D_1^T
+  const float4v z2 = mfma_split(n2t, d2, zero4());   // N_2 D_2
+  return mfma_split(z2, dt2, dt2);                   // D^T = D_2^T + Z_2^T D_2^T
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
@@ -247,6 +299,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const short4v I16 = ident4(lane);
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
+  // (the host bounds the grid to 2^22 workgroups, so these fit in 32 bits)
   const int G = static_cast<int>(gridDim.x);
   const int bid = static_cast<int>(blockIdx.x);
   const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
@@ -269,7 +322,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   uint16_t *gout = static_cast<uint16_t *>(a.out);
 
   // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
-  for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = 0;
+  for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = (&sm.tl[0][0][0])[i] = 0;
   for (int i = tid; i < kC * kLdc; i += kNT) (&sm.p[0][0])[i] = 0;
 
   // Each role runs its own loop with the same barrier sequence, so the compiler allocates
@@ -409,16 +462,22 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         }
         __syncthreads();   // (2) T(c), P(c) complete
         if (c >= 0) {
-          // every LDS operand of this phase is read up front: T and P blocks, R^T for the update
-          const uint16_t *Tm = &sm.t[cur][0][0], *Pm = &sm.p[0][0];
+          // every LDS operand of this phase is read up front: T and P blocks, R^T for the update.
+          // T is held as a bf16 pair (hi + lo): the diagonal blocks pack hi and lo into one K = 32
+          // operand (the other K half of a diagonal block is zero), the others take one operand
+          // per part.  (T and P are lower triangular; their blocks above the diagonal stay zero.)
+          const uint16_t *Tm = &sm.t[cur][0][0], *Tl = &sm.tl[cur][0][0], *Pm = &sm.p[0][0];
           const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-          // (T and P are lower triangular and their upper blocks stay zero in LDS, so the diagonal
-          // blocks are read as K = 32 operands together with the zero block beside them)
-          const short8v t00 = opsp(Tm, kLdc, l16, 0, l4), t10 = opsp(Tm, kLdc, 16 + l16, 0, l4);
-          const short8v t20 = opsp(Tm, kLdc, 32 + l16, 0, l4), t22 = opsp(Tm, kLdc, 32 + l16, 32, l4);
-          const short8v t30 = opsp(Tm, kLdc, 48 + l16, 0, l4), t32 = opsp(Tm, kLdc, 48 + l16, 32, l4);
-          const short8v p00 = opsp(Pm, kLdc, l16, 0, l4), p10 = opsp(Pm, kLdc, 16 + l16, 0, l4);
-          const short8v p20 = opsp(Pm, kLdc, 32 + l16, 0, l4), p22 = opsp(Pm, kLdc, 32 + l16, 32, l4);
+          auto blk = [&](const uint16_t *M, int rb, int kb) { return ld4(M + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
+          const short8v t00 = cat(blk(Tm, 0, 0), blk(Tl, 0, 0));
+          const short8v t10 = cat(blk(Tm, 1, 0), blk(Tm, 1, 1)), t10l = cat(blk(Tl, 1, 0), blk(Tl, 1, 1));
+          const short8v t20 = cat(blk(Tm, 2, 0), blk(Tm, 2, 1)), t20l = cat(blk(Tl, 2, 0), blk(Tl, 2, 1));
+          const short8v t22 = cat(blk(Tm, 2, 2), blk(Tl, 2, 2));
+          const short8v t30 = cat(blk(Tm, 3, 0), blk(Tm, 3, 1)), t30l = cat(blk(Tl, 3, 0), blk(Tl, 3, 1));
+          const short8v t32 = cat(blk(Tm, 3, 2), blk(Tm, 3, 3)), t32l = cat(blk(Tl, 3, 2), blk(Tl, 3, 3));
+          const short4v q00 = blk(Pm, 0, 0), q22 = blk(Pm, 2, 2);
+          const short8v p10 = opsp(Pm, kLdc, 16 + l16, 0, l4);
+          const short8v p20 = opsp(Pm, kLdc, 32 + l16, 0, l4);
           const short8v p30 = opsp(Pm, kLdc, 48 + l16, 0, l4), p32 = opsp(Pm, kLdc, 48 + l16, 32, l4);
           short8v ra[4], rb[4];   // R^T operands of the first half of the update
 #pragma unroll
@@ -431,22 +490,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           for (int j = 0; j < 4; ++j) wdv[j] = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
           const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
 
-          // D = T X
+          // D = T X  (T_hi X + T_lo X)
           const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
           float4v D[4];
-          D[0] = mfma32(t00, x01, zero4());
-          D[1] = mfma32(t10, x01, zero4());
-          D[2] = mfma32(t22, x23, mfma32(t20, x01, zero4()));
-          D[3] = mfma32(t32, x23, mfma32(t30, x01, zero4()));
+          D[0] = mfma32(t00, cat(x4[0], x4[0]), zero4());
+          D[1] = mfma32(t10l, x01, mfma32(t10, x01, zero4()));
+          D[2] = mfma32(t22, cat(x4[2], x4[2]), mfma32(t20l, x01, mfma32(t20, x01, zero4())));
+          D[3] = mfma32(t32l, x23, mfma32(t32, x23, mfma32(t30l, x01, mfma32(t30, x01, zero4()))));
           // state update S^T <- e^{g_C} S^T + R^T (wd (.) D), interleaved with O2 = P D
-          short4v w4[4], d4[4];
+          short4v w4[4], d4[4], dl4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             w4[j] = tobf4(float4v{wdv[j].x * D[j][0], wdv[j].y * D[j][1], wdv[j].z * D[j][2], wdv[j].w * D[j][3]});
-            d4[j] = tobf4(D[j]);
+            const Pair dp = split4(D[j]);
+            d4[j] = dp.h;
+            dl4[j] = dp.l;
           }
           const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
-          const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             float4v acc = st[cb];
@@ -461,12 +521,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
             if (DECAY) acc *= gC;
             st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
           }
+          // O = scale (O1 + P D), D as a bf16 pair (P_00 and P_22 are packed twice against
+          // [D_hi; D_lo]); O1 seeds the accumulator
+          const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
+          const short8v dl01 = cat(dl4[0], dl4[1]), dl23 = cat(dl4[2], dl4[3]);
           float4v O2[4];
-          // O1 seeds the accumulator: O = scale (O1 + P D)
-          O2[0] = mfma32(p00, d01, O1[0]);
-          O2[1] = mfma32(p10, d01, O1[1]);
-          O2[2] = mfma32(p22, d23, mfma32(p20, d01, O1[2]));
-          O2[3] = mfma32(p32, d23, mfma32(p30, d01, O1[3]));
+          O2[0] = mfma32(cat(q00, q00), cat(d4[0], dl4[0]), O1[0]);
+          O2[1] = mfma32(p10, dl01, mfma32(p10, d01, O1[1]));
+          O2[2] = mfma32(cat(q22, q22), cat(d4[2], dl4[2]), mfma32(p20, dl01, mfma32(p20, d01, O1[2])));
+          O2[3] = mfma32(p32, dl23, mfma32(p32, d23, mfma32(p30, dl01, mfma32(p30, d01, O1[3]))));
           // output: transpose each 16 x 16 block by an identity product so a lane holds four
           // consecutive values of one token (the four products issue back to back), then 8-byte
           // stores from a per-lane base and uniform offsets; only a partial last chunk masks
@@ -617,26 +680,44 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       }
     }
   };
-  // (E R^T) tile for rows ib, cols jb (trans: the transposed tile), scaled to A = -L
-  auto a_tile = [&](int buf, int ib, int jb, bool trans) -> float4v {
+  // diagonal block p of A = -L (strictly lower, fp32) as acc(N) and acc(N^T): the two products
+  // run on the same operands, and each entry is scaled by exactly the operations of a_tile, so
+  // acc(N^T) is the transpose of acc(N) bit for bit
+  auto a_diag = [&](int buf, int p, float4v &n, float4v &nt) {
     const uint16_t *E = CHAN ? sm.e[buf] : sm.k[buf];
     const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
-    const uint16_t *A = trans ? R : E;
-    const uint16_t *B = trans ? E : R;
-    const int ra = (trans ? jb : ib) * 16 + l16, rb = (trans ? ib : jb) * 16 + l16;
-    float4v acc = zero4();
+    constexpr bool SYM = !CHAN && WK == kWkSame;   // E R^T = K K^T: each tile is its own transpose
+    const int row = p * 16 + l16;
+    float4v g = zero4(), gt = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma32(opn128(A, ra, 32 * s, l4), opn128(B, rb, 32 * s, l4), acc);
+    for (int s = 0; s < 4; ++s) {
+      const short8v e = opn128(E, row, 32 * s, l4);
+      if constexpr (SYM) {
+        g = mfma32(e, e, g);
+      } else {
+        const short8v r = opn128(R, row, 32 * s, l4);
+        g = mfma32(e, r, g);
+        gt = mfma32(r, e, gt);
+      }
+    }
+    if constexpr (SYM) gt = g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = trans ? ib * 16 + l16 : ib * 16 + 4 * l4 + r;
-      const int j = trans ? jb * 16 + 4 * l4 + r : jb * 16 + l16;
-      float x = acc[r];
-      if (SCALED_E) x *= sm.beta[buf][i];
-      if (DECAY) x *= decay2(sm.g2[buf][i] - sm.g2[buf][j]);
-      acc[r] = (j < i) ? -x : 0.f;
+      {
+        const int i = p * 16 + 4 * l4 + r, j = p * 16 + l16;
+        float x = g[r];
+        if (SCALED_E) x *= sm.beta[buf][i];
+        if (DECAY) x *= decay2(sm.g2[buf][i] - sm.g2[buf][j]);
+        n[r] = (j < i) ? -x : 0.f;
+      }
+      {
+        const int i = p * 16 + l16, j = p * 16 + 4 * l4 + r;
+        float x = gt[r];
+        if (SCALED_E) x *= sm.beta[buf][i];
+        if (DECAY) x *= decay2(sm.g2[buf][i] - sm.g2[buf][j]);
+        nt[r] = (j < i) ? -x : 0.f;
+      }
     }
-    return acc;
   };
   // P tile job (blocks (ib, jb), jb <= ib, numbered row by row), computed transposed
   // (P^T = R Q^T) so each lane writes 4 columns of one row of P
@@ -660,17 +741,31 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     }
     *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(v);
   };
-  // write acc(X^T) of the 16 x 16 block (rb, cb) of a row-major [64][kLdc] bf16 matrix as
-  // 8-byte rows (lane: row rb*16 + l16, columns cb*16 + 4 l4 .. + 3), band-masked
-  auto put_rows = [&](uint16_t *M, int rb, int cb, float4v xt, bool lower_only) {
+  // write acc(X^T) of the 16 x 16 block (rb, cb) of T (buffer buf) as 8-byte rows (lane: row
+  // rb*16 + l16, columns cb*16 + 4 l4 .. + 3), band-masked, as the pair (hi, lo): from fp32 values
+  // (put_rows) or from the two parts already split (put_rows2; each part exactly bf16)
+  auto put_rows2 = [&](int buf, int rb, int cb, float4v xh, float4v xl, bool lower_only) {
     const int i = rb * 16 + l16;
-    float4v v;
+    float4v h, l;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = cb * 16 + 4 * l4 + r;
-      v[r] = (keep(i, j) && (!lower_only || j <= i)) ? xt[r] : 0.f;
+      const bool on = keep(i, j) && (!lower_only || j <= i);
+      h[r] = on ? xh[r] : 0.f;
+      l[r] = on ? xl[r] : 0.f;
     }
-    *reinterpret_cast<short4v *>(M + i * kLdc + cb * 16 + 4 * l4) = tobf4(v);
+    *reinterpret_cast<short4v *>(&sm.t[buf][i][cb * 16 + 4 * l4]) = tobf4(h);
+    *reinterpret_cast<short4v *>(&sm.tl[buf][i][cb * 16 + 4 * l4]) = tobf4(l);
+  };
+  auto put_rows = [&](int buf, int rb, int cb, float4v xt, bool lower_only) {
+    const Pair x = split4(xt);
+    put_rows2(buf, rb, cb, unbf4(x.h), unbf4(x.l), lower_only);
+  };
+  // acc(X^T) of a pair given in acc(X) (B operand) layout: each part transposed exactly by an
+  // identity product
+  auto tr2 = [&](const Pair &x, float4v &th, float4v &tl) {
+    th = mfma16(x.h, I16, zero4());
+    tl = mfma16(x.l, I16, zero4());
   };
 
   // preconditioner accumulator: helper threads ht < 256 own channels 2 p, 2 p + 1 (p = ht / 4)
@@ -694,61 +789,77 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     // chunk c, formed before the barrier) ahead of their staging writes: LDS operations of a
     // wave complete in order, so reads issued after the writes would wait for them to drain,
     // while issued first they let the writes drain under the products.
-    uint16_t *Tc = &sm.t[cur][0][0];
     const int qb = hw;   // column block of the lower-left quadrant formed by this wave
-    // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read
-    auto arow = [&](int rb, int kb) { return ld4(Tc + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
-    auto bcol = [&](int kb, int cb) {
-      return ldtr(Tc + (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3));
+    // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read; every
+    // operand as its bf16 pair
+    auto arow = [&](int rb, int kb) {
+      const int o = (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4;
+      return Pair{ld4(&sm.t[cur][0][0] + o), ld4(&sm.tl[cur][0][0] + o)};
     };
-    auto lrow = [&](int s, int u) { return ld4(&sm.lba[s * 16 + l16][u * 16 + 4 * l4]); };
-    short4v o_a33, o_b22, o_a22, o_a32, o_a10, o_d, o_a11, o_l00, o_l01, o_l10, o_l11;
-    if (c >= 0 && hw < 2) {
-      o_a33 = arow(3, 3);
-      o_b22 = bcol(2, 2);
-      o_a22 = arow(2, 2);
-      o_a32 = ld4(&sm.aod[1][l16][4 * l4]);
-      o_l01 = lrow(0, 1);
-      o_l11 = lrow(1, 1);
+    auto bcol = [&](int kb, int cb) {
+      const int o = (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3);
+      return Pair{ldtr(&sm.t[cur][0][0] + o), ldtr(&sm.tl[cur][0][0] + o)};
+    };
+    auto lrow = [&](int s2, int u) {
+      return Pair{ld4(&sm.lba[s2 * 16 + l16][u * 16 + 4 * l4]), ld4(&sm.lbal[s2 * 16 + l16][u * 16 + 4 * l4])};
+    };
+    auto aodp = [&](int j) { return Pair{ld4(&sm.aod[j][l16][4 * l4]), ld4(&sm.aodl[j][l16][4 * l4])}; };
+    // (the hi parts are requested before the staging writes, the lo parts after them)
+    Pair o_a33, o_b22, o_a22, o_a32, o_a10, o_d, o_a11, o_l00, o_l01, o_l10, o_l11;
+    auto load_ops = [&](auto part) {
+      constexpr bool LO = decltype(part)::value;
+      auto get = [&](Pair &x, const Pair &v) { (LO ? x.l : x.h) = LO ? v.l : v.h; };
+      get(o_a33, arow(3, 3));
+      get(o_b22, bcol(2, 2));
+      get(o_a22, arow(2, 2));
+      get(o_a32, aodp(1));
+      get(o_l01, lrow(0, 1));
+      get(o_l11, lrow(1, 1));
       if (qb == 0) {
-        o_a10 = ld4(&sm.aod[0][l16][4 * l4]);
-        o_d = bcol(0, 0);
-        o_a11 = arow(1, 1);
-        o_l00 = lrow(0, 0);
-        o_l10 = lrow(1, 0);
+        get(o_a10, aodp(0));
+        get(o_d, bcol(0, 0));
+        get(o_a11, arow(1, 1));
+        get(o_l00, lrow(0, 0));
+        get(o_l10, lrow(1, 0));
       } else {
-        o_d = bcol(1, 1);
+        get(o_d, bcol(1, 1));
       }
-    }
+    };
+    if (c >= 0 && hw < 2) load_ops(std::false_type{});
     if (have_next) {
       stage_items(c + 1, nxt);
       if (c + 2 < nchunks) load_items(c + 2);
     }
     if (c >= 0) {
       if (hw < 2) {
+        load_ops(std::true_type{});
         // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
-        // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a
-        const float4v t32 = mfma16(o_a33, tobf4(mfma16(o_a32, o_b22, zero4())), zero4());
-        const short4v t32a = tobf4(mfma16(tobf4(t32), I16, zero4()));   // A layout of T_32
-        float4v z0, z1;                                                  // Z = A_ba T_a[:, qb]
+        // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a, every product on bf16 pairs
+        const Pair t32 = split4(mm2(o_a33, split4(mm2(o_a32, o_b22))));
+        float4v t32h, t32l;
+        tr2(t32, t32h, t32l);
+        const Pair t32a{tobf4(t32h), tobf4(t32l)};   // A layout of T_32
+        float4v z0, z1;                              // Z = A_ba T_a[:, qb]
         if (qb == 0) {
-          const short4v d0 = o_d;
-          const float4v t10 = mfma16(o_a11, tobf4(mfma16(o_a10, d0, zero4())), zero4());
-          const short4v t10b = tobf4(t10);
-          z0 = mfma16(o_l01, t10b, mfma16(o_l00, d0, zero4()));
-          z1 = mfma16(o_l11, t10b, mfma16(o_l10, d0, zero4()));
-          put_rows(Tc, 1, 0, mfma16(t10b, I16, zero4()), false);
+          const Pair t10 = split4(mm2(o_a11, split4(mm2(o_a10, o_d))));
+          z0 = mm2(o_l01, t10, mm2(o_l00, o_d));
+          z1 = mm2(o_l11, t10, mm2(o_l10, o_d));
+          float4v th, tl;
+          tr2(t10, th, tl);
+          put_rows2(cur, 1, 0, th, tl, false);
         } else {
-          const short4v d1 = o_d;
-          z0 = mfma16(o_l01, d1, zero4());
-          z1 = mfma16(o_l11, d1, zero4());
-          put_rows(Tc, 3, 2, mfma16(tobf4(t32), I16, zero4()), false);
+          z0 = mm2(o_l01, o_d);
+          z1 = mm2(o_l11, o_d);
+          put_rows2(cur, 3, 2, t32h, t32l, false);
         }
-        const short4v z0b = tobf4(z0), z1b = tobf4(z1);
-        const float4v tb2 = mfma16(o_a22, z0b, zero4());
-        const float4v tb3 = mfma16(o_a33, z1b, mfma16(t32a, z0b, zero4()));
-        put_rows(Tc, 2, qb, mfma16(tobf4(tb2), I16, zero4()), false);
-        put_rows(Tc, 3, qb, mfma16(tobf4(tb3), I16, zero4()), false);
+        const Pair z0p = split4(z0), z1p = split4(z1);
+        const Pair tb2 = split4(mm2(o_a22, z0p));
+        const Pair tb3 = split4(mm2(o_a33, z1p, mm2(t32a, z0p)));
+        float4v th, tl;
+        tr2(tb2, th, tl);
+        put_rows2(cur, 2, qb, th, tl, false);
+        tr2(tb3, th, tl);
+        put_rows2(cur, 3, qb, th, tl, false);
       }
       // P tiles (10 lower blocks) unless the value waves form them: jobs 8, 9 on the two T_ba
       // waves, 0..7 on the others
@@ -895,8 +1006,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = -(DECAY ? acc[q][r] * bi * decay2(gi - (&gj.x)[r]) : acc[q][r] * bi);
           if (job < 6) {
+            const Pair xp = split4(x);
             uint16_t *dst = job < 2 ? &sm.aod[job][l16][4 * l4] : &sm.lba[(ib[q] - 2) * 16 + l16][jb[q] * 16 + 4 * l4];
-            *reinterpret_cast<short4v *>(dst) = tobf4(x);
+            uint16_t *dstl = job < 2 ? &sm.aodl[job][l16][4 * l4] : &sm.lbal[(ib[q] - 2) * 16 + l16][jb[q] * 16 + 4 * l4];
+            *reinterpret_cast<short4v *>(dst) = xp.h;
+            *reinterpret_cast<short4v *>(dstl) = xp.l;
           }
         }
       };
@@ -907,11 +1021,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       constexpr bool kSplitA = NOW == 2;
       if (hw < 4) {
         // diagonal block hw of T: D = (I - A_pp)^-1
-        const float4v n = a_tile(nb, hw, hw, false);
-        const float4v nt = mfma16(tobf4(n), I16, zero4());
-        float4v d, dt;
-        diag_inverse(n, nt, d, &dt, lane);
-        put_rows(&sm.t[nb][0][0], hw, hw, dt, true);
+        float4v n, nt;
+        a_diag(nb, hw, n, nt);
+        put_rows(nb, hw, hw, diag_inverse_t(n, nt, lane), true);
         if constexpr (kSplitA) {
           if (hw < 2) a_jobs(std::integral_constant<int, 1>{}, 4 + hw, 1);
         }
@@ -931,7 +1043,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 
 template <int BV, bool CHAN, bool DECAY, int WK>
 hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
-  const int grid = a.B * a.H * (kD / BV);
+  const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV);   // <= 2^22
   hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK>), dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }

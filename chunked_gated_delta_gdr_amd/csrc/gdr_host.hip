@@ -53,6 +53,10 @@ Range rng(const char *name, const void *p, long double bytes) {
 
 // Largest element count of any one tensor the library accepts (2^40 elements).
 constexpr long double kMaxElems = 1099511627776.0L;
+// Largest number of (batch, head) streams per call, and of chunks per stream in the backward
+// (whose per-chunk kernels launch one 512-thread workgroup per chunk along the grid's x axis).
+constexpr long long kMaxStreams = 1LL << 19;
+constexpr long long kMaxBwdChunks = 1LL << 22;
 
 // Sections of gdr_chunk_bwd's workspace (byte offsets, each 256-byte aligned).
 struct BwdLayout {
@@ -114,6 +118,10 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
                 sizeof(gdr_desc_t));
   if (d->B < 1 || d->H < 1) return fail(GDR_EINVAL, "B = %d and H = %d must be >= 1", d->B, d->H);
   if (d->B > 65535 || d->H > 65535) return fail(GDR_ENOTSUP, "B = %d, H = %d (max 65535 each)", d->B, d->H);
+  // one workgroup per (batch, head, value tile): with up to 8 (matrix-core kernel) or 32 tiles
+  // of 512 threads per stream, 2^19 streams keep every grid within 2^32 work-items
+  if (static_cast<long long>(d->B) * d->H > kMaxStreams)
+    return fail(GDR_ENOTSUP, "B * H = %lld streams (max %lld)", static_cast<long long>(d->B) * d->H, kMaxStreams);
   if (for_step ? d->T != 1 : d->T < 0)
     return fail(GDR_EINVAL, for_step ? "T = %d; gdr_recurrent_step takes exactly one token"
                                      : "T = %d must be >= 0", d->T);
@@ -287,6 +295,9 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   if (g->dpc_h_in != nullptr && d->wkey != GDR_WKEY_DIAG_PRECOND)
     return fail(GDR_EINVAL, "grads->dpc_h_in given without wkey DIAG_PRECOND");
   if ((reinterpret_cast<uintptr_t>(g->dpc_h_in) & 3u) != 0) return fail(GDR_EINVAL, "grads->dpc_h_in misaligned");
+  if ((static_cast<long long>(d->T) + d->chunk - 1) / d->chunk > kMaxBwdChunks)
+    return fail(GDR_ENOTSUP, "T = %d is %lld chunks of %d (max %lld chunks in the backward)", d->T,
+                (static_cast<long long>(d->T) + d->chunk - 1) / d->chunk, d->chunk, kMaxBwdChunks);
   if (d->neumann_order >= 0 && d->residual_steps > 0)
     return fail(GDR_ENOTSUP, "backward of the residual-corrected T (exact or band-limited T only)");
   if (d->neumann_order >= 0 && d->decay == GDR_DECAY_CHANNEL)

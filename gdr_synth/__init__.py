@@ -30,6 +30,18 @@ the order q, k, v, then the gate logits):
 * erase = sigmoid(N(2, 1))                     [B, T, H, Dk] (channel gain, key axis);
 * write = sigmoid(N(0, 1))                     [B, T, H, Dv] (channel gain, value axis).
 
+Stress options (off by default; a default spec draws exactly the stream above):
+
+* ``key_corr = c > 0``: queries, keys (and an explicit write key) share one direction per
+  (batch, head) stream, q = normalise(z_q + c * u), k = normalise(z_k + c * u), u ~ N(0, I)
+  drawn from its own generator (seed ``seed + 104729``), so every decode step of a stream
+  sees the same u.  Real keys are correlated; this is the regime where the chunk's
+  triangular inverse is ill-conditioned;
+* ``beta_shift = s``: beta = s + sigmoid(N(0, 1)) (s = 1 gives beta in (1, 2), the range where
+  the transition I - beta k k^T has a negative eigenvalue);
+* ``decay_law = "strong"``: log_alpha = -5 U(0, 1) per token (per channel for a per-channel
+  decay) in place of -0.1 softplus(N(0, 1)).
+
 Loss gradients for the backward pass (``make_cotangents``, seed ``spec.seed + 7919`` unless
 given): d_out ~ N(0, 1) [B, T, H, Dv] stored like v, and d_state_out ~ N(0, 1) [B, H, Dv, Dk]
 fp32, drawn in that order.
@@ -75,6 +87,10 @@ class Spec:
     # decode phase (``long`` workload only)
     decode_batch: int = 0
     decode_steps: int = 0
+    # stress options (see the module docstring); the defaults leave the draws unchanged
+    key_corr: float = 0.0
+    beta_shift: float = 0.0
+    decay_law: str = "mild"      # "mild" | "strong"
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -133,30 +149,49 @@ def _softplus(x: np.ndarray) -> np.ndarray:
     return np.logaddexp(0.0, x)
 
 
-def _draw(rng: np.random.Generator, s: Spec, lead: tuple) -> Dict[str, np.ndarray]:
+def _shared_direction(s: Spec, seed: int, lead: tuple) -> np.ndarray:
+    """One direction per (batch, head) stream, broadcast over tokens: shape of ``lead`` with the
+    token axis (if any) set to 1, plus the key axis."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    if len(lead) == 3:   # (B, T, H)
+        return rng.standard_normal((lead[0], 1, lead[2], s.Dk))
+    return rng.standard_normal(lead + (s.Dk,))   # (B, H): decode
+
+
+def _draw(rng: np.random.Generator, s: Spec, lead: tuple, base_seed: int) -> Dict[str, np.ndarray]:
     """Draw one batch of inputs with leading dims ``lead`` (e.g. (B, T, H))."""
     out: Dict[str, np.ndarray] = {}
-    out["q"] = _store(_l2n(rng.standard_normal(lead + (s.Dk,))), s.dtype)
-    out["k"] = _store(_l2n(rng.standard_normal(lead + (s.Dk,))), s.dtype)
+    zq = rng.standard_normal(lead + (s.Dk,))
+    zk = rng.standard_normal(lead + (s.Dk,))
     out["v"] = _store(rng.standard_normal(lead + (s.Dv,)), s.dtype)
     if s.gain == "scalar":
-        out["beta"] = round_to_f32(_sigmoid(rng.standard_normal(lead)))
+        out["beta"] = round_to_f32(s.beta_shift + _sigmoid(rng.standard_normal(lead)))
     else:
         out["erase"] = _store(_sigmoid(rng.normal(2.0, 1.0, lead + (s.Dk,))), s.dtype)
         out["write"] = _store(_sigmoid(rng.standard_normal(lead + (s.Dv,))), s.dtype)
-    if s.decay == "scalar":
-        out["log_alpha"] = round_to_f32(-0.1 * _softplus(rng.standard_normal(lead)))
-    elif s.decay == "channel":
-        out["log_alpha"] = round_to_f32(-0.1 * _softplus(rng.standard_normal(lead + (s.Dk,))))
-    if s.wkey == "explicit":
-        out["write_key"] = _store(rng.standard_normal(lead + (s.Dk,)) / np.sqrt(s.Dk), s.dtype)
-    return out
+    if s.decay != "none":
+        shape = lead if s.decay == "scalar" else lead + (s.Dk,)
+        if s.decay_law == "strong":
+            out["log_alpha"] = round_to_f32(-5.0 * rng.random(shape))
+        else:
+            out["log_alpha"] = round_to_f32(-0.1 * _softplus(rng.standard_normal(shape)))
+    zw = rng.standard_normal(lead + (s.Dk,)) if s.wkey == "explicit" else None
+    if s.key_corr > 0.0:
+        u = s.key_corr * _shared_direction(s, base_seed, lead)
+        zq, zk = zq + u, zk + u
+        zw = None if zw is None else zw + u
+    out["q"] = _store(_l2n(zq), s.dtype)
+    out["k"] = _store(_l2n(zk), s.dtype)
+    if zw is not None:
+        out["write_key"] = _store(zw / np.sqrt(s.Dk), s.dtype)
+    return {k: out[k] for k in ("q", "k", "v", "beta", "erase", "write", "log_alpha", "write_key") if k in out}
 
 
 def make_inputs(s: Spec, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Inputs of one chunked-forward call: arrays in [B, T, H, D] / [B, T, H] layout."""
-    rng = np.random.Generator(np.random.PCG64(s.seed if seed is None else seed))
-    return _draw(rng, s, (s.B, s.T, s.H))
+    base = s.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(base))
+    return _draw(rng, s, (s.B, s.T, s.H), base)
 
 
 def make_decode_inputs(s: Spec, step: int) -> Dict[str, np.ndarray]:
@@ -165,7 +200,7 @@ def make_decode_inputs(s: Spec, step: int) -> Dict[str, np.ndarray]:
     Step ``s`` uses seed ``s.seed + 1 + step`` (5001 + step for the long workload).
     """
     rng = np.random.Generator(np.random.PCG64(s.seed + 1 + step))
-    return _draw(rng, s, (s.decode_batch, s.H))
+    return _draw(rng, s, (s.decode_batch, s.H), s.seed)
 
 
 def make_cotangents(s: Spec, seed: Optional[int] = None) -> Dict[str, np.ndarray]:

@@ -74,14 +74,19 @@ enum { GDR_IMPL_AUTO = 0, GDR_IMPL_GENERIC = 1, GDR_IMPL_MFMA = 2 };    /* impl 
 
 typedef struct gdr_desc {
   uint32_t struct_size;   /* must equal sizeof(gdr_desc_t) (ABI guard)                    */
-  int32_t B, T, H;        /* batch, tokens in this call (1 for gdr_recurrent_step), heads */
+  int32_t B, T, H;        /* batch, tokens in this call (1 for gdr_recurrent_step), heads;
+                             B, H <= 65535 and B * H <= 2^19 streams (GDR_ENOTSUP beyond:
+                             every launch grid then fits HIP's 32-bit work-item counts);
+                             the backward also takes at most 2^22 chunks per stream      */
   int32_t Dk, Dv;         /* key and value head dims: 1 <= Dk <= 128, 1 <= Dv <= 512      */
   int32_t chunk;          /* chunk size C in tokens: 16, 32 or 64 (ignored by the step)   */
   int32_t io_dtype;       /* GDR_F32 | GDR_BF16                                            */
   int32_t gain;           /* GDR_GAIN_*                                                    */
   int32_t decay;          /* GDR_DECAY_*                                                   */
   int32_t wkey;           /* GDR_WKEY_*                                                    */
-  int32_t neumann_order;  /* < 0: exact T = (I - A)^-1 by forward substitution;
+  int32_t neumann_order;  /* < 0: exact T = (I - A)^-1 by blocked forward substitution
+                             (substitution inside 4 x 4 diagonal blocks, block products
+                             T_21 = T_22 A_21 T_11 between them);
                              N >= 0: T restricted to the band i - j <= N (the masked
                              truncated Neumann series sum_{n<=N} A^n, which equals the band
                              of the exact inverse); N >= C - 1 reproduces the exact path

@@ -130,6 +130,31 @@ def test_huge_problem_rejected():
     check(G.GDR_ENOTSUP, d=desc(B=1 << 20, T=1 << 20, H=1 << 10))
 
 
+def test_stream_count_bound():
+    """At most 2^19 (batch, head) streams: every launch grid stays within 2^32 work-items and
+    the kernels' workgroup indices within 2^24, whatever the head dims."""
+    check(G.GDR_OK, d=desc(B=1 << 9, H=1 << 10, T=1, Dk=1, Dv=1))
+    check(G.GDR_ENOTSUP, d=desc(B=(1 << 9) + 1, H=1 << 10, T=1, Dk=1, Dv=1))
+    assert "streams" in G.gdr_last_error()
+    check(G.GDR_ENOTSUP, d=desc(B=65535, H=65535, T=1, Dk=1, Dv=1))
+
+
+def test_bwd_chunk_count_bound():
+    """The backward's per-chunk kernels put the chunks on the grid's x axis: at most 2^22."""
+    far = [BASE + i * (1 << 36) for i in range(30)]   # disjoint for tensors up to 64 GiB
+
+    def validate(T):
+        d = desc(B=1, H=1, T=T, Dk=1, Dv=1, chunk=16)
+        ins = G.gdr_inputs_t(q=far[0], k=far[1], v=far[2], beta=far[3])
+        gr = G.gdr_grads_t(dq=far[10], dk=far[11], dv=far[12], dbeta=far[13], dstate_in=far[19])
+        return G.lib().gdr_validate_bwd(ctypes.byref(d), ctypes.byref(ins), None, far[9], None, ctypes.byref(gr),
+                                        far[24], G.gdr_chunk_bwd_workspace_size(d))
+
+    assert validate((1 << 22) * 16) == G.GDR_OK, G.gdr_last_error()
+    assert validate((1 << 22) * 16 + 1) == G.GDR_ENOTSUP
+    assert "chunks" in G.gdr_last_error()
+
+
 def test_pointer_consistency_with_variant():
     p = ptrs()
     check(G.GDR_EINVAL, ins=inputs(beta=None))                                   # gain scalar, no beta

@@ -241,8 +241,10 @@ def test_variants_bf16_small(variant, impl):
     assert O.rel_l2(host(S), S_ref) <= TOL_BF16
 
 
-def _sampled(s, x, o, S, streams, precond=None, t_mode=None):
-    """Oracle on a few (b, h) streams only; compare those streams."""
+def _sampled(s, x, o, S, streams, precond=None, t_mode=None, blk=64):
+    """Oracle on a few (b, h) streams only; compare those streams.  The output error is the
+    larger of the whole-stream rel-L2 and the worst rel-L2 over the stream's 64-token blocks
+    (a defect confined to one chunk position moves a long stream's norm too little)."""
     if t_mode is None:
         o_ref, S_ref, _ = O.recurrent(x, precond=precond, streams=streams)
     else:
@@ -250,7 +252,9 @@ def _sampled(s, x, o, S, streams, precond=None, t_mode=None):
     o, S = host(o), host(S)
     errs = []
     for (b, h) in streams:
-        errs.append((O.rel_l2(o[b, :, h], o_ref[b, :, h]), O.rel_l2(S[b, h], S_ref[b, h])))
+        e_stream = O.rel_l2(o[b, :, h], o_ref[b, :, h])
+        e_blk = max(O.rel_l2(o[b, t0:t0 + blk, h], o_ref[b, t0:t0 + blk, h]) for t0 in range(0, o.shape[1], blk))
+        errs.append((max(e_stream, e_blk), O.rel_l2(S[b, h], S_ref[b, h])))
     return errs
 
 
