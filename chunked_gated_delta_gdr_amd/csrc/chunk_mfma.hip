@@ -268,8 +268,11 @@ __device__ __forceinline__ float4v diag_inverse_t(float4v n, float4v nt, int lan
   return mfma_split(z2, dt2, dt2);                   // D^T = D_2^T + Z_2^T D_2^T
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK>
-__global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
+// The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
+// the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
+// own role's state across iterations, and both run the kernel's barrier sequence.
+template <int BV, bool CHAN, bool DECAY, int WK, bool STG>
+__device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
   constexpr int NHW = kNW - NVW;           // helper waves
@@ -285,7 +288,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // keep every R block, the helper waves form it
   constexpr bool kPv = NVW == 2;
   constexpr bool kRq = kPv && (CHAN || WK != kWkSame);   // P's R operands read separately
-  __shared__ Smem<BV, CHAN, WK> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -321,267 +323,24 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
   uint16_t *gout = static_cast<uint16_t *>(a.out);
 
-  // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
-  for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = (&sm.tl[0][0][0])[i] = 0;
-  for (int i = tid; i < kC * kLdc; i += kNT) (&sm.p[0][0])[i] = 0;
-
-  // Each role runs its own loop with the same barrier sequence, so the compiler allocates
-  // registers for one role's loop-carried state at a time.
-  if (vwave) {
-    // the wave index is a template constant inside the value-wave loop, so every
-    // wave-dependent choice below (state rows, the P blocks a wave forms) is static
-    auto value_loop = [&](auto wc) {
-      constexpr int W = decltype(wc)::value;
-      // ---------------- value waves: S^T tiles in accumulators ----------------
-      // Tile cb holds S^T[c][v = 16 W + l16] for the channels c = chan(16 cb + 4 l4 + r) =
-      // 32 (cb / 2) + 8 l4 + 4 (cb % 2) + r: with this order the bf16 concatenation of tiles
-      // 2j and 2j + 1 (the K = 32 B operand of Y and O1) covers channels 32 j + 8 l4 .. + 7 in
-      // natural order, so the E / Q / K operands beside it are single 16-byte LDS reads; the
-      // update reads R^T in the same order (optr_state) and the state is loaded and stored
-      // through it once.
-      float4v st[8];
-      const int vrow = v0 + 16 * W + l16;   // this lane's state row
-      // output element (token l16 of a 16-token block, values 4 l4 .. + 3 of this wave's rows)
-      uint16_t *const obase = gout + head0 + static_cast<long long>(l16) * tokstride + v0 + 16 * W + 4 * l4;
-      auto chan0 = [&](int cb) { return 32 * (cb >> 1) + 8 * l4 + 4 * (cb & 1); };
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        st[cb] = zero4();
-        if (a.state_in != nullptr) {
-          const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb));
-          st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
-        }
-      }
-      for (int c = -1; c < nchunks; ++c) {
-        const int cur = c & 1;
-        const int c0 = c * kC;
-        const int n = min(kC, T - c0);
-        short4v x4[4];
-        float4v O1[4];
-        __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
-        if (c >= 0) {
-          // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y.  The
-          // operands of block tb + 1 are read while block tb is multiplied.  With kPv the K
-          // operands of earlier blocks are kept and the blocks (tb, jb), jb <= tb, of P are
-          // formed here, split between the value waves by column block.
-          short8v sb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
-          const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
-          // one register set per block for the E operands (the wave keeps those of its own P column
-          // blocks alive; the others die after their block), double-buffered Q operands
-          short8v ev[4][4], qv[2][4];
-          short8v kq[2][4];   // kRq: R operands of this wave's two P column blocks
-          // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
-          // wave 0, 1 and 2 to wave 1)
-          constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
-          constexpr auto p_slot = [](int jb) { return NVW == 1 ? jb : (jb < 2 ? 0 : 1); };
-          short4v vt[2];
-          // Everything a block reads from LDS is read while the previous block is multiplied:
-          // LDS reads complete in order, so a read issued inside a block would also wait for
-          // the prefetch issued before it.
-          float4 egv[2], btv[2];
-          float giv[2];
-          float4 gjv[4 / NVW];   // kPv: cumulative decay at the columns of this wave's P blocks
-          auto load_e = [&](int tb) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ev[tb][j] = opn128(E, tb * 16 + l16, 32 * j, l4);
-          };
-          auto load_ops = [&](int tb, int slot) {
-            if constexpr (!kPv) load_e(tb);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qv[slot][j] = opn128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
-            // V' block (rows t, columns v) in the accumulator layout, read transposed
-            vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
-            if (kRq && p_owner(tb) == W) {
-              const uint16_t *Rp = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = opn128(Rp, tb * 16 + l16, 32 * j, l4);
-            }
-            egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
-            if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
-            if (kPv) giv[slot] = sm.g2[cur][tb * 16 + l16];
-          };
-          if constexpr (kPv) {
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-              if (p_owner(jb) == W) gjv[p_slot(jb)] = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
-          }
-          load_ops(0, 0);
-          if constexpr (kPv) {
-            // the E operands of every block stay live for P anyway: all of them are requested
-            // now, so the phase waits for one LDS round trip instead of one per block
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) load_e(tb);
-          }
-          GDR_FENCE();
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            const int sl = tb & 1;
-            if (tb + 1 < 4) load_ops(tb + 1, sl ^ 1);
-            GDR_FENCE();   // the prefetch issues before this block's products
-            float4v y = zero4(), o = zero4();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              y = mfma32(ev[tb][j], sb[j], y);
-              o = mfma32(qv[sl][j], sb[j], o);
-            }
-            const float4 eg = egv[sl];
-            float4v xv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xv[r] = bf(static_cast<uint16_t>(vt[sl][r])) - (&eg.x)[r] * y[r];
-            if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
-              const float4 bt = btv[sl];
-              xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
-            }
-            x4[tb] = tobf4(xv);
-            O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
-            if constexpr (kPv) {
-              // P^T block (jb, tb) = K_jb Q_tb^T: lane holds P[i = tb*16 + l16][j = jb*16 + 4 l4 + r]
-              const int i = tb * 16 + l16;
-              const float gi = giv[sl];
-#pragma unroll
-              for (int jb = 0; jb <= tb; ++jb) {
-                if (p_owner(jb) != W) continue;
-                float4v pt = zero4();
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pt = mfma32(kRq ? kq[p_slot(jb)][j] : ev[jb][j], qv[sl][j], pt);
-                const float4 gj = gjv[p_slot(jb)];
-                float4v pv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int jj = jb * 16 + 4 * l4 + r;
-                  const float x = DECAY ? pt[r] * decay2(gi - (&gj.x)[r]) : pt[r];
-                  pv[r] = (jb < tb || jj <= i) ? x : 0.f;   // only the diagonal block is masked
-                }
-                *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(pv);
-              }
-            }
-            GDR_FENCE();
-          }
-        }
-        __syncthreads();   // (2) T(c), P(c) complete
-        if (c >= 0) {
-          // every LDS operand of this phase is read up front: T and P blocks, R^T for the update.
-          // T is held as a bf16 pair (hi + lo): the diagonal blocks pack hi and lo into one K = 32
-          // operand (the other K half of a diagonal block is zero), the others take one operand
-          // per part.  (T and P are lower triangular; their blocks above the diagonal stay zero.)
-          const uint16_t *Tm = &sm.t[cur][0][0], *Tl = &sm.tl[cur][0][0], *Pm = &sm.p[0][0];
-          const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
-          auto blk = [&](const uint16_t *M, int rb, int kb) { return ld4(M + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
-          const short8v t00 = cat(blk(Tm, 0, 0), blk(Tl, 0, 0));
-          const short8v t10 = cat(blk(Tm, 1, 0), blk(Tm, 1, 1)), t10l = cat(blk(Tl, 1, 0), blk(Tl, 1, 1));
-          const short8v t20 = cat(blk(Tm, 2, 0), blk(Tm, 2, 1)), t20l = cat(blk(Tl, 2, 0), blk(Tl, 2, 1));
-          const short8v t22 = cat(blk(Tm, 2, 2), blk(Tl, 2, 2));
-          const short8v t30 = cat(blk(Tm, 3, 0), blk(Tm, 3, 1)), t30l = cat(blk(Tl, 3, 0), blk(Tl, 3, 1));
-          const short8v t32 = cat(blk(Tm, 3, 2), blk(Tm, 3, 3)), t32l = cat(blk(Tl, 3, 2), blk(Tl, 3, 3));
-          const short4v q00 = blk(Pm, 0, 0), q22 = blk(Pm, 2, 2);
-          const short8v p10 = opsp(Pm, kLdc, 16 + l16, 0, l4);
-          const short8v p20 = opsp(Pm, kLdc, 32 + l16, 0, l4);
-          const short8v p30 = opsp(Pm, kLdc, 48 + l16, 0, l4), p32 = opsp(Pm, kLdc, 48 + l16, 32, l4);
-          short8v ra[4], rb[4];   // R^T operands of the first half of the update
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            ra[cb] = optr_state(Rk, cb, 0, lane);
-            rb[cb] = optr_state(Rk, cb, 32, lane);
-          }
-          float4 wdv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) wdv[j] = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
-          const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
-
-          // D = T X  (T_hi X + T_lo X)
-          const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
-          float4v D[4];
-          D[0] = mfma32(t00, cat(x4[0], x4[0]), zero4());
-          D[1] = mfma32(t10l, x01, mfma32(t10, x01, zero4()));
-          D[2] = mfma32(t22, cat(x4[2], x4[2]), mfma32(t20l, x01, mfma32(t20, x01, zero4())));
-          D[3] = mfma32(t32l, x23, mfma32(t32, x23, mfma32(t30l, x01, mfma32(t30, x01, zero4()))));
-          // state update S^T <- e^{g_C} S^T + R^T (wd (.) D), interleaved with O2 = P D
-          short4v w4[4], d4[4], dl4[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            w4[j] = tobf4(float4v{wdv[j].x * D[j][0], wdv[j].y * D[j][1], wdv[j].z * D[j][2], wdv[j].w * D[j][3]});
-            const Pair dp = split4(D[j]);
-            d4[j] = dp.h;
-            dl4[j] = dp.l;
-          }
-          const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            float4v acc = st[cb];
-            if (DECAY) acc *= gC;
-            st[cb] = mfma32(rb[cb], w23, mfma32(ra[cb], w01, acc));
-            ra[cb] = optr_state(Rk, cb + 4, 0, lane);   // second half, read behind the first
-            rb[cb] = optr_state(Rk, cb + 4, 32, lane);
-          }
-#pragma unroll
-          for (int cb = 4; cb < 8; ++cb) {
-            float4v acc = st[cb];
-            if (DECAY) acc *= gC;
-            st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
-          }
-          // O = scale (O1 + P D), D as a bf16 pair (P_00 and P_22 are packed twice against
-          // [D_hi; D_lo]); O1 seeds the accumulator
-          const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
-          const short8v dl01 = cat(dl4[0], dl4[1]), dl23 = cat(dl4[2], dl4[3]);
-          float4v O2[4];
-          O2[0] = mfma32(cat(q00, q00), cat(d4[0], dl4[0]), O1[0]);
-          O2[1] = mfma32(p10, dl01, mfma32(p10, d01, O1[1]));
-          O2[2] = mfma32(cat(q22, q22), cat(d4[2], dl4[2]), mfma32(p20, dl01, mfma32(p20, d01, O1[2])));
-          O2[3] = mfma32(p32, dl23, mfma32(p32, d23, mfma32(p30, dl01, mfma32(p30, d01, O1[3]))));
-          // output: transpose each 16 x 16 block by an identity product so a lane holds four
-          // consecutive values of one token (the four products issue back to back), then 8-byte
-          // stores from a per-lane base and uniform offsets; only a partial last chunk masks
-          if (a.scale != 1.f) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) O2[tb] = a.scale * O2[tb];
-          }
-          short4v pk[4];
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) pk[tb] = tobf4(mfma16(tobf4(O2[tb]), I16, zero4()));
-          uint16_t *ob = obase + static_cast<long long>(c0) * tokstride;
-          if (n == kC) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
-          } else {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-              if (tb * 16 + l16 < n) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
-          }
-        }
-        if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
-      }
-      if (a.state_out != nullptr) {
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb)) =
-              make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
-      }
-    };
-    if constexpr (NVW == 1) {
-      value_loop(std::integral_constant<int, 0>{});
-    } else {
-      if (wave == 0) value_loop(std::integral_constant<int, 0>{});
-      else value_loop(std::integral_constant<int, 1>{});
-    }
-    return;
-  }
-
   // ============================== helper waves ==============================
   // One staging point per chunk: every item of chunk c + 1 is written to LDS from registers
   // loaded a full iteration earlier, then the loads of chunk c + 2 are issued.  Items are
   // 16-byte granules in blocks of 64 (one wave-wide load): 16 blocks each of q, k and an
-  // explicit write key (64 x 128 bf16), then the blocks of the 64 x BV value tile.  Block
-  // s * NHW + hw is slot s of helper wave hw, so everything about a block (source, LDS
-  // destination, row / column split) is wave-uniform.  Every slot loads and is staged
+  // explicit write key (64 x 128 bf16), then the blocks of the 64 x BV value tile.  The two
+  // helpers that form T's off-diagonal blocks (hw 0, 1) stage nothing, so their block products
+  // never wait behind staging writes (a wave's LDS operations complete in order); staging is
+  // bound by the LDS write rate, which the other helpers share.  Block s * NSW + sw is slot s
+  // of staging wave sw = hw - 2, so everything about a block (source, LDS destination, row /
+  // column split) is wave-uniform.  Every slot loads and is staged
   // unconditionally -- a slot past the last block repeats it without storing -- so the
   // registers of a load are first read one iteration after it was issued and the loads of
   // a chunk issue back to back.  Rows past the end of the sequence are read clamped to the
   // last row and zeroed when staged.
   constexpr int NBP = (NQ + NK + NR) / 64;     // blocks of 64 x 128 arrays
   constexpr int NB = NBP + NVI / 64;
-  constexpr int NSB = (NB + NHW - 1) / NHW;    // block slots per helper wave
+  constexpr int NSW = NHW - 2;                 // staging waves: helpers 2 .. NHW - 1
+  constexpr int NSB = (NB + NSW - 1) / NSW;    // block slots per staging wave
   constexpr int VSH = BV == 32 ? 2 : 1;        // log2(items per value-tile row)
   uint4 pa[NSB], pb[NSB];
 #pragma unroll
@@ -589,9 +348,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   float gla = 0.f, gbeta = 0.f;                // gates of token `lane` of the staged chunk
   const bool gate_wave = wave == kNW - 1;
   const int tok32 = H * kD;                    // token stride; 64 * tok32 < 2^31 (H <= 65535)
-  auto slot_block = [&](int s) { return min(s * NHW + hw, NB - 1); };
+  const int sw = hw - 2;
+  auto slot_block = [&](int s) __attribute__((always_inline)) { return max(0, min(s * NSW + sw, NB - 1)); };
   // item u of block blk: row u >> sh, column col0 + (u & msk) * 8
-  auto item_rc = [&](int blk, int &t, int &col) {
+  auto item_rc = [&](int blk, int &t, int &col) __attribute__((always_inline)) {
     const bool isv = blk >= NBP;
     const int u = (isv ? blk - NBP : blk & 15) * 64 + lane;
     t = isv ? u >> VSH : u >> 4;
@@ -621,7 +381,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     eoff[s] = static_cast<int>(reinterpret_cast<char *>(sm.e[0] + (CHAN ? sw128(t, col) : 0)) - smb);
   }
 
-  auto load_items = [&](int c) {
+  auto load_items = [&](int c) __attribute__((always_inline)) {
     const int c0 = c * kC, nm1 = min(kC, T - c0) - 1;
 #pragma unroll
     for (int s = 0; s < NSB; ++s) {
@@ -633,12 +393,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     if (DECAY) gla = a.log_alpha[gi];
     if (!CHAN) gbeta = a.beta[gi];
   };
-  auto stage_items = [&](int c, int buf) {
+  auto stage_items = [&](int c, int buf) __attribute__((always_inline)) {
     const int n = min(kC, T - c * kC);
 #pragma unroll
     for (int s = 0; s < NSB; ++s) {
       const int blk = slot_block(s);
-      const bool live = s * NHW + hw < NB;
+      const bool live = s * NSW + sw < NB;
       const bool isv = blk >= NBP, isk = !isv && (blk >> 4) == 1;
       uint4 x = pa[s];
       if (n < kC) {   // rows past the end of the sequence (read clamped) are zeroed
@@ -683,7 +443,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // diagonal block p of A = -L (strictly lower, fp32) as acc(N) and acc(N^T): the two products
   // run on the same operands, and each entry is scaled by exactly the operations of a_tile, so
   // acc(N^T) is the transpose of acc(N) bit for bit
-  auto a_diag = [&](int buf, int p, float4v &n, float4v &nt) {
+  auto a_diag = [&](int buf, int p, float4v &n, float4v &nt) __attribute__((always_inline)) {
     const uint16_t *E = CHAN ? sm.e[buf] : sm.k[buf];
     const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
     constexpr bool SYM = !CHAN && WK == kWkSame;   // E R^T = K K^T: each tile is its own transpose
@@ -721,7 +481,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   };
   // P tile job (blocks (ib, jb), jb <= ib, numbered row by row), computed transposed
   // (P^T = R Q^T) so each lane writes 4 columns of one row of P
-  auto p_tile = [&](int buf, int job) {
+  auto p_tile = [&](int buf, int job) __attribute__((always_inline)) {
     const uint16_t *R = (WK == kWkSame) ? sm.k[buf] : sm.r[buf];
     const int ib = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
     const int jb = job - ib * (ib + 1) / 2;
@@ -744,7 +504,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // write acc(X^T) of the 16 x 16 block (rb, cb) of T (buffer buf) as 8-byte rows (lane: row
   // rb*16 + l16, columns cb*16 + 4 l4 .. + 3), band-masked, as the pair (hi, lo): from fp32 values
   // (put_rows) or from the two parts already split (put_rows2; each part exactly bf16)
-  auto put_rows2 = [&](int buf, int rb, int cb, float4v xh, float4v xl, bool lower_only) {
+  auto put_rows2 = [&](int buf, int rb, int cb, float4v xh, float4v xl, bool lower_only) __attribute__((always_inline)) {
     const int i = rb * 16 + l16;
     float4v h, l;
 #pragma unroll
@@ -757,29 +517,31 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     *reinterpret_cast<short4v *>(&sm.t[buf][i][cb * 16 + 4 * l4]) = tobf4(h);
     *reinterpret_cast<short4v *>(&sm.tl[buf][i][cb * 16 + 4 * l4]) = tobf4(l);
   };
-  auto put_rows = [&](int buf, int rb, int cb, float4v xt, bool lower_only) {
+  auto put_rows = [&](int buf, int rb, int cb, float4v xt, bool lower_only) __attribute__((always_inline)) {
     const Pair x = split4(xt);
     put_rows2(buf, rb, cb, unbf4(x.h), unbf4(x.l), lower_only);
   };
   // acc(X^T) of a pair given in acc(X) (B operand) layout: each part transposed exactly by an
   // identity product
-  auto tr2 = [&](const Pair &x, float4v &th, float4v &tl) {
+  auto tr2 = [&](const Pair &x, float4v &th, float4v &tl) __attribute__((always_inline)) {
     th = mfma16(x.h, I16, zero4());
     tl = mfma16(x.l, I16, zero4());
   };
 
-  // preconditioner accumulator: helper threads ht < 256 own channels 2 p, 2 p + 1 (p = ht / 4)
-  // and tokens 16 s .. 16 s + 15 (s = ht % 4) of a chunk; the four segments of a channel pair
-  // are the four lanes of a quad.  The accumulator entering the chunk is kept in all four.
-  const bool pc_thread = ht < 256;
-  const int pc_p = ht >> 2, pc_seg = ht & 3;
+  // preconditioner accumulator: the first four staging waves (helpers 2..5); their thread
+  // pt = ht - 128 owns channels 2 p, 2 p + 1 (p = pt / 4) and tokens 16 s .. 16 s + 15
+  // (s = pt % 4) of a chunk; the four segments of a channel pair are the four lanes of a quad.
+  // The accumulator entering the chunk is kept in all four.
+  const int pt = ht - 128;
+  const bool pc_thread = STG && pt >= 0 && pt < 256;
+  const int pc_p = pt >> 2, pc_seg = pt & 3;
   float hc0 = 0.f, hc1 = 0.f;
   if (WK == kWkPrecond && pc_thread) {
     hc0 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p] : a.h0;
     hc1 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p + 1] : a.h0;
   }
 
-  if (nchunks > 0) load_items(0);
+  if (STG && nchunks > 0) load_items(0);
   for (int c = -1; c < nchunks; ++c) {
     const int cur = c & 1, nxt = (c + 1) & 1;
     const bool have_next = c + 1 < nchunks;
@@ -792,23 +554,22 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int qb = hw;   // column block of the lower-left quadrant formed by this wave
     // A layout of block (rb, kb) of T; B layout of block (kb, cb) by a transposing read; every
     // operand as its bf16 pair
-    auto arow = [&](int rb, int kb) {
+    auto arow = [&](int rb, int kb) __attribute__((always_inline)) {
       const int o = (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4;
       return Pair{ld4(&sm.t[cur][0][0] + o), ld4(&sm.tl[cur][0][0] + o)};
     };
-    auto bcol = [&](int kb, int cb) {
+    auto bcol = [&](int kb, int cb) __attribute__((always_inline)) {
       const int o = (kb * 16 + 4 * l4 + (l16 >> 2)) * kLdc + cb * 16 + 4 * (l16 & 3);
       return Pair{ldtr(&sm.t[cur][0][0] + o), ldtr(&sm.tl[cur][0][0] + o)};
     };
-    auto lrow = [&](int s2, int u) {
+    auto lrow = [&](int s2, int u) __attribute__((always_inline)) {
       return Pair{ld4(&sm.lba[s2 * 16 + l16][u * 16 + 4 * l4]), ld4(&sm.lbal[s2 * 16 + l16][u * 16 + 4 * l4])};
     };
-    auto aodp = [&](int j) { return Pair{ld4(&sm.aod[j][l16][4 * l4]), ld4(&sm.aodl[j][l16][4 * l4])}; };
-    // (the hi parts are requested before the staging writes, the lo parts after them)
+    auto aodp = [&](int j) __attribute__((always_inline)) { return Pair{ld4(&sm.aod[j][l16][4 * l4]), ld4(&sm.aodl[j][l16][4 * l4])}; };
     Pair o_a33, o_b22, o_a22, o_a32, o_a10, o_d, o_a11, o_l00, o_l01, o_l10, o_l11;
-    auto load_ops = [&](auto part) {
+    auto load_ops = [&](auto part) __attribute__((always_inline)) {
       constexpr bool LO = decltype(part)::value;
-      auto get = [&](Pair &x, const Pair &v) { (LO ? x.l : x.h) = LO ? v.l : v.h; };
+      auto get = [&](Pair &x, const Pair &v) __attribute__((always_inline)) { (LO ? x.l : x.h) = LO ? v.l : v.h; };
       get(o_a33, arow(3, 3));
       get(o_b22, bcol(2, 2));
       get(o_a22, arow(2, 2));
@@ -825,14 +586,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         get(o_d, bcol(1, 1));
       }
     };
-    if (c >= 0 && hw < 2) load_ops(std::false_type{});
-    if (have_next) {
+    if (!STG && c >= 0) {
+      load_ops(std::false_type{});
+      load_ops(std::true_type{});
+    }
+    if (STG && have_next) {
       stage_items(c + 1, nxt);
       if (c + 2 < nchunks) load_items(c + 2);
     }
     if (c >= 0) {
-      if (hw < 2) {
-        load_ops(std::true_type{});
+      if constexpr (!STG) {
         // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
         // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a, every product on bf16 pairs
         const Pair t32 = split4(mm2(o_a33, split4(mm2(o_a32, o_b22))));
@@ -864,7 +627,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       // P tiles (10 lower blocks) unless the value waves form them: jobs 8, 9 on the two T_ba
       // waves, 0..7 on the others
       if constexpr (!kPv) {
-        if (hw < 2) {
+        if constexpr (!STG) {
           p_tile(cur, 8 + hw);
         } else {
           p_tile(cur, hw - 2);
@@ -970,7 +733,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
       // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba (jobs
       // 0..5); a wave forms its share together (operands first, then the product chains).  Job
       // q of a batch is job0 + q * jstep; jobs past the last repeat it without storing.
-      auto a_jobs = [&](auto njc, int job0, int jstep) {
+      auto a_jobs = [&](auto njc, int job0, int jstep) __attribute__((always_inline)) {
         constexpr int NJ = decltype(njc)::value;
         const uint16_t *E = CHAN ? sm.e[nb] : sm.k[nb];
         const uint16_t *R = (WK == kWkSame) ? sm.k[nb] : sm.r[nb];
@@ -1014,23 +777,18 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           }
         }
       };
-      // With six helpers the two A waves would carry three jobs each against one diagonal
-      // inverse per other wave, so waves 0 and 1 (the lightest: their other work is before the
-      // second barrier) take jobs 4 and 5 after their inverse.
-      constexpr int NOW = NHW - 4;               // waves on A jobs only
-      constexpr bool kSplitA = NOW == 2;
-      if (hw < 4) {
-        // diagonal block hw of T: D = (I - A_pp)^-1
+      // The diagonal inverses (dependent chains of matrix-core products) run on helpers 0, 1 and
+      // the last two, the A blocks on the helpers between them; with two value waves (waves 0,
+      // 1) that puts the inverses on the SIMDs no value wave shares (a wave w runs on SIMD w % 4).
+      constexpr int NAW = NHW - 4;               // waves on the A blocks
+      if (hw < 2 || hw >= NHW - 2) {
+        // diagonal block pb of T: D = (I - A_pp)^-1
+        const int pb = hw < 2 ? hw : hw - NAW;
         float4v n, nt;
-        a_diag(nb, hw, n, nt);
-        put_rows(nb, hw, hw, diag_inverse_t(n, nt, lane), true);
-        if constexpr (kSplitA) {
-          if (hw < 2) a_jobs(std::integral_constant<int, 1>{}, 4 + hw, 1);
-        }
-      } else if constexpr (kSplitA) {
-        a_jobs(std::integral_constant<int, 2>{}, hw - 4, 2);
+        a_diag(nb, pb, n, nt);
+        put_rows(nb, pb, pb, diag_inverse_t(n, nt, lane), true);
       } else {
-        a_jobs(std::integral_constant<int, (6 + NOW - 1) / NOW>{}, hw - 4, NOW);
+        a_jobs(std::integral_constant<int, (6 + NAW - 1) / NAW>{}, hw - 2, NAW);
       }
     }
   }
@@ -1039,6 +797,307 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     a.pc_h_out[static_cast<long long>(bh) * kD + 2 * pc_p] = hc0;
     a.pc_h_out[static_cast<long long>(bh) * kD + 2 * pc_p + 1] = hc1;
   }
+}
+
+template <int BV, bool CHAN, bool DECAY, int WK>
+__global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
+  constexpr int NVW = BV / 16;             // value waves
+  constexpr int NVT = kD / BV;             // value tiles per head
+  constexpr int NHW = kNW - NVW;           // helper waves
+  constexpr int NVI = kC * BV / 8;         // V items (8 bf16 each)
+  constexpr int LDV = BV + 8;              // padded row stride of the V' tile
+  // staging items of 16 bytes: q, k, explicit write key (64 x 128 each), v tile (64 x BV)
+  constexpr int NQ = 1024, NK = 1024, NR = (WK == kWkExplicit) ? 1024 : 0;
+  constexpr bool SCALED_E = !CHAN;         // E = beta k: beta applied after the product
+  // with two value waves, P = tril(Q R^T) is formed by the value waves from the Q operands
+  // they already hold for O1 and the R operands: those of Y when R = k and E = beta k (scalar
+  // gains), else read beside them (channel gates: R = k, E = b (.) k; a preconditioned or
+  // explicit write key: R in its own array); with a single value wave, which would have to
+  // keep every R block, the helper waves form it
+  constexpr bool kPv = NVW == 2;
+  constexpr bool kRq = kPv && (CHAN || WK != kWkSame);   // P's R operands read separately
+  __shared__ Smem<BV, CHAN, WK> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave index as a provably wave-uniform (scalar) value: role dispatch below is then a
+  // scalar branch, and each role's loop (with its barriers) runs only in its own waves
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const bool vwave = wave < NVW;
+  const int hw = wave - NVW;               // helper wave index
+  const int ht = tid - NVW * 64;           // helper thread index
+  const short4v I16 = ident4(lane);
+
+  // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
+  // (the host bounds the grid to 2^22 workgroups, so these fit in 32 bits)
+  const int G = static_cast<int>(gridDim.x);
+  const int bid = static_cast<int>(blockIdx.x);
+  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
+  const int H = a.H, T = a.T;
+  const int b = bh / H, h = bh % H;
+  const long long tokstride = static_cast<long long>(H) * kD;
+  const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
+  const long long gate0 = static_cast<long long>(b) * T * H + h;
+  const int nchunks = (T + kC - 1) / kC;
+  const int N = a.N;
+  auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
+
+  const uint16_t *gq = static_cast<const uint16_t *>(a.q);
+  const uint16_t *gk = static_cast<const uint16_t *>(a.k);
+  const uint16_t *gv = static_cast<const uint16_t *>(a.v);
+  const uint16_t *gwk = static_cast<const uint16_t *>(a.write_key);
+  const uint16_t *ger = static_cast<const uint16_t *>(a.erase);
+  const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
+  uint16_t *gout = static_cast<uint16_t *>(a.out);
+
+  // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
+  for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = (&sm.tl[0][0][0])[i] = 0;
+  for (int i = tid; i < kC * kLdc; i += kNT) (&sm.p[0][0])[i] = 0;
+
+  // Each role runs its own loop with the same barrier sequence, so the compiler allocates
+  // registers for one role's loop-carried state at a time.
+  if (vwave) {
+    // the wave index is a template constant inside the value-wave loop, so every wave-dependent
+    // choice below (state rows, the P blocks a wave forms) is static
+    auto value_loop = [&](auto wc) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      // ---------------- value waves: S^T tiles in accumulators ----------------
+      // Tile cb holds S^T[c][v = 16 W + l16] for the channels c = chan(16 cb + 4 l4 + r) =
+      // 32 (cb / 2) + 8 l4 + 4 (cb % 2) + r: with this order the bf16 concatenation of tiles
+      // 2j and 2j + 1 (the K = 32 B operand of Y and O1) covers channels 32 j + 8 l4 .. + 7 in
+      // natural order, so the E / Q / K operands beside it are single 16-byte LDS reads; the
+      // update reads R^T in the same order (optr_state) and the state is loaded and stored
+      // through it once.
+      float4v st[8];
+      const int vrow = v0 + 16 * W + l16;   // this lane's state row
+      // output element (token l16 of a 16-token block, values 4 l4 .. + 3 of this wave's rows)
+      uint16_t *const obase = gout + head0 + static_cast<long long>(l16) * tokstride + v0 + 16 * W + 4 * l4;
+      auto chan0 = [&](int cb) __attribute__((always_inline)) { return 32 * (cb >> 1) + 8 * l4 + 4 * (cb & 1); };
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        st[cb] = zero4();
+        if (a.state_in != nullptr) {
+          const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb));
+          st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
+        }
+      }
+      for (int c = -1; c < nchunks; ++c) {
+        const int cur = c & 1;
+        const int c0 = c * kC;
+        const int n = min(kC, T - c0);
+        short4v x4[4];
+        float4v O1[4];
+        __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
+        if (c >= 0) {
+          // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y.  The
+          // operands of block tb + 1 are read while block tb is multiplied.  With kPv the K
+          // operands of earlier blocks are kept and the blocks (tb, jb), jb <= tb, of P are
+          // formed here, split between the value waves by column block.
+          short8v sb[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sb[j] = cat(tobf4(st[2 * j]), tobf4(st[2 * j + 1]));
+          const uint16_t *E = CHAN ? sm.e[cur] : sm.k[cur];
+          // one register set per block for the E operands (the wave keeps those of its own P column
+          // blocks alive; the others die after their block), double-buffered Q operands
+          short8v ev[4][4], qv[2][4];
+          short8v kq[2][4];   // kRq: R operands of this wave's two P column blocks
+          // kPv: P column blocks are split 5 / 5 tiles between two value waves (blocks 0 and 3 to
+          // wave 0, 1 and 2 to wave 1)
+          constexpr auto p_owner = [](int jb) { return NVW == 1 ? 0 : (jb == 0 || jb == 3) ? 0 : 1; };
+          constexpr auto p_slot = [](int jb) { return NVW == 1 ? jb : (jb < 2 ? 0 : 1); };
+          short4v vt[2];
+          // Everything a block reads from LDS is read while the previous block is multiplied:
+          // LDS reads complete in order, so a read issued inside a block would also wait for
+          // the prefetch issued before it.
+          float4 egv[2], btv[2];
+          float giv[2];
+          float4 gjv[4 / NVW];   // kPv: cumulative decay at the columns of this wave's P blocks
+          auto load_e = [&](int tb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ev[tb][j] = opn128(E, tb * 16 + l16, 32 * j, l4);
+          };
+          auto load_ops = [&](int tb, int slot) __attribute__((always_inline)) {
+            if constexpr (!kPv) load_e(tb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[slot][j] = opn128(sm.q[cur], tb * 16 + l16, 32 * j, l4);
+            // V' block (rows t, columns v) in the accumulator layout, read transposed
+            vt[slot] = ldtr(&sm.vp[cur][tb * 16 + 4 * l4 + (l16 >> 2)][16 * W + 4 * (l16 & 3)]);
+            if (kRq && p_owner(tb) == W) {
+              const uint16_t *Rp = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) kq[p_slot(tb)][j] = opn128(Rp, tb * 16 + l16, 32 * j, l4);
+            }
+            egv[slot] = ld4f(&sm.eg[cur][tb * 16 + 4 * l4]);
+            if (!CHAN) btv[slot] = ld4f(&sm.beta[cur][tb * 16 + 4 * l4]);
+            if (kPv) giv[slot] = sm.g2[cur][tb * 16 + l16];
+          };
+          if constexpr (kPv) {
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+              if (p_owner(jb) == W) gjv[p_slot(jb)] = ld4f(&sm.g2[cur][jb * 16 + 4 * l4]);
+          }
+          load_ops(0, 0);
+          if constexpr (kPv) {
+            // the E operands of every block stay live for P anyway: all of them are requested
+            // now, so the phase waits for one LDS round trip instead of one per block
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) load_e(tb);
+          }
+          GDR_FENCE();
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const int sl = tb & 1;
+            if (tb + 1 < 4) load_ops(tb + 1, sl ^ 1);
+            GDR_FENCE();   // the prefetch issues before this block's products
+            float4v y = zero4(), o = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              y = mfma32(ev[tb][j], sb[j], y);
+              o = mfma32(qv[sl][j], sb[j], o);
+            }
+            const float4 eg = egv[sl];
+            float4v xv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xv[r] = bf(static_cast<uint16_t>(vt[sl][r])) - (&eg.x)[r] * y[r];
+            if (!CHAN) {   // V' = beta v and E = beta k: beta applied to the difference
+              const float4 bt = btv[sl];
+              xv = float4v{bt.x * xv[0], bt.y * xv[1], bt.z * xv[2], bt.w * xv[3]};
+            }
+            x4[tb] = tobf4(xv);
+            O1[tb] = float4v{eg.x * o[0], eg.y * o[1], eg.z * o[2], eg.w * o[3]};
+            if constexpr (kPv) {
+              // P^T block (jb, tb) = K_jb Q_tb^T: lane holds P[i = tb*16 + l16][j = jb*16 + 4 l4 + r]
+              const int i = tb * 16 + l16;
+              const float gi = giv[sl];
+#pragma unroll
+              for (int jb = 0; jb <= tb; ++jb) {
+                if (p_owner(jb) != W) continue;
+                float4v pt = zero4();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pt = mfma32(kRq ? kq[p_slot(jb)][j] : ev[jb][j], qv[sl][j], pt);
+                const float4 gj = gjv[p_slot(jb)];
+                float4v pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int jj = jb * 16 + 4 * l4 + r;
+                  const float x = DECAY ? pt[r] * decay2(gi - (&gj.x)[r]) : pt[r];
+                  pv[r] = (jb < tb || jj <= i) ? x : 0.f;   // only the diagonal block is masked
+                }
+                *reinterpret_cast<short4v *>(&sm.p[i][jb * 16 + 4 * l4]) = tobf4(pv);
+              }
+            }
+            GDR_FENCE();
+          }
+        }
+        __syncthreads();   // (2) T(c), P(c) complete
+        if (c >= 0) {
+          // every LDS operand of this phase is read up front: T and P blocks, R^T for the update.
+          // T is held as a bf16 pair (hi + lo): the diagonal blocks pack hi and lo into one K = 32
+          // operand (the other K half of a diagonal block is zero), the others take one operand
+          // per part.  (T and P are lower triangular; their blocks above the diagonal stay zero.)
+          const uint16_t *Tm = &sm.t[cur][0][0], *Tl = &sm.tl[cur][0][0], *Pm = &sm.p[0][0];
+          const uint16_t *Rk = (WK == kWkSame) ? sm.k[cur] : sm.r[cur];
+          auto blk = [&](const uint16_t *M, int rb, int kb) __attribute__((always_inline)) { return ld4(M + (rb * 16 + l16) * kLdc + kb * 16 + 4 * l4); };
+          const short8v t00 = cat(blk(Tm, 0, 0), blk(Tl, 0, 0));
+          const short8v t10 = cat(blk(Tm, 1, 0), blk(Tm, 1, 1)), t10l = cat(blk(Tl, 1, 0), blk(Tl, 1, 1));
+          const short8v t20 = cat(blk(Tm, 2, 0), blk(Tm, 2, 1)), t20l = cat(blk(Tl, 2, 0), blk(Tl, 2, 1));
+          const short8v t22 = cat(blk(Tm, 2, 2), blk(Tl, 2, 2));
+          const short8v t30 = cat(blk(Tm, 3, 0), blk(Tm, 3, 1)), t30l = cat(blk(Tl, 3, 0), blk(Tl, 3, 1));
+          const short8v t32 = cat(blk(Tm, 3, 2), blk(Tm, 3, 3)), t32l = cat(blk(Tl, 3, 2), blk(Tl, 3, 3));
+          const short4v q00 = blk(Pm, 0, 0), q22 = blk(Pm, 2, 2);
+          const short8v p10 = opsp(Pm, kLdc, 16 + l16, 0, l4);
+          const short8v p20 = opsp(Pm, kLdc, 32 + l16, 0, l4);
+          const short8v p30 = opsp(Pm, kLdc, 48 + l16, 0, l4), p32 = opsp(Pm, kLdc, 48 + l16, 32, l4);
+          short8v ra[4], rb[4];   // R^T operands of the first half of the update
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            ra[cb] = optr_state(Rk, cb, 0, lane);
+            rb[cb] = optr_state(Rk, cb, 32, lane);
+          }
+          float4 wdv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wdv[j] = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
+          const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
+
+          // D = T X  (T_hi X + T_lo X)
+          const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
+          float4v D[4];
+          D[0] = mfma32(t00, cat(x4[0], x4[0]), zero4());
+          D[1] = mfma32(t10l, x01, mfma32(t10, x01, zero4()));
+          D[2] = mfma32(t22, cat(x4[2], x4[2]), mfma32(t20l, x01, mfma32(t20, x01, zero4())));
+          D[3] = mfma32(t32l, x23, mfma32(t32, x23, mfma32(t30l, x01, mfma32(t30, x01, zero4()))));
+          // state update S^T <- e^{g_C} S^T + R^T (wd (.) D), interleaved with O2 = P D
+          short4v w4[4], d4[4], dl4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            w4[j] = tobf4(float4v{wdv[j].x * D[j][0], wdv[j].y * D[j][1], wdv[j].z * D[j][2], wdv[j].w * D[j][3]});
+            const Pair dp = split4(D[j]);
+            d4[j] = dp.h;
+            dl4[j] = dp.l;
+          }
+          const short8v w01 = cat(w4[0], w4[1]), w23 = cat(w4[2], w4[3]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            float4v acc = st[cb];
+            if (DECAY) acc *= gC;
+            st[cb] = mfma32(rb[cb], w23, mfma32(ra[cb], w01, acc));
+            ra[cb] = optr_state(Rk, cb + 4, 0, lane);   // second half, read behind the first
+            rb[cb] = optr_state(Rk, cb + 4, 32, lane);
+          }
+#pragma unroll
+          for (int cb = 4; cb < 8; ++cb) {
+            float4v acc = st[cb];
+            if (DECAY) acc *= gC;
+            st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
+          }
+          // O = scale (O1 + P D), D as a bf16 pair (P_00 and P_22 are packed twice against
+          // [D_hi; D_lo]); O1 seeds the accumulator
+          const short8v d01 = cat(d4[0], d4[1]), d23 = cat(d4[2], d4[3]);
+          const short8v dl01 = cat(dl4[0], dl4[1]), dl23 = cat(dl4[2], dl4[3]);
+          float4v O2[4];
+          O2[0] = mfma32(cat(q00, q00), cat(d4[0], dl4[0]), O1[0]);
+          O2[1] = mfma32(p10, dl01, mfma32(p10, d01, O1[1]));
+          O2[2] = mfma32(cat(q22, q22), cat(d4[2], dl4[2]), mfma32(p20, dl01, mfma32(p20, d01, O1[2])));
+          O2[3] = mfma32(p32, dl23, mfma32(p32, d23, mfma32(p30, dl01, mfma32(p30, d01, O1[3]))));
+          // output: transpose each 16 x 16 block by an identity product so a lane holds four
+          // consecutive values of one token (the four products issue back to back), then 8-byte
+          // stores from a per-lane base and uniform offsets; only a partial last chunk masks
+          if (a.scale != 1.f) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) O2[tb] = a.scale * O2[tb];
+          }
+          short4v pk[4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) pk[tb] = tobf4(mfma16(tobf4(O2[tb]), I16, zero4()));
+          uint16_t *ob = obase + static_cast<long long>(c0) * tokstride;
+          if (n == kC) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
+          } else {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              if (tb * 16 + l16 < n) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
+          }
+        }
+        if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
+      }
+      if (a.state_out != nullptr) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb)) =
+              make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+      }
+    };
+    if constexpr (NVW == 1) value_loop(std::integral_constant<int, 0>{});
+    else if (wave == 0) value_loop(std::integral_constant<int, 0>{});
+    else value_loop(std::integral_constant<int, 1>{});
+    return;
+  }
+
+  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, true>(sm, a);
+  else helper_loop<BV, CHAN, DECAY, WK, false>(sm, a);
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
