@@ -17,6 +17,6 @@ from ._binding import (  # noqa: F401
     GdrError, gdr_desc_t, gdr_inputs_t, gdr_grads_t,
     lib, lib_path, make_desc,
     gdr_chunk_fwd, gdr_recurrent_step, gdr_validate, gdr_chunk_fwd_impl,
-    gdr_chunk_bwd, gdr_chunk_bwd_workspace_size, gdr_validate_bwd,
+    gdr_chunk_bwd, gdr_chunk_bwd_workspace_size, gdr_validate_bwd, gdr_chunk_bwd_noalloc_max_workspace,
     gdr_status_str, gdr_last_error, gdr_abi_version,
 )

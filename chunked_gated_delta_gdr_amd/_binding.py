@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_void_p, P(gdr_grads_t), ctypes.c_void_p, ctypes.c_uint64,
                                     ctypes.c_void_p]
         L.gdr_chunk_bwd.restype = ctypes.c_int
+        L.gdr_chunk_bwd_noalloc.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, P(gdr_grads_t), ctypes.c_void_p]
+        L.gdr_chunk_bwd_noalloc.restype = ctypes.c_int
+        L.gdr_chunk_bwd_noalloc_max_workspace.argtypes = []
+        L.gdr_chunk_bwd_noalloc_max_workspace.restype = ctypes.c_uint64
         L.gdr_chunk_bwd_workspace_size.argtypes = [P(gdr_desc_t)]
         L.gdr_chunk_bwd_workspace_size.restype = ctypes.c_uint64
         L.gdr_validate_bwd.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
@@ -134,6 +139,10 @@ def gdr_validate(desc: gdr_desc_t, inputs: gdr_inputs_t, state_in=None, out=None
 
 def gdr_chunk_bwd_workspace_size(desc: gdr_desc_t) -> int:
     return int(lib().gdr_chunk_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def gdr_chunk_bwd_noalloc_max_workspace() -> int:
+    return int(lib().gdr_chunk_bwd_noalloc_max_workspace())
 
 
 def gdr_validate_bwd(desc: gdr_desc_t, inputs: gdr_inputs_t, state_in=None, d_out=None,
@@ -311,14 +320,16 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
                   pc_eps: float = 1e-3, pc_h0: float = 1.0, pc_t0: int = 0,
                   state_in=None, d_state_out=None, want_dstate_in: bool = True,
                   chunk: int = 64, neumann_order: int = -1, scale: float = 1.0, workspace=None,
-                  stream=None) -> dict:
+                  stream=None, noalloc: bool = False) -> dict:
     """Gradients through ``gdr_chunk_fwd`` on torch tensors.  ``d_out`` [B, T, H, Dv] (io dtype)
     and ``d_state_out`` [B, H, Dv, Dk] fp32 (or None) are the loss gradients of the forward's
     outputs.  Returns a dict of fp32 tensors: dq, dk, dv, and as the variant has them dbeta |
     derase, dwrite, dlog_alpha, dwrite_key, dpc_h_in (``precond``), and dstate_in (if
     ``want_dstate_in``).  ``neumann_order`` = N >= 0 differentiates the forward with the
     band-limited T.  The workspace (uint8, gdr_chunk_bwd_workspace_size bytes) is allocated
-    when not given."""
+    when not given.  ``noalloc`` calls gdr_chunk_bwd_noalloc instead, whose workspace is the
+    library's own scratch array (no workspace argument; the gradient tensors are still
+    allocated here unless the caller marshals the C call itself)."""
     torch = _torch()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -369,6 +380,13 @@ def gdr_chunk_bwd(q, k, v, d_out, *, beta=None, log_alpha=None, erase=None, writ
     grads = gdr_grads_t(*[_ptr(g.get(name)) for name, _ in gdr_grads_t._fields_])
     ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
                        _ptr(write_key), _ptr(pc_h_in) if precond else None, None)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        st = lib().gdr_chunk_bwd_noalloc(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(d_out),
+                                         _ptr(d_state_out), ctypes.byref(grads), _stream(stream, dev))
+        _raise(st)
+        return g
     nbytes = gdr_chunk_bwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

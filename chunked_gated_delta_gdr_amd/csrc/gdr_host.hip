@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -90,6 +91,33 @@ BwdLayout bwd_layout(const gdr_desc_t &d) {
   L.total = L.dD + (band ? tk : 0u);
   L.NC = static_cast<int>(NC);
   return L;
+}
+
+// Scratch memory of gdr_chunk_bwd_noalloc: a file-scope device array, one copy on every GPU the
+// library runs on, kept until the process ends.  In host code its name is a host-side stand-in,
+// not a device address: the address of a GPU's copy is taken once per device with
+// hipGetSymbolAddress (that device current) and only that pointer is handed to kernels.
+constexpr uint64_t kScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+gdr_status_t scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDR_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ENOTSUP, "device ordinal %d (max %d)", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(GDR_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
 }
 
 }  // namespace
@@ -416,6 +444,25 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
     e = gdr::launch_bwd_pc_grad(b, d->io_dtype, s);
   if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+uint64_t gdr_chunk_bwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+gdr_status_t gdr_chunk_bwd_noalloc(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+                                   const void *d_out, const float *d_state_out, const gdr_grads_t *g,
+                                   void *stream) {
+  // the same validation, kernels and results as gdr_chunk_bwd, with the workspace in this
+  // GPU's scratch array; nothing is allocated
+  if (d == nullptr || d->struct_size != sizeof(gdr_desc_t))
+    return fail(GDR_EINVAL, "desc must be non-NULL with struct_size = %zu", sizeof(gdr_desc_t));
+  const uint64_t need = gdr_chunk_bwd_workspace_size(d);
+  if (need > kScratchBytes)
+    return fail(GDR_ENOTSUP, "the backward needs %llu bytes of workspace; the no-allocation entry point holds %llu",
+                static_cast<unsigned long long>(need), static_cast<unsigned long long>(kScratchBytes));
+  void *ws = nullptr;
+  const gdr_status_t st = scratch_address(&ws);
+  if (st != GDR_OK) return st;
+  return gdr_chunk_bwd(d, in, state_in, d_out, d_state_out, g, ws, kScratchBytes, stream);
 }
 
 gdr_status_t gdr_recurrent_step(const gdr_desc_t *d, const gdr_inputs_t *in, float *state, void *out,

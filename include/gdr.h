@@ -249,6 +249,28 @@ gdr_status_t gdr_chunk_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in, const
  * floats) and dD (B T H Dv floats), each section 256-byte aligned.  No HIP call. */
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *desc);
 
+/*
+ * gdr_chunk_bwd_noalloc -- gdr_chunk_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving or training loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, validation, kernels and results as gdr_chunk_bwd, without the workspace: the
+ * workspace is a file-scope device array of gdr_chunk_bwd_noalloc_max_workspace() bytes
+ * (64 MiB) inside the library, one copy per GPU, held until the process ends.  The call
+ * allocates and frees nothing; the first call on a device looks up that device's copy
+ * (hipGetSymbolAddress), later calls reuse it.  Descriptors whose
+ * gdr_chunk_bwd_workspace_size exceeds the array return GDR_ENOTSUP before anything is
+ * launched (at Dk = Dv = 128, C = 64 the workspace is about 290 KB per (batch, head, chunk):
+ * some 225 of them, e.g. B = 1, H = 4, T = 3584).  Every call on one GPU shares its array, so
+ * calls that overlap in time on one GPU (other streams, other threads) race: order them, e.g.
+ * on one stream.  Nothing in the array needs clearing between calls.
+ */
+gdr_status_t gdr_chunk_bwd_noalloc(const gdr_desc_t *desc, const gdr_inputs_t *in, const float *state_in,
+                                   const void *d_out, const float *d_state_out, const gdr_grads_t *grads,
+                                   void *stream);
+
+/* Size in bytes of the scratch array gdr_chunk_bwd_noalloc uses (no HIP call). */
+uint64_t gdr_chunk_bwd_noalloc_max_workspace(void);
+
 /* gdr_chunk_bwd's argument check on its own (no HIP call). */
 gdr_status_t gdr_validate_bwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
                               const float *state_in, const void *d_out, const float *d_state_out,

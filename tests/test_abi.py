@@ -370,3 +370,18 @@ def test_bwd_preconditioner_arguments():
     assert call_validate_bwd(d, ins=dict(pc_h_in=BASE + 31 * MB), grads=dict(dpc_h_in=BASE + 31 * MB)) == G.GDR_EINVAL
     assert "overlaps" in G.gdr_last_error()
     assert call_validate_bwd(d, grads=dict(dpc_h_in=BASE + 32 * MB + 2)) == G.GDR_EINVAL
+
+
+def test_noalloc_backward_rejects_before_any_hip_call():
+    """gdr_chunk_bwd_noalloc: a descriptor whose workspace exceeds the scratch array is refused
+    with GDR_ENOTSUP before the library touches the GPU (so this runs without one)."""
+    cap = G.gdr_chunk_bwd_noalloc_max_workspace()
+    assert cap == 64 << 20
+    L = G.lib()
+    d = desc(B=4, H=16, T=4096, Dk=128, Dv=128)
+    assert G.gdr_chunk_bwd_workspace_size(d) > cap
+    ins, gr, a = bwd_args(d)
+    st = L.gdr_chunk_bwd_noalloc(ctypes.byref(d), ctypes.byref(ins), None, a["d_out"], None, ctypes.byref(gr), None)
+    assert st == G.GDR_ENOTSUP
+    assert "no-allocation" in G.gdr_last_error()
+    assert L.gdr_chunk_bwd_noalloc(None, ctypes.byref(ins), None, a["d_out"], None, ctypes.byref(gr), None) == G.GDR_EINVAL
