@@ -195,15 +195,7 @@ __device__ __forceinline__ float4v unbf4(short4v v) {
   return float4v{bf(static_cast<uint16_t>(v[0])), bf(static_cast<uint16_t>(v[1])), bf(static_cast<uint16_t>(v[2])),
                  bf(static_cast<uint16_t>(v[3]))};
 }
-// c + X Y for 16 x 16 X, Y given as fp32 acc(X^T) (the A operand of X) and acc(Y), each carried
-// as a bf16 pair hi + lo (about 16 significant bits).  The hi / lo pair of X fills the K slots
-// a K = 16 product would pad with zeros: X_hi Y_hi + X_lo Y_hi in one instruction, X_hi Y_lo in
-// a second (the X_lo Y_lo term, ~2^-16 relative, is dropped).
-__device__ __forceinline__ float4v mfma_split(float4v a, float4v b, float4v c) {
-  const short4v ah = tobf4(a), bh = tobf4(b);
-  const short4v al = tobf4(a - unbf4(ah)), bl = tobf4(b - unbf4(bh));
-  return mfma16(ah, bl, mfma32(cat(ah, al), cat(bh, bh), c));
-}
+
 // fp32 values as a bf16 pair: x[0] = bf16(v), x[1] = bf16(v - x[0])
 struct Pair {
   short4v h, l;
@@ -212,7 +204,10 @@ __device__ __forceinline__ Pair split4(float4v v) {
   const short4v h = tobf4(v);
   return Pair{h, tobf4(v - unbf4(h))};
 }
-// c + X Y for operands already held as pairs (x: A operand of X, y: B operand of Y)
+// c + X Y for 16 x 16 X, Y held as bf16 pairs (x: the A operand of X, y: the B operand of Y),
+// about 16 significant bits each.  The hi / lo pair of X fills the K slots a K = 16 product would
+// pad with zeros: X_hi Y_hi + X_lo Y_hi in one instruction, X_hi Y_lo in a second (the X_lo Y_lo
+// term, ~2^-16 relative, is dropped).
 __device__ __forceinline__ float4v mm2(const Pair &x, const Pair &y, float4v c) {
   return mfma16(x.h, y.l, mfma32(cat(x.h, x.l), cat(y.h, y.h), c));
 }
@@ -257,15 +252,19 @@ __device__ __forceinline__ float4v diag_inverse_t(float4v n, float4v nt, int lan
     const float y0 = fmaf(y3, n30, fmaf(y2, n20, fmaf(y1, n10, one0)));
     dt1 = dq ? float4v{y0, y1, y2, y3} : zero4();
   }
-  // acc(N_m^T): lane (row l16, column block l4) of N
+  // acc(N_m^T): lane (row l16, column block l4) of N; every factor is split into its bf16 pair
+  // once and reused
   const int rb4 = l16 >> 2;
-  const float4v n1t = ((rb4 & 1) != 0 && l4 == rb4 - 1) ? nt : zero4();
-  const float4v n2t = ((l16 >> 3) == 1 && (l4 >> 1) == 0) ? nt : zero4();
-  const float4v z1 = mfma_split(n1t, d1, zero4());   // N_1 D_1
-  const float4v d2 = mfma_split(dt1, z1, d1);        // D_2 = D_1 + D_1 Z_1
-  const float4v dt2 = mfma_split(z1, dt1, dt1);      // D_2^T = D_1^T + Z_1^T D_1^T
-  const float4v z2 = mfma_split(n2t, d2, zero4());   // N_2 D_2
-  return mfma_split(z2, dt2, dt2);                   // D^T = D_2^T + Z_2^T D_2^T
+  const bool m1 = (rb4 & 1) != 0 && l4 == rb4 - 1, m2 = (l16 >> 3) == 1 && (l4 >> 1) == 0;
+  const Pair ntp = split4(nt);
+  const short4v zs = {0, 0, 0, 0};
+  const Pair n1p{m1 ? ntp.h : zs, m1 ? ntp.l : zs}, n2p{m2 ? ntp.h : zs, m2 ? ntp.l : zs};
+  const Pair d1p = split4(d1), dt1p = split4(dt1);
+  const Pair z1p = split4(mm2(n1p, d1p));            // N_1 D_1
+  const float4v d2 = mm2(dt1p, z1p, d1);             // D_2 = D_1 + D_1 Z_1
+  const float4v dt2 = mm2(z1p, dt1p, dt1);           // D_2^T = D_1^T + Z_1^T D_1^T
+  const Pair z2p = split4(mm2(n2p, split4(d2)));     // N_2 D_2
+  return mm2(z2p, split4(dt2), dt2);                 // D^T = D_2^T + Z_2^T D_2^T
 }
 
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
@@ -358,12 +357,14 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
     col = isv ? (u & (BV / 8 - 1)) * 8 : (u & 15) * 8;
   };
 
-  // Per-slot addressing, fixed for the whole sequence: this lane's item of chunk 0 in global
-  // memory (row srow of the chunk) and its LDS byte offset in buffer 0 of its array, so the
-  // per-chunk work is a clamp, one multiply-add, the loads and the stores.
-  const uint16_t *gsrc[NSB], *gsrc2[NSB];
-  int srow[NSB], loff[NSB], lstr[NSB], eoff[NSB];
+  // Per-slot addressing, fixed for the whole sequence: the slot's source array (a wave-uniform
+  // choice: 0 q, 1 k, 2 explicit write key, 3 the value tile), this lane's byte offset from the
+  // chunk's first row of the head in that array (32 bits: 64 rows of at most 65535 heads of 128
+  // channels) and its LDS byte offset in buffer 0.  Per chunk that leaves one scalar base per
+  // array, the loads and the stores; a slot's offset is clamped only on a partial last chunk.
+  int sarr[NSB], srow[NSB], gofs[NSB], loff[NSB], lstr[NSB], eoff[NSB];
   char *const smb = reinterpret_cast<char *>(&sm);
+  const int rowb = static_cast<int>(tokstride) * 2;   // bytes between two tokens' rows
 #pragma unroll
   for (int s = 0; s < NSB; ++s) {
     const int blk = slot_block(s);
@@ -371,10 +372,9 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
     const int arr = blk >> 4;
     int t, col;
     item_rc(blk, t, col);
+    sarr[s] = isv ? 3 : arr;
     srow[s] = t;
-    const long long g0 = head0 + (isv ? v0 : 0) + col;
-    gsrc[s] = (isv ? gv : arr == 0 ? gq : arr == 1 ? gk : gwk) + g0;
-    gsrc2[s] = CHAN ? (isv ? gwr : ger) + g0 : gsrc[s];
+    gofs[s] = t * rowb + ((isv ? v0 : 0) + col) * 2;
     uint16_t *d0 = isv ? &sm.vp[0][t][col] : (arr == 0 ? sm.q[0] : arr == 1 ? sm.k[0] : sm.r[0]) + sw128(t, col);
     loff[s] = static_cast<int>(reinterpret_cast<char *>(d0) - smb);
     lstr[s] = isv ? static_cast<int>(sizeof(sm.vp[0])) : kC * kD * 2;
@@ -383,11 +383,17 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
 
   auto load_items = [&](int c) __attribute__((always_inline)) {
     const int c0 = c * kC, nm1 = min(kC, T - c0) - 1;
+    const long long cb = head0 + static_cast<long long>(c0) * tokstride;   // the chunk's first row
+    const char *const bq = reinterpret_cast<const char *>(gq + cb), *const bk = reinterpret_cast<const char *>(gk + cb);
+    const char *const bw = reinterpret_cast<const char *>(gwk + cb), *const bv = reinterpret_cast<const char *>(gv + cb);
+    const char *const be = reinterpret_cast<const char *>(ger + cb), *const bwv = reinterpret_cast<const char *>(gwr + cb);
 #pragma unroll
     for (int s = 0; s < NSB; ++s) {
-      const long long off = static_cast<long long>(c0 + min(srow[s], nm1)) * tokstride;
-      pa[s] = *reinterpret_cast<const uint4 *>(gsrc[s] + off);
-      if (CHAN) pb[s] = *reinterpret_cast<const uint4 *>(gsrc2[s] + off);
+      // rows past the end of the sequence read the last row (and are zeroed when staged)
+      const uint32_t o = static_cast<uint32_t>(gofs[s] - max(0, srow[s] - nm1) * rowb);
+      const char *const base = sarr[s] == 0 ? bq : sarr[s] == 1 ? bk : sarr[s] == 2 ? bw : bv;
+      pa[s] = *reinterpret_cast<const uint4 *>(base + o);
+      if (CHAN) pb[s] = *reinterpret_cast<const uint4 *>((sarr[s] == 3 ? bwv : be) + o);
     }
     const long long gi = gate0 + static_cast<long long>(c0) * H + min(lane, nm1) * H;
     if (DECAY) gla = a.log_alpha[gi];
@@ -777,18 +783,18 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
           }
         }
       };
-      // The diagonal inverses (dependent chains of matrix-core products) run on helpers 0, 1 and
-      // the last two, the A blocks on the helpers between them; with two value waves (waves 0,
-      // 1) that puts the inverses on the SIMDs no value wave shares (a wave w runs on SIMD w % 4).
+      // The four diagonal inverses (dependent chains of matrix-core products) run on helpers
+      // 2..5, one per SIMD (wave w runs on the SIMD of wave w + 4), the A blocks on the others
       constexpr int NAW = NHW - 4;               // waves on the A blocks
-      if (hw < 2 || hw >= NHW - 2) {
-        // diagonal block pb of T: D = (I - A_pp)^-1
-        const int pb = hw < 2 ? hw : hw - NAW;
-        float4v n, nt;
-        a_diag(nb, pb, n, nt);
-        put_rows(nb, pb, pb, diag_inverse_t(n, nt, lane), true);
+      if (hw >= 2 && hw < 6) {
+        if constexpr (STG) {
+          // diagonal block hw - 2 of T: D = (I - A_pp)^-1
+          float4v n, nt;
+          a_diag(nb, hw - 2, n, nt);
+          put_rows(nb, hw - 2, hw - 2, diag_inverse_t(n, nt, lane), true);
+        }
       } else {
-        a_jobs(std::integral_constant<int, (6 + NAW - 1) / NAW>{}, hw - 2, NAW);
+        a_jobs(std::integral_constant<int, (6 + NAW - 1) / NAW>{}, hw < 2 ? hw : hw - 4, NAW);
       }
     }
   }
