@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "tokens/s chunked gated-delta fwd (B4 H16 T4096 d128 bf16); % MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+ENGINE_CLOCK_HZ = 2.4e9         # MI355X peak engine clock (256 CUs x 4 SIMDs)
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 KERNEL_SOURCES = {
@@ -117,8 +118,12 @@ def mfma_summary(args):
         "alg_flop_per_dispatch": alg_flops(s),
         "cu": 256, "simd_per_cu": 4,
     }
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
-        rec["mfma_busy_frac"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * 256 * 4)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+        # the busy count is summed over every SIMD (it is the same on every dispatch: a count of
+        # issued matrix-core cycles, not a sample); GRBM_GUI_ACTIVE sums the XCDs' clocks over the
+        # counter window, which is wider than the kernel, so the bench divides the per-SIMD
+        # figure by its own launch time at the peak engine clock instead
+        rec["mfma_busy_cycles_per_simd"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (256 * 4)
     out = os.path.join(ROOT, "profiles", mfma_counter_file(args.workload, args.impl_name))
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
@@ -612,14 +617,17 @@ def main():
                         chunk=s.chunk, neumann_order=args.neumann, residual_steps=args.residual,
                         impl=args.impl, stream=stream)
 
-    impl_code = G.gdr_chunk_fwd_impl(G.make_desc(
-        B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
-        io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
-        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
-        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
-        wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=args.neumann,
-        residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
-    impl_name = {G.GDR_IMPL_MFMA: "mfma", G.GDR_IMPL_GENERIC: "generic"}.get(impl_code, "?")
+    def kernel_of(neumann, residual):
+        code = G.gdr_chunk_fwd_impl(G.make_desc(
+            B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
+            io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
+            gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
+            decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
+            wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=neumann,
+            residual_steps=residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
+        return {G.GDR_IMPL_MFMA: "mfma", G.GDR_IMPL_GENERIC: "generic"}.get(code, "?")
+
+    impl_name = kernel_of(args.neumann, args.residual)
     print(f"[bench] workload {args.workload} impl {impl_name} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
@@ -674,7 +682,9 @@ def main():
         # products included), over this run's launch time
         roofline["mfma_bf16_frac_counters"] = round(mc["mfma_bf16_flop_per_dispatch"] / avg_launch_s / 1e12
                                                     / MFMA_BF16_PEAK_TFLOPS, 4)
-        roofline["mfma_busy_frac_counters"] = round(mc.get("mfma_busy_frac", float("nan")), 4)
+        if "mfma_busy_cycles_per_simd" in mc:
+            roofline["mfma_busy_frac_counters"] = round(mc["mfma_busy_cycles_per_simd"]
+                                                        / (avg_launch_s * ENGINE_CLOCK_HZ), 4)
 
     parity = None
     if not args.no_parity:
@@ -722,6 +732,20 @@ def main():
             "rel_l2_exact_vs_approx_oracle_stream00": oracle.rel_l2(o_ap, o_ex),
             "stream": "(0,0)", "tokens": s.T,
         }
+        ex_impl = kernel_of(-1, 0)
+        if ex_impl != impl_name:
+            # the approximation ran on another kernel than the exact T (the residual correction
+            # has no bf16 matrix-core path): the gap above then also holds the two kernels'
+            # different rounding, so the exact T is run on the approximation's kernel as well
+            ex2 = torch.empty_like(outs[j])
+            G.gdr_chunk_fwd(a["q"], a["k"], a["v"], beta=a["beta"], log_alpha=a["log_alpha"], erase=a["erase"],
+                            write=a["write"], write_key=a["write_key"], precond=precond, out=ex2, chunk=s.chunk,
+                            impl=impl_name, stream=stream)
+            torch.cuda.synchronize()
+            ex2d = ex2.double()
+            exact_vs_approx["exact_kernel"] = ex_impl
+            exact_vs_approx[f"rel_l2_exact_vs_approx_gpu_all_streams_both_{impl_name}"] = float(
+                torch.linalg.vector_norm(ap - ex2d) / torch.linalg.vector_norm(ex2d))
 
     cpu = None
     if not args.no_cpu_baseline:
