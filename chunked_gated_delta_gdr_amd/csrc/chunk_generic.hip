@@ -27,6 +27,18 @@
 // [l / 16] and B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16], r < 4).  The tiles of
 // X, D and O are spread one per wave; the ten C x C tiles on and below the diagonal two per
 // wave at most.
+//
+// Chunk 128 with a band-limited T (N <= 15; the C128 variant): the chunk runs as its two
+// 64-row halves a and b in turn, each with the steps above and its own in-chunk cumulative
+// decay.  In block form T = [[T_aa, 0], [T_ba, T_bb]], and the band of T_ba is
+// band(T_bb A_ba T_aa) (every term of an in-band entry uses in-band factors, Lemma 3.1), which
+// for N <= 15 touches only rows 64..79 and columns 48..63.  The chunk's D_b is
+// T_bb X_b + T_ba X_a with X_b read from the chunk's start state S_c; the output and the state
+// update of half b, read from the state after half a, equal the chunk-128 ones, since
+// e^{g} Q_b S_c^T + P_ba D_a = e^{g'} Q_b S_mid^T for any D_a (g' the cumulative decay from the
+// start of half b).  So half a also keeps S_c, rows 48..63 of its write keys, X and T_aa and
+// its last decays, and half b adds the corner (64 + i, 48 + j), kept where i - j + 16 <= N,
+// to the first 16 rows of its D.
 #include <cstdlib>
 
 #include "common.h"
@@ -77,8 +89,9 @@ __device__ __forceinline__ void lower_tile(int u, int &ib, int &jb) {
   jb = u - ib * (ib + 1) / 2;
 }
 
-template <typename IO, int DK, bool CHD, int BV>
+template <typename IO, int DK, bool CHD, int BV, bool C128>
 __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
+  static_assert(!C128 || (!CHD && BV == 16), "chunk 128 runs with scalar or no decay on 16-row value tiles");
   // CHD: one decay per key channel (log_alpha [B, T, H, Dk]).  The pairwise decay of channel
   // c between tokens j <= i is 2^(G_ic - G_jc) with G the in-chunk cumulative log2 decay, so it
   // sits inside the key products: L_ij = sum_c e_ic r_jc 2^(G_ic - G_jc) (P likewise; factored
@@ -136,6 +149,16 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
   float(*const Zs)[36] = kTight ? reinterpret_cast<float(*)[36]>(&Xs[0][0]) : Zs_;
   float(*const Dl)[BV] = kTight ? Xv : Dl_;
   static_assert(!kTight || 32 * 36 <= kCMax * LD, "the inverse's scratch must fit the key tile");
+  // chunk 128: what half a hands to half b.  The start state S_c and write-key rows 48..63 take
+  // the residual series' buffer (the residual correction is not offered at chunk 128).
+  constexpr int kH = C128 ? 16 : 1;
+  __shared__ __align__(16) float Taa[kH][kH + 1];   // T_aa rows / columns 48..63
+  __shared__ __align__(16) float Xat[kH][C128 ? BV : 1];   // X_a rows 48..63
+  __shared__ float Zc[kH][kH + 1];                  // A_ba T_aa, then the band of T_ba
+  __shared__ float wdt[kH], ega[1];                 // e^{g_63 - g_j} (j = 48..63), e^{g_63} of half a
+  float(*const Ss2)[LD] = reinterpret_cast<float(*)[LD]>(&Zb[0][0]);
+  float(*const Rat)[LD] = reinterpret_cast<float(*)[LD]>(&Zb[0][0] + BV * LD);
+  static_assert(!C128 || (BV + 16) * LD <= kCMax * (kCMax + 4), "S_c and the key rows must fit the series buffer");
 
   const long long sh = static_cast<long long>(b) * H + h;  // (b, h) index
   // state tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
@@ -179,14 +202,21 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     return acc;
   };
 
-  for (int c0 = 0; c0 < T; c0 += a.C) {
-    const int n = min(a.C, T - c0);
+  const int step = C128 ? kCMax : a.C;
+  for (int c0 = 0; c0 < T; c0 += step) {
+    const int n = min(step, T - c0);
+    // chunk 128: half b of a chunk, or half a with a half b to follow (then n = 64)
+    const bool hb = C128 && ((c0 / kCMax) & 1) != 0;
+    const bool ha = C128 && !hb && c0 + kCMax < T;
     // token (b, c0 + t, h) row index in [B, T, H]
     auto tok = [&](int t) -> long long { return (static_cast<long long>(b) * T + c0 + t) * H + h; };
     const long long row0 = tok(0);
     const int rstride = H * Dk;
 
     __syncthreads();  // previous chunk done with every buffer
+    if (ha) {   // the chunk's start state, for half b's X
+      for (int idx = tid; idx < BV * LD; idx += kThreads) (&Ss2[0][0])[idx] = (&Ss[0][0])[idx];
+    }
     {   // write keys (the preconditioned ones are formed from them below), erase keys and, with
         // per-channel decays, the log decays: all loads first (clamped), then the masked stores
       float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xl[CHD ? kLoadIt : 1];
@@ -287,8 +317,8 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         }
       }
     };
-    // the read of the state through row t of Y (E or Q): e^g_t Y_t, or 2^G_t (.) Y_t
-    auto state_read = [&](const float(*Y)[LD], float4v &acc) {
+    // the read of the state mirror Sm through row t of Y (E or Q): f e^g_t Y_t, or 2^G_t (.) Y_t
+    auto state_read = [&](const float(*Y)[LD], const float(*Sm)[LD], float f, float4v &acc) {
       const int t = 16 * tb + col;
       if constexpr (CHD) {
         // (k order permuted as in dot_kc)
@@ -297,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
 #pragma unroll 2
         for (int ks = 0; ks < DK; ks += 16) {
           const int kk = ks + 4 * kq;
-          const float4 y = ld4(&Y[t][kk]), g = ld4(&Gs[t][kk]), z = ld4(&Ss[16 * rb + col][kk]);
+          const float4 y = ld4(&Y[t][kk]), g = ld4(&Gs[t][kk]), z = ld4(&Sm[16 * rb + col][kk]);
           acc = mfma4(y.x * chd::ex2(g.x), z.x, acc);
           a1 = mfma4(y.y * chd::ex2(g.y), z.y, a1);
           acc = mfma4(y.z * chd::ex2(g.z), z.z, acc);
@@ -305,14 +335,28 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         }
         acc += a1;
       } else {
-        acc = dot_kc<DK>(&Y[t][0], &Ss[16 * rb + col][0], kq);
+        acc = dot_kc<DK>(&Y[t][0], &Sm[16 * rb + col][0], kq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= eg[16 * tb + 4 * kq + r];
+        for (int r = 0; r < 4; ++r) acc[r] *= C128 ? f * eg[16 * tb + 4 * kq + r] : eg[16 * tb + 4 * kq + r];
       }
     };
 
     // L (strict lower)
     gram(false);
+    if (hb && wave == 7) {
+      // Z = A_ba T_aa on the corner: rows 0..15 of half b against rows 48..63 of half a, where
+      // A_ij = -e^{g'_i} e^{g_63 - g_j} (e_i . r_j)
+      const float4v l = dot_kc<DK>(&Xs[col][0], &Rat[col][0], kq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Zc[4 * kq + r][col] = -eg[4 * kq + r] * wdt[col] * l[r];
+      tri::wave_sync();
+      float4v z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) z = mfma4(Zc[col][k0 + kq], Taa[k0 + kq][col], z);
+      tri::wave_sync();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Zc[4 * kq + r][col] = z[r];
+    }
     // X = V' - (e^g (.) E) S^T on the value tile
     if (xwave) {
       float vp[4];   // (loads from clamped indices; entries outside the tile are masked below)
@@ -324,7 +368,10 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
         vp[r] = (a.gain == GDR_GAIN_SCALAR) ? a.beta[tok(t)] * vv : ld_f(wr, vi) * vv;
       }
       float4v acc;
-      state_read(Xs, acc);
+      if (hb)
+        state_read(Xs, Ss2, ega[0], acc);   // half b reads the chunk's start state
+      else
+        state_read(Xs, Ss, 1.f, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tb + 4 * kq + r, rr = 16 * rb + col;
@@ -351,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     // is formed on the ten lower tiles, each tile summing over the k-blocks between its
     // column and row blocks; every product is formed in registers and written back after a
     // barrier (E over L, Z in place, T over T0).
-    if (CHD ? false : a.S > 0) {
+    if ((CHD || C128) ? false : a.S > 0) {
       float4v e[2];
       for (int u = wave, m = 0; u < 10; u += 8, ++m) e[m] = lower_mm(&LP[0][0], kCMax + 1, &Tm[0][0], kCMax + 4, u, -1.f);
       __syncthreads();   // every row of A has been read
@@ -408,10 +455,30 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     if (xwave) {
       for (int s0 = 0; s0 < 16 * (tb + 1); s0 += 4)
         dacc = mfma4(Tm[16 * tb + col][s0 + kq], Xv[s0 + kq][16 * rb + col], dacc);
+      if (hb && tb == 0) {
+        // + band(T_ba) X_a: W = T_bb Z on the corner, entry (i, j) being T's (64 + i, 48 + j)
+        float4v w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) w = mfma4(Tm[col][k0 + kq], Zc[k0 + kq][col], w);
+        tri::wave_sync();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Zc[4 * kq + r][col] = 4 * kq + r + 16 - col <= a.N ? w[r] : 0.f;
+        tri::wave_sync();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) dacc = mfma4(Zc[col][k0 + kq], Xat[k0 + kq][16 * rb + col], dacc);
+      }
       if constexpr (!kTight) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dl[16 * tb + 4 * kq + r][16 * rb + col] = dacc[r];
       }
+    }
+    if (ha && wave >= 4) {   // (16-row value tiles: waves 4..7 hold no tile of X, D or O)
+      const int t4 = tid - 256;
+      for (int idx = t4; idx < 16 * LD; idx += 256) Rat[idx / LD][idx % LD] = Rs[48 + idx / LD][idx % LD];
+      Taa[t4 >> 4][t4 & 15] = Tm[48 + (t4 >> 4)][48 + (t4 & 15)];
+      Xat[t4 >> 4][t4 & 15] = Xv[48 + (t4 >> 4)][t4 & 15];
+      if (t4 < 16) wdt[t4] = wd[48 + t4];
+      if (t4 == 0) ega[0] = eg[kCMax - 1];
     }
     // P (lower incl. diagonal; L is no longer needed)
     gram(true);
@@ -426,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     // O = scale ((e^g (.) Q) S^T + P D)
     if (xwave) {
       float4v acc;
-      state_read(Xs, acc);
+      state_read(Xs, Ss, 1.f, acc);
       for (int j0 = 0; j0 < 16 * (tb + 1); j0 += 4)
         acc = mfma4(LP[16 * tb + col][j0 + kq], Dl[j0 + kq][16 * rb + col], acc);
 #pragma unroll
@@ -489,15 +556,15 @@ __global__ __launch_bounds__(kThreads) void chunk_generic_kernel(ChunkArgs a) {
     a.pc_h_out[sh * Dk + tid] = hreg;
 }
 
-template <typename IO, bool CHD, int BV>
+template <typename IO, bool CHD, int BV, bool C128 = false>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
   const dim3 grid((a.Dv + BV - 1) / BV, a.H, a.B);
   if (a.Dk <= 32)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32, CHD, BV>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 32, CHD, BV, C128>), grid, dim3(kThreads), 0, s, a);
   else if (a.Dk <= 64)
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64, CHD, BV>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 64, CHD, BV, C128>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128, CHD, BV>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_generic_kernel<IO, 128, CHD, BV, C128>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -507,6 +574,8 @@ hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
 // overrides that choice (tuning and tests).
 template <typename IO>
 hipError_t launch_io(const ChunkArgs &a, hipStream_t s) {
+  // chunk 128 reaches this kernel only with a band limit 0 <= N <= 15 and scalar or no decay
+  if (a.C == 2 * kCMax) return launch_dk<IO, false, 16, true>(a, s);
   if (a.decay != GDR_DECAY_CHANNEL) return launch_dk<IO, false, 32>(a, s);
   const char *e = getenv("GDR_GENERIC_BV");
   const int forced = e == nullptr ? 0 : atoi(e);

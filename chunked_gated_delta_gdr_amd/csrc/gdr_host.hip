@@ -156,8 +156,8 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
   if (d->Dk < 1 || d->Dv < 1) return fail(GDR_EINVAL, "Dk = %d and Dv = %d must be >= 1", d->Dk, d->Dv);
   if (d->Dk > 128 || d->Dv > 512)
     return fail(GDR_ENOTSUP, "Dk = %d (max 128), Dv = %d (max 512)", d->Dk, d->Dv);
-  if (!for_step && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
-    return fail(d->chunk < 1 ? GDR_EINVAL : GDR_ENOTSUP, "chunk = %d; supported: 16, 32, 64", d->chunk);
+  if (!for_step && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
+    return fail(d->chunk < 1 ? GDR_EINVAL : GDR_ENOTSUP, "chunk = %d; supported: 16, 32, 64, 128", d->chunk);
   if (d->io_dtype != GDR_F32 && d->io_dtype != GDR_BF16)
     return fail(GDR_EINVAL, "io_dtype = %d", d->io_dtype);
   if (d->gain != GDR_GAIN_SCALAR && d->gain != GDR_GAIN_CHANNEL) return fail(GDR_EINVAL, "gain = %d", d->gain);
@@ -177,6 +177,15 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
     if (d->residual_steps > 64)
       return fail(GDR_ENOTSUP, "residual_steps = %d (max 64; E^s vanishes once s (N + 1) >= C)",
                   d->residual_steps);
+    if (d->chunk == 128 && d->residual_steps > 0)
+      return fail(GDR_ENOTSUP, "residual_steps at chunk 128 (the residual correction runs at chunk <= 64)");
+    if (d->chunk == 128 && d->neumann_order >= 0 && d->neumann_order < 127) {
+      if (d->neumann_order > 15)
+        return fail(GDR_ENOTSUP, "chunk 128 with neumann_order = %d (supported: exact, N <= 15, or N >= 127)",
+                    d->neumann_order);
+      if (d->decay == GDR_DECAY_CHANNEL)
+        return fail(GDR_ENOTSUP, "chunk 128 with a band-limited T and decay CHANNEL");
+    }
   }
 
   const long double B = d->B, T = d->T, H = d->H, Dk = d->Dk, Dv = d->Dv;
@@ -257,8 +266,23 @@ gdr_status_t gdr_validate(const gdr_desc_t *d, const gdr_inputs_t *in, const flo
   return ok();
 }
 
-int gdr_chunk_fwd_impl(const gdr_desc_t *d) {
-  if (d == nullptr || d->struct_size != sizeof(gdr_desc_t)) return -1;
+// Chunk 128 with the exact T runs as chunk 64: T's block (I - A)^-1 = [[T_aa, 0], [T_ba, T_bb]]
+// has T_ba = T_bb A_ba T_aa, so D_b = T_bb (X_b + A_ba D_a), and X_b + A_ba D_a is X_b read from
+// the state after the chunk's first 64 tokens.  Chunk 64 computes exactly that product,
+// regrouped (the results differ only in rounding).  A band limit N >= 127 keeps every entry.
+static gdr_desc_t lower_chunk(const gdr_desc_t &d) {
+  gdr_desc_t e = d;
+  if (d.chunk == 128 && (d.neumann_order < 0 || d.neumann_order >= 127)) {
+    e.chunk = 64;
+    e.neumann_order = -1;
+  }
+  return e;
+}
+
+int gdr_chunk_fwd_impl(const gdr_desc_t *dd) {
+  if (dd == nullptr || dd->struct_size != sizeof(gdr_desc_t)) return -1;
+  const gdr_desc_t dl = lower_chunk(*dd);
+  const gdr_desc_t *d = &dl;
   gdr_inputs_t none{};
   const bool mfma = gdr::chunk_mfma_supports(*d, none, nullptr, nullptr, nullptr);
   if (d->impl == GDR_IMPL_GENERIC) return GDR_IMPL_GENERIC;
@@ -284,14 +308,16 @@ static gdr::ChunkArgs make_args(const gdr_desc_t *d, const gdr_inputs_t *in, con
   return a;
 }
 
-gdr_status_t gdr_chunk_fwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+gdr_status_t gdr_chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
                            void *out, float *state_out, void *stream) {
-  gdr_status_t st = gdr_validate(d, in, state_in, out, state_out, 0);
+  gdr_status_t st = gdr_validate(dd, in, state_in, out, state_out, 0);
   if (st != GDR_OK) return st;
+  const gdr_desc_t dl = lower_chunk(*dd);
+  const gdr_desc_t *d = &dl;
   const bool mfma_ok = gdr::chunk_mfma_supports(*d, *in, state_in, out, state_out);
   if (d->impl == GDR_IMPL_MFMA && !mfma_ok)
     return fail(GDR_ENOTSUP, "the MFMA kernel does not cover this descriptor "
-                             "(needs bf16, Dk = Dv = 128, chunk 64, 16-byte aligned tensors, "
+                             "(needs bf16, Dk = Dv = 128, chunk 64 or exact chunk 128, 16-byte aligned tensors, "
                              "no residual correction)");
   const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
   const gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
@@ -305,19 +331,24 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *d, const gdr_inputs_t *in, const fl
   return ok();
 }
 
-uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *d) {
-  if (d == nullptr || d->struct_size != sizeof(gdr_desc_t) || d->B < 1 || d->H < 1 || d->T < 0 ||
-      d->Dk < 1 || d->Dv < 1 || (d->chunk != 16 && d->chunk != 32 && d->chunk != 64))
+uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *dd) {
+  if (dd == nullptr || dd->struct_size != sizeof(gdr_desc_t) || dd->B < 1 || dd->H < 1 || dd->T < 0 ||
+      dd->Dk < 1 || dd->Dv < 1 || (dd->chunk != 16 && dd->chunk != 32 && dd->chunk != 64 && dd->chunk != 128))
     return 0;
-  return bwd_layout(*d).total;
+  const gdr_desc_t dl = lower_chunk(*dd);
+  if (dl.chunk == 128) return 0;   // (band-limited T at chunk 128: no backward)
+  return bwd_layout(dl).total;
 }
 
-gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+gdr_status_t gdr_validate_bwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
                               const void *d_out, const float *d_state_out, const gdr_grads_t *g,
                               const void *ws, uint64_t ws_bytes) {
   // the forward's own contract, with d_out in the place of out
-  gdr_status_t st = gdr_validate(d, in, state_in, d_out, nullptr, 0);
+  gdr_status_t st = gdr_validate(dd, in, state_in, d_out, nullptr, 0);
   if (st != GDR_OK) return fail(st, "forward arguments (d_out checked as out): %s", g_last_error.c_str());
+  const gdr_desc_t dl = lower_chunk(*dd);
+  const gdr_desc_t *d = &dl;
+  if (d->chunk == 128) return fail(GDR_ENOTSUP, "backward of the band-limited T at chunk 128");
   if (g == nullptr) return fail(GDR_EINVAL, "grads must be non-NULL");
   if (in->pc_h_out != nullptr) return fail(GDR_EINVAL, "pc_h_out must be NULL (the backward does not write it)");
   if (g->dpc_h_in != nullptr && d->wkey != GDR_WKEY_DIAG_PRECOND)
@@ -387,11 +418,13 @@ gdr_status_t gdr_validate_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const
   return ok();
 }
 
-gdr_status_t gdr_chunk_bwd(const gdr_desc_t *d, const gdr_inputs_t *in, const float *state_in,
+gdr_status_t gdr_chunk_bwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
                            const void *d_out, const float *d_state_out, const gdr_grads_t *g,
                            void *workspace, uint64_t workspace_bytes, void *stream) {
-  gdr_status_t st = gdr_validate_bwd(d, in, state_in, d_out, d_state_out, g, workspace, workspace_bytes);
+  gdr_status_t st = gdr_validate_bwd(dd, in, state_in, d_out, d_state_out, g, workspace, workspace_bytes);
   if (st != GDR_OK) return st;
+  const gdr_desc_t dl = lower_chunk(*dd);
+  const gdr_desc_t *d = &dl;
   const BwdLayout L = bwd_layout(*d);
   char *ws = static_cast<char *>(workspace);
   gdr::BwdArgs b{};

@@ -79,7 +79,14 @@ typedef struct gdr_desc {
                              every launch grid then fits HIP's 32-bit work-item counts);
                              the backward also takes at most 2^22 chunks per stream      */
   int32_t Dk, Dv;         /* key and value head dims: 1 <= Dk <= 128, 1 <= Dv <= 512      */
-  int32_t chunk;          /* chunk size C in tokens: 16, 32 or 64 (ignored by the step)   */
+  int32_t chunk;          /* chunk size C in tokens: 16, 32, 64 or 128 (ignored by the
+                             step; the inversion summary measures 32, 64 and 128).  At 128
+                             the exact T runs as two 64-row blocks, the off-diagonal block
+                             T_ba = T_bb A_ba T_aa applied through the state after the first
+                             64 tokens (the same product regrouped), on either kernel; a
+                             band limit needs N <= 15 (or N >= 127, which is exact), decay
+                             NONE or SCALAR and no residual steps, and runs on the generic
+                             kernel; other chunk-128 descriptors return GDR_ENOTSUP        */
   int32_t io_dtype;       /* GDR_F32 | GDR_BF16                                            */
   int32_t gain;           /* GDR_GAIN_*                                                    */
   int32_t decay;          /* GDR_DECAY_*                                                   */
@@ -222,8 +229,9 @@ typedef struct gdr_grads {
  *
  * Supported: gain SCALAR | CHANNEL, decay NONE | SCALAR | CHANNEL, wkey SAME | EXPLICIT |
  * DIAG_PRECOND, exact T or the band-limited T (not with decay CHANNEL), no residual steps
- * (neumann_order < 0), chunk 16 | 32 | 64, Dk <= 128, Dv <= 512, io fp32 | bf16; anything
- * else returns GDR_ENOTSUP (desc->impl is ignored).
+ * (neumann_order < 0), chunk 16 | 32 | 64, or 128 with the exact T (the chunk-64 backward of
+ * the same function), Dk <= 128, Dv <= 512, io fp32 | bf16; anything else returns
+ * GDR_ENOTSUP (desc->impl is ignored).
  *
  *   in, state_in  the forward's inputs and initial state (NULL for zeros), unchanged.
  *   d_out         [B,T,H,Dv] io_dtype: dL/dout.  May be NULL only if T == 0.

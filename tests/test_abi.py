@@ -88,7 +88,7 @@ def test_valid_call_validates():
     ("B", 0, G.GDR_EINVAL), ("H", 0, G.GDR_EINVAL), ("T", -1, G.GDR_EINVAL),
     ("Dk", 0, G.GDR_EINVAL), ("Dv", 0, G.GDR_EINVAL),
     ("Dk", 256, G.GDR_ENOTSUP), ("Dv", 1024, G.GDR_ENOTSUP),
-    ("chunk", 0, G.GDR_EINVAL), ("chunk", 128, G.GDR_ENOTSUP), ("chunk", 48, G.GDR_ENOTSUP),
+    ("chunk", 0, G.GDR_EINVAL), ("chunk", 256, G.GDR_ENOTSUP), ("chunk", 48, G.GDR_ENOTSUP),
     ("io_dtype", 7, G.GDR_EINVAL), ("gain", 5, G.GDR_EINVAL), ("decay", 3, G.GDR_EINVAL),
     ("wkey", 9, G.GDR_EINVAL), ("impl", 4, G.GDR_EINVAL),
     ("scale", float("nan"), G.GDR_EINVAL), ("scale", float("inf"), G.GDR_EINVAL),
@@ -124,6 +124,42 @@ def test_residual_correction_is_generic_only():
     assert G.gdr_chunk_fwd_impl(d) == -1
     d.residual_steps = 0
     assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_MFMA
+
+
+@pytest.mark.parametrize("N,S,decay,status", [
+    (-1, 0, G.GDR_DECAY_SCALAR, G.GDR_OK), (-1, 0, G.GDR_DECAY_CHANNEL, G.GDR_OK),
+    (0, 0, G.GDR_DECAY_SCALAR, G.GDR_OK), (3, 0, G.GDR_DECAY_NONE, G.GDR_OK), (15, 0, G.GDR_DECAY_SCALAR, G.GDR_OK),
+    (16, 0, G.GDR_DECAY_SCALAR, G.GDR_ENOTSUP), (126, 0, G.GDR_DECAY_NONE, G.GDR_ENOTSUP),
+    (127, 0, G.GDR_DECAY_CHANNEL, G.GDR_OK), (500, 0, G.GDR_DECAY_SCALAR, G.GDR_OK),
+    (3, 0, G.GDR_DECAY_CHANNEL, G.GDR_ENOTSUP), (3, 8, G.GDR_DECAY_SCALAR, G.GDR_ENOTSUP),
+    (127, 2, G.GDR_DECAY_NONE, G.GDR_ENOTSUP)])
+def test_chunk128_descriptor(N, S, decay, status):
+    """Chunk 128: exact T (or N >= 127) for every variant; a band limit N <= 15 with scalar or no
+    decay; nothing else."""
+    p = ptrs()
+    la = p[4] if decay != G.GDR_DECAY_NONE else None
+    check(status, d=desc(chunk=128, neumann_order=N, residual_steps=S, decay=decay), ins=inputs(log_alpha=la))
+
+
+def test_chunk128_kernel_choice():
+    """The exact T at chunk 128 is the chunk-64 computation regrouped, so it keeps the
+    matrix-core kernel; the band-limited T at chunk 128 runs on the fp32 kernel only."""
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=128)) == G.GDR_IMPL_MFMA
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=128, neumann_order=200)) == G.GDR_IMPL_MFMA
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=128, neumann_order=3)) == G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(desc(Dk=128, Dv=128, chunk=128, neumann_order=3, impl=G.GDR_IMPL_MFMA)) == -1
+
+
+def test_chunk128_backward():
+    """The backward at chunk 128 takes the exact T (its workspace is chunk 64's) and rejects
+    the band-limited one."""
+    assert G.gdr_chunk_bwd_workspace_size(desc(chunk=128)) == G.gdr_chunk_bwd_workspace_size(desc(chunk=64))
+    assert G.gdr_chunk_bwd_workspace_size(desc(chunk=128, neumann_order=3)) == 0
+    assert call_validate_bwd(desc(chunk=128)) == G.GDR_OK, G.gdr_last_error()
+    d = desc(chunk=128, neumann_order=3)
+    ins, gr, a = bwd_args(d)
+    assert G.gdr_validate_bwd(d, ins, None, a["d_out"], None, gr, a["workspace"], 1 << 30) == G.GDR_ENOTSUP
+    assert "chunk 128" in G.gdr_last_error()
 
 
 def test_huge_problem_rejected():
