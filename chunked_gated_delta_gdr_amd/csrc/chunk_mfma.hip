@@ -270,7 +270,7 @@ __device__ __forceinline__ float4v diag_inverse_t(float4v n, float4v nt, int lan
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
 // the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
 // own role's state across iterations, and both run the kernel's barrier sequence.
-template <int BV, bool CHAN, bool DECAY, int WK, bool STG>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG>
 __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -734,6 +734,142 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       __syncthreads();   // (3)
     }
 
+    if constexpr (RES) {
+      // Parallel residual correction of the band-limited start T0 = T(c) (MatMul-only
+      // inversion summary, Metodologia 3): E = I - (I - A) T0, Z = sum_{s <= S} E^s formed as
+      // Z <- I + E Z from Z = I + E, and T = T0 Z.  All are lower triangular, and column block jb
+      // of the new Z reads only column block jb of the old one, so a wave keeps one column block
+      // of Z in its accumulators through every step with no exchange: helpers 0 and 1 take
+      // column blocks 0 and 1, helper 2 blocks 2 and 3.  The tiles of E are shared: published
+      // once, as bf16 pairs in A-operand layout, in the Q buffer of chunk c (its last reads were
+      // before barrier (2)).  Three barriers: E published (R1), T0 read (R2), T written (R3).
+      // (Spreading E's tiles over all six helpers measured slower: the staging helpers, which
+      // hold the next chunk's prefetched items, then spill registers.)
+      uint16_t *const ebuf = sm.q[cur];
+      auto etile = [&](int ib, int kb) __attribute__((always_inline)) {   // 16 x 20 hi, then lo
+        return ebuf + (ib * (ib + 1) / 2 + kb) * 640 + l16 * 20 + 4 * l4;
+      };
+      // the A-operand pair of block (ib, kb) of A (kb <= ib): the diagonal blocks formed again
+      // from the chunk's keys, the others as the A jobs left them
+      auto aop = [&](int ib, int kb) __attribute__((always_inline)) {
+        if (ib == kb) {
+          float4v n, nt;
+          a_diag(cur, ib, n, nt);
+          return split4(nt);
+        }
+        if (ib == 1) return aodp(0);
+        if (ib == 3 && kb == 2) return aodp(1);
+        return lrow(ib - 2, kb);
+      };
+      auto identity = [&]() __attribute__((always_inline)) {
+        float4v r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = (4 * l4 + i == l16) ? 1.f : 0.f;
+        return r;
+      };
+      // R1 / R2 / write for the compile-time column blocks J0, J1 (-1: none) of this wave
+      auto res_run = [&](auto j0c, auto j1c) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
+        float4v ez[2][4], tz[2][4];
+        // R1: the tiles of E in column block JB, E_ij = [i == j] - T0_ij + (A T0)_ij
+        auto e_col = [&](auto jbc, float4v(&e_out)[4]) __attribute__((always_inline)) {
+          constexpr int JB = decltype(jbc)::value;
+#pragma unroll
+          for (int ib = JB; ib < 4; ++ib) {
+            const Pair t0 = bcol(ib, JB);
+            float4v e = -(unbf4(t0.h) + unbf4(t0.l));
+            if (ib == JB) e += identity();
+#pragma unroll
+            for (int kb = JB; kb <= ib; ++kb) e = mm2(aop(ib, kb), bcol(kb, JB), e);
+            e_out[ib] = e;
+            const Pair ep = split4(e);
+            float4v th, tl;
+            tr2(ep, th, tl);
+            uint16_t *d = etile(ib, JB);
+            *reinterpret_cast<short4v *>(d) = tobf4(th);
+            *reinterpret_cast<short4v *>(d + 320) = tobf4(tl);
+          }
+        };
+        // R2: Z = I + E, S - 1 steps Z <- I + E Z, then T = T0 Z, on column block JB
+        auto z_col = [&](auto jbc, const float4v(&e_in)[4], float4v(&t_out)[4]) __attribute__((always_inline)) {
+          constexpr int JB = decltype(jbc)::value;
+          Pair ep[4][4];
+#pragma unroll
+          for (int ib = JB; ib < 4; ++ib)
+#pragma unroll
+            for (int kb = JB; kb <= ib; ++kb) {
+              const uint16_t *t = etile(ib, kb);
+              ep[ib][kb] = Pair{ld4(t), ld4(t + 320)};
+            }
+          float4v z[4];
+#pragma unroll
+          for (int ib = JB; ib < 4; ++ib) z[ib] = ib == JB ? e_in[ib] + identity() : e_in[ib];
+          for (int st = 1; st < a.S; ++st) {
+            Pair zp[4];
+#pragma unroll
+            for (int kb = JB; kb < 4; ++kb) zp[kb] = split4(z[kb]);
+#pragma unroll
+            for (int ib = JB; ib < 4; ++ib) {
+              float4v acc = ib == JB ? identity() : zero4();
+#pragma unroll
+              for (int kb = JB; kb <= ib; ++kb) acc = mm2(ep[ib][kb], zp[kb], acc);
+              z[ib] = acc;
+            }
+          }
+          Pair zp[4];
+#pragma unroll
+          for (int kb = JB; kb < 4; ++kb) zp[kb] = split4(z[kb]);
+#pragma unroll
+          for (int ib = JB; ib < 4; ++ib) {
+            float4v acc = zero4();
+#pragma unroll
+            for (int kb = JB; kb <= ib; ++kb) acc = mm2(arow(ib, kb), zp[kb], acc);
+            t_out[ib] = acc;
+          }
+        };
+        // write: T's column block JB (all ten blocks of T are written; no band mask)
+        auto t_put = [&](auto jbc, const float4v(&t_in)[4]) __attribute__((always_inline)) {
+          constexpr int JB = decltype(jbc)::value;
+#pragma unroll
+          for (int ib = JB; ib < 4; ++ib) {
+            const Pair tp = split4(t_in[ib]);
+            float4v th, tl;
+            tr2(tp, th, tl);
+            const int i = ib * 16 + l16;
+            *reinterpret_cast<short4v *>(&sm.t[cur][i][JB * 16 + 4 * l4]) = tobf4(th);
+            *reinterpret_cast<short4v *>(&sm.tl[cur][i][JB * 16 + 4 * l4]) = tobf4(tl);
+          }
+        };
+        if (c >= 0) {
+          if constexpr (J0 >= 0) e_col(j0c, ez[0]);
+          if constexpr (J1 >= 0) e_col(j1c, ez[1]);
+        }
+        __syncthreads();   // (R1) E published
+        if (c >= 0) {
+          if constexpr (J0 >= 0) z_col(j0c, ez[0], tz[0]);
+          if constexpr (J1 >= 0) z_col(j1c, ez[1], tz[1]);
+        }
+        __syncthreads();   // (R2) every read of T0 done
+        if (c >= 0) {
+          if constexpr (J0 >= 0) t_put(j0c, tz[0]);
+          if constexpr (J1 >= 0) t_put(j1c, tz[1]);
+        }
+        __syncthreads();   // (R3) T(c) complete
+      };
+      using std::integral_constant;
+      if constexpr (!STG) {
+        if (hw == 0)
+          res_run(integral_constant<int, 0>{}, integral_constant<int, -1>{});
+        else
+          res_run(integral_constant<int, 1>{}, integral_constant<int, -1>{});
+      } else {
+        if (hw == 2)
+          res_run(integral_constant<int, 2>{}, integral_constant<int, 3>{});
+        else
+          res_run(integral_constant<int, -1>{}, integral_constant<int, -1>{});
+      }
+    }
+
     if (have_next) {
       const int nb = nxt;
       // off-diagonal blocks of A: A_10, A_32 (for T_10, T_32) and the four blocks of A_ba (jobs
@@ -805,7 +941,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   }
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -998,6 +1134,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           }
         }
         __syncthreads();   // (2) T(c), P(c) complete
+        if constexpr (RES) {   // the residual correction of T(c) on the helpers (see there)
+          if (WK == kWkPrecond) __syncthreads();   // (3)
+          __syncthreads();   // (R1)
+          __syncthreads();   // (R2)
+          __syncthreads();   // (R3)
+        }
         if (c >= 0) {
           // every LDS operand of this phase is read up front: T and P blocks, R^T for the update.
           // T is held as a bf16 pair (hi + lo): the diagonal blocks pack hi and lo into one K = 32
@@ -1087,7 +1229,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
               if (tb * 16 + l16 < n) *reinterpret_cast<short4v *>(ob + tb * 16 * tokstride) = pk[tb];
           }
         }
-        if (WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
+        if (!RES && WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
       }
       if (a.state_out != nullptr) {
 #pragma unroll
@@ -1102,14 +1244,17 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     return;
   }
 
-  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, true>(sm, a);
-  else helper_loop<BV, CHAN, DECAY, WK, false>(sm, a);
+  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true>(sm, a);
+  else helper_loop<BV, CHAN, DECAY, WK, RES, false>(sm, a);
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
 hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV);   // <= 2^22
-  hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK>), dim3(grid), dim3(kNT), 0, s, a);
+  if (a.S > 0)
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true>), dim3(grid), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false>), dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1134,7 +1279,6 @@ bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const floa
                          const float *state_out) {
   if (d.io_dtype != GDR_BF16 || d.Dk != kD || d.Dv != kD || d.chunk != kC) return false;
   if (d.gain == GDR_GAIN_CHANNEL && d.wkey != GDR_WKEY_SAME) return false;
-  if (d.neumann_order >= 0 && d.residual_steps > 0) return false;
   if (d.decay == GDR_DECAY_CHANNEL) return false;
   const void *p16[] = {in.q, in.k, in.v, in.erase, in.write, in.write_key, out, state_in, state_out};
   for (const void *p : p16)

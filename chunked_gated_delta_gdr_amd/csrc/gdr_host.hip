@@ -318,7 +318,7 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const f
   if (d->impl == GDR_IMPL_MFMA && !mfma_ok)
     return fail(GDR_ENOTSUP, "the MFMA kernel does not cover this descriptor "
                              "(needs bf16, Dk = Dv = 128, chunk 64 or exact chunk 128, 16-byte aligned tensors, "
-                             "no residual correction)");
+                             "no per-channel decay, channel gains only with write key k)");
   const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
   const gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -102,8 +102,9 @@ typedef struct gdr_desc {
                              parallel residual correction of the band-N start
                              T0 = band_N((I - A)^-1): E = I - (I - A) T0 and
                              T = T0 (I + E + ... + E^S)  (MatMul-only inversion summary,
-                             Metodologia 3).  Exact once (S + 1)(N + 1) >= C.  Only the
-                             generic kernel implements it (GDR_ENOTSUP with impl MFMA)     */
+                             Metodologia 3).  Exact once (S + 1)(N + 1) >= C.  Both
+                             kernels implement it (the matrix-core one at chunk 64); not
+                             at chunk 128 or with decay CHANNEL (GDR_ENOTSUP)              */
   int32_t impl;           /* GDR_IMPL_AUTO picks the fastest kernel for the shape;
                              GENERIC forces the fp32 VALU kernel; MFMA forces the bf16
                              matrix-core kernel (GDR_ENOTSUP if the shape is outside it)   */

@@ -117,13 +117,17 @@ def test_channel_decay_descriptor():
     assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
 
 
-def test_residual_correction_is_generic_only():
+def test_residual_correction_kernels():
+    """The residual-corrected T runs on the matrix-core kernel at chunk 64 (bf16, d = 128) and on
+    the generic kernel otherwise."""
     d = desc(Dk=128, Dv=128, neumann_order=3, residual_steps=8)
-    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
-    d.impl = G.GDR_IMPL_MFMA
-    assert G.gdr_chunk_fwd_impl(d) == -1
-    d.residual_steps = 0
     assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_MFMA
+    d.impl = G.GDR_IMPL_GENERIC
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
+    d = desc(Dk=128, Dv=128, neumann_order=3, residual_steps=8, chunk=32)
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
+    d = desc(Dk=128, Dv=128, neumann_order=3, residual_steps=8, io_dtype=G.GDR_F32)
+    assert G.gdr_chunk_fwd_impl(d) == G.GDR_IMPL_GENERIC
 
 
 @pytest.mark.parametrize("N,S,decay,status", [

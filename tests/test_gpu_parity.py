@@ -98,7 +98,8 @@ def test_residual_fp32_matches_oracle(N, S):
                                                  ("pdn", "bf16", 64), ("gdn", "bf16", 64)])
 def test_residual_variants(variant, dtype, chunk):
     """The residual correction in every gain / decay / write-key combination and chunk size
-    (generic kernel; the auto dispatch picks it for a residual descriptor)."""
+    (the auto dispatch: the fp32 kernel for fp32 or chunk < 64, the matrix-core kernel for the
+    bf16 cases at chunk 64)."""
     s = small(variant, dtype, chunk=chunk, Dk=64 if dtype == "f32" else 128, Dv=48 if dtype == "f32" else 128)
     announce(f"residual N=2 S=4 {variant} {dtype} C{chunk} {s}")
     x = gs.make_inputs(s)
@@ -488,6 +489,46 @@ def test_mfma_band(N):
     o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=mode, precond=pc)
     o, S, _ = run_chunk(s, x, neumann_order=N, impl="mfma")
     eo, eS = O.rel_l2(host(o), o_ref), O.rel_l2(host(S), S_ref)
+    print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+@pytest.mark.parametrize("variant", MFMA_VARIANTS)
+@pytest.mark.parametrize("N,S", [(0, 1), (1, 2), (3, 8)])
+def test_mfma_residual(variant, N, S):
+    """Residual-corrected T (band-N start, S steps) on the matrix-core kernel vs the oracle's
+    literal residual steps.  With N = 0, S = 1 the residual T is 4e-2 away from the exact one on
+    these inputs, so the GPU must be much closer to the residual than to the exact T."""
+    s = small(variant, "bf16", Dk=128, Dv=128, T=200, B=2, H=2)
+    announce(f"mfma residual N={N} S={S} {variant}")
+    x = gs.make_inputs(s)
+    pc = precond_opts(s)
+    o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=("residual", N, S), precond=pc)
+    o, St, _ = run_chunk(s, x, neumann_order=N, residual_steps=S, impl="mfma")
+    eo, eS = O.rel_l2(host(o), o_ref), O.rel_l2(host(St), S_ref)
+    print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+    if (N, S) == (0, 1):
+        o_ex, _, _ = O.chunked(x, chunk=64, precond=pc)
+        ee = O.rel_l2(host(o), o_ex)
+        print(f"  distance to the exact T's output {ee:.3e}", flush=True)
+        assert 3 * eo < ee
+
+
+@pytest.mark.parametrize("BV", [16, 32])
+def test_mfma_residual_value_tiles(BV, monkeypatch):
+    """Both value-tile widths with the residual steps (different helper-wave counts), a start
+    state and a partial last chunk."""
+    monkeypatch.setenv("GDR_MFMA_BV", str(BV))
+    s = small("pdn_decay", "bf16", Dk=128, Dv=128, T=150, B=2, H=3)
+    announce(f"mfma residual N=2 S=4 BV={BV}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(5)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    pc = precond_opts(s)
+    o_ref, S_ref, _ = O.chunked(x, chunk=64, t_mode=("residual", 2, 4), precond=pc, state0=S0.astype(np.float64))
+    o, St, _ = run_chunk(s, x, state_in=S0, neumann_order=2, residual_steps=4, impl="mfma")
+    eo, eS = O.rel_l2(host(o), o_ref), O.rel_l2(host(St), S_ref)
     print(f"  rel-L2 out {eo:.3e} state {eS:.3e}", flush=True)
     assert eo <= TOL_BF16 and eS <= TOL_BF16
 
