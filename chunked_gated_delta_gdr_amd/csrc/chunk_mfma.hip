@@ -267,6 +267,19 @@ __device__ __forceinline__ float4v diag_inverse_t(float4v n, float4v nt, int lan
   return mm2(z2p, split4(dt2), dt2);                 // D^T = D_2^T + Z_2^T D_2^T
 }
 
+// Role index of the calling wave, wave-uniform (a scalar), so role dispatch is a scalar
+// branch.  Waves w and w + 4 share a SIMD; by default the value waves (0, 1) share theirs with
+// two staging waves (4, 5).  With channel gains, whose staging (two loads and a product per
+// item) is the longest helper phase, two value waves instead share their SIMDs with the two
+// T_ba waves (hardware waves 4, 5 take role indices 2, 3) and the four staging waves pair up
+// on the other two SIMDs (hardware waves 2, 3, 6, 7): measured 13 % faster there, and slower
+// for the other variants, whose T_ba products then compete with the value waves.
+template <int NVW, bool CHAN>
+__device__ __forceinline__ int role_wave(int tid) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  return (NVW == 2 && CHAN) ? ((w & 1) | ((w & 2) << 1) | ((w & 4) >> 1)) : w;
+}
+
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
 // the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
 // own role's state across iterations, and both run the kernel's barrier sequence.
@@ -292,11 +305,11 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   const int lane = tid & 63;
   // wave index as a provably wave-uniform (scalar) value: role dispatch below is then a
   // scalar branch, and each role's loop (with its barriers) runs only in its own waves
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = role_wave<NVW, CHAN>(tid);
   const int l16 = lane & 15, l4 = lane >> 4;
   const bool vwave = wave < NVW;
   const int hw = wave - NVW;               // helper wave index
-  const int ht = tid - NVW * 64;           // helper thread index
+  const int ht = (wave - NVW) * 64 + lane;   // helper thread index
   const short4v I16 = ident4(lane);
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
@@ -964,11 +977,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const int lane = tid & 63;
   // wave index as a provably wave-uniform (scalar) value: role dispatch below is then a
   // scalar branch, and each role's loop (with its barriers) runs only in its own waves
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = role_wave<NVW, CHAN>(tid);
   const int l16 = lane & 15, l4 = lane >> 4;
   const bool vwave = wave < NVW;
   const int hw = wave - NVW;               // helper wave index
-  const int ht = tid - NVW * 64;           // helper thread index
+  const int ht = (wave - NVW) * 64 + lane;   // helper thread index
   const short4v I16 = ident4(lane);
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
