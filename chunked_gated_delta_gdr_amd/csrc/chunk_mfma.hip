@@ -339,12 +339,11 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   // One staging point per chunk: every item of chunk c + 1 is written to LDS from registers
   // loaded a full iteration earlier, then the loads of chunk c + 2 are issued.  Items are
   // 16-byte granules in blocks of 64 (one wave-wide load): 16 blocks each of q, k and an
-  // explicit write key (64 x 128 bf16), then (with channel gains) the blocks of the 64 x BV
-  // value tile.  The two helpers that form T's off-diagonal blocks (hw 0, 1) stage only the
-  // value tile (without channel gains), after their block products' operand reads, so those
-  // products never wait behind staging writes (a wave's LDS operations complete in order); the
-  // loads' issue (about 160 cycles per 1 KB load, measured) and the LDS writes bound the
-  // staging waves' phase.  Block s * NSW + sw is slot s
+  // explicit write key (64 x 128 bf16), then the blocks of the 64 x BV value tile.  The two
+  // helpers that form T's off-diagonal blocks (hw 0, 1) stage nothing, so their block products
+  // never wait behind staging writes (a wave's LDS operations complete in order); the loads'
+  // issue (about 160 cycles per 1 KB load, measured) and the LDS writes bound the staging
+  // waves' phase.  Block s * NSW + sw is slot s
   // of staging wave sw = hw - 2, so everything about a block (source, LDS destination, row /
   // column split) is wave-uniform.  Every slot loads and is staged
   // unconditionally -- a slot past the last block repeats it without storing -- so the
@@ -352,10 +351,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   // a chunk issue back to back.  Rows past the end of the sequence are read clamped to the
   // last row and zeroed when staged.
   constexpr int NBP = (NQ + NK + NR) / 64;     // blocks of 64 x 128 arrays
-  // the value tile's blocks: on the T_ba waves (see below), except with channel gains, where
-  // those waves share their SIMDs with the value waves and the staging waves keep them
-  constexpr bool kTV = !CHAN;
-  constexpr int NB = kTV ? NBP : NBP + NVI / 64;
+  constexpr int NB = NBP + NVI / 64;
   constexpr int NSW = NHW - 2;                 // staging waves: helpers 2 .. NHW - 1
   constexpr int NSB = (NB + NSW - 1) / NSW;    // block slots per staging wave
   constexpr int VSH = BV == 32 ? 2 : 1;        // log2(items per value-tile row)
@@ -565,48 +561,6 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
     hc1 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p + 1] : a.h0;
   }
 
-  // (kTV) value-tile blocks hw, hw + 2, .. on the T_ba waves (hw 0, 1), which have time left in
-  // both phases: loaded after the A jobs, written at the start of the next phase (2 % on gdn)
-  constexpr int NVB = NVI / 64, NVBW = NVB / 2;
-  uint4 tva[NVBW], tvb[NVBW];
-#pragma unroll
-  for (int m = 0; m < NVBW; ++m) tva[m] = tvb[m] = make_uint4(0u, 0u, 0u, 0u);
-  auto tv_rc = [&](int m, int &t, int &col) __attribute__((always_inline)) {
-    const int u = (hw + 2 * m) * 64 + lane;
-    t = u >> VSH;
-    col = (u & (BV / 8 - 1)) * 8;
-  };
-  auto tv_load = [&](int c) __attribute__((always_inline)) {
-    const int c0 = c * kC, nm1 = min(kC, T - c0) - 1;
-    const long long cb = head0 + static_cast<long long>(c0) * tokstride;
-#pragma unroll
-    for (int m = 0; m < NVBW; ++m) {
-      int t, col;
-      tv_rc(m, t, col);
-      const uint32_t o = static_cast<uint32_t>(min(t, nm1) * rowb + (v0 + col) * 2);
-      tva[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(gv + cb) + o);
-      if (CHAN) tvb[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(gwr + cb) + o);
-    }
-  };
-  auto tv_stage = [&](int c, int buf) __attribute__((always_inline)) {
-    const int n = min(kC, T - c * kC);
-#pragma unroll
-    for (int m = 0; m < NVBW; ++m) {
-      int t, col;
-      tv_rc(m, t, col);
-      uint4 x = tva[m];
-      if (t >= n) x = make_uint4(0u, 0u, 0u, 0u);
-      if (CHAN) {
-        const uint4 w = tvb[m];
-        x = make_uint4(f32x2_to_bf16x2_bits(elem(w, 0) * elem(x, 0), elem(w, 1) * elem(x, 1)),
-                       f32x2_to_bf16x2_bits(elem(w, 2) * elem(x, 2), elem(w, 3) * elem(x, 3)),
-                       f32x2_to_bf16x2_bits(elem(w, 4) * elem(x, 4), elem(w, 5) * elem(x, 5)),
-                       f32x2_to_bf16x2_bits(elem(w, 6) * elem(x, 6), elem(w, 7) * elem(x, 7)));
-      }
-      *reinterpret_cast<uint4 *>(&sm.vp[buf][t][col]) = x;
-    }
-  };
-  if (kTV && !STG && nchunks > 0) tv_load(0);
   if (STG && nchunks > 0) load_items(0);
   for (int c = -1; c < nchunks; ++c) {
     const int cur = c & 1, nxt = (c + 1) & 1;
@@ -656,7 +610,6 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       load_ops(std::false_type{});
       load_ops(std::true_type{});
     }
-    if (kTV && !STG && have_next) tv_stage(c + 1, nxt);
     if (STG && have_next) {
       stage_items(c + 1, nxt);
       if (c + 2 < nchunks) load_items(c + 2);
@@ -1003,7 +956,6 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
         }
       } else {
         a_jobs(std::integral_constant<int, (6 + NAW - 1) / NAW>{}, hw < 2 ? hw : hw - 4, NAW);
-        if (kTV && !STG && c + 2 < nchunks) tv_load(c + 2);
       }
     }
   }

@@ -116,7 +116,7 @@ def test_bwd_chunk_sizes(variant, chunk):
     compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
 
 
-@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (32, 16), (16, 200)])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (98, 42), (32, 16), (16, 200)])
 def test_bwd_head_dims(Dk, Dv):
     s = spec("gdn", Dk=Dk, Dv=Dv, T=130)
     announce(f"bwd gdn f32 Dk={Dk} Dv={Dv} {s}")
@@ -182,7 +182,7 @@ def test_bwd_full_size_gdn_sampled():
     compare(got, ref, streams=streams)
 
 
-@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (32, 16)])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (100, 40), (98, 42), (32, 16)])
 def test_bwd_kda_head_dims(Dk, Dv):
     s = spec("kda", Dk=Dk, Dv=Dv, T=130)
     announce(f"bwd kda f32 Dk={Dk} Dv={Dv} {s}")
