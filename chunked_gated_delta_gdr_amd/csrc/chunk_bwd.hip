@@ -83,6 +83,27 @@ __device__ __forceinline__ void ldw(const float *p, float (&x)[W]) {
   }
 }
 
+// four consecutive elements of an io (bf16 or fp32) or fp32 array, at an index that is a multiple
+// of four from a 16-byte aligned base: one 8- or 16-byte load instead of four
+__device__ __forceinline__ void ld4e(const float *p, long long i, float *x) {
+  const float4 v = *reinterpret_cast<const float4 *>(p + i);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void ld4e(const uint16_t *p, long long i, float *x) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(p + i);
+  x[0] = bf16_bits_to_f32(v.x & 0xffffu); x[1] = bf16_bits_to_f32(v.x >> 16);
+  x[2] = bf16_bits_to_f32(v.y & 0xffffu); x[3] = bf16_bits_to_f32(v.y >> 16);
+}
+
+// W consecutive floats to LDS: one 16-byte write for W = 4 (p 16-byte aligned), else one write
+template <int W>
+__device__ __forceinline__ void st_row(float *p, const float *x) {
+  if constexpr (W == 4)
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  else
+    p[0] = x[0];
+}
+
 // log alpha of token `lane` of the chunk starting at token row row0 (0 past n or without decay)
 __device__ __forceinline__ float chunk_log_alpha(const ChunkArgs &f, long long row0, int n, int lane) {
   return (f.decay == GDR_DECAY_SCALAR && lane < n) ? f.log_alpha[row0 + static_cast<long long>(lane) * f.H] : 0.f;
@@ -98,6 +119,15 @@ __device__ __forceinline__ float ld_wkey(const BwdArgs &a, const IO *rbase, long
     return a.Rk[row0k + o];
   else
     return ld_f(rbase + row0k, o);
+}
+
+// the same four at once (ld4e)
+template <bool PC, typename IO>
+__device__ __forceinline__ void ld_wkey4(const BwdArgs &a, const IO *rbase, long long row0k, long long o, float *x) {
+  if constexpr (PC)
+    ld4e(a.Rk + row0k, o, x);
+  else
+    ld4e(rbase + row0k, o, x);
 }
 
 // tile u < 10 of the ten 16 x 16 tiles on and below the diagonal of a 64 x 64 matrix
@@ -365,8 +395,9 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 constexpr int kStBV = 32;
 constexpr int kStThreads = 512;
 
-template <typename IO, int DK, bool CHD, bool PC>
+template <typename IO, int DK, bool CHD, bool PC, bool V4>
 __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
+  // V4: four consecutive elements per load and per LDS write, as in the reverse sweep
   constexpr int LD = DK + 4;
   constexpr int kBV = kStBV, kThreads = kStThreads;
   constexpr int kLoadIt = kCMax * DK / kThreads;
@@ -391,7 +422,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   __shared__ __align__(16) float Ws[kCMax][LD];   // W of the chunk
   __shared__ __align__(16) float Rs[kCMax][LD];   // write keys (CHD: decayed)
   __shared__ __align__(16) float Ss[kBV][LD];     // mirror of the state
-  __shared__ __align__(16) float Dl[kCMax][kBV];  // e^{g_n - g} D
+  __shared__ __align__(16) float Dl[kCMax][kBV + 4];  // e^{g_n - g} D (rows padded as in the sweep)
   __shared__ __align__(16) float Us[kCMax][kBV];  // U
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
   __shared__ float gcn[CHD ? DK : 1];            // CHD: 2^G_n per channel
@@ -416,33 +447,81 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     Ss[r][c] = s;
   }
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
+  constexpr int STEP = V4 ? 4 : 1;   // elements per load
+  static_assert(!V4 || (kLoadIt % 4 == 0 && kUIt % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
   float pw[kLoadIt], pu[kUIt], pr[kLoadIt];
-  float pg[CHD ? kLoadIt : 1], pgn = 0.f;   // CHD: G of the staged elements, G_n of the thread's channel
+  // CHD: G of the staged elements, G_n of the thread's channels (the same in every item:
+  // kThreads is a multiple of DK; V4: the four channels 4 (tid mod DK/4) + j)
+  float pg[CHD ? kLoadIt : 1], pgn[STEP] = {};
+  // element `it` of this thread in a chunk's [C][DK] tile and in a [C][kBV] value tile
+  auto elem_tc = [&](int it, int &t, int &c) __attribute__((always_inline)) {
+    if constexpr (V4) {
+      const int iv = tid + (it >> 2) * kThreads;
+      t = iv / (DK / 4);
+      c = 4 * (iv % (DK / 4)) + (it & 3);
+    } else {
+      const int idx = tid + it * kThreads;
+      t = idx / DK;
+      c = idx % DK;
+    }
+  };
+  auto elem_tr = [&](int it, int &t, int &r) __attribute__((always_inline)) {
+    if constexpr (V4) {
+      const int iv = tid + (it >> 2) * kThreads;
+      t = iv / (kBV / 4);
+      r = 4 * (iv % (kBV / 4)) + (it & 3);
+    } else {
+      const int idx = tid + it * kThreads;
+      t = idx / kBV;
+      r = idx % kBV;
+    }
+  };
   // loads of chunk ci into registers (indices clamped into the chunk)
   auto cload = [&](int ci) {
     const int c0 = ci * C, n = min(C, T - c0);
     const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
     const float *Wc = a.Ww + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
-      pw[it] = Wc[static_cast<long long>(t) * Dk + c];
-      pr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c);
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
+      t = min(t, n - 1);
+      if constexpr (V4) {
+        c = min(c, Dk - 4);
+        ld4e(Wc, static_cast<long long>(t) * Dk + c, &pw[it]);
+        ld_wkey4<PC>(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c, &pr[it]);
+      } else {
+        c = min(c, Dk - 1);
+        pw[it] = Wc[static_cast<long long>(t) * Dk + c];
+        pr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, static_cast<long long>(t) * H * Dk + c);
+      }
     }
     if constexpr (CHD) {
-      // (kThreads is a multiple of DK: the thread's channel is the same in every item)
       const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
 #pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
-        pg[it] = Gc[static_cast<long long>(t) * Dk + c];
+      for (int it = 0; it < kLoadIt; it += STEP) {
+        int t, c;
+        elem_tc(it, t, c);
+        t = min(t, n - 1);
+        if constexpr (V4)
+          ld4e(Gc, static_cast<long long>(t) * Dk + min(c, Dk - 4), &pg[it]);
+        else
+          pg[it] = Gc[static_cast<long long>(t) * Dk + min(c, Dk - 1)];
       }
-      pgn = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
+      if constexpr (V4)
+        ld4e(Gc, static_cast<long long>(n - 1) * Dk + min(4 * (tid % (DK / 4)), Dk - 4), pgn);
+      else
+        pgn[0] = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
     }
 #pragma unroll
-    for (int it = 0; it < kUIt; ++it) {
-      const int idx = tid + it * kThreads, t = min(idx / kBV, n - 1), r = min(idx % kBV, nv - 1);
-      pu[it] = a.Uw[(row0 + static_cast<long long>(t) * H) * Dv + v0 + r];
+    for (int it = 0; it < kUIt; it += STEP) {
+      int t, r;
+      elem_tr(it, t, r);
+      t = min(t, n - 1);
+      if constexpr (V4)
+        ld4e(a.Uw, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 4), &pu[it]);
+      else
+        pu[it] = a.Uw[(row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 1)];
     }
   };
   if (a.NC > 0) cload(0);
@@ -465,22 +544,38 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
       const bool in = t < n && c < Dk;
-      Ws[t][c] = in ? pw[it] : 0.f;
-      if constexpr (CHD)
-        Rs[t][c] = in ? pr[it] * chd::ex2(pgn - pg[it]) : 0.f;
-      else
-        Rs[t][c] = in ? pr[it] : 0.f;
+      float w4[STEP], r4[STEP];
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) {
+        w4[j] = in ? pw[it + j] : 0.f;
+        if constexpr (CHD)
+          r4[j] = in ? pr[it + j] * chd::ex2(pgn[j] - pg[it + j]) : 0.f;
+        else
+          r4[j] = in ? pr[it + j] : 0.f;
+      }
+      st_row<STEP>(&Ws[t][c], w4);
+      st_row<STEP>(&Rs[t][c], r4);
     }
     if constexpr (CHD) {
-      if (tid < DK) gcn[tid] = chd::ex2(pgn);
+      if constexpr (V4) {
+        if (tid < DK / 4)
+          for (int j = 0; j < 4; ++j) gcn[4 * tid + j] = chd::ex2(pgn[j]);
+      } else {
+        if (tid < DK) gcn[tid] = chd::ex2(pgn[0]);
+      }
     }
 #pragma unroll
-    for (int it = 0; it < kUIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / kBV, r = idx % kBV;
-      Us[t][r] = (t < n && r < nv) ? pu[it] : 0.f;
+    for (int it = 0; it < kUIt; it += STEP) {
+      int t, r;
+      elem_tr(it, t, r);
+      float u4[STEP];
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) u4[j] = (t < n && r + j < nv) ? pu[it + j] : 0.f;
+      st_row<STEP>(&Us[t][r], u4);
     }
     if (tid < kCMax) chunk_gates(f, tok(0), n, tid, gs, eg, wd);
     __syncthreads();
@@ -506,10 +601,14 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
         if (u >= NTS) continue;
         const int rbs = u / NCB, cbs = u % NCB;
         float4v acc = Sacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
-        // (rows past n of Dl are zero, and n + 7 < 64 + 8: the pairs stay inside the tiles)
-        for (int t0 = 0; t0 < n; t0 += 8) {
-          acc = mfma4(Dl[t0 + kq][16 * rbs + col], Rs[t0 + kq][16 * cbs + col], acc);
-          acc2 = mfma4(Dl[t0 + 4 + kq][16 * rbs + col], Rs[t0 + 4 + kq][16 * cbs + col], acc2);
+        // (rows past n of Dl are zero) tokens in blocks of 16, lane quarter kq taking
+        // t = m0 + j + 4 kq at step j of the block at m0, two steps per pass: the rows read by
+        // one instruction sit 16 banks apart in Rs (row stride DK + 4) and Dl (kBV + 4)
+        const int n16 = (n + 15) & ~15;
+        for (int i = 0; i < n16; i += 8) {
+          const int t = (i & ~15) + ((i >> 2) & 3) + 4 * kq;   // steps (i / 4) mod 4 and the next
+          acc = mfma4(Dl[t][16 * rbs + col], Rs[t][16 * cbs + col], acc);
+          acc2 = mfma4(Dl[t + 1][16 * rbs + col], Rs[t + 1][16 * cbs + col], acc2);
         }
         acc += acc2;
         Sacc[m] = acc;
@@ -535,8 +634,11 @@ constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
 
 
-template <typename IO, int DK, bool CHD, bool PC, bool BAND>
+template <typename IO, int DK, bool CHD, bool PC, bool BAND, bool V4>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
+  // V4 (Dk and Dv multiples of 4, 16-byte aligned tensors): every staged array is read four
+  // consecutive elements per load and written to LDS 16 bytes at a time; a quarter of the
+  // load addresses stay live across the chunk, which keeps this kernel out of scratch
   constexpr int LD = DK + 4;
   constexpr int kBV = kSwBV, kThreads = kSwThreads;
   constexpr int kLoadIt = kCMax * DK / kThreads;
@@ -566,10 +668,13 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   __shared__ __align__(16) float dS[kBV][LD];       // mirror of the gradient at the chunk's end
   __shared__ __align__(16) float dOs[kCMax][kBV];   // dO
   __shared__ __align__(16) float dDs[kCMax][kBV];   // dD
-  __shared__ __align__(16) float Am[kCMax][kBV];    // scale e^g dO
-  __shared__ __align__(16) float Bm[kCMax][kBV];    // e^g dX
+  // (rows padded to kBV + 4: the dS update reads rows t, t + 4, t + 8, t + 12 in one
+  // instruction, on distinct banks)
+  __shared__ __align__(16) float Am[kCMax][kBV + 4];    // scale e^g dO
+  __shared__ __align__(16) float Bm[kCMax][kBV + 4];    // e^g dX
   __shared__ float gs[kCMax], eg[kCMax], wd[kCMax];
   __shared__ float gcn[CHD ? DK : 1];   // CHD: 2^G_n per channel
+  __shared__ float bsm[kCMax];          // scalar gain of the chunk being staged
 
   const long long sh = static_cast<long long>(b) * H + h;
   // dS tiles of this wave: tile u = wave + 8 m -> value-row block u / NCB, channel block u % NCB
@@ -598,50 +703,128 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   // only after the first two barriers of a chunk, are loaded at its start.
   constexpr int kCC = kCMax * kCMax / kThreads, kOIt = kCMax * kBV / kThreads;
   float xr[kLoadIt], xk[kLoadIt], xg[kLoadIt], xq[kLoadIt], xt[kCC], xp[kCC], xo[kOIt], xla = 0.f;
+  // scalar gain: beta of the next chunk's token tid (tid < C), published to bsm after this
+  // chunk's staging has read it (one load per token instead of one per staged element)
+  float xb = 0.f;
   // CHD: G of the staged elements and G_n of the thread's channel (the same in every item:
   // kThreads is a multiple of DK), loaded a chunk ahead once this chunk's queries are staged
-  float xgv[CHD ? kLoadIt : 1], xgn = 0.f;
+  float xgv[CHD ? kLoadIt : 1], xgn[V4 ? 4 : 1] = {};
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
-  auto cload = [&](int ci) {
+  constexpr int STEP = V4 ? 4 : 1;   // elements per load
+  static_assert(!V4 || (kLoadIt % 4 == 0 && kCC % 4 == 0 && kOIt % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
+  // element `it` of this thread in a chunk's [C][DK] tile (V4: four consecutive channels per
+  // group of four elements; the thread's channels are then 4 (tid mod DK/4) + j in every
+  // group, as kThreads is a multiple of DK), in a [C][kBV] value tile, in a C x C matrix (flat)
+  auto elem_tc = [&](int it, int &t, int &c) __attribute__((always_inline)) {
+    if constexpr (V4) {
+      const int iv = tid + (it >> 2) * kThreads;
+      t = iv / (DK / 4);
+      c = 4 * (iv % (DK / 4)) + (it & 3);
+    } else {
+      const int idx = tid + it * kThreads;
+      t = idx / DK;
+      c = idx % DK;
+    }
+  };
+  auto elem_tr = [&](int it, int &t, int &r) __attribute__((always_inline)) {
+    if constexpr (V4) {
+      const int iv = tid + (it >> 2) * kThreads;
+      t = iv / (kBV / 4);
+      r = 4 * (iv % (kBV / 4)) + (it & 3);
+    } else {
+      const int idx = tid + it * kThreads;
+      t = idx / kBV;
+      r = idx % kBV;
+    }
+  };
+  auto elem_cc = [&](int it) __attribute__((always_inline)) {
+    return V4 ? 4 * (tid + (it >> 2) * kThreads) + (it & 3) : tid + it * kThreads;
+  };
+  // write key = key (no explicit or preconditioned write key): the keys are loaded once
+  const bool rk_same = !PC && f.wkey != GDR_WKEY_EXPLICIT;
+  // the next chunk's loads, in three groups: keys (and gains), T and P, dO
+  auto cload_keys = [&](int ci) {
     const int c0 = ci * C, n = min(C, T - c0);
     const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
-    if (tid < kCMax) xla = chunk_log_alpha(f, row0, n, tid);
-    const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
-    const float *bc = f.beta + row0;
-#pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-      xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
-      xk[it] = ld_f(kc, o);
-      xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
+    if (tid < kCMax) {
+      xla = chunk_log_alpha(f, row0, n, tid);
+      if (f.gain == GDR_GAIN_SCALAR) xb = f.beta[row0 + static_cast<long long>(min(tid, n - 1)) * H];
     }
+    const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
+#pragma unroll
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
+      const int tc = min(t, n - 1);
+      if constexpr (V4) {
+        const int o = tc * H * Dk + min(c, Dk - 4);
+        if (!rk_same) ld_wkey4<PC>(a, rbase, row0 * Dk, o, &xr[it]);
+        ld4e(kc, o, &xk[it]);
+        if (f.gain != GDR_GAIN_SCALAR) ld4e(ec, o, &xg[it]);
+      } else {
+        const int o = tc * H * Dk + min(c, Dk - 1);
+        if (!rk_same) xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
+        xk[it] = ld_f(kc, o);
+        if (f.gain != GDR_GAIN_SCALAR) xg[it] = ld_f(ec, o);
+      }
+    }
+  };
+  auto cload_tp = [&](int ci) {
     const long long cc = (sh * a.NC + ci) * static_cast<long long>(C * C);
 #pragma unroll
-    for (int it = 0; it < kCC; ++it) {
-      const int idx = min(tid + it * kThreads, C * C - 1);
-      xt[it] = a.Tw[cc + idx];
-      xp[it] = a.Pw[cc + idx];
+    for (int it = 0; it < kCC; it += STEP) {
+      if constexpr (V4) {
+        const int iv = min(elem_cc(it), C * C - 4);
+        ld4e(a.Tw + cc, iv, &xt[it]);
+        ld4e(a.Pw + cc, iv, &xp[it]);
+      } else {
+        const int idx = min(elem_cc(it), C * C - 1);
+        xt[it] = a.Tw[cc + idx];
+        xp[it] = a.Pw[cc + idx];
+      }
     }
+  };
+  auto cload_do = [&](int ci) {
+    const int c0 = ci * C, n = min(C, T - c0);
+    const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
 #pragma unroll
-    for (int it = 0; it < kOIt; ++it) {
-      const int idx = tid + it * kThreads, t = min(idx / kBV, n - 1), r = min(idx % kBV, nv - 1);
-      xo[it] = ld_f(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + r);
+    for (int it = 0; it < kOIt; it += STEP) {
+      int t, r;
+      elem_tr(it, t, r);
+      t = min(t, n - 1);
+      if constexpr (V4)
+        ld4e(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 4), &xo[it]);
+      else
+        xo[it] = ld_f(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 1));
     }
+  };
+  auto cload = [&](int ci) {
+    cload_keys(ci);
+    cload_tp(ci);
+    cload_do(ci);
   };
   auto gload = [&](int ci) {
     const int n = min(C, T - ci * C);
     const float *Gc = a.Gw + (sh * a.NC + ci) * static_cast<long long>(C) * Dk;
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = min(idx / DK, n - 1), c = min(idx % DK, Dk - 1);
-      xgv[it] = Gc[static_cast<long long>(t) * Dk + c];
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
+      t = min(t, n - 1);
+      if constexpr (V4)
+        ld4e(Gc, static_cast<long long>(t) * Dk + min(c, Dk - 4), &xgv[it]);
+      else
+        xgv[it] = Gc[static_cast<long long>(t) * Dk + min(c, Dk - 1)];
     }
-    xgn = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
+    if constexpr (V4)
+      ld4e(Gc, static_cast<long long>(n - 1) * Dk + min(4 * (tid % (DK / 4)), Dk - 4), xgn);
+    else
+      xgn[0] = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
   };
   if (a.NC > 0) {
     cload(a.NC - 1);
     if constexpr (CHD) gload(a.NC - 1);
+    if (tid < kCMax) bsm[tid] = xb;
   }
 
   for (int ci = a.NC - 1; ci >= 0; --ci) {
@@ -654,9 +837,13 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     {
       const IO *qc = q + row0 * Dk;
 #pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        xq[it] = ld_f(qc, min(t, n - 1) * H * Dk + min(c, Dk - 1));
+      for (int it = 0; it < kLoadIt; it += STEP) {
+        int t, c;
+        elem_tc(it, t, c);
+        if constexpr (V4)
+          ld4e(qc, min(t, n - 1) * H * Dk + min(c, Dk - 4), &xq[it]);
+        else
+          xq[it] = ld_f(qc, min(t, n - 1) * H * Dk + min(c, Dk - 1));
       }
     }
     if (tid < kCMax) chunk_gates_from(xla, n, tid, gs, eg, wd);
@@ -673,39 +860,63 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
         }
       }
     }
+    // (V4: a lane's four elements are consecutive channels of one row, one 16-byte LDS write;
+    // the rows are 16-byte aligned)
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
       const bool in = t < n && c < Dk;
-      if constexpr (CHD) {
-        // (exp2f, not the bare hardware 2^x the other kernels use: measured at B4 H16 T4096,
-        // the schedule the compiler makes around the single instruction costs this kernel
-        // 1.04 -> 1.19 ms)
-        Ks[t][c] = in ? xr[it] * exp2f(xgn - xgv[it]) : 0.f;
-        Es[t][c] = in ? xg[it] * xk[it] * exp2f(xgv[it]) : 0.f;
-      } else {
-        Ks[t][c] = in ? xr[it] : 0.f;
-        Es[t][c] = in ? xg[it] * xk[it] : 0.f;
+      const float gsc = f.gain == GDR_GAIN_SCALAR ? bsm[t] : 0.f;
+      float kr[STEP], ke[STEP];
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) {
+        const float r = rk_same ? xk[it + j] : xr[it + j];
+        const float g = f.gain == GDR_GAIN_SCALAR ? gsc : xg[it + j];
+        if constexpr (CHD) {
+          // (exp2f, not the bare hardware 2^x the other kernels use: measured at B4 H16 T4096,
+          // the schedule the compiler makes around the single instruction costs this kernel
+          // 1.04 -> 1.19 ms)
+          kr[j] = in ? r * exp2f(xgn[j] - xgv[it + j]) : 0.f;
+          ke[j] = in ? g * xk[it + j] * exp2f(xgv[it + j]) : 0.f;
+        } else {
+          kr[j] = in ? r : 0.f;
+          ke[j] = in ? g * xk[it + j] : 0.f;
+        }
       }
+      st_row<STEP>(&Ks[t][c], kr);
+      st_row<STEP>(&Es[t][c], ke);
     }
     if constexpr (CHD) {
-      if (tid < DK) gcn[tid] = exp2f(xgn);
+      if constexpr (V4) {
+        if (tid < DK / 4)
+          for (int j = 0; j < 4; ++j) gcn[4 * tid + j] = exp2f(xgn[j]);
+      } else {
+        if (tid < DK) gcn[tid] = exp2f(xgn[0]);
+      }
     }
 #pragma unroll
     for (int it = 0; it < kCC; ++it) {
-      const int idx = tid + it * kThreads;
+      const int idx = elem_cc(it);
       if (idx < C * C) {
         Tm[idx / C][idx % C] = xt[it];
         Pm[idx / C][idx % C] = xp[it];
       }
     }
 #pragma unroll
-    for (int it = 0; it < kOIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / kBV, r = idx % kBV;
-      dOs[t][r] = (t < n && r < nv) ? xo[it] : 0.f;
+    for (int it = 0; it < kOIt; it += STEP) {
+      int t, r;
+      elem_tr(it, t, r);
+      float o4[STEP];
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) o4[j] = (t < n && r + j < nv) ? xo[it + j] : 0.f;
+      st_row<STEP>(&dOs[t][r], o4);
     }
     __syncthreads();
-    if (ci > 0) cload(ci - 1);   // in flight during this chunk's products
+    // the next chunk's loads, in flight during this chunk's products: T and P here, the keys
+    // and dO after the next barrier (a wave's loads hold up its own instruction issue; split
+    // between two phases they lengthen each less than they would one)
+    if (ci > 0) cload_tp(ci - 1);
     const int tr0 = 16 * tb + 4 * kq;   // the lane's result rows (tokens) of the dD / dX tile
     // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO, tile (tb, rb); P is zero above the
     // diagonal and T, P, dO rows past n (inside the chunk) are zero
@@ -725,6 +936,10 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    if (ci > 0) {
+      cload_keys(ci - 1);
+      cload_do(ci - 1);
+    }
     // dX = T^T dD, tile (tb, rb); written out for the per-chunk pass, and folded with e^g
     // into the state-gradient update
     {
@@ -742,32 +957,69 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     }
     // queries replace the write keys (their last read was before the barrier above)
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      Ks[t][c] = (t < n && c < Dk) ? (CHD ? xq[it] * exp2f(xgv[it]) : xq[it]) : 0.f;
+    for (int it = 0; it < kLoadIt; it += STEP) {
+      int t, c;
+      elem_tc(it, t, c);
+      float q4[STEP];
+#pragma unroll
+      for (int j = 0; j < STEP; ++j)
+        q4[j] = (t < n && c < Dk) ? (CHD ? xq[it + j] * exp2f(xgv[it + j]) : xq[it + j]) : 0.f;
+      st_row<STEP>(&Ks[t][c], q4);
     }
     if constexpr (CHD) {
       if (ci > 0) gload(ci - 1);   // this chunk's G is no longer needed
     }
     __syncthreads();
+    // (the next chunk's gains: this chunk's staging read bsm before the first barrier)
+    if (ci > 0 && tid < kCMax) bsm[tid] = xb;
     // dS <- e^{g_n} dS + A^T Q - B^T E on the wave's tiles; rows of A, B past n are zero
+    // Tokens in blocks of 16, lane quarter kq taking t = m0 + j + 4 kq at step j of the block
+    // at m0: the rows one instruction reads sit 4 apart, i.e. 16 banks apart in Ks and Es (row
+    // stride DK + 4) and in Am and Bm (kBV + 4), so each operand read is free of bank
+    // conflicts; rows of the last block past n are zero.  With two tiles per wave (DK = 128)
+    // both share the channel block (wave + 8 m has the same remainder mod 8), so the two run
+    // in one loop: four independent accumulator chains, and one Q and one E read per step.
     {
       const float gl = eg[n - 1];
-#pragma unroll
-      for (int m = 0; m < NTW; ++m) {
-        const int u = wave + 8 * m;
-        if (u >= NTS) continue;
-        const int rbs = u / NCB, cbs = u % NCB;
-        float4v acc = dSacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
-        for (int t0 = 0; t0 < n; t0 += 4) {
-          acc = mfma4(Am[t0 + kq][16 * rbs + col], Ks[t0 + kq][16 * cbs + col], acc);
-          acc2 = mfma4(Bm[t0 + kq][16 * rbs + col], Es[t0 + kq][16 * cbs + col], acc2);
+      const int n16 = (n + 15) & ~15;
+      if constexpr (NTW == 2) {
+        static_assert(NCB == 8, "two tiles per wave share a channel block");
+        const int cbs = wave;
+        const float sc = CHD ? gcn[16 * cbs + col] : gl;
+        float4v a0 = dSacc[0] * sc, a1 = dSacc[1] * sc;
+        float4v b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < n16; i += 4) {
+          const int t = (i & ~15) + ((i >> 2) & 3) + 4 * kq;   // block i / 16, step (i / 4) mod 4
+          const float qv = Ks[t][16 * cbs + col], ev = Es[t][16 * cbs + col];
+          a0 = mfma4(Am[t][col], qv, a0);
+          a1 = mfma4(Am[t][16 + col], qv, a1);
+          b0 = mfma4(Bm[t][col], ev, b0);
+          b1 = mfma4(Bm[t][16 + col], ev, b1);
         }
-        acc -= acc2;
-        dSacc[m] = acc;
+        dSacc[0] = a0 - b0;
+        dSacc[1] = a1 - b1;
         // the LDS mirror for the next chunk's R dS^T (its reads of this chunk are done)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dS[16 * rbs + 4 * kq + r][16 * cbs + col] = acc[r];
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dS[16 * m + 4 * kq + r][16 * cbs + col] = dSacc[m][r];
+      } else {
+#pragma unroll
+        for (int m = 0; m < NTW; ++m) {
+          const int u = wave + 8 * m;
+          if (u >= NTS) continue;
+          const int rbs = u / NCB, cbs = u % NCB;
+          float4v acc = dSacc[m] * (CHD ? gcn[16 * cbs + col] : gl), acc2 = {0.f, 0.f, 0.f, 0.f};   // two chains
+          for (int i = 0; i < n16; i += 4) {
+            const int t = (i & ~15) + ((i >> 2) & 3) + 4 * kq;
+            acc = mfma4(Am[t][16 * rbs + col], Ks[t][16 * cbs + col], acc);
+            acc2 = mfma4(Bm[t][16 * rbs + col], Es[t][16 * cbs + col], acc2);
+          }
+          acc -= acc2;
+          dSacc[m] = acc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dS[16 * rbs + 4 * kq + r][16 * cbs + col] = acc[r];
+        }
       }
     }
   }
@@ -1592,6 +1844,17 @@ void launch_pc(const BwdArgs &a, F &&fn) {
     fn(std::false_type{});
 }
 
+// the kernels' four-element loads (V4): Dk and Dv multiples of 4 and every tensor they read that
+// way 16-byte aligned (the workspace sections are 256-byte aligned from the workspace's base)
+static bool vec4_ok(const BwdArgs &a) {
+  const ChunkArgs &f = a.f;
+  if (f.Dk % 4 != 0 || f.Dv % 4 != 0) return false;
+  const void *ps[] = {f.q, f.k, f.v, f.erase, f.write, f.write_key, a.dout, a.Tw, a.Pw, a.Gw, a.Rk, a.Ww, a.Uw};
+  for (const void *p : ps)
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
+  return true;
+}
+
 // launch_pc with a second flag, the band-limited T (never with the per-channel decay: the host
 // rejects that combination, and no such kernel is built)
 template <bool CHD, typename F>
@@ -1628,19 +1891,24 @@ hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);
   if (a.f.Dk <= 32) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
+  } else if (vec4_ok(a)) {
+    if (chd)
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value, true>), gs, dim3(kStThreads), 0, s, a); });
+    else
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value, true>), gs, dim3(kStThreads), 0, s, a); });
   } else {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
@@ -1651,19 +1919,24 @@ hipError_t sweep_io(const BwdArgs &a, hipStream_t s) {
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 32) {
     if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
+  } else if (vec4_ok(a)) {
+    if (chd)
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value, true>), grid, dim3(kSwThreads), 0, s, a); });
+    else
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value, true>), grid, dim3(kSwThreads), 0, s, a); });
   } else {
     if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
   }
   return hipGetLastError();
 }
