@@ -221,27 +221,51 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
     if ((j >> 4) > (i >> 4)) Tm[i][j] = 0.f;
   }
   const IO *qc = q + row0 * Dk;
-  {   // E, R, Q (CHD: log alpha): all loads first (clamped), then the masked stores
-    float xk[kLoadIt], xg[kLoadIt], xr[kLoadIt], xq[kLoadIt];
+  {   // E, R, Q (CHD: log alpha): all loads first (clamped), then the masked stores; the keys
+      // once when the write key is the key, a scalar gain once per token (lane t of every
+      // wave holds token t's, handed to the staged elements by a lane shuffle).  One copy of
+      // the loads and stores per case, so that no branch separates the loads (all in flight
+      // at once) and no register array is merged across cases.
     const IO *kc = k + row0 * Dk, *ec = er + row0 * Dk;
     const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
-    const float *bc = f.beta + row0;
+    const int lane = tid & 63;
+    auto stage = [&](auto same, auto scalar) __attribute__((always_inline)) {
+      constexpr bool kSame = decltype(same)::value, kScalar = decltype(scalar)::value;
+      float xk[kLoadIt], xg[kScalar ? 1 : kLoadIt], xr[kSame ? 1 : kLoadIt], xq[kLoadIt];
+      const float bl = kScalar ? f.beta[row0 + static_cast<long long>(min(lane, n - 1)) * H] : 0.f;
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-      xk[it] = ld_f(kc, o);
-      xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-      xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
-      xq[it] = CHD ? f.log_alpha[row0 * Dk + o] : ld_f(qc, o);
-    }
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
+        xk[it] = ld_f(kc, o);
+        if constexpr (!kScalar) xg[it] = ld_f(ec, o);
+        if constexpr (!kSame) xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
+        xq[it] = CHD ? f.log_alpha[row0 * Dk + o] : ld_f(qc, o);
+      }
 #pragma unroll
-    for (int it = 0; it < kLoadIt; ++it) {
-      const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-      const bool in = t < n && c < Dk;
-      Es[t][c] = in ? xg[it] * xk[it] : 0.f;
-      Rs[t][c] = in ? xr[it] : 0.f;
-      Xs[t][c] = in ? xq[it] : 0.f;
+      for (int it = 0; it < kLoadIt; ++it) {
+        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+        const bool in = t < n && c < Dk;
+        float g;
+        if constexpr (kScalar)
+          g = __shfl(bl, t);   // (t < kCMax = 64: a lane of this wave)
+        else
+          g = xg[it];
+        Es[t][c] = in ? g * xk[it] : 0.f;
+        if constexpr (kSame)
+          Rs[t][c] = in ? xk[it] : 0.f;
+        else
+          Rs[t][c] = in ? xr[it] : 0.f;
+        Xs[t][c] = in ? xq[it] : 0.f;
+      }
+    };
+    const bool rk_same = !PC && f.wkey != GDR_WKEY_EXPLICIT, gsc = f.gain == GDR_GAIN_SCALAR;
+    if (rk_same) {
+      if (gsc) stage(std::true_type{}, std::true_type{});
+      else stage(std::true_type{}, std::false_type{});
+    } else {
+      if (gsc) stage(std::false_type{}, std::true_type{});
+      else stage(std::false_type{}, std::false_type{});
     }
   }
   __syncthreads();
@@ -1187,10 +1211,12 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (vb + kVB < Dv) vload(vb + kVB);
-    // K = kVB value rows in steps of 4 (rows past nvb are zero)
+    // K = kVB value rows in steps of 4 (rows past nvb are zero), lane quarter kq taking row
+    // m0 + j + 4 kq at step j of each block of 16: the rows one instruction reads sit 4 apart,
+    // 16 banks apart at the row strides DK + 4 and kCMax + 4, free of bank conflicts
 #pragma unroll
     for (int ks = 0; ks < kVB; ks += 4) {
-      const int kr = ks + kq;
+      const int kr = (ks & ~15) + ((ks >> 2) & 3) + 4 * kq;
       const float ao = sm.A.dOT[kr][16 * tb + col], ax = sm.A.dXT[kr][16 * tb + col];
       const float ad = sm.A.DT[kr][16 * tb + col];
 #pragma unroll
@@ -1485,27 +1511,48 @@ __global__ __launch_bounds__(kCkThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     // ---- key products -------------------------------------------------------------------
     __syncthreads();   // the value-loop tiles are dead (the key tiles share their memory)
-    {   // Q, E, R: all loads first (clamped), then the masked LDS stores
-      float xq[kLoadIt], xk[kLoadIt], xg[kLoadIt], xr[kLoadIt];
+    {   // Q, E, R: all loads first (clamped), then the masked LDS stores; the keys once when
+        // the write key is the key, a scalar gain once per token (lane t holds token t's).  One
+        // copy per case, so that no branch separates the loads and no array is merged.
       const IO *qc = q + row0 * Dk, *kc = k + row0 * Dk, *ec = er + row0 * Dk;
       const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
-      const float *bc = f.beta + row0;
+      auto stage = [&](auto same, auto scalar) __attribute__((always_inline)) {
+        constexpr bool kSame = decltype(same)::value, kScalar = decltype(scalar)::value;
+        float xq[kLoadIt], xk[kLoadIt], xg[kScalar ? 1 : kLoadIt], xr[kSame ? 1 : kLoadIt];
+        const float bl = kScalar ? f.beta[row0 + static_cast<long long>(min(lane, n - 1)) * H] : 0.f;
   #pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
-        xq[it] = ld_f(qc, o);
-        xk[it] = ld_f(kc, o);
-        xg[it] = f.gain == GDR_GAIN_SCALAR ? bc[tc * H] : ld_f(ec, o);
-        xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
-      }
+        for (int it = 0; it < kLoadIt; ++it) {
+          const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+          const int tc = min(t, n - 1), o = tc * H * Dk + min(c, Dk - 1);
+          xq[it] = ld_f(qc, o);
+          xk[it] = ld_f(kc, o);
+          if constexpr (!kScalar) xg[it] = ld_f(ec, o);
+          if constexpr (!kSame) xr[it] = ld_wkey<PC>(a, rbase, row0 * Dk, o);
+        }
   #pragma unroll
-      for (int it = 0; it < kLoadIt; ++it) {
-        const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
-        const bool in = t < n && c < Dk;
-        sm.B.Q[t][c] = in ? xq[it] : 0.f;
-        sm.B.E[t][c] = in ? xg[it] * xk[it] : 0.f;
-        sm.B.R[t][c] = in ? xr[it] : 0.f;
+        for (int it = 0; it < kLoadIt; ++it) {
+          const int idx = tid + it * kThreads, t = idx / DK, c = idx % DK;
+          const bool in = t < n && c < Dk;
+          float g;
+          if constexpr (kScalar)
+            g = __shfl(bl, t);   // (t < kCMax = 64: a lane of this wave)
+          else
+            g = xg[it];
+          sm.B.Q[t][c] = in ? xq[it] : 0.f;
+          sm.B.E[t][c] = in ? g * xk[it] : 0.f;
+          if constexpr (kSame)
+            sm.B.R[t][c] = in ? xk[it] : 0.f;
+          else
+            sm.B.R[t][c] = in ? xr[it] : 0.f;
+        }
+      };
+      const bool rk_same = !PC && f.wkey != GDR_WKEY_EXPLICIT, gsc = f.gain == GDR_GAIN_SCALAR;
+      if (rk_same) {
+        if (gsc) stage(std::true_type{}, std::true_type{});
+        else stage(std::true_type{}, std::false_type{});
+      } else {
+        if (gsc) stage(std::false_type{}, std::true_type{});
+        else stage(std::false_type{}, std::false_type{});
       }
     }
     // the decay factors of the state terms, and the C x C gradients (tiles on and below the
