@@ -132,6 +132,40 @@ def test_bwd_bf16(variant):
     compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
 
 
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_bwd_unaligned_inputs(variant):
+    """Queries, keys and dO one element past a 16-byte boundary: the kernels fall back from
+    their four-element loads to element loads, with the same gradients (bitwise: the same
+    values reach the same products)."""
+    import torch
+    import chunked_gated_delta_gdr_amd as G
+    s = spec(variant, dtype="bf16", Dk=128, Dv=128, T=150)
+    announce(f"bwd {variant} bf16 unaligned q, k, dO {s}")
+    x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
+    io, f32 = torch.bfloat16, torch.float32
+
+    def shifted(a):
+        t = dev(a, io)
+        buf = torch.empty(t.numel() + 1, dtype=io, device=t.device)
+        u = buf[1:].view(t.shape)
+        u.copy_(t)
+        assert u.data_ptr() % 16 != 0
+        return u
+
+    def call(q, k, d_out):
+        g = G.gdr_chunk_bwd(q, k, dev(x["v"], io), d_out, beta=dev(x.get("beta"), f32),
+                            log_alpha=dev(x.get("log_alpha"), f32), state_in=dev(S0, f32),
+                            d_state_out=dev(cot["d_state_out"], f32), chunk=s.chunk)
+        torch.cuda.synchronize()
+        return {n: host(v) for n, v in g.items()}
+
+    got = call(shifted(x["q"]), shifted(x["k"]), shifted(cot["d_out"]))
+    ref = call(dev(x["q"], io), dev(x["k"], io), dev(cot["d_out"], io))
+    for n in ref:
+        assert np.array_equal(got[n], ref[n]), n
+    compare(got, oracle_grads(s, x, cot, state_in=S0))
+
+
 @pytest.mark.parametrize("T", [1, 37, 64, 65])
 def test_bwd_short_and_ragged(T):
     s = spec("gdn", T=T)
