@@ -184,8 +184,8 @@ def host_cpu():
 
 def cpu_baseline(s, x, tokens: int, n_streams: int, min_cpu_s: float = 10.0):
     """The fp64 oracle on every sampled stream, one stream per task, over every core this
-    process may use, capped by OMP_NUM_THREADS when the environment sets it (a GPU machine's share
-    of its host), and by the number of streams.  Passes over the sample repeat until at least
+    process may use, capped by OMP_NUM_THREADS when the environment sets it (a process's share
+    of a shared host), and by the number of streams.  Passes over the sample repeat until at least
     `min_cpu_s` of CPU work has been timed."""
     import multiprocessing as mp
     import numpy as np
@@ -347,17 +347,7 @@ def bench_decode(args):
         step(i)
     torch.cuda.synchronize()
     n_settle = settle(step, args.settle_s)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    launch = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step, launch = time_steps(step, args.steps, stream)
     avg_s = sum(launch) / len(launch) / 1e3
     print(f"[bench] decode {args.steps} steps: launch avg {avg_s * 1e6:.2f} us min {min(launch) * 1e3:.2f} us",
           file=sys.stderr, flush=True)
@@ -393,6 +383,31 @@ def settle(step, seconds: float) -> int:
             n += 1
         torch.cuda.synchronize()
     return n
+
+
+def time_steps(step, steps: int, stream):
+    """The timed region: `steps` launches back to back between one pair of HIP events on the
+    launch stream (synchronized on both sides); returns ms per step.  Then a second region of
+    the same length with an event pair around every launch, for the per-launch durations the
+    roofline uses (recording events between launches widens the gaps between them, so the
+    first region, which `value` comes from, records none).  Returns (ms_per_step, [ms per
+    launch])."""
+    import torch
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return ms_per_step, [a.elapsed_time(b) for a, b in ev]
 
 
 def bwd_alg_bytes(s) -> int:
@@ -461,17 +476,13 @@ def bench_backward(args):
         g = step()
     torch.cuda.synchronize()
     n_settle = settle(lambda i: step(), args.settle_s)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        g = step()
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    last = {}
+
+    def step_keep(i):
+        last["g"] = step()
+
+    ms_per_step, call_ms = time_steps(step_keep, args.steps, stream)
+    g = last["g"]
     avg_s = sum(call_ms) / len(call_ms) / 1e3
     print(f"[bench] backward call avg {avg_s * 1e6:.1f} us min {min(call_ms) * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -569,7 +580,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): every "
               "(batch, head) stream is independent, so more GPUs would each run their own share of "
-              "streams with no communication; this build measures the one-GPU share.", file=sys.stderr)
+              "streams with no communication; bench.py measures the one-GPU share.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "decode":
         bench_decode(args)
@@ -635,25 +646,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
     n_settle = settle(step, args.settle_s)
-    # per-launch events on the launch stream, and one pair around the whole timed region
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, launch_ms = time_steps(step, args.steps, stream)
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / args.steps
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    print(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms events, {wall * 1e3:.3f} ms host wall; "
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * args.steps:.3f} ms events (then {args.steps} "
+          f"launches with per-launch events), {wall * 1e3:.3f} ms host wall for both; "
           f"launch avg {avg_launch_s * 1e6:.2f} us min {min(launch_ms) * 1e3:.2f} us",
           file=sys.stderr, flush=True)
 
