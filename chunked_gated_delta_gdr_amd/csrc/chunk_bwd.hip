@@ -419,11 +419,11 @@ __global__ __launch_bounds__(kPrThreads) void bwd_prep_kernel(BwdArgs a) {
 constexpr int kStBV = 32;
 constexpr int kStThreads = 512;
 
-template <typename IO, int DK, bool CHD, bool PC, bool V4>
+template <typename IO, int DK, bool CHD, bool PC, bool V4, int BVT>
 __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   // V4: four consecutive elements per load and per LDS write, as in the reverse sweep
   constexpr int LD = DK + 4;
-  constexpr int kBV = kStBV, kThreads = kStThreads;
+  constexpr int kBV = BVT, kThreads = kStThreads;   // value rows per workgroup: 32, or 16
   constexpr int kLoadIt = kCMax * DK / kThreads;
   constexpr int kUIt = kCMax * kBV / kThreads;
   constexpr int NCB = DK / 16;
@@ -472,7 +472,10 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
   }
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
   constexpr int STEP = V4 ? 4 : 1;   // elements per load
-  static_assert(!V4 || (kLoadIt % 4 == 0 && kUIt % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
+  // (the U tile in fours only when every thread has whole groups of four: kBV = 32)
+  constexpr bool V4U = V4 && kUIt % 4 == 0;
+  constexpr int STEPU = V4U ? 4 : 1;
+  static_assert(!V4 || (kLoadIt % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
   float pw[kLoadIt], pu[kUIt], pr[kLoadIt];
   // CHD: G of the staged elements, G_n of the thread's channels (the same in every item:
   // kThreads is a multiple of DK; V4: the four channels 4 (tid mod DK/4) + j)
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
     }
   };
   auto elem_tr = [&](int it, int &t, int &r) __attribute__((always_inline)) {
-    if constexpr (V4) {
+    if constexpr (V4U) {
       const int iv = tid + (it >> 2) * kThreads;
       t = iv / (kBV / 4);
       r = 4 * (iv % (kBV / 4)) + (it & 3);
@@ -538,11 +541,11 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
         pgn[0] = Gc[static_cast<long long>(n - 1) * Dk + min(tid % DK, Dk - 1)];
     }
 #pragma unroll
-    for (int it = 0; it < kUIt; it += STEP) {
+    for (int it = 0; it < kUIt; it += STEPU) {
       int t, r;
       elem_tr(it, t, r);
       t = min(t, n - 1);
-      if constexpr (V4)
+      if constexpr (V4U)
         ld4e(a.Uw, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 4), &pu[it]);
       else
         pu[it] = a.Uw[(row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 1)];
@@ -593,18 +596,18 @@ __global__ __launch_bounds__(kStThreads) void bwd_state_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int it = 0; it < kUIt; it += STEP) {
+    for (int it = 0; it < kUIt; it += STEPU) {
       int t, r;
       elem_tr(it, t, r);
-      float u4[STEP];
+      float u4[STEPU];
 #pragma unroll
-      for (int j = 0; j < STEP; ++j) u4[j] = (t < n && r + j < nv) ? pu[it + j] : 0.f;
-      st_row<STEP>(&Us[t][r], u4);
+      for (int j = 0; j < STEPU; ++j) u4[j] = (t < n && r + j < nv) ? pu[it + j] : 0.f;
+      st_row<STEPU>(&Us[t][r], u4);
     }
     if (tid < kCMax) chunk_gates(f, tok(0), n, tid, gs, eg, wd);
     __syncthreads();
     if (ci + 1 < a.NC) cload(ci + 1);   // in flight during this chunk's products
-    {   // D = U - W S^T, tile (tb, rb)
+    if (16 * rb < kBV) {   // D = U - W S^T, tile (tb, rb) (kBV = 16: waves 0..3 only)
       const float4v acc = dot_kc<DK>(&Ws[16 * tb + col][0], &Ss[16 * rb + col][0], kq);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -658,13 +661,13 @@ constexpr int kSwBV = 32;
 constexpr int kSwThreads = 512;
 
 
-template <typename IO, int DK, bool CHD, bool PC, bool BAND, bool V4>
+template <typename IO, int DK, bool CHD, bool PC, bool BAND, bool V4, int BVT>
 __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   // V4 (Dk and Dv multiples of 4, 16-byte aligned tensors): every staged array is read four
   // consecutive elements per load and written to LDS 16 bytes at a time; a quarter of the
   // load addresses stay live across the chunk, which keeps this kernel out of scratch
   constexpr int LD = DK + 4;
-  constexpr int kBV = kSwBV, kThreads = kSwThreads;
+  constexpr int kBV = BVT, kThreads = kSwThreads;   // value rows per workgroup: 32, or 16
   constexpr int kLoadIt = kCMax * DK / kThreads;
   constexpr int NCB = DK / 16;                   // channel blocks
   constexpr int NTS = (kBV / 16) * NCB;          // dS tiles
@@ -735,7 +738,10 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
   float xgv[CHD ? kLoadIt : 1], xgn[V4 ? 4 : 1] = {};
   const IO *rbase = (f.wkey == GDR_WKEY_EXPLICIT) ? wk : k;
   constexpr int STEP = V4 ? 4 : 1;   // elements per load
-  static_assert(!V4 || (kLoadIt % 4 == 0 && kCC % 4 == 0 && kOIt % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
+  // (dO in fours only when every thread has whole groups of four: kBV = 32)
+  constexpr bool V4O = V4 && kOIt % 4 == 0;
+  constexpr int STEPO = V4O ? 4 : 1;
+  static_assert(!V4 || (kLoadIt % 4 == 0 && kCC % 4 == 0 && DK % 4 == 0), "V4 loads take whole groups of four");
   // element `it` of this thread in a chunk's [C][DK] tile (V4: four consecutive channels per
   // group of four elements; the thread's channels are then 4 (tid mod DK/4) + j in every
   // group, as kThreads is a multiple of DK), in a [C][kBV] value tile, in a C x C matrix (flat)
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     }
   };
   auto elem_tr = [&](int it, int &t, int &r) __attribute__((always_inline)) {
-    if constexpr (V4) {
+    if constexpr (V4O) {
       const int iv = tid + (it >> 2) * kThreads;
       t = iv / (kBV / 4);
       r = 4 * (iv % (kBV / 4)) + (it & 3);
@@ -812,11 +818,11 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     const int c0 = ci * C, n = min(C, T - c0);
     const long long row0 = (static_cast<long long>(b) * T + c0) * H + h;
 #pragma unroll
-    for (int it = 0; it < kOIt; it += STEP) {
+    for (int it = 0; it < kOIt; it += STEPO) {
       int t, r;
       elem_tr(it, t, r);
       t = min(t, n - 1);
-      if constexpr (V4)
+      if constexpr (V4O)
         ld4e(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 4), &xo[it]);
       else
         xo[it] = ld_f(dout, (row0 + static_cast<long long>(t) * H) * Dv + v0 + min(r, nv - 1));
@@ -928,13 +934,13 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int it = 0; it < kOIt; it += STEP) {
+    for (int it = 0; it < kOIt; it += STEPO) {
       int t, r;
       elem_tr(it, t, r);
-      float o4[STEP];
+      float o4[STEPO];
 #pragma unroll
-      for (int j = 0; j < STEP; ++j) o4[j] = (t < n && r + j < nv) ? xo[it + j] : 0.f;
-      st_row<STEP>(&dOs[t][r], o4);
+      for (int j = 0; j < STEPO; ++j) o4[j] = (t < n && r + j < nv) ? xo[it + j] : 0.f;
+      st_row<STEPO>(&dOs[t][r], o4);
     }
     __syncthreads();
     // the next chunk's loads, in flight during this chunk's products: T and P here, the keys
@@ -943,8 +949,9 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     if (ci > 0) cload_tp(ci - 1);
     const int tr0 = 16 * tb + 4 * kq;   // the lane's result rows (tokens) of the dD / dX tile
     // dD = e^{g_n - g} (.) (R dS^T) + scale P^T dO, tile (tb, rb); P is zero above the
-    // diagonal and T, P, dO rows past n (inside the chunk) are zero
-    {
+    // diagonal and T, P, dO rows past n (inside the chunk) are zero (kBV = 16: waves 0..3)
+    const bool vtile = 16 * rb < kBV;
+    if (vtile) {
       // R dS^T (16-byte operand reads), then P^T dO
       float4v a1[1], a2 = {0.f, 0.f, 0.f, 0.f};
       a1[0] = dot_kc<DK>(&Ks[16 * tb + col][0], &dS[16 * rb + col][0], kq);
@@ -966,7 +973,7 @@ __global__ __launch_bounds__(kSwThreads) void bwd_sweep_kernel(BwdArgs a) {
     }
     // dX = T^T dD, tile (tb, rb); written out for the per-chunk pass, and folded with e^g
     // into the state-gradient update
-    {
+    if (vtile) {
       float4v x = {0.f, 0.f, 0.f, 0.f};
       for (int i0 = 16 * tb; i0 < n; i0 += 4)
         x = mfma4(Tm[i0 + kq][16 * tb + col], dDs[i0 + kq][16 * rb + col], x);
@@ -1902,6 +1909,22 @@ static bool vec4_ok(const BwdArgs &a) {
   return true;
 }
 
+// the sequential kernels at Dk = 128: four-element loads when vec4_ok, and 16-row value tiles
+// when 32-row ones would give at most 128 workgroups (half the CUs idle)
+template <typename F>
+void dispatch_v4_bv(const BwdArgs &a, F &&go) {
+  const long long tiles32 = static_cast<long long>(a.f.B) * a.f.H * ((a.f.Dv + 31) / 32);
+  const bool half = tiles32 <= 128;
+  const bool v4 = vec4_ok(a);
+  if (half) {
+    if (v4) go(std::true_type{}, std::integral_constant<int, 16>{});
+    else go(std::false_type{}, std::integral_constant<int, 16>{});
+  } else {
+    if (v4) go(std::true_type{}, std::integral_constant<int, 32>{});
+    else go(std::false_type{}, std::integral_constant<int, 32>{});
+  }
+}
+
 // launch_pc with a second flag, the band-limited T (never with the per-channel decay: the host
 // rejects that combination, and no such kernel is built)
 template <bool CHD, typename F>
@@ -1935,55 +1958,59 @@ hipError_t prep_state_io(const BwdArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);
+  const dim3 gs((a.f.Dv + kStBV - 1) / kStBV, a.f.H, a.f.B);   // (Dk <= 64)
   if (a.f.Dk <= 32) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, true, decltype(pc)::value, false, kStBV>), gs, dim3(kStThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 32, false, decltype(pc)::value, false, kStBV>), gs, dim3(kStThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, true, decltype(pc)::value, false, kStBV>), gs, dim3(kStThreads), 0, s, a); });
     else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
-  } else if (vec4_ok(a)) {
-    if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value, true>), gs, dim3(kStThreads), 0, s, a); });
-    else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value, true>), gs, dim3(kStThreads), 0, s, a); });
+      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 64, false, decltype(pc)::value, false, kStBV>), gs, dim3(kStThreads), 0, s, a); });
   } else {
-    if (chd)
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
-    else
-      launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value, false>), gs, dim3(kStThreads), 0, s, a); });
+    // Dk = 128: 16-row value tiles when 32-row ones would leave half the CUs without a
+    // workgroup (at most 128 of them)
+    auto go = [&](auto v4c, auto bvc) {
+      constexpr bool V = decltype(v4c)::value;
+      constexpr int BV = decltype(bvc)::value;
+      const dim3 g((a.f.Dv + BV - 1) / BV, a.f.H, a.f.B);
+      if (chd)
+        launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, true, decltype(pc)::value, V, BV>), g, dim3(kStThreads), 0, s, a); });
+      else
+        launch_pc(a, [&](auto pc) { hipLaunchKernelGGL((bwd_state_kernel<IO, 128, false, decltype(pc)::value, V, BV>), g, dim3(kStThreads), 0, s, a); });
+    };
+    dispatch_v4_bv(a, go);
   }
   return hipGetLastError();
 }
 
 template <typename IO>
 hipError_t sweep_io(const BwdArgs &a, hipStream_t s) {
-  const dim3 grid((a.f.Dv + kSwBV - 1) / kSwBV, a.f.H, a.f.B);
+  const dim3 grid((a.f.Dv + kSwBV - 1) / kSwBV, a.f.H, a.f.B);   // (Dk <= 64)
   const bool chd = a.f.decay == GDR_DECAY_CHANNEL;
   if (a.f.Dk <= 32) {
     if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, true, decltype(pc)::value, decltype(bd)::value, false, kSwBV>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 32, false, decltype(pc)::value, decltype(bd)::value, false, kSwBV>), grid, dim3(kSwThreads), 0, s, a); });
   } else if (a.f.Dk <= 64) {
     if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, true, decltype(pc)::value, decltype(bd)::value, false, kSwBV>), grid, dim3(kSwThreads), 0, s, a); });
     else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
-  } else if (vec4_ok(a)) {
-    if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value, true>), grid, dim3(kSwThreads), 0, s, a); });
-    else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value, true>), grid, dim3(kSwThreads), 0, s, a); });
+      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 64, false, decltype(pc)::value, decltype(bd)::value, false, kSwBV>), grid, dim3(kSwThreads), 0, s, a); });
   } else {
-    if (chd)
-      launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
-    else
-      launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value, false>), grid, dim3(kSwThreads), 0, s, a); });
+    auto go = [&](auto v4c, auto bvc) {
+      constexpr bool V = decltype(v4c)::value;
+      constexpr int BV = decltype(bvc)::value;
+      const dim3 g((a.f.Dv + BV - 1) / BV, a.f.H, a.f.B);
+      if (chd)
+        launch_var<true>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, true, decltype(pc)::value, decltype(bd)::value, V, BV>), g, dim3(kSwThreads), 0, s, a); });
+      else
+        launch_var<false>(a, [&](auto pc, auto bd) { hipLaunchKernelGGL((bwd_sweep_kernel<IO, 128, false, decltype(pc)::value, decltype(bd)::value, V, BV>), g, dim3(kSwThreads), 0, s, a); });
+    };
+    dispatch_v4_bv(a, go);
   }
   return hipGetLastError();
 }
