@@ -132,14 +132,15 @@ def test_bwd_bf16(variant):
     compare(run_bwd(s, x, cot, state_in=S0), oracle_grads(s, x, cot, state_in=S0))
 
 
-@pytest.mark.parametrize("variant", ["gdn", "kda"])
-def test_bwd_unaligned_inputs(variant):
+@pytest.mark.parametrize("variant,H", [("gdn", 2), ("kda", 2), ("gdn", 36)])
+def test_bwd_unaligned_inputs(variant, H):
     """Queries, keys and dO one element past a 16-byte boundary: the kernels fall back from
     their four-element loads to element loads, with the same gradients (bitwise: the same
-    values reach the same products)."""
+    values reach the same products).  H = 36 gives 288 value tiles of 32 rows (the sequential
+    kernels' 32-row variant; the smaller shapes run the 16-row one)."""
     import torch
     import chunked_gated_delta_gdr_amd as G
-    s = spec(variant, dtype="bf16", Dk=128, Dv=128, T=150)
+    s = spec(variant, dtype="bf16", Dk=128, Dv=128, T=150, H=H)
     announce(f"bwd {variant} bf16 unaligned q, k, dO {s}")
     x, cot, S0 = gs.make_inputs(s), gs.make_cotangents(s), state(s)
     io, f32 = torch.bfloat16, torch.float32
@@ -163,7 +164,8 @@ def test_bwd_unaligned_inputs(variant):
     ref = call(dev(x["q"], io), dev(x["k"], io), dev(cot["d_out"], io))
     for n in ref:
         assert np.array_equal(got[n], ref[n]), n
-    compare(got, oracle_grads(s, x, cot, state_in=S0))
+    streams = None if H <= 2 else [(0, 0), (1, H - 1)]
+    compare(got, oracle_grads(s, x, cot, state_in=S0, streams=streams), streams=streams)
 
 
 @pytest.mark.parametrize("T", [1, 37, 64, 65])
