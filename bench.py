@@ -554,6 +554,8 @@ def main():
     ap.add_argument("--residual", type=int, default=0,
                     help="residual-correction steps on the band-N start (needs --neumann N)")
     ap.add_argument("--impl", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="the forward without the workspace (T formed inside the sequential kernel)")
     ap.add_argument("--bwd", action="store_true", help="time gdr_chunk_bwd instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -619,6 +621,16 @@ def main():
     stream = torch.cuda.current_stream(dev)
     precond = s.wkey == "precond"
 
+    # the workspace of gdr_chunk_fwd_ws (T of every chunk formed first) where it applies
+    ws_bytes = 0 if args.no_workspace else G.gdr_chunk_fwd_workspace_size(G.make_desc(
+        B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
+        io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
+        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
+        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
+        wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=args.neumann,
+        residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+
     def step(i):
         j = i % 2
         a = sets[j]
@@ -626,7 +638,7 @@ def main():
                         write=a["write"], write_key=a["write_key"], precond=precond,
                         pc_h_out=hs[j] if precond else None, out=outs[j], state_out=states[j],
                         chunk=s.chunk, neumann_order=args.neumann, residual_steps=args.residual,
-                        impl=args.impl, stream=stream)
+                        impl=args.impl, workspace=ws, stream=stream)
 
     def kernel_of(neumann, residual):
         code = G.gdr_chunk_fwd_impl(G.make_desc(

@@ -18,5 +18,6 @@ from ._binding import (  # noqa: F401
     lib, lib_path, make_desc,
     gdr_chunk_fwd, gdr_recurrent_step, gdr_validate, gdr_chunk_fwd_impl,
     gdr_chunk_bwd, gdr_chunk_bwd_workspace_size, gdr_validate_bwd, gdr_chunk_bwd_noalloc_max_workspace,
+    gdr_chunk_fwd_workspace_size,
     gdr_status_str, gdr_last_error, gdr_abi_version,
 )

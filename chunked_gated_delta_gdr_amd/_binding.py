@@ -98,13 +98,18 @@ def lib() -> ctypes.CDLL:
         L.gdr_validate_bwd.restype = ctypes.c_int
         L.gdr_chunk_fwd_impl.argtypes = [P(gdr_desc_t)]
         L.gdr_chunk_fwd_impl.restype = ctypes.c_int
+        L.gdr_chunk_fwd_ws.argtypes = [P(gdr_desc_t), P(gdr_inputs_t), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        L.gdr_chunk_fwd_ws.restype = ctypes.c_int
+        L.gdr_chunk_fwd_workspace_size.argtypes = [P(gdr_desc_t)]
+        L.gdr_chunk_fwd_workspace_size.restype = ctypes.c_uint64
         L.gdr_status_str.argtypes = [ctypes.c_int]
         L.gdr_status_str.restype = ctypes.c_char_p
         L.gdr_last_error.argtypes = []
         L.gdr_last_error.restype = ctypes.c_char_p
         L.gdr_abi_version.argtypes = []
         L.gdr_abi_version.restype = ctypes.c_int
-        if L.gdr_abi_version() != 4:
+        if L.gdr_abi_version() != 5:
             raise ImportError("libgdr ABI version mismatch")
         _LIB = L
     return _LIB
@@ -210,7 +215,7 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
                   pc_eps: float = 1e-3, pc_h0: float = 1.0, pc_t0: int = 0,
                   state_in=None, out=None, state_out=None, return_state: bool = True,
                   chunk: int = 64, neumann_order: int = -1, residual_steps: int = 0,
-                  scale: float = 1.0, impl: str = "auto",
+                  scale: float = 1.0, impl: str = "auto", workspace=None,
                   stream=None) -> Tuple[object, object, object]:
     """Chunked forward on torch tensors (q, k, v [B, T, H, D]).  Returns (out, state_out, pc_h_out).
 
@@ -221,6 +226,8 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
     fp32 or None for ``pc_h0``).  T: exact (``neumann_order`` < 0), the band N
     (``neumann_order`` = N), or that band corrected by ``residual_steps`` residual steps.
     Outputs are allocated when not given; ``state_out`` is allocated only if ``return_state``.
+    ``workspace``: a uint8 device tensor of at least ``gdr_chunk_fwd_workspace_size(desc)``
+    bytes (gdr_chunk_fwd_ws: T of every chunk formed first, where that applies), or None.
     """
     torch = _torch()
     B, T, H, Dk = q.shape
@@ -262,10 +269,22 @@ def gdr_chunk_fwd(q, k, v, *, beta=None, log_alpha=None, erase=None, write=None,
     ins = gdr_inputs_t(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(erase), _ptr(write),
                        _ptr(write_key), _ptr(pc_h_in) if precond else None,
                        _ptr(pc_h_out) if precond else None)
-    st = lib().gdr_chunk_fwd(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(out),
-                             _ptr(state_out), _stream(stream, dev))
+    if workspace is None:
+        st = lib().gdr_chunk_fwd(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(out),
+                                 _ptr(state_out), _stream(stream, dev))
+    else:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        st = lib().gdr_chunk_fwd_ws(ctypes.byref(desc), ctypes.byref(ins), _ptr(state_in), _ptr(out),
+                                    _ptr(state_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream, dev))
     _raise(st)
     return out, state_out, (pc_h_out if precond else None)
+
+
+def gdr_chunk_fwd_workspace_size(desc) -> int:
+    """Bytes of gdr_chunk_fwd_ws's workspace for a descriptor (0 where it does not apply)."""
+    return int(lib().gdr_chunk_fwd_workspace_size(ctypes.byref(desc)))
 
 
 def gdr_recurrent_step(q, k, v, state, *, beta=None, log_alpha=None, erase=None, write=None,

@@ -283,7 +283,7 @@ __device__ __forceinline__ int role_wave(int tid) {
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
 // the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
 // own role's state across iterations, and both run the kernel's barrier sequence.
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG, bool TP>
 __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -561,6 +561,30 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
     hc1 = a.pc_h_in != nullptr ? a.pc_h_in[static_cast<long long>(bh) * kD + 2 * pc_p + 1] : a.h0;
   }
 
+  // (TP) T formed beforehand: the two T_ba waves copy chunk c + 1's pair from the buffer
+  // (loaded in the update phase) into T's LDS buffers at the start of the next phase, where
+  // they would finish T.  The buffer holds the ten blocks on and below the diagonal (the
+  // others stay zero in LDS), block q = ib (ib + 1) / 2 + jb, each as hi then lo, each part
+  // 16 rows of 16; item u = 128 m + thread of 16 bytes: block u / 64, part (u / 32) % 2, row
+  // (u / 2) % 16, columns 8 (u % 2) .. + 7 of the block.
+  constexpr int kTI = TP ? 5 : 1;   // 640 items over the two waves
+  uint4 tpv[kTI];
+  auto tp_load = [&](int c) __attribute__((always_inline)) {
+    const uint16_t *src = a.tpre + (static_cast<long long>(bh) * nchunks + c) * (10 * 2 * 256);
+#pragma unroll
+    for (int m = 0; m < kTI; ++m) tpv[m] = *reinterpret_cast<const uint4 *>(src + 8 * (128 * m + ht));
+  };
+  auto tp_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < kTI; ++m) {
+      const int u = 128 * m + ht, q = u >> 6;
+      const int ib = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3, jb = q - ib * (ib + 1) / 2;
+      const int row = 16 * ib + ((u >> 1) & 15), col = 16 * jb + 8 * (u & 1);
+      uint16_t *dst = ((u >> 5) & 1) ? &sm.tl[buf][row][col] : &sm.t[buf][row][col];   // 8-byte aligned rows
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(tpv[m].x, tpv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 4) = make_uint2(tpv[m].z, tpv[m].w);
+    }
+  };
   if (STG && nchunks > 0) load_items(0);
   for (int c = -1; c < nchunks; ++c) {
     const int cur = c & 1, nxt = (c + 1) & 1;
@@ -606,7 +630,9 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
         get(o_d, bcol(1, 1));
       }
     };
-    if (!STG && c >= 0) {
+    if constexpr (TP) {
+      if (!STG && c >= 0) tp_stage(cur);
+    } else if (!STG && c >= 0) {
       load_ops(std::false_type{});
       load_ops(std::true_type{});
     }
@@ -615,7 +641,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       if (c + 2 < nchunks) load_items(c + 2);
     }
     if (c >= 0) {
-      if constexpr (!STG) {
+      if constexpr (!STG && !TP) {
         // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
         // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a, every product on bf16 pairs
         const Pair t32 = split4(mm2(o_a33, split4(mm2(o_a32, o_b22))));
@@ -942,7 +968,10 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       // The four diagonal inverses (dependent chains of matrix-core products) run on helpers
       // 2..5, one per SIMD (wave w runs on the SIMD of wave w + 4), the A blocks on the others
       constexpr int NAW = NHW - 4;               // waves on the A blocks
-      if (hw >= 2 && hw < 6) {
+      if constexpr (TP) {
+        // (TP) nothing of T to form: the T_ba waves load chunk c + 1's T
+        if (!STG) tp_load(c + 1);
+      } else if (hw >= 2 && hw < 6) {
         if constexpr (STG) {
           // diagonal block hw - 2 of T: D = (I - A_pp)^-1.  Its chain of dependent products
           // is the longest work of this phase; two of these waves share their SIMDs with the
@@ -966,7 +995,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   }
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool TP>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -1269,17 +1298,206 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     return;
   }
 
-  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true>(sm, a);
-  else helper_loop<BV, CHAN, DECAY, WK, RES, false>(sm, a);
+  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true, TP>(sm, a);
+  else helper_loop<BV, CHAN, DECAY, WK, RES, false, TP>(sm, a);
+}
+
+// ---------------------------------------------------------------------------------------
+// T = (I - A)^-1 of every chunk at once, for the variants with write key k and the exact
+// inverse (gdr_chunk_fwd_ws): one workgroup of four waves per (batch, head, chunk),
+// independent of every other chunk, so the whole grid runs in parallel and the sequential
+// kernel above only copies T.  The diagonal 16 x 16 blocks by the fused kernel's blocked
+// substitution (diag_inverse_t), one per wave; then block forward substitution
+// T_ij = D_i sum_{k = j..i-1} A_ik T_kj (MatMul-only inversion summary, "Declaracao do
+// Problema": T solves (I - A) T = I) by levels of the block distance i - j (three, two, then
+// one block on their own waves), every product on bf16 pairs; the waves exchange blocks through
+// LDS in their operand layouts.  Output: the ten blocks on and below the diagonal of T, block
+// q = ib (ib + 1) / 2 + jb, each as its hi then lo part of 16 x 16 bf16 row-major:
+// [B, H, chunks][10][2][16][16].
+// ---------------------------------------------------------------------------------------
+constexpr int kTW = 4;   // waves per workgroup of the T kernel
+
+template <bool CHAN, bool DECAY>
+__global__ __launch_bounds__(64 * kTW) void chunk_t_kernel(ChunkArgs a, uint16_t *tw) {
+  // keys (the write keys), swizzled, then (CHAN) the erase keys b (.) k
+  __shared__ __align__(16) uint16_t kbuf[(CHAN ? 2 : 1) * kC * kD];
+  __shared__ float g2[kC], bet[kC];
+  uint16_t *const ks = kbuf, *const es = kbuf + (CHAN ? kC * kD : 0);
+  // Once every product of keys has been formed, the keys' space holds the exchanged 16 x 16
+  // blocks, as bf16 pairs in a lane's operand layout (16 bytes per lane): 0..3 acc(D_p^T)
+  // (A operands of D_p), 4..7 acc(D_p) (B operands), 8..13 acc(A_ik^T) for (i, k) = (1,0)
+  // (2,0) (2,1) (3,0) (3,1) (3,2), 14, 15 acc(T_10), acc(T_21).  (LDS of 16.5 KB per
+  // workgroup without channel gains: nine workgroups per CU.)
+  static_assert(16 * 64 * sizeof(uint4) == kC * kD * sizeof(uint16_t), "exchange space");
+  uint4 (*const xb)[64] = reinterpret_cast<uint4 (*)[64]>(kbuf);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, l4 = lane >> 4;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int H = a.H, T = a.T;
+  const int nchunks = (T + kC - 1) / kC;
+  const int c0 = c * kC, n = min(kC, T - c0);
+  const long long tokstride = static_cast<long long>(H) * kD;
+  const long long cb = (static_cast<long long>(b) * T * H + h) * kD + static_cast<long long>(c0) * tokstride;
+  const uint16_t *gk = static_cast<const uint16_t *>(a.k) + cb;
+  const uint16_t *ger = static_cast<const uint16_t *>(a.erase) + (CHAN ? cb : 0);
+  // 1024 items of 16 bytes (item u: row u / 16, columns 8 (u % 16) ..), rows past the end of
+  // the sequence read clamped and zeroed
+  constexpr int NI = 1024 / (64 * kTW);
+  uint4 kv[NI], bv[CHAN ? NI : 1];
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int u = 64 * kTW * m + tid, row = min(u >> 4, n - 1);
+    kv[m] = *reinterpret_cast<const uint4 *>(gk + row * tokstride + 8 * (u & 15));
+    if (CHAN) bv[m] = *reinterpret_cast<const uint4 *>(ger + row * tokstride + 8 * (u & 15));
+  }
+  if (wv == 0) {   // gates of the chunk's tokens (lane t), as the fused kernel's gate wave forms them
+    const long long gi = static_cast<long long>(b) * T * H + h + static_cast<long long>(c0 + min(lane, n - 1)) * H;
+    const bool ok = lane < n;
+    const float la = DECAY ? a.log_alpha[gi] : 0.f;
+    const float bt = CHAN ? 0.f : a.beta[gi];
+    g2[lane] = wave_scan_add(ok ? la * kLog2e : 0.f);
+    bet[lane] = ok ? bt : 0.f;
+  }
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int u = 64 * kTW * m + tid, row = u >> 4, col = 8 * (u & 15);
+    uint4 x = kv[m];
+    if (row >= n) x = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4 *>(ks + sw128(row, col)) = x;
+    if (CHAN) {
+      const uint4 w = bv[m];
+      *reinterpret_cast<uint4 *>(es + sw128(row, col)) =
+          make_uint4(f32x2_to_bf16x2_bits(elem(w, 0) * elem(x, 0), elem(w, 1) * elem(x, 1)),
+                     f32x2_to_bf16x2_bits(elem(w, 2) * elem(x, 2), elem(w, 3) * elem(x, 3)),
+                     f32x2_to_bf16x2_bits(elem(w, 4) * elem(x, 4), elem(w, 5) * elem(x, 5)),
+                     f32x2_to_bf16x2_bits(elem(w, 6) * elem(x, 6), elem(w, 7) * elem(x, 7)));
+    }
+  }
+  __syncthreads();
+  const uint16_t *E = CHAN ? es : ks;
+  const uint16_t *R = ks;
+  constexpr bool SCALED_E = !CHAN;   // E = beta k: beta applied after the product
+  // the scaled entry of A = -L at (i, j), j < i, from the raw product x = (E R^T)_ij
+  auto a_of = [&](float x, int i, int j) __attribute__((always_inline)) {
+    if (SCALED_E) x *= bet[i];
+    if (DECAY) x *= decay2(g2[i] - g2[j]);
+    return -x;
+  };
+  const short4v I16 = ident4(lane);
+  auto trp = [&](const Pair &x) __attribute__((always_inline)) {   // acc(X^T) of acc(X), exactly
+    return Pair{tobf4(mfma16(x.h, I16, zero4())), tobf4(mfma16(x.l, I16, zero4()))};
+  };
+  auto put = [&](int slot, const Pair &x) __attribute__((always_inline)) {
+    xb[slot][lane] = make_uint4(__builtin_bit_cast(uint32_t, short2{x.h[0], x.h[1]}),
+                                __builtin_bit_cast(uint32_t, short2{x.h[2], x.h[3]}),
+                                __builtin_bit_cast(uint32_t, short2{x.l[0], x.l[1]}),
+                                __builtin_bit_cast(uint32_t, short2{x.l[2], x.l[3]}));
+  };
+  auto get = [&](int slot) __attribute__((always_inline)) {
+    const uint4 v = xb[slot][lane];
+    const short2 h0 = __builtin_bit_cast(short2, v.x), h1 = __builtin_bit_cast(short2, v.y);
+    const short2 l0 = __builtin_bit_cast(short2, v.z), l1 = __builtin_bit_cast(short2, v.w);
+    return Pair{short4v{h0.x, h0.y, h1.x, h1.y}, short4v{l0.x, l0.y, l1.x, l1.y}};
+  };
+  // block (i, j), j <= i: lane (row l16, columns 4 l4 .. + 3) of the pair x = acc(T_ij^T),
+  // the 64 lanes' 8 bytes of a part contiguous
+  uint16_t *dst = tw + (static_cast<long long>(b * H + h) * nchunks + c) * (10 * 2 * 256);
+  auto out = [&](int i, int j, const Pair &x) __attribute__((always_inline)) {
+    uint16_t *blk = dst + (i * (i + 1) / 2 + j) * 512 + l16 * 16 + 4 * l4;
+    *reinterpret_cast<short4v *>(blk) = x.h;
+    *reinterpret_cast<short4v *>(blk + 256) = x.l;
+  };
+  // A operand of the block (i, k) below the diagonal: acc(A_ik^T) = acc(R_k E_i^T), scaled
+  auto aop = [&](int i, int k) __attribute__((always_inline)) {
+    float4v x = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x = mfma32(opn128(R, k * 16 + l16, 32 * s, l4), opn128(E, i * 16 + l16, 32 * s, l4), x);
+    float4v y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = a_of(x[r], i * 16 + l16, k * 16 + 4 * l4 + r);
+    return split4(y);
+  };
+  const short4v zs = {0, 0, 0, 0};
+  {   // wave p: the diagonal block p and its share of the blocks of A below the diagonal
+    const int p = wv;
+    const int row = p * 16 + l16;
+    float4v g = zero4(), gt = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const short8v e = opn128(E, row, 32 * s, l4);
+      if constexpr (!CHAN) {
+        g = mfma32(e, e, g);
+      } else {
+        const short8v r = opn128(R, row, 32 * s, l4);
+        g = mfma32(e, r, g);
+        gt = mfma32(r, e, gt);
+      }
+    }
+    if constexpr (!CHAN) gt = g;
+    // blocks of A: wave 0 (1,0) (2,0); wave 1 (2,1) (3,0); wave 2 (3,1); wave 3 (3,2)
+    const int n_a = p < 2 ? 2 : 1;
+    Pair ap[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int slot = p < 2 ? 2 * p + q : 2 + p;   // 0 1 | 2 3 | 4 | 5
+      const int ai = slot < 1 ? 1 : slot < 3 ? 2 : 3;
+      const int ak = slot - (ai * (ai - 1)) / 2;
+      if (q < n_a) ap[q] = aop(ai, ak);
+    }
+    __syncthreads();   // every read of the keys done: the exchange space may be written
+    float4v nn, nt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i0 = p * 16 + 4 * l4 + r, j0 = p * 16 + l16;
+      nn[r] = j0 < i0 ? a_of(g[r], i0, j0) : 0.f;
+      const int i1 = p * 16 + l16, j1 = p * 16 + 4 * l4 + r;
+      nt[r] = j1 < i1 ? a_of(gt[r], i1, j1) : 0.f;
+    }
+    Pair dt = split4(diag_inverse_t(nn, nt, lane));   // acc(D_p^T): rows of D_p
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * l4 + r > l16) dt.h[r] = dt.l[r] = 0;   // (lower triangle kept)
+    put(p, dt);
+    put(4 + p, trp(dt));
+    out(p, p, dt);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < n_a) put(8 + (p < 2 ? 2 * p + q : 2 + p), ap[q]);
+  }
+  __syncthreads();
+  // level 1: T_10, T_21, T_32 = D_i A_i,i-1 D_i-1 (waves 0, 1, 2)
+  if (wv < 3) {
+    const int i = wv + 1, j = wv;
+    const int aslot = 8 + (i == 1 ? 0 : i == 2 ? 2 : 5);
+    const Pair t = split4(mm2(get(i), split4(mm2(get(aslot), get(4 + j)))));
+    if (i < 3) put(14 + wv, t);   // T_10, T_21 (T_32 is not read again)
+    out(i, j, trp(t));
+  }
+  __syncthreads();
+  // level 2: T_20 = D_2 (A_20 D_0 + A_21 T_10) (wave 0), T_31 = D_3 (A_31 D_1 + A_32 T_21) (wave 1)
+  Pair t20{zs, zs};
+  if (wv == 0) {
+    t20 = split4(mm2(get(2), split4(mm2(get(9), get(4), mm2(get(10), get(14))))));
+    out(2, 0, trp(t20));
+  } else if (wv == 1) {
+    const Pair t31 = split4(mm2(get(3), split4(mm2(get(12), get(5), mm2(get(13), get(15))))));
+    out(3, 1, trp(t31));
+  }
+  // level 3: T_30 = D_3 (A_30 D_0 + A_31 T_10 + A_32 T_20) (wave 0, which holds T_20)
+  if (wv == 0) {
+    const float4v s = mm2(get(11), get(4), mm2(get(12), get(14), mm2(get(13), t20)));
+    out(3, 0, trp(split4(mm2(get(3), split4(s)))));
+  }
 }
 
 template <int BV, bool CHAN, bool DECAY, int WK>
 hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV);   // <= 2^22
   if (a.S > 0)
-    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true>), dim3(grid), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true, false>), dim3(grid), dim3(kNT), 0, s, a);
+  else if (WK == kWkSame && BV == 32 && a.tpre != nullptr)
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false, WK == kWkSame && BV == 32>), dim3(grid), dim3(kNT), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false>), dim3(grid), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false, false>), dim3(grid), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1325,7 +1543,34 @@ static int chunk_mfma_bv(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
+  if (a.tpre != nullptr) {   // T of every chunk first (the host passes tpre only where it applies)
+    const int nchunks = (a.T + kC - 1) / kC;
+    if (nchunks > 0) {
+      const dim3 g(nchunks, a.H, a.B);
+      uint16_t *tw = const_cast<uint16_t *>(a.tpre);
+      const bool decay = a.decay == GDR_DECAY_SCALAR;
+      if (a.gain == GDR_GAIN_CHANNEL) {
+        if (decay) hipLaunchKernelGGL((chunk_t_kernel<true, true>), g, dim3(64 * kTW), 0, s, a, tw);
+        else hipLaunchKernelGGL((chunk_t_kernel<true, false>), g, dim3(64 * kTW), 0, s, a, tw);
+      } else {
+        if (decay) hipLaunchKernelGGL((chunk_t_kernel<false, true>), g, dim3(64 * kTW), 0, s, a, tw);
+        else hipLaunchKernelGGL((chunk_t_kernel<false, false>), g, dim3(64 * kTW), 0, s, a, tw);
+      }
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return launch_bv<32>(a, s);
+  }
   return chunk_mfma_bv(a) == 32 ? launch_bv<32>(a, s) : launch_bv<16>(a, s);
+}
+
+// bytes of the precomputed T for gdr_chunk_fwd_ws: its ten lower 16 x 16 blocks as bf16 pairs,
+// 10 KB per (batch, head, chunk), where it applies (matrix-core kernel, write key k, exact T,
+// no residual steps), else 0
+unsigned long long chunk_mfma_tpre_bytes(const gdr_desc_t &d) {
+  if (d.wkey != GDR_WKEY_SAME || d.neumann_order >= 0 || d.decay == GDR_DECAY_CHANNEL) return 0;
+  const unsigned long long nchunks = (static_cast<unsigned long long>(d.T) + kC - 1) / kC;
+  return static_cast<unsigned long long>(d.B) * d.H * nchunks * (10ull * 2 * 256 * 2);
 }
 
 }  // namespace gdr

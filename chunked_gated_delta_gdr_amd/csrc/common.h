@@ -24,6 +24,9 @@ struct ChunkArgs {
   int S;                      // residual-correction steps on the band start (0: none)
   float scale, rho, log_rho, eps, h0;
   long long t0;
+  // the chunks' T (exact, write key k) formed beforehand, as bf16 pairs row-major,
+  // [B, H, chunks][hi, lo][64][64] (gdr_chunk_fwd_ws); null: the matrix-core kernel forms it
+  const uint16_t *tpre;
 };
 
 // Backward pass (gdr_chunk_bwd): the forward's arguments plus the incoming gradients, the
@@ -51,6 +54,7 @@ struct BwdArgs {
 // Host launchers (return hipSuccess or the launch error).
 hipError_t launch_chunk_generic(const ChunkArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
+unsigned long long chunk_mfma_tpre_bytes(const gdr_desc_t &d);
 bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in,
                          const void *out, const float *state_out);
 hipError_t launch_step(const ChunkArgs &a, int io_dtype, hipStream_t s);

@@ -308,8 +308,9 @@ static gdr::ChunkArgs make_args(const gdr_desc_t *d, const gdr_inputs_t *in, con
   return a;
 }
 
-gdr_status_t gdr_chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
-                           void *out, float *state_out, void *stream) {
+// the chunk forward with an optional workspace for the precomputed T (null: none)
+static gdr_status_t chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
+                              void *out, float *state_out, void *ws, uint64_t ws_bytes, void *stream) {
   gdr_status_t st = gdr_validate(dd, in, state_in, out, state_out, 0);
   if (st != GDR_OK) return st;
   const gdr_desc_t dl = lower_chunk(*dd);
@@ -320,15 +321,58 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const f
                              "(needs bf16, Dk = Dv = 128, chunk 64 or exact chunk 128, 16-byte aligned tensors, "
                              "no per-channel decay, channel gains only with write key k)");
   const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
-  const gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
+  gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
+  if (ws != nullptr && use_mfma) {
+    const uint64_t need = gdr::chunk_mfma_tpre_bytes(*d);
+    if (need > 0) {
+      if (ws_bytes < need)
+        return fail(GDR_EINVAL, "workspace of %llu bytes, this descriptor needs %llu",
+                    static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(need));
+      if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(GDR_EINVAL, "workspace must be 256-byte aligned");
+      const long double ntok = static_cast<long double>(d->B) * d->T * d->H;
+      const long double sbytes = static_cast<long double>(d->B) * d->H * d->Dv * d->Dk * 4;
+      const Range r_ws = rng("workspace", ws, static_cast<long double>(need));
+      const Range others[] = {
+          rng("q", in->q, ntok * d->Dk * 2), rng("k", in->k, ntok * d->Dk * 2), rng("v", in->v, ntok * d->Dv * 2),
+          rng("beta", in->beta, ntok * 4), rng("log_alpha", in->log_alpha, ntok * 4),
+          rng("erase", in->erase, ntok * d->Dk * 2), rng("write", in->write, ntok * d->Dv * 2),
+          rng("out", out, ntok * d->Dv * 2), rng("state_in", state_in, sbytes), rng("state_out", state_out, sbytes)};
+      for (const Range &r : others)
+        if (overlap(r_ws, r)) return fail(GDR_EINVAL, "workspace overlaps %s", r.name);
+      a.tpre = static_cast<const uint16_t *>(ws);
+    }
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled())
-    std::fprintf(stderr, "[gdr] chunk_fwd %s B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d N=%d S=%d\n",
-                 use_mfma ? "mfma" : "generic", d->B, d->T, d->H, d->Dk, d->Dv, d->chunk,
-                 d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay, d->wkey, a.N, a.S);
+    std::fprintf(stderr, "[gdr] chunk_fwd %s%s B=%d T=%d H=%d Dk=%d Dv=%d C=%d io=%s gain=%d decay=%d wkey=%d N=%d S=%d\n",
+                 use_mfma ? "mfma" : "generic", a.tpre != nullptr ? " (T formed beforehand)" : "", d->B, d->T,
+                 d->H, d->Dk, d->Dv, d->chunk, d->io_dtype == GDR_BF16 ? "bf16" : "f32", d->gain, d->decay,
+                 d->wkey, a.N, a.S);
   const hipError_t e = use_mfma ? gdr::launch_chunk_mfma(a, s) : gdr::launch_chunk_generic(a, d->io_dtype, s);
   if (e != hipSuccess) return fail(GDR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+gdr_status_t gdr_chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
+                           void *out, float *state_out, void *stream) {
+  return chunk_fwd(dd, in, state_in, out, state_out, nullptr, 0, stream);
+}
+
+uint64_t gdr_chunk_fwd_workspace_size(const gdr_desc_t *dd) {
+  if (dd == nullptr || dd->struct_size != sizeof(gdr_desc_t) || dd->B < 1 || dd->H < 1 || dd->T < 0 ||
+      (dd->chunk != 16 && dd->chunk != 32 && dd->chunk != 64 && dd->chunk != 128))
+    return 0;
+  if (dd->impl == GDR_IMPL_GENERIC) return 0;
+  const gdr_desc_t dl = lower_chunk(*dd);
+  gdr_inputs_t none{};
+  if (!gdr::chunk_mfma_supports(dl, none, nullptr, nullptr, nullptr)) return 0;
+  return gdr::chunk_mfma_tpre_bytes(dl);
+}
+
+gdr_status_t gdr_chunk_fwd_ws(const gdr_desc_t *dd, const gdr_inputs_t *in, const float *state_in,
+                              void *out, float *state_out, void *workspace, uint64_t workspace_bytes,
+                              void *stream) {
+  return chunk_fwd(dd, in, state_in, out, state_out, workspace, workspace_bytes, stream);
 }
 
 uint64_t gdr_chunk_bwd_workspace_size(const gdr_desc_t *dd) {

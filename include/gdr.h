@@ -36,8 +36,9 @@
  *  - Element types: q, k, v, erase, write, write_key and out use io_dtype (fp32 or bf16);
  *    beta, log_alpha, state and pc_h are always fp32.
  *  - Memory: every pointer is a device pointer owned by the caller.  The library never
- *    allocates, frees or keeps a pointer after the call returns.  Only gdr_chunk_bwd needs
- *    scratch memory, and the caller passes it in (gdr_chunk_bwd_workspace_size).
+ *    allocates, frees or keeps a pointer after the call returns.  Scratch memory, where an
+ *    entry point uses it, is passed in by the caller (gdr_chunk_bwd_workspace_size,
+ *    gdr_chunk_fwd_workspace_size).
  *  - Execution: the work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the null stream) and the call returns without synchronising.
  *  - Errors: arguments are validated on the host before anything is enqueued.  On
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 
 typedef enum {
   GDR_OK = 0,
@@ -154,6 +155,31 @@ typedef struct gdr_inputs {
 gdr_status_t gdr_chunk_fwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
                            const float *state_in, void *out, float *state_out,
                            void *stream);
+
+/*
+ * gdr_chunk_fwd_ws -- gdr_chunk_fwd with caller-owned scratch memory in which T of every
+ * chunk is formed first, all chunks at once, before the sequential pass reads it (same
+ * results as gdr_chunk_fwd to rounding: the same stable inverse, its blocks in a different
+ * order).  T = (I - A)^-1 of each chunk depends only on the chunk's own keys and gates
+ * (MatMul-only inversion summary, "Declaracao do Problema"), so forming it apart from the
+ * state pass is exact.  It applies where the matrix-core kernel runs with write key k and
+ * the exact T (no band limit, no residual steps); elsewhere the workspace is not used.
+ *
+ *   workspace        device memory of at least gdr_chunk_fwd_workspace_size(desc) bytes,
+ *                    256-byte aligned, overlapping no other argument; its contents on entry
+ *                    do not matter and are overwritten.  NULL: exactly gdr_chunk_fwd.
+ *   workspace_bytes  its size; less than needed returns GDR_EINVAL.
+ * Other arguments and errors as gdr_chunk_fwd.
+ */
+gdr_status_t gdr_chunk_fwd_ws(const gdr_desc_t *desc, const gdr_inputs_t *in,
+                              const float *state_in, void *out, float *state_out,
+                              void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Bytes of gdr_chunk_fwd_ws's workspace: 10 KB per (batch, head, chunk of 64 tokens) where it
+ * applies (T's ten 16 x 16 blocks on and below the diagonal, each as a pair of bf16 parts), 0
+ * where it does not (any workspace is then ignored) or for an invalid descriptor.  Pure host
+ * arithmetic. */
+uint64_t gdr_chunk_fwd_workspace_size(const gdr_desc_t *desc);
 
 /*
  * gdr_recurrent_step -- one token for every stream, updating the state in place:

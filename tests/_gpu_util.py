@@ -30,12 +30,18 @@ def precond_opts(s):
 
 
 def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, residual_steps=0,
-              impl="auto", scale=1.0, chunk=None, sync=True):
-    """gdr_chunk_fwd on inputs ``x`` (numpy, from gdr_synth).  Returns torch tensors."""
+              impl="auto", scale=1.0, chunk=None, sync=True, workspace=False):
+    """gdr_chunk_fwd on inputs ``x`` (numpy, from gdr_synth).  Returns torch tensors.
+    ``workspace``: call gdr_chunk_fwd_ws with a workspace of 16 KB per (batch, head, chunk of
+    64 tokens), filled with garbage first (its contents on entry must not matter)."""
     import torch
     import chunked_gated_delta_gdr_amd as G
     io = torch_dtype(s.dtype)
     f32 = torch.float32
+    ws = None
+    if workspace:
+        nch = (s.T + 63) // 64
+        ws = torch.full((max(1, s.B * s.H * nch * 16384),), 0x7f, dtype=torch.uint8, device="cuda")
     out = G.gdr_chunk_fwd(
         dev(x["q"], io), dev(x["k"], io), dev(x["v"], io),
         beta=dev(x.get("beta"), f32), log_alpha=dev(x.get("log_alpha"), f32),
@@ -45,7 +51,7 @@ def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, r
         pc_h0=s.pc_h0, pc_t0=pc_t0,
         state_in=dev(state_in, f32), chunk=chunk or s.chunk, neumann_order=neumann_order,
         residual_steps=residual_steps,
-        scale=scale, impl=impl)
+        scale=scale, impl=impl, workspace=ws)
     if sync:
         torch.cuda.synchronize()
     return out

@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert G.gdr_abi_version() == 4
+    assert G.gdr_abi_version() == 5
     for s in (G.GDR_OK, G.GDR_EINVAL, G.GDR_ENOTSUP, G.GDR_EHIP):
         assert G.gdr_status_str(s).startswith("GDR_")
     assert "UNKNOWN" in G.gdr_status_str(42)
@@ -425,3 +425,29 @@ def test_noalloc_backward_rejects_before_any_hip_call():
     assert st == G.GDR_ENOTSUP
     assert "no-allocation" in G.gdr_last_error()
     assert L.gdr_chunk_bwd_noalloc(None, ctypes.byref(ins), None, a["d_out"], None, ctypes.byref(gr), None) == G.GDR_EINVAL
+
+
+def test_forward_workspace_size_and_checks():
+    """gdr_chunk_fwd_ws: the workspace is 10 KB per (batch, head, chunk of 64 tokens) where T can
+    be formed beforehand (matrix-core kernel, write key k, exact T), 0 elsewhere; a workspace
+    that is too small, misaligned or overlapping an argument is rejected before anything runs."""
+    d = desc(Dk=128, Dv=128)
+    need = G.gdr_chunk_fwd_workspace_size(d)
+    assert need == 2 * 3 * 2 * 10240   # ten 16 x 16 blocks of T as bf16 pairs
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, chunk=128)) == need
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, wkey=G.GDR_WKEY_DIAG_PRECOND)) == 0
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, neumann_order=3)) == 0
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, impl=G.GDR_IMPL_GENERIC)) == 0
+    assert G.gdr_chunk_fwd_workspace_size(desc()) == 0   # Dk = 64: the fp32 kernel
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, io_dtype=G.GDR_F32)) == 0
+    L = G.lib()
+    ins = inputs()
+    ws = BASE + 40 * MB
+
+    def call(wptr, nbytes):
+        return L.gdr_chunk_fwd_ws(ctypes.byref(d), ctypes.byref(ins), None, OUT, SOUT, wptr, nbytes, None)
+
+    assert call(ws, need - 1) == G.GDR_EINVAL and "workspace" in G.gdr_last_error()
+    assert call(ws + 16, need) == G.GDR_EINVAL and "aligned" in G.gdr_last_error()
+    assert call(OUT, need) == G.GDR_EINVAL and "overlaps" in G.gdr_last_error()
+    assert call(BASE + 1 * MB, need) == G.GDR_EINVAL and "overlaps" in G.gdr_last_error()
