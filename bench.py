@@ -38,7 +38,7 @@ ENGINE_CLOCK_HZ = 2.4e9         # MI355X peak engine clock (256 CUs x 4 SIMDs)
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 KERNEL_SOURCES = {
-    "mfma": ["chunked_gated_delta_gdr_amd/csrc/chunk_mfma.hip"],
+    "mfma": ["chunked_gated_delta_gdr_amd/csrc/chunk_mfma.hip", "chunked_gated_delta_gdr_amd/csrc/kda_prep.hip"],
     "generic": ["chunked_gated_delta_gdr_amd/csrc/chunk_generic.hip"],
     "step": ["chunked_gated_delta_gdr_amd/csrc/recurrent_step.hip"],
 }
@@ -651,6 +651,8 @@ def main():
         return {G.GDR_IMPL_MFMA: "mfma", G.GDR_IMPL_GENERIC: "generic"}.get(code, "?")
 
     impl_name = kernel_of(args.neumann, args.residual)
+    if s.decay == "channel" and ws is not None:   # the per-channel decay's matrix-core path needs the workspace
+        impl_name = "mfma"
     print(f"[bench] workload {args.workload} impl {impl_name} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
 

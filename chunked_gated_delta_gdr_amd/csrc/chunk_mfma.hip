@@ -93,6 +93,13 @@ struct __align__(16) Smem {
   float g2[2][kC], eg[2][kC], wd[2][kC], beta[2][kC], ic[2][kC];
 };
 
+// (per-channel decay on the prepared record) the chunk's state decay per key channel, double
+// buffered, in the space of A_ba, which that variant never forms
+template <int BV, bool CHAN, int WK>
+__device__ __forceinline__ float *gcv_of(Smem<BV, CHAN, WK> &sm, int buf) {
+  static_assert(sizeof(Smem<BV, CHAN, WK>::lba) >= 2 * kD * sizeof(float), "per-channel decay buffer");
+  return reinterpret_cast<float *>(&sm.lba[0][0]) + buf * kD;
+}
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 // 2^x by the hardware instruction alone: the arguments are decays between two tokens of a
 // chunk (x <= 0 wherever the result is kept); results below the normal range flush to zero
@@ -283,7 +290,7 @@ __device__ __forceinline__ int role_wave(int tid) {
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
 // the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
 // own role's state across iterations, and both run the kernel's barrier sequence.
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG, bool TP>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG, bool TP, bool KD>
 __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -298,7 +305,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   // gains), else read beside them (channel gates: R = k, E = b (.) k; a preconditioned or
   // explicit write key: R in its own array); with a single value wave, which would have to
   // keep every R block, the helper waves form it
-  constexpr bool kPv = NVW == 2;
+  constexpr bool kPv = NVW == 2 && !KD;
   constexpr bool kRq = kPv && (CHAN || WK != kWkSame);   // P's R operands read separately
 
   const int tid = threadIdx.x;
@@ -567,22 +574,40 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   // others stay zero in LDS), block q = ib (ib + 1) / 2 + jb, each as hi then lo, each part
   // 16 rows of 16; item u = 128 m + thread of 16 bytes: block u / 64, part (u / 32) % 2, row
   // (u / 2) % 16, columns 8 (u % 2) .. + 7 of the block.
-  constexpr int kTI = TP ? 5 : 1;   // 640 items over the two waves
+  // (KD) the per-channel decay's record adds P (items 640..959: block (u - 640) / 32, row
+  // ((u - 640) / 2) % 16, columns 8 (u % 2) .., single bf16) and the chunk's per-channel state
+  // decay (items 960..991, four fp32 channels each), copied the same way into P's buffer and
+  // the per-channel decay buffer (which lives in the unused A_ba space)
+  constexpr int kTItems = KD ? 992 : 640;
+  constexpr int kTI = TP ? (kTItems + 127) / 128 : 1;
   uint4 tpv[kTI];
   auto tp_load = [&](int c) __attribute__((always_inline)) {
-    const uint16_t *src = a.tpre + (static_cast<long long>(bh) * nchunks + c) * (10 * 2 * 256);
+    const uint16_t *src = a.tpre + (static_cast<long long>(bh) * nchunks + c) * (kTItems * 8);
 #pragma unroll
-    for (int m = 0; m < kTI; ++m) tpv[m] = *reinterpret_cast<const uint4 *>(src + 8 * (128 * m + ht));
+    for (int m = 0; m < kTI; ++m)
+      if (128 * m + 127 < kTItems || 128 * m + ht < kTItems)
+        tpv[m] = *reinterpret_cast<const uint4 *>(src + 8 * (128 * m + ht));
   };
   auto tp_stage = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < kTI; ++m) {
-      const int u = 128 * m + ht, q = u >> 6;
-      const int ib = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3, jb = q - ib * (ib + 1) / 2;
-      const int row = 16 * ib + ((u >> 1) & 15), col = 16 * jb + 8 * (u & 1);
-      uint16_t *dst = ((u >> 5) & 1) ? &sm.tl[buf][row][col] : &sm.t[buf][row][col];   // 8-byte aligned rows
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(tpv[m].x, tpv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 4) = make_uint2(tpv[m].z, tpv[m].w);
+      const int u = 128 * m + ht;
+      if (u < 640) {
+        const int q = u >> 6;
+        const int ib = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3, jb = q - ib * (ib + 1) / 2;
+        const int row = 16 * ib + ((u >> 1) & 15), col = 16 * jb + 8 * (u & 1);
+        uint16_t *dst = ((u >> 5) & 1) ? &sm.tl[buf][row][col] : &sm.t[buf][row][col];   // 8-byte aligned rows
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(tpv[m].x, tpv[m].y);
+        *reinterpret_cast<uint2 *>(dst + 4) = make_uint2(tpv[m].z, tpv[m].w);
+      } else if (KD && u < 960) {
+        const int v = u - 640, q = v >> 5;
+        const int ib = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3, jb = q - ib * (ib + 1) / 2;
+        uint16_t *dst = &sm.p[16 * ib + ((v >> 1) & 15)][16 * jb + 8 * (v & 1)];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(tpv[m].x, tpv[m].y);
+        *reinterpret_cast<uint2 *>(dst + 4) = make_uint2(tpv[m].z, tpv[m].w);
+      } else if (KD && u < kTItems) {
+        *reinterpret_cast<uint4 *>(&gcv_of(sm, buf)[4 * (u - 960)]) = tpv[m];
+      }
     }
   };
   if (STG && nchunks > 0) load_items(0);
@@ -670,9 +695,9 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
         tr2(tb3, th, tl);
         put_rows2(cur, 3, qb, th, tl, false);
       }
-      // P tiles (10 lower blocks) unless the value waves form them: jobs 8, 9 on the two T_ba
-      // waves, 0..7 on the others
-      if constexpr (!kPv) {
+      // P tiles (10 lower blocks) unless the value waves form them (or, KD, the record holds
+      // them): jobs 8, 9 on the two T_ba waves, 0..7 on the others
+      if constexpr (!kPv && !KD) {
         if constexpr (!STG) {
           p_tile(cur, 8 + hw);
         } else {
@@ -995,7 +1020,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   }
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool TP>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool TP, bool KD = false>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -1010,7 +1035,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // gains), else read beside them (channel gates: R = k, E = b (.) k; a preconditioned or
   // explicit write key: R in its own array); with a single value wave, which would have to
   // keep every R block, the helper waves form it
-  constexpr bool kPv = NVW == 2;
+  constexpr bool kPv = NVW == 2 && !KD;
   constexpr bool kRq = kPv && (CHAN || WK != kWkSame);   // P's R operands read separately
   __shared__ Smem<BV, CHAN, WK> sm;
 
@@ -1222,6 +1247,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) wdv[j] = ld4f(&sm.wd[cur][16 * j + 4 * l4]);
           const float gC = DECAY ? sm.eg[cur][kC - 1] : 1.f;
+          float4 gcc[KD ? 8 : 1];   // (KD) the state decay of this lane's channels of each tile
+          if constexpr (KD) {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) gcc[cb] = ld4f(&gcv_of(sm, cur)[chan0(cb)]);
+          }
 
           // D = T X  (T_hi X + T_lo X)
           const short8v x01 = cat(x4[0], x4[1]), x23 = cat(x4[2], x4[3]);
@@ -1244,6 +1274,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           for (int cb = 0; cb < 4; ++cb) {
             float4v acc = st[cb];
             if (DECAY) acc *= gC;
+            if constexpr (KD) acc = float4v{acc[0] * gcc[cb].x, acc[1] * gcc[cb].y, acc[2] * gcc[cb].z, acc[3] * gcc[cb].w};
             st[cb] = mfma32(rb[cb], w23, mfma32(ra[cb], w01, acc));
             ra[cb] = optr_state(Rk, cb + 4, 0, lane);   // second half, read behind the first
             rb[cb] = optr_state(Rk, cb + 4, 32, lane);
@@ -1252,6 +1283,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           for (int cb = 4; cb < 8; ++cb) {
             float4v acc = st[cb];
             if (DECAY) acc *= gC;
+            if constexpr (KD) acc = float4v{acc[0] * gcc[cb].x, acc[1] * gcc[cb].y, acc[2] * gcc[cb].z, acc[3] * gcc[cb].w};
             st[cb] = mfma32(rb[cb - 4], w23, mfma32(ra[cb - 4], w01, acc));
           }
           // O = scale (O1 + P D), D as a bf16 pair (P_00 and P_22 are packed twice against
@@ -1298,8 +1330,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     return;
   }
 
-  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true, TP>(sm, a);
-  else helper_loop<BV, CHAN, DECAY, WK, RES, false, TP>(sm, a);
+  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true, TP, KD>(sm, a);
+  else helper_loop<BV, CHAN, DECAY, WK, RES, false, TP, KD>(sm, a);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1516,7 +1548,42 @@ hipError_t launch_bv(const ChunkArgs &a, hipStream_t s) {
   }
 }
 
+// Workspace of the per-channel decay on this kernel: the decayed operand arrays E~, Q~, R~
+// ([B, T, H, 128] bf16 each), then one record per (batch, head, chunk) (T, P and the state
+// decay; see kda_prep.hip), each section 256-byte aligned.
+struct KdaWs {
+  unsigned long long q, e, r, rec, total;
+};
+KdaWs kda_ws(long long B, long long T, long long H) {
+  auto al = [](unsigned long long x) { return (x + 255ull) & ~255ull; };
+  const unsigned long long arr = al(static_cast<unsigned long long>(B * T * H) * kD * 2);
+  const unsigned long long nch = static_cast<unsigned long long>((T + kC - 1) / kC);
+  KdaWs w;
+  w.q = 0;
+  w.e = arr;
+  w.r = 2 * arr;
+  w.rec = 3 * arr;
+  w.total = w.rec + al(static_cast<unsigned long long>(B * H) * nch * (992ull * 16));
+  return w;
+}
+
 }  // namespace
+
+hipError_t launch_kda_prep(const ChunkArgs &a, uint16_t *qt, uint16_t *et, uint16_t *rt, uint16_t *rec,
+                           hipStream_t s);
+
+// The per-channel decay runs on this kernel only through the workspace (prepared operands):
+// bf16, Dk = Dv = 128, chunk 64, scalar gains, write key k, exact T.
+bool chunk_mfma_kda_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in, const void *out,
+                             const float *state_out) {
+  if (d.io_dtype != GDR_BF16 || d.Dk != kD || d.Dv != kD || d.chunk != kC) return false;
+  if (d.decay != GDR_DECAY_CHANNEL || d.gain != GDR_GAIN_SCALAR || d.wkey != GDR_WKEY_SAME) return false;
+  if (d.neumann_order >= 0) return false;
+  const void *p16[] = {in.q, in.k, in.v, in.log_alpha, out, state_in, state_out};
+  for (const void *p : p16)
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
+  return true;
+}
 
 bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in, const void *out,
                          const float *state_out) {
@@ -1543,6 +1610,31 @@ static int chunk_mfma_bv(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
+  if (a.decay == GDR_DECAY_CHANNEL) {
+    // prepared operands first (every chunk at once), then the sequential pass as the
+    // explicit-write-key variant without a decay, reading T, P and the state decay from the
+    // records (the host passes this descriptor here only with its workspace)
+    // (an empty sequence needs no workspace: the pass only carries the state through)
+    if (a.tpre == nullptr && a.T > 0) return hipErrorInvalidValue;
+    const KdaWs w = kda_ws(a.B, a.T, a.H);
+    char *ws = reinterpret_cast<char *>(const_cast<uint16_t *>(a.tpre));
+    uint16_t *qt = reinterpret_cast<uint16_t *>(ws + w.q), *et = reinterpret_cast<uint16_t *>(ws + w.e);
+    uint16_t *rt = reinterpret_cast<uint16_t *>(ws + w.r), *rec = reinterpret_cast<uint16_t *>(ws + w.rec);
+    hipError_t e = launch_kda_prep(a, qt, et, rt, rec, s);
+    if (e != hipSuccess) return e;
+    ChunkArgs b = a;
+    b.q = qt;
+    b.k = et;
+    b.write_key = rt;
+    b.log_alpha = nullptr;
+    b.decay = GDR_DECAY_NONE;
+    b.wkey = GDR_WKEY_EXPLICIT;
+    b.tpre = rec;
+    const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / 32);
+    hipLaunchKernelGGL((chunk_mfma_kernel<32, false, false, kWkExplicit, false, true, true>), dim3(grid), dim3(kNT), 0, s,
+                       b);
+    return hipGetLastError();
+  }
   if (a.tpre != nullptr) {   // T of every chunk first (the host passes tpre only where it applies)
     const int nchunks = (a.T + kC - 1) / kC;
     if (nchunks > 0) {
@@ -1568,6 +1660,10 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
 // 10 KB per (batch, head, chunk), where it applies (matrix-core kernel, write key k, exact T,
 // no residual steps), else 0
 unsigned long long chunk_mfma_tpre_bytes(const gdr_desc_t &d) {
+  if (d.decay == GDR_DECAY_CHANNEL) {
+    gdr_inputs_t none{};
+    return chunk_mfma_kda_supports(d, none, nullptr, nullptr, nullptr) ? kda_ws(d.B, d.T, d.H).total : 0;
+  }
   if (d.wkey != GDR_WKEY_SAME || d.neumann_order >= 0 || d.decay == GDR_DECAY_CHANNEL) return 0;
   const unsigned long long nchunks = (static_cast<unsigned long long>(d.T) + kC - 1) / kC;
   return static_cast<unsigned long long>(d.B) * d.H * nchunks * (10ull * 2 * 256 * 2);

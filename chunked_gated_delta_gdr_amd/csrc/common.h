@@ -25,7 +25,8 @@ struct ChunkArgs {
   float scale, rho, log_rho, eps, h0;
   long long t0;
   // the chunks' T (exact, write key k) formed beforehand, as bf16 pairs row-major,
-  // [B, H, chunks][hi, lo][64][64] (gdr_chunk_fwd_ws); null: the matrix-core kernel forms it
+  // [B, H, chunks][hi, lo][64][64] (gdr_chunk_fwd_ws); null: the matrix-core kernel forms it.
+  // With the per-channel decay on the matrix-core kernel: the base of its whole workspace
   const uint16_t *tpre;
 };
 
@@ -57,6 +58,9 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 unsigned long long chunk_mfma_tpre_bytes(const gdr_desc_t &d);
 bool chunk_mfma_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in,
                          const void *out, const float *state_out);
+// the per-channel decay on the matrix-core kernel (only with gdr_chunk_fwd_ws's workspace)
+bool chunk_mfma_kda_supports(const gdr_desc_t &d, const gdr_inputs_t &in, const float *state_in,
+                             const void *out, const float *state_out);
 hipError_t launch_step(const ChunkArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_prep_state(const BwdArgs &a, int io_dtype, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdArgs &a, int io_dtype, hipStream_t s);

@@ -315,15 +315,18 @@ static gdr_status_t chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, cons
   if (st != GDR_OK) return st;
   const gdr_desc_t dl = lower_chunk(*dd);
   const gdr_desc_t *d = &dl;
-  const bool mfma_ok = gdr::chunk_mfma_supports(*d, *in, state_in, out, state_out);
+  // the per-channel decay runs on the matrix-core kernel only with the workspace
+  const bool kda_ok = ws != nullptr && gdr::chunk_mfma_kda_supports(*d, *in, state_in, out, state_out);
+  const bool mfma_ok = kda_ok || gdr::chunk_mfma_supports(*d, *in, state_in, out, state_out);
   if (d->impl == GDR_IMPL_MFMA && !mfma_ok)
     return fail(GDR_ENOTSUP, "the MFMA kernel does not cover this descriptor "
                              "(needs bf16, Dk = Dv = 128, chunk 64 or exact chunk 128, 16-byte aligned tensors, "
-                             "no per-channel decay, channel gains only with write key k)");
+                             "channel gains only with write key k; a per-channel decay needs scalar gains, write key k, "
+                             "exact T and the workspace of gdr_chunk_fwd_ws)");
   const bool use_mfma = mfma_ok && d->impl != GDR_IMPL_GENERIC;
   gdr::ChunkArgs a = make_args(d, in, state_in, out, state_out);
   if (ws != nullptr && use_mfma) {
-    const uint64_t need = gdr::chunk_mfma_tpre_bytes(*d);
+    const uint64_t need = gdr::chunk_mfma_tpre_bytes(*d);   // (per-channel decay: operands and records)
     if (need > 0) {
       if (ws_bytes < need)
         return fail(GDR_EINVAL, "workspace of %llu bytes, this descriptor needs %llu",
@@ -334,7 +337,8 @@ static gdr_status_t chunk_fwd(const gdr_desc_t *dd, const gdr_inputs_t *in, cons
       const Range r_ws = rng("workspace", ws, static_cast<long double>(need));
       const Range others[] = {
           rng("q", in->q, ntok * d->Dk * 2), rng("k", in->k, ntok * d->Dk * 2), rng("v", in->v, ntok * d->Dv * 2),
-          rng("beta", in->beta, ntok * 4), rng("log_alpha", in->log_alpha, ntok * 4),
+          rng("beta", in->beta, ntok * 4),
+          rng("log_alpha", in->log_alpha, ntok * 4 * (d->decay == GDR_DECAY_CHANNEL ? d->Dk : 1)),
           rng("erase", in->erase, ntok * d->Dk * 2), rng("write", in->write, ntok * d->Dv * 2),
           rng("out", out, ntok * d->Dv * 2), rng("state_in", state_in, sbytes), rng("state_out", state_out, sbytes)};
       for (const Range &r : others)
@@ -365,7 +369,9 @@ uint64_t gdr_chunk_fwd_workspace_size(const gdr_desc_t *dd) {
   if (dd->impl == GDR_IMPL_GENERIC) return 0;
   const gdr_desc_t dl = lower_chunk(*dd);
   gdr_inputs_t none{};
-  if (!gdr::chunk_mfma_supports(dl, none, nullptr, nullptr, nullptr)) return 0;
+  if (!gdr::chunk_mfma_supports(dl, none, nullptr, nullptr, nullptr) &&
+      !gdr::chunk_mfma_kda_supports(dl, none, nullptr, nullptr, nullptr))
+    return 0;
   return gdr::chunk_mfma_tpre_bytes(dl);
 }
 

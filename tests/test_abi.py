@@ -440,6 +440,20 @@ def test_forward_workspace_size_and_checks():
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, impl=G.GDR_IMPL_GENERIC)) == 0
     assert G.gdr_chunk_fwd_workspace_size(desc()) == 0   # Dk = 64: the fp32 kernel
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, io_dtype=G.GDR_F32)) == 0
+    # per-channel decay (matrix-core kernel through the workspace only): the three decayed operand
+    # arrays [B, T, H, 128] bf16, then a 15872-byte record per (batch, head, chunk), each section
+    # rounded up to 256 bytes
+    al = lambda x: (x + 255) // 256 * 256
+    kd = desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL)
+    assert G.gdr_chunk_fwd_workspace_size(kd) == 3 * al(2 * 100 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872)
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL, T=77)) == \
+        3 * al(2 * 77 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872)
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL, chunk=128)) == \
+        G.gdr_chunk_fwd_workspace_size(kd)
+    for kw in (dict(neumann_order=3), dict(gain=G.GDR_GAIN_CHANNEL), dict(wkey=G.GDR_WKEY_DIAG_PRECOND),
+               dict(wkey=G.GDR_WKEY_EXPLICIT), dict(io_dtype=G.GDR_F32), dict(impl=G.GDR_IMPL_GENERIC)):
+        assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL, **kw)) == 0, kw
+    assert G.gdr_chunk_fwd_impl(kd) == G.GDR_IMPL_GENERIC   # gdr_chunk_fwd itself: the fp32 kernel
     L = G.lib()
     ins = inputs()
     ws = BASE + 40 * MB

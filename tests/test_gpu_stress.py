@@ -139,6 +139,16 @@ def test_stress_generic_fp32(variant, stress, chunk):
     check(s, x, o, S, TOL_F32, label=f"generic f32 {variant} {stress} C={chunk}")
 
 
+@pytest.mark.parametrize("stress", list(STRESS))
+def test_stress_kda_matrix_cores(stress):
+    """The per-channel decay on the bf16 matrix-core kernel (prepared operands, gdr_chunk_fwd_ws)."""
+    s = stress_spec("kda", stress)
+    announce(f"kda matrix cores {stress} {s}")
+    x = gs.make_inputs(s)
+    o, S, _ = run_chunk(s, x, impl="mfma", workspace=True)
+    check(s, x, o, S, TOL_BF16, label=f"kda matrix cores {stress}")
+
+
 @pytest.mark.parametrize("variant,stress", [("kda", "corr3_strong"), ("kda", "corr3_beta12"), ("kda", "strong"),
                                             ("gdn", "corr3_beta12"), ("gdn2_decay", "corr3_strong")])
 def test_stress_generic_bf16(variant, stress):

@@ -111,3 +111,92 @@ def test_tpre_full_size_sampled(workload):
     o_ref, S_ref, _ = O.recurrent(x, streams=streams)
     o, S, _ = run_chunk(s, x, workspace=True)
     check_streams(host(o), host(S), o_ref, S_ref, streams, s.T)
+
+
+# --------------------------------------------------------------------------------------
+# Per-channel decay on the matrix-core kernel: operands, T and P prepared for every chunk
+# at once, then the sequential pass with the state decayed per channel
+# --------------------------------------------------------------------------------------
+
+def kda_spec(**kw):
+    over = dict(B=2, H=2, T=200, Dk=128, Dv=128, dtype="bf16", seed=43)
+    over.update(kw)
+    return gs.spec("kda", **over)
+
+
+@pytest.mark.parametrize("B,H,T", [(2, 2, 200), (4, 16, 130), (1, 3, 64)])
+def test_kda_matrix_cores(B, H, T):
+    """Against the fp64 oracle per stream and per 64-token block, and against the fp32 kernel."""
+    s = kda_spec(B=B, H=H, T=T)
+    announce(f"kda matrix cores B={B} H={H} T={T}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(6)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    streams = sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
+    o_ref, S_ref, _ = O.recurrent(x, state0=S0.astype(np.float64), scale=0.9, streams=streams)
+    o, S, _ = run_chunk(s, x, state_in=S0, scale=0.9, impl="mfma", workspace=True)
+    og, Sg, _ = run_chunk(s, x, state_in=S0, scale=0.9, impl="generic")
+    o, S, og, Sg = host(o), host(S), host(og), host(Sg)
+    check_streams(o, S, o_ref, S_ref, streams, T)
+    gap, gapS = O.rel_l2(o, og), O.rel_l2(S, Sg)
+    print(f"  rel-L2(matrix cores, fp32 kernel) over every stream: out {gap:.3e} state {gapS:.3e}", flush=True)
+    assert gap <= TOL_BF16 and gapS <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 127])
+def test_kda_matrix_cores_lengths(T):
+    s = kda_spec(T=T)
+    announce(f"kda matrix cores T={T}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(7)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32)
+    o_ref, S_ref, _ = O.recurrent(x, state0=S0.astype(np.float64))
+    o, S, _ = run_chunk(s, x, state_in=S0, impl="mfma", workspace=True)
+    o, S = host(o), host(S)
+    if T > 0:
+        assert O.rel_l2(o, o_ref) <= TOL_BF16
+    assert O.rel_l2(S, S_ref) <= TOL_BF16
+
+
+def test_kda_matrix_cores_chunk128_exact():
+    s = kda_spec(T=300, chunk=128)
+    announce("kda matrix cores chunk 128 exact T=300")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.recurrent(x)
+    o, S, _ = run_chunk(s, x, impl="mfma", workspace=True)
+    assert O.rel_l2(host(o), o_ref) <= TOL_BF16 and O.rel_l2(host(S), S_ref) <= TOL_BF16
+
+
+def test_kda_matrix_cores_need_the_workspace():
+    """Without the workspace the per-channel decay stays on the fp32 kernel: asking for the
+    matrix cores is refused, the automatic choice runs the fp32 kernel."""
+    s = kda_spec(T=70)
+    announce("kda: matrix cores without the workspace")
+    x = gs.make_inputs(s)
+    with pytest.raises(Exception):
+        run_chunk(s, x, impl="mfma")
+    import torch
+    o, S, _ = run_chunk(s, x)
+    og, Sg, _ = run_chunk(s, x, impl="generic")
+    assert torch.equal(o, og) and torch.equal(S, Sg)
+
+
+def test_kda_matrix_cores_deterministic():
+    import torch
+    s = kda_spec(B=2, H=4, T=257)
+    announce("kda matrix cores twice, bitwise")
+    x = gs.make_inputs(s)
+    o1, S1, _ = run_chunk(s, x, impl="mfma", workspace=True)
+    o2, S2, _ = run_chunk(s, x, impl="mfma", workspace=True)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.timeout(300)
+def test_kda_matrix_cores_full_size_sampled():
+    s = gs.spec("kda")
+    streams = [(0, 0), (s.B - 1, s.H - 1), (1, 7)]
+    announce(f"kda matrix cores full size {s}, streams {streams}")
+    x = gs.make_inputs(s)
+    o_ref, S_ref, _ = O.recurrent(x, streams=streams)
+    o, S, _ = run_chunk(s, x, workspace=True)
+    check_streams(host(o), host(S), o_ref, S_ref, streams, s.T)
