@@ -1549,10 +1549,11 @@ hipError_t launch_bv(const ChunkArgs &a, hipStream_t s) {
 }
 
 // Workspace of the per-channel decay on this kernel: the decayed operand arrays E~, Q~, R~
-// ([B, T, H, 128] bf16 each), then one record per (batch, head, chunk) (T, P and the state
-// decay; see kda_prep.hip), each section 256-byte aligned.
+// ([B, T, H, 128] bf16 each), one record per (batch, head, chunk) (T, P and the state decay;
+// see kda_prep.hip), then one flag per (batch, head, chunk) (the preparation's route), each
+// section 256-byte aligned.
 struct KdaWs {
-  unsigned long long q, e, r, rec, total;
+  unsigned long long q, e, r, rec, flags, total;
 };
 KdaWs kda_ws(long long B, long long T, long long H) {
   auto al = [](unsigned long long x) { return (x + 255ull) & ~255ull; };
@@ -1563,14 +1564,15 @@ KdaWs kda_ws(long long B, long long T, long long H) {
   w.e = arr;
   w.r = 2 * arr;
   w.rec = 3 * arr;
-  w.total = w.rec + al(static_cast<unsigned long long>(B * H) * nch * (992ull * 16));
+  w.flags = w.rec + al(static_cast<unsigned long long>(B * H) * nch * (992ull * 16));
+  w.total = w.flags + al(static_cast<unsigned long long>(B * H) * nch * 4);
   return w;
 }
 
 }  // namespace
 
 hipError_t launch_kda_prep(const ChunkArgs &a, uint16_t *qt, uint16_t *et, uint16_t *rt, uint16_t *rec,
-                           hipStream_t s);
+                           uint32_t *flags, hipStream_t s);
 
 // The per-channel decay runs on this kernel only through the workspace (prepared operands):
 // bf16, Dk = Dv = 128, chunk 64, scalar gains, write key k, exact T.
@@ -1620,7 +1622,7 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
     char *ws = reinterpret_cast<char *>(const_cast<uint16_t *>(a.tpre));
     uint16_t *qt = reinterpret_cast<uint16_t *>(ws + w.q), *et = reinterpret_cast<uint16_t *>(ws + w.e);
     uint16_t *rt = reinterpret_cast<uint16_t *>(ws + w.r), *rec = reinterpret_cast<uint16_t *>(ws + w.rec);
-    hipError_t e = launch_kda_prep(a, qt, et, rt, rec, s);
+    hipError_t e = launch_kda_prep(a, qt, et, rt, rec, reinterpret_cast<uint32_t *>(ws + w.flags), s);
     if (e != hipSuccess) return e;
     ChunkArgs b = a;
     b.q = qt;

@@ -441,13 +441,13 @@ def test_forward_workspace_size_and_checks():
     assert G.gdr_chunk_fwd_workspace_size(desc()) == 0   # Dk = 64: the fp32 kernel
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, io_dtype=G.GDR_F32)) == 0
     # per-channel decay (matrix-core kernel through the workspace only): the three decayed operand
-    # arrays [B, T, H, 128] bf16, then a 15872-byte record per (batch, head, chunk), each section
-    # rounded up to 256 bytes
+    # arrays [B, T, H, 128] bf16, a 15872-byte record and a 4-byte flag per (batch, head, chunk),
+    # each section rounded up to 256 bytes
     al = lambda x: (x + 255) // 256 * 256
     kd = desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL)
-    assert G.gdr_chunk_fwd_workspace_size(kd) == 3 * al(2 * 100 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872)
+    assert G.gdr_chunk_fwd_workspace_size(kd) == 3 * al(2 * 100 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872) + al(2 * 3 * 2 * 4)
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL, T=77)) == \
-        3 * al(2 * 77 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872)
+        3 * al(2 * 77 * 3 * 128 * 2) + al(2 * 3 * 2 * 15872) + al(2 * 3 * 2 * 4)
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, decay=G.GDR_DECAY_CHANNEL, chunk=128)) == \
         G.gdr_chunk_fwd_workspace_size(kd)
     for kw in (dict(neumann_order=3), dict(gain=G.GDR_GAIN_CHANNEL), dict(wkey=G.GDR_WKEY_DIAG_PRECOND),

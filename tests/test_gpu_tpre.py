@@ -200,3 +200,22 @@ def test_kda_matrix_cores_full_size_sampled():
     o_ref, S_ref, _ = O.recurrent(x, streams=streams)
     o, S, _ = run_chunk(s, x, workspace=True)
     check_streams(host(o), host(S), o_ref, S_ref, streams, s.T)
+
+
+@pytest.mark.parametrize("strong_chunks", [(1,), (0, 3), ()])
+def test_kda_matrix_cores_mixed_routes(strong_chunks):
+    """Chunks whose per-channel decay over the chunk falls below 2^-120 take the preparation's
+    robust route, the others the fast one: strong decays (log a = -5 U(0, 1) per token and
+    channel) in the listed 64-token chunks only, mild ones elsewhere, against the fp64 oracle."""
+    s = kda_spec(B=2, H=3, T=256)
+    announce(f"kda matrix cores, strong decays in chunks {strong_chunks}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(11)
+    la = np.array(x["log_alpha"], dtype=np.float64)
+    for c in strong_chunks:
+        la[:, 64 * c:64 * (c + 1)] = -5.0 * rng.random(la[:, 64 * c:64 * (c + 1)].shape)
+    x["log_alpha"] = la.astype(np.float32).astype(np.float64)
+    streams = [(0, 0), (1, 2)]
+    o_ref, S_ref, _ = O.recurrent(x, streams=streams)
+    o, S, _ = run_chunk(s, x, impl="mfma", workspace=True)
+    check_streams(host(o), host(S), o_ref, S_ref, streams, s.T)
