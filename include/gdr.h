@@ -164,6 +164,13 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
  * (MatMul-only inversion summary, "Declaracao do Problema"), so forming it apart from the
  * state pass is exact.  It applies where the matrix-core kernel runs with write key k and
  * the exact T (no band limit, no residual steps); elsewhere the workspace is not used.
+ * With one decay per key channel (GDR_DECAY_CHANNEL: the diagonal gate the Preconditioned
+ * DeltaNet summaries name beside Gated DeltaNet, section 2c) this entry point is the one that
+ * runs it on the bf16 matrix cores (bf16, Dk = Dv = 128, chunk 64 or exact 128, scalar gains,
+ * write key k, exact T): the workspace then also holds each chunk's decayed keys and queries,
+ * P and the per-channel state decay, all formed before the sequential pass; gdr_chunk_fwd
+ * runs that descriptor on the fp32 kernel.  Results equal gdr_chunk_fwd's within the bf16
+ * bound.
  *
  *   workspace        device memory of at least gdr_chunk_fwd_workspace_size(desc) bytes,
  *                    256-byte aligned, overlapping no other argument; its contents on entry
@@ -177,8 +184,10 @@ gdr_status_t gdr_chunk_fwd_ws(const gdr_desc_t *desc, const gdr_inputs_t *in,
 
 /* Bytes of gdr_chunk_fwd_ws's workspace: 10 KB per (batch, head, chunk of 64 tokens) where it
  * applies (T's ten 16 x 16 blocks on and below the diagonal, each as a pair of bf16 parts), 0
- * where it does not (any workspace is then ignored) or for an invalid descriptor.  Pure host
- * arithmetic. */
+ * where it does not (any workspace is then ignored) or for an invalid descriptor.  With the
+ * per-channel decay: three [B, T, H, 128] bf16 arrays (the decayed keys and queries), then
+ * 15872 bytes and a 4-byte flag per (batch, head, chunk), each section rounded up to 256 bytes
+ * (about 64 KB per chunk).  Pure host arithmetic. */
 uint64_t gdr_chunk_fwd_workspace_size(const gdr_desc_t *desc);
 
 /*
