@@ -42,7 +42,6 @@ KERNEL_SOURCES = {
     "generic": ["chunked_gated_delta_gdr_amd/csrc/chunk_generic.hip"],
     "step": ["chunked_gated_delta_gdr_amd/csrc/recurrent_step.hip"],
 }
-KERNEL_SYMBOLS = {"mfma": "chunk_mfma", "generic": "chunk_generic", "step": "step_kernel"}
 
 
 def alg_bytes(s) -> int:
@@ -79,14 +78,14 @@ def source_sha(impl: str) -> str:
     return h.hexdigest()[:16]
 
 
-def mfma_counter_file(workload: str, impl: str) -> str:
-    return f"chunk_fwd_{impl}_{workload}_mfma_counters.json"
+def mfma_counter_file(workload: str, impl: str, tag: str = "") -> str:
+    return f"chunk_fwd_{impl}_{workload}{tag}_mfma_counters.json"
 
 
-def mfma_counters_from_profile(workload: str, impl: str):
+def mfma_counters_from_profile(workload: str, impl: str, tag: str = ""):
     """The committed matrix-core counter summary of the kernel, if it was taken on the current
     source; else None."""
-    p = os.path.join(ROOT, "profiles", mfma_counter_file(workload, impl))
+    p = os.path.join(ROOT, "profiles", mfma_counter_file(workload, impl, tag))
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -99,14 +98,12 @@ def mfma_summary(args):
     holding SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 matrix operations in units of 512 FLOPs),
     SQ_VALU_MFMA_BUSY_CYCLES (matrix-core busy cycles, summed over SIMDs), SQ_BUSY_CYCLES,
     GRBM_GUI_ACTIVE (GPU active cycles) and SQ_LDS_BANK_CONFLICT."""
-    import statistics
-    kern = KERNEL_SYMBOLS[args.impl_name]
     names = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT",
              "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_WAVES"]
     med = {}
     for n in names:
         try:
-            med[n] = statistics.median(_counter_per_dispatch(args.mfma_summary, n, kern))
+            med[n] = _counter_per_call(args.mfma_summary, n, args.impl_name)[0]
         except SystemExit:
             pass
     s = __import__("gdr_synth").spec(args.workload)
@@ -124,20 +121,54 @@ def mfma_summary(args):
         # counter window, which is wider than the kernel, so the bench divides the per-SIMD
         # figure by its own launch time at the peak engine clock instead
         rec["mfma_busy_cycles_per_simd"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (256 * 4)
-    out = os.path.join(ROOT, "profiles", mfma_counter_file(args.workload, args.impl_name))
+    out = os.path.join(ROOT, "profiles", mfma_counter_file(args.workload, args.impl_name, profile_tag(args)))
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def traffic_file(workload: str, impl: str) -> str:
-    return "step_decode_traffic.json" if impl == "step" else f"chunk_fwd_{impl}_{workload}_traffic.json"
+# gdr_chunk_fwd_ws (T, or the per-channel decay's operands, formed for every chunk first) where
+# it applies, except on gdn: there the fused kernel is as fast (171-174 us either way on one
+# MI355X) at 1.01x the algorithmic HBM bytes instead of 1.57x (keys read twice, T written and
+# read back); on gdn2 and the long prefill the workspace path is 20 % and 7 % faster, and the
+# per-channel decay runs on the matrix cores only through it
+WS_OFF_BY_DEFAULT = {"gdn"}
 
 
-def traffic_from_profile(workload: str, impl: str):
+def wants_workspace(args) -> bool:
+    if args.no_workspace or args.workspace == "off":
+        return False
+    return args.workspace == "on" or args.workload not in WS_OFF_BY_DEFAULT
+
+
+def workspace_bytes(args, s) -> int:
+    if not wants_workspace(args):
+        return 0
+    import chunked_gated_delta_gdr_amd as G
+    return G.gdr_chunk_fwd_workspace_size(G.make_desc(
+        B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
+        io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
+        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
+        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
+        wkey=G.GDR_WKEY_DIAG_PRECOND if s.wkey == "precond" else G.GDR_WKEY_SAME, neumann_order=args.neumann,
+        residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
+
+
+def profile_tag(args) -> str:
+    """Suffix of the committed counter summaries: '_ws' for a call through the workspace."""
+    if args.workload == "decode":
+        return ""
+    return "_ws" if workspace_bytes(args, __import__("gdr_synth").spec(args.workload)) > 0 else ""
+
+
+def traffic_file(workload: str, impl: str, tag: str = "") -> str:
+    return "step_decode_traffic.json" if impl == "step" else f"chunk_fwd_{impl}_{workload}{tag}_traffic.json"
+
+
+def traffic_from_profile(workload: str, impl: str, tag: str = ""):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", traffic_file(workload, impl))
+    p = os.path.join(ROOT, "profiles", traffic_file(workload, impl, tag))
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -258,19 +289,43 @@ def _counter_per_dispatch(csv_path: str, counter: str, name_has: str):
     return sorted(per.values())
 
 
+# the kernels one forward call may launch: the sequential pass and, with the workspace, the
+# kernels that form T (or the per-channel decay's operands and records) for every chunk first
+CALL_KERNELS = {"mfma": ("chunk_mfma_kernel", "chunk_t_kernel", "kda_prep_fast_kernel", "kda_prep_robust_kernel"),
+                "generic": ("chunk_generic",), "step": ("step_kernel",)}
+
+
+def _counter_per_call(csv_path: str, counter: str, impl: str):
+    """The counter per forward call: the median per dispatch of each kernel the call launches,
+    summed over those kernels (each launches once per call)."""
+    import csv
+    import statistics
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            for k in CALL_KERNELS[impl]:
+                if k in r["Kernel_Name"]:
+                    d = per.setdefault(k, {})
+                    d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for the kernels of '{impl}' in {csv_path}")
+    meds = {k: statistics.median(v.values()) for k, v in per.items()}
+    return sum(meds.values()), {k: (m, len(per[k])) for k, m in meds.items()}
+
+
 def traffic_summary(args):
     """Writes profiles/chunk_fwd_<impl>_<workload>_traffic.json from four counter CSVs."""
     import statistics
-    kern = KERNEL_SYMBOLS[args.impl_name]
-    f_k = _counter_per_dispatch(args.traffic_summary[0], "FETCH_SIZE", kern)
-    w_k = _counter_per_dispatch(args.traffic_summary[1], "WRITE_SIZE", kern)
+    fetch, f_parts = _counter_per_call(args.traffic_summary[0], "FETCH_SIZE", args.impl_name)
+    write, w_parts = _counter_per_call(args.traffic_summary[1], "WRITE_SIZE", args.impl_name)
     f_c = _counter_per_dispatch(args.traffic_summary[2], "FETCH_SIZE", "copy")
     w_c = _counter_per_dispatch(args.traffic_summary[3], "WRITE_SIZE", "copy")
     copy_kib = args.copy_probe_mb * 1024.0
     # the last copy of the probe is the representative one (the first may find the source
     # still in the last-level cache from the fill)
     fac_f, fac_w = copy_kib / f_c[-1], copy_kib / w_c[-1]
-    fetch, write = statistics.median(f_k), statistics.median(w_k)
     if args.workload == "decode":
         sd = __import__("gdr_synth").spec("long")
         ab = decode_alg_bytes(sd.decode_batch, sd.H, sd.Dk, sd.Dv)
@@ -280,14 +335,14 @@ def traffic_summary(args):
         "kernel": "gdr_recurrent_step" if args.impl_name == "step" else f"gdr_chunk_fwd/{args.impl_name}",
         "workload": args.workload,
         "source_sha": source_sha(args.impl_name),
-        "fetch_kib_per_dispatch_median": fetch, "write_kib_per_dispatch_median": write,
-        "dispatches": [len(f_k), len(w_k)],
+        "fetch_kib_per_call": fetch, "write_kib_per_call": write,
+        "per_kernel_fetch_kib_median_and_dispatches": f_parts, "per_kernel_write_kib_median_and_dispatches": w_parts,
         "copy_probe_mib": args.copy_probe_mb, "copy_fetch_kib": f_c[-1], "copy_write_kib": w_c[-1],
         "scale_fetch": fac_f, "scale_write": fac_w,
         "hbm_bytes_per_launch": round((fetch * fac_f + write * fac_w) * 1024.0),
         "alg_bytes_per_launch": ab,
     }
-    out = os.path.join(ROOT, "profiles", traffic_file(args.workload, args.impl_name))
+    out = os.path.join(ROOT, "profiles", traffic_file(args.workload, args.impl_name, profile_tag(args)))
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -554,8 +609,9 @@ def main():
     ap.add_argument("--residual", type=int, default=0,
                     help="residual-correction steps on the band-N start (needs --neumann N)")
     ap.add_argument("--impl", default="auto", choices=["auto", "generic", "mfma"])
-    ap.add_argument("--no-workspace", action="store_true",
-                    help="the forward without the workspace (T formed inside the sequential kernel)")
+    ap.add_argument("--workspace", default="auto", choices=["auto", "on", "off"],
+                    help="call gdr_chunk_fwd_ws with its workspace (auto: everywhere it applies but gdn)")
+    ap.add_argument("--no-workspace", action="store_true", help="same as --workspace off")
     ap.add_argument("--bwd", action="store_true", help="time gdr_chunk_bwd instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -622,13 +678,8 @@ def main():
     precond = s.wkey == "precond"
 
     # the workspace of gdr_chunk_fwd_ws (T of every chunk formed first) where it applies
-    ws_bytes = 0 if args.no_workspace else G.gdr_chunk_fwd_workspace_size(G.make_desc(
-        B=s.B, T=s.T, H=s.H, Dk=s.Dk, Dv=s.Dv, chunk=s.chunk,
-        io_dtype=G.GDR_BF16 if s.dtype == "bf16" else G.GDR_F32,
-        gain=G.GDR_GAIN_SCALAR if s.gain == "scalar" else G.GDR_GAIN_CHANNEL,
-        decay={"scalar": G.GDR_DECAY_SCALAR, "channel": G.GDR_DECAY_CHANNEL}.get(s.decay, G.GDR_DECAY_NONE),
-        wkey=G.GDR_WKEY_DIAG_PRECOND if precond else G.GDR_WKEY_SAME, neumann_order=args.neumann,
-        residual_steps=args.residual, impl={"auto": 0, "generic": 1, "mfma": 2}[args.impl]))
+    ws_bytes = workspace_bytes(args, s)
+    tag = "_ws" if ws_bytes > 0 else ""
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
 
     def step(i):
@@ -681,14 +732,14 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
         # (the counters are taken on the exact-T configuration of the workload)
-        "traffic": traffic_from_profile(args.workload, impl_name) if args.neumann < 0 else None,
+        "traffic": traffic_from_profile(args.workload, impl_name, tag) if args.neumann < 0 else None,
         "kernel": f"gdr_chunk_fwd/{impl_name}",
         "alg_bytes_per_launch": ab,
         "avg_launch_us": round(avg_launch_s * 1e6, 2),
         "mfma_bf16_frac": round(af / avg_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "alg_gflop_per_launch": round(af / 1e9, 3),
     }
-    mc = mfma_counters_from_profile(args.workload, impl_name) if args.neumann < 0 and args.residual == 0 else None
+    mc = mfma_counters_from_profile(args.workload, impl_name, tag) if args.neumann < 0 and args.residual == 0 else None
     if mc is not None:
         # the matrix-core work the counters saw per dispatch (dense tiles, padding and the split
         # products included), over this run's launch time
@@ -784,7 +835,7 @@ def main():
                                + (f" band N={args.neumann}" if args.neumann >= 0 else " exact T")
                                + (f" + {args.residual} residual steps" if args.neumann >= 0 and args.residual > 0 else ""),
                    "B": s.B, "T": s.T, "H": s.H, "Dk": s.Dk, "Dv": s.Dv, "chunk": s.chunk,
-                   "impl": impl_name, "parallelism": "single GPU"},
+                   "impl": impl_name, "workspace": ws is not None, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
