@@ -321,9 +321,12 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
   // (the host bounds the grid to 2^22 workgroups, so these fit in 32 bits)
-  const int G = static_cast<int>(gridDim.x);
-  const int bid = static_cast<int>(blockIdx.x);
-  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  // With the sequence split the grid holds three groups of the batch's value tiles, in this
+  // order (so the first two are resident first): role 0 the first segment, role 1 the second
+  // from a zero state, role 2 the second's transition (V' = 0 from the identity)
+  const int per = a.seg_split > 0 ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
+  const int role = static_cast<int>(blockIdx.x) / per, local = static_cast<int>(blockIdx.x) % per;
+  const int logical = (per % 8 == 0) ? (local % 8) * (per / 8) + local / 8 : local;
   const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
   const int H = a.H, T = a.T;
   const int b = bh / H, h = bh % H;
@@ -331,6 +334,8 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
   const long long gate0 = static_cast<long long>(b) * T * H + h;
   const int nchunks = (T + kC - 1) / kC;
+  const int cbeg = role == 0 ? 0 : a.seg_split;                                  // this workgroup's chunks
+  const int cend = (role == 0 && a.seg_split > 0) ? a.seg_split : nchunks;
   const int N = a.N;
   auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
 
@@ -432,6 +437,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
         const uint32_t m = srow[s] < n ? 0xffffffffu : 0u;
         x = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
       }
+      if (role == 2 && isv) x = make_uint4(0u, 0u, 0u, 0u);   // the transition: V' = 0
       uint4 xg = x;   // gated copy: erase (.) k, write (.) v
       if (CHAN) {
         xg.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(x, 0), elem(pb[s], 1) * elem(x, 1));
@@ -610,10 +616,10 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       }
     }
   };
-  if (STG && nchunks > 0) load_items(0);
-  for (int c = -1; c < nchunks; ++c) {
+  if (STG && cbeg < cend) load_items(cbeg);
+  for (int c = cbeg - 1; c < cend; ++c) {
     const int cur = c & 1, nxt = (c + 1) & 1;
-    const bool have_next = c + 1 < nchunks;
+    const bool have_next = c + 1 < cend;
 
     __syncthreads();   // (1)
     // The two T_ba waves read every operand of their block products (T blocks and A blocks of
@@ -656,16 +662,16 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
       }
     };
     if constexpr (TP) {
-      if (!STG && c >= 0) tp_stage(cur);
-    } else if (!STG && c >= 0) {
+      if (!STG && c >= cbeg) tp_stage(cur);
+    } else if (!STG && c >= cbeg) {
       load_ops(std::false_type{});
       load_ops(std::true_type{});
     }
     if (STG && have_next) {
       stage_items(c + 1, nxt);
-      if (c + 2 < nchunks) load_items(c + 2);
+      if (c + 2 < cend) load_items(c + 2);
     }
-    if (c >= 0) {
+    if (c >= cbeg) {
       if constexpr (!STG && !TP) {
         // remaining blocks of T(c): T_10 = D_1 A_10 D_0, T_32 = D_3 A_32 D_2 and column block
         // qb = hw of the lower-left quadrant T_ba = T_b A_ba T_a, every product on bf16 pairs
@@ -911,17 +917,17 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
             *reinterpret_cast<short4v *>(&sm.tl[cur][i][JB * 16 + 4 * l4]) = tobf4(tl);
           }
         };
-        if (c >= 0) {
+        if (c >= cbeg) {
           if constexpr (J0 >= 0) e_col(j0c, ez[0]);
           if constexpr (J1 >= 0) e_col(j1c, ez[1]);
         }
         __syncthreads();   // (R1) E published
-        if (c >= 0) {
+        if (c >= cbeg) {
           if constexpr (J0 >= 0) z_col(j0c, ez[0], tz[0]);
           if constexpr (J1 >= 0) z_col(j1c, ez[1], tz[1]);
         }
         __syncthreads();   // (R2) every read of T0 done
-        if (c >= 0) {
+        if (c >= cbeg) {
           if constexpr (J0 >= 0) t_put(j0c, tz[0]);
           if constexpr (J1 >= 0) t_put(j1c, tz[1]);
         }
@@ -1052,9 +1058,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 
   // XCD-aware tile order: the value tiles of one head land on one XCD (shared L2)
   // (the host bounds the grid to 2^22 workgroups, so these fit in 32 bits)
-  const int G = static_cast<int>(gridDim.x);
-  const int bid = static_cast<int>(blockIdx.x);
-  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  // With the sequence split the grid holds three groups of the batch's value tiles, in this
+  // order (so the first two are resident first): role 0 the first segment, role 1 the second
+  // from a zero state, role 2 the second's transition (V' = 0 from the identity)
+  const int per = a.seg_split > 0 ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
+  const int role = static_cast<int>(blockIdx.x) / per, local = static_cast<int>(blockIdx.x) % per;
+  const int logical = (per % 8 == 0) ? (local % 8) * (per / 8) + local / 8 : local;
   const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
   const int H = a.H, T = a.T;
   const int b = bh / H, h = bh % H;
@@ -1062,6 +1071,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
   const long long gate0 = static_cast<long long>(b) * T * H + h;
   const int nchunks = (T + kC - 1) / kC;
+  const int cbeg = role == 0 ? 0 : a.seg_split;                                  // this workgroup's chunks
+  const int cend = (role == 0 && a.seg_split > 0) ? a.seg_split : nchunks;
   const int N = a.N;
   auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
 
@@ -1071,7 +1082,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const uint16_t *gwk = static_cast<const uint16_t *>(a.write_key);
   const uint16_t *ger = static_cast<const uint16_t *>(a.erase);
   const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
-  uint16_t *gout = static_cast<uint16_t *>(a.out);
+  uint16_t *gout = role == 2 ? a.seg_qt : static_cast<uint16_t *>(a.out);
+  // final state: with the sequence split each role's goes to its slot of seg_state
+  float *const sout = a.seg_split > 0 ? a.seg_state + static_cast<long long>(role) * a.B * a.H * kD * kD : a.state_out;
 
   // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
   for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = (&sm.tl[0][0][0])[i] = 0;
@@ -1099,19 +1112,22 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         st[cb] = zero4();
-        if (a.state_in != nullptr) {
+        if (role == 2) {   // the transition starts from the identity (its rows are unit rows)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[cb][r] = chan0(cb) + r == vrow ? 1.f : 0.f;
+        } else if (role == 0 && a.state_in != nullptr) {
           const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb));
           st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
         }
       }
-      for (int c = -1; c < nchunks; ++c) {
+      for (int c = cbeg - 1; c < cend; ++c) {
         const int cur = c & 1;
         const int c0 = c * kC;
         const int n = min(kC, T - c0);
         short4v x4[4];
         float4v O1[4];
         __syncthreads();   // (1) chunk c staged, T(c) diagonal part ready
-        if (c >= 0) {
+        if (c >= cbeg) {
           // Y = E S^T and O1 = e^g Q S^T for the four 16-token blocks; X = V' - e^g Y.  The
           // operands of block tb + 1 are read while block tb is multiplied.  With kPv the K
           // operands of earlier blocks are kept and the blocks (tb, jb), jb <= tb, of P are
@@ -1219,7 +1235,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
           __syncthreads();   // (R2)
           __syncthreads();   // (R3)
         }
-        if (c >= 0) {
+        if (c >= cbeg) {
           // every LDS operand of this phase is read up front: T and P blocks, R^T for the update.
           // T is held as a bf16 pair (hi + lo): the diagonal blocks pack hi and lo into one K = 32
           // operand (the other K half of a diagonal block is zero), the others take one operand
@@ -1317,10 +1333,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
         }
         if (!RES && WK == kWkPrecond) __syncthreads();   // (3) write keys of chunk c + 1 formed
       }
-      if (a.state_out != nullptr) {
+      if (sout != nullptr) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
-          *reinterpret_cast<float4 *>(a.state_out + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb)) =
+          *reinterpret_cast<float4 *>(sout + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb)) =
               make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
       }
     };
@@ -1521,9 +1537,106 @@ __global__ __launch_bounds__(64 * kTW) void chunk_t_kernel(ChunkArgs a, uint16_t
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Sequence split, fix-up.  The state after token t of the second segment is
+// S_t = S_mid M_t + S_loc,t (the recurrence is linear in its state; M_t is the transition from
+// the segment's start, whose rows evolve as state rows with V' = 0 from the identity), so
+// o_t = S_mid (scale M_t q_t) + o_loc,t = S_mid q~_t + o_loc,t and S_end = S_mid M + S_loc.
+// ---------------------------------------------------------------------------------------
+// out[b, t, h, :] += S_mid q~_t for the second segment's tokens: one workgroup of four waves per
+// (64 tokens, head, batch); wave w owns state rows 32 w .. + 31 and keeps their columns of
+// S_mid^T as bf16 hi / lo B operands; per 16-token block the A operand is q~ (bf16), and the
+// 16 x 32 fp32 result goes through LDS so that each lane adds 8 consecutive values of one
+// token with one 16-byte read and write of out
+__global__ __launch_bounds__(256) void seg_out_fixup_kernel(ChunkArgs a, const float *smid, const uint16_t *qt,
+                                                             int t0) {
+  __shared__ float tile[4][16][33];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int H = a.H, T = a.T;
+  const float *S = smid + (static_cast<long long>(b) * H + h) * kD * kD;   // [v][i]
+  short8v bhi[2][4], blo[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float *p = S + (32 * wave + 16 * j + l16) * kD + 32 * s2 + 8 * l4;
+      const float4 x0 = ld4f(p), x1 = ld4f(p + 4);
+      const Pair p0 = split4(float4v{x0.x, x0.y, x0.z, x0.w}), p1 = split4(float4v{x1.x, x1.y, x1.z, x1.w});
+      bhi[j][s2] = cat(p0.h, p1.h);
+      blo[j][s2] = cat(p0.l, p1.l);
+    }
+  const long long tokstride = static_cast<long long>(H) * kD;
+  const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
+  uint16_t *out = static_cast<uint16_t *>(a.out);
+  const int tb0 = t0 + static_cast<int>(blockIdx.x) * 64;
+  for (int blk = 0; blk < 4; ++blk) {
+    const int tt = tb0 + 16 * blk;
+    if (tt >= T) break;
+    // A operand: token row tt + l16 (read clamped past the end), K = 32 s + 8 l4 ..
+    const long long arow = head0 + static_cast<long long>(min(tt + l16, T - 1)) * tokstride;
+    short8v av[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) av[s2] = ld8(qt + arow + 32 * s2 + 8 * l4);
+    float4v acc[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32(av[s2], blo[j][s2], mfma32(av[s2], bhi[j][s2], acc[j]));
+    // lane: tokens tt + 4 l4 + r, state row 32 wave + 16 j + l16; read back as token lane / 4,
+    // rows 32 wave + 8 (lane % 4) .. + 7
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tile[wave][4 * l4 + r][16 * j + l16] = acc[j][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int tr = lane >> 2, c8 = 8 * (lane & 3), t = tt + tr;
+    if (t < T) {
+      uint4 *o = reinterpret_cast<uint4 *>(out + head0 + static_cast<long long>(t) * tokstride + 32 * wave + c8);
+      const uint4 w = *o;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = elem(w, e) + tile[wave][tr][c8 + e];
+      *o = make_uint4(f32x2_to_bf16x2_bits(x[0], x[1]), f32x2_to_bf16x2_bits(x[2], x[3]),
+                      f32x2_to_bf16x2_bits(x[4], x[5]), f32x2_to_bf16x2_bits(x[6], x[7]));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// state_out = S_mid M + S_loc in fp32: one workgroup per (batch-head, 8 state rows), one thread
+// per column (each element of M read once for the 8 rows, which sit in LDS)
+__global__ __launch_bounds__(kD) void seg_state_fixup_kernel(const float *seg_state, float *state_out, long long nbh) {
+  __shared__ float rows[8][kD];
+  const long long bh = blockIdx.x;
+  const int v0 = 8 * static_cast<int>(blockIdx.y), k = threadIdx.x;
+  const long long sz = nbh * kD * kD;
+  const float *smid = seg_state + bh * kD * kD, *sloc = seg_state + sz + bh * kD * kD, *m = seg_state + 2 * sz + bh * kD * kD;
+  float acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    acc[r] = sloc[(v0 + r) * kD + k];
+    rows[r][k] = smid[(v0 + r) * kD + k];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < kD; ++i) {
+    const float mk = m[i * kD + k];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = fmaf(rows[r][i], mk, acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) state_out[(bh * kD + v0 + r) * kD + k] = acc[r];
+}
+
 template <int BV, bool CHAN, bool DECAY, int WK>
 hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV);   // <= 2^22
+  // <= 2^22 (three groups of the value tiles with the sequence split, which needs <= 128 of them)
+  const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV) * (a.seg_split > 0 ? 3u : 1u);
   if (a.S > 0)
     hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true, false>), dim3(grid), dim3(kNT), 0, s, a);
   else if (WK == kWkSame && BV == 32 && a.tpre != nullptr)
@@ -1555,6 +1668,25 @@ hipError_t launch_bv(const ChunkArgs &a, hipStream_t s) {
 struct KdaWs {
   unsigned long long q, e, r, rec, flags, total;
 };
+// Sequence split (see ChunkArgs): where the batch's 32-row value tiles number at most 128 (half
+// of MI355X's 256 CUs) and the sequence has two chunks or more.  The second segment starts at
+// half the chunks when all three groups of workgroups fit on the CUs at once, else at two
+// thirds (roles 0 and 1 start first; role 2 takes the CUs that role 1 frees).
+constexpr long long kCUs = 256;
+int seg_split_of(long long B, long long H, long long T) {
+  const long long per = B * H * (kD / 32), nch = (T + kC - 1) / kC;
+  if (per * 2 > kCUs || nch < 2) return 0;
+  const long long cs = per * 3 <= kCUs ? nch / 2 : (2 * nch + 1) / 3;
+  return static_cast<int>(max(1ll, min(cs, nch - 1)));
+}
+// bytes of T of every chunk, then (sequence split) q~ [B,T,H,128] bf16 and the three states
+unsigned long long tpre_t_bytes(long long B, long long T, long long H) {
+  return static_cast<unsigned long long>(B * H) * static_cast<unsigned long long>((T + kC - 1) / kC) * (10ull * 2 * 256 * 2);
+}
+unsigned long long seg_qt_bytes(long long B, long long T, long long H) {
+  return (static_cast<unsigned long long>(B * T * H) * kD * 2 + 255ull) & ~255ull;
+}
+
 KdaWs kda_ws(long long B, long long T, long long H) {
   auto al = [](unsigned long long x) { return (x + 255ull) & ~255ull; };
   const unsigned long long arr = al(static_cast<unsigned long long>(B * T * H) * kD * 2);
@@ -1653,7 +1785,23 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    return launch_bv<32>(a, s);
+    ChunkArgs b = a;
+    const int cs = seg_split_of(a.B, a.H, a.T);
+    if (cs > 0) {
+      char *ws = reinterpret_cast<char *>(const_cast<uint16_t *>(a.tpre)) + tpre_t_bytes(a.B, a.T, a.H);
+      b.seg_split = cs;
+      b.seg_qt = reinterpret_cast<uint16_t *>(ws);
+      b.seg_state = reinterpret_cast<float *>(ws + seg_qt_bytes(a.B, a.T, a.H));
+    }
+    hipError_t e = launch_bv<32>(b, s);
+    if (e != hipSuccess || cs == 0) return e;
+    const int t0 = cs * kC;
+    hipLaunchKernelGGL(seg_out_fixup_kernel, dim3((a.T - t0 + 63) / 64, a.H, a.B), dim3(256), 0, s, a, b.seg_state,
+                       b.seg_qt, t0);
+    if (a.state_out != nullptr)
+      hipLaunchKernelGGL(seg_state_fixup_kernel, dim3(static_cast<unsigned>(a.B * a.H), kD / 8), dim3(kD), 0, s,
+                         b.seg_state, a.state_out, static_cast<long long>(a.B) * a.H);
+    return hipGetLastError();
   }
   return chunk_mfma_bv(a) == 32 ? launch_bv<32>(a, s) : launch_bv<16>(a, s);
 }
@@ -1667,8 +1815,9 @@ unsigned long long chunk_mfma_tpre_bytes(const gdr_desc_t &d) {
     return chunk_mfma_kda_supports(d, none, nullptr, nullptr, nullptr) ? kda_ws(d.B, d.T, d.H).total : 0;
   }
   if (d.wkey != GDR_WKEY_SAME || d.neumann_order >= 0 || d.decay == GDR_DECAY_CHANNEL) return 0;
-  const unsigned long long nchunks = (static_cast<unsigned long long>(d.T) + kC - 1) / kC;
-  return static_cast<unsigned long long>(d.B) * d.H * nchunks * (10ull * 2 * 256 * 2);
+  const unsigned long long tb = tpre_t_bytes(d.B, d.T, d.H);
+  if (seg_split_of(d.B, d.H, d.T) == 0) return tb;
+  return tb + seg_qt_bytes(d.B, d.T, d.H) + 3ull * d.B * d.H * kD * kD * 4;
 }
 
 }  // namespace gdr

@@ -28,6 +28,16 @@ struct ChunkArgs {
   // [B, H, chunks][hi, lo][64][64] (gdr_chunk_fwd_ws); null: the matrix-core kernel forms it.
   // With the per-channel decay on the matrix-core kernel: the base of its whole workspace
   const uint16_t *tpre;
+  // Sequence split (gdr_chunk_fwd_ws, where the batch's value tiles fill at most half the GPU):
+  // seg_split > 0 is the first chunk of the second segment.  The sequential pass then runs
+  // three groups of workgroups: the first segment from state_in (its final state S_mid to
+  // seg_state[0]), the second from a zero state (outputs to out, final state S_loc to
+  // seg_state[1]), and the second again with V' = 0 from the identity (its outputs
+  // q~ = scale M q to seg_qt [B,T,H,128] bf16, its final state M to seg_state[2]);
+  // a fix-up adds S_mid q~ to the second segment's outputs and forms S_mid M + S_loc.
+  int seg_split;
+  uint16_t *seg_qt;
+  float *seg_state;   // [3][B,H,Dv,Dk]
 };
 
 // Backward pass (gdr_chunk_bwd): the forward's arguments plus the incoming gradients, the

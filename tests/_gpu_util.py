@@ -32,9 +32,10 @@ def precond_opts(s):
 def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, residual_steps=0,
               impl="auto", scale=1.0, chunk=None, sync=True, workspace=False):
     """gdr_chunk_fwd on inputs ``x`` (numpy, from gdr_synth).  Returns torch tensors.
-    ``workspace``: call gdr_chunk_fwd_ws with a workspace of 64 KB per (batch, head, chunk of
-    64 tokens) and 1 KB more (above both layouts: T alone, or the per-channel decay's operands
-    and records), filled with garbage first (its contents on entry must not matter)."""
+    ``workspace``: call gdr_chunk_fwd_ws with a workspace above every layout it may need (64 KB
+    per (batch, head, chunk of 64 tokens) for T or the per-channel decay's operands and records,
+    plus the sequence split's q~ and three states), filled with garbage first (its contents on
+    entry must not matter)."""
     import torch
     import chunked_gated_delta_gdr_amd as G
     io = torch_dtype(s.dtype)
@@ -42,7 +43,8 @@ def run_chunk(s, x, *, state_in=None, pc_h_in=None, pc_t0=0, neumann_order=-1, r
     ws = None
     if workspace:
         nch = (s.T + 63) // 64
-        ws = torch.full((s.B * s.H * nch * 65536 + 1024,), 0x7f, dtype=torch.uint8, device="cuda")
+        nbytes = s.B * s.H * nch * 65536 + s.B * s.T * s.H * 256 + s.B * s.H * 3 * 65536 + 2048
+        ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
     out = G.gdr_chunk_fwd(
         dev(x["q"], io), dev(x["k"], io), dev(x["v"], io),
         beta=dev(x.get("beta"), f32), log_alpha=dev(x.get("log_alpha"), f32),

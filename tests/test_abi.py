@@ -433,7 +433,13 @@ def test_forward_workspace_size_and_checks():
     that is too small, misaligned or overlapping an argument is rejected before anything runs."""
     d = desc(Dk=128, Dv=128)
     need = G.gdr_chunk_fwd_workspace_size(d)
-    assert need == 2 * 3 * 2 * 10240   # ten 16 x 16 blocks of T as bf16 pairs
+    al = lambda x: (x + 255) // 256 * 256
+    # ten 16 x 16 blocks of T as bf16 pairs per chunk; this batch's 24 value tiles of 32 rows fill
+    # at most half of the CUs, so the sequence split adds q~ [B, T, H, 128] bf16 and three states
+    assert need == 2 * 3 * 2 * 10240 + al(2 * 100 * 3 * 128 * 2) + 3 * 2 * 3 * 128 * 128 * 4
+    big = desc(Dk=128, Dv=128, B=16, H=16)   # 1024 value tiles: no split
+    assert G.gdr_chunk_fwd_workspace_size(big) == 16 * 16 * 2 * 10240
+    assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, T=64)) == 2 * 3 * 1 * 10240   # one chunk: no split
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, chunk=128)) == need
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, wkey=G.GDR_WKEY_DIAG_PRECOND)) == 0
     assert G.gdr_chunk_fwd_workspace_size(desc(Dk=128, Dv=128, neumann_order=3)) == 0
