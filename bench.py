@@ -751,19 +751,27 @@ def main():
 
     parity = None
     if not args.no_parity:
+        # stream (0,0) of the last timed input set against the oracle: with the exact T the whole
+        # stream (the worst 64-token block and the final state too), with a band limit its first
+        # 512 tokens against the oracle's chunk form
         import oracle
-        n = min(512, s.T)
+        n = s.T if args.neumann < 0 else min(512, s.T)
         j = (args.steps - 1) % 2
         xs = x if j == 0 else rolled
         sub = {k: (None if v is None else v[:1, :n, :1]) for k, v in xs.items()}
         pre = dict(rho=s.pc_rho, eps=s.pc_eps, h0=s.pc_h0, t0=0) if precond else None
         if args.neumann < 0:
-            o_ref, _, _ = oracle.recurrent(sub, precond=pre)
+            o_ref, s_ref, _ = oracle.recurrent(sub, precond=pre)
         else:
             mode = ("neumann", args.neumann) if args.residual <= 0 else ("residual", args.neumann, args.residual)
             o_ref, _, _ = oracle.chunked(sub, chunk=s.chunk, t_mode=mode, precond=pre)
         got = outs[j][:1, :n, :1].double().cpu().numpy()
         parity = {"stream": "(0,0)", "tokens": n, "rel_l2_out": oracle.rel_l2(got, o_ref)}
+        if args.neumann < 0:
+            parity["rel_l2_out_worst_64_token_block"] = max(
+                oracle.rel_l2(got[:, t:t + 64], o_ref[:, t:t + 64]) for t in range(0, n, 64))
+            parity["rel_l2_out_last_512_tokens"] = oracle.rel_l2(got[:, -512:], o_ref[:, -512:])
+            parity["rel_l2_state"] = oracle.rel_l2(states[j][:1, :1].double().cpu().numpy(), s_ref)
 
     exact_vs_approx = None
     if args.neumann >= 0 and not args.no_parity:

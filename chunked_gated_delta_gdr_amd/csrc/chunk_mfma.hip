@@ -290,7 +290,7 @@ __device__ __forceinline__ int role_wave(int tid) {
 // The helper waves' loop, instantiated per role: STG (helpers 2 and up) stage the inputs,
 // the others (helpers 0, 1) form T's off-diagonal blocks.  Each instantiation holds only its
 // own role's state across iterations, and both run the kernel's barrier sequence.
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG, bool TP, bool KD>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool STG, bool TP, bool KD, bool SEG>
 __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -324,8 +324,10 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   // With the sequence split the grid holds three groups of the batch's value tiles, in this
   // order (so the first two are resident first): role 0 the first segment, role 1 the second
   // from a zero state, role 2 the second's transition (V' = 0 from the identity)
-  const int per = a.seg_split > 0 ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
-  const int role = static_cast<int>(blockIdx.x) / per, local = static_cast<int>(blockIdx.x) % per;
+  // (SEG, a compile-time choice, so the unsplit kernel keeps its constant chunk range)
+  const int per = SEG ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
+  const int role = SEG ? static_cast<int>(blockIdx.x) / per : 0;
+  const int local = SEG ? static_cast<int>(blockIdx.x) % per : static_cast<int>(blockIdx.x);
   const int logical = (per % 8 == 0) ? (local % 8) * (per / 8) + local / 8 : local;
   const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
   const int H = a.H, T = a.T;
@@ -334,8 +336,8 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
   const long long gate0 = static_cast<long long>(b) * T * H + h;
   const int nchunks = (T + kC - 1) / kC;
-  const int cbeg = role == 0 ? 0 : a.seg_split;                                  // this workgroup's chunks
-  const int cend = (role == 0 && a.seg_split > 0) ? a.seg_split : nchunks;
+  const int cbeg = (SEG && role != 0) ? a.seg_split : 0;   // this workgroup's chunks
+  const int cend = (SEG && role == 0) ? a.seg_split : nchunks;
   const int N = a.N;
   auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
 
@@ -437,7 +439,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
         const uint32_t m = srow[s] < n ? 0xffffffffu : 0u;
         x = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
       }
-      if (role == 2 && isv) x = make_uint4(0u, 0u, 0u, 0u);   // the transition: V' = 0
+      if (SEG && role == 2 && isv) x = make_uint4(0u, 0u, 0u, 0u);   // the transition: V' = 0
       uint4 xg = x;   // gated copy: erase (.) k, write (.) v
       if (CHAN) {
         xg.x = f32x2_to_bf16x2_bits(elem(pb[s], 0) * elem(x, 0), elem(pb[s], 1) * elem(x, 1));
@@ -1026,7 +1028,7 @@ __device__ __forceinline__ void helper_loop(Smem<BV, CHAN, WK> &sm, const ChunkA
   }
 }
 
-template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool TP, bool KD = false>
+template <int BV, bool CHAN, bool DECAY, int WK, bool RES, bool TP, bool KD = false, bool SEG = false>
 __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int NVW = BV / 16;             // value waves
   constexpr int NVT = kD / BV;             // value tiles per head
@@ -1061,8 +1063,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   // With the sequence split the grid holds three groups of the batch's value tiles, in this
   // order (so the first two are resident first): role 0 the first segment, role 1 the second
   // from a zero state, role 2 the second's transition (V' = 0 from the identity)
-  const int per = a.seg_split > 0 ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
-  const int role = static_cast<int>(blockIdx.x) / per, local = static_cast<int>(blockIdx.x) % per;
+  // (SEG, a compile-time choice, so the unsplit kernel keeps its constant chunk range)
+  const int per = SEG ? static_cast<int>(gridDim.x) / 3 : static_cast<int>(gridDim.x);
+  const int role = SEG ? static_cast<int>(blockIdx.x) / per : 0;
+  const int local = SEG ? static_cast<int>(blockIdx.x) % per : static_cast<int>(blockIdx.x);
   const int logical = (per % 8 == 0) ? (local % 8) * (per / 8) + local / 8 : local;
   const int bh = logical / NVT, vt = logical % NVT, v0 = vt * BV;
   const int H = a.H, T = a.T;
@@ -1071,8 +1075,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
   const long long gate0 = static_cast<long long>(b) * T * H + h;
   const int nchunks = (T + kC - 1) / kC;
-  const int cbeg = role == 0 ? 0 : a.seg_split;                                  // this workgroup's chunks
-  const int cend = (role == 0 && a.seg_split > 0) ? a.seg_split : nchunks;
+  const int cbeg = (SEG && role != 0) ? a.seg_split : 0;   // this workgroup's chunks
+  const int cend = (SEG && role == 0) ? a.seg_split : nchunks;
   const int N = a.N;
   auto keep = [N](int i, int j) { return N < 0 || i - j <= N; };
 
@@ -1082,9 +1086,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
   const uint16_t *gwk = static_cast<const uint16_t *>(a.write_key);
   const uint16_t *ger = static_cast<const uint16_t *>(a.erase);
   const uint16_t *gwr = static_cast<const uint16_t *>(a.write);
-  uint16_t *gout = role == 2 ? a.seg_qt : static_cast<uint16_t *>(a.out);
+  uint16_t *gout = (SEG && role == 2) ? a.seg_qt : static_cast<uint16_t *>(a.out);
   // final state: with the sequence split each role's goes to its slot of seg_state
-  float *const sout = a.seg_split > 0 ? a.seg_state + static_cast<long long>(role) * a.B * a.H * kD * kD : a.state_out;
+  float *const sout = SEG ? a.seg_state + static_cast<long long>(role) * a.B * a.H * kD * kD : a.state_out;
 
   // ---------------- one-time init: zero T (upper blocks stay zero) and P ----------------
   for (int i = tid; i < 2 * kC * kLdc; i += kNT) (&sm.t[0][0][0])[i] = (&sm.tl[0][0][0])[i] = 0;
@@ -1112,10 +1116,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         st[cb] = zero4();
-        if (role == 2) {   // the transition starts from the identity (its rows are unit rows)
+        if (SEG && role == 2) {   // the transition starts from the identity (its rows are unit rows)
 #pragma unroll
           for (int r = 0; r < 4; ++r) st[cb][r] = chan0(cb) + r == vrow ? 1.f : 0.f;
-        } else if (role == 0 && a.state_in != nullptr) {
+        } else if ((!SEG || role == 0) && a.state_in != nullptr) {
           const float4 sv = ld4f(a.state_in + (static_cast<long long>(bh) * kD + vrow) * kD + chan0(cb));
           st[cb] = float4v{sv.x, sv.y, sv.z, sv.w};
         }
@@ -1346,8 +1350,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_mfma_kernel(ChunkArgs a) {
     return;
   }
 
-  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true, TP, KD>(sm, a);
-  else helper_loop<BV, CHAN, DECAY, WK, RES, false, TP, KD>(sm, a);
+  if (hw >= 2) helper_loop<BV, CHAN, DECAY, WK, RES, true, TP, KD, SEG>(sm, a);
+  else helper_loop<BV, CHAN, DECAY, WK, RES, false, TP, KD, SEG>(sm, a);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1639,6 +1643,9 @@ hipError_t launch4(const ChunkArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (kD / BV) * (a.seg_split > 0 ? 3u : 1u);
   if (a.S > 0)
     hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, true, false>), dim3(grid), dim3(kNT), 0, s, a);
+  else if (WK == kWkSame && BV == 32 && a.tpre != nullptr && a.seg_split > 0)
+    hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false, WK == kWkSame && BV == 32, false, true>), dim3(grid),
+                       dim3(kNT), 0, s, a);
   else if (WK == kWkSame && BV == 32 && a.tpre != nullptr)
     hipLaunchKernelGGL((chunk_mfma_kernel<BV, CHAN, DECAY, WK, false, WK == kWkSame && BV == 32>), dim3(grid), dim3(kNT), 0, s, a);
   else
