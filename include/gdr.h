@@ -170,7 +170,10 @@ gdr_status_t gdr_chunk_fwd(const gdr_desc_t *desc, const gdr_inputs_t *in,
  * write key k, exact T): the workspace then also holds each chunk's decayed keys and queries,
  * P and the per-channel state decay, all formed before the sequential pass; gdr_chunk_fwd
  * runs that descriptor on the fp32 kernel.  Results equal gdr_chunk_fwd's within the bf16
- * bound.
+ * bound.  Where the batch's 32-row value tiles (B * H * 4) number at most 128, the sequential
+ * pass also splits each sequence in two segments that run at once: the second from a zero
+ * state and again as its own transition from the identity.  Their outputs are then corrected
+ * by the first segment's final state (linearity of the recurrence in its state).
  *
  *   workspace        device memory of at least gdr_chunk_fwd_workspace_size(desc) bytes,
  *                    256-byte aligned, overlapping no other argument; its contents on entry
@@ -183,7 +186,9 @@ gdr_status_t gdr_chunk_fwd_ws(const gdr_desc_t *desc, const gdr_inputs_t *in,
                               void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* Bytes of gdr_chunk_fwd_ws's workspace: 10 KB per (batch, head, chunk of 64 tokens) where it
- * applies (T's ten 16 x 16 blocks on and below the diagonal, each as a pair of bf16 parts), 0
+ * applies (T's ten 16 x 16 blocks on and below the diagonal, each as a pair of bf16 parts); with
+ * the sequence split (B * H * 4 <= 128, at least two chunks) also B * T * H * 256 bytes rounded
+ * up to 256 (the transition's outputs) and 3 * B * H * 65536 bytes (three fp32 states); 0
  * where it does not (any workspace is then ignored) or for an invalid descriptor.  With the
  * per-channel decay: three [B, T, H, 128] bf16 arrays (the decayed keys and queries), then
  * 15872 bytes and a 4-byte flag per (batch, head, chunk), each section rounded up to 256 bytes
