@@ -1548,12 +1548,13 @@ __global__ __launch_bounds__(64 * kTW) void chunk_t_kernel(ChunkArgs a, uint16_t
 // o_t = S_mid (scale M_t q_t) + o_loc,t = S_mid q~_t + o_loc,t and S_end = S_mid M + S_loc.
 // ---------------------------------------------------------------------------------------
 // out[b, t, h, :] += S_mid q~_t for the second segment's tokens: one workgroup of four waves per
-// (64 tokens, head, batch); wave w owns state rows 32 w .. + 31 and keeps their columns of
+// (ngrp groups of 64 tokens, head, batch; more groups per workgroup amortize loading S_mid when
+// there are many); wave w owns state rows 32 w .. + 31 and keeps their columns of
 // S_mid^T as bf16 hi / lo B operands; per 16-token block the A operand is q~ (bf16), and the
 // 16 x 32 fp32 result goes through LDS so that each lane adds 8 consecutive values of one
 // token with one 16-byte read and write of out
 __global__ __launch_bounds__(256) void seg_out_fixup_kernel(ChunkArgs a, const float *smid, const uint16_t *qt,
-                                                             int t0) {
+                                                             int t0, int ngrp) {
   __shared__ float tile[4][16][33];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -1573,22 +1574,35 @@ __global__ __launch_bounds__(256) void seg_out_fixup_kernel(ChunkArgs a, const f
   const long long tokstride = static_cast<long long>(H) * kD;
   const long long head0 = (static_cast<long long>(b) * T * H + h) * kD;
   uint16_t *out = static_cast<uint16_t *>(a.out);
-  const int tb0 = t0 + static_cast<int>(blockIdx.x) * 64;
+#pragma unroll 1
+  for (int grp = 0; grp < ngrp; ++grp) {
+  const int tb0 = t0 + (static_cast<int>(blockIdx.x) * ngrp + grp) * 64;
+  if (tb0 >= T) break;
+  // every load of the group's four 16-token blocks is issued first: the A operands (q~ rows
+  // tb0 + 16 blk + l16, read clamped past the end) and this lane's 16-byte piece of out for
+  // each block (token tb0 + 16 blk + lane / 4, state rows 32 wave + 8 (lane % 4) ..)
+  const int tr = lane >> 2, c8 = 8 * (lane & 3);
+  short8v av[4][4];
+  uint4 ow[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const long long arow = head0 + static_cast<long long>(min(tb0 + 16 * blk + l16, T - 1)) * tokstride;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) av[blk][s2] = ld8(qt + arow + 32 * s2 + 8 * l4);
+    const int t = min(tb0 + 16 * blk + tr, T - 1);
+    ow[blk] = *reinterpret_cast<const uint4 *>(out + head0 + static_cast<long long>(t) * tokstride + 32 * wave + c8);
+  }
+#pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     const int tt = tb0 + 16 * blk;
     if (tt >= T) break;
-    // A operand: token row tt + l16 (read clamped past the end), K = 32 s + 8 l4 ..
-    const long long arow = head0 + static_cast<long long>(min(tt + l16, T - 1)) * tokstride;
-    short8v av[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) av[s2] = ld8(qt + arow + 32 * s2 + 8 * l4);
     float4v acc[2] = {zero4(), zero4()};
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32(av[s2], blo[j][s2], mfma32(av[s2], bhi[j][s2], acc[j]));
+      for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32(av[blk][s2], blo[j][s2], mfma32(av[blk][s2], bhi[j][s2], acc[j]));
     // lane: tokens tt + 4 l4 + r, state row 32 wave + 16 j + l16; read back as token lane / 4,
-    // rows 32 wave + 8 (lane % 4) .. + 7
+    // rows 32 wave + 8 (lane % 4) .. + 7, added to the piece of out loaded above
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1596,19 +1610,20 @@ __global__ __launch_bounds__(256) void seg_out_fixup_kernel(ChunkArgs a, const f
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int tr = lane >> 2, c8 = 8 * (lane & 3), t = tt + tr;
+    const int t = tt + tr;
     if (t < T) {
-      uint4 *o = reinterpret_cast<uint4 *>(out + head0 + static_cast<long long>(t) * tokstride + 32 * wave + c8);
-      const uint4 w = *o;
+      const uint4 w = ow[blk];
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = elem(w, e) + tile[wave][tr][c8 + e];
-      *o = make_uint4(f32x2_to_bf16x2_bits(x[0], x[1]), f32x2_to_bf16x2_bits(x[2], x[3]),
-                      f32x2_to_bf16x2_bits(x[4], x[5]), f32x2_to_bf16x2_bits(x[6], x[7]));
+      *reinterpret_cast<uint4 *>(out + head0 + static_cast<long long>(t) * tokstride + 32 * wave + c8) =
+          make_uint4(f32x2_to_bf16x2_bits(x[0], x[1]), f32x2_to_bf16x2_bits(x[2], x[3]),
+                     f32x2_to_bf16x2_bits(x[4], x[5]), f32x2_to_bf16x2_bits(x[6], x[7]));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   }
 }
 
@@ -1803,8 +1818,10 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s) {
     hipError_t e = launch_bv<32>(b, s);
     if (e != hipSuccess || cs == 0) return e;
     const int t0 = cs * kC;
-    hipLaunchKernelGGL(seg_out_fixup_kernel, dim3((a.T - t0 + 63) / 64, a.H, a.B), dim3(256), 0, s, a, b.seg_state,
-                       b.seg_qt, t0);
+    const long long groups = (a.T - t0 + 63) / 64;
+    const int ngrp = groups * a.H * a.B >= 4096 ? 4 : 1;
+    hipLaunchKernelGGL(seg_out_fixup_kernel, dim3(static_cast<unsigned>((groups + ngrp - 1) / ngrp), a.H, a.B), dim3(256), 0,
+                       s, a, b.seg_state, b.seg_qt, t0, ngrp);
     if (a.state_out != nullptr)
       hipLaunchKernelGGL(seg_state_fixup_kernel, dim3(static_cast<unsigned>(a.B * a.H), kD / 8), dim3(kD), 0, s,
                          b.seg_state, a.state_out, static_cast<long long>(a.B) * a.H);
