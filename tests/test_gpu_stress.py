@@ -175,6 +175,36 @@ def test_stress_full_size_sampled(name, stress):
 
 
 # --------------------------------------------------------------------------------------
+# The workspace path (gdr_chunk_fwd_ws): T of every chunk formed first, and at these batch
+# sizes (B * H * 4 <= 128 value tiles) the sequence split, whose second segment's outputs and
+# final state come from the linear combination S_mid M + S_loc
+# --------------------------------------------------------------------------------------
+
+WS_CASES = [(v, st) for (v, st) in MFMA_CASES if v in ("gdn", "plain", "gdn2", "gdn2_decay")]
+
+
+@pytest.mark.parametrize("variant,stress", WS_CASES)
+def test_stress_workspace_split(variant, stress):
+    s = stress_spec(variant, stress)
+    announce(f"workspace + split {variant} {stress} {s}")
+    x = gs.make_inputs(s)
+    rng = np.random.default_rng(21)
+    S0 = (rng.standard_normal((s.B, s.H, s.Dv, s.Dk)) * 0.2).astype(np.float32).astype(np.float64)
+    o, S, _ = run_chunk(s, x, state_in=S0.astype(np.float32), impl="mfma", workspace=True)
+    check(s, x, o, S, TOL_BF16, S0=S0, label=f"workspace {variant} {stress}")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,stress", [("gdn2", "corr3"), ("long", "corr3_beta12"), ("long", "corr3_strong")])
+def test_stress_full_size_sampled_workspace(name, stress):
+    s = gs.spec(name, **STRESS[stress])
+    announce(f"full size through the workspace (sequence split) {name} {stress} {s}")
+    x = gs.make_inputs(s)
+    o, S, _ = run_chunk(s, x, workspace=True)
+    check(s, x, o, S, TOL_BF16, streams=[(0, 0), (s.B - 1, s.H - 1)], label=f"full ws {name} {stress}")
+
+
+# --------------------------------------------------------------------------------------
 # Decode step
 # --------------------------------------------------------------------------------------
 
