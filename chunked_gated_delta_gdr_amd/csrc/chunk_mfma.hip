@@ -1628,7 +1628,8 @@ __global__ __launch_bounds__(256) void seg_out_fixup_kernel(ChunkArgs a, const f
 }
 
 // state_out = S_mid M + S_loc in fp32: one workgroup per (batch-head, 8 state rows), one thread
-// per column (each element of M read once for the 8 rows, which sit in LDS)
+// per column; the 8 rows of S_mid sit in LDS, and each thread reads its column of M in slices
+// of 32 loads issued back to back (each element of M read once for the 8 rows)
 __global__ __launch_bounds__(kD) void seg_state_fixup_kernel(const float *seg_state, float *state_out, long long nbh) {
   __shared__ float rows[8][kD];
   const long long bh = blockIdx.x;
@@ -1642,11 +1643,14 @@ __global__ __launch_bounds__(kD) void seg_state_fixup_kernel(const float *seg_st
     rows[r][k] = smid[(v0 + r) * kD + k];
   }
   __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < kD; ++i) {
-    const float mk = m[i * kD + k];
+  for (int i0 = 0; i0 < kD; i0 += 32) {
+    float mv[32];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = fmaf(rows[r][i], mk, acc[r]);
+    for (int i = 0; i < 32; ++i) mv[i] = m[(i0 + i) * kD + k];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(rows[r][i0 + i], mv[i], acc[r]);
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) state_out[(bh * kD + v0 + r) * kD + k] = acc[r];
